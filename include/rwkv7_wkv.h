@@ -1,0 +1,146 @@
+/*
+ * rwkv7_wkv.h -- C ABI of the MI355X (gfx950) WKV7 library, librwkv7_wkv.so.
+ *
+ * The WKV7 recurrence is the generalised delta-rule state update of RWKV-7
+ * "Goose".  Per (batch b, head h), with an N x N float32 state S whose row
+ * index i is the VALUE index and whose column index j is the KEY index, each
+ * token t computes
+ *
+ *     u      = S kappa_t                                  (state before the step)
+ *     S      = S diag(w_t) - u (kappa_t * a_t)^T + v_t k_t^T
+ *     y_t    = S r_t                                      (state after the step)
+ *
+ * Sources: RWKV-7 "Goose" author response (paperhub), numpy time_mixing
+ * listing (the update, the readout, the per-head GroupNorm and the bonus);
+ * ARWKV verdict (pith.science, arXiv 2501.15570), key_machinery field (the same
+ * update in row-vector form); RWKV-7 "Goose" summary (paperlayer, arXiv
+ * 2503.14456v2), §4 Method (diagonal-plus-rank-one transition, parallel
+ * chunked form), §8 Speed and Memory (head size 64, float32 states,
+ * constant-memory single-token inference, chunked pre-fill).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is a DEVICE pointer owned by the caller.  The
+ *    library allocates no device memory, keeps no mutable global state and
+ *    may be called from several host threads on different streams.
+ *  - Per-token vectors r, w, k, v, kappa, a and the output y are dense,
+ *    C-order [B, T, H, N] (forward) or [B, H, N] (decode) in the element type
+ *    `dt`.  kappa is the removal key (the normalised key of the pages), k the
+ *    replacement key that is written, a the in-context learning rate, w the
+ *    decay, r the receptance.  The library applies no transform to any of them.
+ *  - States are float32 [B, H, N, N], row-major: state[b][h][i][j], i = value
+ *    index, j = key index.
+ *  - N must be 64 (the head size the pages' kernels are tuned for); B, H >= 1;
+ *    T >= 0.  All internal offsets are 64-bit.
+ *  - Every pointer must be 16-byte aligned.
+ *  - All validation runs on the host, synchronously, before anything is
+ *    enqueued: on any error nothing is launched and nothing is written.
+ *    Kernel faults surface at the caller's next synchronisation.  No C++
+ *    exception crosses this interface.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without waiting.
+ *  - Numerics: float32 state and accumulation; y is rounded to nearest even
+ *    when dt is bf16; NaN/Inf propagate; kappa is used exactly as given (not
+ *    renormalised); a is not clamped.
+ */
+#ifndef RWKV7_WKV_H
+#define RWKV7_WKV_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RWKV7_ABI_VERSION 1
+
+typedef enum {
+    RWKV7_OK = 0,
+    RWKV7_ERR_NULL = 1,        /* a required pointer is NULL                         */
+    RWKV7_ERR_SHAPE = 2,       /* B < 1, H < 1, T < 0, or a size overflows            */
+    RWKV7_ERR_DTYPE = 3,       /* unknown dtype / algo value                          */
+    RWKV7_ERR_UNSUPPORTED = 4, /* N != 64, or algo not available for this dtype      */
+    RWKV7_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                    */
+    RWKV7_ERR_ALIAS = 6,       /* an output overlaps an input (other than s_out==s0) */
+    RWKV7_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required          */
+    RWKV7_ERR_HIP = 8          /* the HIP runtime refused a launch                    */
+} rwkv7_status;
+
+typedef enum { RWKV7_DT_F32 = 0, RWKV7_DT_BF16 = 1 } rwkv7_dtype;
+
+typedef enum {
+    RWKV7_ALGO_AUTO = 0,    /* CHUNKED for bf16, SCAN for f32                          */
+    RWKV7_ALGO_SCAN = 1,    /* token-by-token recurrence, state kept on chip           */
+    RWKV7_ALGO_CHUNKED = 2  /* chunked-parallel form on bf16 MFMA, float32 state;      */
+                            /* bf16 only; requires 0 < w <= 1 (the pages' decay        */
+                            /* parameterisation keeps w above 0.545)                   */
+} rwkv7_algo;
+
+/*
+ * Optional fused epilogue: per-head GroupNorm of y over the N value channels
+ * (mean and population variance, eps inside the square root, then the
+ * per-channel affine ln_w, ln_b over the flattened H*N channels), followed by
+ * the current-token bonus (sum_j r_j k_j r_k[h*N+j]) * v_i added after the
+ * norm.  Source: RWKV-7 "Goose" author response (paperhub), numpy
+ * time_mixing listing (group_norm with eps 64e-5 and the bonus line);
+ * RWKV-7 "Goose" summary, App. F (per-head normalisation after receptance).
+ * All three arrays are float32 device pointers of H*N entries.  ln_w == NULL
+ * means all ones, ln_b == NULL all zeros; r_k is required.  The state is never
+ * affected by the epilogue.
+ */
+typedef struct {
+    const float *ln_w;
+    const float *ln_b;
+    const float *r_k;
+    float eps; /* the pages use 64e-5 */
+} rwkv7_epilogue;
+
+/*
+ * Forward over T tokens for B independent sequences (prefill).
+ *   r, w, k, v, kappa, a : [B,T,H,N] in dt (inputs)
+ *   s0    : [B,H,N,N] float32 initial state, or NULL for a zero state
+ *   y     : [B,T,H,N] in dt (output; after the epilogue when epi != NULL)
+ *   s_out : [B,H,N,N] float32 final state S_T, or NULL to skip it; may equal s0
+ *           (updated in place); any other overlap with an input is an error
+ *   epi   : NULL, or the fused epilogue above
+ *   workspace / workspace_bytes : device scratch of at least
+ *           rwkv7_wkv_forward_workspace(...) bytes (may be NULL when that is 0)
+ * T == 0: y is untouched and s_out receives s0 (or zeros).
+ */
+rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, const void *v,
+                               const void *kappa, const void *a, const float *s0, void *y,
+                               float *s_out, int B, int T, int H, int N, rwkv7_dtype dt,
+                               rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace rwkv7_wkv_forward needs for this problem (0 if none). */
+size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
+                                   rwkv7_algo algo);
+
+/*
+ * One token for each of B resident states (single-token inference, the
+ * recurrence at T = 1 with the state read from and written back to HBM).
+ *   r, w, k, v, kappa, a : [B,H,N] in dt
+ *   state : [B,H,N,N] float32, updated in place (for a layer-major pool the
+ *           caller passes the layer's slice)
+ *   y     : [B,H,N] in dt, must not overlap any other argument
+ * Source: RWKV-7 "Goose" summary, §8 Speed and Memory (constant-memory
+ * single-token inference); RWKV-X verdict (pith.science, arXiv 2504.21463):
+ * RWKV-7 keeps no KV cache, only this state.
+ */
+rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const void *v,
+                              const void *kappa, const void *a, float *state, void *y, int B,
+                              int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
+                              void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *rwkv7_status_str(rwkv7_status s);
+
+/* RWKV7_ABI_VERSION of the built library. */
+int rwkv7_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RWKV7_WKV_H */

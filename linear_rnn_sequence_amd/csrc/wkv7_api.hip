@@ -1,0 +1,243 @@
+// Host side of librwkv7_wkv.so: argument validation and dispatch for the C ABI
+// declared in include/rwkv7_wkv.h.  Every check runs before anything is
+// enqueued, so a failed call launches nothing and writes nothing.
+#include <stdint.h>
+#include <string.h>
+
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+__global__ void state_copy_kernel(const float4 *src, float4 *dst, size_t n4) {
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n4) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// a * b * ... with overflow detection against SIZE_MAX / 2
+bool mul_ok(size_t &acc, size_t x) {
+    if (x != 0 && acc > (SIZE_MAX / 2) / x) return false;
+    acc *= x;
+    return true;
+}
+
+rwkv7_status check_epilogue(const rwkv7_epilogue *epi) {
+    if (!epi) return RWKV7_OK;
+    if (!epi->r_k) return RWKV7_ERR_NULL;
+    if (!aligned16(epi->r_k) || (epi->ln_w && !aligned16(epi->ln_w)) ||
+        (epi->ln_b && !aligned16(epi->ln_b)))
+        return RWKV7_ERR_ALIGN;
+    return RWKV7_OK;
+}
+
+EpilogueArgs to_epi(const rwkv7_epilogue *epi) {
+    EpilogueArgs e{};
+    if (epi) {
+        e.ln_w = epi->ln_w;
+        e.ln_b = epi->ln_b;
+        e.r_k = epi->r_k;
+        e.eps = epi->eps;
+    }
+    return e;
+}
+
+}  // namespace
+
+hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream) {
+    const size_t n4 = count / 4;
+    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(state_copy_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const float4 *>(s0), reinterpret_cast<float4 *>(s_out),
+                       n4);
+    return hipGetLastError();
+}
+
+}  // namespace wkv7
+
+using namespace wkv7;
+
+extern "C" {
+
+int rwkv7_abi_version(void) { return RWKV7_ABI_VERSION; }
+
+const char *rwkv7_status_str(rwkv7_status s) {
+    switch (s) {
+        case RWKV7_OK: return "ok";
+        case RWKV7_ERR_NULL: return "a required pointer is NULL";
+        case RWKV7_ERR_SHAPE: return "invalid shape (B, H >= 1, T >= 0, sizes must fit)";
+        case RWKV7_ERR_DTYPE: return "unknown dtype or algorithm";
+        case RWKV7_ERR_UNSUPPORTED: return "unsupported (N must be 64; chunked needs bf16)";
+        case RWKV7_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case RWKV7_ERR_ALIAS: return "an output overlaps an input";
+        case RWKV7_ERR_WORKSPACE: return "workspace missing or too small";
+        case RWKV7_ERR_HIP: return "HIP launch failed";
+    }
+    return "unknown status";
+}
+
+static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt) {
+    if (algo == RWKV7_ALGO_AUTO)
+        return (dt == RWKV7_DT_BF16 && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+    return algo;
+}
+
+size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo) {
+    if (B < 1 || H < 1 || T < 0 || N != kN) return 0;
+    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return 0;
+    if (resolve_algo(algo, dt) != RWKV7_ALGO_CHUNKED || T == 0) return 0;
+    return chunked_workspace_bytes(B, T, H);
+}
+
+rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, const void *v,
+                               const void *kappa, const void *a, const float *s0, void *y,
+                               float *s_out, int B, int T, int H, int N, rwkv7_dtype dt,
+                               rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
+        return RWKV7_ERR_DTYPE;
+    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
+    const rwkv7_algo al = resolve_algo(algo, dt);
+    if (al == RWKV7_ALGO_CHUNKED && (dt != RWKV7_DT_BF16 || !kChunkedAvailable))
+        return RWKV7_ERR_UNSUPPORTED;
+
+    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    size_t tok = 1, st = 1;
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
+        !mul_ok(tok, (size_t)N) || !mul_ok(tok, esz))
+        return RWKV7_ERR_SHAPE;
+    if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
+        return RWKV7_ERR_SHAPE;
+    if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+
+    const void *ins[6] = {r, w, k, v, kappa, a};
+    if (T > 0) {
+        for (const void *p : ins)
+            if (!p) return RWKV7_ERR_NULL;
+        if (!y) return RWKV7_ERR_NULL;
+    }
+    rwkv7_status es = check_epilogue(epi);
+    if (es != RWKV7_OK) return es;
+    for (const void *p : ins)
+        if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
+    if ((y && !aligned16(y)) || (s0 && !aligned16(s0)) || (s_out && !aligned16(s_out)))
+        return RWKV7_ERR_ALIGN;
+
+    // outputs may not overlap inputs (s_out == s0 exactly is the in-place case)
+    auto rng = [](const void *p, size_t n) {
+        return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+    };
+    if (T > 0) {
+        const Range ry = rng(y, tok);
+        for (const void *p : ins)
+            if (overlap(ry, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        if (s0 && overlap(ry, rng(s0, st))) return RWKV7_ERR_ALIAS;
+        if (s_out && overlap(ry, rng(s_out, st))) return RWKV7_ERR_ALIAS;
+        if (epi) {
+            const size_t pn = (size_t)H * N * 4;
+            if (overlap(ry, rng(epi->r_k, pn)) || (epi->ln_w && overlap(ry, rng(epi->ln_w, pn))) ||
+                (epi->ln_b && overlap(ry, rng(epi->ln_b, pn))))
+                return RWKV7_ERR_ALIAS;
+        }
+    }
+    if (s_out) {
+        const Range rs = rng(s_out, st);
+        if (T > 0)
+            for (const void *p : ins)
+                if (overlap(rs, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        if (s0 && s0 != s_out && overlap(rs, rng(s0, st))) return RWKV7_ERR_ALIAS;
+        if (epi) {
+            const size_t pn = (size_t)H * N * 4;
+            if (overlap(rs, rng(epi->r_k, pn)) || (epi->ln_w && overlap(rs, rng(epi->ln_w, pn))) ||
+                (epi->ln_b && overlap(rs, rng(epi->ln_b, pn))))
+                return RWKV7_ERR_ALIAS;
+        }
+    }
+    const size_t need = rwkv7_wkv_forward_workspace(B, T, H, N, dt, al);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need) return RWKV7_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
+        const Range rw = rng(workspace, need);
+        for (const void *p : ins)
+            if (overlap(rw, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        if (overlap(rw, rng(y, tok)) || (s0 && overlap(rw, rng(s0, st))) ||
+            (s_out && overlap(rw, rng(s_out, st))))
+            return RWKV7_ERR_ALIAS;
+    }
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        if (!s_out || s_out == s0) return RWKV7_OK;
+        return launch_state_copy(s0, s_out, st / 4, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+    }
+
+    ForwardArgs p{};
+    p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
+    p.s0 = s0; p.y = y; p.s_out = s_out;
+    p.B = B; p.T = T; p.H = H;
+    p.bf16 = dt == RWKV7_DT_BF16;
+    p.epilogue = epi != nullptr;
+    p.epi = to_epi(epi);
+    p.workspace = workspace;
+    p.workspace_bytes = workspace_bytes;
+    const hipError_t e = al == RWKV7_ALGO_CHUNKED ? launch_chunked(p, hs) : launch_scan(p, hs);
+    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
+
+rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const void *v,
+                              const void *kappa, const void *a, float *state, void *y, int B,
+                              int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
+                              void *stream) {
+    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1) return RWKV7_ERR_SHAPE;
+    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    size_t tok = 1, st = 1;
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)H) || !mul_ok(tok, (size_t)N * esz))
+        return RWKV7_ERR_SHAPE;
+    if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
+        return RWKV7_ERR_SHAPE;
+    if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+    const void *ins[6] = {r, w, k, v, kappa, a};
+    for (const void *p : ins)
+        if (!p) return RWKV7_ERR_NULL;
+    if (!state || !y) return RWKV7_ERR_NULL;
+    rwkv7_status es = check_epilogue(epi);
+    if (es != RWKV7_OK) return es;
+    for (const void *p : ins)
+        if (!aligned16(p)) return RWKV7_ERR_ALIGN;
+    if (!aligned16(state) || !aligned16(y)) return RWKV7_ERR_ALIGN;
+    auto rng = [](const void *p, size_t n) {
+        return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+    };
+    const Range ry = rng(y, tok), rs = rng(state, st);
+    if (overlap(ry, rs)) return RWKV7_ERR_ALIAS;
+    for (const void *p : ins)
+        if (overlap(ry, rng(p, tok)) || overlap(rs, rng(p, tok))) return RWKV7_ERR_ALIAS;
+    if (epi) {
+        const size_t pn = (size_t)H * N * 4;
+        const void *ps[3] = {epi->r_k, epi->ln_w, epi->ln_b};
+        for (const void *p : ps)
+            if (p && (overlap(ry, rng(p, pn)) || overlap(rs, rng(p, pn)))) return RWKV7_ERR_ALIAS;
+    }
+    DecodeArgs p{};
+    p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
+    p.state = state; p.y = y; p.B = B; p.H = H;
+    p.bf16 = dt == RWKV7_DT_BF16;
+    p.epilogue = epi != nullptr;
+    p.epi = to_epi(epi);
+    return launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RWKV7_OK
+                                                                             : RWKV7_ERR_HIP;
+}
+
+}  // extern "C"

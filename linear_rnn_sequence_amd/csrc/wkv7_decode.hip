@@ -1,0 +1,168 @@
+// WKV7 single-token step over a batch of resident states (decode).
+//
+// One token of the recurrence (RWKV-7 "Goose" author response, numpy
+// time_mixing listing) for each of B*H heads whose float32 states live in HBM:
+//   u_i = sum_j S_ij kappa_j
+//   S_ij <- S_ij w_j - u_i (a_j kappa_j) + v_i k_j      (written back in place)
+//   y_i = sum_j S_ij (w_j r_j) + v_i (k . r) - u_i ((a*kappa) . r)  (= S_new r)
+// This is the constant-memory single-token inference of the RWKV-7 "Goose"
+// summary, §8 Speed and Memory.  The state read and write (32 KiB per head)
+// is all but the whole traffic, so the kernel is laid out for HBM streaming.
+//
+// One wave per head, four heads per 256-thread workgroup.  Lane (c, g) =
+// (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value rows
+// 16g .. 16g+15: every state load instruction reads four complete 256-byte
+// rows (16 lanes x 16 bytes each), so each wave moves its 16 KiB in 16 fully
+// coalesced dwordx4 loads issued back to back.  Row sums (S kappa and
+// S (w*r)) are 16-lane DPP reductions; the per-head GroupNorm of the optional
+// epilogue adds a 4-way exchange across the DPP rows.  Lane c finally holds
+// y of row 16g + c, so the 64 readouts leave as one 128-byte (bf16) store.
+#include "wkv7_device.h"
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+constexpr int kDecodeThreads = 256;
+constexpr int kHeadsPerBlock = kDecodeThreads / 64;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT>
+__device__ __forceinline__ f32x4 ld_state(const float *p) {
+    if (NT) return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    return *reinterpret_cast<const f32x4 *>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void st_state(float *p, f32x4 x) {
+    if (NT)
+        __builtin_nontemporal_store(x, reinterpret_cast<f32x4 *>(p));
+    else
+        *reinterpret_cast<f32x4 *>(p) = x;
+}
+
+// 16 consecutive elements (value rows 16g .. 16g+15), widened to float.
+__device__ __forceinline__ void load16(const uint16_t *p, float *out) {
+    const uint4 a = *reinterpret_cast<const uint4 *>(p);
+    const uint4 b = *reinterpret_cast<const uint4 *>(p + 8);
+    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        out[2 * e] = bf16_lo(u[e]);
+        out[2 * e + 1] = bf16_hi(u[e]);
+    }
+}
+__device__ __forceinline__ void load16(const float *p, float *out) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float4 x = *reinterpret_cast<const float4 *>(p + 4 * q);
+        out[4 * q] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
+    }
+}
+
+template <class IO, bool EPI, bool NT>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
+    using E = typename IO::elem;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const long head = (long)blockIdx.x * kHeadsPerBlock + wave;
+    if (head >= (long)p.B * p.H) return;  // whole wave leaves together
+    const int h = (int)(head % p.H);
+    const int c = lane & 15, g = lane >> 4;
+
+    float *st = p.state + head * (kN * kN) + (16 * g) * kN + 4 * c;
+    f32x4 S[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) S[m] = ld_state<NT>(st + m * kN);
+
+    const long vo = head * kN;
+    const E *pr = static_cast<const E *>(p.r) + vo;
+    const float4 kap = IO::load4(static_cast<const E *>(p.kappa) + vo + 4 * c);
+    const float4 w = IO::load4(static_cast<const E *>(p.w) + vo + 4 * c);
+    const float4 a = IO::load4(static_cast<const E *>(p.a) + vo + 4 * c);
+    const float4 k = IO::load4(static_cast<const E *>(p.k) + vo + 4 * c);
+    const float4 r = IO::load4(pr + 4 * c);
+    float v[16];
+    load16(static_cast<const E *>(p.v) + vo + 16 * g, v);
+
+    const float4 bb = make_float4(a.x * kap.x, a.y * kap.y, a.z * kap.z, a.w * kap.w);
+    const float4 wr = make_float4(w.x * r.x, w.y * r.y, w.z * r.z, w.w * r.w);
+    float kr = k.x * r.x + k.y * r.y + k.z * r.z + k.w * r.w;
+    float br = bb.x * r.x + bb.y * r.y + bb.z * r.z + bb.w * r.w;
+    float bon = 0.f;
+    if (EPI) {
+        const float4 rk = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 4 * c);
+        bon = r.x * k.x * rk.x + r.y * k.y * rk.y + r.z * k.z * rk.z + r.w * k.w * rk.w;
+    }
+
+    float u[16], y[16];
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        u[m] = S[m].x * kap.x + S[m].y * kap.y + S[m].z * kap.z + S[m].w * kap.w;
+        y[m] = S[m].x * wr.x + S[m].y * wr.y + S[m].z * wr.z + S[m].w * wr.w;
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        u[m] = sum_lanes16(u[m]);
+        y[m] = sum_lanes16(y[m]);
+    }
+    kr = sum_lanes16(kr);
+    br = sum_lanes16(br);
+    if (EPI) bon = sum_lanes16(bon);
+
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        y[m] = y[m] + v[m] * kr - u[m] * br;
+        f32x4 s = S[m];
+        s.x = s.x * w.x - u[m] * bb.x + v[m] * k.x;
+        s.y = s.y * w.y - u[m] * bb.y + v[m] * k.y;
+        s.z = s.z * w.z - u[m] * bb.z + v[m] * k.z;
+        s.w = s.w * w.w - u[m] * bb.w + v[m] * k.w;
+        st_state<NT>(st + m * kN, s);
+    }
+
+    // lane c keeps row 16g + c
+    float yo = y[0], vo1 = v[0];
+#pragma unroll
+    for (int m = 1; m < 16; ++m) {
+        yo = (c == m) ? y[m] : yo;
+        vo1 = (c == m) ? v[m] : vo1;
+    }
+    if (EPI) {
+        float s1 = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s1 += y[m];
+        const float mu = sum_rows4(s1) * (1.f / kN);
+        float s2 = 0.f;
+#pragma unroll
+        for (int m = 0; m < 16; ++m) s2 += (y[m] - mu) * (y[m] - mu);
+        const float var = sum_rows4(s2) * (1.f / kN);
+        const float rs = 1.f / sqrtf(var + p.epi.eps);
+        const int ch = h * kN + 16 * g + c;
+        const float gw = p.epi.ln_w ? p.epi.ln_w[ch] : 1.f;
+        const float gb = p.epi.ln_b ? p.epi.ln_b[ch] : 0.f;
+        yo = (yo - mu) * rs * gw + gb + bon * vo1;
+    }
+    IO::store1(static_cast<E *>(p.y) + vo + 16 * g + c, yo);
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream) {
+    const long heads = (long)p.B * p.H;
+    const dim3 grid((unsigned)((heads + kHeadsPerBlock - 1) / kHeadsPerBlock)),
+        block(kDecodeThreads);
+    if (p.bf16) {
+        if (p.epilogue)
+            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true>), grid, block, 0, stream, p);
+    } else {
+        if (p.epilogue)
+            hipLaunchKernelGGL((decode_kernel<F32In, true, true>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<F32In, false, true>), grid, block, 0, stream, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace wkv7

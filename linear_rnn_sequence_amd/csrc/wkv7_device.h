@@ -1,0 +1,92 @@
+// Device-side helpers shared by the WKV7 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wkv7 {
+
+// ---------------------------------------------------------------------------
+// bf16 <-> f32.  Widening is exact (a 16-bit shift); narrowing rounds to
+// nearest, ties to even, and keeps NaN a (quiet) NaN.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// Four consecutive elements of a per-token vector, widened to float.
+struct Bf16In {
+    using elem = uint16_t;
+    static __device__ __forceinline__ float4 load4(const uint16_t *p) {
+        const uint2 u = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    }
+    static __device__ __forceinline__ void store4(uint16_t *p, float4 x) {
+        uint2 u;
+        u.x = pack_bf16x2(x.x, x.y);
+        u.y = pack_bf16x2(x.z, x.w);
+        *reinterpret_cast<uint2 *>(p) = u;
+    }
+    static __device__ __forceinline__ void store1(uint16_t *p, float x) {
+        *p = (uint16_t)f32_to_bf16_rne(x);
+    }
+};
+
+struct F32In {
+    using elem = float;
+    static __device__ __forceinline__ float4 load4(const float *p) {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+    static __device__ __forceinline__ void store4(float *p, float4 x) {
+        *reinterpret_cast<float4 *>(p) = x;
+    }
+    static __device__ __forceinline__ void store1(float *p, float x) { *p = x; }
+};
+
+// ---------------------------------------------------------------------------
+// Cross-lane sums with DPP (no LDS traffic).  Lanes are grouped in DPP "rows"
+// of 16; quad_perm swaps within groups of 4, row_half_mirror reverses each
+// group of 8, row_mirror reverses the row of 16.  After the steps every lane
+// of the group holds the group's sum.
+// ---------------------------------------------------------------------------
+constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float sum_lanes8(float x) {
+    x += dpp_mov<kDppQuadXor1>(x);
+    x += dpp_mov<kDppQuadXor2>(x);
+    x += dpp_mov<kDppRowHalfMirror>(x);
+    return x;
+}
+
+__device__ __forceinline__ float sum_lanes16(float x) {
+    x = sum_lanes8(x);
+    x += dpp_mov<kDppRowMirror>(x);
+    return x;
+}
+
+// Sum over the four DPP rows (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float sum_rows4(float x) {
+    x += __shfl_xor(x, 16, 64);
+    x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+}  // namespace wkv7

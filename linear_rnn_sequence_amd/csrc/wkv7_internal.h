@@ -1,0 +1,55 @@
+// Internal interface between the host entry points (wkv7_api.hip) and the
+// kernel launchers of librwkv7_wkv.so.  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rwkv7_wkv.h"
+
+namespace wkv7 {
+
+constexpr int kN = 64;  // head size (the only one supported)
+extern const bool kChunkedAvailable;
+
+struct EpilogueArgs {
+    const float *ln_w;  // [H*N] or nullptr (= 1)
+    const float *ln_b;  // [H*N] or nullptr (= 0)
+    const float *r_k;   // [H*N]
+    float eps;
+};
+
+struct ForwardArgs {
+    const void *r, *w, *k, *v, *kappa, *a;  // [B,T,H,N] in dt
+    const float *s0;                        // [B,H,N,N] or nullptr (zero state)
+    void *y;                                // [B,T,H,N] in dt
+    float *s_out;                           // [B,H,N,N] or nullptr
+    int B, T, H;
+    bool bf16;
+    bool epilogue;
+    EpilogueArgs epi;
+    void *workspace;
+    size_t workspace_bytes;
+};
+
+struct DecodeArgs {
+    const void *r, *w, *k, *v, *kappa, *a;  // [B,H,N] in dt
+    float *state;                           // [B,H,N,N], in place
+    void *y;                                // [B,H,N] in dt
+    int B, H;
+    bool bf16;
+    bool epilogue;
+    EpilogueArgs epi;
+};
+
+// Each launcher enqueues its kernels on `stream` and returns hipSuccess or the
+// launch error.  Arguments were validated by the caller.
+hipError_t launch_scan(const ForwardArgs &p, hipStream_t stream);
+hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream);
+size_t chunked_workspace_bytes(int B, int T, int H);
+hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
+// S_T for T == 0: copy s0 (or zeros) into s_out.
+hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream);
+
+}  // namespace wkv7

@@ -1,0 +1,173 @@
+"""Thin ctypes binding of librwkv7_wkv.so (the C ABI of include/rwkv7_wkv.h).
+
+Argument marshalling only: every step of the recurrence runs in the HIP
+kernels of the library.  torch provides device memory and the stream; the
+functions take CUDA (HIP) tensors and pass their data pointers and
+``torch.cuda.current_stream().cuda_stream`` (unless a stream is given).
+
+There is no CPU fallback: if the library is not built, :func:`lib` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+STATUS = {
+    0: "RWKV7_OK", 1: "RWKV7_ERR_NULL", 2: "RWKV7_ERR_SHAPE", 3: "RWKV7_ERR_DTYPE",
+    4: "RWKV7_ERR_UNSUPPORTED", 5: "RWKV7_ERR_ALIGN", 6: "RWKV7_ERR_ALIAS",
+    7: "RWKV7_ERR_WORKSPACE", 8: "RWKV7_ERR_HIP",
+}
+DT_F32, DT_BF16 = 0, 1
+ALGOS = {"auto": 0, "scan": 1, "chunked": 2}
+N_HEAD = 64
+
+
+class Rwkv7Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({_status_str(code)})")
+
+
+class Epilogue(ctypes.Structure):
+    _fields_ = [("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p),
+                ("r_k", ctypes.c_void_p), ("eps", ctypes.c_float)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the built library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError(
+                f"librwkv7_wkv.so is not built ({_build.LIB}); run "
+                "`python -m linear_rnn_sequence_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(_build.LIB)
+        vp, ci, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.rwkv7_wkv_forward.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue), vp,
+                                                             sz, vp]
+        L.rwkv7_wkv_forward.restype = ci
+        L.rwkv7_wkv_forward_workspace.argtypes = [ci] * 6
+        L.rwkv7_wkv_forward_workspace.restype = sz
+        L.rwkv7_wkv_decode.argtypes = [vp] * 8 + [ci] * 4 + [ctypes.POINTER(Epilogue), vp]
+        L.rwkv7_wkv_decode.restype = ci
+        L.rwkv7_status_str.argtypes = [ci]
+        L.rwkv7_status_str.restype = ctypes.c_char_p
+        L.rwkv7_abi_version.argtypes = []
+        L.rwkv7_abi_version.restype = ci
+        _lib = L
+    return _lib
+
+
+def _status_str(code: int) -> str:
+    try:
+        return lib().rwkv7_status_str(code).decode()
+    except Exception:  # pragma: no cover - only for messages
+        return "?"
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(torch, dt):
+    if dt == torch.bfloat16:
+        return DT_BF16
+    if dt == torch.float32:
+        return DT_F32
+    raise TypeError(f"unsupported dtype {dt}; use torch.bfloat16 or torch.float32")
+
+
+def _stream(torch, stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _epilogue(epilogue):
+    if epilogue is None:
+        return None, ()
+    keep = tuple(x for x in (epilogue.get("ln_w"), epilogue.get("ln_b"), epilogue["r_k"])
+                 if x is not None)
+    e = Epilogue(
+        ln_w=None if epilogue.get("ln_w") is None else epilogue["ln_w"].data_ptr(),
+        ln_b=None if epilogue.get("ln_b") is None else epilogue["ln_b"].data_ptr(),
+        r_k=epilogue["r_k"].data_ptr(),
+        eps=float(epilogue.get("eps", 64e-5)),
+    )
+    return ctypes.byref(e), (e, keep)
+
+
+def _check_same(torch, xs, shape, dtype):
+    for x in xs:
+        if tuple(x.shape) != tuple(shape):
+            raise ValueError(f"shape {tuple(x.shape)} != {tuple(shape)}")
+        if x.dtype != dtype:
+            raise TypeError("all per-token inputs must share one dtype")
+        if not x.is_contiguous():
+            raise ValueError("inputs must be contiguous")
+        if x.device.type != "cuda":
+            raise ValueError("inputs must live on the GPU")
+
+
+def forward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
+    dt = DT_BF16 if dtype in ("bf16", "bfloat16") else DT_F32
+    return int(lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo]))
+
+
+def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None, s_out=None,
+            want_state=True, workspace=None, stream=None):
+    """rwkv7_wkv_forward.  Inputs [B,T,H,N] (bf16 or f32, one dtype), s0 [B,H,N,N] f32.
+
+    Returns (y, s_out).  ``epilogue``: dict of f32 device tensors ln_w, ln_b ([H*N] or
+    None), r_k ([H,N] or [H*N]) and float eps.  ``s_out`` may be ``s0`` (in place).
+    """
+    import torch
+
+    B, T, H, N = r.shape
+    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    if y is None:
+        y = torch.empty_like(r)
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    need = lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo])
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=r.device)
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_forward(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(s0), _ptr(y),
+        _ptr(s_out), B, T, H, N, dt, ALGOS[algo], epi_ptr, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_forward")
+    return y, s_out
+
+
+def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):
+    """rwkv7_wkv_decode.  Inputs [B,H,N]; ``state`` [B,H,N,N] f32 updated in place.
+    Returns y [B,H,N]."""
+    import torch
+
+    B, H, N = r.shape
+    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    if y is None:
+        y = torch.empty_like(r)
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_decode(_ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a),
+                                  _ptr(state), _ptr(y), B, H, N, dt, epi_ptr,
+                                  _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_decode")
+    return y
+
+
+def abi_version() -> int:
+    return int(lib().rwkv7_abi_version())

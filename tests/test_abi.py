@@ -1,0 +1,101 @@
+"""Host-side checks of the C ABI that need no GPU: the built library loads,
+exports every function include/rwkv7_wkv.h declares, and rejects bad
+arguments before anything is enqueued (these calls launch nothing)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_rnn_sequence_amd import build as hbuild
+from linear_rnn_sequence_amd import wkv
+
+HEADER = os.path.join(hbuild.INCLUDE, "rwkv7_wkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hbuild.LIB),
+                                reason="librwkv7_wkv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rwkv7_\w+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert {"rwkv7_wkv_forward", "rwkv7_wkv_decode", "rwkv7_wkv_forward_workspace",
+            "rwkv7_status_str", "rwkv7_abi_version"} <= set(names)
+    L = ctypes.CDLL(hbuild.LIB)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert wkv.abi_version() == 1
+    L = wkv.lib()
+    for code in range(9):
+        assert L.rwkv7_status_str(code)
+    assert L.rwkv7_status_str(0) == b"ok"
+
+
+# fake, suitably aligned device addresses: validation must reject before use
+A = 1 << 40
+STRIDE = 1 << 32
+
+
+def fake(i, off=0):
+    return ctypes.c_void_p(A + i * STRIDE + off)
+
+
+def fwd(B=2, T=8, H=3, N=64, dt=1, algo=1, s0=fake(6), y=fake(7), s_out=fake(8), ins=None,
+        epi=None, ws=None, ws_bytes=0):
+    ins = ins or [fake(i) for i in range(6)]
+    return wkv.lib().rwkv7_wkv_forward(*ins, s0, y, s_out, B, T, H, N, dt, algo, epi, ws,
+                                       ws_bytes, None)
+
+
+def test_forward_validation_codes():
+    assert fwd(N=32) == 4                      # only head size 64
+    assert fwd(B=0) == 2 and fwd(H=0) == 2 and fwd(T=-1) == 2
+    assert fwd(dt=7) == 3 and fwd(algo=9) == 3
+    assert fwd(dt=0, algo=2) == 4              # chunked is bf16 only
+    ins = [fake(i) for i in range(6)]
+    ins[3] = None
+    assert fwd(ins=ins) == 1                   # NULL input
+    assert fwd(y=None) == 1
+    ins = [fake(i) for i in range(6)]
+    ins[2] = fake(2, 8)
+    assert fwd(ins=ins) == 5                   # misaligned input
+    assert fwd(s_out=fake(8, 4)) == 5
+    assert fwd(y=fake(0, 64)) == 6             # y overlaps r
+    assert fwd(s_out=fake(6, 16)) == 6         # s_out overlaps s0 without being equal
+    assert fwd(s_out=fake(3)) == 6             # s_out overlaps v
+    e = wkv.Epilogue(ln_w=None, ln_b=None, r_k=None, eps=64e-5)
+    assert fwd(epi=ctypes.byref(e)) == 1       # epilogue needs r_k
+    e = wkv.Epilogue(ln_w=A + 9 * STRIDE + 4, ln_b=None, r_k=A + 10 * STRIDE, eps=64e-5)
+    assert fwd(epi=ctypes.byref(e)) == 5
+    # T == 0 needs no per-token pointers; overflowing sizes are rejected
+    assert fwd(B=1 << 30, H=1 << 30) == 2
+
+
+def test_decode_validation_codes():
+    L = wkv.lib()
+
+    def dec(B=2, H=3, N=64, dt=1, state=fake(6), y=fake(7), ins=None, epi=None):
+        ins = ins or [fake(i) for i in range(6)]
+        return L.rwkv7_wkv_decode(*ins, state, y, B, H, N, dt, epi, None)
+
+    assert dec(N=128) == 4
+    assert dec(B=0) == 2
+    assert dec(dt=5) == 3
+    assert dec(state=None) == 1 and dec(y=None) == 1
+    assert dec(state=fake(6, 8)) == 5
+    assert dec(y=fake(6, 64)) == 6             # y inside the state
+    assert dec(state=fake(1)) == 6             # state overlaps w
+
+
+def test_workspace_query_is_pure():
+    L = wkv.lib()
+    assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 64, 0, 1) == 0   # scan needs none
+    assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 32, 1, 2) == 0   # unsupported -> 0
