@@ -1,0 +1,338 @@
+"""Benchmark of the WKV7 hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  * prefill: the 2.9B-model shape, B=8, T=4096, H=40, N=64, bf16 inputs, fp32
+    state, with the fused per-head GroupNorm + bonus epilogue (one layer);
+  * decode: 32 layers x B=256 x H=40 resident fp32 states (5.4 GB), 64
+    sequential single-token steps, each step calling every layer in order,
+    with fresh bf16 inputs for every (token, layer).
+Throughput is token*heads per second over both parts (decode counts every
+layer's heads).  Inputs are resident in HBM before the timed region.
+
+Prints ONE JSON line.  Extra options (--only, --copy-probe, --steps) exist for
+profiling runs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+NAMES = ("r", "w", "k", "v", "kappa", "a")
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+N = 64
+PREFILL = dict(B=8, T=4096, H=40)
+DECODE = dict(layers=32, B=256, H=40, steps=64)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--decode-steps", type=int, default=DECODE["steps"],
+                    help="tokens per decode run (default 64)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=32,
+                    help="decode layers (all sequences and heads) the oracle replays")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 4 GiB device copy (counter calibration)")
+    ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
+    return ap.parse_args()
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(profile_name, src_hash):
+    """Per-launch HBM bytes from a committed counter summary, if it was taken on
+    the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on exactly one GPU; the WKV7 path is not sharded "
+              "across GPUs (see the sharding notes in the design document). Use --gpus 1.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import linear_rnn_sequence_amd as wkv
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wkv.lib()
+
+    if args.copy_probe:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
+                          "launches": 3}))
+        return
+
+    do_prefill = args.only in ("all", "prefill")
+    do_decode = args.only in ("all", "decode")
+    stream = torch.cuda.current_stream()
+
+    # ------------------------------------------------------------------ prefill
+    if do_prefill:
+        t0 = time.time()
+        px = synth.config_inputs(2)
+        pd = {}
+        for n in NAMES:
+            pd[n] = torch.from_numpy(px[n].view(np.int16)).to(dev).view(torch.bfloat16)
+        e = px["epi"]
+        p_epi = {"ln_w": torch.from_numpy(e["ln_w"]).to(dev),
+                 "ln_b": torch.from_numpy(e["ln_b"]).to(dev),
+                 "r_k": torch.from_numpy(e["r_k"]).to(dev), "eps": e["eps"]}
+        B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
+        p_y = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=dev)
+        p_s = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+        ws_bytes = wkv.forward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
+        p_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        p_gen_s = time.time() - t0
+
+        def prefill():
+            wkv.forward(*(pd[n] for n in NAMES), s0=None, algo=args.prefill_algo,
+                        epilogue=p_epi, y=p_y, s_out=p_s, workspace=p_ws)
+
+    # ------------------------------------------------------------------- decode
+    if do_decode:
+        t0 = time.time()
+        L, DB, DH, DS = DECODE["layers"], DECODE["B"], DECODE["H"], args.decode_steps
+        pool = synth.decode_states_device(torch, dev, layers=L, B=DB, H=DH, N=N, seed=3)
+        # host copies of the initial states of the layers the oracle replays (parity and
+        # CPU baseline), taken before any step
+        samp_l = list(range(min(args.cpu_layers, L)))
+        s_init = pool[samp_l].cpu().numpy() if not args.no_cpu_baseline else None
+        d_in = {n: [] for n in NAMES}
+        for t in range(DS):
+            one = synth.decode_step_inputs_device(torch, dev, B=DB, H=DH, N=N, seed=1000 + t,
+                                                  count=L)
+            for n in NAMES:
+                d_in[n].append(one[n])
+        d_in = {n: torch.stack(v) for n, v in d_in.items()}  # [DS, L, B, H, N]
+        d_y = torch.empty((DS, L, DB, DH, N), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        d_gen_s = time.time() - t0
+        n_launch = DS * L
+        # argument marshalling done once: one prepared launch per (token, layer)
+        calls = [wkv.prepare_decode(*(d_in[n][t, l] for n in NAMES), pool[l], y=d_y[t, l])
+                 for t in range(DS) for l in range(L)]
+        ev_steps = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                     for _ in range(n_launch)] for _ in range(args.steps)]
+
+        def decode(events=None):
+            if events is None:
+                for c in calls:
+                    c()
+                return
+            for c, (a, b) in zip(calls, events):
+                a.record(stream)
+                c()
+                b.record(stream)
+
+    # -------------------------------------------------------- warmup + parity
+    for wi in range(args.warmup):
+        if do_prefill:
+            prefill()
+        if do_decode:
+            decode()
+        if wi == 0:
+            torch.cuda.synchronize()
+            if do_decode and not args.no_cpu_baseline:
+                d_y_first = d_y[:, samp_l].cpu()
+            if do_prefill:
+                p_y_first = p_y.float().cpu().numpy()
+                p_s_first = p_s.cpu().numpy()
+    torch.cuda.synchronize()
+
+    # ------------------------------------------------------------- timed region
+    launch_ms = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        if do_prefill:
+            prefill()
+        if do_decode:
+            # per-launch durations of this step are read after the final sync
+            decode(ev_steps[len(launch_ms)])
+            launch_ms.append(ev_steps[len(launch_ms)])
+    end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / max(args.steps, 1)
+
+    # prefill kernel time alone (events around each prefill call, outside the timed loop)
+    prefill_ms = None
+    if do_prefill:
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(3)]
+        for a, b in pe:
+            a.record(stream)
+            prefill()
+            b.record(stream)
+        torch.cuda.synchronize()
+        prefill_ms = float(np.median([a.elapsed_time(b) for a, b in pe]))
+
+    work = 0
+    if do_prefill:
+        work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
+    if do_decode:
+        work += DS * L * DB * DH
+    value = work / (ms_per_step / 1e3)
+
+    out = {
+        "metric": "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)",
+        "value": value,
+        "unit": "token*heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; recipes of the pages' parameterisations)",
+        "config": {
+            "workload": ("2.9B-shape WKV7: prefill B8 T4096 H40 N64 with fused GroupNorm+bonus "
+                         "epilogue, then decode of 64 tokens through 32 layers x B256 x H40 "
+                         "resident fp32 states"),
+            "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=True)
+            if do_prefill else None,
+            "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
+            "state_dtype": "f32",
+        },
+    }
+
+    if do_decode:
+        durs = np.array([a.elapsed_time(b) for evs in launch_ms for a, b in evs])
+        avg_ms = float(durs.mean())
+        bytes_per_launch = DB * DH * (2 * N * N * 4 + 7 * N * 2)
+        achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
+        traffic = read_traffic("decode_kernel_traffic.txt",
+                               source_hash("wkv7_decode.hip", "wkv7_device.h"))
+        out["roofline"] = {
+            "kernel": "wkv7 decode_kernel<bf16> (one layer, B256 x H40)",
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+            "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_ms * 1e3,
+            "launches_timed": int(durs.size),
+        }
+        out["decode_ms_per_step"] = float(durs.sum() / max(args.steps, 1))
+    if do_prefill:
+        B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
+        p_bytes = B * T * H * 7 * N * 2 + B * H * N * N * 4 + 2 * H * N * 4 + H * N * 4
+        ach = p_bytes / (prefill_ms / 1e3) / 1e9
+        out["prefill"] = {
+            "ms": prefill_ms, "token_heads_per_s": B * T * H / (prefill_ms / 1e3),
+            "algo": args.prefill_algo,
+            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": p_bytes},
+        }
+
+    # ------------------------- parity against the oracle, timed as the CPU baseline
+    # The oracle runs on the full prefill batch (every head, every token) and on the
+    # sampled decode chains (layers 0 and 31 x sequences 0, 1, 255 x 40 heads x all
+    # tokens, replayed from their initial states).  Its wall time over that sample is the
+    # CPU baseline; the GPU outputs of the first warmup step are compared with it.
+    import oracle
+
+    threads = len(os.sched_getaffinity(0))
+    par, cpu_work, cpu_s = {}, 0, 0.0
+    if do_prefill and not args.no_cpu_baseline:
+        sub = [px.as_f64(n) for n in NAMES]
+        t0 = time.perf_counter()
+        y_ref, s_ref = oracle.forward(*sub, s0=None, epilogue=px["epi"], threads=threads)
+        cpu_s += time.perf_counter() - t0
+        cpu_work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
+        del sub
+        par["prefill_y_rel_err"] = float(np.abs(p_y_first - y_ref).max() / np.abs(y_ref).max())
+        par["prefill_state_rel_err"] = float(np.abs(p_s_first - s_ref).max()
+                                             / np.abs(s_ref).max())
+        par["prefill_checked"] = "all outputs"
+        del y_ref, s_ref
+    if do_decode and not args.no_cpu_baseline:
+        errs = []
+        for li, l in enumerate(samp_l):
+            # inputs of layer l for every token: [DS, B, H, N] -> [B, DS, H, N]
+            seq = [np.ascontiguousarray(np.moveaxis(d_in[n][:, l].cpu().double().numpy(), 0, 1))
+                   for n in NAMES]
+            t0 = time.perf_counter()
+            y_ref, _ = oracle.forward(*seq, s0=s_init[li], threads=threads)
+            cpu_s += time.perf_counter() - t0
+            cpu_work += seq[0].shape[0] * seq[0].shape[1] * seq[0].shape[2]
+            del seq
+            y_got = np.moveaxis(d_y_first[:, li].double().numpy(), 0, 1)
+            errs.append(np.abs(y_got - y_ref).max() / np.abs(y_ref).max())
+            del y_ref, y_got
+        par["decode_y_rel_err"] = float(max(errs))
+        par["decode_checked"] = (f"every output of layers 0..{len(samp_l) - 1} (all 256 "
+                                 f"sequences x 40 heads x {DS} tokens)")
+    if par:
+        par["bound"] = 2e-2
+        out["parity_sampled"] = par
+    if cpu_work:
+        out["cpu_baseline"] = {
+            "value": cpu_work / cpu_s, "unit": "token*heads/s", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"fp64 C oracle ({cpu_model()}, {threads} threads) over {cpu_work} "
+                       f"token*heads in {cpu_s:.2f} s: the whole prefill batch (B8 T4096 H40 "
+                       f"with epilogue) and the full decode runs of {len(samp_l)} layers"),
+        }
+
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -169,5 +169,31 @@ def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):
     return y
 
 
+def prepare_decode(r, w, k, v, kappa, a, state, *, y, epilogue=None, stream=None):
+    """Marshal the arguments of one rwkv7_wkv_decode call once and return a
+    zero-argument callable that enqueues it (for launch loops where Python-side
+    argument handling would otherwise dominate).  The tensors must stay alive and
+    unchanged in address while the callable is used."""
+    import torch
+
+    B, H, N = r.shape
+    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
+    if tuple(y.shape) != (B, H, N) or y.dtype != r.dtype:
+        raise ValueError("y must match the inputs")
+    dt = _dtype_code(torch, r.dtype)
+    epi_ptr, keep = _epilogue(epilogue)
+    fn = lib().rwkv7_wkv_decode
+    args = (_ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(state), _ptr(y),
+            B, H, N, dt, epi_ptr, _stream(torch, stream))
+
+    def launch():
+        code = fn(*args)
+        if code != 0:
+            raise Rwkv7Error(code, "rwkv7_wkv_decode")
+
+    launch.keep = (keep, r, w, k, v, kappa, a, state, y)
+    return launch
+
+
 def abi_version() -> int:
     return int(lib().rwkv7_abi_version())
