@@ -327,8 +327,11 @@ def main():
             "value": cpu_work / cpu_s, "unit": "token*heads/s", "cores": threads,
             "kind": "oracle",
             "sample": (f"fp64 C oracle ({cpu_model()}, {threads} threads) over {cpu_work} "
-                       f"token*heads in {cpu_s:.2f} s: the whole prefill batch (B8 T4096 H40 "
-                       f"with epilogue) and the full decode runs of {len(samp_l)} layers"),
+                       f"token*heads in {cpu_s:.2f} s: "
+                       + ("the whole prefill batch (B8 T4096 H40 with epilogue)"
+                          if do_prefill else "")
+                       + (" and " if do_prefill and do_decode else "")
+                       + (f"the full decode runs of {len(samp_l)} layers" if do_decode else "")),
         }
 
     print(json.dumps(out))

@@ -25,6 +25,9 @@ HIPCC_FLAGS = [
     "-shared",
     # keep the device compiler from forming packed fp32 (v_pk_*_f32) instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA results in arch VGPRs (the chunked kernel feeds them straight back
+    # into VALU conversions; AGPR results would add a copy per value)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

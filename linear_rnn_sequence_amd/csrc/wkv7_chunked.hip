@@ -1,12 +1,431 @@
-// WKV7 chunked-parallel prefill (ALGO_CHUNKED) -- not built yet.
+// WKV7 chunked-parallel prefill (ALGO_CHUNKED) on bf16 MFMA with a float32
+// state carried between chunks.
+//
+// The pages state that the transition is diagonal plus rank one and that this
+// keeps the recurrence parallelisable in chunks (RWKV-7 "Goose" summary, §4
+// Method, "efficient computation"; §8 Speed and Memory, chunked pre-fill), and
+// that a chunked bf16 kernel exists (author response on numerical precision),
+// but they give no algorithm.  The form used here follows from the update
+//   S_t = S_{t-1} diag(w_t) - u_t b_t^T + v_t k_t^T,  u_t = S_{t-1} kappa_t,
+//   b_t = a_t * kappa_t,  y_t = S_t r_t
+// (author response, numpy time_mixing listing) by unrolling it over a chunk of
+// C = 16 tokens with entry state S0.  With G_t = prod_{s<=t} w_s (G_{-1} = 1):
+//   Kp_t = kappa_t * G_{t-1}   Rp_t = r_t * G_t   Km_s = k_s / G_s   Bm_s = b_s / G_s
+//   M_kk[t,s] = Kp_t.Km_s (s<t)   M_bk[t,s] = Kp_t.Bm_s (s<t)
+//   M_kr[t,s] = Rp_t.Km_s (s<=t)  M_br[t,s] = Rp_t.Bm_s (s<=t)
+//   U   = (I + M_bk)^-1 (Kp S0^T + M_kk V)        (rows: the u_t of the chunk)
+//   Y   = Rp S0^T + M_kr V - M_br U
+//   S_C^T = diag(G_C) (S0^T + Km^T V - Bm^T U)
+// (the last line is diag(G_C) S0^T plus the writes and removals decayed by
+// G_C / G_s; summing before the scaling keeps every term's relative error at
+// fp32 level because the scaled result is a sum of terms of ordinary size).
+// The kernel carries U' = -U (it stores -(I + M_bk)^-1) so no other operand
+// needs a sign flip.
+// Every product is a 16 x 16 x 16 MFMA (v_mfma_f32_16x16x16_bf16) with bf16
+// operands and fp32 accumulation; the state stays fp32 in the accumulators.
+// The unit lower-triangular inverse uses (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8)
+// for the nilpotent N = M_bk (N^16 = 0), also on MFMA.  The decay ratios stay
+// within w_min^-16 (1.6e4 for the pages' w > 0.545).  Requires 0 < w <= 1.
+//
+// Work split: one workgroup (4 waves) per (batch, head), walking the chunks in
+// order.  Wave w prepares key block j in [16w, 16w+16) of every chunk operand
+// (prefix products of w over the chunk by DPP row shifts), then owns value
+// block i in [16w, 16w+16) of the state: S^T is held as four 16x16 fp32
+// accumulator tiles per wave, in exactly the layout the next chunk's MFMAs
+// consume, so the state never leaves registers.  Operands of chunk c+1 are
+// prepared and their C x C matrices and inverse formed while the MFMA chain
+// of chunk c runs; LDS holds two chunks of operands.
+//
+// MFMA 16x16x16 bf16 lane layouts (lane l, g = l / 16, e = 0..3):
+//   A[m][k]: lane holds A[l%16][4g+e];  B[k][n]: lane holds B[4g+e][l%16];
+//   D[m][n]: lane holds D[4g+e][l%16].
+// So a D tile is directly a B operand, and the A form of X is the B form of X^T.
+#include "wkv7_device.h"
 #include "wkv7_internal.h"
 
 namespace wkv7 {
 
-const bool kChunkedAvailable = false;
+const bool kChunkedAvailable = true;
+
+namespace {
+
+constexpr int kC = 16;                  // tokens per chunk
+constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per lane
+constexpr int kThreads = 256;           // 4 waves
+constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
+constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
+
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x4 mfma(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32;
+// written as a vector conversion so the compiler sees it and inserts the wait
+// states an MFMA result needs before a VALU reads it)
+__device__ __forceinline__ unsigned cvt_pk(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x4 to_bf16(f32x4 x) {
+    u32x2 v = {cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// row shift by N inside each 16-lane DPP row; lanes without a source get 1.0
+template <int N>
+__device__ __forceinline__ float shr_fill1(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x),
+                                                      0x110 + N, 0xF, 0xF, false));
+}
+
+struct __align__(16) ChunkOps {
+    short kp[4][kTile];    // Kp  [jb][t][j]   (A form rows t; also B form of Kp^T)
+    short rp[4][kTile];    // Rp  [jb][t][j]
+    short km[4][kTile];    // Km  [jb][s][j]
+    short bm[4][kTile];    // Bm  [jb][s][j]
+    short kmt[4][kTile];   // Km^T  [jb][j][s]
+    short bmt[4][kTile];   // Bm^T  [jb][j][s]
+    short mkk[kTile];      // M_kk  [t][s]
+    short mkr[kTile];      // M_kr  [t][s]
+    short mbr[kTile];      // M_br  [t][s]
+    short xinv[kTile];     // -(I + M_bk)^-1 [t][s]
+    short vt[4][kTile];    // V^T [value block][i][t]  (B form of V)
+    float gc[64];          // G_C per key j
+    float bon[4][16];      // bonus partial sums per (key block, token)
+    float dkr[4][16];      // r_t.k_t partial sums per (key block, token), fp32
+    float dbr[4][16];      // r_t.(a_t*kappa_t) partial sums, fp32
+};
+
+struct __align__(16) ChunkSmem {
+    ChunkOps ops[2];
+    float2 stats[16][4];   // per token, per value block: (mean, M2) of 16 readouts
+};
+
+__device__ __forceinline__ bf16x4 ld_a(const short *tile, int lane) {
+    return *reinterpret_cast<const bf16x4 *>(tile + (lane & 15) * kRow + 4 * (lane >> 4));
+}
+__device__ __forceinline__ void st_a(short *tile, int lane, bf16x4 x) {
+    *reinterpret_cast<bf16x4 *>(tile + (lane & 15) * kRow + 4 * (lane >> 4)) = x;
+}
+
+// Raw inputs of one chunk held by one lane: token t = lane % 16 of the chunk,
+// channels 16w + 4g .. +3 of each of the six vectors (keys for r, w, k, kappa,
+// a; values for v).
+struct Raw {
+    uint2 r, w, k, kap, a, v;
+};
+
+template <bool EPI>
+struct Chunked {
+    const ForwardArgs &p;
+    ChunkSmem &sm;
+    const int lane, wv, g, lo;  // lo = lane % 16
+    const int b, h;
+    const long HN, tok0;        // elements between tokens; offset of (b, t=0, h, 0)
+    const long lane_off;        // offset of this lane's 4 channels at token lo of chunk 0
+
+    __device__ Chunked(const ForwardArgs &p_, ChunkSmem &sm_, int b_, int h_)
+        : p(p_), sm(sm_), lane(threadIdx.x & 63), wv(threadIdx.x >> 6), g((threadIdx.x & 63) >> 4),
+          lo(threadIdx.x & 15), b(b_), h(h_), HN((long)p_.H * kN),
+          tok0((long)b_ * p_.T * ((long)p_.H * kN) + (long)h_ * kN),
+          lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * (threadIdx.x >> 6) +
+                   4 * ((threadIdx.x & 63) >> 4)) {}
+
+    __device__ void load(int c, Raw &x) const {
+        const long off = lane_off + (long)c * kC * HN;
+        if (c * kC + lo < p.T) {  // token exists
+            x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
+            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
+            x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
+            x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
+            x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
+            x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
+        } else {  // padding token past T: no write, no removal, no decay
+            x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
+            x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
+        }
+    }
+
+    // Chunk operands for key block jb = wv, written to LDS buffer `o`.
+    __device__ void prep(const Raw &x, ChunkOps &o, const float (&rk)[4]) const {
+        const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
+        const float w[4] = {bf16_lo(x.w.x), bf16_hi(x.w.x), bf16_lo(x.w.y), bf16_hi(x.w.y)};
+        const float k[4] = {bf16_lo(x.k.x), bf16_hi(x.k.x), bf16_lo(x.k.y), bf16_hi(x.k.y)};
+        const float kp[4] = {bf16_lo(x.kap.x), bf16_hi(x.kap.x), bf16_lo(x.kap.y),
+                             bf16_hi(x.kap.y)};
+        const float a[4] = {bf16_lo(x.a.x), bf16_hi(x.a.x), bf16_lo(x.a.y), bf16_hi(x.a.y)};
+        f32x4 G, Gx, GC, Kp, Rp, Km, Bm;
+        float bon = 0.f, dkr = 0.f, dbr = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            // inclusive prefix product of w over the chunk's tokens (lanes of the DPP row)
+            float q = w[e];
+            q *= shr_fill1<1>(q);
+            q *= shr_fill1<2>(q);
+            q *= shr_fill1<4>(q);
+            q *= shr_fill1<8>(q);
+            G[e] = q;
+            Gx[e] = shr_fill1<1>(q);
+            GC[e] = __shfl(q, (lane & 48) | 15, 64);
+            const float iG = __builtin_amdgcn_rcpf(q);  // 1 ulp; operands are rounded to bf16
+            const float be = a[e] * kp[e];
+            Kp[e] = kp[e] * Gx[e];
+            Rp[e] = r[e] * q;
+            Km[e] = k[e] * iG;
+            Bm[e] = be * iG;
+            if (EPI) bon += r[e] * k[e] * rk[e];
+            dkr += r[e] * k[e];
+            dbr += r[e] * be;
+        }
+        const int jb = wv;
+        st_a(o.kp[jb], lane, to_bf16(Kp));
+        st_a(o.rp[jb], lane, to_bf16(Rp));
+        const bf16x4 kmb = to_bf16(Km), bmb = to_bf16(Bm);
+        st_a(o.km[jb], lane, kmb);
+        st_a(o.bm[jb], lane, bmb);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {  // transposed: row = key 4g+e, column = token lo
+            o.kmt[jb][(4 * g + e) * kRow + lo] = kmb[e];
+            o.bmt[jb][(4 * g + e) * kRow + lo] = bmb[e];
+        }
+        const unsigned short vv[4] = {(unsigned short)(x.v.x & 0xffffu),
+                                      (unsigned short)(x.v.x >> 16),
+                                      (unsigned short)(x.v.y & 0xffffu),
+                                      (unsigned short)(x.v.y >> 16)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o.vt[jb][(4 * g + e) * kRow + lo] = (short)vv[e];
+        if (lo == 0) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
+            make_float4(GC[0], GC[1], GC[2], GC[3]);
+        // fp32 diagonals of M_kr and M_br: at s = t the decay ratio is exactly 1, so
+        // r_t.k_t and r_t.(a_t*kappa_t) need no bf16 factors; the two-factor bf16
+        // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
+        // early readouts whose dot product nearly cancels
+        dkr = sum_rows4(dkr);
+        dbr = sum_rows4(dbr);
+        if (g == 0) {
+            o.dkr[jb][lo] = dkr;
+            o.dbr[jb][lo] = dbr;
+        }
+        if (EPI) {
+            bon = sum_rows4(bon);
+            if (g == 0) o.bon[jb][lo] = bon;
+        }
+    }
+
+    // C x C matrices of a chunk (one per wave) and the triangular inverse.
+    __device__ void matrices(ChunkOps &o) const {
+        const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
+        if (wv == 1) {
+            // N = M_bk in B form (D of Kp.Bm^T) and in A form (D of Bm.Kp^T)
+            f32x4 nb = zero4(), na = zero4();
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const bf16x4 kpa = ld_a(o.kp[jb], lane), bma = ld_a(o.bm[jb], lane);
+                nb = mfma(kpa, bma, nb);
+                na = mfma(bma, kpa, na);
+            }
+            f32x4 imn, n4i, n2i;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nb[e] = (lo < row + e) ? nb[e] : 0.f;   // B form: [t = row+e][s = lo], s < t
+                na[e] = (row + e < lo) ? na[e] : 0.f;   // A form: [t = lo][s = row+e], s < t
+                imn[e] = (row + e == lo ? 1.f : 0.f) - nb[e];
+            }
+            const bf16x4 Nb = to_bf16(nb), Na = to_bf16(na);
+            const f32x4 n2 = mfma(Na, Nb, zero4());    // N^2      (B form)
+            const f32x4 n2t = mfma(Nb, Na, zero4());   // (N^2)^T  (B form) = N^2 (A form)
+            const bf16x4 N2b = to_bf16(n2), N2a = to_bf16(n2t);
+            const f32x4 n4 = mfma(N2a, N2b, zero4());
+            const f32x4 n4t = mfma(N2b, N2a, zero4());
+            const bf16x4 N4b = to_bf16(n4), N4a = to_bf16(n4t);
+            f32x4 z = mfma(N4b, N4a, zero4());         // (N^8)^T (B form)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float id = (row + e == lo) ? 1.f : 0.f;
+                z[e] += id;
+                n4i[e] = n4[e] + id;
+                n2i[e] = n2[e] + id;
+            }
+            // X^T = (I - N^T)(I + (N^2)^T)(I + (N^4)^T)(I + (N^8)^T); the B form of
+            // I + N^p is the A form of (I + N^p)^T
+            z = mfma(to_bf16(n4i), to_bf16(z), zero4());
+            z = mfma(to_bf16(n2i), to_bf16(z), zero4());
+            z = mfma(to_bf16(imn), to_bf16(z), zero4());
+            st_a(o.xinv, lane, to_bf16(-z));           // D of X^T = A form of X; stored negated
+        } else {
+            // wave 0: M_kk^T = Km.Kp^T, strict; wave 2: M_kr^T = Km.Rp^T; wave 3: M_br^T
+            const short(*lhs)[kTile] = (wv == 3) ? o.bm : o.km;
+            const short(*rhs)[kTile] = (wv == 0) ? o.kp : o.rp;
+            f32x4 m = zero4();
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) m = mfma(ld_a(lhs[jb], lane), ld_a(rhs[jb], lane), m);
+            // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
+            float diag = 0.f;
+            if (wv != 0) {
+                const float(*dd)[16] = (wv == 2) ? o.dkr : o.dbr;
+                diag = dd[0][lo] + dd[1][lo] + dd[2][lo] + dd[3][lo];
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool keep = (wv == 0) ? (row + e < lo) : (row + e <= lo);
+                const float val = (wv != 0 && row + e == lo) ? diag : m[e];
+                m[e] = keep ? val : 0.f;
+            }
+            short *dst = (wv == 0) ? o.mkk : (wv == 2 ? o.mkr : o.mbr);
+            st_a(dst, lane, to_bf16(m));
+        }
+    }
+};
+
+template <bool EPI>
+__global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
+    __shared__ ChunkSmem sm;
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh - b * p.H;
+    Chunked<EPI> K(p, sm, b, h);
+    const int lane = K.lane, wv = K.wv, g = K.g, lo = K.lo;
+    const int T = p.T;
+    const int nch = (T + kC - 1) / kC;
+
+    // state S^T: tile jb holds rows j = 16jb + 4g + e, column i = 16wv + lo
+    f32x4 Z[4];
+    const long sb = (long)bh * kN * kN + (long)(16 * wv + lo) * kN;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        if (p.s0) {
+            const float4 x = *reinterpret_cast<const float4 *>(p.s0 + sb + 16 * jb + 4 * g);
+            Z[jb] = f32x4{x.x, x.y, x.z, x.w};
+        } else {
+            Z[jb] = zero4();
+        }
+    }
+    float rk[4] = {0.f, 0.f, 0.f, 0.f};
+    float lnw = 1.f, lnb = 0.f;
+    if (EPI) {
+        const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * wv + 4 * g);
+        rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
+        if (p.epi.ln_w) lnw = p.epi.ln_w[h * kN + 16 * wv + lo];
+        if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * wv + lo];
+    }
+
+    // raw inputs of the next kPrefetch chunks stay in flight in a register ring
+    Raw xs[kPrefetch];
+#pragma unroll
+    for (int d = 0; d < kPrefetch; ++d)
+        if (d < nch) K.load(d, xs[d]);
+    K.prep(xs[0], sm.ops[0], rk);
+    if (kPrefetch < nch) K.load(kPrefetch, xs[0]);
+    __syncthreads();
+    K.matrices(sm.ops[0]);
+    __syncthreads();
+
+    uint16_t *yout = static_cast<uint16_t *>(p.y);
+    for (int c0 = 0; c0 < nch; c0 += kPrefetch) {
+#pragma unroll
+        for (int d = 0; d < kPrefetch; ++d) {
+            const int c = c0 + d;
+            if (c >= nch) break;
+            Raw &xn = xs[(d + 1) % kPrefetch];  // holds chunk c + 1
+            ChunkOps &o = sm.ops[c & 1];
+            // ---- the state-dependent chain of chunk c (wave owns value block wv) ----
+            const bf16x4 Vb = ld_a(o.vt[wv], lane);
+            bf16x4 Zb[4];
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
+            f32x4 rhs = mfma(ld_a(o.mkk, lane), Vb, zero4());
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) rhs = mfma(ld_a(o.kp[jb], lane), Zb[jb], rhs);
+            const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
+            const bf16x4 Ub = to_bf16(U);
+            f32x4 Y = mfma(ld_a(o.mkr, lane), Vb, zero4());
+            Y = mfma(ld_a(o.mbr, lane), Ub, Y);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) Y = mfma(ld_a(o.rp[jb], lane), Zb[jb], Y);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                Z[jb] = mfma(ld_a(o.kmt[jb], lane), Vb, Z[jb]);
+                Z[jb] = mfma(ld_a(o.bmt[jb], lane), Ub, Z[jb]);
+                const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
+                Z[jb][0] *= gc.x;
+                Z[jb][1] *= gc.y;
+                Z[jb][2] *= gc.z;
+                Z[jb][3] *= gc.w;
+            }
+            // readouts: lane holds y[t = 4g+e][i = 16wv + lo]
+            if (EPI) {
+                float2 st[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float mu = sum_lanes16(Y[e]) * (1.f / 16.f);
+                    const float dd = Y[e] - mu;
+                    st[e] = make_float2(mu, sum_lanes16(dd * dd));
+                }
+                if (lo == 0) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sm.stats[4 * g + e][wv] = st[e];
+                }
+            }
+
+            // ---- operands of chunk c+1 (other buffer); refill the ring slot ----
+            if (c + 1 < nch) {
+                K.prep(xn, sm.ops[(c + 1) & 1], rk);
+                if (c + 1 + kPrefetch < nch) K.load(c + 1 + kPrefetch, xn);
+            }
+            __syncthreads();
+
+            // ---- finish chunk c's readouts ----
+            const int tbase = c * kC + 4 * g;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                float yv = Y[e];
+                if (EPI) {
+                    const float4 m01 = *reinterpret_cast<const float4 *>(&sm.stats[4 * g + e][0]);
+                    const float4 m23 = *reinterpret_cast<const float4 *>(&sm.stats[4 * g + e][2]);
+                    const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
+                    const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
+                    const float m2 = (m01.y + m01.w + m23.y + m23.w) +
+                                     16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
+                    const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
+                    const int t = 4 * g + e;
+                    const float bz = o.bon[0][t] + o.bon[1][t] + o.bon[2][t] + o.bon[3][t];
+                    yv = (yv - mu) * rs * lnw + lnb + bz * bf16_lo((unsigned)(unsigned short)Vb[e]);
+                }
+                if (tbase + e < T)
+                    yout[K.tok0 + (long)(tbase + e) * K.HN + 16 * wv + lo] =
+                        (uint16_t)f32_to_bf16_rne(yv);
+            }
+            if (c + 1 < nch) K.matrices(sm.ops[(c + 1) & 1]);
+            __syncthreads();
+        }
+    }
+
+    if (p.s_out) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            *reinterpret_cast<float4 *>(p.s_out + sb + 16 * jb + 4 * g) =
+                make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+    }
+}
+
+}  // namespace
 
 size_t chunked_workspace_bytes(int, int, int) { return 0; }
 
-hipError_t launch_chunked(const ForwardArgs &, hipStream_t) { return hipErrorNotSupported; }
+hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
+    const dim3 grid((unsigned)((long)p.B * p.H)), block(kThreads);
+    if (p.epilogue)
+        hipLaunchKernelGGL((chunked_kernel<true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((chunked_kernel<false>), grid, block, 0, stream, p);
+    return hipGetLastError();
+}
 
 }  // namespace wkv7

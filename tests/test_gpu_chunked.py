@@ -1,0 +1,157 @@
+"""GPU parity of the chunked-parallel prefill (bf16 MFMA, fp32 state) against
+the oracle through the C ABI.  Bound (bf16 inputs): max|err| / max|ref| <= 2e-2
+for y and for the final state."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.helpers import NAMES, assert_close, oracle_forward, rel_err, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def wkv():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_rnn_sequence_amd as m
+
+    m.lib()
+    return m
+
+
+def run(wkv, x, algo="chunked", d=None, **kw):
+    d = d or to_device(x, torch)
+    y, s = wkv.forward(*(d[n] for n in NAMES), s0=d["s0"], algo=algo, epilogue=d["epi"], **kw)
+    torch.cuda.synchronize()
+    return y, s
+
+
+def check(wkv, x, what, **kw):
+    y, s = run(wkv, x)
+    y_ref, s_ref = oracle_forward(x, **kw)
+    y, s = to_f64(y), to_f64(s)
+    if kw:
+        bi = kw.get("b_idx")
+        hi = kw.get("h_idx")
+        bi = slice(None) if bi is None else np.asarray(bi)
+        hi = slice(None) if hi is None else np.asarray(hi)
+        y, s = y[bi][:, :, hi], s[bi][:, hi]
+    ey = assert_close(y, y_ref, TOL, f"{what} y")
+    es = assert_close(s, s_ref, TOL, f"{what} S_T")
+    return ey, es
+
+
+def test_auto_picks_chunked_for_bf16(wkv):
+    assert wkv.forward_workspace_bytes(2, 64, 3) >= 0
+    x = synth.draw(1, 40, 2, seed=1, dtype="bf16", s0="normal")
+    d = to_device(x, torch)
+    ya, sa = run(wkv, x, algo="auto", d=d)
+    yc, sc = run(wkv, x, algo="chunked", d=d)
+    assert torch.equal(ya, yc) and torch.equal(sa, sc)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 31, 32, 33, 47, 64, 65, 200, 1000])
+def test_chunked_sweep_T(wkv, T):
+    x = synth.draw(1, T, 1, seed=2000 + T, dtype="bf16", s0="normal")
+    check(wkv, x, f"T={T}")
+
+
+@pytest.mark.parametrize("B,H,T", [(3, 5, 37), (2, 1, 129), (1, 7, 48), (4, 3, 256)])
+@pytest.mark.parametrize("epi", [False, True])
+@pytest.mark.parametrize("s0", ["zero", "normal"])
+@pytest.mark.parametrize("w_recipe", ["wide", "slow"])
+def test_chunked_sweep(wkv, B, H, T, epi, s0, w_recipe):
+    x = synth.draw(B, T, H, seed=B * 100 + H * 10 + T, dtype="bf16", s0=s0, w_recipe=w_recipe,
+                   a_mean=2.0 if w_recipe == "slow" else 0.0, epilogue=epi)
+    check(wkv, x, f"B{B} H{H} T{T} epi={epi} s0={s0} {w_recipe}")
+
+
+def test_chunked_019b_shape(wkv):
+    x = synth.config_inputs(1)
+    ey, es = check(wkv, x, "cfg1")
+    print(f"0.19B shape chunked: y err {ey:.2e}, S err {es:.2e}")
+
+
+def test_chunked_29b_shape_with_epilogue(wkv):
+    x = synth.config_inputs(2)
+    ey, es = check(wkv, x, "cfg2")
+    print(f"2.9B shape chunked+epilogue: y err {ey:.2e}, S err {es:.2e}")
+
+
+def test_chunked_long_context_single_pass_and_segments(wkv):
+    """T = 65536, slow decay, near-full replacement: one pass and 16 segments of
+    4096 with the state passed between them, both against the oracle, and the
+    drift between the two."""
+    x = synth.config_inputs(4)
+    d = to_device(x, torch)
+    ins = [d[n] for n in NAMES]
+    y1, s1 = wkv.forward(*ins, algo="chunked")
+    st = torch.zeros_like(s1)
+    ys = []
+    for seg in range(16):
+        sl = slice(seg * 4096, (seg + 1) * 4096)
+        y, _ = wkv.forward(*(t[:, sl].contiguous() for t in ins), s0=st, s_out=st,
+                           algo="chunked")
+        ys.append(y)
+    torch.cuda.synchronize()
+    yseg = torch.cat(ys, 1)
+    y_ref, s_ref = oracle_forward(x)
+    e1 = assert_close(to_f64(y1), y_ref, TOL, "single pass y")
+    assert_close(to_f64(s1), s_ref, TOL, "single pass S")
+    e2 = assert_close(to_f64(yseg), y_ref, TOL, "segmented y")
+    assert_close(to_f64(st), s_ref, TOL, "segmented S")
+    drift = rel_err(to_f64(yseg), to_f64(y1))
+    print(f"long context: single {e1:.2e}, segmented {e2:.2e}, drift {drift:.2e}")
+    assert drift <= TOL
+
+
+def test_chunked_matches_scan(wkv):
+    x = synth.draw(2, 300, 4, seed=44, dtype="bf16", s0="normal", w_recipe="wide",
+                   epilogue=True)
+    d = to_device(x, torch)
+    yc, sc = run(wkv, x, "chunked", d=d)
+    ys, ss = run(wkv, x, "scan", d=d)
+    assert rel_err(to_f64(yc), to_f64(ys)) <= TOL
+    assert rel_err(to_f64(sc), to_f64(ss)) <= TOL
+
+
+def _transition_inputs(rng, T, B=2, H=3, N=64):
+    """Per chunk, swaps on disjoint column pairs (so M_bk = 0 inside a chunk)
+    with v = 0, w = 1 and small integer states: every intermediate is a small
+    integer and the chunked form is exact."""
+    S0 = rng.integers(-8, 9, (B, H, N, N)).astype(np.float32)
+    kap = np.zeros((B, T, H, N), np.float32)
+    a = np.zeros((B, T, H, N), np.float32)
+    for t in range(T):
+        pair = 2 * (t % 16)
+        i, j = pair, pair + 1
+        kap[:, t, :, i] = 1.0
+        kap[:, t, :, j] = -1.0
+        a[:, t, :, :] = 1.0 if t % 3 else 0.0
+    r = rng.integers(-2, 3, (B, T, H, N)).astype(np.float32)
+    vecs = dict(r=r, w=np.ones_like(r), k=r[..., ::-1].copy(), v=np.zeros_like(r), kappa=kap,
+                a=a)
+    return vecs, S0
+
+
+@pytest.mark.parametrize("T", [1, 2, 16, 40])
+def test_chunked_exact_transitions(wkv, T):
+    rng = np.random.default_rng(T)
+    vecs, S0 = _transition_inputs(rng, T)
+    _, s_ref = oracle.forward(*(vecs[n] for n in NAMES), s0=S0)
+    ins = [torch.from_numpy(np.ascontiguousarray(vecs[n])).to("cuda", torch.bfloat16)
+           for n in NAMES]
+    y, s = wkv.forward(*ins, s0=torch.from_numpy(S0).cuda(), algo="chunked")
+    torch.cuda.synchronize()
+    assert np.array_equal(to_f64(s), s_ref)
+
+
+def test_chunked_rejects_fp32(wkv):
+    x = synth.draw(1, 8, 1, seed=3, dtype="f32")
+    d = to_device(x, torch)
+    with pytest.raises(wkv.Rwkv7Error):
+        wkv.forward(*(d[n] for n in NAMES), algo="chunked")
