@@ -27,14 +27,20 @@
 // for the nilpotent N = M_bk (N^16 = 0), also on MFMA.  The decay ratios stay
 // within w_min^-16 (1.6e4 for the pages' w > 0.545).  Requires 0 < w <= 1.
 //
-// Work split: one workgroup (4 waves) per (batch, head), walking the chunks in
-// order.  Wave w prepares key block j in [16w, 16w+16) of every chunk operand
-// (prefix products of w over the chunk by DPP row shifts), then owns value
-// block i in [16w, 16w+16) of the state: S^T is held as four 16x16 fp32
-// accumulator tiles per wave, in exactly the layout the next chunk's MFMAs
-// consume, so the state never leaves registers.  Operands of chunk c+1 are
-// prepared and their C x C matrices and inverse formed while the MFMA chain
-// of chunk c runs; LDS holds two chunks of operands.
+// Work split: one workgroup of 8 waves per (batch, head), walking the chunks
+// in order as a three-stage pipeline with one barrier per chunk:
+//   waves 4..7 ("prep"): wave 4+b prepares key block j in [16b, 16b+16) of the
+//     operands of chunk c+2 (prefix products of w over the chunk by DPP row
+//     shifts, bf16 tiles into LDS) from raw inputs held 4 chunks deep in a
+//     register ring, and forms one C x C matrix of chunk c+1 (wave 5: the
+//     triangular inverse);
+//   waves 0..3 ("chain"): wave b owns value block i in [16b, 16b+16) of the
+//     state: S^T is held as four 16x16 fp32 accumulator tiles per wave, in
+//     exactly the layout the next chunk's MFMAs consume, so the state never
+//     leaves registers; they run chunk c's MFMA chain and finish chunk c-1's
+//     readouts (GroupNorm statistics need all four value blocks).
+// A SIMD thus holds one MFMA-bound chain wave and one VALU-bound prep wave.
+// LDS holds the operands of three chunks.
 //
 // MFMA 16x16x16 bf16 lane layouts (lane l, g = l / 16, e = 0..3):
 //   A[m][k]: lane holds A[l%16][4g+e];  B[k][n]: lane holds B[4g+e][l%16];
@@ -51,7 +57,7 @@ namespace {
 
 constexpr int kC = 16;                  // tokens per chunk
 constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per lane
-constexpr int kThreads = 256;           // 4 waves
+constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
 
@@ -105,8 +111,8 @@ struct __align__(16) ChunkOps {
 };
 
 struct __align__(16) ChunkSmem {
-    ChunkOps ops[2];
-    float2 stats[16][4];   // per token, per value block: (mean, M2) of 16 readouts
+    ChunkOps ops[3];
+    float2 stats[2][16][4];  // per token, per value block: (mean, M2) of 16 readouts
 };
 
 __device__ __forceinline__ bf16x4 ld_a(const short *tile, int lane) {
@@ -126,17 +132,15 @@ struct Raw {
 template <bool EPI>
 struct Chunked {
     const ForwardArgs &p;
-    ChunkSmem &sm;
-    const int lane, wv, g, lo;  // lo = lane % 16
-    const int b, h;
-    const long HN, tok0;        // elements between tokens; offset of (b, t=0, h, 0)
-    const long lane_off;        // offset of this lane's 4 channels at token lo of chunk 0
+    const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
+    const long HN, tok0;         // elements between tokens; offset of (b, t=0, h, 0)
+    const long lane_off;         // prep lane: its 4 channels at token lo of chunk 0
 
-    __device__ Chunked(const ForwardArgs &p_, ChunkSmem &sm_, int b_, int h_)
-        : p(p_), sm(sm_), lane(threadIdx.x & 63), wv(threadIdx.x >> 6), g((threadIdx.x & 63) >> 4),
-          lo(threadIdx.x & 15), b(b_), h(h_), HN((long)p_.H * kN),
+    __device__ Chunked(const ForwardArgs &p_, int b_, int h_)
+        : p(p_), lane(threadIdx.x & 63), blk((threadIdx.x >> 6) & 3),
+          g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), HN((long)p_.H * kN),
           tok0((long)b_ * p_.T * ((long)p_.H * kN) + (long)h_ * kN),
-          lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * (threadIdx.x >> 6) +
+          lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * ((threadIdx.x >> 6) & 3) +
                    4 * ((threadIdx.x & 63) >> 4)) {}
 
     __device__ void load(int c, Raw &x) const {
@@ -154,7 +158,7 @@ struct Chunked {
         }
     }
 
-    // Chunk operands for key block jb = wv, written to LDS buffer `o`.
+    // Chunk operands for key block jb = blk, written to LDS buffer `o`.
     __device__ void prep(const Raw &x, ChunkOps &o, const float (&rk)[4]) const {
         const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
         const float w[4] = {bf16_lo(x.w.x), bf16_hi(x.w.x), bf16_lo(x.w.y), bf16_hi(x.w.y)};
@@ -185,23 +189,21 @@ struct Chunked {
             dkr += r[e] * k[e];
             dbr += r[e] * be;
         }
-        const int jb = wv;
+        const int jb = blk;
         st_a(o.kp[jb], lane, to_bf16(Kp));
         st_a(o.rp[jb], lane, to_bf16(Rp));
         const bf16x4 kmb = to_bf16(Km), bmb = to_bf16(Bm);
         st_a(o.km[jb], lane, kmb);
         st_a(o.bm[jb], lane, bmb);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // transposed: row = key 4g+e, column = token lo
+        for (int e = 0; e < 4; ++e) {  // transposed: row = channel 4g+e, column = token lo
             o.kmt[jb][(4 * g + e) * kRow + lo] = kmb[e];
             o.bmt[jb][(4 * g + e) * kRow + lo] = bmb[e];
         }
-        const unsigned short vv[4] = {(unsigned short)(x.v.x & 0xffffu),
-                                      (unsigned short)(x.v.x >> 16),
-                                      (unsigned short)(x.v.y & 0xffffu),
-                                      (unsigned short)(x.v.y >> 16)};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o.vt[jb][(4 * g + e) * kRow + lo] = (short)vv[e];
+        o.vt[jb][(4 * g + 0) * kRow + lo] = (short)(x.v.x & 0xffffu);
+        o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(x.v.x >> 16);
+        o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(x.v.y & 0xffffu);
+        o.vt[jb][(4 * g + 3) * kRow + lo] = (short)(x.v.y >> 16);
         if (lo == 0) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
             make_float4(GC[0], GC[1], GC[2], GC[3]);
         // fp32 diagonals of M_kr and M_br: at s = t the decay ratio is exactly 1, so
@@ -220,10 +222,10 @@ struct Chunked {
         }
     }
 
-    // C x C matrices of a chunk (one per wave) and the triangular inverse.
+    // One C x C matrix of a chunk per prep wave; wave 5 forms the triangular inverse.
     __device__ void matrices(ChunkOps &o) const {
         const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
-        if (wv == 1) {
+        if (blk == 1) {
             // N = M_bk in B form (D of Kp.Bm^T) and in A form (D of Bm.Kp^T)
             f32x4 nb = zero4(), na = zero4();
 #pragma unroll
@@ -261,157 +263,178 @@ struct Chunked {
             z = mfma(to_bf16(imn), to_bf16(z), zero4());
             st_a(o.xinv, lane, to_bf16(-z));           // D of X^T = A form of X; stored negated
         } else {
-            // wave 0: M_kk^T = Km.Kp^T, strict; wave 2: M_kr^T = Km.Rp^T; wave 3: M_br^T
-            const short(*lhs)[kTile] = (wv == 3) ? o.bm : o.km;
-            const short(*rhs)[kTile] = (wv == 0) ? o.kp : o.rp;
+            // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
+            const short(*lhs)[kTile] = (blk == 3) ? o.bm : o.km;
+            const short(*rhs)[kTile] = (blk == 0) ? o.kp : o.rp;
             f32x4 m = zero4();
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) m = mfma(ld_a(lhs[jb], lane), ld_a(rhs[jb], lane), m);
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
             float diag = 0.f;
-            if (wv != 0) {
-                const float(*dd)[16] = (wv == 2) ? o.dkr : o.dbr;
+            if (blk != 0) {
+                const float(*dd)[16] = (blk == 2) ? o.dkr : o.dbr;
                 diag = dd[0][lo] + dd[1][lo] + dd[2][lo] + dd[3][lo];
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool keep = (wv == 0) ? (row + e < lo) : (row + e <= lo);
-                const float val = (wv != 0 && row + e == lo) ? diag : m[e];
+                const bool keep = (blk == 0) ? (row + e < lo) : (row + e <= lo);
+                const float val = (blk != 0 && row + e == lo) ? diag : m[e];
                 m[e] = keep ? val : 0.f;
             }
-            short *dst = (wv == 0) ? o.mkk : (wv == 2 ? o.mkr : o.mbr);
+            short *dst = (blk == 0) ? o.mkk : (blk == 2 ? o.mkr : o.mbr);
             st_a(dst, lane, to_bf16(m));
         }
     }
 };
+
+// Per-chain-lane state carried from chunk c's chain to its readout stores one
+// interval later: the 4 readouts y[t = 4g+e][i], the token bonus sums and v.
+struct Pending {
+    f32x4 y;
+    float bon[4];
+    bf16x4 v;
+};
+
+template <bool EPI>
+__device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI> &K,
+                                                const ChunkSmem &sm, const Pending &pd, int c,
+                                                float lnw, float lnb) {
+    const int g = K.g, lo = K.lo;
+    float yv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        yv[e] = pd.y[e];
+        if (EPI) {
+            const float2 *st = sm.stats[c & 1][4 * g + e];
+            const float4 m01 = *reinterpret_cast<const float4 *>(st);
+            const float4 m23 = *reinterpret_cast<const float4 *>(st + 2);
+            const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
+            const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
+            const float m2 = (m01.y + m01.w + m23.y + m23.w) +
+                             16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
+            const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
+            yv[e] = (yv[e] - mu) * rs * lnw + lnb +
+                    pd.bon[e] * bf16_lo((unsigned)(unsigned short)pd.v[e]);
+        }
+    }
+    const unsigned lo2 = cvt_pk(yv[0], yv[1]), hi2 = cvt_pk(yv[2], yv[3]);
+    const unsigned short out[4] = {(unsigned short)(lo2 & 0xffffu), (unsigned short)(lo2 >> 16),
+                                   (unsigned short)(hi2 & 0xffffu), (unsigned short)(hi2 >> 16)};
+    const int t0 = c * kC + 4 * g;
+    uint16_t *y = static_cast<uint16_t *>(p.y) + K.tok0 + (long)t0 * K.HN + 16 * K.blk + lo;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        if (t0 + e < p.T) y[e * K.HN] = out[e];
+}
 
 template <bool EPI>
 __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
     __shared__ ChunkSmem sm;
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H;
-    Chunked<EPI> K(p, sm, b, h);
-    const int lane = K.lane, wv = K.wv, g = K.g, lo = K.lo;
-    const int T = p.T;
-    const int nch = (T + kC - 1) / kC;
+    const Chunked<EPI> K(p, b, h);
+    const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
+    const bool chain_wave = threadIdx.x < 256;  // waves 0..3
+    const int nch = (p.T + kC - 1) / kC;
+    const long sb = (long)bh * kN * kN + (long)(16 * blk + lo) * kN;
 
-    // state S^T: tile jb holds rows j = 16jb + 4g + e, column i = 16wv + lo
-    f32x4 Z[4];
-    const long sb = (long)bh * kN * kN + (long)(16 * wv + lo) * kN;
+    if (chain_wave) {
+        // ---------------- chain waves: state, MFMA chain, readouts ----------------
+        // S^T tile jb holds rows j = 16jb + 4g + e, column i = 16blk + lo
+        f32x4 Z[4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        if (p.s0) {
-            const float4 x = *reinterpret_cast<const float4 *>(p.s0 + sb + 16 * jb + 4 * g);
-            Z[jb] = f32x4{x.x, x.y, x.z, x.w};
-        } else {
-            Z[jb] = zero4();
+        for (int jb = 0; jb < 4; ++jb) {
+            if (p.s0) {
+                const float4 x = *reinterpret_cast<const float4 *>(p.s0 + sb + 16 * jb + 4 * g);
+                Z[jb] = f32x4{x.x, x.y, x.z, x.w};
+            } else {
+                Z[jb] = zero4();
+            }
         }
-    }
-    float rk[4] = {0.f, 0.f, 0.f, 0.f};
-    float lnw = 1.f, lnb = 0.f;
-    if (EPI) {
-        const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * wv + 4 * g);
-        rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
-        if (p.epi.ln_w) lnw = p.epi.ln_w[h * kN + 16 * wv + lo];
-        if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * wv + lo];
-    }
-
-    // raw inputs of the next kPrefetch chunks stay in flight in a register ring
-    Raw xs[kPrefetch];
+        float lnw = 1.f, lnb = 0.f;
+        if (EPI) {
+            if (p.epi.ln_w) lnw = p.epi.ln_w[h * kN + 16 * blk + lo];
+            if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * blk + lo];
+        }
+        Pending pd;
+        __syncthreads();  // interval 0: chunk 0 prepared
+        __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
+        for (int c = 0; c <= nch; ++c) {
+            if (c > 0) finish_readouts<EPI>(p, K, sm, pd, c - 1, lnw, lnb);
+            if (c < nch) {
+                const ChunkOps &o = sm.ops[c % 3];
+                const bf16x4 Vb = ld_a(o.vt[blk], lane);
+                bf16x4 Zb[4];
 #pragma unroll
-    for (int d = 0; d < kPrefetch; ++d)
-        if (d < nch) K.load(d, xs[d]);
-    K.prep(xs[0], sm.ops[0], rk);
-    if (kPrefetch < nch) K.load(kPrefetch, xs[0]);
-    __syncthreads();
-    K.matrices(sm.ops[0]);
-    __syncthreads();
-
-    uint16_t *yout = static_cast<uint16_t *>(p.y);
-    for (int c0 = 0; c0 < nch; c0 += kPrefetch) {
+                for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
+                f32x4 rhs = mfma(ld_a(o.mkk, lane), Vb, zero4());
 #pragma unroll
-        for (int d = 0; d < kPrefetch; ++d) {
-            const int c = c0 + d;
-            if (c >= nch) break;
-            Raw &xn = xs[(d + 1) % kPrefetch];  // holds chunk c + 1
-            ChunkOps &o = sm.ops[c & 1];
-            // ---- the state-dependent chain of chunk c (wave owns value block wv) ----
-            const bf16x4 Vb = ld_a(o.vt[wv], lane);
-            bf16x4 Zb[4];
+                for (int jb = 0; jb < 4; ++jb) rhs = mfma(ld_a(o.kp[jb], lane), Zb[jb], rhs);
+                const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
+                const bf16x4 Ub = to_bf16(U);
+                f32x4 Y = mfma(ld_a(o.mkr, lane), Vb, zero4());
+                Y = mfma(ld_a(o.mbr, lane), Ub, Y);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
-            f32x4 rhs = mfma(ld_a(o.mkk, lane), Vb, zero4());
+                for (int jb = 0; jb < 4; ++jb) Y = mfma(ld_a(o.rp[jb], lane), Zb[jb], Y);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) rhs = mfma(ld_a(o.kp[jb], lane), Zb[jb], rhs);
-            const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
-            const bf16x4 Ub = to_bf16(U);
-            f32x4 Y = mfma(ld_a(o.mkr, lane), Vb, zero4());
-            Y = mfma(ld_a(o.mbr, lane), Ub, Y);
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) Y = mfma(ld_a(o.rp[jb], lane), Zb[jb], Y);
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                Z[jb] = mfma(ld_a(o.kmt[jb], lane), Vb, Z[jb]);
-                Z[jb] = mfma(ld_a(o.bmt[jb], lane), Ub, Z[jb]);
-                const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
-                Z[jb][0] *= gc.x;
-                Z[jb][1] *= gc.y;
-                Z[jb][2] *= gc.z;
-                Z[jb][3] *= gc.w;
-            }
-            // readouts: lane holds y[t = 4g+e][i = 16wv + lo]
-            if (EPI) {
-                float2 st[4];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float mu = sum_lanes16(Y[e]) * (1.f / 16.f);
-                    const float dd = Y[e] - mu;
-                    st[e] = make_float2(mu, sum_lanes16(dd * dd));
+                for (int jb = 0; jb < 4; ++jb) {
+                    Z[jb] = mfma(ld_a(o.kmt[jb], lane), Vb, Z[jb]);
+                    Z[jb] = mfma(ld_a(o.bmt[jb], lane), Ub, Z[jb]);
+                    const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
+                    Z[jb][0] *= gc.x;
+                    Z[jb][1] *= gc.y;
+                    Z[jb][2] *= gc.z;
+                    Z[jb][3] *= gc.w;
                 }
-                if (lo == 0) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) sm.stats[4 * g + e][wv] = st[e];
-                }
-            }
-
-            // ---- operands of chunk c+1 (other buffer); refill the ring slot ----
-            if (c + 1 < nch) {
-                K.prep(xn, sm.ops[(c + 1) & 1], rk);
-                if (c + 1 + kPrefetch < nch) K.load(c + 1 + kPrefetch, xn);
-            }
-            __syncthreads();
-
-            // ---- finish chunk c's readouts ----
-            const int tbase = c * kC + 4 * g;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                float yv = Y[e];
+                pd.y = Y;
+                pd.v = Vb;
                 if (EPI) {
-                    const float4 m01 = *reinterpret_cast<const float4 *>(&sm.stats[4 * g + e][0]);
-                    const float4 m23 = *reinterpret_cast<const float4 *>(&sm.stats[4 * g + e][2]);
-                    const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
-                    const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
-                    const float m2 = (m01.y + m01.w + m23.y + m23.w) +
-                                     16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
-                    const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
-                    const int t = 4 * g + e;
-                    const float bz = o.bon[0][t] + o.bon[1][t] + o.bon[2][t] + o.bon[3][t];
-                    yv = (yv - mu) * rs * lnw + lnb + bz * bf16_lo((unsigned)(unsigned short)Vb[e]);
+                    // readouts: lane holds y[t = 4g+e][i = 16blk + lo]
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = 4 * g + e;
+                        pd.bon[e] = o.bon[0][t] + o.bon[1][t] + o.bon[2][t] + o.bon[3][t];
+                        const float mu = sum_lanes16(Y[e]) * (1.f / 16.f);
+                        const float dd = Y[e] - mu;
+                        const float m2 = sum_lanes16(dd * dd);
+                        if (lo == 0) sm.stats[c & 1][t][blk] = make_float2(mu, m2);
+                    }
                 }
-                if (tbase + e < T)
-                    yout[K.tok0 + (long)(tbase + e) * K.HN + 16 * wv + lo] =
-                        (uint16_t)f32_to_bf16_rne(yv);
             }
-            if (c + 1 < nch) K.matrices(sm.ops[(c + 1) & 1]);
             __syncthreads();
         }
-    }
-
-    if (p.s_out) {
+        if (p.s_out) {
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            *reinterpret_cast<float4 *>(p.s_out + sb + 16 * jb + 4 * g) =
-                make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+            for (int jb = 0; jb < 4; ++jb)
+                *reinterpret_cast<float4 *>(p.s_out + sb + 16 * jb + 4 * g) =
+                    make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+        }
+    } else {
+        // ---------------- prep waves: loads, operands, chunk matrices ----------------
+        float rk[4] = {0.f, 0.f, 0.f, 0.f};
+        if (EPI) {
+            const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * blk + 4 * g);
+            rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
+        }
+        // raw inputs of the next kPrefetch chunks stay in flight in a register ring;
+        // interval q (q = 0 .. nch + 2) prepares chunk q and forms chunk q-1's matrices
+        Raw xs[kPrefetch];
+#pragma unroll
+        for (int d = 0; d < kPrefetch; ++d)
+            if (d < nch) K.load(d, xs[d]);
+        for (int q0 = 0; q0 < nch + 3; q0 += kPrefetch) {
+#pragma unroll
+            for (int d = 0; d < kPrefetch; ++d) {
+                const int q = q0 + d;
+                if (q >= nch + 3) break;
+                if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
+                if (q < nch) {
+                    K.prep(xs[d], sm.ops[q % 3], rk);
+                    if (q + kPrefetch < nch) K.load(q + kPrefetch, xs[d]);
+                }
+                __syncthreads();
+            }
+        }
     }
 }
 
