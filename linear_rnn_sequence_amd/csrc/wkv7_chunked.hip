@@ -106,6 +106,7 @@ struct __align__(16) ChunkOps {
     short vt[4][kTile];    // V^T [value block][i][t]  (B form of V)
     float gc[64];          // G_C per key j
     float bon[4][16];      // bonus partial sums per (key block, token)
+    float bon_tot[16];     // bonus sum per token (all keys)
     float dkr[4][16];      // r_t.k_t partial sums per (key block, token), fp32
     float dbr[4][16];      // r_t.(a_t*kappa_t) partial sums, fp32
 };
@@ -166,7 +167,7 @@ struct Chunked {
         const float kp[4] = {bf16_lo(x.kap.x), bf16_hi(x.kap.x), bf16_lo(x.kap.y),
                              bf16_hi(x.kap.y)};
         const float a[4] = {bf16_lo(x.a.x), bf16_hi(x.a.x), bf16_lo(x.a.y), bf16_hi(x.a.y)};
-        f32x4 G, Gx, GC, Kp, Rp, Km, Bm;
+        f32x4 G, Gx, Kp, Rp, Km, Bm;
         float bon = 0.f, dkr = 0.f, dbr = 0.f;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -178,7 +179,6 @@ struct Chunked {
             q *= shr_fill1<8>(q);
             G[e] = q;
             Gx[e] = shr_fill1<1>(q);
-            GC[e] = __shfl(q, (lane & 48) | 15, 64);
             const float iG = __builtin_amdgcn_rcpf(q);  // 1 ulp; operands are rounded to bf16
             const float be = a[e] * kp[e];
             Kp[e] = kp[e] * Gx[e];
@@ -204,8 +204,9 @@ struct Chunked {
         o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(x.v.x >> 16);
         o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(x.v.y & 0xffffu);
         o.vt[jb][(4 * g + 3) * kRow + lo] = (short)(x.v.y >> 16);
-        if (lo == 0) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
-            make_float4(GC[0], GC[1], GC[2], GC[3]);
+        // the last token's lane holds the whole-chunk decay G_C of its 4 channels
+        if (lo == 15) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
+            make_float4(G[0], G[1], G[2], G[3]);
         // fp32 diagonals of M_kr and M_br: at s = t the decay ratio is exactly 1, so
         // r_t.k_t and r_t.(a_t*kappa_t) need no bf16 factors; the two-factor bf16
         // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
@@ -263,6 +264,8 @@ struct Chunked {
             z = mfma(to_bf16(imn), to_bf16(z), zero4());
             st_a(o.xinv, lane, to_bf16(-z));           // D of X^T = A form of X; stored negated
         } else {
+            if (EPI && blk == 0 && lane < 16)
+                o.bon_tot[lane] = o.bon[0][lane] + o.bon[1][lane] + o.bon[2][lane] + o.bon[3][lane];
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kTile] = (blk == 3) ? o.bm : o.km;
             const short(*rhs)[kTile] = (blk == 0) ? o.kp : o.rp;
@@ -298,8 +301,8 @@ struct Pending {
 template <bool EPI>
 __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI> &K,
                                                 const ChunkSmem &sm, const Pending &pd, int c,
-                                                float lnw, float lnb) {
-    const int g = K.g, lo = K.lo;
+                                                float lnw, float lnb, uint16_t *y) {
+    const int g = K.g;
     float yv[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -320,11 +323,16 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
     const unsigned lo2 = cvt_pk(yv[0], yv[1]), hi2 = cvt_pk(yv[2], yv[3]);
     const unsigned short out[4] = {(unsigned short)(lo2 & 0xffffu), (unsigned short)(lo2 >> 16),
                                    (unsigned short)(hi2 & 0xffffu), (unsigned short)(hi2 >> 16)};
+    // y points at token c*16 + 4g of this lane's value channel
     const int t0 = c * kC + 4 * g;
-    uint16_t *y = static_cast<uint16_t *>(p.y) + K.tok0 + (long)t0 * K.HN + 16 * K.blk + lo;
+    if (t0 + 3 < p.T) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-        if (t0 + e < p.T) y[e * K.HN] = out[e];
+        for (int e = 0; e < 4; ++e) y[e * K.HN] = out[e];
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (t0 + e < p.T) y[e * K.HN] = out[e];
+    }
 }
 
 template <bool EPI>
@@ -357,10 +365,15 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
             if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * blk + lo];
         }
         Pending pd;
+        uint16_t *ylane = static_cast<uint16_t *>(p.y) + K.tok0 + (long)(4 * g) * K.HN + 16 * blk + lo;
+        const long ystep = (long)kC * K.HN;
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
-            if (c > 0) finish_readouts<EPI>(p, K, sm, pd, c - 1, lnw, lnb);
+            if (c > 0) {
+                finish_readouts<EPI>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
+                ylane += ystep;
+            }
             if (c < nch) {
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = ld_a(o.vt[blk], lane);
@@ -390,10 +403,14 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
                 pd.v = Vb;
                 if (EPI) {
                     // readouts: lane holds y[t = 4g+e][i = 16blk + lo]
+                    const float4 bt = *reinterpret_cast<const float4 *>(&o.bon_tot[4 * g]);
+                    pd.bon[0] = bt.x;
+                    pd.bon[1] = bt.y;
+                    pd.bon[2] = bt.z;
+                    pd.bon[3] = bt.w;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int t = 4 * g + e;
-                        pd.bon[e] = o.bon[0][t] + o.bon[1][t] + o.bon[2][t] + o.bon[3][t];
                         const float mu = sum_lanes16(Y[e]) * (1.f / 16.f);
                         const float dd = Y[e] - mu;
                         const float m2 = sum_lanes16(dd * dd);

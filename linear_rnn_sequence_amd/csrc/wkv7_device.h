@@ -82,11 +82,18 @@ __device__ __forceinline__ float sum_lanes16(float x) {
     return x;
 }
 
-// Sum over the four DPP rows (lanes l, l^16, l^32, l^48).
+// Sum over the four DPP rows (lanes l, l^16, l^32, l^48), in VALU only:
+// v_permlane32_swap exchanges the upper half of its first operand with the
+// lower half of its second, so with both operands x the two results add up to
+// x + x^32 in every lane; v_permlane16_swap does the same between odd and even
+// rows, giving + x^16.
 __device__ __forceinline__ float sum_rows4(float x) {
-    x += __shfl_xor(x, 16, 64);
-    x += __shfl_xor(x, 32, 64);
-    return x;
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x),
+                                                    false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 }  // namespace wkv7
