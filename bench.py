@@ -79,6 +79,23 @@ def read_traffic(profile_name, src_hash):
         return None
 
 
+def read_profile_value(profile_name, key, src_hash):
+    path = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != src_hash:
+        return None
+    try:
+        return float(kv[key])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -279,12 +296,30 @@ def main():
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         p_bytes = B * T * H * 7 * N * 2 + B * H * N * N * 4 + 2 * H * N * 4 + H * N * 4
         ach = p_bytes / (prefill_ms / 1e3) / 1e9
+        chunked = args.prefill_algo in ("auto", "chunked")
+        src = source_hash("wkv7_chunked.hip", "wkv7_device.h")
+        traffic = (read_traffic("chunked_kernel_traffic_b8_t4096_h40_epilogue.txt", src)
+                   if chunked else None)
         out["prefill"] = {
             "ms": prefill_ms, "token_heads_per_s": B * T * H / (prefill_ms / 1e3),
             "algo": args.prefill_algo,
-            "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": ach / HBM_PEAK_GBS, "bytes_per_launch": p_bytes},
+            "roofline": {"kernel": "wkv7 chunked_kernel<epilogue>" if chunked else
+                         "wkv7 scan_kernel<bf16, epilogue>",
+                         "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
+                         "bytes_per_launch": p_bytes},
         }
+        if chunked:
+            # executed MFMA work per launch is fixed by the kernel (counted once with
+            # SQ_INSTS_VALU_MFMA_MOPS_BF16); divided by the live duration it gives the
+            # MFMA utilisation against the 2.5 PFLOP/s dense bf16 peak
+            mf = read_profile_value("chunked_kernel_mfma_b8_t4096_h40_epilogue.txt",
+                                    "mfma_bf16_flops_per_launch", src)
+            if mf is not None:
+                tf = mf / (prefill_ms / 1e3) / 1e12
+                out["prefill"]["mfma"] = {"achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": tf / BF16_MFMA_PEAK_TFLOPS,
+                                          "flops_per_launch": mf}
 
     # ------------------------- parity against the oracle, timed as the CPU baseline
     # The oracle runs on the full prefill batch (every head, every token) and on the
