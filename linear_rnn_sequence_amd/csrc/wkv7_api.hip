@@ -207,7 +207,8 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
         return RWKV7_ERR_SHAPE;
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
-    if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+    // two waves (workgroups) per head: keep 2*B*H within the grid's x limit
+    if ((size_t)B * H > 0x3fffffffu) return RWKV7_ERR_SHAPE;
     const void *ins[6] = {r, w, k, v, kappa, a};
     for (const void *p : ins)
         if (!p) return RWKV7_ERR_NULL;

@@ -9,15 +9,17 @@
 // summary, §8 Speed and Memory.  The state read and write (32 KiB per head)
 // is all but the whole traffic, so the kernel is laid out for HBM streaming.
 //
-// One wave per head and one wave per workgroup (measured faster than 2, 4, 8 or
-// 16 waves per workgroup, and than two heads per wave).  Lane (c, g) =
-// (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value rows
-// 16g .. 16g+15: every state load instruction reads four complete 256-byte
-// rows (16 lanes x 16 bytes each), so each wave moves its 16 KiB in 16 fully
-// coalesced dwordx4 loads issued back to back.  Row sums (S kappa and
-// S (w*r)) are 16-lane DPP reductions; the per-head GroupNorm of the optional
-// epilogue adds a 4-way exchange across the DPP rows.  Lane c finally holds
-// y of row 16g + c, so the 64 readouts leave as one 128-byte (bf16) store.
+// Two waves per head (each owns 32 value rows, 8 per lane), one wave per
+// workgroup; with the fused epilogue the head's two waves share a 128-thread
+// workgroup so the GroupNorm statistics can meet in LDS.  (Measured against 1,
+// 2, 4, 8 and 16 waves per workgroup, whole heads per wave, four waves per
+// head and persistent waves: this layout streamed fastest, 77% of 8 TB/s.)
+// Lane (c, g) = (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value
+// rows r0 + 8g .. r0 + 8g + 7: every state load instruction reads four complete
+// 256-byte rows (16 lanes x 16 bytes each), so each wave moves its 8 KiB in
+// eight fully coalesced dwordx4 loads issued back to back.  Row sums (S kappa
+// and S (w*r)) are 16-lane DPP reductions.  Lanes c < 8 finally hold y of rows
+// r0 + 8g + c, so each wave's 32 readouts leave as one 64-byte (bf16) store.
 // State loads and stores are non-temporal: each state is touched once per call
 // and the next layer's states should not be evicted for it.
 #include "wkv7_device.h"
@@ -26,8 +28,7 @@
 namespace wkv7 {
 namespace {
 
-constexpr int kDecodeThreads = 64;
-constexpr int kHeadsPerBlock = kDecodeThreads / 64;
+constexpr int kRows = 8;  // value rows per lane; a wave covers 32 rows, a head two waves
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -44,38 +45,40 @@ __device__ __forceinline__ void st_state(float *p, f32x4 x) {
         *reinterpret_cast<f32x4 *>(p) = x;
 }
 
-// 16 consecutive elements (value rows 16g .. 16g+15), widened to float.
-__device__ __forceinline__ void load16(const uint16_t *p, float *out) {
+// 8 consecutive elements (value rows r .. r+7), widened to float.
+__device__ __forceinline__ void load8(const uint16_t *p, float *out) {
     const uint4 a = *reinterpret_cast<const uint4 *>(p);
-    const uint4 b = *reinterpret_cast<const uint4 *>(p + 8);
-    const uint32_t u[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t u[4] = {a.x, a.y, a.z, a.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
+    for (int e = 0; e < 4; ++e) {
         out[2 * e] = bf16_lo(u[e]);
         out[2 * e + 1] = bf16_hi(u[e]);
     }
 }
-__device__ __forceinline__ void load16(const float *p, float *out) {
+__device__ __forceinline__ void load8(const float *p, float *out) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
         const float4 x = *reinterpret_cast<const float4 *>(p + 4 * q);
         out[4 * q] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
     }
 }
 
 template <class IO, bool EPI, bool NT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     using E = typename IO::elem;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const long head = (long)blockIdx.x * kHeadsPerBlock + wave;
-    if (head >= (long)p.B * p.H) return;  // whole wave leaves together
+    __shared__ float2 xch[2];  // epilogue: (mean, M2) of each half head
+    const int lane = threadIdx.x & 63;
+    const long head = EPI ? (long)blockIdx.x : (long)(blockIdx.x >> 1);
+    const int part = EPI ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x & 1);
+    if (head >= (long)p.B * p.H) return;  // whole workgroup leaves together
     const int h = (int)(head % p.H);
     const int c = lane & 15, g = lane >> 4;
+    const int r0 = 32 * part + kRows * g;  // this lane's value rows r0 .. r0+7
 
-    float *st = p.state + head * (kN * kN) + (16 * g) * kN + 4 * c;
-    f32x4 S[16];
+    float *st = p.state + head * (kN * kN) + r0 * kN + 4 * c;
+    f32x4 S[kRows];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) S[m] = ld_state<NT>(st + m * kN);
+    for (int m = 0; m < kRows; ++m) S[m] = ld_state<NT>(st + m * kN);
 
     const long vo = head * kN;
     const E *pr = static_cast<const E *>(p.r) + vo;
@@ -84,8 +87,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     const float4 a = IO::load4(static_cast<const E *>(p.a) + vo + 4 * c);
     const float4 k = IO::load4(static_cast<const E *>(p.k) + vo + 4 * c);
     const float4 r = IO::load4(pr + 4 * c);
-    float v[16];
-    load16(static_cast<const E *>(p.v) + vo + 16 * g, v);
+    float v[kRows];
+    load8(static_cast<const E *>(p.v) + vo + r0, v);
 
     const float4 bb = make_float4(a.x * kap.x, a.y * kap.y, a.z * kap.z, a.w * kap.w);
     const float4 wr = make_float4(w.x * r.x, w.y * r.y, w.z * r.z, w.w * r.w);
@@ -97,14 +100,14 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
         bon = r.x * k.x * rk.x + r.y * k.y * rk.y + r.z * k.z * rk.z + r.w * k.w * rk.w;
     }
 
-    float u[16], y[16];
+    float u[kRows], y[kRows];
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < kRows; ++m) {
         u[m] = S[m].x * kap.x + S[m].y * kap.y + S[m].z * kap.z + S[m].w * kap.w;
         y[m] = S[m].x * wr.x + S[m].y * wr.y + S[m].z * wr.z + S[m].w * wr.w;
     }
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < kRows; ++m) {
         u[m] = sum_lanes16(u[m]);
         y[m] = sum_lanes16(y[m]);
     }
@@ -113,7 +116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
     if (EPI) bon = sum_lanes16(bon);
 
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
+    for (int m = 0; m < kRows; ++m) {
         y[m] = y[m] + v[m] * kr - u[m] * br;
         f32x4 s = S[m];
         s.x = s.x * w.x - u[m] * bb.x + v[m] * k.x;
@@ -123,47 +126,56 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeArgs p) {
         st_state<NT>(st + m * kN, s);
     }
 
-    // lane c keeps row 16g + c
+    // lane c < 8 keeps row r0 + c
+    const int sel = c & (kRows - 1);
     float yo = y[0], vo1 = v[0];
 #pragma unroll
-    for (int m = 1; m < 16; ++m) {
-        yo = (c == m) ? y[m] : yo;
-        vo1 = (c == m) ? v[m] : vo1;
+    for (int m = 1; m < kRows; ++m) {
+        yo = (sel == m) ? y[m] : yo;
+        vo1 = (sel == m) ? v[m] : vo1;
     }
     if (EPI) {
+        // statistics of this wave's 32 rows, then Chan's combination of the two halves
         float s1 = 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) s1 += y[m];
-        const float mu = sum_rows4(s1) * (1.f / kN);
+        for (int m = 0; m < kRows; ++m) s1 += y[m];
+        const float mu_w = sum_rows4(s1) * (1.f / 32.f);
         float s2 = 0.f;
 #pragma unroll
-        for (int m = 0; m < 16; ++m) s2 += (y[m] - mu) * (y[m] - mu);
-        const float var = sum_rows4(s2) * (1.f / kN);
+        for (int m = 0; m < kRows; ++m) s2 += (y[m] - mu_w) * (y[m] - mu_w);
+        const float m2_w = sum_rows4(s2);
+        if (lane == 0) xch[part] = make_float2(mu_w, m2_w);
+        __syncthreads();
+        const float2 q0 = xch[0], q1 = xch[1];
+        const float mu = 0.5f * (q0.x + q1.x);
+        const float d0 = q0.x - mu, d1 = q1.x - mu;
+        const float var = (q0.y + q1.y + 32.f * (d0 * d0 + d1 * d1)) * (1.f / kN);
         const float rs = __builtin_amdgcn_rsqf(var + p.epi.eps);
-        const int ch = h * kN + 16 * g + c;
+        const int ch = h * kN + r0 + sel;
         const float gw = p.epi.ln_w ? p.epi.ln_w[ch] : 1.f;
         const float gb = p.epi.ln_b ? p.epi.ln_b[ch] : 0.f;
         yo = (yo - mu) * rs * gw + gb + bon * vo1;
     }
-    IO::store1(static_cast<E *>(p.y) + vo + 16 * g + c, yo);
+    if (c < kRows) IO::store1(static_cast<E *>(p.y) + vo + r0 + c, yo);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream) {
     const long heads = (long)p.B * p.H;
-    const dim3 grid((unsigned)((heads + kHeadsPerBlock - 1) / kHeadsPerBlock)),
-        block(kDecodeThreads);
+    // without the epilogue: one 64-thread workgroup per half head; with it: one
+    // 128-thread workgroup per head
+    const dim3 grid_half((unsigned)(2 * heads)), grid_head((unsigned)heads);
     if (p.bf16) {
         if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true>), grid_head, dim3(128), 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true>), grid_half, dim3(64), 0, stream, p);
     } else {
         if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<F32In, true, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<F32In, true, true>), grid_head, dim3(128), 0, stream, p);
         else
-            hipLaunchKernelGGL((decode_kernel<F32In, false, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<F32In, false, true>), grid_half, dim3(64), 0, stream, p);
     }
     return hipGetLastError();
 }
