@@ -57,6 +57,12 @@ namespace {
 
 constexpr int kC = 16;                  // tokens per chunk
 constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per lane
+// s_waitcnt immediate (gfx9 encoding: vmcnt[3:0] + vmcnt[15:14], expcnt[6:4],
+// lgkmcnt[11:8]) that waits until at most 6*(kPrefetch-1) vector loads are
+// outstanding and does not wait on expcnt or lgkmcnt.
+constexpr int kLoadsPerChunk = 6;
+constexpr int kVm = kLoadsPerChunk * (kPrefetch - 1);
+constexpr int kWaitOlderChunks = (kVm & 0xF) | (0x7 << 4) | (0xF << 8) | (((kVm >> 4) & 0x3) << 14);
 constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
@@ -144,16 +150,27 @@ struct Chunked {
           lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * ((threadIdx.x >> 6) & 3) +
                    4 * ((threadIdx.x & 63) >> 4)) {}
 
+    // Issues exactly six loads on every path (no branch around them), so the
+    // compiler's wait-count bookkeeping can leave the later chunks of the ring in
+    // flight: the chunk index is clamped to the last chunk and the token index to
+    // T-1, which keeps every address inside the tensors; prep() replaces the
+    // values of tokens past T.
     __device__ void load(int c, Raw &x) const {
-        const long off = lane_off + (long)c * kC * HN;
-        if (c * kC + lo < p.T) {  // token exists
-            x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
-            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
-            x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
-            x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
-            x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
-            x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
-        } else {  // padding token past T: no write, no removal, no decay
+        const int cc = min(c, (p.T - 1) / kC);
+        const int t = min(cc * kC + lo, p.T - 1);
+        const long off = lane_off + (long)(t - lo) * HN;
+        x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
+        x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
+        x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
+        x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
+        x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
+        x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
+    }
+
+    // Padding token past T (only in a partial last chunk): no write, no removal,
+    // no decay, no readout.
+    __device__ __forceinline__ void pad(int c, Raw &x) const {
+        if (c * kC + lo >= p.T) {
             x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
             x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
         }
@@ -437,8 +454,7 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
         // interval q (q = 0 .. nch + 2) prepares chunk q and forms chunk q-1's matrices
         Raw xs[kPrefetch];
 #pragma unroll
-        for (int d = 0; d < kPrefetch; ++d)
-            if (d < nch) K.load(d, xs[d]);
+        for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
         for (int q0 = 0; q0 < nch + 3; q0 += kPrefetch) {
 #pragma unroll
             for (int d = 0; d < kPrefetch; ++d) {
@@ -446,9 +462,15 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
                 if (q >= nch + 3) break;
                 if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
                 if (q < nch) {
+                    if ((q + 1) * kC > p.T) K.pad(q, xs[d]);  // partial last chunk only
                     K.prep(xs[d], sm.ops[q % 3], rk);
-                    if (q + kPrefetch < nch) K.load(q + kPrefetch, xs[d]);
                 }
+                K.load(q + kPrefetch, xs[d]);  // clamped: always six loads per interval
+                // the next interval consumes the oldest ring slot: let only the
+                // (kPrefetch-1) younger chunks' loads stay in flight.  Stated
+                // explicitly because the compiler's own count is lost across the
+                // loop's back edge and would wait for nearly every load.
+                __builtin_amdgcn_s_waitcnt(kWaitOlderChunks);
                 __syncthreads();
             }
         }
