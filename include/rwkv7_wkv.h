@@ -113,7 +113,12 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
                                rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
                                size_t workspace_bytes, void *stream);
 
-/* Bytes of device workspace rwkv7_wkv_forward needs for this problem (0 if none). */
+/* Bytes of device workspace rwkv7_wkv_forward needs for this problem (0 if none).
+ * The chunked path splits long sequences of few heads into segments that run
+ * in parallel (their transitions and offsets are combined exactly, by the
+ * linearity of the state update in the entry state); the split, and so this
+ * size, depends on the compute-unit count of the current device: query it with
+ * the device current that the forward call will run on. */
 size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                    rwkv7_algo algo);
 

@@ -64,6 +64,7 @@ constexpr int kLoadsPerChunk = 6;
 constexpr int kVm = kLoadsPerChunk * (kPrefetch - 1);
 constexpr int kWaitOlderChunks = (kVm & 0xF) | (0x7 << 4) | (0xF << 8) | (((kVm >> 4) & 0x3) << 14);
 constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
+constexpr int kThreadsSummary = 768;    // + 4 chain waves for the transition rows
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
 
@@ -117,6 +118,17 @@ struct __align__(16) ChunkOps {
     float dbr[4][16];      // r_t.(a_t*kappa_t) partial sums, fp32
 };
 
+// Launch description: the sequence may be split into nseg segments of seg_len
+// tokens (the last one shorter) that are processed in parallel; the workspace
+// holds per (b, h, segment) the transition P, the offset dS and the entry state.
+struct ChunkedParams {
+    ForwardArgs p;
+    int nseg;         // segments per sequence
+    int nseg_launch;  // segments per (b, h) covered by this launch
+    int seg_len;      // tokens per segment (a multiple of kC)
+    float *ws_p, *ws_ds, *ws_sin;
+};
+
 struct __align__(16) ChunkSmem {
     ChunkOps ops[3];
     float2 stats[2][16][4];  // per token, per value block: (mean, M2) of 16 readouts
@@ -140,13 +152,14 @@ template <bool EPI>
 struct Chunked {
     const ForwardArgs &p;
     const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
-    const long HN, tok0;         // elements between tokens; offset of (b, t=0, h, 0)
+    const int Tl;                // tokens of this workgroup's range
+    const long HN, tok0;         // elements between tokens; offset of (b, t = t0, h, 0)
     const long lane_off;         // prep lane: its 4 channels at token lo of chunk 0
 
-    __device__ Chunked(const ForwardArgs &p_, int b_, int h_)
+    __device__ Chunked(const ForwardArgs &p_, int b_, int h_, int t0, int tl)
         : p(p_), lane(threadIdx.x & 63), blk((threadIdx.x >> 6) & 3),
-          g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), HN((long)p_.H * kN),
-          tok0((long)b_ * p_.T * ((long)p_.H * kN) + (long)h_ * kN),
+          g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), Tl(tl), HN((long)p_.H * kN),
+          tok0(((long)b_ * p_.T + t0) * ((long)p_.H * kN) + (long)h_ * kN),
           lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * ((threadIdx.x >> 6) & 3) +
                    4 * ((threadIdx.x & 63) >> 4)) {}
 
@@ -156,8 +169,8 @@ struct Chunked {
     // T-1, which keeps every address inside the tensors; prep() replaces the
     // values of tokens past T.
     __device__ void load(int c, Raw &x) const {
-        const int cc = min(c, (p.T - 1) / kC);
-        const int t = min(cc * kC + lo, p.T - 1);
+        const int cc = min(c, (Tl - 1) / kC);
+        const int t = min(cc * kC + lo, Tl - 1);
         const long off = lane_off + (long)(t - lo) * HN;
         x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
         x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
@@ -170,7 +183,7 @@ struct Chunked {
     // Padding token past T (only in a partial last chunk): no write, no removal,
     // no decay, no readout.
     __device__ __forceinline__ void pad(int c, Raw &x) const {
-        if (c * kC + lo >= p.T) {
+        if (c * kC + lo >= Tl) {
             x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
             x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
         }
@@ -342,26 +355,44 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
                                    (unsigned short)(hi2 & 0xffffu), (unsigned short)(hi2 >> 16)};
     // y points at token c*16 + 4g of this lane's value channel
     const int t0 = c * kC + 4 * g;
-    if (t0 + 3 < p.T) {
+    if (t0 + 3 < K.Tl) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) y[e * K.HN] = out[e];
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (t0 + e < p.T) y[e * K.HN] = out[e];
+            if (t0 + e < K.Tl) y[e * K.HN] = out[e];
     }
 }
 
-template <bool EPI>
-__global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
+// SUMMARY = false: y and the final state of each (b, h, segment) from its entry
+//   state (the whole sequence when there is one segment).
+// SUMMARY = true: for each (b, h, segment) but the last, the segment's offset
+//   dS (waves 0..3: entry state 0) and transition P (waves 8..11: entry state I,
+//   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
+template <bool EPI, bool SUMMARY>
+__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_kernel(
+    ChunkedParams cp) {
     __shared__ ChunkSmem sm;
-    const int bh = blockIdx.x;
+    const ForwardArgs &p = cp.p;
+    const int bh = blockIdx.x / cp.nseg_launch;
+    const int seg = blockIdx.x - bh * cp.nseg_launch;
     const int b = bh / p.H, h = bh - b * p.H;
-    const Chunked<EPI> K(p, b, h);
+    const int t0 = seg * cp.seg_len;
+    const Chunked<EPI> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
     const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
-    const bool chain_wave = threadIdx.x < 256;  // waves 0..3
-    const int nch = (p.T + kC - 1) / kC;
-    const long sb = (long)bh * kN * kN + (long)(16 * blk + lo) * kN;
+    const int wave = threadIdx.x >> 6;
+    const bool chain_wave = wave < 4 || wave >= 8;  // waves 0..3 (and 8..11 in SUMMARY)
+    const bool p_rows = SUMMARY && wave >= 8;       // transition rows
+    const int nch = (K.Tl + kC - 1) / kC;
+    const long srow = (long)(16 * blk + lo) * kN;   // this lane's value row i in a state
+    const long sidx = (long)bh * cp.nseg + seg;     // (b, h, segment) slot in the workspace
+    // entry state and where the final state goes
+    const float *s_in = SUMMARY ? nullptr
+                      : (cp.nseg == 1 ? (p.s0 ? p.s0 + (long)bh * kN * kN : nullptr)
+                                      : cp.ws_sin + sidx * kN * kN);
+    float *s_fin = SUMMARY ? (p_rows ? cp.ws_p : cp.ws_ds) + sidx * kN * kN
+                 : (seg == cp.nseg - 1 && p.s_out ? p.s_out + (long)bh * kN * kN : nullptr);
 
     if (chain_wave) {
         // ---------------- chain waves: state, MFMA chain, readouts ----------------
@@ -369,11 +400,13 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
         f32x4 Z[4];
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-            if (p.s0) {
-                const float4 x = *reinterpret_cast<const float4 *>(p.s0 + sb + 16 * jb + 4 * g);
+            if (s_in) {
+                const float4 x = *reinterpret_cast<const float4 *>(s_in + srow + 16 * jb + 4 * g);
                 Z[jb] = f32x4{x.x, x.y, x.z, x.w};
             } else {
-                Z[jb] = zero4();
+#pragma unroll
+                for (int e = 0; e < 4; ++e)  // identity for the transition rows
+                    Z[jb][e] = (p_rows && 16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
             }
         }
         float lnw = 1.f, lnb = 0.f;
@@ -387,13 +420,13 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
-            if (c > 0) {
+            if (!SUMMARY && c > 0) {
                 finish_readouts<EPI>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
                 ylane += ystep;
             }
             if (c < nch) {
                 const ChunkOps &o = sm.ops[c % 3];
-                const bf16x4 Vb = ld_a(o.vt[blk], lane);
+                const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
                 bf16x4 Zb[4];
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
@@ -418,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
                 }
                 pd.y = Y;
                 pd.v = Vb;
-                if (EPI) {
+                if (EPI && !SUMMARY) {
                     // readouts: lane holds y[t = 4g+e][i = 16blk + lo]
                     const float4 bt = *reinterpret_cast<const float4 *>(&o.bon_tot[4 * g]);
                     pd.bon[0] = bt.x;
@@ -437,16 +470,16 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
             }
             __syncthreads();
         }
-        if (p.s_out) {
+        if (s_fin) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb)
-                *reinterpret_cast<float4 *>(p.s_out + sb + 16 * jb + 4 * g) =
+                *reinterpret_cast<float4 *>(s_fin + srow + 16 * jb + 4 * g) =
                     make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
         }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
         float rk[4] = {0.f, 0.f, 0.f, 0.f};
-        if (EPI) {
+        if (EPI && !SUMMARY) {
             const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * blk + 4 * g);
             rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
         }
@@ -462,7 +495,7 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
                 if (q >= nch + 3) break;
                 if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
                 if (q < nch) {
-                    if ((q + 1) * kC > p.T) K.pad(q, xs[d]);  // partial last chunk only
+                    if ((q + 1) * kC > K.Tl) K.pad(q, xs[d]);  // partial last chunk only
                     K.prep(xs[d], sm.ops[q % 3], rk);
                 }
                 K.load(q + kPrefetch, xs[d]);  // clamped: always six loads per interval
@@ -477,16 +510,121 @@ __global__ __launch_bounds__(kThreads) void chunked_kernel(ForwardArgs p) {
     }
 }
 
+// Entry states of the segments of one (b, h): S_in[0] = s0 (or 0) and
+// S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  One workgroup per (b, h); thread t
+// owns row i = t / 4, columns 16 (t % 4) .. +15.
+__global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) {
+    __shared__ float S[kN][kN + 4];
+    __shared__ float P[kN][kN + 4];
+    const long bh = blockIdx.x;
+    const int t = threadIdx.x, i = t >> 2, j0 = 16 * (t & 3);
+    const float *s0 = cp.p.s0 ? cp.p.s0 + bh * kN * kN : nullptr;
+    float acc[16];
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) acc[jj] = s0 ? s0[i * kN + j0 + jj] : 0.f;
+    for (int sg = 0; sg < cp.nseg; ++sg) {
+        float *sin = cp.ws_sin + (bh * cp.nseg + sg) * kN * kN;
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) sin[i * kN + j0 + jj] = acc[jj];
+        if (sg == cp.nseg - 1) break;
+        const float *Pg = cp.ws_p + (bh * cp.nseg + sg) * kN * kN;
+        const float *Dg = cp.ws_ds + (bh * cp.nseg + sg) * kN * kN;
+        __syncthreads();  // previous step's readers are done with S and P
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) {
+            S[i][j0 + jj] = acc[jj];
+            P[i][j0 + jj] = Pg[i * kN + j0 + jj];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int jj = 0; jj < 16; ++jj) acc[jj] = Dg[i * kN + j0 + jj];
+        for (int k = 0; k < kN; ++k) {
+            const float sik = S[i][k];
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) acc[jj] += sik * P[k][j0 + jj];
+        }
+    }
+}
+
 }  // namespace
 
-size_t chunked_workspace_bytes(int, int, int) { return 0; }
+namespace {
+
+int device_cu_count() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Segments per sequence: split the time axis only when the (b, h) pairs alone
+// leave at least half the compute units idle and each segment keeps at least
+// 64 chunks (the split costs a summary pass over all but the last segment).
+// G segments per (b, h) with B*H*G <= CUs: one workgroup per compute unit.
+void segment_plan(int B, int T, int H, int &nseg, int &seg_len) {
+    nseg = 1;
+    seg_len = T;
+    const long bh = (long)B * H;
+    const int cu = device_cu_count();
+    if (T < 4096 || 2 * bh > cu) return;
+    int G = (int)(cu / bh);
+    G = min(G, T / 1024);
+    G = min(G, 64);
+    if (G < 2) return;
+    int L = (T + G - 1) / G;
+    L = (L + kC - 1) / kC * kC;
+    nseg = (T + L - 1) / L;
+    seg_len = L;
+    if (nseg < 2) {
+        nseg = 1;
+        seg_len = T;
+    }
+}
+
+}  // namespace
+
+size_t chunked_workspace_bytes(int B, int T, int H) {
+    int nseg, seg_len;
+    segment_plan(B, T, H, nseg, seg_len);
+    if (nseg == 1) return 0;
+    return (size_t)3 * B * H * nseg * kN * kN * sizeof(float);
+}
 
 hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
-    const dim3 grid((unsigned)((long)p.B * p.H)), block(kThreads);
+    ChunkedParams cp{};
+    cp.p = p;
+    segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
+    const long bh = (long)p.B * p.H;
+    if (cp.nseg > 1) {
+        const size_t slab = (size_t)bh * cp.nseg * kN * kN;
+        cp.ws_p = static_cast<float *>(p.workspace);
+        cp.ws_ds = cp.ws_p + slab;
+        cp.ws_sin = cp.ws_ds + slab;
+        // 1. transitions and offsets of every segment but the last
+        cp.nseg_launch = cp.nseg - 1;
+        hipLaunchKernelGGL((chunked_kernel<false, true>), dim3((unsigned)(bh * cp.nseg_launch)),
+                           dim3(kThreadsSummary), 0, stream, cp);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // 2. entry state of every segment
+        hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)bh), dim3(256), 0, stream, cp);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    // 3. readouts and final states, all segments in parallel
+    cp.nseg_launch = cp.nseg;
+    const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunked_kernel<true, false>), grid, block, 0, stream, cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false>), grid, block, 0, stream, p);
+        hipLaunchKernelGGL((chunked_kernel<false, false>), grid, block, 0, stream, cp);
     return hipGetLastError();
 }
 

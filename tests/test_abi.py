@@ -99,3 +99,18 @@ def test_workspace_query_is_pure():
     L = wkv.lib()
     assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 64, 0, 1) == 0   # scan needs none
     assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 32, 1, 2) == 0   # unsupported -> 0
+
+
+def test_workspace_query_segments():
+    """Long sequences of few heads are split into segments (one workgroup per
+    compute unit); each segment keeps three float32 N x N states in the
+    workspace.  Many heads, short sequences or the scan need none."""
+    L = wkv.lib()
+    per_seg = 3 * 64 * 64 * 4
+    big = L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 2)
+    assert big > 0 and big % per_seg == 0 and 2 <= big // per_seg <= 64
+    assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 0) == big  # auto = chunked
+    assert L.rwkv7_wkv_forward_workspace(1, 4095, 1, 64, 1, 2) == 0
+    assert L.rwkv7_wkv_forward_workspace(64, 65536, 64, 64, 1, 2) == 0
+    assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 1) == 0
+    assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 4 * per_seg  # 1024 tokens each

@@ -83,17 +83,20 @@ def test_chunked_29b_shape_with_epilogue(wkv):
 
 
 def test_chunked_long_context_single_pass_and_segments(wkv):
-    """T = 65536, slow decay, near-full replacement: one pass and 16 segments of
-    4096 with the state passed between them, both against the oracle, and the
+    """T = 65536, slow decay, near-full replacement: one call (which splits the
+    sequence into parallel segments) and 32 calls of 2048 tokens (too short to
+    split) with the state passed between them, both against the oracle, and the
     drift between the two."""
     x = synth.config_inputs(4)
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
+    assert wkv.forward_workspace_bytes(1, 65536, 40) > 0  # split into segments
+    assert wkv.forward_workspace_bytes(1, 2048, 40) == 0
     y1, s1 = wkv.forward(*ins, algo="chunked")
     st = torch.zeros_like(s1)
     ys = []
-    for seg in range(16):
-        sl = slice(seg * 4096, (seg + 1) * 4096)
+    for seg in range(32):
+        sl = slice(seg * 2048, (seg + 1) * 2048)
         y, _ = wkv.forward(*(t[:, sl].contiguous() for t in ins), s0=st, s_out=st,
                            algo="chunked")
         ys.append(y)
@@ -107,6 +110,53 @@ def test_chunked_long_context_single_pass_and_segments(wkv):
     drift = rel_err(to_f64(yseg), to_f64(y1))
     print(f"long context: single {e1:.2e}, segmented {e2:.2e}, drift {drift:.2e}")
     assert drift <= TOL
+
+
+# Few heads and long sequences: the time axis is split into segments run in
+# parallel; their transitions and offsets are combined into each segment's
+# entry state (linearity of the update in the state).
+@pytest.mark.parametrize("B,H,T", [(1, 1, 4096), (1, 2, 8229), (2, 3, 5000), (1, 1, 20000)])
+@pytest.mark.parametrize("epi", [False, True])
+@pytest.mark.parametrize("s0", ["zero", "normal"])
+def test_segmented_sweep(wkv, B, H, T, epi, s0):
+    assert wkv.forward_workspace_bytes(B, T, H) > 0
+    x = synth.draw(B, T, H, seed=7 * T + B + H, dtype="bf16", s0=s0, w_recipe="wide",
+                   epilogue=epi)
+    check(wkv, x, f"segmented B{B} H{H} T{T} epi={epi} s0={s0}")
+
+
+def test_segmented_in_place_and_pieces(wkv):
+    """s_out == s0 with a split sequence, against the same tokens run as pieces
+    of 2000 (each too short to split) with the state passed between them."""
+    x = synth.draw(1, 10000, 2, seed=71, dtype="bf16", s0="normal", w_recipe="slow",
+                   a_mean=2.0, epilogue=True)
+    d = to_device(x, torch)
+    ins = [d[n] for n in NAMES]
+    st = d["s0"].clone()
+    y1, _ = wkv.forward(*ins, s0=st, s_out=st, epilogue=d["epi"], algo="chunked")
+    sp = d["s0"].clone()
+    ys = []
+    for i in range(5):
+        sl = slice(i * 2000, (i + 1) * 2000)
+        y, _ = wkv.forward(*(t[:, sl].contiguous() for t in ins), s0=sp, s_out=sp,
+                           epilogue=d["epi"], algo="chunked")
+        ys.append(y)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle_forward(x)
+    assert_close(to_f64(y1), y_ref, TOL, "split y")
+    assert_close(to_f64(st), s_ref, TOL, "split S in place")
+    assert_close(to_f64(torch.cat(ys, 1)), y_ref, TOL, "pieces y")
+    assert rel_err(to_f64(st), to_f64(sp)) <= TOL
+
+
+def test_segmented_workspace_too_small(wkv):
+    x = synth.draw(1, 4096, 1, seed=72, dtype="bf16")
+    d = to_device(x, torch)
+    need = wkv.forward_workspace_bytes(1, 4096, 1)
+    assert need > 0
+    ws = torch.empty(need - 16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(wkv.Rwkv7Error):
+        wkv.forward(*(d[n] for n in NAMES), algo="chunked", workspace=ws)
 
 
 def test_chunked_matches_scan(wkv):
@@ -138,10 +188,12 @@ def _transition_inputs(rng, T, B=2, H=3, N=64):
     return vecs, S0
 
 
-@pytest.mark.parametrize("T", [1, 2, 16, 40])
+@pytest.mark.parametrize("T", [1, 2, 16, 40, 4096 + 40])
 def test_chunked_exact_transitions(wkv, T):
+    """Exact also when the sequence is split: each segment's transition is a
+    permutation matrix and its offset zero."""
     rng = np.random.default_rng(T)
-    vecs, S0 = _transition_inputs(rng, T)
+    vecs, S0 = _transition_inputs(rng, T, B=1 if T > 4096 else 2)
     _, s_ref = oracle.forward(*(vecs[n] for n in NAMES), s0=S0)
     ins = [torch.from_numpy(np.ascontiguousarray(vecs[n])).to("cuda", torch.bfloat16)
            for n in NAMES]
