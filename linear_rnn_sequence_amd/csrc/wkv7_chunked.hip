@@ -511,37 +511,59 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
 }
 
 // Entry states of the segments of one (b, h): S_in[0] = s0 (or 0) and
-// S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  One workgroup per (b, h); thread t
-// owns row i = t / 4, columns 16 (t % 4) .. +15.
+// S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  The value rows i are independent,
+// so each workgroup owns kCombineRows rows of one (b, h); thread (rr, c) keeps
+// columns 2c, 2c+1 of row rr.  P_g (shared by the rows) goes through a double
+// buffer in LDS, one barrier per segment; the next segment's P and dS are
+// loaded while the current product runs.
+constexpr int kCombineRows = 8;
+constexpr int kCombineParts = kN / kCombineRows;
+
 __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) {
-    __shared__ float S[kN][kN + 4];
-    __shared__ float P[kN][kN + 4];
-    const long bh = blockIdx.x;
-    const int t = threadIdx.x, i = t >> 2, j0 = 16 * (t & 3);
-    const float *s0 = cp.p.s0 ? cp.p.s0 + bh * kN * kN : nullptr;
-    float acc[16];
+    __shared__ float2 Pl[2][kN][kN / 2];
+    __shared__ float Sl[2][kCombineRows][kN];
+    const long bh = blockIdx.x / kCombineParts;
+    const int part = blockIdx.x - (int)bh * kCombineParts;
+    const int t = threadIdx.x, rr = t >> 5, c = t & 31;
+    const long cell = (long)(kCombineRows * part + rr) * kN + 2 * c;  // (i, 2c) in a state
+    const long slot0 = bh * cp.nseg * kN * kN;                          // segment 0 of (b, h)
+    float2 acc = make_float2(0.f, 0.f);
+    if (cp.p.s0) acc = *reinterpret_cast<const float2 *>(cp.p.s0 + bh * kN * kN + cell);
+    // thread t carries P elements 4 (t + 256 m) .. +3, m = 0..3, between global and LDS
+    float4 pn[4];
+    float2 dn = make_float2(0.f, 0.f);
+    if (cp.nseg > 1) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) acc[jj] = s0 ? s0[i * kN + j0 + jj] : 0.f;
+        for (int m = 0; m < 4; ++m)
+            pn[m] = *reinterpret_cast<const float4 *>(cp.ws_p + slot0 + 4 * (t + 256 * m));
+        dn = *reinterpret_cast<const float2 *>(cp.ws_ds + slot0 + cell);
+    }
     for (int sg = 0; sg < cp.nseg; ++sg) {
-        float *sin = cp.ws_sin + (bh * cp.nseg + sg) * kN * kN;
-#pragma unroll
-        for (int jj = 0; jj < 16; ++jj) sin[i * kN + j0 + jj] = acc[jj];
+        const long slot = slot0 + (long)sg * kN * kN;
+        *reinterpret_cast<float2 *>(cp.ws_sin + slot + cell) = acc;
         if (sg == cp.nseg - 1) break;
-        const float *Pg = cp.ws_p + (bh * cp.nseg + sg) * kN * kN;
-        const float *Dg = cp.ws_ds + (bh * cp.nseg + sg) * kN * kN;
-        __syncthreads();  // previous step's readers are done with S and P
+        const int buf = sg & 1;
+        float *pl = &Pl[buf][0][0].x;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) {
-            S[i][j0 + jj] = acc[jj];
-            P[i][j0 + jj] = Pg[i * kN + j0 + jj];
+        for (int m = 0; m < 4; ++m) *reinterpret_cast<float4 *>(pl + 4 * (t + 256 * m)) = pn[m];
+        Sl[buf][rr][2 * c] = acc.x;
+        Sl[buf][rr][2 * c + 1] = acc.y;
+        const float2 d = dn;
+        if (sg + 1 < cp.nseg - 1) {  // operands of the next segment
+            const long nx = slot + kN * kN;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+                pn[m] = *reinterpret_cast<const float4 *>(cp.ws_p + nx + 4 * (t + 256 * m));
+            dn = *reinterpret_cast<const float2 *>(cp.ws_ds + nx + cell);
         }
         __syncthreads();
+        acc = d;
 #pragma unroll
-        for (int jj = 0; jj < 16; ++jj) acc[jj] = Dg[i * kN + j0 + jj];
         for (int k = 0; k < kN; ++k) {
-            const float sik = S[i][k];
-#pragma unroll
-            for (int jj = 0; jj < 16; ++jj) acc[jj] += sik * P[k][j0 + jj];
+            const float sk = Sl[buf][rr][k];
+            const float2 pk = Pl[buf][k][c];
+            acc.x += sk * pk.x;
+            acc.y += sk * pk.y;
         }
     }
 }
@@ -614,7 +636,8 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         // 2. entry state of every segment
-        hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)bh), dim3(256), 0, stream, cp);
+        hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)(bh * kCombineParts)), dim3(256),
+                           0, stream, cp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
