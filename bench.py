@@ -9,8 +9,10 @@ One step = one pass of the whole path over one batch of synthetic input:
 Throughput is token*heads per second over both parts (decode counts every
 layer's heads).  Inputs are resident in HBM before the timed region.
 
-Prints ONE JSON line.  Extra options (--only, --copy-probe, --steps) exist for
-profiling runs.
+Prints ONE JSON line.  Extra options (--only, --copy-probe, --steps,
+--prefill-shape) exist for profiling runs; "--only prefill --prefill-shape long"
+times the long-context prefill instead (B=1, T=65536, H=40, slow decay, no
+epilogue), which the chunked path splits into parallel time segments.
 """
 from __future__ import annotations
 
@@ -32,6 +34,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 N = 64
 PREFILL = dict(B=8, T=4096, H=40)
+# prefill shapes: (synthetic config index, shape, fused epilogue)
+PREFILL_SHAPES = {"2.9b": (2, PREFILL, True), "long": (4, dict(B=1, T=65536, H=40), False)}
 DECODE = dict(layers=32, B=256, H=40, steps=64)
 
 
@@ -49,6 +53,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
+    ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
+                    help="'long' needs --only prefill")
     return ap.parse_args()
 
 
@@ -114,6 +120,12 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
+    cfg_idx, PREFILL, p_with_epi = PREFILL_SHAPES[args.prefill_shape]
+    if args.prefill_shape != "2.9b" and args.only != "prefill":
+        print("bench.py: --prefill-shape long is a prefill-only measurement (--only prefill)",
+              file=sys.stderr)
+        sys.exit(2)
+
     import torch
 
     import linear_rnn_sequence_amd as wkv
@@ -142,14 +154,16 @@ def main():
     # ------------------------------------------------------------------ prefill
     if do_prefill:
         t0 = time.time()
-        px = synth.config_inputs(2)
+        px = synth.config_inputs(cfg_idx)
         pd = {}
         for n in NAMES:
             pd[n] = torch.from_numpy(px[n].view(np.int16)).to(dev).view(torch.bfloat16)
         e = px["epi"]
-        p_epi = {"ln_w": torch.from_numpy(e["ln_w"]).to(dev),
-                 "ln_b": torch.from_numpy(e["ln_b"]).to(dev),
-                 "r_k": torch.from_numpy(e["r_k"]).to(dev), "eps": e["eps"]}
+        p_epi = None
+        if p_with_epi:
+            p_epi = {"ln_w": torch.from_numpy(e["ln_w"]).to(dev),
+                     "ln_b": torch.from_numpy(e["ln_b"]).to(dev),
+                     "r_k": torch.from_numpy(e["r_k"]).to(dev), "eps": e["eps"]}
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         p_y = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=dev)
         p_s = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
@@ -252,8 +266,10 @@ def main():
         work += DS * L * DB * DH
     value = work / (ms_per_step / 1e3)
 
+    long_shape = args.prefill_shape == "long"
     out = {
-        "metric": "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)",
+        "metric": ("WKV7 tokens x heads per second (long-context prefill)" if long_shape else
+                   "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)"),
         "value": value,
         "unit": "token*heads/s",
         "n_gpus": 1,
@@ -266,11 +282,13 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; recipes of the pages' parameterisations)",
         "config": {
-            "workload": ("2.9B-shape WKV7: prefill B8 T4096 H40 N64 with fused GroupNorm+bonus "
+            "workload": ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue)"
+                         if long_shape else
+                         "2.9B-shape WKV7: prefill B8 T4096 H40 N64 with fused GroupNorm+bonus "
                          "epilogue, then decode of 64 tokens through 32 layers x B256 x H40 "
                          "resident fp32 states"),
-            "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=True)
-            if do_prefill else None,
+            "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=p_with_epi,
+                            workspace_bytes=ws_bytes) if do_prefill else None,
             "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
             "state_dtype": "f32",
         },
@@ -294,22 +312,25 @@ def main():
         out["decode_ms_per_step"] = float(run_ms.mean())
     if do_prefill:
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
-        p_bytes = B * T * H * 7 * N * 2 + B * H * N * N * 4 + 2 * H * N * 4 + H * N * 4
+        # six inputs + y, the final state, and the epilogue parameters when fused
+        p_bytes = B * T * H * 7 * N * 2 + B * H * N * N * 4
+        if p_with_epi:
+            p_bytes += 2 * H * N * 4 + H * N * 4
         ach = p_bytes / (prefill_ms / 1e3) / 1e9
         chunked = args.prefill_algo in ("auto", "chunked")
         src = source_hash("wkv7_chunked.hip", "wkv7_device.h")
         traffic = (read_traffic("chunked_kernel_traffic_b8_t4096_h40_epilogue.txt", src)
-                   if chunked else None)
+                   if chunked and not long_shape else None)
         out["prefill"] = {
             "ms": prefill_ms, "token_heads_per_s": B * T * H / (prefill_ms / 1e3),
             "algo": args.prefill_algo,
-            "roofline": {"kernel": "wkv7 chunked_kernel<epilogue>" if chunked else
-                         "wkv7 scan_kernel<bf16, epilogue>",
+            "roofline": {"kernel": ("wkv7 chunked prefill (all its launches)" if chunked else
+                                    "wkv7 scan_kernel<bf16>"),
                          "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                          "bytes_per_launch": p_bytes},
         }
-        if chunked:
+        if chunked and not long_shape:
             # executed MFMA work per launch is fixed by the kernel (counted once with
             # SQ_INSTS_VALU_MFMA_MOPS_BF16); divided by the live duration it gives the
             # MFMA utilisation against the 2.5 PFLOP/s dense bf16 peak
@@ -333,7 +354,8 @@ def main():
     if do_prefill and not args.no_cpu_baseline:
         sub = [px.as_f64(n) for n in NAMES]
         t0 = time.perf_counter()
-        y_ref, s_ref = oracle.forward(*sub, s0=None, epilogue=px["epi"], threads=threads)
+        y_ref, s_ref = oracle.forward(*sub, s0=None, epilogue=px["epi"] if p_with_epi else None,
+                                      threads=threads)
         cpu_s += time.perf_counter() - t0
         cpu_work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
         del sub
@@ -368,7 +390,8 @@ def main():
             "kind": "oracle",
             "sample": (f"fp64 C oracle ({cpu_model()}, {threads} threads) over {cpu_work} "
                        f"token*heads in {cpu_s:.2f} s: "
-                       + ("the whole prefill batch (B8 T4096 H40 with epilogue)"
+                       + (f"the whole prefill batch (B{PREFILL['B']} T{PREFILL['T']} "
+                          f"H{PREFILL['H']}{' with epilogue' if p_with_epi else ''})"
                           if do_prefill else "")
                        + (" and " if do_prefill and do_decode else "")
                        + (f"the full decode runs of {len(samp_l)} layers" if do_decode else "")),
