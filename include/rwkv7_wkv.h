@@ -138,6 +138,55 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
                               int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
                               void *stream);
 
+/* ---------------------------------------------------------------------------
+ * Training path: forward with state storage, and the backward pass.
+ * Source: RWKV-7 "Goose" summary, §8 Speed and Memory (forward inference with
+ * state storage, then a backward computation); RWKV-7 "Goose" author response
+ * (paperhub), answer on numerical precision (an fp32 gradient kernel and a
+ * faster bf16 chunked one).  The pages give timings and error levels, not the
+ * algorithm: the states stored here are the fp32 states at every 16th token,
+ * and the backward recomputes the states in between from them.
+ * ------------------------------------------------------------------------- */
+
+/* Tokens between stored states. */
+#define RWKV7_CKPT_INTERVAL 16
+
+/*
+ * rwkv7_wkv_forward without epilogue (the normalisation and bonus are separate
+ * operations when training) that also stores
+ *   s_ckpt : [B,H,C,N,N] float32, C = ceil(T / RWKV7_CKPT_INTERVAL):
+ *            s_ckpt[b,h,c] = the state before token 16c (c = 0: s0, or zeros)
+ * All other arguments, the workspace and the errors are those of
+ * rwkv7_wkv_forward (query the workspace with rwkv7_wkv_forward_workspace).
+ * s_ckpt must not overlap any other argument; it may be NULL only when T == 0.
+ */
+rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k,
+                                     const void *v, const void *kappa, const void *a,
+                                     const float *s0, void *y, float *s_out, float *s_ckpt,
+                                     int B, int T, int H, int N, rwkv7_dtype dt,
+                                     rwkv7_algo algo, void *workspace, size_t workspace_bytes,
+                                     void *stream);
+
+/*
+ * Gradients of L = sum_t <y_t, dy_t> + <S_T, ds_T> with respect to the inputs
+ * of rwkv7_wkv_forward_train (without epilogue):
+ *   r, w, k, v, kappa, a : [B,T,H,N] in dt, the forward's inputs
+ *   dy     : [B,T,H,N] in dt, the cotangent of y
+ *   s_ckpt : [B,H,C,N,N] float32 from rwkv7_wkv_forward_train on these inputs
+ *   ds_T   : [B,H,N,N] float32 cotangent of the final state, or NULL (zero)
+ *   dr, dw, dk, dv, dkappa, da : [B,T,H,N] in dt (outputs)
+ *   ds0    : [B,H,N,N] float32 gradient for s0 (output), or NULL to skip it;
+ *            may equal ds_T (in place)
+ * Computed in fp32 (states recomputed from s_ckpt, token by token), rounded
+ * once to dt.  The six gradient outputs must not overlap each other or any
+ * input.  T == 0: ds0 receives ds_T (or zeros).
+ */
+rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v,
+                                const void *kappa, const void *a, const void *dy,
+                                const float *s_ckpt, const float *ds_T, void *dr, void *dw,
+                                void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
+                                int T, int H, int N, rwkv7_dtype dt, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *rwkv7_status_str(rwkv7_status s);
 

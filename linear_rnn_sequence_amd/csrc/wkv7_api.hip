@@ -97,11 +97,16 @@ size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt, r
     return chunked_workspace_bytes(B, T, H);
 }
 
-rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, const void *v,
-                               const void *kappa, const void *a, const float *s0, void *y,
-                               float *s_out, int B, int T, int H, int N, rwkv7_dtype dt,
-                               rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
-                               size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+// rwkv7_wkv_forward, and with s_ckpt (training forward, no epilogue) the
+// states before every kCkpt-th token as well.
+static rwkv7_status forward_impl(const void *r, const void *w, const void *k, const void *v,
+                                 const void *kappa, const void *a, const float *s0, void *y,
+                                 float *s_out, float *s_ckpt, bool want_ckpt, int B, int T,
+                                 int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                 const rwkv7_epilogue *epi, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
     if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
@@ -119,18 +124,23 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+    size_t ck = st;  // bytes of the stored states
+    if (want_ckpt && !mul_ok(ck, (size_t)((T + kCkpt - 1) / kCkpt))) return RWKV7_ERR_SHAPE;
 
     const void *ins[6] = {r, w, k, v, kappa, a};
     if (T > 0) {
         for (const void *p : ins)
             if (!p) return RWKV7_ERR_NULL;
         if (!y) return RWKV7_ERR_NULL;
+        if (want_ckpt && !s_ckpt) return RWKV7_ERR_NULL;
     }
+    if (!want_ckpt || T == 0) s_ckpt = nullptr;
     rwkv7_status es = check_epilogue(epi);
     if (es != RWKV7_OK) return es;
     for (const void *p : ins)
         if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
-    if ((y && !aligned16(y)) || (s0 && !aligned16(s0)) || (s_out && !aligned16(s_out)))
+    if ((y && !aligned16(y)) || (s0 && !aligned16(s0)) || (s_out && !aligned16(s_out)) ||
+        (s_ckpt && !aligned16(s_ckpt)))
         return RWKV7_ERR_ALIGN;
 
     // outputs may not overlap inputs (s_out == s0 exactly is the in-place case)
@@ -163,6 +173,14 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
                 return RWKV7_ERR_ALIAS;
         }
     }
+    if (s_ckpt) {
+        const Range rc = rng(s_ckpt, ck);
+        for (const void *p : ins)
+            if (overlap(rc, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        if (overlap(rc, rng(y, tok)) || (s0 && overlap(rc, rng(s0, st))) ||
+            (s_out && overlap(rc, rng(s_out, st))))
+            return RWKV7_ERR_ALIAS;
+    }
     const size_t need = rwkv7_wkv_forward_workspace(B, T, H, N, dt, al);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return RWKV7_ERR_WORKSPACE;
@@ -171,7 +189,7 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
         for (const void *p : ins)
             if (overlap(rw, rng(p, tok))) return RWKV7_ERR_ALIAS;
         if (overlap(rw, rng(y, tok)) || (s0 && overlap(rw, rng(s0, st))) ||
-            (s_out && overlap(rw, rng(s_out, st))))
+            (s_out && overlap(rw, rng(s_out, st))) || (s_ckpt && overlap(rw, rng(s_ckpt, ck))))
             return RWKV7_ERR_ALIAS;
     }
 
@@ -190,8 +208,106 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
     p.epi = to_epi(epi);
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
+    p.s_ckpt = s_ckpt;
     const hipError_t e = al == RWKV7_ALGO_CHUNKED ? launch_chunked(p, hs) : launch_scan(p, hs);
     return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+}
+
+extern "C" {
+
+rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, const void *v,
+                               const void *kappa, const void *a, const float *s0, void *y,
+                               float *s_out, int B, int T, int H, int N, rwkv7_dtype dt,
+                               rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, nullptr, false, B, T, H, N, dt, algo,
+                        epi, workspace, workspace_bytes, stream);
+}
+
+rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k,
+                                     const void *v, const void *kappa, const void *a,
+                                     const float *s0, void *y, float *s_out, float *s_ckpt,
+                                     int B, int T, int H, int N, rwkv7_dtype dt,
+                                     rwkv7_algo algo, void *workspace, size_t workspace_bytes,
+                                     void *stream) {
+    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, s_ckpt, true, B, T, H, N, dt, algo,
+                        nullptr, workspace, workspace_bytes, stream);
+}
+
+rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v,
+                                const void *kappa, const void *a, const void *dy,
+                                const float *s_ckpt, const float *ds_T, void *dr, void *dw,
+                                void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
+                                int T, int H, int N, rwkv7_dtype dt, void *stream) {
+    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
+    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    size_t tok = 1, st = 1;
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
+        !mul_ok(tok, (size_t)N) || !mul_ok(tok, esz))
+        return RWKV7_ERR_SHAPE;
+    if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
+        return RWKV7_ERR_SHAPE;
+    size_t ck = st;
+    if (!mul_ok(ck, (size_t)((T + kCkpt - 1) / kCkpt))) return RWKV7_ERR_SHAPE;
+    if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+
+    const void *ins[7] = {r, w, k, v, kappa, a, dy};
+    void *outs[6] = {dr, dw, dk, dv, dkappa, da};
+    if (T > 0) {
+        for (const void *p : ins)
+            if (!p) return RWKV7_ERR_NULL;
+        for (const void *p : outs)
+            if (!p) return RWKV7_ERR_NULL;
+        if (!s_ckpt) return RWKV7_ERR_NULL;
+    }
+    for (const void *p : ins)
+        if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
+    for (const void *p : outs)
+        if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
+    if ((s_ckpt && !aligned16(s_ckpt)) || (ds_T && !aligned16(ds_T)) || (ds0 && !aligned16(ds0)))
+        return RWKV7_ERR_ALIGN;
+
+    // outputs overlap neither each other nor an input (ds0 == ds_T is the in-place case)
+    auto rng = [](const void *p, size_t n) {
+        return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
+    };
+    if (T > 0) {
+        for (int o = 0; o < 6; ++o) {
+            const Range ro = rng(outs[o], tok);
+            for (const void *p : ins)
+                if (overlap(ro, rng(p, tok))) return RWKV7_ERR_ALIAS;
+            for (int o2 = o + 1; o2 < 6; ++o2)
+                if (overlap(ro, rng(outs[o2], tok))) return RWKV7_ERR_ALIAS;
+            if (overlap(ro, rng(s_ckpt, ck)) || (ds_T && overlap(ro, rng(ds_T, st))) ||
+                (ds0 && overlap(ro, rng(ds0, st))))
+                return RWKV7_ERR_ALIAS;
+        }
+    }
+    if (ds0) {
+        const Range rd = rng(ds0, st);
+        if (T > 0) {
+            for (const void *p : ins)
+                if (overlap(rd, rng(p, tok))) return RWKV7_ERR_ALIAS;
+            if (overlap(rd, rng(s_ckpt, ck))) return RWKV7_ERR_ALIAS;
+        }
+        if (ds_T && ds_T != ds0 && overlap(rd, rng(ds_T, st))) return RWKV7_ERR_ALIAS;
+    }
+
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    if (T == 0) {
+        if (!ds0 || ds0 == ds_T) return RWKV7_OK;
+        return launch_state_copy(ds_T, ds0, st / 4, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+    }
+    BackwardArgs p{};
+    p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a; p.dy = dy;
+    p.s_ckpt = s_ckpt; p.ds_T = ds_T;
+    p.dr = dr; p.dw = dw; p.dk = dk; p.dv = dv; p.dkappa = dkappa; p.da = da;
+    p.ds0 = ds0;
+    p.B = B; p.T = T; p.H = H;
+    p.bf16 = dt == RWKV7_DT_BF16;
+    return launch_backward(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
 rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const void *v,

@@ -393,6 +393,11 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                                       : cp.ws_sin + sidx * kN * kN);
     float *s_fin = SUMMARY ? (p_rows ? cp.ws_p : cp.ws_ds) + sidx * kN * kN
                  : (seg == cp.nseg - 1 && p.s_out ? p.s_out + (long)bh * kN * kN : nullptr);
+    // stored states (training forward): chunk c of this range is global chunk t0/kC + c
+    static_assert(kC == kCkpt, "a chunk is one checkpoint interval");
+    float *ckpt = (!SUMMARY && p.s_ckpt)
+                      ? p.s_ckpt + ((long)bh * ((p.T + kC - 1) / kC) + t0 / kC) * kN * kN
+                      : nullptr;
 
     if (chain_wave) {
         // ---------------- chain waves: state, MFMA chain, readouts ----------------
@@ -425,6 +430,13 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 ylane += ystep;
             }
             if (c < nch) {
+                if (ckpt) {  // the state before this chunk
+                    float *ck = ckpt + (long)c * kN * kN + srow + 4 * g;
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+                        *reinterpret_cast<float4 *>(ck + 16 * jb) =
+                            make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+                }
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
                 bf16x4 Zb[4];

@@ -53,6 +53,30 @@ struct F32In {
     static __device__ __forceinline__ void store1(float *p, float x) { *p = x; }
 };
 
+// Raw 4-element loads kept in flight in registers (prefetch), widened later.
+template <class IO>
+struct RawLoad;
+template <>
+struct RawLoad<Bf16In> {
+    using T = uint2;
+    static __device__ __forceinline__ T load(const void *p, long off) {
+        return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + off);
+    }
+    static __device__ __forceinline__ float4 widen(T u) {
+        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
+    }
+    static __device__ __forceinline__ T zero() { return make_uint2(0u, 0u); }
+};
+template <>
+struct RawLoad<F32In> {
+    using T = float4;
+    static __device__ __forceinline__ T load(const void *p, long off) {
+        return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + off);
+    }
+    static __device__ __forceinline__ float4 widen(T u) { return u; }
+    static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
+};
+
 // ---------------------------------------------------------------------------
 // Cross-lane sums with DPP (no LDS traffic).  Lanes are grouped in DPP "rows"
 // of 16; quad_perm swaps within groups of 4, row_half_mirror reverses each

@@ -31,6 +31,20 @@ struct ForwardArgs {
     EpilogueArgs epi;
     void *workspace;
     size_t workspace_bytes;
+    float *s_ckpt;  // [B,H,ceil(T/kCkpt),N,N]: state before every kCkpt-th token, or nullptr
+};
+
+constexpr int kCkpt = RWKV7_CKPT_INTERVAL;  // tokens between stored states
+
+struct BackwardArgs {
+    const void *r, *w, *k, *v, *kappa, *a;  // [B,T,H,N] in dt (forward inputs)
+    const void *dy;                         // [B,T,H,N] in dt
+    const float *s_ckpt;                    // [B,H,ceil(T/kCkpt),N,N]
+    const float *ds_T;                      // [B,H,N,N] or nullptr (zero)
+    void *dr, *dw, *dk, *dv, *dkappa, *da;  // [B,T,H,N] in dt
+    float *ds0;                             // [B,H,N,N] or nullptr
+    int B, T, H;
+    bool bf16;
 };
 
 struct DecodeArgs {
@@ -49,6 +63,7 @@ hipError_t launch_scan(const ForwardArgs &p, hipStream_t stream);
 hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream);
 size_t chunked_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
+hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
 // S_T for T == 0: copy s0 (or zeros) into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream);
 

@@ -40,29 +40,6 @@ struct __align__(16) ScanStage {
     float ybuf[kTC][kN];
 };
 
-template <class IO>
-struct RawLoad;
-template <>
-struct RawLoad<Bf16In> {
-    using T = uint2;
-    static __device__ __forceinline__ T load(const void *p, long off) {
-        return *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p) + off);
-    }
-    static __device__ __forceinline__ float4 widen(T u) {
-        return make_float4(bf16_lo(u.x), bf16_hi(u.x), bf16_lo(u.y), bf16_hi(u.y));
-    }
-    static __device__ __forceinline__ T zero() { return make_uint2(0u, 0u); }
-};
-template <>
-struct RawLoad<F32In> {
-    using T = float4;
-    static __device__ __forceinline__ T load(const void *p, long off) {
-        return *reinterpret_cast<const float4 *>(static_cast<const float *>(p) + off);
-    }
-    static __device__ __forceinline__ float4 widen(T u) { return u; }
-    static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
-};
-
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }
@@ -130,9 +107,20 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
     };
 
     const int nchunks = (T + kTC - 1) / kTC;
+    static_assert(kTC == kCkpt, "a staging round is one checkpoint interval");
     issue(0);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int tl = min(kTC, T - ch * kTC);
+        if (p.s_ckpt) {  // the state before token ch * kTC
+            float *ck = p.s_ckpt + ((long)bh * nchunks + ch) * kN * kN;
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                *reinterpret_cast<float4 *>(ck + (i0 + r) * kN + j0) =
+                    make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
+                *reinterpret_cast<float4 *>(ck + (i0 + r) * kN + j0 + 4) =
+                    make_float4(S[r][4], S[r][5], S[r][6], S[r][7]);
+            }
+        }
         // ---- stage this chunk's vectors ----
         const float4 r4 = L::widen(xr), w4 = L::widen(xw), k4 = L::widen(xk);
         const float4 v4 = L::widen(xv), kap4 = L::widen(xkap), a4 = L::widen(xa);

@@ -55,6 +55,10 @@ def lib():
         L.rwkv7_wkv_forward_workspace.restype = sz
         L.rwkv7_wkv_decode.argtypes = [vp] * 8 + [ci] * 4 + [ctypes.POINTER(Epilogue), vp]
         L.rwkv7_wkv_decode.restype = ci
+        L.rwkv7_wkv_forward_train.argtypes = [vp] * 10 + [ci] * 6 + [vp, sz, vp]
+        L.rwkv7_wkv_forward_train.restype = ci
+        L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [ci] * 5 + [vp]
+        L.rwkv7_wkv_backward.restype = ci
         L.rwkv7_status_str.argtypes = [ci]
         L.rwkv7_status_str.restype = ctypes.c_char_p
         L.rwkv7_abi_version.argtypes = []
@@ -147,6 +151,61 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_forward")
     return y, s_out
+
+
+CKPT_INTERVAL = 16  # RWKV7_CKPT_INTERVAL
+
+
+def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=None,
+                  s_ckpt=None, want_state=True, workspace=None, stream=None):
+    """rwkv7_wkv_forward_train (no epilogue).  Returns (y, s_out, s_ckpt) with
+    s_ckpt [B,H,ceil(T/16),N,N] f32, the state before every 16th token."""
+    import torch
+
+    B, T, H, N = r.shape
+    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    if y is None:
+        y = torch.empty_like(r)
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    if s_ckpt is None:
+        nck = (T + CKPT_INTERVAL - 1) // CKPT_INTERVAL
+        s_ckpt = torch.empty((B, H, nck, N, N), dtype=torch.float32, device=r.device)
+    need = lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo])
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=r.device)
+    code = lib().rwkv7_wkv_forward_train(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(s0), _ptr(y),
+        _ptr(s_out), _ptr(s_ckpt), B, T, H, N, dt, ALGOS[algo], _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(torch, stream))
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_forward_train")
+    return y, s_out, s_ckpt
+
+
+def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=None,
+             want_ds0=True, stream=None):
+    """rwkv7_wkv_backward.  Returns (dr, dw, dk, dv, dkappa, da, ds0): the gradients of
+    sum_t <y_t, dy_t> + <S_T, ds_T> for the inputs of :func:`forward_train`.  ``grads``
+    may pass the six output tensors; ``ds0`` may be ``ds_T`` (in place)."""
+    import torch
+
+    B, T, H, N = r.shape
+    _check_same(torch, (r, w, k, v, kappa, a, dy), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    if grads is None:
+        grads = tuple(torch.empty_like(r) for _ in range(6))
+    if ds0 is None and want_ds0:
+        ds0 = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    code = lib().rwkv7_wkv_backward(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(dy), _ptr(s_ckpt),
+        _ptr(ds_T), *(_ptr(g) for g in grads), _ptr(ds0), B, T, H, N, dt,
+        _stream(torch, stream))
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_backward")
+    return (*grads, ds0)
 
 
 def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):

@@ -178,6 +178,23 @@ def draw(
     return out
 
 
+def cotangents(B: int, T: int, H: int, N: int = N_HEAD_SIZE, *, seed: int,
+               dtype: str = "bf16", with_state: bool = True, std: float = 1.0):
+    """Output cotangents for the training path: dy [B,T,H,N] ~ N(0, std) stored in
+    ``dtype`` (bf16 bits or float32) and, if ``with_state``, ds_T [B,H,N,N] ~ N(0, std)
+    float32.  numpy PCG64 ``default_rng(seed)``, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    dy = (rng.standard_normal((B, T, H, N), dtype=f32) * f32(std)).astype(f32)
+    ds_T = ((rng.standard_normal((B, H, N, N), dtype=f32) * f32(std)).astype(f32)
+            if with_state else None)
+    if dtype == "bf16":
+        dy = f32_to_bf16_bits(dy)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return dy, ds_T
+
+
 # ---------------------------------------------------------------------------
 # the five workloads (sizes of the 0.19B..2.9B model shapes, head size 64)
 # ---------------------------------------------------------------------------

@@ -114,3 +114,48 @@ def test_workspace_query_segments():
     assert L.rwkv7_wkv_forward_workspace(64, 65536, 64, 64, 1, 2) == 0
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 1) == 0
     assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 4 * per_seg  # 1024 tokens each
+
+
+def fwd_train(B=2, T=8, H=3, N=64, dt=1, algo=1, s0=fake(6), y=fake(7), s_out=fake(8),
+              ck=fake(9), ins=None):
+    ins = ins or [fake(i) for i in range(6)]
+    return wkv.lib().rwkv7_wkv_forward_train(*ins, s0, y, s_out, ck, B, T, H, N, dt, algo, None,
+                                             0, None)
+
+
+def test_forward_train_validation_codes():
+    assert fwd_train(N=32) == 4
+    assert fwd_train(B=0) == 2 and fwd_train(T=-1) == 2
+    assert fwd_train(ck=None) == 1                   # stored states required
+    assert fwd_train(ck=fake(9, 8)) == 5             # misaligned
+    assert fwd_train(ck=fake(6)) == 6                # on top of s0
+    assert fwd_train(ck=fake(0, 64)) == 6            # inside r
+    assert fwd_train(y=fake(9, 4096)) == 6           # y inside the stored states
+    assert fwd_train(dt=0, algo=2) == 4              # chunked needs bf16
+    # T == 0 stores nothing: no stored-state buffer needed (s_out NULL: nothing to do)
+    assert fwd_train(T=0, ck=None, s_out=None) == 0
+
+
+def bwd(B=2, T=8, H=3, N=64, dt=1, ins=None, dy=fake(6), ck=fake(7), dsT=fake(8), outs=None,
+        ds0=fake(15)):
+    ins = ins or [fake(i) for i in range(6)]
+    outs = outs or [fake(9 + i) for i in range(6)]
+    return wkv.lib().rwkv7_wkv_backward(*ins, dy, ck, dsT, *outs, ds0, B, T, H, N, dt, None)
+
+
+def test_backward_validation_codes():
+    assert bwd(N=128) == 4
+    assert bwd(B=0) == 2 and bwd(H=0) == 2 and bwd(T=-1) == 2
+    assert bwd(dt=7) == 3
+    assert bwd(dy=None) == 1 and bwd(ck=None) == 1
+    assert bwd(outs=[fake(9 + i) for i in range(5)] + [None]) == 1
+    assert bwd(ins=[fake(i) for i in range(5)] + [None]) == 1
+    assert bwd(dy=fake(6, 2)) == 5
+    assert bwd(ds0=fake(15, 4)) == 5
+    assert bwd(outs=[fake(9)] * 6) == 6                            # outputs overlap
+    assert bwd(outs=[fake(9 + i) for i in range(5)] + [fake(0)]) == 6   # da on top of r
+    assert bwd(ds0=fake(7, 64)) == 6                              # ds0 inside the states
+    assert bwd(ds0=fake(8, 16)) == 6                              # ds0 partly over ds_T
+    # ds0 == ds_T is the in-place case: passes validation (T == 0 then has nothing to do)
+    assert bwd(T=0, ds0=fake(8), dsT=fake(8), ck=None, dy=None) == 0
+    assert bwd(T=0, ds0=None, ck=None) == 0
