@@ -44,7 +44,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "train"], default="all",
+                    help="'train': the training step (forward with stored states + backward) "
+                         "on the 2.9B prefill shape, printed as its own line")
     ap.add_argument("--decode-steps", type=int, default=DECODE["steps"],
                     help="tokens per decode run (default 64)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -112,6 +114,125 @@ def cpu_model():
     return platform.processor() or "unknown"
 
 
+# fp32 VALU peak without packed math (the kernels are built with packed fp32
+# disabled): 256 CUs x 4 SIMDs x 16 lanes x 2 flop (FMA) x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
+# backward flops per token-head: the gradient recurrence (G += dy r^T, the
+# column sums dr, dk, db, dw, S^T du, the row sums dv, du: 2N^2 each; the
+# cotangent update G diag(w) + du kappa^T: 3N^2) plus one forward recompute of
+# the states (probe 2N^2, update 5N^2)
+BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
+
+
+def bench_train(args, torch, wkv, synth, dev):
+    """Training step on the 2.9B prefill shape (no epilogue): forward with stored
+    states + backward, inputs and cotangents resident before timing."""
+    B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
+    px = synth.config_inputs(2)
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    ins = [bf(px[n]) for n in NAMES]
+    dy_bits, ds_T = synth.cotangents(B, T, H, seed=102, dtype="bf16")
+    dy, dst = bf(dy_bits), torch.from_numpy(ds_T).to(dev)
+    ws_bytes = wkv.forward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(ins[0])
+    s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
+    ck = torch.empty((B, H, (T + 15) // 16, N, N), dtype=torch.float32, device=dev)
+    grads = tuple(torch.empty_like(ins[0]) for _ in range(6))
+    ds0 = torch.empty_like(s_out)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        wkv.forward_train(*ins, algo=args.prefill_algo, y=y, s_out=s_out, s_ckpt=ck,
+                          workspace=ws)
+
+    def bwd():
+        wkv.backward(*ins, dy, ck, dst, grads=grads, ds0=ds0)
+
+    for wi in range(args.warmup):
+        fwd()
+        bwd()
+        if wi == 0:
+            torch.cuda.synchronize()
+            g_first = [g.float().cpu().numpy() for g in grads] + [ds0.cpu().numpy()]
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        fwd()
+        bwd()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / max(args.steps, 1)
+    # each half alone, events on the launch stream around single calls
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(3)]
+    for e in ev:
+        e[0].record(stream)
+        fwd()
+        e[1].record(stream)
+        e[2].record(stream)
+        bwd()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = float(np.median([e[0].elapsed_time(e[1]) for e in ev]))
+    bwd_ms = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
+
+    work = B * T * H
+    bwd_flops = work * BWD_FLOPS_PER_TOKEN_HEAD
+    tf = bwd_flops / (bwd_ms / 1e3) / 1e12
+    nck = (T + 15) // 16
+    fwd_bytes = work * 7 * N * 2 + B * H * N * N * 4 * (1 + nck)
+    bwd_bytes = work * 13 * N * 2 + B * H * N * N * 4 * (2 + nck)
+    src = source_hash("wkv7_backward.hip", "wkv7_device.h")
+    out = {
+        "metric": "WKV7 training tokens x heads per second (forward with stored states + backward)",
+        "value": work / (ms_per_step / 1e3),
+        "unit": "token*heads/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; recipes of the pages' parameterisations)",
+        "config": {"workload": ("2.9B-shape WKV7 training step: forward with fp32 states stored "
+                                "every 16 tokens, then backward to r, w, k, v, kappa, a, S0; "
+                                "B8 T4096 H40 N64, no epilogue"),
+                   "B": B, "T": T, "H": H, "N": N, "forward_algo": args.prefill_algo,
+                   "state_dtype": "f32"},
+        "roofline": {"kernel": "wkv7 backward_kernel<bf16>", "bound": "alu",
+                     "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / FP32_VALU_PEAK_TFLOPS,
+                     "traffic": read_traffic("backward_kernel_traffic_b8_t4096_h40.txt", src),
+                     "flops_per_launch": bwd_flops, "avg_launch_us": bwd_ms * 1e3,
+                     "hbm_GBps_algorithmic": bwd_bytes / (bwd_ms / 1e3) / 1e9},
+        "forward_train": {"ms": fwd_ms, "bytes_per_launch": fwd_bytes,
+                          "hbm_GBps": fwd_bytes / (fwd_ms / 1e3) / 1e9},
+        "backward_ms": bwd_ms,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import grad as og
+
+        b_idx, h_idx = [0, 7], [3, 39]
+        dy64 = synth.bf16_bits_to_f32(dy_bits).astype(np.float64)
+        t0 = time.perf_counter()
+        ref = og.backward(*(px.as_f64(n) for n in NAMES), dy64, s0=None,
+                          ds_T=ds_T.astype(np.float64), b_idx=b_idx, h_idx=h_idx)
+        cpu_s = time.perf_counter() - t0
+        errs = {}
+        for n, g in zip(NAMES + ("s0",), g_first):
+            got = g[np.asarray(b_idx)]
+            got = got[:, :, h_idx] if n != "s0" else got[:, h_idx]
+            errs["d" + n] = float(np.abs(got - ref[n]).max() / np.abs(ref[n]).max())
+        out["parity_sampled"] = dict(errs, bound=2e-2, checked=(
+            "every gradient element of (b, h) in {0, 7} x {3, 39}, all 4096 tokens"))
+        cpu_work = len(b_idx) * len(h_idx) * T
+        out["cpu_baseline"] = {
+            "value": cpu_work / cpu_s, "unit": "token*heads/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": (f"float64 autograd gradient oracle ({cpu_model()}, torch CPU, "
+                       f"{torch.get_num_threads()} threads) on 4 (b, h) pairs x 4096 tokens "
+                       f"({cpu_work} token*heads, forward + backward) in {cpu_s:.2f} s"),
+        }
+    print(json.dumps(out))
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -145,6 +266,10 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_probe_bytes_read": 4 * n, "copy_probe_bytes_written": 4 * n,
                           "launches": 3}))
+        return
+
+    if args.only == "train":
+        bench_train(args, torch, wkv, synth, dev)
         return
 
     do_prefill = args.only in ("all", "prefill")
