@@ -148,16 +148,38 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p) {
             issue_ck(c - 1);
         }
 
+        float S4[4][4], S8[4][4];  // the states before tokens 4 and 8
         for (int blk = kNBlk - 1; blk >= 0; --blk) {
             const int t0 = kBlk * blk;
             // ---- recompute: the states before tokens t0 .. t0+3 ----
+            // (the last block walks from the stored state and keeps the states
+            // before tokens 4 and 8 for the blocks after it)
             float S[4][4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int q = 0; q < 4; ++q) S[e][q] = C0[e][q];
             float u[kBlk][4];
-            for (int t = 0; t < t0; ++t) step(S, t, u[0]);
+            if (blk == kNBlk - 1) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) S[e][q] = C0[e][q];
+                for (int t = 0; t < 4; ++t) step(S, t, u[0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) S4[e][q] = S[e][q];
+                for (int t = 4; t < 8; ++t) step(S, t, u[0]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) S8[e][q] = S[e][q];
+                for (int t = 8; t < 12; ++t) step(S, t, u[0]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        S[e][q] = blk == 2 ? S8[e][q] : (blk == 1 ? S4[e][q] : C0[e][q]);
+            }
+            static_assert(kNBlk == 4, "the walk above keeps the states of blocks 1 and 2");
             float Sp[kBlk][4][4];
 #pragma unroll
             for (int tt = 0; tt < kBlk; ++tt) {
@@ -228,16 +250,12 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p) {
                 for (int e = 0; e < 4; ++e)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) G[e][q] = G[e][q] * wq[q] + du[e] * kpq[q];
-                // column sums over the wave's 16 rows
+                // column sums over the wave's 16 rows, four columns per register:
+                // lanes of row group rg end with column j0 + kPackedCol[rg]
 #pragma unroll
-                for (int x = 0; x < kNCol; ++x)
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) cs[x][q] = sum_rows4(cs[x][q]);
-                if (rg == 0) {
-#pragma unroll
-                    for (int x = 0; x < kNCol; ++x)
-                        *reinterpret_cast<float4 *>(&sm.col[buf][wave][tt][x][j0]) =
-                            make_float4(cs[x][0], cs[x][1], cs[x][2], cs[x][3]);
+                for (int x = 0; x < kNCol; ++x) {
+                    const float s4 = sum_rows4_packed(cs[x][0], cs[x][1], cs[x][2], cs[x][3]);
+                    sm.col[buf][wave][tt][x][j0 + packed_col(rg)] = s4;
                 }
                 if (cg == 0)
                     *reinterpret_cast<float4 *>(&sm.dv[buf][tt][i0]) =

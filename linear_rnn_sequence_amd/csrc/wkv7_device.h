@@ -120,4 +120,25 @@ __device__ __forceinline__ float sum_rows4(float x) {
     return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Four independent sums over the four DPP rows at the cost of three swaps:
+// v_permlane32_swap pairs (a, b) so that lanes 0..31 add up a and lanes
+// 32..63 add up b over lane bit 5 (likewise (c, d)); v_permlane16_swap then
+// pairs the two results over lane bit 4.  Row 0 of the result holds the total
+// of a, row 1 of c, row 2 of b, row 3 of d (see packed_col).
+__device__ __forceinline__ float swap32_add(float a, float b) {
+    const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b),
+                                                    false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+__device__ __forceinline__ float swap16_add(float a, float b) {
+    const auto h = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b),
+                                                    false, false);
+    return __uint_as_float(h[0]) + __uint_as_float(h[1]);
+}
+__device__ __forceinline__ float sum_rows4_packed(float a, float b, float c, float d) {
+    return swap16_add(swap32_add(a, b), swap32_add(c, d));
+}
+// Which of (a, b, c, d) = operands 0..3 the lanes of DPP row `row` hold.
+__device__ __forceinline__ int packed_col(int row) { return (row & 1) * 2 + (row >> 1); }
+
 }  // namespace wkv7
