@@ -66,7 +66,16 @@ typedef enum {
     RWKV7_ERR_HIP = 8          /* the HIP runtime refused a launch                    */
 } rwkv7_status;
 
-typedef enum { RWKV7_DT_F32 = 0, RWKV7_DT_BF16 = 1 } rwkv7_dtype;
+typedef enum {
+    RWKV7_DT_F32 = 0,      /* every per-token vector (and y) float32                   */
+    RWKV7_DT_BF16 = 1,     /* every per-token vector (and y) bfloat16                  */
+    RWKV7_DT_BF16_W32 = 2  /* bfloat16, except the decay w, which is float32: slow
+                              forgetting (w near 1) survives the input rounding.  The
+                              RWKV-7 "Goose" author response (paperhub) names precision
+                              sensitivity of the kernel; with w in (0.99, 1), bf16 rounds
+                              most decays to exactly 1.  Forward, training forward and
+                              decode; the backward returns RWKV7_ERR_UNSUPPORTED.       */
+} rwkv7_dtype;
 
 typedef enum {
     RWKV7_ALGO_AUTO = 0,    /* CHUNKED for bf16, SCAN for f32                          */

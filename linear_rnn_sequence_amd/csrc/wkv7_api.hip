@@ -84,15 +84,19 @@ const char *rwkv7_status_str(rwkv7_status s) {
     return "unknown status";
 }
 
+static bool valid_dtype(rwkv7_dtype dt) {
+    return dt == RWKV7_DT_F32 || dt == RWKV7_DT_BF16 || dt == RWKV7_DT_BF16_W32;
+}
+
 static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt) {
     if (algo == RWKV7_ALGO_AUTO)
-        return (dt == RWKV7_DT_BF16 && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+        return (dt != RWKV7_DT_F32 && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
     return algo;
 }
 
 size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo) {
     if (B < 1 || H < 1 || T < 0 || N != kN) return 0;
-    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return 0;
+    if (!valid_dtype(dt)) return 0;
     if (resolve_algo(algo, dt) != RWKV7_ALGO_CHUNKED || T == 0) return 0;
     return chunked_workspace_bytes(B, T, H);
 }
@@ -107,20 +111,22 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
                                  int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
                                  const rwkv7_epilogue *epi, void *workspace,
                                  size_t workspace_bytes, void *stream) {
-    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
     const rwkv7_algo al = resolve_algo(algo, dt);
-    if (al == RWKV7_ALGO_CHUNKED && (dt != RWKV7_DT_BF16 || !kChunkedAvailable))
+    if (al == RWKV7_ALGO_CHUNKED && (dt == RWKV7_DT_F32 || !kChunkedAvailable))
         return RWKV7_ERR_UNSUPPORTED;
 
-    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
     if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
-        !mul_ok(tok, (size_t)N) || !mul_ok(tok, esz))
+        !mul_ok(tok, (size_t)N) || !mul_ok(tok, 4))
         return RWKV7_ERR_SHAPE;
+    const size_t tok_w = dt == RWKV7_DT_BF16 ? tok / 2 : tok;  // bytes of w
+    tok = tok / 4 * esz;                                       // bytes of the other vectors
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
@@ -128,6 +134,10 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (want_ckpt && !mul_ok(ck, (size_t)((T + kCkpt - 1) / kCkpt))) return RWKV7_ERR_SHAPE;
 
     const void *ins[6] = {r, w, k, v, kappa, a};
+    auto in_rng = [&](int i) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(ins[i]);
+        return Range{lo, lo + (i == 1 ? tok_w : tok)};
+    };
     if (T > 0) {
         for (const void *p : ins)
             if (!p) return RWKV7_ERR_NULL;
@@ -149,8 +159,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     };
     if (T > 0) {
         const Range ry = rng(y, tok);
-        for (const void *p : ins)
-            if (overlap(ry, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(ry, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (s0 && overlap(ry, rng(s0, st))) return RWKV7_ERR_ALIAS;
         if (s_out && overlap(ry, rng(s_out, st))) return RWKV7_ERR_ALIAS;
         if (epi) {
@@ -163,8 +173,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (s_out) {
         const Range rs = rng(s_out, st);
         if (T > 0)
-            for (const void *p : ins)
-                if (overlap(rs, rng(p, tok))) return RWKV7_ERR_ALIAS;
+            for (int i = 0; i < 6; ++i)
+                if (overlap(rs, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (s0 && s0 != s_out && overlap(rs, rng(s0, st))) return RWKV7_ERR_ALIAS;
         if (epi) {
             const size_t pn = (size_t)H * N * 4;
@@ -175,8 +185,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     }
     if (s_ckpt) {
         const Range rc = rng(s_ckpt, ck);
-        for (const void *p : ins)
-            if (overlap(rc, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(rc, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (overlap(rc, rng(y, tok)) || (s0 && overlap(rc, rng(s0, st))) ||
             (s_out && overlap(rc, rng(s_out, st))))
             return RWKV7_ERR_ALIAS;
@@ -186,8 +196,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
         if (!workspace || workspace_bytes < need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
         const Range rw = rng(workspace, need);
-        for (const void *p : ins)
-            if (overlap(rw, rng(p, tok))) return RWKV7_ERR_ALIAS;
+        for (int i = 0; i < 6; ++i)
+            if (overlap(rw, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (overlap(rw, rng(y, tok)) || (s0 && overlap(rw, rng(s0, st))) ||
             (s_out && overlap(rw, rng(s_out, st))) || (s_ckpt && overlap(rw, rng(s_ckpt, ck))))
             return RWKV7_ERR_ALIAS;
@@ -203,7 +213,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
     p.s0 = s0; p.y = y; p.s_out = s_out;
     p.B = B; p.T = T; p.H = H;
-    p.bf16 = dt == RWKV7_DT_BF16;
+    p.bf16 = dt != RWKV7_DT_F32;
+    p.w32 = dt == RWKV7_DT_BF16_W32;
     p.epilogue = epi != nullptr;
     p.epi = to_epi(epi);
     p.workspace = workspace;
@@ -239,6 +250,7 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
                                 const float *s_ckpt, const float *ds_T, void *dr, void *dw,
                                 void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
                                 int T, int H, int N, rwkv7_dtype dt, void *stream) {
+    if (dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
@@ -314,18 +326,24 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
                               const void *kappa, const void *a, float *state, void *y, int B,
                               int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
                               void *stream) {
-    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1) return RWKV7_ERR_SHAPE;
-    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
-    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)H) || !mul_ok(tok, (size_t)N * esz))
+    if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)H) || !mul_ok(tok, (size_t)N * 4))
         return RWKV7_ERR_SHAPE;
+    const size_t tok_w = dt == RWKV7_DT_BF16 ? tok / 2 : tok;  // bytes of w
+    tok = tok / 4 * esz;                                       // bytes of the other vectors
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     // two waves (workgroups) per head: keep 2*B*H within the grid's x limit
     if ((size_t)B * H > 0x3fffffffu) return RWKV7_ERR_SHAPE;
     const void *ins[6] = {r, w, k, v, kappa, a};
+    auto in_rng = [&](int i) {
+        const uintptr_t lo = reinterpret_cast<uintptr_t>(ins[i]);
+        return Range{lo, lo + (i == 1 ? tok_w : tok)};
+    };
     for (const void *p : ins)
         if (!p) return RWKV7_ERR_NULL;
     if (!state || !y) return RWKV7_ERR_NULL;
@@ -339,8 +357,8 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
     };
     const Range ry = rng(y, tok), rs = rng(state, st);
     if (overlap(ry, rs)) return RWKV7_ERR_ALIAS;
-    for (const void *p : ins)
-        if (overlap(ry, rng(p, tok)) || overlap(rs, rng(p, tok))) return RWKV7_ERR_ALIAS;
+    for (int i = 0; i < 6; ++i)
+        if (overlap(ry, in_rng(i)) || overlap(rs, in_rng(i))) return RWKV7_ERR_ALIAS;
     if (epi) {
         const size_t pn = (size_t)H * N * 4;
         const void *ps[3] = {epi->r_k, epi->ln_w, epi->ln_b};
@@ -350,7 +368,8 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
     DecodeArgs p{};
     p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
     p.state = state; p.y = y; p.B = B; p.H = H;
-    p.bf16 = dt == RWKV7_DT_BF16;
+    p.bf16 = dt != RWKV7_DT_F32;
+    p.w32 = dt == RWKV7_DT_BF16_W32;
     p.epilogue = epi != nullptr;
     p.epi = to_epi(epi);
     return launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RWKV7_OK

@@ -143,12 +143,22 @@ __device__ __forceinline__ void st_a(short *tile, int lane, bf16x4 x) {
 
 // Raw inputs of one chunk held by one lane: token t = lane % 16 of the chunk,
 // channels 16w + 4g .. +3 of each of the six vectors (keys for r, w, k, kappa,
-// a; values for v).
+// a; values for v).  W32: the decay arrives as float32.
+template <bool W32>
+struct RawW {
+    using T = uint2;  // four bf16
+};
+template <>
+struct RawW<true> {
+    using T = float4;
+};
+template <bool W32>
 struct Raw {
-    uint2 r, w, k, kap, a, v;
+    uint2 r, k, kap, a, v;
+    typename RawW<W32>::T w;
 };
 
-template <bool EPI>
+template <bool EPI, bool W32>
 struct Chunked {
     const ForwardArgs &p;
     const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
@@ -168,12 +178,15 @@ struct Chunked {
     // flight: the chunk index is clamped to the last chunk and the token index to
     // T-1, which keeps every address inside the tensors; prep() replaces the
     // values of tokens past T.
-    __device__ void load(int c, Raw &x) const {
+    __device__ void load(int c, Raw<W32> &x) const {
         const int cc = min(c, (Tl - 1) / kC);
         const int t = min(cc * kC + lo, Tl - 1);
         const long off = lane_off + (long)(t - lo) * HN;
         x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
-        x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
+        if constexpr (W32)
+            x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + off);
+        else
+            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
         x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
         x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
         x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
@@ -182,17 +195,26 @@ struct Chunked {
 
     // Padding token past T (only in a partial last chunk): no write, no removal,
     // no decay, no readout.
-    __device__ __forceinline__ void pad(int c, Raw &x) const {
+    __device__ __forceinline__ void pad(int c, Raw<W32> &x) const {
         if (c * kC + lo >= Tl) {
             x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
-            x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
+            if constexpr (W32)
+                x.w = make_float4(1.f, 1.f, 1.f, 1.f);
+            else
+                x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
         }
     }
 
     // Chunk operands for key block jb = blk, written to LDS buffer `o`.
-    __device__ void prep(const Raw &x, ChunkOps &o, const float (&rk)[4]) const {
+    __device__ void prep(const Raw<W32> &x, ChunkOps &o, const float (&rk)[4]) const {
         const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
-        const float w[4] = {bf16_lo(x.w.x), bf16_hi(x.w.x), bf16_lo(x.w.y), bf16_hi(x.w.y)};
+        float w[4];
+        if constexpr (W32) {
+            w[0] = x.w.x; w[1] = x.w.y; w[2] = x.w.z; w[3] = x.w.w;
+        } else {
+            w[0] = bf16_lo(x.w.x); w[1] = bf16_hi(x.w.x);
+            w[2] = bf16_lo(x.w.y); w[3] = bf16_hi(x.w.y);
+        }
         const float k[4] = {bf16_lo(x.k.x), bf16_hi(x.k.x), bf16_lo(x.k.y), bf16_hi(x.k.y)};
         const float kp[4] = {bf16_lo(x.kap.x), bf16_hi(x.kap.x), bf16_lo(x.kap.y),
                              bf16_hi(x.kap.y)};
@@ -328,8 +350,8 @@ struct Pending {
     bf16x4 v;
 };
 
-template <bool EPI>
-__device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI> &K,
+template <bool EPI, bool W32>
+__device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI, W32> &K,
                                                 const ChunkSmem &sm, const Pending &pd, int c,
                                                 float lnw, float lnb, uint16_t *y) {
     const int g = K.g;
@@ -370,7 +392,7 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
 // SUMMARY = true: for each (b, h, segment) but the last, the segment's offset
 //   dS (waves 0..3: entry state 0) and transition P (waves 8..11: entry state I,
 //   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
-template <bool EPI, bool SUMMARY>
+template <bool EPI, bool SUMMARY, bool W32>
 __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_kernel(
     ChunkedParams cp) {
     __shared__ ChunkSmem sm;
@@ -379,7 +401,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
     const int seg = blockIdx.x - bh * cp.nseg_launch;
     const int b = bh / p.H, h = bh - b * p.H;
     const int t0 = seg * cp.seg_len;
-    const Chunked<EPI> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
+    const Chunked<EPI, W32> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
     const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
     const int wave = threadIdx.x >> 6;
     const bool chain_wave = wave < 4 || wave >= 8;  // waves 0..3 (and 8..11 in SUMMARY)
@@ -426,7 +448,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
             if (!SUMMARY && c > 0) {
-                finish_readouts<EPI>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
+                finish_readouts<EPI, W32>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
                 ylane += ystep;
             }
             if (c < nch) {
@@ -497,7 +519,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
         // raw inputs of the next kPrefetch chunks stay in flight in a register ring;
         // interval q (q = 0 .. nch + 2) prepares chunk q and forms chunk q-1's matrices
-        Raw xs[kPrefetch];
+        Raw<W32> xs[kPrefetch];
 #pragma unroll
         for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
         for (int q0 = 0; q0 < nch + 3; q0 += kPrefetch) {
@@ -631,10 +653,9 @@ size_t chunked_workspace_bytes(int B, int T, int H) {
     return (size_t)3 * B * H * nseg * kN * kN * sizeof(float);
 }
 
-hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
-    ChunkedParams cp{};
-    cp.p = p;
-    segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
+template <bool W32>
+hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
+    const ForwardArgs &p = cp.p;
     const long bh = (long)p.B * p.H;
     if (cp.nseg > 1) {
         const size_t slab = (size_t)bh * cp.nseg * kN * kN;
@@ -643,8 +664,9 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
         cp.ws_sin = cp.ws_ds + slab;
         // 1. transitions and offsets of every segment but the last
         cp.nseg_launch = cp.nseg - 1;
-        hipLaunchKernelGGL((chunked_kernel<false, true>), dim3((unsigned)(bh * cp.nseg_launch)),
-                           dim3(kThreadsSummary), 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<false, true, W32>),
+                           dim3((unsigned)(bh * cp.nseg_launch)), dim3(kThreadsSummary), 0,
+                           stream, cp);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         // 2. entry state of every segment
@@ -657,10 +679,17 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
     cp.nseg_launch = cp.nseg;
     const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32>), grid, block, 0, stream, cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false, false>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32>), grid, block, 0, stream, cp);
     return hipGetLastError();
+}
+
+hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
+    ChunkedParams cp{};
+    cp.p = p;
+    segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
+    return p.w32 ? launch_chunked_w<true>(cp, stream) : launch_chunked_w<false>(cp, stream);
 }
 
 }  // namespace wkv7

@@ -63,7 +63,7 @@ __device__ __forceinline__ void load8(const float *p, float *out) {
     }
 }
 
-template <class IO, bool EPI, bool NT>
+template <class IO, bool EPI, bool NT, bool W32>
 __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     using E = typename IO::elem;
     __shared__ float2 xch[2];  // epilogue: (mean, M2) of each half head
@@ -83,7 +83,8 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     const long vo = head * kN;
     const E *pr = static_cast<const E *>(p.r) + vo;
     const float4 kap = IO::load4(static_cast<const E *>(p.kappa) + vo + 4 * c);
-    const float4 w = IO::load4(static_cast<const E *>(p.w) + vo + 4 * c);
+    const float4 w = W32 ? F32In::load4(static_cast<const float *>(p.w) + vo + 4 * c)
+                         : IO::load4(static_cast<const E *>(p.w) + vo + 4 * c);
     const float4 a = IO::load4(static_cast<const E *>(p.a) + vo + 4 * c);
     const float4 k = IO::load4(static_cast<const E *>(p.k) + vo + 4 * c);
     const float4 r = IO::load4(pr + 4 * c);
@@ -166,16 +167,27 @@ hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream) {
     // without the epilogue: one 64-thread workgroup per half head; with it: one
     // 128-thread workgroup per head
     const dim3 grid_half((unsigned)(2 * heads)), grid_head((unsigned)heads);
-    if (p.bf16) {
+    if (p.bf16 && p.w32) {
         if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true>), grid_head, dim3(128), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true, true>), grid_head, dim3(128), 0,
+                               stream, p);
         else
-            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true>), grid_half, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true, true>), grid_half, dim3(64), 0,
+                               stream, p);
+    } else if (p.bf16) {
+        if (p.epilogue)
+            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true, false>), grid_head, dim3(128), 0,
+                               stream, p);
+        else
+            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true, false>), grid_half, dim3(64), 0,
+                               stream, p);
     } else {
         if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<F32In, true, true>), grid_head, dim3(128), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<F32In, true, true, false>), grid_head, dim3(128), 0,
+                               stream, p);
         else
-            hipLaunchKernelGGL((decode_kernel<F32In, false, true>), grid_half, dim3(64), 0, stream, p);
+            hipLaunchKernelGGL((decode_kernel<F32In, false, true, false>), grid_half, dim3(64), 0,
+                               stream, p);
     }
     return hipGetLastError();
 }

@@ -27,6 +27,7 @@ struct ForwardArgs {
     float *s_out;                           // [B,H,N,N] or nullptr
     int B, T, H;
     bool bf16;
+    bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;
     EpilogueArgs epi;
     void *workspace;
@@ -53,6 +54,7 @@ struct DecodeArgs {
     void *y;                                // [B,H,N] in dt
     int B, H;
     bool bf16;
+    bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;
     EpilogueArgs epi;
 };

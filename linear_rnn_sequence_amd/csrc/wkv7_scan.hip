@@ -47,9 +47,19 @@ __device__ __forceinline__ float4 mul4(float4 a, float4 b) {
     return make_float4(a.x * b.x, a.y * b.y, a.z * b.z, a.w * b.w);
 }
 
-template <class IO, bool EPI>
+template <bool W32, class L>
+struct DecayLoad {
+    using type = L;
+};
+template <class L>
+struct DecayLoad<true, L> {
+    using type = RawLoad<F32In>;  // w as float32
+};
+
+template <class IO, bool EPI, bool W32>
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
     using L = RawLoad<IO>;
+    using LW = typename DecayLoad<W32, L>::type;
     using E = typename IO::elem;
     __shared__ ScanStage st;
 
@@ -90,19 +100,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
         if (p.epi.ln_b) lnb4 = *reinterpret_cast<const float4 *>(p.epi.ln_b + h * kN + 4 * s_q);
     }
 
-    typename L::T xr, xw, xk, xv, xkap, xa;
+    typename L::T xr, xk, xv, xkap, xa;
+    typename LW::T xw;
     auto issue = [&](int chunk) {
         const int t = chunk * kTC + s_t;
         if (t < T) {
             const long off = tok0 + (long)t * HN + 4 * s_q;
             xr = L::load(p.r, off);
-            xw = L::load(p.w, off);
+            xw = LW::load(p.w, off);
             xk = L::load(p.k, off);
             xv = L::load(p.v, off);
             xkap = L::load(p.kappa, off);
             xa = L::load(p.a, off);
         } else {
-            xr = xw = xk = xv = xkap = xa = L::zero();
+            xr = xk = xv = xkap = xa = L::zero();
+            xw = LW::zero();
         }
     };
 
@@ -122,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
             }
         }
         // ---- stage this chunk's vectors ----
-        const float4 r4 = L::widen(xr), w4 = L::widen(xw), k4 = L::widen(xk);
+        const float4 r4 = L::widen(xr), w4 = LW::widen(xw), k4 = L::widen(xk);
         const float4 v4 = L::widen(xv), kap4 = L::widen(xkap), a4 = L::widen(xa);
         const float4 b4 = mul4(a4, kap4);
         const float4 wr4 = mul4(w4, r4);
@@ -219,16 +231,21 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
 
 hipError_t launch_scan(const ForwardArgs &p, hipStream_t stream) {
     const dim3 grid((unsigned)((long)p.B * p.H)), block(kScanThreads);
-    if (p.bf16) {
+    if (p.bf16 && p.w32) {
         if (p.epilogue)
-            hipLaunchKernelGGL((scan_kernel<Bf16In, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((scan_kernel<Bf16In, true, true>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((scan_kernel<Bf16In, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((scan_kernel<Bf16In, false, true>), grid, block, 0, stream, p);
+    } else if (p.bf16) {
+        if (p.epilogue)
+            hipLaunchKernelGGL((scan_kernel<Bf16In, true, false>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((scan_kernel<Bf16In, false, false>), grid, block, 0, stream, p);
     } else {
         if (p.epilogue)
-            hipLaunchKernelGGL((scan_kernel<F32In, true>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((scan_kernel<F32In, true, false>), grid, block, 0, stream, p);
         else
-            hipLaunchKernelGGL((scan_kernel<F32In, false>), grid, block, 0, stream, p);
+            hipLaunchKernelGGL((scan_kernel<F32In, false, false>), grid, block, 0, stream, p);
     }
     return hipGetLastError();
 }

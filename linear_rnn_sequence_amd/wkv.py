@@ -19,7 +19,7 @@ STATUS = {
     4: "RWKV7_ERR_UNSUPPORTED", 5: "RWKV7_ERR_ALIGN", 6: "RWKV7_ERR_ALIAS",
     7: "RWKV7_ERR_WORKSPACE", 8: "RWKV7_ERR_HIP",
 }
-DT_F32, DT_BF16 = 0, 1
+DT_F32, DT_BF16, DT_BF16_W32 = 0, 1, 2
 ALGOS = {"auto": 0, "scan": 1, "chunked": 2}
 N_HEAD = 64
 
@@ -105,6 +105,17 @@ def _epilogue(epilogue):
     return ctypes.byref(e), (e, keep)
 
 
+def _inputs_dtype(torch, r, w, k, v, kappa, a):
+    """Check the six per-token inputs and return the ABI dtype code: one dtype for
+    all, or bf16 with a float32 decay w (RWKV7_DT_BF16_W32)."""
+    _check_same(torch, (r, k, v, kappa, a), r.shape, r.dtype)
+    if r.dtype == torch.bfloat16 and w.dtype == torch.float32:
+        _check_same(torch, (w,), r.shape, torch.float32)
+        return DT_BF16_W32
+    _check_same(torch, (w,), r.shape, r.dtype)
+    return _dtype_code(torch, r.dtype)
+
+
 def _check_same(torch, xs, shape, dtype):
     for x in xs:
         if tuple(x.shape) != tuple(shape):
@@ -124,7 +135,8 @@ def forward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> 
 
 def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None, s_out=None,
             want_state=True, workspace=None, stream=None):
-    """rwkv7_wkv_forward.  Inputs [B,T,H,N] (bf16 or f32, one dtype), s0 [B,H,N,N] f32.
+    """rwkv7_wkv_forward.  Inputs [B,T,H,N] (bf16 or f32, one dtype; or bf16 with a f32
+    decay w), s0 [B,H,N,N] f32.
 
     Returns (y, s_out).  ``epilogue``: dict of f32 device tensors ln_w, ln_b ([H*N] or
     None), r_k ([H,N] or [H*N]) and float eps.  ``s_out`` may be ``s0`` (in place).
@@ -132,8 +144,7 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
     import torch
 
     B, T, H, N = r.shape
-    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
-    dt = _dtype_code(torch, r.dtype)
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
@@ -163,8 +174,7 @@ def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=N
     import torch
 
     B, T, H, N = r.shape
-    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
-    dt = _dtype_code(torch, r.dtype)
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
@@ -214,8 +224,7 @@ def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):
     import torch
 
     B, H, N = r.shape
-    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
-    dt = _dtype_code(torch, r.dtype)
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
     if y is None:
         y = torch.empty_like(r)
     epi_ptr, keep = _epilogue(epilogue)
@@ -236,10 +245,9 @@ def prepare_decode(r, w, k, v, kappa, a, state, *, y, epilogue=None, stream=None
     import torch
 
     B, H, N = r.shape
-    _check_same(torch, (r, w, k, v, kappa, a), r.shape, r.dtype)
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
     if tuple(y.shape) != (B, H, N) or y.dtype != r.dtype:
         raise ValueError("y must match the inputs")
-    dt = _dtype_code(torch, r.dtype)
     epi_ptr, keep = _epilogue(epilogue)
     fn = lib().rwkv7_wkv_decode
     args = (_ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(state), _ptr(y),

@@ -126,6 +126,7 @@ def draw(
                   fixed over b and t (a per-channel bias, as the listing's w_bias)
       "slow"    : w = clamp(exp(-sigmoid(z - 8)/sqrt(e)), 0.99, 1)
     s0: "zero" or "normal" (N(0, s0_std), float32).
+    dtype: "bf16", "f32", or "bf16_w32" (bf16 except w, which stays float32).
     """
     rng = np.random.default_rng(seed)
     shp = (B, T, H, N)
@@ -164,14 +165,16 @@ def draw(
         epi = {"ln_w": ln_w, "ln_b": ln_b, "r_k": r_k, "eps": GN_EPS}
 
     def store(x):
-        if dtype == "bf16":
+        if dtype in ("bf16", "bf16_w32"):
             return f32_to_bf16_bits(x)
         if dtype == "f32":
             return np.ascontiguousarray(x, dtype=f32)
         raise ValueError(dtype)
 
+    # "bf16_w32": bf16 vectors, except the decay w, kept as float32
+    w_st = np.ascontiguousarray(w, dtype=f32) if dtype == "bf16_w32" else store(w)
     out = Inputs(
-        r=store(r), w=store(w), k=store(k), v=store(v), kappa=store(kappa), a=store(a),
+        r=store(r), w=w_st, k=store(k), v=store(v), kappa=store(kappa), a=store(a),
         s0=S0, epi=epi,
         meta={"B": B, "T": T, "H": H, "N": N, "dtype": dtype, "seed": seed},
     )

@@ -159,3 +159,18 @@ def test_backward_validation_codes():
     # ds0 == ds_T is the in-place case: passes validation (T == 0 then has nothing to do)
     assert bwd(T=0, ds0=fake(8), dsT=fake(8), ck=None, dy=None) == 0
     assert bwd(T=0, ds0=None, ck=None) == 0
+
+
+def test_fp32_decay_dtype_codes():
+    # RWKV7_DT_BF16_W32 = 2: accepted by forward (scan and chunked) and decode
+    # validation; the backward refuses it; w spans 4 bytes per element
+    assert fwd(dt=2, algo=1, T=0, s_out=None) == 0
+    assert fwd(dt=2, algo=2, T=0, s_out=None) == 0
+    assert fwd(dt=3) == 3
+    B, T, H = 2, 8, 3
+    half_w = B * T * H * 64 * 2
+    assert fwd(dt=2, y=fake(1, half_w)) == 6     # y over the float32 w's second half
+    assert bwd(dt=2) == 4
+    L = wkv.lib()
+    assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 2, 0) == \
+        L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 0)
