@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' needs --only prefill")
+    ap.add_argument("--decay-f32", action="store_true",
+                    help="prefill with the decay w in float32 (other vectors bf16); "
+                         "needs --only prefill")
     return ap.parse_args()
 
 
@@ -122,6 +125,20 @@ FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # cotangent update G diag(w) + du kappa^T: 3N^2) plus one forward recompute of
 # the states (probe 2N^2, update 5N^2)
 BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
+
+
+def _slow_decay_f32(px):
+    """The long-context draw's decay before its bf16 rounding: the same recipe and
+    seed with dtype 'bf16_w32' keeps w in float32 (all other vectors identical)."""
+    import synth
+
+    m = px["meta"]
+    x = synth.draw(m["B"], m["T"], m["H"], m["N"], seed=m["seed"], dtype="bf16_w32",
+                   w_recipe="slow", a_mean=2.0)
+    for n in NAMES:
+        if n != "w":
+            assert np.array_equal(x[n], px[n])
+    return x["w"]
 
 
 def bench_train(args, torch, wkv, synth, dev):
@@ -242,9 +259,9 @@ def main():
         sys.exit(2)
 
     cfg_idx, PREFILL, p_with_epi = PREFILL_SHAPES[args.prefill_shape]
-    if args.prefill_shape != "2.9b" and args.only != "prefill":
-        print("bench.py: --prefill-shape long is a prefill-only measurement (--only prefill)",
-              file=sys.stderr)
+    if (args.prefill_shape != "2.9b" or args.decay_f32) and args.only != "prefill":
+        print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
+              "(--only prefill)", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -283,6 +300,10 @@ def main():
         pd = {}
         for n in NAMES:
             pd[n] = torch.from_numpy(px[n].view(np.int16)).to(dev).view(torch.bfloat16)
+        if args.decay_f32:  # the decay in float32, from the same draw's values
+            if cfg_idx != 4:
+                raise SystemExit("--decay-f32 is defined for the long-context shape")
+            pd["w"] = torch.from_numpy(_slow_decay_f32(px)).to(dev)
         e = px["epi"]
         p_epi = None
         if p_with_epi:
@@ -407,13 +428,16 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; recipes of the pages' parameterisations)",
         "config": {
-            "workload": ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue)"
+            "workload": ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue"
+                         + (", decay w in float32)" if args.decay_f32 else ")")
                          if long_shape else
                          "2.9B-shape WKV7: prefill B8 T4096 H40 N64 with fused GroupNorm+bonus "
                          "epilogue, then decode of 64 tokens through 32 layers x B256 x H40 "
                          "resident fp32 states"),
             "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=p_with_epi,
-                            workspace_bytes=ws_bytes) if do_prefill else None,
+                            workspace_bytes=ws_bytes,
+                            decay_dtype="f32" if args.decay_f32 else "bf16")
+            if do_prefill else None,
             "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
             "state_dtype": "f32",
         },
@@ -438,7 +462,7 @@ def main():
     if do_prefill:
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         # six inputs + y, the final state, and the epilogue parameters when fused
-        p_bytes = B * T * H * 7 * N * 2 + B * H * N * N * 4
+        p_bytes = B * T * H * (7 + (1 if args.decay_f32 else 0)) * N * 2 + B * H * N * N * 4
         if p_with_epi:
             p_bytes += 2 * H * N * 4 + H * N * 4
         ach = p_bytes / (prefill_ms / 1e3) / 1e9
@@ -478,6 +502,8 @@ def main():
     par, cpu_work, cpu_s = {}, 0, 0.0
     if do_prefill and not args.no_cpu_baseline:
         sub = [px.as_f64(n) for n in NAMES]
+        if args.decay_f32:
+            sub[1] = pd["w"].cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
         y_ref, s_ref = oracle.forward(*sub, s0=None, epilogue=px["epi"] if p_with_epi else None,
                                       threads=threads)
