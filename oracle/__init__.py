@@ -159,3 +159,31 @@ def bonus(r, k, r_k, v):
     s = np.sum(np.asarray(r, np.float64) * np.asarray(k, np.float64)
                * np.asarray(r_k, np.float64), axis=-1, keepdims=True)
     return s * np.asarray(v, np.float64)
+
+
+def forward_bidir(r, w, k, v, kappa, a, s0=None, epilogue=None, *, threads=None):
+    """Bidirectional reading of the recurrence (RWKV-7 "Goose" summary, §9
+    Multimodal Experiments: AudioRWKV-7 uses a bidirectional RWKV-7; the page
+    gives no formula).  The plain reading: run the recurrence over tokens
+    0..T-1 from s0[0] and over tokens T-1..0 from s0[1], add the two readouts of
+    each token, then apply the optional per-head GroupNorm and bonus to the sum.
+
+    Returns (y [B,T,H,N], S [2,B,H,N,N]): the final state of each pass (the
+    reverse pass ends after token 0).  float64, through :func:`forward`.
+    """
+    ins = [np.asarray(x) for x in (r, w, k, v, kappa, a)]
+    s0f = s0r = None
+    if s0 is not None:
+        s0f, s0r = np.asarray(s0)[0], np.asarray(s0)[1]
+    y_f, s_f = forward(*ins, s0=s0f, threads=threads)
+    y_r, s_r = forward(*(np.ascontiguousarray(x[:, ::-1]) for x in ins), s0=s0r,
+                       threads=threads)
+    y = y_f + y_r[:, ::-1]
+    if epilogue is not None:
+        H, N = y.shape[-2:]
+        y = group_norm_heads(y, epilogue.get("ln_w"), epilogue.get("ln_b"),
+                             epilogue.get("eps", 64e-5))
+        rk = np.asarray(epilogue["r_k"], dtype=np.float64).reshape(H, N)
+        y = y + bonus(np.asarray(ins[0], np.float64), np.asarray(ins[2], np.float64), rk,
+                      np.asarray(ins[3], np.float64))
+    return y, np.stack([s_f, s_r])

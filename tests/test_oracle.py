@@ -16,6 +16,7 @@ import pytest
 import oracle
 
 HERE = os.path.dirname(os.path.abspath(__file__))
+NAMES = ("r", "w", "k", "v", "kappa", "a")
 
 
 def rand_inputs(rng, B, T, H, N, *, unit_kappa=True, w_lo=0.55, a_hi=1.0, s0=True):
@@ -392,3 +393,49 @@ def test_decode_is_one_step():
     y, sT = run(d, S0)
     yd, sd = oracle.decode(*(d[n][:, 0] for n in ("r", "w", "k", "v", "kappa", "a")), S0)
     assert np.array_equal(yd, y[:, 0]) and np.array_equal(sd, sT)
+
+
+# --------------------------------------------------------------------------
+# bidirectional reading ([summary] §9, AudioRWKV-7; formula not on the page)
+# --------------------------------------------------------------------------
+
+def test_bidir_brute_force_and_symmetry():
+    """Against per-token loops written here (the readout of token t from the
+    state after tokens 0..t plus from the state after tokens T-1..t), and the
+    time-reversal symmetry: reversing the sequence and swapping the two initial
+    states reverses y and swaps the final states."""
+    rng = np.random.default_rng(91)
+    d, _ = rand_inputs(rng, 2, 7, 3, 5)
+    S0 = rng.standard_normal((2, 2, 3, 5, 5)) * 0.3
+    y, S = oracle.forward_bidir(*(d[n] for n in NAMES), s0=S0)
+    want = np.zeros_like(y)
+    for (order, s_init) in ((range(7), S0[0]), (range(6, -1, -1), S0[1])):
+        St = s_init.copy()
+        for t in order:
+            kap, at = d["kappa"][:, t], d["a"][:, t]
+            u = np.einsum("bhij,bhj->bhi", St, kap)
+            St = (St * d["w"][:, t][:, :, None, :] - u[..., None] * (kap * at)[:, :, None, :]
+                  + d["v"][:, t][..., None] * d["k"][:, t][:, :, None, :])
+            want[:, t] += np.einsum("bhij,bhj->bhi", St, d["r"][:, t])
+    assert rel(y, want) < 1e-13
+    rev = {n: np.ascontiguousarray(d[n][:, ::-1]) for n in NAMES}
+    y2, S2 = oracle.forward_bidir(*(rev[n] for n in NAMES), s0=S0[::-1])
+    assert rel(y2[:, ::-1], y) < 1e-13 and rel(S2[::-1], S) < 1e-13
+
+
+def test_bidir_single_token_and_epilogue():
+    """T = 1: both passes see the one token, so y = S1_f r + S1_r r; the epilogue
+    normalises that sum (then adds the bonus once)."""
+    rng = np.random.default_rng(92)
+    d, _ = rand_inputs(rng, 1, 1, 2, 64)
+    S0 = rng.standard_normal((2, 1, 2, 64, 64)) * 0.3
+    y1, _ = oracle.forward(*(d[n] for n in NAMES), s0=S0[0])
+    y2, _ = oracle.forward(*(d[n] for n in NAMES), s0=S0[1])
+    y, _ = oracle.forward_bidir(*(d[n] for n in NAMES), s0=S0)
+    assert rel(y, y1 + y2) < 1e-14
+    epi = {"ln_w": rng.standard_normal(128), "ln_b": rng.standard_normal(128),
+           "r_k": rng.standard_normal((2, 64)), "eps": 64e-5}
+    ye, _ = oracle.forward_bidir(*(d[n] for n in NAMES), s0=S0, epilogue=epi)
+    ref = oracle.group_norm_heads(y1 + y2, epi["ln_w"], epi["ln_b"]) + oracle.bonus(
+        d["r"], d["k"], epi["r_k"], d["v"])
+    assert rel(ye, ref) < 1e-13
