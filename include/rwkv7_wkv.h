@@ -132,6 +132,31 @@ size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                    rwkv7_algo algo);
 
 /*
+ * Bidirectional forward: the recurrence is run twice over the same inputs,
+ * once over tokens 0 .. T-1 and once over tokens T-1 .. 0, and the two
+ * readouts of each token are added; the optional epilogue then applies to the
+ * sum.  Source: RWKV-7 "Goose" summary, §9 Multimodal Experiments (AudioRWKV-7
+ * uses a bidirectional RWKV-7); the page gives no formula, and the plain
+ * reading taken is this sum of a causal and an anti-causal pass.
+ *   s0, s_out : [2,B,H,N,N] float32 (index 0: forward pass, 1: reverse pass),
+ *               or NULL; s_out may equal s0 (in place).  The reverse pass's final
+ *               state is the one after token 0.
+ *   workspace  : at least rwkv7_wkv_forward_bidir_workspace(...) bytes (the
+ *               reverse pass's float32 readouts, plus what the chunked path needs)
+ * Everything else as rwkv7_wkv_forward.
+ */
+rwkv7_status rwkv7_wkv_forward_bidir(const void *r, const void *w, const void *k,
+                                     const void *v, const void *kappa, const void *a,
+                                     const float *s0, void *y, float *s_out, int B, int T, int H,
+                                     int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                     const rwkv7_epilogue *epi, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace rwkv7_wkv_forward_bidir needs (0 for T == 0). */
+size_t rwkv7_wkv_forward_bidir_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
+                                         rwkv7_algo algo);
+
+/*
  * One token for each of B resident states (single-token inference, the
  * recurrence at T = 1 with the state read from and written back to HBM).
  *   r, w, k, v, kappa, a : [B,H,N] in dt

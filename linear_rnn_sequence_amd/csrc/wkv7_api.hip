@@ -101,14 +101,28 @@ size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt, r
     return chunked_workspace_bytes(B, T, H);
 }
 
+size_t rwkv7_wkv_forward_bidir_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
+                                         rwkv7_algo algo) {
+    if (B < 1 || H < 1 || T <= 0 || N != kN || !valid_dtype(dt)) return 0;
+    size_t n = 1;
+    if (!mul_ok(n, (size_t)B) || !mul_ok(n, (size_t)T) || !mul_ok(n, (size_t)H) ||
+        !mul_ok(n, (size_t)N * 4))
+        return 0;
+    return n + rwkv7_wkv_forward_workspace(B, T, H, N, dt, algo);
+}
+
 }  // extern "C"
 
-// rwkv7_wkv_forward, and with s_ckpt (training forward, no epilogue) the
-// states before every kCkpt-th token as well.
+// Bytes of the float32 readouts of a bidirectional call's reverse pass.
+static size_t bidir_yrev_bytes(int B, int T, int H) { return (size_t)B * T * H * kN * 4; }
+
+// rwkv7_wkv_forward; with s_ckpt (training forward, no epilogue) the states
+// before every kCkpt-th token as well; with bidir the bidirectional forward
+// (s0 / s_out hold two states per head).
 static rwkv7_status forward_impl(const void *r, const void *w, const void *k, const void *v,
                                  const void *kappa, const void *a, const float *s0, void *y,
-                                 float *s_out, float *s_ckpt, bool want_ckpt, int B, int T,
-                                 int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                 float *s_out, float *s_ckpt, bool want_ckpt, bool bidir, int B,
+                                 int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
                                  const rwkv7_epilogue *epi, void *workspace,
                                  size_t workspace_bytes, void *stream) {
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
@@ -130,7 +144,9 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
-    size_t ck = st;  // bytes of the stored states
+    const size_t st1 = st;  // bytes of one state per head
+    if (bidir && !mul_ok(st, 2)) return RWKV7_ERR_SHAPE;
+    size_t ck = st1;  // bytes of the stored states
     if (want_ckpt && !mul_ok(ck, (size_t)((T + kCkpt - 1) / kCkpt))) return RWKV7_ERR_SHAPE;
 
     const void *ins[6] = {r, w, k, v, kappa, a};
@@ -191,7 +207,8 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
             (s_out && overlap(rc, rng(s_out, st))))
             return RWKV7_ERR_ALIAS;
     }
-    const size_t need = rwkv7_wkv_forward_workspace(B, T, H, N, dt, al);
+    const size_t need = bidir ? rwkv7_wkv_forward_bidir_workspace(B, T, H, N, dt, al)
+                              : rwkv7_wkv_forward_workspace(B, T, H, N, dt, al);
     if (need > 0) {
         if (!workspace || workspace_bytes < need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
@@ -220,8 +237,31 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
     p.s_ckpt = s_ckpt;
-    const hipError_t e = al == RWKV7_ALGO_CHUNKED ? launch_chunked(p, hs) : launch_scan(p, hs);
-    return e == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+    auto run = [&](const ForwardArgs &q) {
+        return al == RWKV7_ALGO_CHUNKED ? launch_chunked(q, hs) : launch_scan(q, hs);
+    };
+    if (!bidir) return run(p) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+
+    // bidirectional: the reverse pass (tokens T-1 .. 0, second state of each head)
+    // leaves float32 readouts in the workspace; the forward pass adds them to its
+    // own before the epilogue
+    const size_t yrev = bidir_yrev_bytes(B, T, H);
+    const size_t heads_elems = st1 / 4;
+    float *ws_y = static_cast<float *>(workspace);
+    ForwardArgs rev = p;
+    rev.reverse = true;
+    rev.epilogue = false;
+    rev.y_f32 = ws_y;
+    rev.s0 = s0 ? s0 + heads_elems : nullptr;
+    rev.s_out = s_out ? s_out + heads_elems : nullptr;
+    rev.workspace = static_cast<char *>(workspace) + yrev;
+    rev.workspace_bytes = workspace_bytes - yrev;
+    if (run(rev) != hipSuccess) return RWKV7_ERR_HIP;
+    ForwardArgs fwd = p;
+    fwd.y_add = ws_y;
+    fwd.workspace = rev.workspace;
+    fwd.workspace_bytes = rev.workspace_bytes;
+    return run(fwd) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
 extern "C" {
@@ -231,8 +271,18 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
                                float *s_out, int B, int T, int H, int N, rwkv7_dtype dt,
                                rwkv7_algo algo, const rwkv7_epilogue *epi, void *workspace,
                                size_t workspace_bytes, void *stream) {
-    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, nullptr, false, B, T, H, N, dt, algo,
-                        epi, workspace, workspace_bytes, stream);
+    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, nullptr, false, false, B, T, H, N,
+                        dt, algo, epi, workspace, workspace_bytes, stream);
+}
+
+rwkv7_status rwkv7_wkv_forward_bidir(const void *r, const void *w, const void *k,
+                                     const void *v, const void *kappa, const void *a,
+                                     const float *s0, void *y, float *s_out, int B, int T, int H,
+                                     int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                     const rwkv7_epilogue *epi, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, nullptr, false, true, B, T, H, N,
+                        dt, algo, epi, workspace, workspace_bytes, stream);
 }
 
 rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k,
@@ -241,8 +291,8 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
                                      int B, int T, int H, int N, rwkv7_dtype dt,
                                      rwkv7_algo algo, void *workspace, size_t workspace_bytes,
                                      void *stream) {
-    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, s_ckpt, true, B, T, H, N, dt, algo,
-                        nullptr, workspace, workspace_bytes, stream);
+    return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, s_ckpt, true, false, B, T, H, N, dt,
+                        algo, nullptr, workspace, workspace_bytes, stream);
 }
 
 rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v,

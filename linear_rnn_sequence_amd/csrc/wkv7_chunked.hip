@@ -163,14 +163,19 @@ struct Chunked {
     const ForwardArgs &p;
     const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
     const int Tl;                // tokens of this workgroup's range
-    const long HN, tok0;         // elements between tokens; offset of (b, t = t0, h, 0)
+    // Elements from one token to the next in processing order (negative when the
+    // sequence is walked from its end), and the offset of (b, token t0 of the
+    // processing order, h, 0).
+    const long TS, tok0;
     const long lane_off;         // prep lane: its 4 channels at token lo of chunk 0
 
     __device__ Chunked(const ForwardArgs &p_, int b_, int h_, int t0, int tl)
         : p(p_), lane(threadIdx.x & 63), blk((threadIdx.x >> 6) & 3),
-          g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), Tl(tl), HN((long)p_.H * kN),
-          tok0(((long)b_ * p_.T + t0) * ((long)p_.H * kN) + (long)h_ * kN),
-          lane_off(tok0 + (long)(threadIdx.x & 15) * HN + 16 * ((threadIdx.x >> 6) & 3) +
+          g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), Tl(tl),
+          TS(p_.reverse ? -(long)p_.H * kN : (long)p_.H * kN),
+          tok0(((long)b_ * p_.T + (p_.reverse ? p_.T - 1 - t0 : t0)) * ((long)p_.H * kN) +
+               (long)h_ * kN),
+          lane_off(tok0 + (long)(threadIdx.x & 15) * TS + 16 * ((threadIdx.x >> 6) & 3) +
                    4 * ((threadIdx.x & 63) >> 4)) {}
 
     // Issues exactly six loads on every path (no branch around them), so the
@@ -181,7 +186,7 @@ struct Chunked {
     __device__ void load(int c, Raw<W32> &x) const {
         const int cc = min(c, (Tl - 1) / kC);
         const int t = min(cc * kC + lo, Tl - 1);
-        const long off = lane_off + (long)(t - lo) * HN;
+        const long off = lane_off + (long)(t - lo) * TS;
         x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
         if constexpr (W32)
             x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + off);
@@ -353,7 +358,7 @@ struct Pending {
 template <bool EPI, bool W32>
 __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI, W32> &K,
                                                 const ChunkSmem &sm, const Pending &pd, int c,
-                                                float lnw, float lnb, uint16_t *y) {
+                                                float lnw, float lnb, long yoff) {
     const int g = K.g;
     float yv[4];
 #pragma unroll
@@ -372,18 +377,26 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
                     pd.bon[e] * bf16_lo((unsigned)(unsigned short)pd.v[e]);
         }
     }
+    // yoff: element offset of token c*16 + 4g of this lane's value channel
+    const int t0 = c * kC + 4 * g;
+    const int nt = min(4, K.Tl - t0);
+    if (p.y_f32) {  // float32 readouts, no rounding (first pass of a bidirectional call)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (e < nt) p.y_f32[yoff + e * K.TS] = yv[e];
+        return;
+    }
+    uint16_t *y = static_cast<uint16_t *>(p.y) + yoff;
     const unsigned lo2 = cvt_pk(yv[0], yv[1]), hi2 = cvt_pk(yv[2], yv[3]);
     const unsigned short out[4] = {(unsigned short)(lo2 & 0xffffu), (unsigned short)(lo2 >> 16),
                                    (unsigned short)(hi2 & 0xffffu), (unsigned short)(hi2 >> 16)};
-    // y points at token c*16 + 4g of this lane's value channel
-    const int t0 = c * kC + 4 * g;
-    if (t0 + 3 < K.Tl) {
+    if (nt == 4) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) y[e * K.HN] = out[e];
+        for (int e = 0; e < 4; ++e) y[e * K.TS] = out[e];
     } else {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-            if (t0 + e < K.Tl) y[e * K.HN] = out[e];
+            if (e < nt) y[e * K.TS] = out[e];
     }
 }
 
@@ -442,8 +455,8 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
             if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * blk + lo];
         }
         Pending pd;
-        uint16_t *ylane = static_cast<uint16_t *>(p.y) + K.tok0 + (long)(4 * g) * K.HN + 16 * blk + lo;
-        const long ystep = (long)kC * K.HN;
+        long ylane = K.tok0 + (long)(4 * g) * K.TS + 16 * blk + lo;  // y element offset
+        const long ystep = (long)kC * K.TS;
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
@@ -458,6 +471,13 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     for (int jb = 0; jb < 4; ++jb)
                         *reinterpret_cast<float4 *>(ck + 16 * jb) =
                             make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+                }
+                // the other direction's readouts of this chunk's tokens, if any
+                float yadd[4] = {0.f, 0.f, 0.f, 0.f};
+                if (!SUMMARY && p.y_add) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (c * kC + 4 * g + e < K.Tl) yadd[e] = p.y_add[ylane + e * K.TS];
                 }
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
@@ -483,6 +503,8 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     Z[jb][2] *= gc.z;
                     Z[jb][3] *= gc.w;
                 }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) Y[e] += yadd[e];
                 pd.y = Y;
                 pd.v = Vb;
                 if (EPI && !SUMMARY) {

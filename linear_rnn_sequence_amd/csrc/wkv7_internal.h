@@ -33,6 +33,12 @@ struct ForwardArgs {
     void *workspace;
     size_t workspace_bytes;
     float *s_ckpt;  // [B,H,ceil(T/kCkpt),N,N]: state before every kCkpt-th token, or nullptr
+    // bidirectional calls: the reverse pass walks tokens T-1 .. 0 and writes its
+    // readouts as float32 to y_f32 (no epilogue); the forward pass adds y_add to
+    // its readouts before the epilogue.  Both [B,T,H,N] float32, or nullptr.
+    bool reverse;
+    float *y_f32;
+    const float *y_add;
 };
 
 constexpr int kCkpt = RWKV7_CKPT_INTERVAL;  // tokens between stored states

@@ -71,8 +71,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
     const int c = lane & 7, g = lane >> 3;
     const int i0 = wave * 16 + 2 * g;  // value rows i0, i0 + 1
     const int j0 = 8 * c;              // key columns j0 .. j0 + 7
-    const long HN = (long)p.H * kN;
-    const long tok0 = (long)b * T * HN + (long)h * kN;
+    // elements from one token to the next in processing order (negative when the
+    // sequence is walked from its end) and the offset of the first processed token
+    const long HN = p.reverse ? -(long)p.H * kN : (long)p.H * kN;
+    const long tok0 = ((long)b * T + (p.reverse ? T - 1 : 0)) * ((long)p.H * kN) + (long)h * kN;
     const int s_t = tid >> 4, s_q = tid & 15;  // staging role: token, 4-column slice
 
     float S[2][8];
@@ -198,7 +200,13 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
         // (s_t is uniform over each 16-lane DPP row, so the row reductions
         // below see all of their lanes active)
         if (s_t < tl) {
+            const int t = ch * kTC + s_t;
+            const long yo = tok0 + (long)t * HN + 4 * s_q;
             float4 y4 = *reinterpret_cast<const float4 *>(&st.ybuf[s_t][4 * s_q]);
+            if (p.y_add) {  // the other direction's readouts
+                const float4 ya = *reinterpret_cast<const float4 *>(p.y_add + yo);
+                y4.x += ya.x; y4.y += ya.y; y4.z += ya.z; y4.w += ya.w;
+            }
             if (EPI) {
                 const float mu = sum_lanes16(y4.x + y4.y + y4.z + y4.w) * (1.f / kN);
                 const float4 d = make_float4(y4.x - mu, y4.y - mu, y4.z - mu, y4.w - mu);
@@ -211,8 +219,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
                 y4.z = d.z * rs * lnw4.z + lnb4.z + bz * vz.z;
                 y4.w = d.w * rs * lnw4.w + lnb4.w + bz * vz.w;
             }
-            const int t = ch * kTC + s_t;
-            IO::store4(static_cast<E *>(p.y) + tok0 + (long)t * HN + 4 * s_q, y4);
+            if (p.y_f32)  // float32 readouts (first pass of a bidirectional call)
+                *reinterpret_cast<float4 *>(p.y_f32 + yo) = y4;
+            else
+                IO::store4(static_cast<E *>(p.y) + yo, y4);
         }
     }
 

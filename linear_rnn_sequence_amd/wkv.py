@@ -55,6 +55,11 @@ def lib():
         L.rwkv7_wkv_forward_workspace.restype = sz
         L.rwkv7_wkv_decode.argtypes = [vp] * 8 + [ci] * 4 + [ctypes.POINTER(Epilogue), vp]
         L.rwkv7_wkv_decode.restype = ci
+        L.rwkv7_wkv_forward_bidir.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue),
+                                                                   vp, sz, vp]
+        L.rwkv7_wkv_forward_bidir.restype = ci
+        L.rwkv7_wkv_forward_bidir_workspace.argtypes = [ci] * 6
+        L.rwkv7_wkv_forward_bidir_workspace.restype = sz
         L.rwkv7_wkv_forward_train.argtypes = [vp] * 10 + [ci] * 6 + [vp, sz, vp]
         L.rwkv7_wkv_forward_train.restype = ci
         L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [ci] * 5 + [vp]
@@ -162,6 +167,39 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_forward")
     return y, s_out
+
+
+def forward_bidir(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None,
+                  s_out=None, want_state=True, workspace=None, stream=None):
+    """rwkv7_wkv_forward_bidir: readouts of the pass over tokens 0..T-1 plus those of the
+    pass over T-1..0, epilogue on the sum.  s0 / s_out [2,B,H,N,N] f32 (forward, reverse).
+    Returns (y, s_out)."""
+    import torch
+
+    B, T, H, N = r.shape
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    if y is None:
+        y = torch.empty_like(r)
+    if s_out is None and want_state:
+        s_out = torch.empty((2, B, H, N, N), dtype=torch.float32, device=r.device)
+    need = lib().rwkv7_wkv_forward_bidir_workspace(B, T, H, N, dt, ALGOS[algo])
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=r.device)
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_forward_bidir(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(s0), _ptr(y),
+        _ptr(s_out), B, T, H, N, dt, ALGOS[algo], epi_ptr, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_forward_bidir")
+    return y, s_out
+
+
+def forward_bidir_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
+    dt = {"bf16": DT_BF16, "bfloat16": DT_BF16, "f32": DT_F32, "bf16_w32": DT_BF16_W32}[dtype]
+    return int(lib().rwkv7_wkv_forward_bidir_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
 CKPT_INTERVAL = 16  # RWKV7_CKPT_INTERVAL

@@ -174,3 +174,26 @@ def test_fp32_decay_dtype_codes():
     L = wkv.lib()
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 2, 0) == \
         L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 0)
+
+
+def test_bidir_workspace_query():
+    L = wkv.lib()
+    assert L.rwkv7_wkv_forward_bidir_workspace(2, 0, 3, 64, 1, 0) == 0
+    assert L.rwkv7_wkv_forward_bidir_workspace(2, 10, 3, 64, 1, 0) == 2 * 10 * 3 * 64 * 4
+    assert L.rwkv7_wkv_forward_bidir_workspace(2, 10, 3, 32, 1, 0) == 0
+    big = L.rwkv7_wkv_forward_bidir_workspace(1, 65536, 1, 64, 1, 2)
+    assert big == 65536 * 64 * 4 + L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 2)
+    assert L.rwkv7_wkv_forward_bidir_workspace(1, 65536, 1, 64, 0, 1) == 65536 * 64 * 4
+
+
+def test_bidir_validation_codes():
+    L = wkv.lib()
+
+    def bid(B=2, T=8, H=3, s0=fake(6), s_out=fake(7), ws=fake(8), ws_bytes=1 << 20, dt=1):
+        return L.rwkv7_wkv_forward_bidir(*[fake(i) for i in range(6)], s0, fake(9), s_out, B, T,
+                                         H, 64, dt, 1, None, ws, ws_bytes, None)
+    assert bid(ws=None) == 7                       # workspace required
+    assert bid(ws_bytes=100) == 7
+    st = 2 * 3 * 64 * 64 * 4
+    assert bid(s_out=fake(6, st)) == 6             # s_out over s0's second state
+    assert bid(T=0, s_out=None) == 0
