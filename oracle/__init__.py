@@ -187,3 +187,31 @@ def forward_bidir(r, w, k, v, kappa, a, s0=None, epilogue=None, *, threads=None)
         y = y + bonus(np.asarray(ins[0], np.float64), np.asarray(ins[2], np.float64), rk,
                       np.asarray(ins[3], np.float64))
     return y, np.stack([s_f, s_r])
+
+
+def prologue(k, a, k_k, k_a):
+    """The time-mix prologue of the RWKV-7 "Goose" author response (paperhub),
+    numpy time_mixing listing, on per-token keys k and rates a ([..., H, N]):
+      kk     = k * k_k, then L2-normalised per head with a 1e-12 floor -> kappa
+      k_tilde = k + k * (a - 1) * k_a
+    k_k, k_a are per-channel parameters ([H*N] or [H, N]).  float64.
+    Returns (kappa, k_tilde)."""
+    k = np.asarray(k, np.float64)
+    a = np.asarray(a, np.float64)
+    H, N = k.shape[-2:]
+    kk = k * np.asarray(k_k, np.float64).reshape(H, N)
+    nrm = np.sqrt(np.sum(kk * kk, axis=-1, keepdims=True))
+    kappa = kk / np.maximum(nrm, 1e-12)
+    k_t = k + k * (a - 1.0) * np.asarray(k_a, np.float64).reshape(H, N)
+    return kappa, k_t
+
+
+def forward_fused(r, w, k, v, a, k_k, k_a, g=None, s0=None, epilogue=None, *, threads=None):
+    """The recurrence fed from raw keys through :func:`prologue`, with the
+    optional epilogue and then the output gate y * g (the listing returns
+    Wo @ (y * g); the projection is outside the recurrence).  float64."""
+    kappa, k_t = prologue(k, a, k_k, k_a)
+    y, sT = forward(r, w, k_t, v, kappa, a, s0=s0, epilogue=epilogue, threads=threads)
+    if g is not None:
+        y = y * np.asarray(g, np.float64)
+    return y, sT

@@ -439,3 +439,50 @@ def test_bidir_single_token_and_epilogue():
     ref = oracle.group_norm_heads(y1 + y2, epi["ln_w"], epi["ln_b"]) + oracle.bonus(
         d["r"], d["k"], epi["r_k"], d["v"])
     assert rel(ye, ref) < 1e-13
+
+
+# --------------------------------------------------------------------------
+# time-mix prologue and output gate ([listing]: kk, k, normalisation, y * g)
+# --------------------------------------------------------------------------
+
+def test_prologue_worked_example():
+    """N = 2, one head, by hand: k = (3, 4), k_k = (1, 2), k_a = (0.5, 1), a = (0.5, 0)
+    -> kk = (3, 8), |kk| = sqrt(73); k_tilde = (3 - 0.75, 4 - 4) = (2.25, 0)."""
+    k = np.array([[[[3.0, 4.0]]]])
+    a = np.array([[[[0.5, 0.0]]]])
+    kap, kt = oracle.prologue(k, a, np.array([1.0, 2.0]), np.array([0.5, 1.0]))
+    assert np.allclose(kap[0, 0, 0], np.array([3.0, 8.0]) / np.sqrt(73.0), rtol=0, atol=1e-15)
+    assert np.array_equal(kt[0, 0, 0], np.array([2.25, 0.0]))
+
+
+def test_prologue_invariants():
+    rng = np.random.default_rng(93)
+    k = rng.standard_normal((2, 5, 3, 64))
+    a = rng.uniform(0, 1, (2, 5, 3, 64))
+    k_k, k_a = rng.standard_normal(3 * 64), rng.standard_normal(3 * 64)
+    kap, kt = oracle.prologue(k, a, k_k, k_a)
+    assert np.allclose(np.linalg.norm(kap, axis=-1), 1.0, atol=1e-14)   # unit removal key
+    _, kt1 = oracle.prologue(k, np.ones_like(a), k_k, k_a)
+    assert np.array_equal(kt1, k)                                       # a = 1: k unchanged
+    _, kt0 = oracle.prologue(k, a, k_k, np.zeros_like(k_a))
+    assert np.array_equal(kt0, k)                                       # k_a = 0: unchanged
+    kz, _ = oracle.prologue(np.zeros_like(k), a, k_k, k_a)
+    assert np.array_equal(kz, np.zeros_like(k))                         # 1e-12 floor: no NaN
+    # the normalisation ignores the scale of k_k
+    kap2, _ = oracle.prologue(k, a, 3.0 * k_k, k_a)
+    assert rel(kap2, kap) < 1e-14
+
+
+def test_forward_fused_composes():
+    """Fused = prologue then the pinned recurrence, then the gate; a gate of ones
+    changes nothing and the gate scales y channel by channel."""
+    rng = np.random.default_rng(94)
+    d, S0 = rand_inputs(rng, 2, 9, 2, 64)
+    k_k, k_a = rng.standard_normal(128), rng.standard_normal(128)
+    g = rng.standard_normal(d["r"].shape)
+    kap, kt = oracle.prologue(d["k"], d["a"], k_k, k_a)
+    y_ref, s_ref = oracle.forward(d["r"], d["w"], kt, d["v"], kap, d["a"], s0=S0)
+    y1, s1 = oracle.forward_fused(d["r"], d["w"], d["k"], d["v"], d["a"], k_k, k_a, s0=S0)
+    yg, _ = oracle.forward_fused(d["r"], d["w"], d["k"], d["v"], d["a"], k_k, k_a, g=g, s0=S0)
+    assert np.array_equal(y1, y_ref) and np.array_equal(s1, s_ref)
+    assert np.array_equal(yg, y_ref * g)
