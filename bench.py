@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' needs --only prefill")
+    ap.add_argument("--bidir", action="store_true",
+                    help="time the bidirectional forward (needs --only prefill)")
     ap.add_argument("--decay-f32", action="store_true",
                     help="prefill with the decay w in float32 (other vectors bf16); "
                          "needs --only prefill")
@@ -125,6 +127,18 @@ FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # cotangent update G diag(w) + du kappa^T: 3N^2) plus one forward recompute of
 # the states (probe 2N^2, update 5N^2)
 BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
+
+
+def workload_name(args, long_shape, do_prefill, do_decode):
+    if long_shape:
+        return ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue"
+                + (", decay w in float32)" if args.decay_f32 else ")"))
+    pre = ("2.9B-shape WKV7 prefill B8 T4096 H40 N64 with fused GroupNorm+bonus epilogue"
+           + (" (bidirectional: epilogue on the sum of both passes)" if args.bidir else ""))
+    dec = "decode of 64 tokens through 32 layers x B256 x H40 resident fp32 states"
+    if do_prefill and do_decode:
+        return "2.9B-shape WKV7: " + pre.replace("2.9B-shape WKV7 ", "") + ", then " + dec
+    return pre if do_prefill else "2.9B-shape WKV7 " + dec
 
 
 def _slow_decay_f32(px):
@@ -259,7 +273,7 @@ def main():
         sys.exit(2)
 
     cfg_idx, PREFILL, p_with_epi = PREFILL_SHAPES[args.prefill_shape]
-    if (args.prefill_shape != "2.9b" or args.decay_f32) and args.only != "prefill":
+    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir) and args.only != "prefill":
         print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
               "(--only prefill)", file=sys.stderr)
         sys.exit(2)
@@ -312,14 +326,17 @@ def main():
                      "r_k": torch.from_numpy(e["r_k"]).to(dev), "eps": e["eps"]}
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         p_y = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=dev)
-        p_s = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
-        ws_bytes = wkv.forward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
+        p_s = torch.empty(((2,) if args.bidir else ()) + (B, H, N, N), dtype=torch.float32,
+                          device=dev)
+        ws_bytes = (wkv.forward_bidir_workspace_bytes if args.bidir else
+                    wkv.forward_workspace_bytes)(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
         p_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         p_gen_s = time.time() - t0
 
         def prefill():
-            wkv.forward(*(pd[n] for n in NAMES), s0=None, algo=args.prefill_algo,
-                        epilogue=p_epi, y=p_y, s_out=p_s, workspace=p_ws)
+            (wkv.forward_bidir if args.bidir else wkv.forward)(
+                *(pd[n] for n in NAMES), s0=None, algo=args.prefill_algo, epilogue=p_epi, y=p_y,
+                s_out=p_s, workspace=p_ws)
 
     # ------------------------------------------------------------------- decode
     if do_decode:
@@ -415,6 +432,8 @@ def main():
     long_shape = args.prefill_shape == "long"
     out = {
         "metric": ("WKV7 tokens x heads per second (long-context prefill)" if long_shape else
+                   "WKV7 tokens x heads per second (bidirectional 2.9B-shape prefill)"
+                   if args.bidir else
                    "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)"),
         "value": value,
         "unit": "token*heads/s",
@@ -428,14 +447,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded; recipes of the pages' parameterisations)",
         "config": {
-            "workload": ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue"
-                         + (", decay w in float32)" if args.decay_f32 else ")")
-                         if long_shape else
-                         "2.9B-shape WKV7: prefill B8 T4096 H40 N64 with fused GroupNorm+bonus "
-                         "epilogue, then decode of 64 tokens through 32 layers x B256 x H40 "
-                         "resident fp32 states"),
+            "workload": workload_name(args, long_shape, do_prefill, do_decode),
             "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=p_with_epi,
-                            workspace_bytes=ws_bytes,
+                            workspace_bytes=ws_bytes, bidirectional=args.bidir,
                             decay_dtype="f32" if args.decay_f32 else "bf16")
             if do_prefill else None,
             "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
@@ -505,8 +519,8 @@ def main():
         if args.decay_f32:
             sub[1] = pd["w"].cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        y_ref, s_ref = oracle.forward(*sub, s0=None, epilogue=px["epi"] if p_with_epi else None,
-                                      threads=threads)
+        y_ref, s_ref = (oracle.forward_bidir if args.bidir else oracle.forward)(
+            *sub, s0=None, epilogue=px["epi"] if p_with_epi else None, threads=threads)
         cpu_s += time.perf_counter() - t0
         cpu_work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
         del sub

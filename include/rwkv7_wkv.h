@@ -132,6 +132,35 @@ size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                    rwkv7_algo algo);
 
 /*
+ * Fused time-mix prologue and output gate (RWKV-7 "Goose" author response,
+ * paperhub, numpy time_mixing listing): from raw keys k the kernels form
+ *   kappa = (k * k_k) / max(||k * k_k||, 1e-12)   (per head, over its N channels)
+ *   k     <- k + k * (a - 1) * k_a                 (written and used by the bonus)
+ * run the recurrence, apply the optional epilogue, then multiply y by g.
+ *   k_k, k_a : [H*N] float32 per-channel parameters (required)
+ *   g        : [B,T,H,N] in dt, or NULL for no gate
+ */
+typedef struct {
+    const float *k_k;
+    const float *k_a;
+    const void *g;
+} rwkv7_prologue;
+
+/*
+ * rwkv7_wkv_forward fed from raw keys: r, w, k (raw), v, a : [B,T,H,N] in dt
+ * (float32 or bfloat16; RWKV7_DT_BF16_W32 returns RWKV7_ERR_UNSUPPORTED); no
+ * kappa argument.  pro is required.  Workspace, s0, s_out, y, the epilogue and
+ * the errors as rwkv7_wkv_forward (query the workspace there); g counts as an
+ * input for the overlap checks.
+ */
+rwkv7_status rwkv7_wkv_forward_fused(const void *r, const void *w, const void *k,
+                                     const void *v, const void *a, const rwkv7_prologue *pro,
+                                     const float *s0, void *y, float *s_out, int B, int T, int H,
+                                     int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                     const rwkv7_epilogue *epi, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
  * Bidirectional forward: the recurrence is run twice over the same inputs,
  * once over tokens 0 .. T-1 and once over tokens T-1 .. 0, and the two
  * readouts of each token are added; the optional epilogue then applies to the

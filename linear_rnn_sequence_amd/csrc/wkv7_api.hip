@@ -124,8 +124,10 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
                                  float *s_out, float *s_ckpt, bool want_ckpt, bool bidir, int B,
                                  int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
                                  const rwkv7_epilogue *epi, void *workspace,
-                                 size_t workspace_bytes, void *stream) {
+                                 size_t workspace_bytes, void *stream,
+                                 const rwkv7_prologue *pro = nullptr) {
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
+    if (pro && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
@@ -149,14 +151,20 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     size_t ck = st1;  // bytes of the stored states
     if (want_ckpt && !mul_ok(ck, (size_t)((T + kCkpt - 1) / kCkpt))) return RWKV7_ERR_SHAPE;
 
-    const void *ins[6] = {r, w, k, v, kappa, a};
+    // the six vectors, and the output gate of the fused prologue (kappa is
+    // formed in the kernel then: its pointer is not used)
+    const void *ins[7] = {r, w, k, v, pro ? nullptr : kappa, a, pro ? pro->g : nullptr};
     auto in_rng = [&](int i) {
         const uintptr_t lo = reinterpret_cast<uintptr_t>(ins[i]);
-        return Range{lo, lo + (i == 1 ? tok_w : tok)};
+        return lo ? Range{lo, lo + (i == 1 ? tok_w : tok)} : Range{0, 0};
     };
+    if (pro) {
+        if (!pro->k_k || !pro->k_a) return RWKV7_ERR_NULL;
+        if (!aligned16(pro->k_k) || !aligned16(pro->k_a)) return RWKV7_ERR_ALIGN;
+    }
     if (T > 0) {
-        for (const void *p : ins)
-            if (!p) return RWKV7_ERR_NULL;
+        for (int i = 0; i < 6; ++i)
+            if (!ins[i] && !(pro && i == 4)) return RWKV7_ERR_NULL;
         if (!y) return RWKV7_ERR_NULL;
         if (want_ckpt && !s_ckpt) return RWKV7_ERR_NULL;
     }
@@ -175,7 +183,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     };
     if (T > 0) {
         const Range ry = rng(y, tok);
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 7; ++i)
             if (overlap(ry, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (s0 && overlap(ry, rng(s0, st))) return RWKV7_ERR_ALIAS;
         if (s_out && overlap(ry, rng(s_out, st))) return RWKV7_ERR_ALIAS;
@@ -189,7 +197,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (s_out) {
         const Range rs = rng(s_out, st);
         if (T > 0)
-            for (int i = 0; i < 6; ++i)
+            for (int i = 0; i < 7; ++i)
                 if (overlap(rs, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (s0 && s0 != s_out && overlap(rs, rng(s0, st))) return RWKV7_ERR_ALIAS;
         if (epi) {
@@ -201,7 +209,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     }
     if (s_ckpt) {
         const Range rc = rng(s_ckpt, ck);
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 7; ++i)
             if (overlap(rc, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (overlap(rc, rng(y, tok)) || (s0 && overlap(rc, rng(s0, st))) ||
             (s_out && overlap(rc, rng(s_out, st))))
@@ -213,7 +221,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
         if (!workspace || workspace_bytes < need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
         const Range rw = rng(workspace, need);
-        for (int i = 0; i < 6; ++i)
+        for (int i = 0; i < 7; ++i)
             if (overlap(rw, in_rng(i))) return RWKV7_ERR_ALIAS;
         if (overlap(rw, rng(y, tok)) || (s0 && overlap(rw, rng(s0, st))) ||
             (s_out && overlap(rw, rng(s_out, st))) || (s_ckpt && overlap(rw, rng(s_ckpt, ck))))
@@ -237,6 +245,13 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     p.workspace = workspace;
     p.workspace_bytes = workspace_bytes;
     p.s_ckpt = s_ckpt;
+    if (pro) {
+        p.fused = true;
+        p.kappa = nullptr;
+        p.k_k = pro->k_k;
+        p.k_a = pro->k_a;
+        p.g = pro->g;
+    }
     auto run = [&](const ForwardArgs &q) {
         return al == RWKV7_ALGO_CHUNKED ? launch_chunked(q, hs) : launch_scan(q, hs);
     };
@@ -273,6 +288,17 @@ rwkv7_status rwkv7_wkv_forward(const void *r, const void *w, const void *k, cons
                                size_t workspace_bytes, void *stream) {
     return forward_impl(r, w, k, v, kappa, a, s0, y, s_out, nullptr, false, false, B, T, H, N,
                         dt, algo, epi, workspace, workspace_bytes, stream);
+}
+
+rwkv7_status rwkv7_wkv_forward_fused(const void *r, const void *w, const void *k,
+                                     const void *v, const void *a, const rwkv7_prologue *pro,
+                                     const float *s0, void *y, float *s_out, int B, int T, int H,
+                                     int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                     const rwkv7_epilogue *epi, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+    if (!pro) return RWKV7_ERR_NULL;
+    return forward_impl(r, w, k, v, nullptr, a, s0, y, s_out, nullptr, false, false, B, T, H, N,
+                        dt, algo, epi, workspace, workspace_bytes, stream, pro);
 }
 
 rwkv7_status rwkv7_wkv_forward_bidir(const void *r, const void *w, const void *k,

@@ -60,9 +60,14 @@ constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per la
 // s_waitcnt immediate (gfx9 encoding: vmcnt[3:0] + vmcnt[15:14], expcnt[6:4],
 // lgkmcnt[11:8]) that waits until at most 6*(kPrefetch-1) vector loads are
 // outstanding and does not wait on expcnt or lgkmcnt.
-constexpr int kLoadsPerChunk = 6;
-constexpr int kVm = kLoadsPerChunk * (kPrefetch - 1);
-constexpr int kWaitOlderChunks = (kVm & 0xF) | (0x7 << 4) | (0xF << 8) | (((kVm >> 4) & 0x3) << 14);
+// s_waitcnt immediate that lets the (kPrefetch-1) youngest chunks' loads stay in
+// flight: vmcnt = loads per chunk x (kPrefetch-1), lgkmcnt and expcnt unlimited.
+// Six loads per chunk (r, w, k, kappa, a, v); eight with the fused prologue
+// (r, w, k, a, v and the raw keys of the three other key blocks).
+constexpr int wait_older_chunks(int loads_per_chunk) {
+    return ((loads_per_chunk * (kPrefetch - 1)) & 0xF) | (0x7 << 4) | (0xF << 8) |
+           ((((loads_per_chunk * (kPrefetch - 1)) >> 4) & 0x3) << 14);
+}
 constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
 constexpr int kThreadsSummary = 768;    // + 4 chain waves for the transition rows
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
@@ -156,9 +161,17 @@ template <bool W32>
 struct Raw {
     uint2 r, k, kap, a, v;
     typename RawW<W32>::T w;
+    uint2 kx[3];  // fused prologue: raw keys of key blocks blk+1, blk+2, blk+3 (mod 4)
 };
 
-template <bool EPI, bool W32>
+// Fused prologue parameters of a prep lane: k_k of its four channels in each
+// key block (kk[i]: block blk+i mod 4) and k_a of its own channels.
+struct ProParams {
+    float kk[4][4];
+    float ka[4];
+};
+
+template <bool EPI, bool W32, bool FUSED>
 struct Chunked {
     const ForwardArgs &p;
     const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
@@ -193,7 +206,14 @@ struct Chunked {
         else
             x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
         x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
-        x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
+        if constexpr (FUSED) {
+#pragma unroll
+            for (int i = 0; i < 3; ++i)  // same token, the other key blocks' channels
+                x.kx[i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) +
+                                                           off + 16 * (((blk + 1 + i) & 3) - blk));
+        } else {
+            x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
+        }
         x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
         x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
     }
@@ -203,6 +223,7 @@ struct Chunked {
     __device__ __forceinline__ void pad(int c, Raw<W32> &x) const {
         if (c * kC + lo >= Tl) {
             x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
+            x.kx[0] = x.kx[1] = x.kx[2] = make_uint2(0u, 0u);
             if constexpr (W32)
                 x.w = make_float4(1.f, 1.f, 1.f, 1.f);
             else
@@ -211,7 +232,8 @@ struct Chunked {
     }
 
     // Chunk operands for key block jb = blk, written to LDS buffer `o`.
-    __device__ void prep(const Raw<W32> &x, ChunkOps &o, const float (&rk)[4]) const {
+    __device__ void prep(const Raw<W32> &x, ChunkOps &o, const float (&rk)[4],
+                         const ProParams &pro) const {
         const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
         float w[4];
         if constexpr (W32) {
@@ -220,10 +242,39 @@ struct Chunked {
             w[0] = bf16_lo(x.w.x); w[1] = bf16_hi(x.w.x);
             w[2] = bf16_lo(x.w.y); w[3] = bf16_hi(x.w.y);
         }
-        const float k[4] = {bf16_lo(x.k.x), bf16_hi(x.k.x), bf16_lo(x.k.y), bf16_hi(x.k.y)};
-        const float kp[4] = {bf16_lo(x.kap.x), bf16_hi(x.kap.x), bf16_lo(x.kap.y),
-                             bf16_hi(x.kap.y)};
+        float k[4] = {bf16_lo(x.k.x), bf16_hi(x.k.x), bf16_lo(x.k.y), bf16_hi(x.k.y)};
         const float a[4] = {bf16_lo(x.a.x), bf16_hi(x.a.x), bf16_lo(x.a.y), bf16_hi(x.a.y)};
+        float kp[4];
+        if constexpr (FUSED) {
+            // kappa = normalise(k * k_k) over the token's 64 channels (this lane's 4 in
+            // each key block, the four lanes g of the DPP column); k <- k + k (a-1) k_a
+            float kk[4], ss = 0.f;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kk[e] = k[e] * pro.kk[0][e];
+                ss += kk[e] * kk[e];
+            }
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                const float xo[4] = {bf16_lo(x.kx[i].x), bf16_hi(x.kx[i].x), bf16_lo(x.kx[i].y),
+                                     bf16_hi(x.kx[i].y)};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = xo[e] * pro.kk[i + 1][e];
+                    ss += t * t;
+                }
+            }
+            ss = sum_rows4(ss);
+            const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                kp[e] = kk[e] * inv;
+                k[e] = k[e] + k[e] * (a[e] - 1.f) * pro.ka[e];
+            }
+        } else {
+            kp[0] = bf16_lo(x.kap.x); kp[1] = bf16_hi(x.kap.x);
+            kp[2] = bf16_lo(x.kap.y); kp[3] = bf16_hi(x.kap.y);
+        }
         f32x4 G, Gx, Kp, Rp, Km, Bm;
         float bon = 0.f, dkr = 0.f, dbr = 0.f;
 #pragma unroll
@@ -352,11 +403,13 @@ struct Chunked {
 struct Pending {
     f32x4 y;
     float bon[4];
+    float gate[4];  // fused prologue: output gate of the four tokens
     bf16x4 v;
 };
 
-template <bool EPI, bool W32>
-__device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chunked<EPI, W32> &K,
+template <bool EPI, bool W32, bool FUSED>
+__device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
+                                                const Chunked<EPI, W32, FUSED> &K,
                                                 const ChunkSmem &sm, const Pending &pd, int c,
                                                 float lnw, float lnb, long yoff) {
     const int g = K.g;
@@ -376,6 +429,7 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
             yv[e] = (yv[e] - mu) * rs * lnw + lnb +
                     pd.bon[e] * bf16_lo((unsigned)(unsigned short)pd.v[e]);
         }
+        if (FUSED) yv[e] *= pd.gate[e];  // output gate (1 when none is given)
     }
     // yoff: element offset of token c*16 + 4g of this lane's value channel
     const int t0 = c * kC + 4 * g;
@@ -405,7 +459,7 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p, const Chun
 // SUMMARY = true: for each (b, h, segment) but the last, the segment's offset
 //   dS (waves 0..3: entry state 0) and transition P (waves 8..11: entry state I,
 //   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
-template <bool EPI, bool SUMMARY, bool W32>
+template <bool EPI, bool SUMMARY, bool W32, bool FUSED>
 __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_kernel(
     ChunkedParams cp) {
     __shared__ ChunkSmem sm;
@@ -414,7 +468,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
     const int seg = blockIdx.x - bh * cp.nseg_launch;
     const int b = bh / p.H, h = bh - b * p.H;
     const int t0 = seg * cp.seg_len;
-    const Chunked<EPI, W32> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
+    const Chunked<EPI, W32, FUSED> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
     const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
     const int wave = threadIdx.x >> 6;
     const bool chain_wave = wave < 4 || wave >= 8;  // waves 0..3 (and 8..11 in SUMMARY)
@@ -461,7 +515,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
             if (!SUMMARY && c > 0) {
-                finish_readouts<EPI, W32>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
+                finish_readouts<EPI, W32, FUSED>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
                 ylane += ystep;
             }
             if (c < nch) {
@@ -478,6 +532,14 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         if (c * kC + 4 * g + e < K.Tl) yadd[e] = p.y_add[ylane + e * K.TS];
+                }
+                if (FUSED && !SUMMARY) {  // output gate of this chunk's readouts
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        pd.gate[e] = (p.g && c * kC + 4 * g + e < K.Tl)
+                                         ? bf16_lo(static_cast<const uint16_t *>(p.g)
+                                                       [ylane + e * K.TS])
+                                         : 1.f;
                 }
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
@@ -534,6 +596,17 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
+        ProParams pro{};
+        if (FUSED) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 q = *reinterpret_cast<const float4 *>(
+                    p.k_k + h * kN + 16 * ((blk + i) & 3) + 4 * g);
+                pro.kk[i][0] = q.x; pro.kk[i][1] = q.y; pro.kk[i][2] = q.z; pro.kk[i][3] = q.w;
+            }
+            const float4 q = *reinterpret_cast<const float4 *>(p.k_a + h * kN + 16 * blk + 4 * g);
+            pro.ka[0] = q.x; pro.ka[1] = q.y; pro.ka[2] = q.z; pro.ka[3] = q.w;
+        }
         float rk[4] = {0.f, 0.f, 0.f, 0.f};
         if (EPI && !SUMMARY) {
             const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * blk + 4 * g);
@@ -552,14 +625,14 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
                 if (q < nch) {
                     if ((q + 1) * kC > K.Tl) K.pad(q, xs[d]);  // partial last chunk only
-                    K.prep(xs[d], sm.ops[q % 3], rk);
+                    K.prep(xs[d], sm.ops[q % 3], rk, pro);
                 }
                 K.load(q + kPrefetch, xs[d]);  // clamped: always six loads per interval
                 // the next interval consumes the oldest ring slot: let only the
                 // (kPrefetch-1) younger chunks' loads stay in flight.  Stated
                 // explicitly because the compiler's own count is lost across the
                 // loop's back edge and would wait for nearly every load.
-                __builtin_amdgcn_s_waitcnt(kWaitOlderChunks);
+                __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
                 __syncthreads();
             }
         }
@@ -675,7 +748,7 @@ size_t chunked_workspace_bytes(int B, int T, int H) {
     return (size_t)3 * B * H * nseg * kN * kN * sizeof(float);
 }
 
-template <bool W32>
+template <bool W32, bool FUSED>
 hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     const ForwardArgs &p = cp.p;
     const long bh = (long)p.B * p.H;
@@ -686,7 +759,7 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
         cp.ws_sin = cp.ws_ds + slab;
         // 1. transitions and offsets of every segment but the last
         cp.nseg_launch = cp.nseg - 1;
-        hipLaunchKernelGGL((chunked_kernel<false, true, W32>),
+        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED>),
                            dim3((unsigned)(bh * cp.nseg_launch)), dim3(kThreadsSummary), 0,
                            stream, cp);
         hipError_t e = hipGetLastError();
@@ -701,9 +774,9 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     cp.nseg_launch = cp.nseg;
     const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false, W32>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED>), grid, block, 0, stream, cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false, false, W32>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED>), grid, block, 0, stream, cp);
     return hipGetLastError();
 }
 
@@ -711,7 +784,10 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
     ChunkedParams cp{};
     cp.p = p;
     segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
-    return p.w32 ? launch_chunked_w<true>(cp, stream) : launch_chunked_w<false>(cp, stream);
+    // the fused prologue comes with bf16 decays only (the API refuses it with float32 w)
+    if (p.fused) return launch_chunked_w<false, true>(cp, stream);
+    return p.w32 ? launch_chunked_w<true, false>(cp, stream)
+                 : launch_chunked_w<false, false>(cp, stream);
 }
 
 }  // namespace wkv7

@@ -39,6 +39,12 @@ struct ForwardArgs {
     bool reverse;
     float *y_f32;
     const float *y_add;
+    // fused time-mix prologue: k holds the raw keys, kappa is unused; the kernels
+    // form kappa = normalise(k * k_k) and k <- k + k (a-1) k_a, and multiply the
+    // readouts (after the epilogue) by the gate g when it is given
+    bool fused;
+    const float *k_k, *k_a;  // [H*N]
+    const void *g;           // [B,T,H,N] in dt, or nullptr
 };
 
 constexpr int kCkpt = RWKV7_CKPT_INTERVAL;  // tokens between stored states

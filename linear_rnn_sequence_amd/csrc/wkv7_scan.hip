@@ -94,6 +94,12 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
             for (int e = 0; e < 8; ++e) S[r][e] = 0.f;
     }
 
+    // fused prologue parameters of this staging thread's 4 channels
+    float4 kk4p = make_float4(0.f, 0.f, 0.f, 0.f), ka4p = kk4p;
+    if (p.fused) {
+        kk4p = *reinterpret_cast<const float4 *>(p.k_k + h * kN + 4 * s_q);
+        ka4p = *reinterpret_cast<const float4 *>(p.k_a + h * kN + 4 * s_q);
+    }
     float4 rk4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 lnw4 = make_float4(1.f, 1.f, 1.f, 1.f), lnb4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (EPI) {
@@ -112,7 +118,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
             xw = LW::load(p.w, off);
             xk = L::load(p.k, off);
             xv = L::load(p.v, off);
-            xkap = L::load(p.kappa, off);
+            xkap = p.fused ? L::zero() : L::load(p.kappa, off);
             xa = L::load(p.a, off);
         } else {
             xr = xk = xv = xkap = xa = L::zero();
@@ -136,8 +142,18 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
             }
         }
         // ---- stage this chunk's vectors ----
-        const float4 r4 = L::widen(xr), w4 = LW::widen(xw), k4 = L::widen(xk);
-        const float4 v4 = L::widen(xv), kap4 = L::widen(xkap), a4 = L::widen(xa);
+        const float4 r4 = L::widen(xr), w4 = LW::widen(xw);
+        float4 k4 = L::widen(xk), kap4 = L::widen(xkap);
+        const float4 v4 = L::widen(xv), a4 = L::widen(xa);
+        if (p.fused) {
+            // kappa = normalise(k * k_k) over the token's 64 channels (the 16 lanes of
+            // this DPP row); k <- k + k (a-1) k_a
+            const float4 kk = mul4(k4, kk4p);
+            const float inv = 1.f / fmaxf(sqrtf(sum_lanes16(dot4(kk, kk))), 1e-12f);
+            kap4 = make_float4(kk.x * inv, kk.y * inv, kk.z * inv, kk.w * inv);
+            k4 = make_float4(k4.x + k4.x * (a4.x - 1.f) * ka4p.x, k4.y + k4.y * (a4.y - 1.f) * ka4p.y,
+                             k4.z + k4.z * (a4.z - 1.f) * ka4p.z, k4.w + k4.w * (a4.w - 1.f) * ka4p.w);
+        }
         const float4 b4 = mul4(a4, kap4);
         const float4 wr4 = mul4(w4, r4);
         float kr = sum_lanes16(dot4(k4, r4));
@@ -218,6 +234,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
                 y4.y = d.y * rs * lnw4.y + lnb4.y + bz * vz.y;
                 y4.z = d.z * rs * lnw4.z + lnb4.z + bz * vz.z;
                 y4.w = d.w * rs * lnw4.w + lnb4.w + bz * vz.w;
+            }
+            if (p.g) {  // output gate (fused prologue)
+                const float4 g4 = L::widen(L::load(p.g, yo));
+                y4.x *= g4.x; y4.y *= g4.y; y4.z *= g4.z; y4.w *= g4.w;
             }
             if (p.y_f32)  // float32 readouts (first pass of a bidirectional call)
                 *reinterpret_cast<float4 *>(p.y_f32 + yo) = y4;

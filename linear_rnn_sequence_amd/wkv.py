@@ -30,6 +30,10 @@ class Rwkv7Error(RuntimeError):
         super().__init__(f"{where}: {STATUS.get(code, code)} ({_status_str(code)})")
 
 
+class Prologue(ctypes.Structure):
+    _fields_ = [("k_k", ctypes.c_void_p), ("k_a", ctypes.c_void_p), ("g", ctypes.c_void_p)]
+
+
 class Epilogue(ctypes.Structure):
     _fields_ = [("ln_w", ctypes.c_void_p), ("ln_b", ctypes.c_void_p),
                 ("r_k", ctypes.c_void_p), ("eps", ctypes.c_float)]
@@ -55,6 +59,10 @@ def lib():
         L.rwkv7_wkv_forward_workspace.restype = sz
         L.rwkv7_wkv_decode.argtypes = [vp] * 8 + [ci] * 4 + [ctypes.POINTER(Epilogue), vp]
         L.rwkv7_wkv_decode.restype = ci
+        L.rwkv7_wkv_forward_fused.argtypes = ([vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 3
+                                              + [ci] * 6 + [ctypes.POINTER(Epilogue), vp, sz,
+                                                            vp])
+        L.rwkv7_wkv_forward_fused.restype = ci
         L.rwkv7_wkv_forward_bidir.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue),
                                                                    vp, sz, vp]
         L.rwkv7_wkv_forward_bidir.restype = ci
@@ -166,6 +174,40 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
     del keep
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_forward")
+    return y, s_out
+
+
+def forward_fused(r, w, k, v, a, k_k, k_a, g=None, s0=None, *, algo="auto", epilogue=None,
+                  y=None, s_out=None, want_state=True, workspace=None, stream=None):
+    """rwkv7_wkv_forward_fused: the recurrence fed from raw keys k.  The kernels form
+    kappa = normalise(k * k_k) and k + k (a-1) k_a, and multiply y (after the epilogue) by
+    the gate g if given.  k_k, k_a: f32 [H*N] (or [H,N]); g like r.  Returns (y, s_out)."""
+    import torch
+
+    B, T, H, N = r.shape
+    _check_same(torch, (r, w, k, v, a) + (() if g is None else (g,)), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    for prm in (k_k, k_a):
+        if prm.dtype != torch.float32 or prm.numel() != H * N or not prm.is_contiguous():
+            raise ValueError("k_k and k_a must be contiguous float32 tensors of H*N elements")
+    if y is None:
+        y = torch.empty_like(r)
+    if s_out is None and want_state:
+        s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    need = lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo])
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=r.device)
+    pro = Prologue(k_k=k_k.data_ptr(), k_a=k_a.data_ptr(),
+                   g=None if g is None else g.data_ptr())
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_forward_fused(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a), ctypes.byref(pro), _ptr(s0), _ptr(y),
+        _ptr(s_out), B, T, H, N, dt, ALGOS[algo], epi_ptr, _ptr(workspace),
+        0 if workspace is None else workspace.numel() * workspace.element_size(),
+        _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_forward_fused")
     return y, s_out
 
 

@@ -181,6 +181,24 @@ def draw(
     return out
 
 
+def prologue_extras(B: int, T: int, H: int, N: int = N_HEAD_SIZE, *, seed: int,
+                    dtype: str = "bf16"):
+    """Parameters of the fused time-mix prologue and the output gate: k_k, k_a
+    [H*N] float32 ~ N(1, 0.1) (per-channel scales near one; the pages give no
+    values) and g [B,T,H,N] ~ N(0, 1) stored in ``dtype``.  numpy PCG64
+    ``default_rng(seed)``, drawn in that order."""
+    rng = np.random.default_rng(seed)
+    f32 = np.float32
+    k_k = (f32(1.0) + rng.standard_normal(H * N, dtype=f32) * f32(0.1)).astype(f32)
+    k_a = (f32(1.0) + rng.standard_normal(H * N, dtype=f32) * f32(0.1)).astype(f32)
+    g = rng.standard_normal((B, T, H, N), dtype=f32)
+    if dtype == "bf16":
+        g = f32_to_bf16_bits(g)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return k_k, k_a, g
+
+
 def cotangents(B: int, T: int, H: int, N: int = N_HEAD_SIZE, *, seed: int,
                dtype: str = "bf16", with_state: bool = True, std: float = 1.0):
     """Output cotangents for the training path: dy [B,T,H,N] ~ N(0, std) stored in

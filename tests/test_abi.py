@@ -197,3 +197,23 @@ def test_bidir_validation_codes():
     st = 2 * 3 * 64 * 64 * 4
     assert bid(s_out=fake(6, st)) == 6             # s_out over s0's second state
     assert bid(T=0, s_out=None) == 0
+
+
+_Pro = wkv.Prologue
+
+
+def test_fused_validation_codes():
+    L = wkv.lib()
+
+    def fu(pro=None, dt=1, T=8, y=fake(9), s_out=fake(10)):
+        p = None if pro is None else ctypes.byref(pro)
+        return L.rwkv7_wkv_forward_fused(*[fake(i) for i in range(5)], p, fake(6), y, s_out, 2,
+                                         T, 3, 64, dt, 1, None, None, 0, None)
+    ok = _Pro(k_k=A + 11 * STRIDE, k_a=A + 12 * STRIDE, g=A + 13 * STRIDE)
+    assert fu(None) == 1
+    assert fu(_Pro(k_k=None, k_a=A + 12 * STRIDE, g=None)) == 1
+    assert fu(_Pro(k_k=A + 11 * STRIDE + 4, k_a=A + 12 * STRIDE, g=None)) == 5
+    assert fu(ok, dt=2) == 4                           # no fused prologue with float32 w
+    assert fu(ok, y=fake(13, 128)) == 6                # y over the gate
+    assert fu(ok, s_out=fake(13)) == 6                 # s_out over the gate
+    assert fu(ok, T=0, s_out=None) == 0                # no kappa argument needed
