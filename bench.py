@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' needs --only prefill")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the fused prologue + output gate forward from raw keys "
+                         "(needs --only prefill)")
     ap.add_argument("--bidir", action="store_true",
                     help="time the bidirectional forward (needs --only prefill)")
     ap.add_argument("--decay-f32", action="store_true",
@@ -134,7 +137,9 @@ def workload_name(args, long_shape, do_prefill, do_decode):
         return ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue"
                 + (", decay w in float32)" if args.decay_f32 else ")"))
     pre = ("2.9B-shape WKV7 prefill B8 T4096 H40 N64 with fused GroupNorm+bonus epilogue"
-           + (" (bidirectional: epilogue on the sum of both passes)" if args.bidir else ""))
+           + (" (bidirectional: epilogue on the sum of both passes)" if args.bidir else "")
+           + (" and the fused prologue (kappa, k-tilde from raw keys) and output gate"
+              if args.fused else ""))
     dec = "decode of 64 tokens through 32 layers x B256 x H40 resident fp32 states"
     if do_prefill and do_decode:
         return "2.9B-shape WKV7: " + pre.replace("2.9B-shape WKV7 ", "") + ", then " + dec
@@ -273,7 +278,8 @@ def main():
         sys.exit(2)
 
     cfg_idx, PREFILL, p_with_epi = PREFILL_SHAPES[args.prefill_shape]
-    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir) and args.only != "prefill":
+    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir or args.fused) and \
+            args.only != "prefill":
         print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
               "(--only prefill)", file=sys.stderr)
         sys.exit(2)
@@ -333,7 +339,17 @@ def main():
         p_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         p_gen_s = time.time() - t0
 
+        if args.fused:  # raw keys (the draw's k), prologue parameters and the gate
+            pk_k, pk_a, pg = synth.prologue_extras(B, T, H, seed=1000 + cfg_idx)
+            f_kk, f_ka = torch.from_numpy(pk_k).to(dev), torch.from_numpy(pk_a).to(dev)
+            f_g = torch.from_numpy(pg.view(np.int16)).to(dev).view(torch.bfloat16)
+
         def prefill():
+            if args.fused:
+                wkv.forward_fused(*(pd[n] for n in ("r", "w", "k", "v", "a")), f_kk, f_ka,
+                                  g=f_g, algo=args.prefill_algo, epilogue=p_epi, y=p_y,
+                                  s_out=p_s, workspace=p_ws)
+                return
             (wkv.forward_bidir if args.bidir else wkv.forward)(
                 *(pd[n] for n in NAMES), s0=None, algo=args.prefill_algo, epilogue=p_epi, y=p_y,
                 s_out=p_s, workspace=p_ws)
@@ -450,6 +466,7 @@ def main():
             "workload": workload_name(args, long_shape, do_prefill, do_decode),
             "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=p_with_epi,
                             workspace_bytes=ws_bytes, bidirectional=args.bidir,
+                            fused_prologue=args.fused,
                             decay_dtype="f32" if args.decay_f32 else "bf16")
             if do_prefill else None,
             "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
@@ -519,8 +536,14 @@ def main():
         if args.decay_f32:
             sub[1] = pd["w"].cpu().numpy().astype(np.float64)
         t0 = time.perf_counter()
-        y_ref, s_ref = (oracle.forward_bidir if args.bidir else oracle.forward)(
-            *sub, s0=None, epilogue=px["epi"] if p_with_epi else None, threads=threads)
+        if args.fused:
+            g64 = synth.bf16_bits_to_f32(pg).astype(np.float64)
+            y_ref, s_ref = oracle.forward_fused(
+                *(px.as_f64(n) for n in ("r", "w", "k", "v", "a")), pk_k, pk_a, g=g64, s0=None,
+                epilogue=px["epi"] if p_with_epi else None, threads=threads)
+        else:
+            y_ref, s_ref = (oracle.forward_bidir if args.bidir else oracle.forward)(
+                *sub, s0=None, epilogue=px["epi"] if p_with_epi else None, threads=threads)
         cpu_s += time.perf_counter() - t0
         cpu_work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
         del sub

@@ -30,8 +30,9 @@
  *    decay, r the receptance.  The library applies no transform to any of them.
  *  - States are float32 [B, H, N, N], row-major: state[b][h][i][j], i = value
  *    index, j = key index.
- *  - N must be 64 (the head size the pages' kernels are tuned for); B, H >= 1;
- *    T >= 0.  All internal offsets are 64-bit.
+ *  - N must be 64 (the head size the pages' kernels are tuned for), except
+ *    for rwkv7_wkv_decode, which also takes N = 128; B, H >= 1; T >= 0.  All
+ *    internal offsets are 64-bit.
  *  - Every pointer must be 16-byte aligned.
  *  - All validation runs on the host, synchronously, before anything is
  *    enqueued: on any error nothing is launched and nothing is written.
@@ -59,7 +60,7 @@ typedef enum {
     RWKV7_ERR_NULL = 1,        /* a required pointer is NULL                         */
     RWKV7_ERR_SHAPE = 2,       /* B < 1, H < 1, T < 0, or a size overflows            */
     RWKV7_ERR_DTYPE = 3,       /* unknown dtype / algo value                          */
-    RWKV7_ERR_UNSUPPORTED = 4, /* N != 64, or algo not available for this dtype      */
+    RWKV7_ERR_UNSUPPORTED = 4, /* head size, or algo/entry not available for dtype    */
     RWKV7_ERR_ALIGN = 5,       /* a pointer is not 16-byte aligned                    */
     RWKV7_ERR_ALIAS = 6,       /* an output overlaps an input (other than s_out==s0) */
     RWKV7_ERR_WORKSPACE = 7,   /* workspace missing or smaller than required          */
@@ -188,6 +189,8 @@ size_t rwkv7_wkv_forward_bidir_workspace(int B, int T, int H, int N, rwkv7_dtype
 /*
  * One token for each of B resident states (single-token inference, the
  * recurrence at T = 1 with the state read from and written back to HBM).
+ * Head size N = 64 or 128 (RWKV-7 "Goose" summary, §8 Speed and Memory: the
+ * pages' kernels are tuned for 64 and lose efficiency at larger heads).
  *   r, w, k, v, kappa, a : [B,H,N] in dt
  *   state : [B,H,N,N] float32, updated in place (for a layer-major pool the
  *           caller passes the layer's slice)

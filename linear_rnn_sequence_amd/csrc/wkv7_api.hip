@@ -75,7 +75,8 @@ const char *rwkv7_status_str(rwkv7_status s) {
         case RWKV7_ERR_NULL: return "a required pointer is NULL";
         case RWKV7_ERR_SHAPE: return "invalid shape (B, H >= 1, T >= 0, sizes must fit)";
         case RWKV7_ERR_DTYPE: return "unknown dtype or algorithm";
-        case RWKV7_ERR_UNSUPPORTED: return "unsupported (N must be 64; chunked needs bf16)";
+        case RWKV7_ERR_UNSUPPORTED:
+            return "unsupported (head size, or algorithm/entry point for this dtype)";
         case RWKV7_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case RWKV7_ERR_ALIAS: return "an output overlaps an input";
         case RWKV7_ERR_WORKSPACE: return "workspace missing or too small";
@@ -403,7 +404,7 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
                               int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
                               void *stream) {
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
-    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1) return RWKV7_ERR_SHAPE;
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
@@ -413,8 +414,8 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
     tok = tok / 4 * esz;                                       // bytes of the other vectors
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
-    // two waves (workgroups) per head: keep 2*B*H within the grid's x limit
-    if ((size_t)B * H > 0x3fffffffu) return RWKV7_ERR_SHAPE;
+    // N/32 * 2 waves (workgroups) per head: keep the grid within its x limit
+    if ((size_t)B * H * (N == 128 ? 8 : 2) > 0xffffffffu) return RWKV7_ERR_SHAPE;
     const void *ins[6] = {r, w, k, v, kappa, a};
     auto in_rng = [&](int i) {
         const uintptr_t lo = reinterpret_cast<uintptr_t>(ins[i]);
@@ -443,7 +444,7 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
     }
     DecodeArgs p{};
     p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
-    p.state = state; p.y = y; p.B = B; p.H = H;
+    p.state = state; p.y = y; p.B = B; p.H = H; p.N = N;
     p.bf16 = dt != RWKV7_DT_F32;
     p.w32 = dt == RWKV7_DT_BF16_W32;
     p.epilogue = epi != nullptr;

@@ -28,7 +28,7 @@
 namespace wkv7 {
 namespace {
 
-constexpr int kRows = 8;  // value rows per lane; a wave covers 32 rows, a head two waves
+constexpr int kRows = 8;  // value rows per lane
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -63,24 +63,45 @@ __device__ __forceinline__ void load8(const float *p, float *out) {
     }
 }
 
-template <class IO, bool EPI, bool NT, bool W32>
-__global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
+// Lane layout for head size N: N/4 lanes cover one state row (4 key columns
+// each, 16 bytes), so a wave holds 64/(N/4) row groups of kRows rows.
+template <int N>
+struct DecodeShape {
+    static constexpr int kLanesPerRow = N / 4;                  // 16 (N=64) or 32 (N=128)
+    static constexpr int kGroups = 64 / kLanesPerRow;           // 4 or 2
+    static constexpr int kRowsPerWave = kGroups * kRows;        // 32 or 16
+    static constexpr int kWavesPerHead = N / kRowsPerWave;      // 2 or 8
+};
+
+// Sum over the lanes of one state row (16 or 32 lanes).
+template <int N>
+__device__ __forceinline__ float row_sum(float x) {
+    x = sum_lanes16(x);
+    if constexpr (N == 128) x = swap16_add(x, x);  // adjacent DPP rows: lanes l, l^16
+    return x;
+}
+
+template <class IO, bool EPI, bool NT, bool W32, int N>
+__global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void decode_kernel(
+    DecodeArgs p) {
     using E = typename IO::elem;
-    __shared__ float2 xch[2];  // epilogue: (mean, M2) of each half head
+    using Sh = DecodeShape<N>;
+    constexpr int kW = Sh::kWavesPerHead;
+    __shared__ float2 xch[kW];  // epilogue: (mean, M2) of each wave's rows
     const int lane = threadIdx.x & 63;
-    const long head = EPI ? (long)blockIdx.x : (long)(blockIdx.x >> 1);
-    const int part = EPI ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x & 1);
+    const long head = EPI ? (long)blockIdx.x : (long)(blockIdx.x / kW);
+    const int part = EPI ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x % kW);
     if (head >= (long)p.B * p.H) return;  // whole workgroup leaves together
     const int h = (int)(head % p.H);
-    const int c = lane & 15, g = lane >> 4;
-    const int r0 = 32 * part + kRows * g;  // this lane's value rows r0 .. r0+7
+    const int c = lane % Sh::kLanesPerRow, g = lane / Sh::kLanesPerRow;
+    const int r0 = Sh::kRowsPerWave * part + kRows * g;  // this lane's value rows r0 .. r0+7
 
-    float *st = p.state + head * (kN * kN) + r0 * kN + 4 * c;
+    float *st = p.state + head * (N * N) + r0 * N + 4 * c;
     f32x4 S[kRows];
 #pragma unroll
-    for (int m = 0; m < kRows; ++m) S[m] = ld_state<NT>(st + m * kN);
+    for (int m = 0; m < kRows; ++m) S[m] = ld_state<NT>(st + m * N);
 
-    const long vo = head * kN;
+    const long vo = head * N;
     const E *pr = static_cast<const E *>(p.r) + vo;
     const float4 kap = IO::load4(static_cast<const E *>(p.kappa) + vo + 4 * c);
     const float4 w = W32 ? F32In::load4(static_cast<const float *>(p.w) + vo + 4 * c)
@@ -97,7 +118,7 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     float br = bb.x * r.x + bb.y * r.y + bb.z * r.z + bb.w * r.w;
     float bon = 0.f;
     if (EPI) {
-        const float4 rk = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 4 * c);
+        const float4 rk = *reinterpret_cast<const float4 *>(p.epi.r_k + h * N + 4 * c);
         bon = r.x * k.x * rk.x + r.y * k.y * rk.y + r.z * k.z * rk.z + r.w * k.w * rk.w;
     }
 
@@ -109,12 +130,12 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     }
 #pragma unroll
     for (int m = 0; m < kRows; ++m) {
-        u[m] = sum_lanes16(u[m]);
-        y[m] = sum_lanes16(y[m]);
+        u[m] = row_sum<N>(u[m]);
+        y[m] = row_sum<N>(y[m]);
     }
-    kr = sum_lanes16(kr);
-    br = sum_lanes16(br);
-    if (EPI) bon = sum_lanes16(bon);
+    kr = row_sum<N>(kr);
+    br = row_sum<N>(br);
+    if (EPI) bon = row_sum<N>(bon);
 
 #pragma unroll
     for (int m = 0; m < kRows; ++m) {
@@ -124,7 +145,7 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
         s.y = s.y * w.y - u[m] * bb.y + v[m] * k.y;
         s.z = s.z * w.z - u[m] * bb.z + v[m] * k.z;
         s.w = s.w * w.w - u[m] * bb.w + v[m] * k.w;
-        st_state<NT>(st + m * kN, s);
+        st_state<NT>(st + m * N, s);
     }
 
     // lane c < 8 keeps row r0 + c
@@ -136,23 +157,33 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
         vo1 = (sel == m) ? v[m] : vo1;
     }
     if (EPI) {
-        // statistics of this wave's 32 rows, then Chan's combination of the two halves
+        // statistics of this wave's rows, then Chan's combination over the head's waves
         float s1 = 0.f;
 #pragma unroll
         for (int m = 0; m < kRows; ++m) s1 += y[m];
-        const float mu_w = sum_rows4(s1) * (1.f / 32.f);
+        // sum over the wave's row groups (every lane of a group holds its 8 rows' sums)
+        s1 = (N == 64) ? sum_rows4(s1) : swap32_add(s1, s1);
+        const float mu_w = s1 * (1.f / Sh::kRowsPerWave);
         float s2 = 0.f;
 #pragma unroll
         for (int m = 0; m < kRows; ++m) s2 += (y[m] - mu_w) * (y[m] - mu_w);
-        const float m2_w = sum_rows4(s2);
+        const float m2_w = (N == 64) ? sum_rows4(s2) : swap32_add(s2, s2);
         if (lane == 0) xch[part] = make_float2(mu_w, m2_w);
         __syncthreads();
-        const float2 q0 = xch[0], q1 = xch[1];
-        const float mu = 0.5f * (q0.x + q1.x);
-        const float d0 = q0.x - mu, d1 = q1.x - mu;
-        const float var = (q0.y + q1.y + 32.f * (d0 * d0 + d1 * d1)) * (1.f / kN);
+        float mu = 0.f;
+#pragma unroll
+        for (int q = 0; q < kW; ++q) mu += xch[q].x;
+        mu *= 1.f / kW;
+        float m2 = 0.f, dev = 0.f;
+#pragma unroll
+        for (int q = 0; q < kW; ++q) {
+            const float2 x = xch[q];
+            m2 += x.y;
+            dev += (x.x - mu) * (x.x - mu);
+        }
+        const float var = (m2 + (float)Sh::kRowsPerWave * dev) * (1.f / N);
         const float rs = __builtin_amdgcn_rsqf(var + p.epi.eps);
-        const int ch = h * kN + r0 + sel;
+        const int ch = h * N + r0 + sel;
         const float gw = p.epi.ln_w ? p.epi.ln_w[ch] : 1.f;
         const float gb = p.epi.ln_b ? p.epi.ln_b[ch] : 0.f;
         yo = (yo - mu) * rs * gw + gb + bon * vo1;
@@ -160,36 +191,32 @@ __global__ __launch_bounds__(EPI ? 128 : 64) void decode_kernel(DecodeArgs p) {
     if (c < kRows) IO::store1(static_cast<E *>(p.y) + vo + r0 + c, yo);
 }
 
+template <int N, class IO, bool W32>
+hipError_t launch_decode_n(const DecodeArgs &p, hipStream_t stream) {
+    constexpr int kW = DecodeShape<N>::kWavesPerHead;
+    const long heads = (long)p.B * p.H;
+    // without the epilogue: one 64-thread workgroup per wave of a head; with it:
+    // one workgroup per head holding all its waves
+    if (p.epilogue)
+        hipLaunchKernelGGL((decode_kernel<IO, true, true, W32, N>), dim3((unsigned)heads),
+                           dim3(64 * kW), 0, stream, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N>),
+                           dim3((unsigned)(kW * heads)), dim3(64), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <int N>
+hipError_t launch_decode_dt(const DecodeArgs &p, hipStream_t stream) {
+    if (p.bf16 && p.w32) return launch_decode_n<N, Bf16In, true>(p, stream);
+    if (p.bf16) return launch_decode_n<N, Bf16In, false>(p, stream);
+    return launch_decode_n<N, F32In, false>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream) {
-    const long heads = (long)p.B * p.H;
-    // without the epilogue: one 64-thread workgroup per half head; with it: one
-    // 128-thread workgroup per head
-    const dim3 grid_half((unsigned)(2 * heads)), grid_head((unsigned)heads);
-    if (p.bf16 && p.w32) {
-        if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true, true>), grid_head, dim3(128), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true, true>), grid_half, dim3(64), 0,
-                               stream, p);
-    } else if (p.bf16) {
-        if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<Bf16In, true, true, false>), grid_head, dim3(128), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<Bf16In, false, true, false>), grid_half, dim3(64), 0,
-                               stream, p);
-    } else {
-        if (p.epilogue)
-            hipLaunchKernelGGL((decode_kernel<F32In, true, true, false>), grid_head, dim3(128), 0,
-                               stream, p);
-        else
-            hipLaunchKernelGGL((decode_kernel<F32In, false, true, false>), grid_half, dim3(64), 0,
-                               stream, p);
-    }
-    return hipGetLastError();
+    return p.N == 128 ? launch_decode_dt<128>(p, stream) : launch_decode_dt<64>(p, stream);
 }
 
 }  // namespace wkv7

@@ -65,6 +65,7 @@ struct DecodeArgs {
     float *state;                           // [B,H,N,N], in place
     void *y;                                // [B,H,N] in dt
     int B, H;
+    int N;                                  // head size: 64 or 128
     bool bf16;
     bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;

@@ -86,7 +86,7 @@ def test_decode_validation_codes():
         ins = ins or [fake(i) for i in range(6)]
         return L.rwkv7_wkv_decode(*ins, state, y, B, H, N, dt, epi, None)
 
-    assert dec(N=128) == 4
+    assert dec(N=96) == 4
     assert dec(B=0) == 2
     assert dec(dt=5) == 3
     assert dec(state=None) == 1 and dec(y=None) == 1
@@ -217,3 +217,15 @@ def test_fused_validation_codes():
     assert fu(ok, y=fake(13, 128)) == 6                # y over the gate
     assert fu(ok, s_out=fake(13)) == 6                 # s_out over the gate
     assert fu(ok, T=0, s_out=None) == 0                # no kappa argument needed
+
+
+def test_decode_head_size_128_validation():
+    L = wkv.lib()
+    ins = [fake(i) for i in range(6)]
+
+    def dec(N, state=fake(6), y=fake(7)):
+        return L.rwkv7_wkv_decode(*ins, state, y, 2, 3, N, 1, None, None)
+    assert dec(96) == 4 and dec(256) == 4
+    # N = 128: the state spans 2*3*128*128*4 bytes, so y just inside its end overlaps
+    assert dec(128, y=fake(6, 2 * 3 * 128 * 128 * 4 - 16)) == 6
+    assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 128, 1, 0) == 0
