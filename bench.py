@@ -57,6 +57,9 @@ def parse():
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' needs --only prefill")
+    ap.add_argument("--decode-head", type=int, default=64, choices=[64, 128],
+                    help="decode head size; 128 keeps the state bytes (H = 20) and needs "
+                         "--only decode")
     ap.add_argument("--fused", action="store_true",
                     help="time the fused prologue + output gate forward from raw keys "
                          "(needs --only prefill)")
@@ -140,7 +143,10 @@ def workload_name(args, long_shape, do_prefill, do_decode):
            + (" (bidirectional: epilogue on the sum of both passes)" if args.bidir else "")
            + (" and the fused prologue (kappa, k-tilde from raw keys) and output gate"
               if args.fused else ""))
-    dec = "decode of 64 tokens through 32 layers x B256 x H40 resident fp32 states"
+    dec = ("decode of 64 tokens through 32 layers x B256 x H40 resident fp32 states"
+           if args.decode_head == 64 else
+           "decode of 64 tokens through 32 layers x B256 x H20 resident fp32 states of head "
+           "size 128")
     if do_prefill and do_decode:
         return "2.9B-shape WKV7: " + pre.replace("2.9B-shape WKV7 ", "") + ", then " + dec
     return pre if do_prefill else "2.9B-shape WKV7 " + dec
@@ -278,6 +284,10 @@ def main():
         sys.exit(2)
 
     cfg_idx, PREFILL, p_with_epi = PREFILL_SHAPES[args.prefill_shape]
+    if args.decode_head != 64 and args.only != "decode":
+        print("bench.py: --decode-head 128 is a decode-only measurement (--only decode)",
+              file=sys.stderr)
+        sys.exit(2)
     if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir or args.fused) and \
             args.only != "prefill":
         print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
@@ -357,20 +367,22 @@ def main():
     # ------------------------------------------------------------------- decode
     if do_decode:
         t0 = time.time()
-        L, DB, DH, DS = DECODE["layers"], DECODE["B"], DECODE["H"], args.decode_steps
-        pool = synth.decode_states_device(torch, dev, layers=L, B=DB, H=DH, N=N, seed=3)
+        L, DB, DS = DECODE["layers"], DECODE["B"], args.decode_steps
+        DN = args.decode_head
+        DH = DECODE["H"] * 64 // DN  # head size 128: 20 heads, the same state bytes
+        pool = synth.decode_states_device(torch, dev, layers=L, B=DB, H=DH, N=DN, seed=3)
         # host copies of the initial states of the layers the oracle replays (parity and
         # CPU baseline), taken before any step
         samp_l = list(range(min(args.cpu_layers, L)))
         s_init = pool[samp_l].cpu().numpy() if not args.no_cpu_baseline else None
         d_in = {n: [] for n in NAMES}
         for t in range(DS):
-            one = synth.decode_step_inputs_device(torch, dev, B=DB, H=DH, N=N, seed=1000 + t,
+            one = synth.decode_step_inputs_device(torch, dev, B=DB, H=DH, N=DN, seed=1000 + t,
                                                   count=L)
             for n in NAMES:
                 d_in[n].append(one[n])
         d_in = {n: torch.stack(v) for n, v in d_in.items()}  # [DS, L, B, H, N]
-        d_y = torch.empty((DS, L, DB, DH, N), dtype=torch.bfloat16, device=dev)
+        d_y = torch.empty((DS, L, DB, DH, DN), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         d_gen_s = time.time() - t0
         n_launch = DS * L
@@ -469,7 +481,7 @@ def main():
                             fused_prologue=args.fused,
                             decay_dtype="f32" if args.decay_f32 else "bf16")
             if do_prefill else None,
-            "decode": dict(DECODE, N=N, steps=args.decode_steps) if do_decode else None,
+            "decode": dict(DECODE, N=DN, H=DH, steps=args.decode_steps) if do_decode else None,
             "state_dtype": "f32",
         },
     }
@@ -477,12 +489,13 @@ def main():
     if do_decode:
         run_ms = np.array([a.elapsed_time(b) for a, b in launch_ms])
         avg_ms = float(run_ms.sum() / (len(run_ms) * n_launch))  # per launch, gaps included
-        bytes_per_launch = DB * DH * (2 * N * N * 4 + 7 * N * 2)
+        bytes_per_launch = DB * DH * (2 * DN * DN * 4 + 7 * DN * 2)
         achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
-        traffic = read_traffic("decode_kernel_traffic.txt",
-                               source_hash("wkv7_decode.hip", "wkv7_device.h"))
+        traffic = (read_traffic("decode_kernel_traffic.txt",
+                                source_hash("wkv7_decode.hip", "wkv7_device.h"))
+                   if DN == 64 else None)
         out["roofline"] = {
-            "kernel": "wkv7 decode_kernel<bf16> (one layer, B256 x H40)",
+            "kernel": f"wkv7 decode_kernel<bf16, N={DN}> (one layer, B256 x H{DH})",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
             "bytes_per_launch": bytes_per_launch, "avg_launch_us": avg_ms * 1e3,
@@ -567,8 +580,8 @@ def main():
             errs.append(np.abs(y_got - y_ref).max() / np.abs(y_ref).max())
             del y_ref, y_got
         par["decode_y_rel_err"] = float(max(errs))
-        par["decode_checked"] = (f"every output of layers 0..{len(samp_l) - 1} (all 256 "
-                                 f"sequences x 40 heads x {DS} tokens)")
+        par["decode_checked"] = (f"every output of layers 0..{len(samp_l) - 1} (all {DB} "
+                                 f"sequences x {DH} heads x {DS} tokens)")
     if par:
         par["bound"] = 2e-2
         out["parity_sampled"] = par
