@@ -89,22 +89,24 @@ static bool valid_dtype(rwkv7_dtype dt) {
     return dt == RWKV7_DT_F32 || dt == RWKV7_DT_BF16 || dt == RWKV7_DT_BF16_W32;
 }
 
-static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt) {
+// AUTO: the chunked kernel for bf16 inputs at head size 64, else the scan.
+static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt, int N = kN) {
     if (algo == RWKV7_ALGO_AUTO)
-        return (dt != RWKV7_DT_F32 && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+        return (dt != RWKV7_DT_F32 && N == kN && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED
+                                                                    : RWKV7_ALGO_SCAN;
     return algo;
 }
 
 size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo) {
-    if (B < 1 || H < 1 || T < 0 || N != kN) return 0;
+    if (B < 1 || H < 1 || T < 0 || (N != 64 && N != 128)) return 0;
     if (!valid_dtype(dt)) return 0;
-    if (resolve_algo(algo, dt) != RWKV7_ALGO_CHUNKED || T == 0) return 0;
+    if (resolve_algo(algo, dt, N) != RWKV7_ALGO_CHUNKED || T == 0 || N != kN) return 0;
     return chunked_workspace_bytes(B, T, H);
 }
 
 size_t rwkv7_wkv_forward_bidir_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                          rwkv7_algo algo) {
-    if (B < 1 || H < 1 || T <= 0 || N != kN || !valid_dtype(dt)) return 0;
+    if (B < 1 || H < 1 || T <= 0 || (N != 64 && N != 128) || !valid_dtype(dt)) return 0;
     size_t n = 1;
     if (!mul_ok(n, (size_t)B) || !mul_ok(n, (size_t)T) || !mul_ok(n, (size_t)H) ||
         !mul_ok(n, (size_t)N * 4))
@@ -115,7 +117,7 @@ size_t rwkv7_wkv_forward_bidir_workspace(int B, int T, int H, int N, rwkv7_dtype
 }  // extern "C"
 
 // Bytes of the float32 readouts of a bidirectional call's reverse pass.
-static size_t bidir_yrev_bytes(int B, int T, int H) { return (size_t)B * T * H * kN * 4; }
+static size_t bidir_yrev_bytes(int B, int T, int H, int N) { return (size_t)B * T * H * N * 4; }
 
 // rwkv7_wkv_forward; with s_ckpt (training forward, no epilogue) the states
 // before every kCkpt-th token as well; with bidir the bidirectional forward
@@ -131,11 +133,13 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (pro && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
-    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
-    const rwkv7_algo al = resolve_algo(algo, dt);
-    if (al == RWKV7_ALGO_CHUNKED && (dt == RWKV7_DT_F32 || !kChunkedAvailable))
+    const rwkv7_algo al = resolve_algo(algo, dt, N);
+    if (al == RWKV7_ALGO_CHUNKED && (dt == RWKV7_DT_F32 || N != kN || !kChunkedAvailable))
         return RWKV7_ERR_UNSUPPORTED;
+    // the stored states feed the backward, which is built for head size 64
+    if (want_ckpt && N != kN) return RWKV7_ERR_UNSUPPORTED;
 
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
@@ -238,7 +242,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     ForwardArgs p{};
     p.r = r; p.w = w; p.k = k; p.v = v; p.kappa = kappa; p.a = a;
     p.s0 = s0; p.y = y; p.s_out = s_out;
-    p.B = B; p.T = T; p.H = H;
+    p.B = B; p.T = T; p.H = H; p.N = N;
     p.bf16 = dt != RWKV7_DT_F32;
     p.w32 = dt == RWKV7_DT_BF16_W32;
     p.epilogue = epi != nullptr;
@@ -261,7 +265,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     // bidirectional: the reverse pass (tokens T-1 .. 0, second state of each head)
     // leaves float32 readouts in the workspace; the forward pass adds them to its
     // own before the epilogue
-    const size_t yrev = bidir_yrev_bytes(B, T, H);
+    const size_t yrev = bidir_yrev_bytes(B, T, H, N);
     const size_t heads_elems = st1 / 4;
     float *ws_y = static_cast<float *>(workspace);
     ForwardArgs rev = p;

@@ -26,6 +26,7 @@ struct ForwardArgs {
     void *y;                                // [B,T,H,N] in dt
     float *s_out;                           // [B,H,N,N] or nullptr
     int B, T, H;
+    int N;  // head size: 64, or 128 (scan only)
     bool bf16;
     bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;

@@ -1,5 +1,6 @@
 // WKV7 sequential scan (ALGO_SCAN): the recurrence token by token, with each
-// head's 64 x 64 float32 state held in VGPRs for the whole sequence.
+// head's N x N float32 state (N = 64 or 128) held in VGPRs for the whole
+// sequence.
 //
 // Per token (RWKV-7 "Goose" author response, numpy time_mixing listing; the
 // ARWKV verdict's key_machinery field gives the same update in row form):
@@ -10,9 +11,9 @@
 //   y_i = sum_j S_ij (w_j r_j) + v_i (k . r) - u_i ((a*kappa) . r),
 // which is the same sum regrouped, so one cross-lane reduction serves both.
 //
-// Work split.  One workgroup (4 waves) per (batch, head).  Value rows are
+// Work split.  One workgroup (N/16 waves) per (batch, head).  Value rows are
 // independent (row i of S only ever meets v_i and u_i), so wave w owns rows
-// 16w .. 16w+15; inside a wave a lane owns 2 rows x 8 key columns and the
+// 16w .. 16w+15; inside a wave a lane owns 2 rows x N/8 key columns and the
 // row sums need an 8-lane DPP reduction.  The per-token vectors are staged
 // 16 tokens at a time: every thread widens one 4-column slice of one token
 // (bf16 -> f32 is exact), forms a*kappa, w*r and the per-token scalars
@@ -26,19 +27,34 @@
 namespace wkv7 {
 namespace {
 
-constexpr int kScanThreads = 256;
 constexpr int kTC = 16;  // tokens staged per round
 
-struct __align__(16) ScanStage {
-    float kap[kTC][kN];
-    float w[kTC][kN];
-    float b[kTC][kN];   // a * kappa
-    float k[kTC][kN];
-    float wr[kTC][kN];  // w * r
-    float v[kTC][kN];
-    float4 sc[kTC];     // x = k.r, y = (a*kappa).r, z = sum_j r_j k_j r_k[j]
-    float ybuf[kTC][kN];
+template <int N>
+struct ScanShape {
+    static constexpr int kThreads = 4 * N;   // N/16 waves of 16 rows
+    static constexpr int kCols = N / 8;      // key columns per lane (8 lanes per row)
+    static constexpr int kStage = N / 4;     // staging lanes per token (4 channels each)
 };
+
+template <int N>
+struct __align__(16) ScanStage {
+    float kap[kTC][N];
+    float w[kTC][N];
+    float b[kTC][N];   // a * kappa
+    float k[kTC][N];
+    float wr[kTC][N];  // w * r
+    float v[kTC][N];
+    float4 sc[kTC];    // x = k.r, y = (a*kappa).r, z = sum_j r_j k_j r_k[j]
+    float ybuf[kTC][N];
+};
+
+// Sum over the staging lanes of one token (16 lanes for N = 64, 32 for 128).
+template <int N>
+__device__ __forceinline__ float stage_sum(float x) {
+    x = sum_lanes16(x);
+    if constexpr (N == 128) x = swap16_add(x, x);
+    return x;
+}
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
@@ -56,12 +72,13 @@ struct DecayLoad<true, L> {
     using type = RawLoad<F32In>;  // w as float32
 };
 
-template <class IO, bool EPI, bool W32>
-__global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
+template <class IO, bool EPI, bool W32, int N>
+__global__ __launch_bounds__(ScanShape<N>::kThreads) void scan_kernel(ForwardArgs p) {
     using L = RawLoad<IO>;
     using LW = typename DecayLoad<W32, L>::type;
     using E = typename IO::elem;
-    __shared__ ScanStage st;
+    constexpr int kCols = ScanShape<N>::kCols;
+    __shared__ ScanStage<N> st;
 
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh - b * p.H;
@@ -70,42 +87,56 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
     const int wave = tid >> 6, lane = tid & 63;
     const int c = lane & 7, g = lane >> 3;
     const int i0 = wave * 16 + 2 * g;  // value rows i0, i0 + 1
-    const int j0 = 8 * c;              // key columns j0 .. j0 + 7
+    const int j0 = kCols * c;          // key columns j0 .. j0 + kCols - 1
     // elements from one token to the next in processing order (negative when the
     // sequence is walked from its end) and the offset of the first processed token
-    const long HN = p.reverse ? -(long)p.H * kN : (long)p.H * kN;
-    const long tok0 = ((long)b * T + (p.reverse ? T - 1 : 0)) * ((long)p.H * kN) + (long)h * kN;
-    const int s_t = tid >> 4, s_q = tid & 15;  // staging role: token, 4-column slice
+    const long HN = p.reverse ? -(long)p.H * N : (long)p.H * N;
+    const long tok0 = ((long)b * T + (p.reverse ? T - 1 : 0)) * ((long)p.H * N) + (long)h * N;
+    // staging role: token, 4-column slice
+    const int s_t = tid / ScanShape<N>::kStage, s_q = tid % ScanShape<N>::kStage;
 
-    float S[2][8];
-    const long sb = (long)bh * kN * kN;
-    if (p.s0) {
+    // the lane's state columns moved as float4s
+    auto ld_rows = [&](const float *base, float (&S)[2][kCols]) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const float4 lo = *reinterpret_cast<const float4 *>(p.s0 + sb + (i0 + r) * kN + j0);
-            const float4 hi = *reinterpret_cast<const float4 *>(p.s0 + sb + (i0 + r) * kN + j0 + 4);
-            S[r][0] = lo.x; S[r][1] = lo.y; S[r][2] = lo.z; S[r][3] = lo.w;
-            S[r][4] = hi.x; S[r][5] = hi.y; S[r][6] = hi.z; S[r][7] = hi.w;
-        }
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int q = 0; q < kCols / 4; ++q) {
+                const float4 x = *reinterpret_cast<const float4 *>(base + (i0 + r) * N + j0 + 4 * q);
+                S[r][4 * q] = x.x; S[r][4 * q + 1] = x.y; S[r][4 * q + 2] = x.z; S[r][4 * q + 3] = x.w;
+            }
+    };
+    auto st_rows = [&](float *base, const float (&S)[2][kCols]) {
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+#pragma unroll
+            for (int q = 0; q < kCols / 4; ++q)
+                *reinterpret_cast<float4 *>(base + (i0 + r) * N + j0 + 4 * q) =
+                    make_float4(S[r][4 * q], S[r][4 * q + 1], S[r][4 * q + 2], S[r][4 * q + 3]);
+    };
+
+    float S[2][kCols];
+    const long sb = (long)bh * N * N;
+    if (p.s0) {
+        ld_rows(p.s0 + sb, S);
     } else {
 #pragma unroll
         for (int r = 0; r < 2; ++r)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S[r][e] = 0.f;
+            for (int e = 0; e < kCols; ++e) S[r][e] = 0.f;
     }
 
     // fused prologue parameters of this staging thread's 4 channels
     float4 kk4p = make_float4(0.f, 0.f, 0.f, 0.f), ka4p = kk4p;
     if (p.fused) {
-        kk4p = *reinterpret_cast<const float4 *>(p.k_k + h * kN + 4 * s_q);
-        ka4p = *reinterpret_cast<const float4 *>(p.k_a + h * kN + 4 * s_q);
+        kk4p = *reinterpret_cast<const float4 *>(p.k_k + h * N + 4 * s_q);
+        ka4p = *reinterpret_cast<const float4 *>(p.k_a + h * N + 4 * s_q);
     }
     float4 rk4 = make_float4(0.f, 0.f, 0.f, 0.f);
     float4 lnw4 = make_float4(1.f, 1.f, 1.f, 1.f), lnb4 = make_float4(0.f, 0.f, 0.f, 0.f);
     if (EPI) {
-        rk4 = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 4 * s_q);
-        if (p.epi.ln_w) lnw4 = *reinterpret_cast<const float4 *>(p.epi.ln_w + h * kN + 4 * s_q);
-        if (p.epi.ln_b) lnb4 = *reinterpret_cast<const float4 *>(p.epi.ln_b + h * kN + 4 * s_q);
+        rk4 = *reinterpret_cast<const float4 *>(p.epi.r_k + h * N + 4 * s_q);
+        if (p.epi.ln_w) lnw4 = *reinterpret_cast<const float4 *>(p.epi.ln_w + h * N + 4 * s_q);
+        if (p.epi.ln_b) lnb4 = *reinterpret_cast<const float4 *>(p.epi.ln_b + h * N + 4 * s_q);
     }
 
     typename L::T xr, xk, xv, xkap, xa;
@@ -131,35 +162,27 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
     issue(0);
     for (int ch = 0; ch < nchunks; ++ch) {
         const int tl = min(kTC, T - ch * kTC);
-        if (p.s_ckpt) {  // the state before token ch * kTC
-            float *ck = p.s_ckpt + ((long)bh * nchunks + ch) * kN * kN;
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                *reinterpret_cast<float4 *>(ck + (i0 + r) * kN + j0) =
-                    make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
-                *reinterpret_cast<float4 *>(ck + (i0 + r) * kN + j0 + 4) =
-                    make_float4(S[r][4], S[r][5], S[r][6], S[r][7]);
-            }
-        }
+        if (p.s_ckpt)  // the state before token ch * kTC
+            st_rows(p.s_ckpt + ((long)bh * nchunks + ch) * N * N, S);
         // ---- stage this chunk's vectors ----
         const float4 r4 = L::widen(xr), w4 = LW::widen(xw);
         float4 k4 = L::widen(xk), kap4 = L::widen(xkap);
         const float4 v4 = L::widen(xv), a4 = L::widen(xa);
         if (p.fused) {
-            // kappa = normalise(k * k_k) over the token's 64 channels (the 16 lanes of
-            // this DPP row); k <- k + k (a-1) k_a
+            // kappa = normalise(k * k_k) over the token's N channels (its staging
+            // lanes); k <- k + k (a-1) k_a
             const float4 kk = mul4(k4, kk4p);
-            const float inv = 1.f / fmaxf(sqrtf(sum_lanes16(dot4(kk, kk))), 1e-12f);
+            const float inv = 1.f / fmaxf(sqrtf(stage_sum<N>(dot4(kk, kk))), 1e-12f);
             kap4 = make_float4(kk.x * inv, kk.y * inv, kk.z * inv, kk.w * inv);
             k4 = make_float4(k4.x + k4.x * (a4.x - 1.f) * ka4p.x, k4.y + k4.y * (a4.y - 1.f) * ka4p.y,
                              k4.z + k4.z * (a4.z - 1.f) * ka4p.z, k4.w + k4.w * (a4.w - 1.f) * ka4p.w);
         }
         const float4 b4 = mul4(a4, kap4);
         const float4 wr4 = mul4(w4, r4);
-        float kr = sum_lanes16(dot4(k4, r4));
-        float br = sum_lanes16(dot4(b4, r4));
+        float kr = stage_sum<N>(dot4(k4, r4));
+        float br = stage_sum<N>(dot4(b4, r4));
         float bon = 0.f;
-        if (EPI) bon = sum_lanes16(dot4(mul4(r4, k4), rk4));
+        if (EPI) bon = stage_sum<N>(dot4(mul4(r4, k4), rk4));
         __syncthreads();  // the previous round is done with the staging area
         *reinterpret_cast<float4 *>(&st.kap[s_t][4 * s_q]) = kap4;
         *reinterpret_cast<float4 *>(&st.w[s_t][4 * s_q]) = w4;
@@ -173,25 +196,24 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
 
         // ---- the recurrence over this chunk's tokens ----
         for (int tt = 0; tt < tl; ++tt) {
-            float kap[8], w[8], bb[8], kk[8], wr[8];
-#define WKV7_LD8(dst, arr)                                                          \
-    {                                                                               \
-        const float4 lo_ = *reinterpret_cast<const float4 *>(&st.arr[tt][j0]);     \
-        const float4 hi_ = *reinterpret_cast<const float4 *>(&st.arr[tt][j0 + 4]); \
-        dst[0] = lo_.x; dst[1] = lo_.y; dst[2] = lo_.z; dst[3] = lo_.w;             \
-        dst[4] = hi_.x; dst[5] = hi_.y; dst[6] = hi_.z; dst[7] = hi_.w;             \
-    }
-            WKV7_LD8(kap, kap)
-            WKV7_LD8(w, w)
-            WKV7_LD8(bb, b)
-            WKV7_LD8(kk, k)
-            WKV7_LD8(wr, wr)
-#undef WKV7_LD8
+            float kap[kCols], w[kCols], bb[kCols], kk[kCols], wr[kCols];
+            auto ld_cols = [&](const float (&arr)[kTC][N], float (&dst)[kCols]) {
+#pragma unroll
+                for (int q = 0; q < kCols / 4; ++q) {
+                    const float4 x = *reinterpret_cast<const float4 *>(&arr[tt][j0 + 4 * q]);
+                    dst[4 * q] = x.x; dst[4 * q + 1] = x.y; dst[4 * q + 2] = x.z; dst[4 * q + 3] = x.w;
+                }
+            };
+            ld_cols(st.kap, kap);
+            ld_cols(st.w, w);
+            ld_cols(st.b, bb);
+            ld_cols(st.k, kk);
+            ld_cols(st.wr, wr);
             const float2 vv = *reinterpret_cast<const float2 *>(&st.v[tt][i0]);
             const float4 sc = st.sc[tt];
             float pu0 = 0.f, pu1 = 0.f, py0 = 0.f, py1 = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < kCols; ++e) {
                 pu0 += S[0][e] * kap[e];
                 pu1 += S[1][e] * kap[e];
                 py0 += S[0][e] * wr[e];
@@ -204,7 +226,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
             const float y0 = py0 + vv.x * sc.x - pu0 * sc.y;
             const float y1 = py1 + vv.y * sc.x - pu1 * sc.y;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
+            for (int e = 0; e < kCols; ++e) {
                 S[0][e] = S[0][e] * w[e] - pu0 * bb[e] + vv.x * kk[e];
                 S[1][e] = S[1][e] * w[e] - pu1 * bb[e] + vv.y * kk[e];
             }
@@ -213,7 +235,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
         __syncthreads();
 
         // ---- readouts of this chunk: epilogue and coalesced store ----
-        // (s_t is uniform over each 16-lane DPP row, so the row reductions
+        // (s_t is uniform over each token's staging lanes, so the reductions
         // below see all of their lanes active)
         if (s_t < tl) {
             const int t = ch * kTC + s_t;
@@ -224,9 +246,9 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
                 y4.x += ya.x; y4.y += ya.y; y4.z += ya.z; y4.w += ya.w;
             }
             if (EPI) {
-                const float mu = sum_lanes16(y4.x + y4.y + y4.z + y4.w) * (1.f / kN);
+                const float mu = stage_sum<N>(y4.x + y4.y + y4.z + y4.w) * (1.f / N);
                 const float4 d = make_float4(y4.x - mu, y4.y - mu, y4.z - mu, y4.w - mu);
-                const float var = sum_lanes16(dot4(d, d)) * (1.f / kN);
+                const float var = stage_sum<N>(dot4(d, d)) * (1.f / N);
                 const float rs = 1.f / sqrtf(var + p.epi.eps);
                 const float bz = st.sc[s_t].z;
                 const float4 vz = *reinterpret_cast<const float4 *>(&st.v[s_t][4 * s_q]);
@@ -246,38 +268,39 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(ForwardArgs p) {
         }
     }
 
-    if (p.s_out) {
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            *reinterpret_cast<float4 *>(p.s_out + sb + (i0 + r) * kN + j0) =
-                make_float4(S[r][0], S[r][1], S[r][2], S[r][3]);
-            *reinterpret_cast<float4 *>(p.s_out + sb + (i0 + r) * kN + j0 + 4) =
-                make_float4(S[r][4], S[r][5], S[r][6], S[r][7]);
-        }
+    if (p.s_out) st_rows(p.s_out + sb, S);
+}
+
+}  // namespace
+
+namespace {
+
+template <int N>
+hipError_t launch_scan_n(const ForwardArgs &p, hipStream_t stream) {
+    const dim3 grid((unsigned)((long)p.B * p.H)), block(ScanShape<N>::kThreads);
+    if (p.bf16 && p.w32) {
+        if (p.epilogue)
+            hipLaunchKernelGGL((scan_kernel<Bf16In, true, true, N>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((scan_kernel<Bf16In, false, true, N>), grid, block, 0, stream, p);
+    } else if (p.bf16) {
+        if (p.epilogue)
+            hipLaunchKernelGGL((scan_kernel<Bf16In, true, false, N>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((scan_kernel<Bf16In, false, false, N>), grid, block, 0, stream, p);
+    } else {
+        if (p.epilogue)
+            hipLaunchKernelGGL((scan_kernel<F32In, true, false, N>), grid, block, 0, stream, p);
+        else
+            hipLaunchKernelGGL((scan_kernel<F32In, false, false, N>), grid, block, 0, stream, p);
     }
+    return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_scan(const ForwardArgs &p, hipStream_t stream) {
-    const dim3 grid((unsigned)((long)p.B * p.H)), block(kScanThreads);
-    if (p.bf16 && p.w32) {
-        if (p.epilogue)
-            hipLaunchKernelGGL((scan_kernel<Bf16In, true, true>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((scan_kernel<Bf16In, false, true>), grid, block, 0, stream, p);
-    } else if (p.bf16) {
-        if (p.epilogue)
-            hipLaunchKernelGGL((scan_kernel<Bf16In, true, false>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((scan_kernel<Bf16In, false, false>), grid, block, 0, stream, p);
-    } else {
-        if (p.epilogue)
-            hipLaunchKernelGGL((scan_kernel<F32In, true, false>), grid, block, 0, stream, p);
-        else
-            hipLaunchKernelGGL((scan_kernel<F32In, false, false>), grid, block, 0, stream, p);
-    }
-    return hipGetLastError();
+    return p.N == 128 ? launch_scan_n<128>(p, stream) : launch_scan_n<64>(p, stream);
 }
 
 }  // namespace wkv7

@@ -229,3 +229,10 @@ def test_decode_head_size_128_validation():
     # N = 128: the state spans 2*3*128*128*4 bytes, so y just inside its end overlaps
     assert dec(128, y=fake(6, 2 * 3 * 128 * 128 * 4 - 16)) == 6
     assert L.rwkv7_wkv_forward_workspace(1, 64, 1, 128, 1, 0) == 0
+
+
+def test_forward_head_size_128_validation():
+    assert fwd(N=96) == 4
+    assert fwd(N=128, algo=2) == 4                 # chunked is built for 64
+    assert fwd_train(N=128) == 4                   # the backward is built for 64
+    assert fwd(N=128, T=0, s_out=None) == 0        # scan at 128 passes validation

@@ -53,8 +53,8 @@ def test_decode_n128_run(wkv):
     assert_close(to_f64(st), s_ref, TOL["bf16"], "S run")
 
 
-def test_forward_rejects_n128(wkv):
+def test_forward_n128_chunked_refused(wkv):
     x = synth.draw(1, 4, 1, 128, seed=1, dtype="bf16")
     d = to_device(x, torch)
     with pytest.raises(wkv.Rwkv7Error):
-        wkv.forward(*(d[n] for n in NAMES))
+        wkv.forward(*(d[n] for n in NAMES), algo="chunked")
