@@ -403,7 +403,7 @@ struct Chunked {
 struct Pending {
     f32x4 y;
     float bon[4];
-    float gate[4];  // fused prologue: output gate of the four tokens
+    uint16_t graw[4];  // fused prologue: raw bf16 output gate of the four tokens
     bf16x4 v;
 };
 
@@ -429,7 +429,7 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
             yv[e] = (yv[e] - mu) * rs * lnw + lnb +
                     pd.bon[e] * bf16_lo((unsigned)(unsigned short)pd.v[e]);
         }
-        if (FUSED) yv[e] *= pd.gate[e];  // output gate (1 when none is given)
+        if (FUSED && p.g) yv[e] *= bf16_lo(pd.graw[e]);  // output gate
     }
     // yoff: element offset of token c*16 + 4g of this lane's value channel
     const int t0 = c * kC + 4 * g;
@@ -533,13 +533,19 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     for (int e = 0; e < 4; ++e)
                         if (c * kC + 4 * g + e < K.Tl) yadd[e] = p.y_add[ylane + e * K.TS];
                 }
-                if (FUSED && !SUMMARY) {  // output gate of this chunk's readouts
+                if (FUSED && !SUMMARY) {
+                    // output gate of this chunk's readouts, loaded without branches (a
+                    // branch around loads makes the compiler wait for all of them):
+                    // the token index is clamped into the range and, without a gate,
+                    // the raw keys (same shape) are read and the value discarded
+                    // (the bits are only widened where the readouts are finished, one
+                    // chunk later, so nothing waits for these loads before the barrier)
+                    const uint16_t *gsrc = static_cast<const uint16_t *>(p.g ? p.g : p.k);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        pd.gate[e] = (p.g && c * kC + 4 * g + e < K.Tl)
-                                         ? bf16_lo(static_cast<const uint16_t *>(p.g)
-                                                       [ylane + e * K.TS])
-                                         : 1.f;
+                    for (int e = 0; e < 4; ++e) {
+                        const int t = c * kC + 4 * g + e;
+                        pd.graw[e] = gsrc[K.tok0 + (long)min(t, K.Tl - 1) * K.TS + 16 * blk + lo];
+                    }
                 }
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
