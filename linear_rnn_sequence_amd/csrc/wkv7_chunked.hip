@@ -64,6 +64,9 @@ constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per la
 // flight: vmcnt = loads per chunk x (kPrefetch-1), lgkmcnt and expcnt unlimited.
 // Six loads per chunk (r, w, k, kappa, a, v); eight with the fused prologue
 // (r, w, k, a, v and the raw keys of the three other key blocks).
+constexpr int kWaitAllLoads = (0x7 << 4) | (0xF << 8);  // vmcnt(0) only
+constexpr int kUnroll = 2 * kPrefetch;                   // prep loop unroll
+
 constexpr int wait_older_chunks(int loads_per_chunk) {
     return ((loads_per_chunk * (kPrefetch - 1)) & 0xF) | (0x7 << 4) | (0xF << 8) |
            ((((loads_per_chunk * (kPrefetch - 1)) >> 4) & 0x3) << 14);
@@ -459,7 +462,9 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
 // SUMMARY = true: for each (b, h, segment) but the last, the segment's offset
 //   dS (waves 0..3: entry state 0) and transition P (waves 8..11: entry state I,
 //   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
-template <bool EPI, bool SUMMARY, bool W32, bool FUSED>
+// YADD: add the float32 readouts p.y_add (the reverse pass of a bidirectional
+// call) before the epilogue.
+template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD>
 __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_kernel(
     ChunkedParams cp) {
     __shared__ ChunkSmem sm;
@@ -510,6 +515,20 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
         Pending pd;
         long ylane = K.tok0 + (long)(4 * g) * K.TS + 16 * blk + lo;  // y element offset
+        // added readouts, loaded one chunk ahead (token index clamped into the
+        // range: no branch around the loads)
+        constexpr bool kYadd = YADD && !SUMMARY;
+        float ya[4] = {0.f, 0.f, 0.f, 0.f};
+        auto load_ya = [&](int cc) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                ya[e] = p.y_add[K.tok0 + (long)min(cc * kC + 4 * g + e, K.Tl - 1) * K.TS +
+                                16 * blk + lo];
+        };
+        if (kYadd) load_ya(0);
+        // everything loaded so far is in registers before the chunk loop, so no
+        // wait for these loads is left inside it
+        __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         const long ystep = (long)kC * K.TS;
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
@@ -526,12 +545,11 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                         *reinterpret_cast<float4 *>(ck + 16 * jb) =
                             make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
                 }
-                // the other direction's readouts of this chunk's tokens, if any
+                // the other direction's readouts of this chunk's tokens
                 float yadd[4] = {0.f, 0.f, 0.f, 0.f};
-                if (!SUMMARY && p.y_add) {
+                if (kYadd) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c * kC + 4 * g + e < K.Tl) yadd[e] = p.y_add[ylane + e * K.TS];
+                    for (int e = 0; e < 4; ++e) yadd[e] = (c * kC + 4 * g + e < K.Tl) ? ya[e] : 0.f;
                 }
                 if (FUSED && !SUMMARY) {
                     // output gate of this chunk's readouts, loaded without branches (a
@@ -571,8 +589,11 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     Z[jb][2] *= gc.z;
                     Z[jb][3] *= gc.w;
                 }
+                if (kYadd) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) Y[e] += yadd[e];
+                    for (int e = 0; e < 4; ++e) Y[e] += yadd[e];
+                    load_ya(min(c + 1, nch - 1));  // the next chunk's, used one iteration later
+                }
                 pd.y = Y;
                 pd.v = Vb;
                 if (EPI && !SUMMARY) {
@@ -623,17 +644,20 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         Raw<W32> xs[kPrefetch];
 #pragma unroll
         for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
-        for (int q0 = 0; q0 < nch + 3; q0 += kPrefetch) {
+        // (unrolled over two turns of the ring: the compiler's wait-count analysis
+        // turns conservative only in the first interval after the loop's back edge)
+        for (int q0 = 0; q0 < nch + 3; q0 += kUnroll) {
 #pragma unroll
-            for (int d = 0; d < kPrefetch; ++d) {
+            for (int d = 0; d < kUnroll; ++d) {
                 const int q = q0 + d;
                 if (q >= nch + 3) break;
+                Raw<W32> &x = xs[d % kPrefetch];
                 if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
                 if (q < nch) {
-                    if ((q + 1) * kC > K.Tl) K.pad(q, xs[d]);  // partial last chunk only
-                    K.prep(xs[d], sm.ops[q % 3], rk, pro);
+                    if ((q + 1) * kC > K.Tl) K.pad(q, x);  // partial last chunk only
+                    K.prep(x, sm.ops[q % 3], rk, pro);
                 }
-                K.load(q + kPrefetch, xs[d]);  // clamped: always six loads per interval
+                K.load(q + kPrefetch, x);  // clamped: always the same loads per interval
                 // the next interval consumes the oldest ring slot: let only the
                 // (kPrefetch-1) younger chunks' loads stay in flight.  Stated
                 // explicitly because the compiler's own count is lost across the
@@ -754,7 +778,7 @@ size_t chunked_workspace_bytes(int B, int T, int H) {
     return (size_t)3 * B * H * nseg * kN * kN * sizeof(float);
 }
 
-template <bool W32, bool FUSED>
+template <bool W32, bool FUSED, bool YADD>
 hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     const ForwardArgs &p = cp.p;
     const long bh = (long)p.B * p.H;
@@ -765,7 +789,7 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
         cp.ws_sin = cp.ws_ds + slab;
         // 1. transitions and offsets of every segment but the last
         cp.nseg_launch = cp.nseg - 1;
-        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED>),
+        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED, false>),
                            dim3((unsigned)(bh * cp.nseg_launch)), dim3(kThreadsSummary), 0,
                            stream, cp);
         hipError_t e = hipGetLastError();
@@ -780,9 +804,11 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     cp.nseg_launch = cp.nseg;
     const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED, YADD>), grid, block, 0, stream,
+                           cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED>), grid, block, 0, stream, cp);
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED, YADD>), grid, block, 0,
+                           stream, cp);
     return hipGetLastError();
 }
 
@@ -791,9 +817,12 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
     cp.p = p;
     segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
     // the fused prologue comes with bf16 decays only (the API refuses it with float32 w)
-    if (p.fused) return launch_chunked_w<false, true>(cp, stream);
-    return p.w32 ? launch_chunked_w<true, false>(cp, stream)
-                 : launch_chunked_w<false, false>(cp, stream);
+    if (p.fused) return launch_chunked_w<false, true, false>(cp, stream);
+    if (p.y_add)
+        return p.w32 ? launch_chunked_w<true, false, true>(cp, stream)
+                     : launch_chunked_w<false, false, true>(cp, stream);
+    return p.w32 ? launch_chunked_w<true, false, false>(cp, stream)
+                 : launch_chunked_w<false, false, false>(cp, stream);
 }
 
 }  // namespace wkv7
