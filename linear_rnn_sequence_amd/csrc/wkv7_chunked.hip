@@ -515,8 +515,9 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
         Pending pd;
         long ylane = K.tok0 + (long)(4 * g) * K.TS + 16 * blk + lo;  // y element offset
-        // added readouts, loaded one chunk ahead (token index clamped into the
-        // range: no branch around the loads)
+        // added readouts of a chunk, loaded at the start of its iteration and used
+        // after its MFMA chain (token index clamped into the range: no branch
+        // around the loads, and no load waited for across the loop's back edge)
         constexpr bool kYadd = YADD && !SUMMARY;
         float ya[4] = {0.f, 0.f, 0.f, 0.f};
         auto load_ya = [&](int cc) {
@@ -525,7 +526,6 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 ya[e] = p.y_add[K.tok0 + (long)min(cc * kC + 4 * g + e, K.Tl - 1) * K.TS +
                                 16 * blk + lo];
         };
-        if (kYadd) load_ya(0);
         // everything loaded so far is in registers before the chunk loop, so no
         // wait for these loads is left inside it
         __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
@@ -545,12 +545,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                         *reinterpret_cast<float4 *>(ck + 16 * jb) =
                             make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
                 }
-                // the other direction's readouts of this chunk's tokens
-                float yadd[4] = {0.f, 0.f, 0.f, 0.f};
-                if (kYadd) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) yadd[e] = (c * kC + 4 * g + e < K.Tl) ? ya[e] : 0.f;
-                }
+                if (kYadd) load_ya(c);  // the other direction's readouts of this chunk
                 if (FUSED && !SUMMARY) {
                     // output gate of this chunk's readouts, loaded without branches (a
                     // branch around loads makes the compiler wait for all of them):
@@ -591,8 +586,8 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 }
                 if (kYadd) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) Y[e] += yadd[e];
-                    load_ya(min(c + 1, nch - 1));  // the next chunk's, used one iteration later
+                    for (int e = 0; e < 4; ++e)
+                        if (c * kC + 4 * g + e < K.Tl) Y[e] += ya[e];
                 }
                 pd.y = Y;
                 pd.v = Vb;
