@@ -21,6 +21,7 @@ import hashlib
 import json
 import os
 import platform
+import re
 import sys
 import time
 
@@ -72,10 +73,15 @@ def parse():
 
 
 def source_hash(*names):
+    """Hash of the kernel sources' code: comments and whitespace are removed
+    first, so a profile summary stays attached to the code it measured."""
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "linear_rnn_sequence_amd", "csrc", n)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

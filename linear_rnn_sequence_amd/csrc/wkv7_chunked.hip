@@ -39,8 +39,29 @@
 //     exactly the layout the next chunk's MFMAs consume, so the state never
 //     leaves registers; they run chunk c's MFMA chain and finish chunk c-1's
 //     readouts (GroupNorm statistics need all four value blocks).
-// A SIMD thus holds one MFMA-bound chain wave and one VALU-bound prep wave.
-// LDS holds the operands of three chunks.
+// A SIMD thus holds one chain wave and one prep wave; together they issue
+// ~430 VALU and ~27 MFMA instructions per chunk, which bounds the kernel (a
+// second resident workgroup per CU adds no throughput).  LDS holds the
+// operands of three chunks.
+//
+// Wait counts: vector stores count with loads on this target, so a full wait
+// inside the chunk loop would also wait for the chunk's stores.  Loads made
+// before the loop are waited for once before it, optional loads are
+// branch-free and consumed in the iteration that issues them (or carried raw
+// to the next one), and the prep ring states its own wait count.
+//
+// Variants (template parameters and ForwardArgs fields):
+//   - segments: long sequences of few heads are cut into parallel time
+//     segments; a 12-wave summary pass computes each segment's transition
+//     (state started at I, v = 0) and offset (started at 0), a combine kernel
+//     forms the entry states S_in[g+1] = S_in[g] P_g + dS_g in fp32, and the
+//     main pass reruns every segment from its entry state;
+//   - W32: the decay arrives as float32;
+//   - FUSED: raw keys in, kappa = normalise(k * k_k) and k + k (a-1) k_a formed
+//     in the prep lanes, output gate applied to the finished readouts;
+//   - reverse / y_f32 / YADD: the two passes of the bidirectional forward (a
+//     negative token stride; float32 readouts out; added readouts in);
+//   - s_ckpt: the training forward stores the state entering every chunk.
 //
 // MFMA 16x16x16 bf16 lane layouts (lane l, g = l / 16, e = 0..3):
 //   A[m][k]: lane holds A[l%16][4g+e];  B[k][n]: lane holds B[4g+e][l%16];

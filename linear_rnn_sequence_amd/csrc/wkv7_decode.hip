@@ -9,11 +9,13 @@
 // summary, §8 Speed and Memory.  The state read and write (32 KiB per head)
 // is all but the whole traffic, so the kernel is laid out for HBM streaming.
 //
-// Two waves per head (each owns 32 value rows, 8 per lane), one wave per
-// workgroup; with the fused epilogue the head's two waves share a 128-thread
-// workgroup so the GroupNorm statistics can meet in LDS.  (Measured against 1,
-// 2, 4, 8 and 16 waves per workgroup, whole heads per wave, four waves per
-// head and persistent waves: this layout streamed fastest, 77% of 8 TB/s.)
+// Head size 64: two waves per head (each owns 32 value rows, 8 per lane), one
+// wave per workgroup; with the fused epilogue the head's two waves share a
+// 128-thread workgroup so the GroupNorm statistics can meet in LDS.  (Measured
+// against 1, 2, 4, 8 and 16 waves per workgroup, whole heads per wave, four
+// waves per head and persistent waves: this layout streamed fastest, ~76% of
+// 8 TB/s.)  Head size 128 uses the same lane layout with 32 lanes per row:
+// eight waves per head (see DecodeShape).
 // Lane (c, g) = (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value
 // rows r0 + 8g .. r0 + 8g + 7: every state load instruction reads four complete
 // 256-byte rows (16 lanes x 16 bytes each), so each wave moves its 8 KiB in
