@@ -551,6 +551,13 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         // wait for these loads is left inside it
         __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         const long ystep = (long)kC * K.TS;
+        auto store_state = [&](float *dst) {  // non-temporal: read back only by the backward
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                __builtin_nontemporal_store(Z[jb],
+                                            reinterpret_cast<f32x4 *>(dst + srow + 16 * jb + 4 * g));
+        };
+        if (ckpt && nch > 0) store_state(ckpt);  // the state before chunk 0
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
@@ -559,13 +566,6 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 ylane += ystep;
             }
             if (c < nch) {
-                if (ckpt) {  // the state before this chunk
-                    float *ck = ckpt + (long)c * kN * kN + srow + 4 * g;
-#pragma unroll
-                    for (int jb = 0; jb < 4; ++jb)
-                        *reinterpret_cast<float4 *>(ck + 16 * jb) =
-                            make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
-                }
                 if (kYadd) load_ya(c);  // the other direction's readouts of this chunk
                 if (FUSED && !SUMMARY) {
                     // output gate of this chunk's readouts, loaded without branches (a
@@ -612,6 +612,10 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 }
                 pd.y = Y;
                 pd.v = Vb;
+                // stored states: the one leaving this chunk enters the next; stored
+                // here, in the slack before the barrier, rather than just before
+                // the MFMAs that overwrite the accumulators
+                if (ckpt && c + 1 < nch) store_state(ckpt + (long)(c + 1) * kN * kN);
                 if (EPI && !SUMMARY) {
                     // readouts: lane holds y[t = 4g+e][i = 16blk + lo]
                     const float4 bt = *reinterpret_cast<const float4 *>(&o.bon_tot[4 * g]);
