@@ -256,6 +256,17 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
                                 void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
                                 int T, int H, int N, rwkv7_dtype dt, void *stream);
 
+/*
+ * rwkv7_wkv_decode fed from raw keys through the fused time-mix prologue
+ * (rwkv7_prologue above; g is [B,H,N] in dt or NULL): r, w, k (raw), v, a :
+ * [B,H,N] in dt (float32 or bfloat16); no kappa argument.  N = 64 or 128.
+ * State, y, epilogue and errors as rwkv7_wkv_decode.
+ */
+rwkv7_status rwkv7_wkv_decode_fused(const void *r, const void *w, const void *k, const void *v,
+                                    const void *a, const rwkv7_prologue *pro, float *state,
+                                    void *y, int B, int H, int N, rwkv7_dtype dt,
+                                    const rwkv7_epilogue *epi, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *rwkv7_status_str(rwkv7_status s);
 

@@ -403,11 +403,16 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     return launch_backward(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 
-rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const void *v,
-                              const void *kappa, const void *a, float *state, void *y, int B,
-                              int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
-                              void *stream) {
+}  // extern "C"
+
+// rwkv7_wkv_decode; with pro, fed from raw keys through the time-mix prologue
+// (kappa unused) and gated by pro->g.
+static rwkv7_status decode_impl(const void *r, const void *w, const void *k, const void *v,
+                                const void *kappa, const void *a, float *state, void *y, int B,
+                                int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
+                                void *stream, const rwkv7_prologue *pro) {
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
+    if (pro && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1) return RWKV7_ERR_SHAPE;
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
@@ -420,26 +425,35 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
         return RWKV7_ERR_SHAPE;
     // N/32 * 2 waves (workgroups) per head: keep the grid within its x limit
     if ((size_t)B * H * (N == 128 ? 8 : 2) > 0xffffffffu) return RWKV7_ERR_SHAPE;
-    const void *ins[6] = {r, w, k, v, kappa, a};
+    // the six vectors (kappa unused with the prologue) and the prologue's gate
+    const void *ins[7] = {r, w, k, v, pro ? nullptr : kappa, a, pro ? pro->g : nullptr};
     auto in_rng = [&](int i) {
         const uintptr_t lo = reinterpret_cast<uintptr_t>(ins[i]);
-        return Range{lo, lo + (i == 1 ? tok_w : tok)};
+        return lo ? Range{lo, lo + (i == 1 ? tok_w : tok)} : Range{0, 0};
     };
-    for (const void *p : ins)
-        if (!p) return RWKV7_ERR_NULL;
+    for (int i = 0; i < 6; ++i)
+        if (!ins[i] && !(pro && i == 4)) return RWKV7_ERR_NULL;
     if (!state || !y) return RWKV7_ERR_NULL;
+    if (pro && (!pro->k_k || !pro->k_a)) return RWKV7_ERR_NULL;
     rwkv7_status es = check_epilogue(epi);
     if (es != RWKV7_OK) return es;
     for (const void *p : ins)
-        if (!aligned16(p)) return RWKV7_ERR_ALIGN;
+        if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
     if (!aligned16(state) || !aligned16(y)) return RWKV7_ERR_ALIGN;
+    if (pro && (!aligned16(pro->k_k) || !aligned16(pro->k_a))) return RWKV7_ERR_ALIGN;
     auto rng = [](const void *p, size_t n) {
         return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
     };
     const Range ry = rng(y, tok), rs = rng(state, st);
     if (overlap(ry, rs)) return RWKV7_ERR_ALIAS;
-    for (int i = 0; i < 6; ++i)
+    for (int i = 0; i < 7; ++i)
         if (overlap(ry, in_rng(i)) || overlap(rs, in_rng(i))) return RWKV7_ERR_ALIAS;
+    if (pro) {
+        const size_t pn = (size_t)H * N * 4;
+        if (overlap(ry, rng(pro->k_k, pn)) || overlap(rs, rng(pro->k_k, pn)) ||
+            overlap(ry, rng(pro->k_a, pn)) || overlap(rs, rng(pro->k_a, pn)))
+            return RWKV7_ERR_ALIAS;
+    }
     if (epi) {
         const size_t pn = (size_t)H * N * 4;
         const void *ps[3] = {epi->r_k, epi->ln_w, epi->ln_b};
@@ -453,8 +467,32 @@ rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const
     p.w32 = dt == RWKV7_DT_BF16_W32;
     p.epilogue = epi != nullptr;
     p.epi = to_epi(epi);
+    if (pro) {
+        p.fused = true;
+        p.kappa = nullptr;
+        p.k_k = pro->k_k;
+        p.k_a = pro->k_a;
+        p.g = pro->g;
+    }
     return launch_decode(p, static_cast<hipStream_t>(stream)) == hipSuccess ? RWKV7_OK
                                                                              : RWKV7_ERR_HIP;
+}
+
+extern "C" {
+
+rwkv7_status rwkv7_wkv_decode(const void *r, const void *w, const void *k, const void *v,
+                              const void *kappa, const void *a, float *state, void *y, int B,
+                              int H, int N, rwkv7_dtype dt, const rwkv7_epilogue *epi,
+                              void *stream) {
+    return decode_impl(r, w, k, v, kappa, a, state, y, B, H, N, dt, epi, stream, nullptr);
+}
+
+rwkv7_status rwkv7_wkv_decode_fused(const void *r, const void *w, const void *k, const void *v,
+                                    const void *a, const rwkv7_prologue *pro, float *state,
+                                    void *y, int B, int H, int N, rwkv7_dtype dt,
+                                    const rwkv7_epilogue *epi, void *stream) {
+    if (!pro) return RWKV7_ERR_NULL;
+    return decode_impl(r, w, k, v, nullptr, a, state, y, B, H, N, dt, epi, stream, pro);
 }
 
 }  // extern "C"

@@ -83,7 +83,7 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
-template <class IO, bool EPI, bool NT, bool W32, int N>
+template <class IO, bool EPI, bool NT, bool W32, int N, bool FUSED = false>
 __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void decode_kernel(
     DecodeArgs p) {
     using E = typename IO::elem;
@@ -105,11 +105,25 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
 
     const long vo = head * N;
     const E *pr = static_cast<const E *>(p.r) + vo;
-    const float4 kap = IO::load4(static_cast<const E *>(p.kappa) + vo + 4 * c);
     const float4 w = W32 ? F32In::load4(static_cast<const float *>(p.w) + vo + 4 * c)
                          : IO::load4(static_cast<const E *>(p.w) + vo + 4 * c);
     const float4 a = IO::load4(static_cast<const E *>(p.a) + vo + 4 * c);
-    const float4 k = IO::load4(static_cast<const E *>(p.k) + vo + 4 * c);
+    float4 k = IO::load4(static_cast<const E *>(p.k) + vo + 4 * c);
+    float4 kap;
+    if (FUSED) {
+        // time-mix prologue from raw keys: kappa = normalise(k * k_k) over the
+        // head's N channels (this row's lanes), k <- k + k (a-1) k_a
+        const float4 kk4 = *reinterpret_cast<const float4 *>(p.k_k + h * N + 4 * c);
+        const float4 ka4 = *reinterpret_cast<const float4 *>(p.k_a + h * N + 4 * c);
+        const float4 kk = make_float4(k.x * kk4.x, k.y * kk4.y, k.z * kk4.z, k.w * kk4.w);
+        const float ss = row_sum<N>(kk.x * kk.x + kk.y * kk.y + kk.z * kk.z + kk.w * kk.w);
+        const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
+        kap = make_float4(kk.x * inv, kk.y * inv, kk.z * inv, kk.w * inv);
+        k = make_float4(k.x + k.x * (a.x - 1.f) * ka4.x, k.y + k.y * (a.y - 1.f) * ka4.y,
+                        k.z + k.z * (a.z - 1.f) * ka4.z, k.w + k.w * (a.w - 1.f) * ka4.w);
+    } else {
+        kap = IO::load4(static_cast<const E *>(p.kappa) + vo + 4 * c);
+    }
     const float4 r = IO::load4(pr + 4 * c);
     float v[kRows];
     load8(static_cast<const E *>(p.v) + vo + r0, v);
@@ -190,29 +204,40 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
         const float gb = p.epi.ln_b ? p.epi.ln_b[ch] : 0.f;
         yo = (yo - mu) * rs * gw + gb + bon * vo1;
     }
+    if (FUSED && p.g) {  // output gate
+        float gv[kRows];
+        load8(static_cast<const E *>(p.g) + vo + r0, gv);
+        float gsel = gv[0];
+#pragma unroll
+        for (int m = 1; m < kRows; ++m) gsel = (sel == m) ? gv[m] : gsel;
+        yo *= gsel;
+    }
     if (c < kRows) IO::store1(static_cast<E *>(p.y) + vo + r0 + c, yo);
 }
 
-template <int N, class IO, bool W32>
+template <int N, class IO, bool W32, bool FUSED>
 hipError_t launch_decode_n(const DecodeArgs &p, hipStream_t stream) {
     constexpr int kW = DecodeShape<N>::kWavesPerHead;
     const long heads = (long)p.B * p.H;
     // without the epilogue: one 64-thread workgroup per wave of a head; with it:
     // one workgroup per head holding all its waves
     if (p.epilogue)
-        hipLaunchKernelGGL((decode_kernel<IO, true, true, W32, N>), dim3((unsigned)heads),
+        hipLaunchKernelGGL((decode_kernel<IO, true, true, W32, N, FUSED>), dim3((unsigned)heads),
                            dim3(64 * kW), 0, stream, p);
     else
-        hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N>),
+        hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N, FUSED>),
                            dim3((unsigned)(kW * heads)), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
 template <int N>
 hipError_t launch_decode_dt(const DecodeArgs &p, hipStream_t stream) {
-    if (p.bf16 && p.w32) return launch_decode_n<N, Bf16In, true>(p, stream);
-    if (p.bf16) return launch_decode_n<N, Bf16In, false>(p, stream);
-    return launch_decode_n<N, F32In, false>(p, stream);
+    if (p.fused)  // (the fused prologue comes with one dtype for all vectors)
+        return p.bf16 ? launch_decode_n<N, Bf16In, false, true>(p, stream)
+                      : launch_decode_n<N, F32In, false, true>(p, stream);
+    if (p.bf16 && p.w32) return launch_decode_n<N, Bf16In, true, false>(p, stream);
+    if (p.bf16) return launch_decode_n<N, Bf16In, false, false>(p, stream);
+    return launch_decode_n<N, F32In, false, false>(p, stream);
 }
 
 }  // namespace

@@ -71,6 +71,10 @@ struct DecodeArgs {
     bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;
     EpilogueArgs epi;
+    // fused time-mix prologue (as in ForwardArgs): k raw, kappa unused
+    bool fused;
+    const float *k_k, *k_a;  // [H*N]
+    const void *g;           // [B,H,N] in dt, or nullptr
 };
 
 // Each launcher enqueues its kernels on `stream` and returns hipSuccess or the

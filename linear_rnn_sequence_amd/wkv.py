@@ -63,6 +63,9 @@ def lib():
                                               + [ci] * 6 + [ctypes.POINTER(Epilogue), vp, sz,
                                                             vp])
         L.rwkv7_wkv_forward_fused.restype = ci
+        L.rwkv7_wkv_decode_fused.argtypes = ([vp] * 5 + [ctypes.POINTER(Prologue)] + [vp] * 2
+                                             + [ci] * 4 + [ctypes.POINTER(Epilogue), vp])
+        L.rwkv7_wkv_decode_fused.restype = ci
         L.rwkv7_wkv_forward_bidir.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue),
                                                                    vp, sz, vp]
         L.rwkv7_wkv_forward_bidir.restype = ci
@@ -314,6 +317,33 @@ def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):
     del keep
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_decode")
+    return y
+
+
+def decode_fused(r, w, k, v, a, k_k, k_a, state, *, g=None, epilogue=None, y=None,
+                 stream=None):
+    """rwkv7_wkv_decode_fused: one token per resident state, fed from raw keys k through
+    the fused time-mix prologue (k_k, k_a: f32 [H*N]) and gated by g ([B,H,N]) if given.
+    Returns y [B,H,N]."""
+    import torch
+
+    B, H, N = r.shape
+    _check_same(torch, (r, w, k, v, a) + (() if g is None else (g,)), r.shape, r.dtype)
+    dt = _dtype_code(torch, r.dtype)
+    for prm in (k_k, k_a):
+        if prm.dtype != torch.float32 or prm.numel() != H * N or not prm.is_contiguous():
+            raise ValueError("k_k and k_a must be contiguous float32 tensors of H*N elements")
+    if y is None:
+        y = torch.empty_like(r)
+    pro = Prologue(k_k=k_k.data_ptr(), k_a=k_a.data_ptr(),
+                   g=None if g is None else g.data_ptr())
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_decode_fused(_ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(a),
+                                        ctypes.byref(pro), _ptr(state), _ptr(y), B, H, N, dt,
+                                        epi_ptr, _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_decode_fused")
     return y
 
 

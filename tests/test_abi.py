@@ -236,3 +236,20 @@ def test_forward_head_size_128_validation():
     assert fwd(N=128, algo=2) == 4                 # chunked is built for 64
     assert fwd_train(N=128) == 4                   # the backward is built for 64
     assert fwd(N=128, T=0, s_out=None) == 0        # scan at 128 passes validation
+
+
+def test_decode_fused_validation_codes():
+    L = wkv.lib()
+
+    def dfu(pro=None, dt=1, N=64, y=fake(7), state=fake(6)):
+        p = None if pro is None else ctypes.byref(pro)
+        return L.rwkv7_wkv_decode_fused(*[fake(i) for i in range(5)], p, state, y, 2, 3, N, dt,
+                                        None, None)
+    ok = _Pro(k_k=A + 11 * STRIDE, k_a=A + 12 * STRIDE, g=A + 13 * STRIDE)
+    assert dfu(None) == 1
+    assert dfu(_Pro(k_k=A + 11 * STRIDE, k_a=None, g=None)) == 1
+    assert dfu(_Pro(k_k=A + 11 * STRIDE, k_a=A + 12 * STRIDE + 8, g=None)) == 5
+    assert dfu(ok, dt=2) == 4
+    assert dfu(ok, N=96) == 4
+    assert dfu(ok, y=fake(13, 64)) == 6            # y over the gate
+    assert dfu(ok, state=fake(11)) == 6            # state over k_k

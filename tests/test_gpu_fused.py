@@ -86,3 +86,29 @@ def test_fused_zero_keys_stay_finite(wkv):
     y_ref, s_ref = oracle.forward_fused(*raw, k_k, k_a)
     assert_close(to_f64(y), y_ref, TOL["bf16"], "zero keys y")
     assert_close(to_f64(s), s_ref, TOL["bf16"], "zero keys S")
+
+
+@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("epi", [False, True])
+@pytest.mark.parametrize("gate", [False, True])
+def test_decode_fused(wkv, N, dtype, epi, gate):
+    """One decode step from raw keys (rwkv7_wkv_decode_fused) against the oracle's
+    prologue + recurrence at T = 1."""
+    B, H = 6, 3
+    x = synth.draw(B, 1, H, N, seed=N + B, dtype=dtype, s0="normal", epilogue=epi)
+    k_k, k_a, g = synth.prologue_extras(B, 1, H, N, seed=N + 7, dtype=dtype)
+    d_epi = None
+    if x["epi"] is not None:
+        e = x["epi"]
+        d_epi = {"ln_w": dev(e["ln_w"]), "ln_b": dev(e["ln_b"]),
+                 "r_k": dev(np.ascontiguousarray(e["r_k"])), "eps": e["eps"]}
+    st = dev(x["s0"]).clone()
+    y = wkv.decode_fused(*(dev(x[n][:, 0]) for n in RAW), dev(k_k), dev(k_a), st,
+                         g=dev(g[:, 0]) if gate else None, epilogue=d_epi)
+    torch.cuda.synchronize()
+    y_ref, s_ref = oracle.forward_fused(*(x.as_f64(n) for n in RAW), k_k, k_a,
+                                        g=f64(g) if gate else None, s0=x["s0"], epilogue=x["epi"])
+    tol = TOL["f32" if dtype == "f32" else "bf16"]
+    assert_close(to_f64(y), y_ref[:, 0], tol, "decode fused y")
+    assert_close(to_f64(st), s_ref, tol, "decode fused S")
