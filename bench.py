@@ -62,8 +62,8 @@ def parse():
                     help="decode head size; 128 keeps the state bytes (H = 20) and needs "
                          "--only decode")
     ap.add_argument("--fused", action="store_true",
-                    help="time the fused prologue + output gate forward from raw keys "
-                         "(needs --only prefill)")
+                    help="prefill or decode from raw keys through the fused prologue, with "
+                         "the output gate (needs --only prefill or --only decode)")
     ap.add_argument("--bidir", action="store_true",
                     help="time the bidirectional forward (needs --only prefill)")
     ap.add_argument("--decay-f32", action="store_true",
@@ -153,6 +153,8 @@ def workload_name(args, long_shape, do_prefill, do_decode):
            if args.decode_head == 64 else
            "decode of 64 tokens through 32 layers x B256 x H20 resident fp32 states of head "
            "size 128")
+    if args.fused and do_decode and not do_prefill:
+        dec += ", fed from raw keys through the fused prologue, with the output gate"
     if do_prefill and do_decode:
         return "2.9B-shape WKV7: " + pre.replace("2.9B-shape WKV7 ", "") + ", then " + dec
     return pre if do_prefill else "2.9B-shape WKV7 " + dec
@@ -294,7 +296,10 @@ def main():
         print("bench.py: --decode-head 128 is a decode-only measurement (--only decode)",
               file=sys.stderr)
         sys.exit(2)
-    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir or args.fused) and \
+    if args.fused and args.only not in ("prefill", "decode"):
+        print("bench.py: --fused needs --only prefill or --only decode", file=sys.stderr)
+        sys.exit(2)
+    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir) and \
             args.only != "prefill":
         print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
               "(--only prefill)", file=sys.stderr)
@@ -388,6 +393,12 @@ def main():
             for n in NAMES:
                 d_in[n].append(one[n])
         d_in = {n: torch.stack(v) for n, v in d_in.items()}  # [DS, L, B, H, N]
+        if args.fused:  # raw keys = the draws' k; prologue parameters and gates
+            gg = torch.Generator(device=dev)
+            gg.manual_seed(77)
+            dk_k = 1.0 + 0.1 * torch.randn(DH * DN, device=dev, generator=gg)
+            dk_a = 1.0 + 0.1 * torch.randn(DH * DN, device=dev, generator=gg)
+            d_g = torch.randn(d_in["r"].shape, device=dev, generator=gg).to(torch.bfloat16)
         d_y = torch.empty((DS, L, DB, DH, DN), dtype=torch.bfloat16, device=dev)
         torch.cuda.synchronize()
         d_gen_s = time.time() - t0
@@ -400,7 +411,11 @@ def main():
         with torch.cuda.graph(graph, stream=cap_stream):
             for t in range(DS):
                 for l in range(L):
-                    wkv.decode(*(d_in[n][t, l] for n in NAMES), pool[l], y=d_y[t, l])
+                    if args.fused:
+                        wkv.decode_fused(*(d_in[n][t, l] for n in ("r", "w", "k", "v", "a")),
+                                         dk_k, dk_a, pool[l], g=d_g[t, l], y=d_y[t, l])
+                    else:
+                        wkv.decode(*(d_in[n][t, l] for n in NAMES), pool[l], y=d_y[t, l])
         torch.cuda.synchronize()
         ev_steps = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                     for _ in range(args.steps)]
@@ -495,11 +510,12 @@ def main():
     if do_decode:
         run_ms = np.array([a.elapsed_time(b) for a, b in launch_ms])
         avg_ms = float(run_ms.sum() / (len(run_ms) * n_launch))  # per launch, gaps included
+        # state in and out, six vectors in and y out (fused: r, w, k, v, a and g in)
         bytes_per_launch = DB * DH * (2 * DN * DN * 4 + 7 * DN * 2)
         achieved = bytes_per_launch / (avg_ms / 1e3) / 1e9
         traffic = (read_traffic("decode_kernel_traffic.txt",
                                 source_hash("wkv7_decode.hip", "wkv7_device.h"))
-                   if DN == 64 else None)
+                   if DN == 64 and not args.fused else None)
         out["roofline"] = {
             "kernel": f"wkv7 decode_kernel<bf16, N={DN}> (one layer, B256 x H{DH})",
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -578,7 +594,15 @@ def main():
             seq = [np.ascontiguousarray(np.moveaxis(d_in[n][:, l].cpu().double().numpy(), 0, 1))
                    for n in NAMES]
             t0 = time.perf_counter()
-            y_ref, _ = oracle.forward(*seq, s0=s_init[li], threads=threads)
+            if args.fused:
+                gseq = np.ascontiguousarray(
+                    np.moveaxis(d_g[:, l].cpu().double().numpy(), 0, 1))
+                y_ref, _ = oracle.forward_fused(seq[0], seq[1], seq[2], seq[3], seq[5],
+                                                dk_k.cpu().double().numpy(),
+                                                dk_a.cpu().double().numpy(), g=gseq,
+                                                s0=s_init[li], threads=threads)
+            else:
+                y_ref, _ = oracle.forward(*seq, s0=s_init[li], threads=threads)
             cpu_s += time.perf_counter() - t0
             cpu_work += seq[0].shape[0] * seq[0].shape[1] * seq[0].shape[2]
             del seq
