@@ -88,6 +88,13 @@ constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per la
 constexpr int kWaitAllLoads = (0x7 << 4) | (0xF << 8);  // vmcnt(0) only
 constexpr int kUnroll = 2 * kPrefetch;                   // prep loop unroll
 
+// Intervals 0 .. S-1 of the prep waves' loop: the nch chunks rounded up to
+// whole loop trips.  In all, the prep waves run max(nch + 3, S) intervals and
+// the chain waves match them.
+__device__ __forceinline__ int steady_intervals(int nch) {
+    return (nch + kUnroll - 1) / kUnroll * kUnroll;
+}
+
 constexpr int wait_older_chunks(int loads_per_chunk) {
     return ((loads_per_chunk * (kPrefetch - 1)) & 0xF) | (0x7 << 4) | (0xF << 8) |
            ((((loads_per_chunk * (kPrefetch - 1)) >> 4) & 0x3) << 14);
@@ -103,6 +110,22 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x4 mfma(bf16x4 a, bf16x4 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+typedef short bf16x8s __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// Two K = 16 products summed in one v_mfma_f32_16x16x32_bf16:
+//   c + A0 B0 + A1 B1   (A0, A1 in K = 16 A form; B0, B1 in K = 16 B form).
+// Each lane holds 8 consecutive k of the K = 32 operands in both A and B, so
+// placing (A0, A1) and (B0, B1) side by side in the lanes pairs every k of
+// A0 with the same k of B0 and likewise for A1, B1: the contraction over the
+// 32 k is the sum of the two 16-k contractions.
+__device__ __forceinline__ f32x4 mfma2(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c) {
+    const bf16x8s a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const bf16x8s b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -121,11 +144,35 @@ __device__ __forceinline__ bf16x4 to_bf16(f32x4 x) {
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
-// row shift by N inside each 16-lane DPP row; lanes without a source get 1.0
-template <int N>
-__device__ __forceinline__ float shr_fill1(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(1.0f), __float_as_int(x),
-                                                      0x110 + N, 0xF, 0xF, false));
+// value of lane E of this lane's quad (DPP quad_perm [E, E, E, E])
+template <int E>
+__device__ __forceinline__ float quad_bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), E * 0x55, 0xF, 0xF, true));
+}
+
+// Inclusive prefix products over the 16 lanes (tokens) of each DPP row, for a
+// lane's four channels at once, then kp[e] *= q[e] of the lane below (lane 0 of
+// the row keeps kp[e]):
+//   q[e] <- prod_{s <= t} w_s[e],   kp[e] <- kp[e] * prod_{s < t} w_s[e].
+// Each step is one v_mul_f32 with a DPP row shift and bound_ctrl off, which
+// leaves lanes without a source unwritten (multiplied by one); the compiler
+// forms such a fused DPP multiply only for integer identities, so the steps are
+// written out.  The four channels are interleaved, so every DPP read comes four
+// instructions after the write of its source (two wait states are required);
+// the leading s_nop 1 covers a write just before the block.
+__device__ __forceinline__ void prefix_products(float (&q)[4], float (&kp)[4]) {
+#define WKV7_DPP_MUL(D, S, SH) "v_mul_f32_dpp %" #D ", %" #S ", %" #D " row_shr:" #SH \
+                               " row_mask:0xf bank_mask:0xf\n\t"
+#define WKV7_DPP_STEP(SH) WKV7_DPP_MUL(0, 0, SH) WKV7_DPP_MUL(1, 1, SH) \
+                          WKV7_DPP_MUL(2, 2, SH) WKV7_DPP_MUL(3, 3, SH)
+    asm volatile("s_nop 1\n\t"
+                 WKV7_DPP_STEP(1) WKV7_DPP_STEP(2) WKV7_DPP_STEP(4) WKV7_DPP_STEP(8)
+                 WKV7_DPP_MUL(4, 0, 1) WKV7_DPP_MUL(5, 1, 1) WKV7_DPP_MUL(6, 2, 1)
+                 WKV7_DPP_MUL(7, 3, 1)
+                 : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]),
+                   "+v"(kp[0]), "+v"(kp[1]), "+v"(kp[2]), "+v"(kp[3]));
+#undef WKV7_DPP_STEP
+#undef WKV7_DPP_MUL
 }
 
 struct __align__(16) ChunkOps {
@@ -140,11 +187,12 @@ struct __align__(16) ChunkOps {
     short mbr[kTile];      // M_br  [t][s]
     short xinv[kTile];     // -(I + M_bk)^-1 [t][s]
     short vt[4][kTile];    // V^T [value block][i][t]  (B form of V)
+    short vr[4][kTile];    // V   [value block][t][i]  (epilogue only)
     float gc[64];          // G_C per key j
-    float bon[4][16];      // bonus partial sums per (key block, token)
+    // per (key block, token) partial sums over the block's 16 keys, fp32:
+    // [0] r_t.k_t, [1] r_t.(a_t*kappa_t), [2] the bonus sum_j r k r_k
+    float rsum[3][4][16];
     float bon_tot[16];     // bonus sum per token (all keys)
-    float dkr[4][16];      // r_t.k_t partial sums per (key block, token), fp32
-    float dbr[4][16];      // r_t.(a_t*kappa_t) partial sums, fp32
 };
 
 // Launch description: the sequence may be split into nseg segments of seg_len
@@ -242,31 +290,28 @@ struct Chunked {
         x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
     }
 
-    // Padding token past T (only in a partial last chunk): no write, no removal,
-    // no decay, no readout.
-    __device__ __forceinline__ void pad(int c, Raw<W32> &x) const {
-        if (c * kC + lo >= Tl) {
-            x.r = x.k = x.kap = x.a = x.v = make_uint2(0u, 0u);
-            x.kx[0] = x.kx[1] = x.kx[2] = make_uint2(0u, 0u);
-            if constexpr (W32)
-                x.w = make_float4(1.f, 1.f, 1.f, 1.f);
-            else
-                x.w = make_uint2(0x3F803F80u, 0x3F803F80u);
-        }
-    }
-
     // Chunk operands for key block jb = blk, written to LDS buffer `o`.
-    __device__ void prep(const Raw<W32> &x, ChunkOps &o, const float (&rk)[4],
+    // valid: the lane's token lies inside the range.  A padding token of a
+    // partial last chunk (its loads were clamped to the last token) gets k = 0,
+    // kappa = 0 and w = 1: no write, no removal and no decay, so it changes
+    // neither the state nor any other token's readout (its own is not stored).
+    // Selects rather than a branch: a branch that rewrites the prefetch ring's
+    // registers turns the compiler's wait counts for the ring conservative.
+    __device__ void prep(const Raw<W32> &x, bool valid, ChunkOps &o, const float (&rk)[4],
                          const ProParams &pro) const {
         const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
         float w[4];
         if constexpr (W32) {
             w[0] = x.w.x; w[1] = x.w.y; w[2] = x.w.z; w[3] = x.w.w;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) w[e] = valid ? w[e] : 1.f;
         } else {
-            w[0] = bf16_lo(x.w.x); w[1] = bf16_hi(x.w.x);
-            w[2] = bf16_lo(x.w.y); w[3] = bf16_hi(x.w.y);
+            const unsigned w01 = valid ? x.w.x : 0x3F803F80u, w23 = valid ? x.w.y : 0x3F803F80u;
+            w[0] = bf16_lo(w01); w[1] = bf16_hi(w01);
+            w[2] = bf16_lo(w23); w[3] = bf16_hi(w23);
         }
-        float k[4] = {bf16_lo(x.k.x), bf16_hi(x.k.x), bf16_lo(x.k.y), bf16_hi(x.k.y)};
+        const unsigned k01 = valid ? x.k.x : 0u, k23 = valid ? x.k.y : 0u;
+        float k[4] = {bf16_lo(k01), bf16_hi(k01), bf16_lo(k23), bf16_hi(k23)};
         const float a[4] = {bf16_lo(x.a.x), bf16_hi(x.a.x), bf16_lo(x.a.y), bf16_hi(x.a.y)};
         float kp[4];
         if constexpr (FUSED) {
@@ -296,30 +341,30 @@ struct Chunked {
                 k[e] = k[e] + k[e] * (a[e] - 1.f) * pro.ka[e];
             }
         } else {
-            kp[0] = bf16_lo(x.kap.x); kp[1] = bf16_hi(x.kap.x);
-            kp[2] = bf16_lo(x.kap.y); kp[3] = bf16_hi(x.kap.y);
+            const unsigned c01 = valid ? x.kap.x : 0u, c23 = valid ? x.kap.y : 0u;
+            kp[0] = bf16_lo(c01); kp[1] = bf16_hi(c01);
+            kp[2] = bf16_lo(c23); kp[3] = bf16_hi(c23);
         }
-        f32x4 G, Gx, Kp, Rp, Km, Bm;
+        f32x4 G, Kp, Rp, Km, Bm;
         float bon = 0.f, dkr = 0.f, dbr = 0.f;
+        float be[4], kpg[4] = {kp[0], kp[1], kp[2], kp[3]};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) be[e] = a[e] * kp[e];
+        // G_t = prod_{s<=t} w_s over the chunk's tokens (lanes of the DPP row) and
+        // kappa_t G_{t-1} (G_{-1} = 1)
+        prefix_products(w, kpg);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            // inclusive prefix product of w over the chunk's tokens (lanes of the DPP row)
-            float q = w[e];
-            q *= shr_fill1<1>(q);
-            q *= shr_fill1<2>(q);
-            q *= shr_fill1<4>(q);
-            q *= shr_fill1<8>(q);
+            const float q = w[e];
             G[e] = q;
-            Gx[e] = shr_fill1<1>(q);
             const float iG = __builtin_amdgcn_rcpf(q);  // 1 ulp; operands are rounded to bf16
-            const float be = a[e] * kp[e];
-            Kp[e] = kp[e] * Gx[e];
+            Kp[e] = kpg[e];
             Rp[e] = r[e] * q;
             Km[e] = k[e] * iG;
-            Bm[e] = be * iG;
+            Bm[e] = be[e] * iG;
             if (EPI) bon += r[e] * k[e] * rk[e];
             dkr += r[e] * k[e];
-            dbr += r[e] * be;
+            dbr += r[e] * be[e];
         }
         const int jb = blk;
         st_a(o.kp[jb], lane, to_bf16(Kp));
@@ -332,6 +377,8 @@ struct Chunked {
             o.kmt[jb][(4 * g + e) * kRow + lo] = kmb[e];
             o.bmt[jb][(4 * g + e) * kRow + lo] = bmb[e];
         }
+        if (EPI)  // V rows [t][i] for the bonus term of the readouts
+            *reinterpret_cast<uint2 *>(o.vr[jb] + lo * kRow + 4 * g) = x.v;
         o.vt[jb][(4 * g + 0) * kRow + lo] = (short)(x.v.x & 0xffffu);
         o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(x.v.x >> 16);
         o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(x.v.y & 0xffffu);
@@ -343,71 +390,65 @@ struct Chunked {
         // r_t.k_t and r_t.(a_t*kappa_t) need no bf16 factors; the two-factor bf16
         // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
         // early readouts whose dot product nearly cancels
-        dkr = sum_rows4(dkr);
-        dbr = sum_rows4(dbr);
-        if (g == 0) {
-            o.dkr[jb][lo] = dkr;
-            o.dbr[jb][lo] = dbr;
-        }
-        if (EPI) {
-            bon = sum_rows4(bon);
-            if (g == 0) o.bon[jb][lo] = bon;
-        }
+        // the three sums over the four lanes g in one pass: DPP row g ends up
+        // holding sum number packed_col(g) (row 3 the unused fourth)
+        const float sums = sum_rows4_packed(dkr, dbr, EPI ? bon : 0.f, 0.f);
+        const int qn = packed_col(g);
+        if (qn < (EPI ? 3 : 2)) o.rsum[qn][jb][lo] = sums;
     }
 
     // One C x C matrix of a chunk per prep wave; wave 5 forms the triangular inverse.
     __device__ void matrices(ChunkOps &o) const {
         const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
         if (blk == 1) {
-            // N = M_bk in B form (D of Kp.Bm^T) and in A form (D of Bm.Kp^T)
-            f32x4 nb = zero4(), na = zero4();
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) {
-                const bf16x4 kpa = ld_a(o.kp[jb], lane), bma = ld_a(o.bm[jb], lane);
-                nb = mfma(kpa, bma, nb);
-                na = mfma(bma, kpa, na);
-            }
-            f32x4 imn, n4i, n2i;
+            // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
+            // is the B form of M and the A form of M^T.
+            // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
+            const bf16x4 kp0 = ld_a(o.kp[0], lane), kp1 = ld_a(o.kp[1], lane);
+            const bf16x4 kp2 = ld_a(o.kp[2], lane), kp3 = ld_a(o.kp[3], lane);
+            const bf16x4 bm0 = ld_a(o.bm[0], lane), bm1 = ld_a(o.bm[1], lane);
+            const bf16x4 bm2 = ld_a(o.bm[2], lane), bm3 = ld_a(o.bm[3], lane);
+            f32x4 nb = mfma2(kp2, kp3, bm2, bm3, mfma2(kp0, kp1, bm0, bm1, zero4()));
+            f32x4 na = mfma2(bm2, bm3, kp2, kp3, mfma2(bm0, bm1, kp0, kp1, zero4()));
+            f32x4 imnt;  // D(I - N^T)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                nb[e] = (lo < row + e) ? nb[e] : 0.f;   // B form: [t = row+e][s = lo], s < t
-                na[e] = (row + e < lo) ? na[e] : 0.f;   // A form: [t = lo][s = row+e], s < t
-                imn[e] = (row + e == lo ? 1.f : 0.f) - nb[e];
+                nb[e] = (lo < row + e) ? nb[e] : 0.f;   // [t = row+e][s = lo], s < t
+                na[e] = (row + e < lo) ? na[e] : 0.f;   // [s = row+e][t = lo], s < t
+                imnt[e] = (row + e == lo ? 1.f : 0.f) - na[e];
             }
+            // X = (I + N)^-1 = F1 (I + N^4)(I + N^8) with F1 = (I - N)(I + N^2), all
+            // polynomials in N (they commute); evaluated as
+            //   F1^T = (I - N^T) + N2^T (I - N^T),  G^T = F1^T + N4^T F1^T,
+            //   X^T = G^T + N8^T G^T
+            // so the chain is N, N^2, N^4 | F1^T, N^8 | G^T, X^T: four products deep
             const bf16x4 Nb = to_bf16(nb), Na = to_bf16(na);
-            const f32x4 n2 = mfma(Na, Nb, zero4());    // N^2      (B form)
-            const f32x4 n2t = mfma(Nb, Na, zero4());   // (N^2)^T  (B form) = N^2 (A form)
+            const f32x4 n2 = mfma(Na, Nb, zero4());                // D(N^2)
+            const f32x4 n2t = mfma(Nb, Na, zero4());               // D(N^2^T)
             const bf16x4 N2b = to_bf16(n2), N2a = to_bf16(n2t);
-            const f32x4 n4 = mfma(N2a, N2b, zero4());
-            const f32x4 n4t = mfma(N2b, N2a, zero4());
-            const bf16x4 N4b = to_bf16(n4), N4a = to_bf16(n4t);
-            f32x4 z = mfma(N4b, N4a, zero4());         // (N^8)^T (B form)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const float id = (row + e == lo) ? 1.f : 0.f;
-                z[e] += id;
-                n4i[e] = n4[e] + id;
-                n2i[e] = n2[e] + id;
-            }
-            // X^T = (I - N^T)(I + (N^2)^T)(I + (N^4)^T)(I + (N^8)^T); the B form of
-            // I + N^p is the A form of (I + N^p)^T
-            z = mfma(to_bf16(n4i), to_bf16(z), zero4());
-            z = mfma(to_bf16(n2i), to_bf16(z), zero4());
-            z = mfma(to_bf16(imn), to_bf16(z), zero4());
-            st_a(o.xinv, lane, to_bf16(-z));           // D of X^T = A form of X; stored negated
+            const f32x4 n4 = mfma(N2a, N2b, zero4());              // D(N^4)
+            const f32x4 n4t = mfma(N2b, N2a, zero4());             // D(N^4^T)
+            const f32x4 f1t = mfma(N2b, to_bf16(imnt), imnt);      // D(F1^T)
+            const bf16x4 N4b = to_bf16(n4);
+            const f32x4 gt = mfma(N4b, to_bf16(f1t), f1t);         // D(G^T)
+            const f32x4 n8 = mfma(to_bf16(n4t), N4b, zero4());     // D(N^8)
+            const f32x4 z = mfma(to_bf16(n8), to_bf16(gt), gt);    // D(X^T) = A form of X
+            st_a(o.xinv, lane, to_bf16(-z));                       // stored negated
         } else {
             if (EPI && blk == 0 && lane < 16)
-                o.bon_tot[lane] = o.bon[0][lane] + o.bon[1][lane] + o.bon[2][lane] + o.bon[3][lane];
+                o.bon_tot[lane] = o.rsum[2][0][lane] + o.rsum[2][1][lane] + o.rsum[2][2][lane] +
+                                  o.rsum[2][3][lane];
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kTile] = (blk == 3) ? o.bm : o.km;
             const short(*rhs)[kTile] = (blk == 0) ? o.kp : o.rp;
-            f32x4 m = zero4();
-#pragma unroll
-            for (int jb = 0; jb < 4; ++jb) m = mfma(ld_a(lhs[jb], lane), ld_a(rhs[jb], lane), m);
+            f32x4 m = mfma2(ld_a(lhs[0], lane), ld_a(lhs[1], lane), ld_a(rhs[0], lane),
+                            ld_a(rhs[1], lane), zero4());
+            m = mfma2(ld_a(lhs[2], lane), ld_a(lhs[3], lane), ld_a(rhs[2], lane),
+                      ld_a(rhs[3], lane), m);
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
             float diag = 0.f;
             if (blk != 0) {
-                const float(*dd)[16] = (blk == 2) ? o.dkr : o.dbr;
+                const float(*dd)[16] = o.rsum[blk == 2 ? 0 : 1];
                 diag = dd[0][lo] + dd[1][lo] + dd[2][lo] + dd[3][lo];
             }
 #pragma unroll
@@ -423,59 +464,53 @@ struct Chunked {
 };
 
 // Per-chain-lane state carried from chunk c's chain to its readout stores one
-// interval later: the 4 readouts y[t = 4g+e][i], the token bonus sums and v.
+// interval later.  The chain forms Y^T, so lane (g, lo) of chain wave blk holds
+// the readouts of token lo of the chunk at the four value channels
+// i = 16blk + 4g + e: y[e], with v of the same token and channels, the token's
+// bonus sum and (fused prologue) the raw bf16 output gates.
 struct Pending {
     f32x4 y;
-    float bon[4];
-    uint16_t graw[4];  // fused prologue: raw bf16 output gate of the four tokens
-    bf16x4 v;
+    float bon;
+    uint2 graw;  // four bf16 gates
+    uint2 v;     // four bf16 values
 };
 
 template <bool EPI, bool W32, bool FUSED>
 __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
                                                 const Chunked<EPI, W32, FUSED> &K,
                                                 const ChunkSmem &sm, const Pending &pd, int c,
-                                                float lnw, float lnb, long yoff) {
-    const int g = K.g;
-    float yv[4];
+                                                const float (&lnw)[4], const float (&lnb)[4],
+                                                long yoff) {
+    float yv[4] = {pd.y[0], pd.y[1], pd.y[2], pd.y[3]};
+    if (EPI) {
+        // GroupNorm statistics of this lane's token from the four value blocks'
+        // (mean, M2) (Chan et al. pairwise combination of equal-sized groups)
+        const float2 *st = sm.stats[c & 1][K.lo];
+        const float4 m01 = *reinterpret_cast<const float4 *>(st);
+        const float4 m23 = *reinterpret_cast<const float4 *>(st + 2);
+        const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
+        const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
+        const float m2 = (m01.y + m01.w + m23.y + m23.w) +
+                         16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
+        const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
+        const float v[4] = {bf16_lo(pd.v.x), bf16_hi(pd.v.x), bf16_lo(pd.v.y), bf16_hi(pd.v.y)};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        yv[e] = pd.y[e];
-        if (EPI) {
-            const float2 *st = sm.stats[c & 1][4 * g + e];
-            const float4 m01 = *reinterpret_cast<const float4 *>(st);
-            const float4 m23 = *reinterpret_cast<const float4 *>(st + 2);
-            const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
-            const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
-            const float m2 = (m01.y + m01.w + m23.y + m23.w) +
-                             16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
-            const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
-            yv[e] = (yv[e] - mu) * rs * lnw + lnb +
-                    pd.bon[e] * bf16_lo((unsigned)(unsigned short)pd.v[e]);
-        }
-        if (FUSED && p.g) yv[e] *= bf16_lo(pd.graw[e]);  // output gate
+        for (int e = 0; e < 4; ++e) yv[e] = (yv[e] - mu) * (rs * lnw[e]) + lnb[e] + pd.bon * v[e];
     }
-    // yoff: element offset of token c*16 + 4g of this lane's value channel
-    const int t0 = c * kC + 4 * g;
-    const int nt = min(4, K.Tl - t0);
+    if (FUSED && p.g) {  // output gate
+        yv[0] *= bf16_lo(pd.graw.x);
+        yv[1] *= bf16_hi(pd.graw.x);
+        yv[2] *= bf16_lo(pd.graw.y);
+        yv[3] *= bf16_hi(pd.graw.y);
+    }
+    // yoff: element offset of (token c*16 + lo, channel 16blk + 4g)
+    if (c * kC + K.lo >= K.Tl) return;  // padding token of a partial last chunk
     if (p.y_f32) {  // float32 readouts, no rounding (first pass of a bidirectional call)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (e < nt) p.y_f32[yoff + e * K.TS] = yv[e];
+        *reinterpret_cast<float4 *>(p.y_f32 + yoff) = make_float4(yv[0], yv[1], yv[2], yv[3]);
         return;
     }
-    uint16_t *y = static_cast<uint16_t *>(p.y) + yoff;
-    const unsigned lo2 = cvt_pk(yv[0], yv[1]), hi2 = cvt_pk(yv[2], yv[3]);
-    const unsigned short out[4] = {(unsigned short)(lo2 & 0xffffu), (unsigned short)(lo2 >> 16),
-                                   (unsigned short)(hi2 & 0xffffu), (unsigned short)(hi2 >> 16)};
-    if (nt == 4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) y[e * K.TS] = out[e];
-    } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (e < nt) y[e * K.TS] = out[e];
-    }
+    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.y) + yoff) =
+        make_uint2(cvt_pk(yv[0], yv[1]), cvt_pk(yv[2], yv[3]));
 }
 
 // SUMMARY = false: y and the final state of each (b, h, segment) from its entry
@@ -529,23 +564,28 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     Z[jb][e] = (p_rows && 16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
             }
         }
-        float lnw = 1.f, lnb = 0.f;
-        if (EPI) {
-            if (p.epi.ln_w) lnw = p.epi.ln_w[h * kN + 16 * blk + lo];
-            if (p.epi.ln_b) lnb = p.epi.ln_b[h * kN + 16 * blk + lo];
+        // GroupNorm weight and bias of this lane's four value channels
+        float lnw[4] = {1.f, 1.f, 1.f, 1.f}, lnb[4] = {0.f, 0.f, 0.f, 0.f};
+        const int ich = h * kN + 16 * blk + 4 * g;
+        if (EPI && p.epi.ln_w) {
+            const float4 q = *reinterpret_cast<const float4 *>(p.epi.ln_w + ich);
+            lnw[0] = q.x; lnw[1] = q.y; lnw[2] = q.z; lnw[3] = q.w;
+        }
+        if (EPI && p.epi.ln_b) {
+            const float4 q = *reinterpret_cast<const float4 *>(p.epi.ln_b + ich);
+            lnb[0] = q.x; lnb[1] = q.y; lnb[2] = q.z; lnb[3] = q.w;
         }
         Pending pd;
-        long ylane = K.tok0 + (long)(4 * g) * K.TS + 16 * blk + lo;  // y element offset
+        // element offset of (token lo of the chunk, value channel 16blk + 4g)
+        long ylane = K.tok0 + (long)lo * K.TS + 16 * blk + 4 * g;
         // added readouts of a chunk, loaded at the start of its iteration and used
         // after its MFMA chain (token index clamped into the range: no branch
         // around the loads, and no load waited for across the loop's back edge)
         constexpr bool kYadd = YADD && !SUMMARY;
-        float ya[4] = {0.f, 0.f, 0.f, 0.f};
+        float4 ya = make_float4(0.f, 0.f, 0.f, 0.f);
         auto load_ya = [&](int cc) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                ya[e] = p.y_add[K.tok0 + (long)min(cc * kC + 4 * g + e, K.Tl - 1) * K.TS +
-                                16 * blk + lo];
+            ya = *reinterpret_cast<const float4 *>(
+                p.y_add + K.tok0 + (long)min(cc * kC + lo, K.Tl - 1) * K.TS + 16 * blk + 4 * g);
         };
         // everything loaded so far is in registers before the chunk loop, so no
         // wait for these loads is left inside it
@@ -575,66 +615,63 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                     // (the bits are only widened where the readouts are finished, one
                     // chunk later, so nothing waits for these loads before the barrier)
                     const uint16_t *gsrc = static_cast<const uint16_t *>(p.g ? p.g : p.k);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = c * kC + 4 * g + e;
-                        pd.graw[e] = gsrc[K.tok0 + (long)min(t, K.Tl - 1) * K.TS + 16 * blk + lo];
-                    }
+                    pd.graw = *reinterpret_cast<const uint2 *>(
+                        gsrc + K.tok0 + (long)min(c * kC + lo, K.Tl - 1) * K.TS + 16 * blk + 4 * g);
                 }
                 const ChunkOps &o = sm.ops[c % 3];
                 const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
                 bf16x4 Zb[4];
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
-                f32x4 rhs = mfma(ld_a(o.mkk, lane), Vb, zero4());
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) rhs = mfma(ld_a(o.kp[jb], lane), Zb[jb], rhs);
+                // rhs = M_kk V + Kp S0^T: five 16-k products in three K = 32 MFMAs (the
+                // last one half empty), so the accumulation chain stays within one
+                // MFMA opcode
+                f32x4 rhs = mfma2(ld_a(o.mkk, lane), ld_a(o.kp[0], lane), Vb, Zb[0], zero4());
+                rhs = mfma2(ld_a(o.kp[1], lane), ld_a(o.kp[2], lane), Zb[1], Zb[2], rhs);
+                rhs = mfma2(ld_a(o.kp[3], lane), bf16x4{0, 0, 0, 0}, Zb[3], bf16x4{0, 0, 0, 0}, rhs);
+                // readouts as Y^T = S0 Rp^T + V^T M_kr^T - U^T M_br^T (the operands of
+                // Y with their roles swapped): lane holds Y^T[i = 4g+e][t = lo]; the
+                // terms without U first, so only one product waits for U
+                f32x4 Y = mfma2(Zb[0], Zb[1], ld_a(o.rp[0], lane), ld_a(o.rp[1], lane), zero4());
+                Y = mfma2(Zb[2], Zb[3], ld_a(o.rp[2], lane), ld_a(o.rp[3], lane), Y);
                 const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
                 const bf16x4 Ub = to_bf16(U);
-                f32x4 Y = mfma(ld_a(o.mkr, lane), Vb, zero4());
-                Y = mfma(ld_a(o.mbr, lane), Ub, Y);
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) Y = mfma(ld_a(o.rp[jb], lane), Zb[jb], Y);
+                Y = mfma2(Vb, Ub, ld_a(o.mkr, lane), ld_a(o.mbr, lane), Y);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
-                    Z[jb] = mfma(ld_a(o.kmt[jb], lane), Vb, Z[jb]);
-                    Z[jb] = mfma(ld_a(o.bmt[jb], lane), Ub, Z[jb]);
+                    Z[jb] = mfma2(ld_a(o.kmt[jb], lane), ld_a(o.bmt[jb], lane), Vb, Ub, Z[jb]);
                     const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
                     Z[jb][0] *= gc.x;
                     Z[jb][1] *= gc.y;
                     Z[jb][2] *= gc.z;
                     Z[jb][3] *= gc.w;
                 }
-                if (kYadd) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (c * kC + 4 * g + e < K.Tl) Y[e] += ya[e];
+                if (kYadd) {  // (a padding token's sum is never stored)
+                    Y[0] += ya.x;
+                    Y[1] += ya.y;
+                    Y[2] += ya.z;
+                    Y[3] += ya.w;
                 }
                 pd.y = Y;
-                pd.v = Vb;
                 // stored states: the one leaving this chunk enters the next; stored
                 // here, in the slack before the barrier, rather than just before
                 // the MFMAs that overwrite the accumulators
                 if (ckpt && c + 1 < nch) store_state(ckpt + (long)(c + 1) * kN * kN);
                 if (EPI && !SUMMARY) {
-                    // readouts: lane holds y[t = 4g+e][i = 16blk + lo]
-                    const float4 bt = *reinterpret_cast<const float4 *>(&o.bon_tot[4 * g]);
-                    pd.bon[0] = bt.x;
-                    pd.bon[1] = bt.y;
-                    pd.bon[2] = bt.z;
-                    pd.bon[3] = bt.w;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int t = 4 * g + e;
-                        const float mu = sum_lanes16(Y[e]) * (1.f / 16.f);
-                        const float dd = Y[e] - mu;
-                        const float m2 = sum_lanes16(dd * dd);
-                        if (lo == 0) sm.stats[c & 1][t][blk] = make_float2(mu, m2);
-                    }
+                    pd.bon = o.bon_tot[lo];
+                    pd.v = *reinterpret_cast<const uint2 *>(o.vr[blk] + lo * kRow + 4 * g);
+                    // mean and M2 of token lo's readouts over this value block: four
+                    // in the lane, summed over the four DPP rows g
+                    const float mu = sum_rows4((Y[0] + Y[1]) + (Y[2] + Y[3])) * (1.f / 16.f);
+                    const float d0 = Y[0] - mu, d1 = Y[1] - mu, d2 = Y[2] - mu, d3 = Y[3] - mu;
+                    const float m2 = sum_rows4((d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3));
+                    if (g == 0) sm.stats[c & 1][lo][blk] = make_float2(mu, m2);
                 }
             }
             __syncthreads();
         }
+        // the prep waves' extra intervals past nch + 2 (see steady_intervals)
+        for (int q = nch + 3; q < steady_intervals(nch); ++q) __syncthreads();
         if (s_fin) {
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb)
@@ -659,32 +696,50 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
             const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * blk + 4 * g);
             rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
         }
-        // raw inputs of the next kPrefetch chunks stay in flight in a register ring;
-        // interval q (q = 0 .. nch + 2) prepares chunk q and forms chunk q-1's matrices
+        // Raw inputs of the next kPrefetch chunks stay in flight in a register ring.
+        // Interval q (one barrier each) forms chunk q-1's matrices and prepares
+        // chunk q from ring slot q % kPrefetch, which then receives chunk
+        // q + kPrefetch.  The intervals run in a loop without branches inside its
+        // body, unrolled over whole turns of the ring and entered with the ring
+        // in its steady state: every join or extra back edge there makes the
+        // compiler's wait counts for the ring conservative (it then waits for
+        // loads issued one interval earlier instead of kPrefetch - 1).  So the
+        // loop runs whole trips, S = steady_intervals(nch) >= nch intervals:
+        //   - interval 0 forms the matrices of buffer 2, which nobody reads
+        //     before prep fills it in interval 2 and matrices in interval 3;
+        //   - intervals past nch - 1 prepare chunks made only of padding tokens
+        //     (clamped loads).
+        // Both are harmless because interval q writes only the buffers of
+        // chunks q and q-1 while the chain waves read chunk q-2's.
+        // (the parameters above are in registers before the ring's loads start,
+        // so no wait for them is left inside the loop)
+        __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         Raw<W32> xs[kPrefetch];
 #pragma unroll
         for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
-        // (unrolled over two turns of the ring: the compiler's wait-count analysis
-        // turns conservative only in the first interval after the loop's back edge)
-        for (int q0 = 0; q0 < nch + 3; q0 += kUnroll) {
+        // the next interval consumes the oldest ring slot: let only the
+        // (kPrefetch-1) younger chunks' loads stay in flight (stated explicitly,
+        // since the compiler's count does not survive the loop's back edge)
+        __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
+        static_assert(kUnroll % kPrefetch == 0, "the loop advances whole ring turns");
+        const int S = steady_intervals(nch);
+        for (int q0 = 0; q0 < S; q0 += kUnroll) {
 #pragma unroll
             for (int d = 0; d < kUnroll; ++d) {
                 const int q = q0 + d;
-                if (q >= nch + 3) break;
                 Raw<W32> &x = xs[d % kPrefetch];
-                if (q >= 1 && q - 1 < nch) K.matrices(sm.ops[(q - 1) % 3]);
-                if (q < nch) {
-                    if ((q + 1) * kC > K.Tl) K.pad(q, x);  // partial last chunk only
-                    K.prep(x, sm.ops[q % 3], rk, pro);
-                }
+                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
+                K.prep(x, q * kC + lo < K.Tl, sm.ops[q % 3], rk, pro);
                 K.load(q + kPrefetch, x);  // clamped: always the same loads per interval
-                // the next interval consumes the oldest ring slot: let only the
-                // (kPrefetch-1) younger chunks' loads stay in flight.  Stated
-                // explicitly because the compiler's own count is lost across the
-                // loop's back edge and would wait for nearly every load.
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
                 __syncthreads();
             }
+        }
+        // the intervals left up to nch + 2: the last chunk's matrices if the loop
+        // stopped at interval nch, then barriers only
+        for (int q = S; q < nch + 3; ++q) {
+            if (q == nch) K.matrices(sm.ops[(nch - 1) % 3]);
+            __syncthreads();
         }
     }
 }
