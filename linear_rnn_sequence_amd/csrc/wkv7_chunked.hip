@@ -290,17 +290,22 @@ struct Chunked {
         x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
     }
 
-    // Chunk operands for key block jb = blk, written to LDS buffer `o`.
     // valid: the lane's token lies inside the range.  A padding token of a
     // partial last chunk (its loads were clamped to the last token) gets k = 0,
     // kappa = 0 and w = 1: no write, no removal and no decay, so it changes
     // neither the state nor any other token's readout (its own is not stored).
     // Selects rather than a branch: a branch that rewrites the prefetch ring's
     // registers turns the compiler's wait counts for the ring conservative.
-    __device__ void prep(const Raw<W32> &x, bool valid, ChunkOps &o, const float (&rk)[4],
-                         const ProParams &pro) const {
-        const float r[4] = {bf16_lo(x.r.x), bf16_hi(x.r.x), bf16_lo(x.r.y), bf16_hi(x.r.y)};
-        float w[4];
+    // The raw inputs of one lane (token lo of the chunk, four channels) widened
+    // to float, kp = kappa (with the fused prologue formed here from raw keys).
+    struct Unpacked {
+        float r[4], w[4], k[4], a[4], kp[4];
+        uint2 v;
+    };
+    __device__ Unpacked unpack(const Raw<W32> &x, bool valid, const ProParams &pro) const {
+        Unpacked u;
+        float *r = u.r, *w = u.w, *k = u.k, *a = u.a, *kp = u.kp;
+        r[0] = bf16_lo(x.r.x); r[1] = bf16_hi(x.r.x); r[2] = bf16_lo(x.r.y); r[3] = bf16_hi(x.r.y);
         if constexpr (W32) {
             w[0] = x.w.x; w[1] = x.w.y; w[2] = x.w.z; w[3] = x.w.w;
 #pragma unroll
@@ -311,9 +316,8 @@ struct Chunked {
             w[2] = bf16_lo(w23); w[3] = bf16_hi(w23);
         }
         const unsigned k01 = valid ? x.k.x : 0u, k23 = valid ? x.k.y : 0u;
-        float k[4] = {bf16_lo(k01), bf16_hi(k01), bf16_lo(k23), bf16_hi(k23)};
-        const float a[4] = {bf16_lo(x.a.x), bf16_hi(x.a.x), bf16_lo(x.a.y), bf16_hi(x.a.y)};
-        float kp[4];
+        k[0] = bf16_lo(k01); k[1] = bf16_hi(k01); k[2] = bf16_lo(k23); k[3] = bf16_hi(k23);
+        a[0] = bf16_lo(x.a.x); a[1] = bf16_hi(x.a.x); a[2] = bf16_lo(x.a.y); a[3] = bf16_hi(x.a.y);
         if constexpr (FUSED) {
             // kappa = normalise(k * k_k) over the token's 64 channels (this lane's 4 in
             // each key block, the four lanes g of the DPP column); k <- k + k (a-1) k_a
@@ -345,6 +349,15 @@ struct Chunked {
             kp[0] = bf16_lo(c01); kp[1] = bf16_hi(c01);
             kp[2] = bf16_lo(c23); kp[3] = bf16_hi(c23);
         }
+        u.v = x.v;
+        return u;
+    }
+
+    // Chunk operands for key block blk from the unpacked inputs, written to LDS
+    // buffer `o`.
+    __device__ void prep(const Unpacked &u, ChunkOps &o, const float (&rk)[4]) const {
+        const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
+        float w[4] = {u.w[0], u.w[1], u.w[2], u.w[3]};
         f32x4 G, Kp, Rp, Km, Bm;
         float bon = 0.f, dkr = 0.f, dbr = 0.f;
         float be[4], kpg[4] = {kp[0], kp[1], kp[2], kp[3]};
@@ -378,11 +391,11 @@ struct Chunked {
             o.bmt[jb][(4 * g + e) * kRow + lo] = bmb[e];
         }
         if (EPI)  // V rows [t][i] for the bonus term of the readouts
-            *reinterpret_cast<uint2 *>(o.vr[jb] + lo * kRow + 4 * g) = x.v;
-        o.vt[jb][(4 * g + 0) * kRow + lo] = (short)(x.v.x & 0xffffu);
-        o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(x.v.x >> 16);
-        o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(x.v.y & 0xffffu);
-        o.vt[jb][(4 * g + 3) * kRow + lo] = (short)(x.v.y >> 16);
+            *reinterpret_cast<uint2 *>(o.vr[jb] + lo * kRow + 4 * g) = u.v;
+        o.vt[jb][(4 * g + 0) * kRow + lo] = (short)(u.v.x & 0xffffu);
+        o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(u.v.x >> 16);
+        o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(u.v.y & 0xffffu);
+        o.vt[jb][(4 * g + 3) * kRow + lo] = (short)(u.v.y >> 16);
         // the last token's lane holds the whole-chunk decay G_C of its 4 channels
         if (lo == 15) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
             make_float4(G[0], G[1], G[2], G[3]);
@@ -729,8 +742,16 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 const int q = q0 + d;
                 Raw<W32> &x = xs[d % kPrefetch];
                 K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
-                K.prep(x, q * kC + lo < K.Tl, sm.ops[q % 3], rk, pro);
-                K.load(q + kPrefetch, x);  // clamped: always the same loads per interval
+                // widen the slot, form chunk q's operands and refill the slot with
+                // chunk q + kPrefetch (clamped: always the same loads per
+                // interval).  With the fused prologue the refill goes out before
+                // the operands are formed: its loads then overlap the prologue's
+                // arithmetic (measured faster there; without the prologue the
+                // extra live registers cost more than the overlap gains).
+                const auto u = K.unpack(x, q * kC + lo < K.Tl, pro);
+                if constexpr (FUSED) K.load(q + kPrefetch, x);
+                K.prep(u, sm.ops[q % 3], rk);
+                if constexpr (!FUSED) K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
                 __syncthreads();
             }
