@@ -150,31 +150,6 @@ __device__ __forceinline__ float quad_bcast(float x) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), E * 0x55, 0xF, 0xF, true));
 }
 
-// Inclusive prefix products over the 16 lanes (tokens) of each DPP row, for a
-// lane's four channels at once, then kp[e] *= q[e] of the lane below (lane 0 of
-// the row keeps kp[e]):
-//   q[e] <- prod_{s <= t} w_s[e],   kp[e] <- kp[e] * prod_{s < t} w_s[e].
-// Each step is one v_mul_f32 with a DPP row shift and bound_ctrl off, which
-// leaves lanes without a source unwritten (multiplied by one); the compiler
-// forms such a fused DPP multiply only for integer identities, so the steps are
-// written out.  The four channels are interleaved, so every DPP read comes four
-// instructions after the write of its source (two wait states are required);
-// the leading s_nop 1 covers a write just before the block.
-__device__ __forceinline__ void prefix_products(float (&q)[4], float (&kp)[4]) {
-#define WKV7_DPP_MUL(D, S, SH) "v_mul_f32_dpp %" #D ", %" #S ", %" #D " row_shr:" #SH \
-                               " row_mask:0xf bank_mask:0xf\n\t"
-#define WKV7_DPP_STEP(SH) WKV7_DPP_MUL(0, 0, SH) WKV7_DPP_MUL(1, 1, SH) \
-                          WKV7_DPP_MUL(2, 2, SH) WKV7_DPP_MUL(3, 3, SH)
-    asm volatile("s_nop 1\n\t"
-                 WKV7_DPP_STEP(1) WKV7_DPP_STEP(2) WKV7_DPP_STEP(4) WKV7_DPP_STEP(8)
-                 WKV7_DPP_MUL(4, 0, 1) WKV7_DPP_MUL(5, 1, 1) WKV7_DPP_MUL(6, 2, 1)
-                 WKV7_DPP_MUL(7, 3, 1)
-                 : "+v"(q[0]), "+v"(q[1]), "+v"(q[2]), "+v"(q[3]),
-                   "+v"(kp[0]), "+v"(kp[1]), "+v"(kp[2]), "+v"(kp[3]));
-#undef WKV7_DPP_STEP
-#undef WKV7_DPP_MUL
-}
-
 struct __align__(16) ChunkOps {
     short kp[4][kTile];    // Kp  [jb][t][j]   (A form rows t; also B form of Kp^T)
     short rp[4][kTile];    // Rp  [jb][t][j]
@@ -189,10 +164,9 @@ struct __align__(16) ChunkOps {
     short vt[4][kTile];    // V^T [value block][i][t]  (B form of V)
     short vr[4][kTile];    // V   [value block][t][i]  (epilogue only)
     float gc[64];          // G_C per key j
-    // per (key block, token) partial sums over the block's 16 keys, fp32:
-    // [0] r_t.k_t, [1] r_t.(a_t*kappa_t), [2] the bonus sum_j r k r_k
-    float rsum[3][4][16];
-    float bon_tot[16];     // bonus sum per token (all keys)
+    // per token sums over the 64 keys, fp32: [0] r_t.k_t, [1] r_t.(a_t*kappa_t),
+    // [2] the bonus sum_j r k r_k
+    float rsum[3][16];
 };
 
 // Launch description: the sequence may be split into nseg segments of seg_len
@@ -209,6 +183,7 @@ struct ChunkedParams {
 struct __align__(16) ChunkSmem {
     ChunkOps ops[3];
     float2 stats[2][16][4];  // per token, per value block: (mean, M2) of 16 readouts
+    float4 carry[2][4][16];  // per chunk parity and prep wave: w over its 4 tokens
 };
 
 __device__ __forceinline__ bf16x4 ld_a(const short *tile, int lane) {
@@ -231,15 +206,13 @@ struct RawW<true> {
 };
 template <bool W32>
 struct Raw {
-    uint2 r, k, kap, a, v;
+    uint2 r, k, kap, a, v;  // kap unused with the fused prologue
     typename RawW<W32>::T w;
-    uint2 kx[3];  // fused prologue: raw keys of key blocks blk+1, blk+2, blk+3 (mod 4)
 };
 
-// Fused prologue parameters of a prep lane: k_k of its four channels in each
-// key block (kk[i]: block blk+i mod 4) and k_a of its own channels.
+// Fused prologue parameters of a prep lane: k_k and k_a of its four channels.
 struct ProParams {
-    float kk[4][4];
+    float kk[4];
     float ka[4];
 };
 
@@ -252,7 +225,7 @@ struct Chunked {
     // sequence is walked from its end), and the offset of (b, token t0 of the
     // processing order, h, 0).
     const long TS, tok0;
-    const long lane_off;         // prep lane: its 4 channels at token lo of chunk 0
+    const long lane_off;         // prep lane: its token (ptok) of chunk 0, channels 4lo..4lo+3
 
     __device__ Chunked(const ForwardArgs &p_, int b_, int h_, int t0, int tl)
         : p(p_), lane(threadIdx.x & 63), blk((threadIdx.x >> 6) & 3),
@@ -260,32 +233,32 @@ struct Chunked {
           TS(p_.reverse ? -(long)p_.H * kN : (long)p_.H * kN),
           tok0(((long)b_ * p_.T + (p_.reverse ? p_.T - 1 - t0 : t0)) * ((long)p_.H * kN) +
                (long)h_ * kN),
-          lane_off(tok0 + (long)(threadIdx.x & 15) * TS + 16 * ((threadIdx.x >> 6) & 3) +
-                   4 * ((threadIdx.x & 63) >> 4)) {}
+          lane_off(tok0 + (long)(4 * ((threadIdx.x >> 6) & 3) + ((threadIdx.x & 63) >> 4)) * TS +
+                   4 * (threadIdx.x & 15)) {}
 
-    // Issues exactly six loads on every path (no branch around them), so the
+    // Prep lanes are token-major: prep wave b holds tokens 4b .. 4b+3 of a chunk,
+    // one per DPP row g, and lane lo of the row holds keys 4lo .. 4lo+3, so the
+    // row holds the token's whole 64-key vector and each load instruction reads
+    // four whole rows (a key-block split would touch sixteen partial lines).
+    __device__ __forceinline__ int ptok() const { return 4 * blk + g; }
+
+    // Issues the same loads on every path (no branch around them), so the
     // compiler's wait-count bookkeeping can leave the later chunks of the ring in
     // flight: the chunk index is clamped to the last chunk and the token index to
-    // T-1, which keeps every address inside the tensors; prep() replaces the
+    // T-1, which keeps every address inside the tensors; unpack() replaces the
     // values of tokens past T.
     __device__ void load(int c, Raw<W32> &x) const {
         const int cc = min(c, (Tl - 1) / kC);
-        const int t = min(cc * kC + lo, Tl - 1);
-        const long off = lane_off + (long)(t - lo) * TS;
+        const int t = min(cc * kC + ptok(), Tl - 1);
+        const long off = lane_off + (long)(t - ptok()) * TS;
         x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + off);
         if constexpr (W32)
             x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + off);
         else
             x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + off);
         x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) + off);
-        if constexpr (FUSED) {
-#pragma unroll
-            for (int i = 0; i < 3; ++i)  // same token, the other key blocks' channels
-                x.kx[i] = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.k) +
-                                                           off + 16 * (((blk + 1 + i) & 3) - blk));
-        } else {
+        if constexpr (!FUSED)
             x.kap = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + off);
-        }
         x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + off);
         x.v = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.v) + off);
     }
@@ -296,16 +269,7 @@ struct Chunked {
     // neither the state nor any other token's readout (its own is not stored).
     // Selects rather than a branch: a branch that rewrites the prefetch ring's
     // registers turns the compiler's wait counts for the ring conservative.
-    // The raw inputs of one lane (token lo of the chunk, four channels) widened
-    // to float, kp = kappa (with the fused prologue formed here from raw keys).
-    struct Unpacked {
-        float r[4], w[4], k[4], a[4], kp[4];
-        uint2 v;
-    };
-    __device__ Unpacked unpack(const Raw<W32> &x, bool valid, const ProParams &pro) const {
-        Unpacked u;
-        float *r = u.r, *w = u.w, *k = u.k, *a = u.a, *kp = u.kp;
-        r[0] = bf16_lo(x.r.x); r[1] = bf16_hi(x.r.x); r[2] = bf16_lo(x.r.y); r[3] = bf16_hi(x.r.y);
+    __device__ __forceinline__ void unpack_w(const Raw<W32> &x, bool valid, float (&w)[4]) const {
         if constexpr (W32) {
             w[0] = x.w.x; w[1] = x.w.y; w[2] = x.w.z; w[3] = x.w.w;
 #pragma unroll
@@ -315,29 +279,31 @@ struct Chunked {
             w[0] = bf16_lo(w01); w[1] = bf16_hi(w01);
             w[2] = bf16_lo(w23); w[3] = bf16_hi(w23);
         }
+    }
+
+    // The raw inputs of one lane (its token, four keys) widened to float, kp =
+    // kappa (with the fused prologue formed here from the raw keys).
+    struct Unpacked {
+        float r[4], k[4], a[4], kp[4];
+        uint2 v;
+    };
+    __device__ Unpacked unpack(const Raw<W32> &x, bool valid, const ProParams &pro) const {
+        Unpacked u;
+        float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
+        r[0] = bf16_lo(x.r.x); r[1] = bf16_hi(x.r.x); r[2] = bf16_lo(x.r.y); r[3] = bf16_hi(x.r.y);
         const unsigned k01 = valid ? x.k.x : 0u, k23 = valid ? x.k.y : 0u;
         k[0] = bf16_lo(k01); k[1] = bf16_hi(k01); k[2] = bf16_lo(k23); k[3] = bf16_hi(k23);
         a[0] = bf16_lo(x.a.x); a[1] = bf16_hi(x.a.x); a[2] = bf16_lo(x.a.y); a[3] = bf16_hi(x.a.y);
         if constexpr (FUSED) {
-            // kappa = normalise(k * k_k) over the token's 64 channels (this lane's 4 in
-            // each key block, the four lanes g of the DPP column); k <- k + k (a-1) k_a
+            // kappa = normalise(k * k_k) over the token's 64 keys (the DPP row);
+            // k <- k + k (a-1) k_a
             float kk[4], ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                kk[e] = k[e] * pro.kk[0][e];
+                kk[e] = k[e] * pro.kk[e];
                 ss += kk[e] * kk[e];
             }
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const float xo[4] = {bf16_lo(x.kx[i].x), bf16_hi(x.kx[i].x), bf16_lo(x.kx[i].y),
-                                     bf16_hi(x.kx[i].y)};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float t = xo[e] * pro.kk[i + 1][e];
-                    ss += t * t;
-                }
-            }
-            ss = sum_rows4(ss);
+            ss = sum_lanes16(ss);
             const float inv = 1.f / fmaxf(sqrtf(ss), 1e-12f);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -353,61 +319,92 @@ struct Chunked {
         return u;
     }
 
-    // Chunk operands for key block blk from the unpacked inputs, written to LDS
-    // buffer `o`.
-    __device__ void prep(const Unpacked &u, ChunkOps &o, const float (&rk)[4]) const {
-        const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
-        float w[4] = {u.w[0], u.w[1], u.w[2], u.w[3]};
-        f32x4 G, Kp, Rp, Km, Bm;
-        float bon = 0.f, dkr = 0.f, dbr = 0.f;
-        float be[4], kpg[4] = {kp[0], kp[1], kp[2], kp[3]};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) be[e] = a[e] * kp[e];
-        // G_t = prod_{s<=t} w_s over the chunk's tokens (lanes of the DPP row) and
-        // kappa_t G_{t-1} (G_{-1} = 1)
-        prefix_products(w, kpg);
+    // Products of w over the prep wave's four tokens (the DPP rows g) for the
+    // lane's four keys: lp inclusive, lx exclusive.  Row pairs by
+    // v_permlane16_swap (even rows receive row g+1, odd rows row g-1), then the
+    // pair (0, 1) total into rows 2, 3 by v_permlane32_swap (its first result
+    // holds, in lanes 32..63, lanes 0..31 of the second operand).  Row 3's lp is
+    // the wave's total, stored in `out` for the chunk's later prep waves.
+    __device__ void scan(const float (&w)[4], float (&lp)[4], float (&lx)[4], float4 *out) const {
+        const bool odd = g & 1, upper = g >= 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const float q = w[e];
+            const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[e]),
+                                                              __float_as_uint(w[e]), false, false);
+            const float partner = __uint_as_float(odd ? h16[0] : h16[1]);
+            const float pair = w[e] * partner;
+            const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
+                                                              __float_as_uint(pair), false, false);
+            const float below = upper ? __uint_as_float(h32[0]) : 1.f;
+            lp[e] = (odd ? pair : w[e]) * below;
+            lx[e] = (odd ? partner : 1.f) * below;
+        }
+        if (g == 3) *out = make_float4(lp[0], lp[1], lp[2], lp[3]);
+    }
+
+    // Chunk operands of the lane's token and keys, written to LDS buffer `o`.
+    // lp, lx: the scan of this chunk; carry: the per-wave totals of the chunk.
+    __device__ void prep(const Unpacked &u, ChunkOps &o, const float (&rk)[4],
+                         const float (&lp)[4], const float (&lx)[4],
+                         const float4 (&carry)[4][16]) const {
+        const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
+        // decay of the chunk's tokens before this wave's four
+        float c[4] = {1.f, 1.f, 1.f, 1.f};
+        for (int b = 0; b < blk; ++b) {
+            const float4 t = carry[b][lo];
+            c[0] *= t.x; c[1] *= t.y; c[2] *= t.z; c[3] *= t.w;
+        }
+        f32x4 G, Kp, Rp, Km, Bm;
+        float bon = 0.f, dkr = 0.f, dbr = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float q = c[e] * lp[e];               // G_t = prod_{s<=t} w_s
             G[e] = q;
             const float iG = __builtin_amdgcn_rcpf(q);  // 1 ulp; operands are rounded to bf16
-            Kp[e] = kpg[e];
+            const float be = a[e] * kp[e];
+            Kp[e] = kp[e] * (c[e] * lx[e]);             // kappa_t G_{t-1} (G_{-1} = 1)
             Rp[e] = r[e] * q;
             Km[e] = k[e] * iG;
-            Bm[e] = be[e] * iG;
+            Bm[e] = be * iG;
             if (EPI) bon += r[e] * k[e] * rk[e];
             dkr += r[e] * k[e];
-            dbr += r[e] * be[e];
+            dbr += r[e] * be;
         }
-        const int jb = blk;
-        st_a(o.kp[jb], lane, to_bf16(Kp));
-        st_a(o.rp[jb], lane, to_bf16(Rp));
+        // the lane's 4 keys sit in key block jb at columns c0 .. c0+3
+        const int t = ptok(), jb = lo >> 2, c0 = 4 * (lo & 3);
+        const int rowoff = t * kRow + c0;
+        *reinterpret_cast<bf16x4 *>(o.kp[jb] + rowoff) = to_bf16(Kp);
+        *reinterpret_cast<bf16x4 *>(o.rp[jb] + rowoff) = to_bf16(Rp);
         const bf16x4 kmb = to_bf16(Km), bmb = to_bf16(Bm);
-        st_a(o.km[jb], lane, kmb);
-        st_a(o.bm[jb], lane, bmb);
+        *reinterpret_cast<bf16x4 *>(o.km[jb] + rowoff) = kmb;
+        *reinterpret_cast<bf16x4 *>(o.bm[jb] + rowoff) = bmb;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {  // transposed: row = channel 4g+e, column = token lo
-            o.kmt[jb][(4 * g + e) * kRow + lo] = kmb[e];
-            o.bmt[jb][(4 * g + e) * kRow + lo] = bmb[e];
+        for (int e = 0; e < 4; ++e) {  // transposed: row = key c0+e, column = token t
+            o.kmt[jb][(c0 + e) * kRow + t] = kmb[e];
+            o.bmt[jb][(c0 + e) * kRow + t] = bmb[e];
         }
         if (EPI)  // V rows [t][i] for the bonus term of the readouts
-            *reinterpret_cast<uint2 *>(o.vr[jb] + lo * kRow + 4 * g) = u.v;
-        o.vt[jb][(4 * g + 0) * kRow + lo] = (short)(u.v.x & 0xffffu);
-        o.vt[jb][(4 * g + 1) * kRow + lo] = (short)(u.v.x >> 16);
-        o.vt[jb][(4 * g + 2) * kRow + lo] = (short)(u.v.y & 0xffffu);
-        o.vt[jb][(4 * g + 3) * kRow + lo] = (short)(u.v.y >> 16);
-        // the last token's lane holds the whole-chunk decay G_C of its 4 channels
-        if (lo == 15) *reinterpret_cast<float4 *>(&o.gc[16 * jb + 4 * g]) =
+            *reinterpret_cast<uint2 *>(o.vr[jb] + rowoff) = u.v;
+        o.vt[jb][(c0 + 0) * kRow + t] = (short)(u.v.x & 0xffffu);
+        o.vt[jb][(c0 + 1) * kRow + t] = (short)(u.v.x >> 16);
+        o.vt[jb][(c0 + 2) * kRow + t] = (short)(u.v.y & 0xffffu);
+        o.vt[jb][(c0 + 3) * kRow + t] = (short)(u.v.y >> 16);
+        // the last token's lanes hold the whole-chunk decay G_C
+        if (t == kC - 1) *reinterpret_cast<float4 *>(&o.gc[4 * lo]) =
             make_float4(G[0], G[1], G[2], G[3]);
         // fp32 diagonals of M_kr and M_br: at s = t the decay ratio is exactly 1, so
         // r_t.k_t and r_t.(a_t*kappa_t) need no bf16 factors; the two-factor bf16
         // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
-        // early readouts whose dot product nearly cancels
-        // the three sums over the four lanes g in one pass: DPP row g ends up
-        // holding sum number packed_col(g) (row 3 the unused fourth)
-        const float sums = sum_rows4_packed(dkr, dbr, EPI ? bon : 0.f, 0.f);
-        const int qn = packed_col(g);
-        if (qn < (EPI ? 3 : 2)) o.rsum[qn][jb][lo] = sums;
+        // early readouts whose dot product nearly cancels.  Sums over the token's
+        // 64 keys: the 16 lanes of the DPP row.
+        dkr = sum_lanes16(dkr);
+        dbr = sum_lanes16(dbr);
+        if (EPI) bon = sum_lanes16(bon);
+        if (lo == 0) {
+            o.rsum[0][t] = dkr;
+            o.rsum[1][t] = dbr;
+            if (EPI) o.rsum[2][t] = bon;
+        }
     }
 
     // One C x C matrix of a chunk per prep wave; wave 5 forms the triangular inverse.
@@ -448,9 +445,6 @@ struct Chunked {
             const f32x4 z = mfma(to_bf16(n8), to_bf16(gt), gt);    // D(X^T) = A form of X
             st_a(o.xinv, lane, to_bf16(-z));                       // stored negated
         } else {
-            if (EPI && blk == 0 && lane < 16)
-                o.bon_tot[lane] = o.rsum[2][0][lane] + o.rsum[2][1][lane] + o.rsum[2][2][lane] +
-                                  o.rsum[2][3][lane];
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kTile] = (blk == 3) ? o.bm : o.km;
             const short(*rhs)[kTile] = (blk == 0) ? o.kp : o.rp;
@@ -459,11 +453,7 @@ struct Chunked {
             m = mfma2(ld_a(lhs[2], lane), ld_a(lhs[3], lane), ld_a(rhs[2], lane),
                       ld_a(rhs[3], lane), m);
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
-            float diag = 0.f;
-            if (blk != 0) {
-                const float(*dd)[16] = o.rsum[blk == 2 ? 0 : 1];
-                diag = dd[0][lo] + dd[1][lo] + dd[2][lo] + dd[3][lo];
-            }
+            const float diag = (blk != 0) ? o.rsum[blk == 2 ? 0 : 1][lo] : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool keep = (blk == 0) ? (row + e < lo) : (row + e <= lo);
@@ -611,6 +601,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                                             reinterpret_cast<f32x4 *>(dst + srow + 16 * jb + 4 * g));
         };
         if (ckpt && nch > 0) store_state(ckpt);  // the state before chunk 0
+        __syncthreads();  // interval -1: decay totals of chunk 0
         __syncthreads();  // interval 0: chunk 0 prepared
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
@@ -671,7 +662,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 // the MFMAs that overwrite the accumulators
                 if (ckpt && c + 1 < nch) store_state(ckpt + (long)(c + 1) * kN * kN);
                 if (EPI && !SUMMARY) {
-                    pd.bon = o.bon_tot[lo];
+                    pd.bon = o.rsum[2][lo];
                     pd.v = *reinterpret_cast<const uint2 *>(o.vr[blk] + lo * kRow + 4 * g);
                     // mean and M2 of token lo's readouts over this value block: four
                     // in the lane, summed over the four DPP rows g
@@ -693,47 +684,58 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
+        // The prep waves bound each interval (the chain waves wait at the barrier),
+        // so they win the issue arbitration on their SIMD.
+        __builtin_amdgcn_s_setprio(2);
         ProParams pro{};
+        const int kch = h * kN + 4 * lo;  // the lane's four keys
         if (FUSED) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float4 q = *reinterpret_cast<const float4 *>(
-                    p.k_k + h * kN + 16 * ((blk + i) & 3) + 4 * g);
-                pro.kk[i][0] = q.x; pro.kk[i][1] = q.y; pro.kk[i][2] = q.z; pro.kk[i][3] = q.w;
-            }
-            const float4 q = *reinterpret_cast<const float4 *>(p.k_a + h * kN + 16 * blk + 4 * g);
-            pro.ka[0] = q.x; pro.ka[1] = q.y; pro.ka[2] = q.z; pro.ka[3] = q.w;
+            const float4 q = *reinterpret_cast<const float4 *>(p.k_k + kch);
+            pro.kk[0] = q.x; pro.kk[1] = q.y; pro.kk[2] = q.z; pro.kk[3] = q.w;
+            const float4 s = *reinterpret_cast<const float4 *>(p.k_a + kch);
+            pro.ka[0] = s.x; pro.ka[1] = s.y; pro.ka[2] = s.z; pro.ka[3] = s.w;
         }
         float rk[4] = {0.f, 0.f, 0.f, 0.f};
         if (EPI && !SUMMARY) {
-            const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + h * kN + 16 * blk + 4 * g);
+            const float4 q = *reinterpret_cast<const float4 *>(p.epi.r_k + kch);
             rk[0] = q.x; rk[1] = q.y; rk[2] = q.z; rk[3] = q.w;
         }
+        // (the parameters above are in registers before the ring's loads start,
+        // so no wait for them is left inside the loop)
+        __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         // Raw inputs of the next kPrefetch chunks stay in flight in a register ring.
         // Interval q (one barrier each) forms chunk q-1's matrices and prepares
         // chunk q from ring slot q % kPrefetch, which then receives chunk
-        // q + kPrefetch.  The intervals run in a loop without branches inside its
-        // body, unrolled over whole turns of the ring and entered with the ring
-        // in its steady state: every join or extra back edge there makes the
-        // compiler's wait counts for the ring conservative (it then waits for
-        // loads issued one interval earlier instead of kPrefetch - 1).  So the
-        // loop runs whole trips, S = steady_intervals(nch) >= nch intervals:
+        // q + kPrefetch; at its end, once slot q+1 has arrived, each wave scans
+        // the decay of chunk q+1 over its four tokens and leaves its total in LDS
+        // for the later waves (read after the barrier).  The intervals run in a
+        // loop without branches inside its body, unrolled over whole turns of the
+        // ring and entered with the ring in its steady state: every join or extra
+        // back edge there makes the compiler's wait counts for the ring
+        // conservative (it then waits for loads issued one interval earlier
+        // instead of kPrefetch - 1).  So the loop runs whole trips,
+        // S = steady_intervals(nch) >= nch intervals:
         //   - interval 0 forms the matrices of buffer 2, which nobody reads
         //     before prep fills it in interval 2 and matrices in interval 3;
         //   - intervals past nch - 1 prepare chunks made only of padding tokens
         //     (clamped loads).
         // Both are harmless because interval q writes only the buffers of
         // chunks q and q-1 while the chain waves read chunk q-2's.
-        // (the parameters above are in registers before the ring's loads start,
-        // so no wait for them is left inside the loop)
-        __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         Raw<W32> xs[kPrefetch];
 #pragma unroll
         for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
+        constexpr int kLoads = FUSED ? 5 : 6;  // loads per chunk (no kappa when fused)
         // the next interval consumes the oldest ring slot: let only the
         // (kPrefetch-1) younger chunks' loads stay in flight (stated explicitly,
         // since the compiler's count does not survive the loop's back edge)
-        __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
+        __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
+        float lp[4], lx[4];
+        {
+            float w[4];
+            K.unpack_w(xs[0], K.ptok() < K.Tl, w);
+            K.scan(w, lp, lx, &sm.carry[0][blk][lo]);
+        }
+        __syncthreads();  // interval -1: decay totals of chunk 0
         static_assert(kUnroll % kPrefetch == 0, "the loop advances whole ring turns");
         const int S = steady_intervals(nch);
         for (int q0 = 0; q0 < S; q0 += kUnroll) {
@@ -748,11 +750,14 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 // the operands are formed: its loads then overlap the prologue's
                 // arithmetic (measured faster there; without the prologue the
                 // extra live registers cost more than the overlap gains).
-                const auto u = K.unpack(x, q * kC + lo < K.Tl, pro);
+                const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
                 if constexpr (FUSED) K.load(q + kPrefetch, x);
-                K.prep(u, sm.ops[q % 3], rk);
+                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1]);
                 if constexpr (!FUSED) K.load(q + kPrefetch, x);
-                __builtin_amdgcn_s_waitcnt(wait_older_chunks(FUSED ? 8 : 6));
+                __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
+                float w[4];
+                K.unpack_w(xs[(d + 1) % kPrefetch], (q + 1) * kC + K.ptok() < K.Tl, w);
+                K.scan(w, lp, lx, &sm.carry[(q + 1) & 1][blk][lo]);
                 __syncthreads();
             }
         }
