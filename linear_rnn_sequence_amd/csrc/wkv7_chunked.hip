@@ -21,28 +21,31 @@
 // fp32 level because the scaled result is a sum of terms of ordinary size).
 // The kernel carries U' = -U (it stores -(I + M_bk)^-1) so no other operand
 // needs a sign flip.
-// Every product is a 16 x 16 x 16 MFMA (v_mfma_f32_16x16x16_bf16) with bf16
-// operands and fp32 accumulation; the state stays fp32 in the accumulators.
-// The unit lower-triangular inverse uses (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8)
-// for the nilpotent N = M_bk (N^16 = 0), also on MFMA.  The decay ratios stay
-// within w_min^-16 (1.6e4 for the pages' w > 0.545).  Requires 0 < w <= 1.
+// Every product is a 16 x 16 bf16 MFMA with fp32 accumulation (pairs of K = 16
+// products as one v_mfma_f32_16x16x32_bf16); the state stays fp32 in the
+// accumulators.  The unit lower-triangular inverse uses
+// (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8) for the nilpotent N = M_bk (N^16 = 0),
+// also on MFMA.  The decay ratios stay within w_min^-16 (1.6e4 for the pages'
+// w > 0.545).  Requires 0 < w <= 1.
 //
 // Work split: one workgroup of 8 waves per (batch, head), walking the chunks
 // in order as a three-stage pipeline with one barrier per chunk:
-//   waves 4..7 ("prep"): wave 4+b prepares key block j in [16b, 16b+16) of the
-//     operands of chunk c+2 (prefix products of w over the chunk by DPP row
-//     shifts, bf16 tiles into LDS) from raw inputs held 4 chunks deep in a
-//     register ring, and forms one C x C matrix of chunk c+1 (wave 5: the
-//     triangular inverse);
+//   waves 4..7 ("prep"): wave 4+b prepares tokens 4b .. 4b+3 of chunk c+2
+//     (one token per DPP row, its 64 keys over the row's 16 lanes, so loads
+//     read whole token rows) from raw inputs held 4 chunks deep in a register
+//     ring, writes the chunk's bf16 operand tiles to LDS, and forms one C x C
+//     matrix of chunk c+1 (wave 5: the triangular inverse).  The decay
+//     prefix over the chunk is a scan over each wave's four rows plus the
+//     earlier waves' totals, left in LDS one interval ahead;
 //   waves 0..3 ("chain"): wave b owns value block i in [16b, 16b+16) of the
 //     state: S^T is held as four 16x16 fp32 accumulator tiles per wave, in
 //     exactly the layout the next chunk's MFMAs consume, so the state never
 //     leaves registers; they run chunk c's MFMA chain and finish chunk c-1's
 //     readouts (GroupNorm statistics need all four value blocks).
-// A SIMD thus holds one chain wave and one prep wave; together they issue
-// ~430 VALU and ~27 MFMA instructions per chunk, which bounds the kernel (a
-// second resident workgroup per CU adds no throughput).  LDS holds the
-// operands of three chunks.
+// A SIMD thus holds one chain wave and one prep wave; LDS holds the operands
+// of three chunks (72 KB, so two workgroups fit on a CU).  Alone on a CU an
+// interval is bound by the inverse wave; with two workgroups, by instruction
+// issue on the SIMDs (the prep waves run at a raised wave priority).
 //
 // Wait counts: vector stores count with loads on this target, so a full wait
 // inside the chunk loop would also wait for the chunk's stores.  Loads made
@@ -63,7 +66,8 @@
 //     negative token stride; float32 readouts out; added readouts in);
 //   - s_ckpt: the training forward stores the state entering every chunk.
 //
-// MFMA 16x16x16 bf16 lane layouts (lane l, g = l / 16, e = 0..3):
+// MFMA 16x16x16 bf16 lane layouts (lane l, g = l / 16, e = 0..3; the
+// 16x16x32 form holds 8 consecutive k per lane in both A and B):
 //   A[m][k]: lane holds A[l%16][4g+e];  B[k][n]: lane holds B[4g+e][l%16];
 //   D[m][n]: lane holds D[4g+e][l%16].
 // So a D tile is directly a B operand, and the A form of X is the B form of X^T.
