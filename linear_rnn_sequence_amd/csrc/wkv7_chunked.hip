@@ -750,14 +750,12 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 // widen the slot, form chunk q's operands and refill the slot with
                 // chunk q + kPrefetch (clamped: always the same loads per
-                // interval).  With the fused prologue the refill goes out before
-                // the operands are formed: its loads then overlap the prologue's
-                // arithmetic (measured faster there; without the prologue the
-                // extra live registers cost more than the overlap gains).
+                // interval; refilling before the operands are formed keeps both
+                // live and, with the fused prologue, costs the register budget
+                // that lets two workgroups share a CU)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
-                if constexpr (FUSED) K.load(q + kPrefetch, x);
                 K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1]);
-                if constexpr (!FUSED) K.load(q + kPrefetch, x);
+                K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];
                 K.unpack_w(xs[(d + 1) % kPrefetch], (q + 1) * kC + K.ptok() < K.Tl, w);
