@@ -352,12 +352,13 @@ struct Chunked {
                          const float (&lp)[4], const float (&lx)[4],
                          const float4 (&carry)[4][16]) const {
         const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
-        // decay of the chunk's tokens before this wave's four
-        float c[4] = {1.f, 1.f, 1.f, 1.f};
-        for (int b = 0; b < blk; ++b) {
-            const float4 t = carry[b][lo];
-            c[0] *= t.x; c[1] *= t.y; c[2] *= t.z; c[3] *= t.w;
-        }
+        // decay of the chunk's tokens before this wave's four: the three earlier
+        // waves' totals read together (one LDS round trip), unused ones masked
+        const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
+        const float4 t0 = carry[0][lo], t1 = carry[1][lo], t2 = carry[2][lo];
+        const float4 w0 = blk > 0 ? t0 : one, w1 = blk > 1 ? t1 : one, w2 = blk > 2 ? t2 : one;
+        const float c[4] = {w0.x * w1.x * w2.x, w0.y * w1.y * w2.y, w0.z * w1.z * w2.z,
+                            w0.w * w1.w * w2.w};
         f32x4 G, Kp, Rp, Km, Bm;
         float bon = 0.f, dkr = 0.f, dbr = 0.f;
 #pragma unroll
