@@ -187,7 +187,10 @@ struct ChunkedParams {
 struct __align__(16) ChunkSmem {
     ChunkOps ops[3];
     float2 stats[2][16][4];  // per token, per value block: (mean, M2) of 16 readouts
-    float4 carry[2][4][16];  // per chunk parity and prep wave: w over its 4 tokens
+    // per chunk parity, reading prep wave r and slot b < 3: the product of w over
+    // prep wave b's four tokens if b < r, else 1 (set once), so a reader
+    // multiplies its three slots without selects
+    float4 carry[2][4][3][16];
 };
 
 __device__ __forceinline__ bf16x4 ld_a(const short *tile, int lane) {
@@ -328,8 +331,9 @@ struct Chunked {
     // v_permlane16_swap (even rows receive row g+1, odd rows row g-1), then the
     // pair (0, 1) total into rows 2, 3 by v_permlane32_swap (its first result
     // holds, in lanes 32..63, lanes 0..31 of the second operand).  Row 3's lp is
-    // the wave's total, stored in `out` for the chunk's later prep waves.
-    __device__ void scan(const float (&w)[4], float (&lp)[4], float (&lx)[4], float4 *out) const {
+    // the wave's total, stored in the slots of the chunk's later prep waves.
+    __device__ void scan(const float (&w)[4], float (&lp)[4], float (&lx)[4],
+                         float4 (&slots)[4][3][16]) const {
         const bool odd = g & 1, upper = g >= 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -343,20 +347,23 @@ struct Chunked {
             lp[e] = (odd ? pair : w[e]) * below;
             lx[e] = (odd ? partner : 1.f) * below;
         }
-        if (g == 3) *out = make_float4(lp[0], lp[1], lp[2], lp[3]);
+        if (g == 3) {
+            const float4 t = make_float4(lp[0], lp[1], lp[2], lp[3]);
+#pragma unroll
+            for (int r = 1; r < 4; ++r)
+                if (r > blk) slots[r][blk][lo] = t;
+        }
     }
 
     // Chunk operands of the lane's token and keys, written to LDS buffer `o`.
-    // lp, lx: the scan of this chunk; carry: the per-wave totals of the chunk.
+    // lp, lx: the scan of this chunk; carry: this wave's slots of the chunk.
     __device__ void prep(const Unpacked &u, ChunkOps &o, const float (&rk)[4],
                          const float (&lp)[4], const float (&lx)[4],
-                         const float4 (&carry)[4][16]) const {
+                         const float4 (&carry)[3][16]) const {
         const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
-        // decay of the chunk's tokens before this wave's four: the three earlier
-        // waves' totals read together (one LDS round trip), unused ones masked
-        const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
-        const float4 t0 = carry[0][lo], t1 = carry[1][lo], t2 = carry[2][lo];
-        const float4 w0 = blk > 0 ? t0 : one, w1 = blk > 1 ? t1 : one, w2 = blk > 2 ? t2 : one;
+        // decay of the chunk's tokens before this wave's four: the earlier waves'
+        // totals (slots of later waves hold 1), read in one LDS round trip
+        const float4 w0 = carry[0][lo], w1 = carry[1][lo], w2 = carry[2][lo];
         const float c[4] = {w0.x * w1.x * w2.x, w0.y * w1.y * w2.y, w0.z * w1.z * w2.z,
                             w0.w * w1.w * w2.w};
         f32x4 G, Kp, Rp, Km, Bm;
@@ -738,7 +745,14 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         {
             float w[4];
             K.unpack_w(xs[0], K.ptok() < K.Tl, w);
-            K.scan(w, lp, lx, &sm.carry[0][blk][lo]);
+            // this wave's slots that no earlier wave writes hold 1 for good
+            if (g == 0) {
+#pragma unroll
+                for (int b = 0; b < 3; ++b)
+                    if (b >= blk) sm.carry[0][blk][b][lo] = sm.carry[1][blk][b][lo] =
+                        make_float4(1.f, 1.f, 1.f, 1.f);
+            }
+            K.scan(w, lp, lx, sm.carry[0]);
         }
         __syncthreads();  // interval -1: decay totals of chunk 0
         static_assert(kUnroll % kPrefetch == 0, "the loop advances whole ring turns");
@@ -755,12 +769,12 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 // live and, with the fused prologue, costs the register budget
                 // that lets two workgroups share a CU)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
-                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1]);
+                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1][blk]);
                 K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];
                 K.unpack_w(xs[(d + 1) % kPrefetch], (q + 1) * kC + K.ptok() < K.Tl, w);
-                K.scan(w, lp, lx, &sm.carry[(q + 1) & 1][blk][lo]);
+                K.scan(w, lp, lx, sm.carry[(q + 1) & 1]);
                 __syncthreads();
             }
         }
