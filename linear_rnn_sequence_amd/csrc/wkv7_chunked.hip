@@ -107,6 +107,21 @@ constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
 constexpr int kThreadsSummary = 768;    // + 4 chain waves for the transition rows
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
+// A pair tile holds two 16x16 tiles (X | Y) so that a lane's K = 32 operand
+// (X's four k beside Y's four) is 16 contiguous bytes: row r, column c of half
+// h at r * kPRow + (c / 4) * 8 + 4h + c % 4 (80-byte rows: the 16-byte reads
+// of eight lanes of one column group hit disjoint banks).
+constexpr int kPRow = 40;
+constexpr int kPTile = 16 * kPRow;
+// Distances between the tiles of one array (16 rows plus padding) chosen so
+// that the prep waves' stores (a lane writes one token of four keys; the
+// transposed tiles take them as 2-byte stores down a column) and the chain
+// waves' reads spread over the LDS banks: with the bare tile sizes the key
+// blocks of one store instruction all met in the same banks (up to 8-way).
+constexpr int kPTileRows = 672;  // Kp, Rp, Km, Bm pair tiles
+constexpr int kPTileCols = 648;  // (Km^T | Bm^T) pair tiles
+constexpr int kTileVt = 324;     // V^T tiles
+constexpr int kTileVr = 336;     // V row tiles
 
 typedef short bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -120,14 +135,12 @@ typedef short bf16x8s __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // Two K = 16 products summed in one v_mfma_f32_16x16x32_bf16:
-//   c + A0 B0 + A1 B1   (A0, A1 in K = 16 A form; B0, B1 in K = 16 B form).
-// Each lane holds 8 consecutive k of the K = 32 operands in both A and B, so
-// placing (A0, A1) and (B0, B1) side by side in the lanes pairs every k of
-// A0 with the same k of B0 and likewise for A1, B1: the contraction over the
-// 32 k is the sum of the two 16-k contractions.
-__device__ __forceinline__ f32x4 mfma2(bf16x4 a0, bf16x4 a1, bf16x4 b0, bf16x4 b1, f32x4 c) {
-    const bf16x8s a = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
-    const bf16x8s b = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+//   c + A0 B0 + A1 B1   (A0, A1 in K = 16 A form; B0, B1 in K = 16 B form),
+// with a = (A0 | A1) and b = (B0 | B1) side by side in the lanes.  Each lane
+// holds 8 consecutive k of the K = 32 operands in both A and B, so every k of
+// A0 pairs with the same k of B0 and likewise for A1, B1: the contraction over
+// the 32 k is the sum of the two 16-k contractions.
+__device__ __forceinline__ f32x4 mfma2(bf16x8s a, bf16x8s b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
@@ -155,18 +168,17 @@ __device__ __forceinline__ float quad_bcast(float x) {
 }
 
 struct __align__(16) ChunkOps {
-    short kp[4][kTile];    // Kp  [jb][t][j]   (A form rows t; also B form of Kp^T)
-    short rp[4][kTile];    // Rp  [jb][t][j]
-    short km[4][kTile];    // Km  [jb][s][j]
-    short bm[4][kTile];    // Bm  [jb][s][j]
-    short kmt[4][kTile];   // Km^T  [jb][j][s]
-    short bmt[4][kTile];   // Bm^T  [jb][j][s]
-    short mkk[kTile];      // M_kk  [t][s]
-    short mkr[kTile];      // M_kr  [t][s]
-    short mbr[kTile];      // M_br  [t][s]
+    // pair tiles over key blocks (2p | 2p+1), rows t (or s), columns j
+    short kp[2][kPTileRows];  // Kp  (A form rows t; also B form of Kp^T)
+    short rp[2][kPTileRows];  // Rp
+    short km[2][kPTileRows];  // Km
+    short bm[2][kPTileRows];  // Bm
+    short kbt[4][kPTileCols]; // (Km^T | Bm^T) of key block jb: rows j, columns s
+    short mkz[kPTile];     // (M_kk | 0)  [t][s]; the zero half is set once
+    short mrb[kPTile];     // (M_kr | M_br)  [t][s]
     short xinv[kTile];     // -(I + M_bk)^-1 [t][s]
-    short vt[4][kTile];    // V^T [value block][i][t]  (B form of V)
-    short vr[4][kTile];    // V   [value block][t][i]  (epilogue only)
+    short vt[4][kTileVt];  // V^T [value block][i][t]  (B form of V)
+    short vr[4][kTileVr];  // V   [value block][t][i]  (epilogue only)
     float gc[64];          // G_C per key j
     // per token sums over the 64 keys, fp32: [0] r_t.k_t, [1] r_t.(a_t*kappa_t),
     // [2] the bonus sum_j r k r_k
@@ -193,6 +205,14 @@ struct __align__(16) ChunkSmem {
     float4 carry[2][4][3][16];
 };
 
+// lane's K = 32 operand of a pair tile (A form of X | Y side by side)
+__device__ __forceinline__ bf16x8s ld_pair(const short *ptile, int lane) {
+    return *reinterpret_cast<const bf16x8s *>(ptile + (lane & 15) * kPRow + 8 * (lane >> 4));
+}
+// lane's A-form values of half h of a pair tile
+__device__ __forceinline__ void st_pair(short *ptile, int h, int lane, bf16x4 x) {
+    *reinterpret_cast<bf16x4 *>(ptile + (lane & 15) * kPRow + 8 * (lane >> 4) + 4 * h) = x;
+}
 __device__ __forceinline__ bf16x4 ld_a(const short *tile, int lane) {
     return *reinterpret_cast<const bf16x4 *>(tile + (lane & 15) * kRow + 4 * (lane >> 4));
 }
@@ -382,18 +402,21 @@ struct Chunked {
             dkr += r[e] * k[e];
             dbr += r[e] * be;
         }
-        // the lane's 4 keys sit in key block jb at columns c0 .. c0+3
+        // the lane's 4 keys sit in key block jb at columns c0 .. c0+3: row t of
+        // half jb % 2 of pair tile jb / 2
         const int t = ptok(), jb = lo >> 2, c0 = 4 * (lo & 3);
         const int rowoff = t * kRow + c0;
-        *reinterpret_cast<bf16x4 *>(o.kp[jb] + rowoff) = to_bf16(Kp);
-        *reinterpret_cast<bf16x4 *>(o.rp[jb] + rowoff) = to_bf16(Rp);
+        const int poff = t * kPRow + 8 * (lo & 3) + 4 * (jb & 1);
+        *reinterpret_cast<bf16x4 *>(o.kp[jb >> 1] + poff) = to_bf16(Kp);
+        *reinterpret_cast<bf16x4 *>(o.rp[jb >> 1] + poff) = to_bf16(Rp);
         const bf16x4 kmb = to_bf16(Km), bmb = to_bf16(Bm);
-        *reinterpret_cast<bf16x4 *>(o.km[jb] + rowoff) = kmb;
-        *reinterpret_cast<bf16x4 *>(o.bm[jb] + rowoff) = bmb;
+        *reinterpret_cast<bf16x4 *>(o.km[jb >> 1] + poff) = kmb;
+        *reinterpret_cast<bf16x4 *>(o.bm[jb >> 1] + poff) = bmb;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {  // transposed: row = key c0+e, column = token t
-            o.kmt[jb][(c0 + e) * kRow + t] = kmb[e];
-            o.bmt[jb][(c0 + e) * kRow + t] = bmb[e];
+            const int toff = (c0 + e) * kPRow + 8 * (t >> 2) + (t & 3);
+            o.kbt[jb][toff] = kmb[e];
+            o.kbt[jb][toff + 4] = bmb[e];
         }
         if (EPI)  // V rows [t][i] for the bonus term of the readouts
             *reinterpret_cast<uint2 *>(o.vr[jb] + rowoff) = u.v;
@@ -426,12 +449,10 @@ struct Chunked {
             // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
             // is the B form of M and the A form of M^T.
             // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
-            const bf16x4 kp0 = ld_a(o.kp[0], lane), kp1 = ld_a(o.kp[1], lane);
-            const bf16x4 kp2 = ld_a(o.kp[2], lane), kp3 = ld_a(o.kp[3], lane);
-            const bf16x4 bm0 = ld_a(o.bm[0], lane), bm1 = ld_a(o.bm[1], lane);
-            const bf16x4 bm2 = ld_a(o.bm[2], lane), bm3 = ld_a(o.bm[3], lane);
-            f32x4 nb = mfma2(kp2, kp3, bm2, bm3, mfma2(kp0, kp1, bm0, bm1, zero4()));
-            f32x4 na = mfma2(bm2, bm3, kp2, kp3, mfma2(bm0, bm1, kp0, kp1, zero4()));
+            const bf16x8s kp01 = ld_pair(o.kp[0], lane), kp23 = ld_pair(o.kp[1], lane);
+            const bf16x8s bm01 = ld_pair(o.bm[0], lane), bm23 = ld_pair(o.bm[1], lane);
+            f32x4 nb = mfma2(kp23, bm23, mfma2(kp01, bm01, zero4()));
+            f32x4 na = mfma2(bm23, kp23, mfma2(bm01, kp01, zero4()));
             f32x4 imnt;  // D(I - N^T)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -458,12 +479,10 @@ struct Chunked {
             st_a(o.xinv, lane, to_bf16(-z));                       // stored negated
         } else {
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
-            const short(*lhs)[kTile] = (blk == 3) ? o.bm : o.km;
-            const short(*rhs)[kTile] = (blk == 0) ? o.kp : o.rp;
-            f32x4 m = mfma2(ld_a(lhs[0], lane), ld_a(lhs[1], lane), ld_a(rhs[0], lane),
-                            ld_a(rhs[1], lane), zero4());
-            m = mfma2(ld_a(lhs[2], lane), ld_a(lhs[3], lane), ld_a(rhs[2], lane),
-                      ld_a(rhs[3], lane), m);
+            const short(*lhs)[kPTileRows] = (blk == 3) ? o.bm : o.km;
+            const short(*rhs)[kPTileRows] = (blk == 0) ? o.kp : o.rp;
+            f32x4 m = mfma2(ld_pair(lhs[0], lane), ld_pair(rhs[0], lane), zero4());
+            m = mfma2(ld_pair(lhs[1], lane), ld_pair(rhs[1], lane), m);
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
             const float diag = (blk != 0) ? o.rsum[blk == 2 ? 0 : 1][lo] : 0.f;
 #pragma unroll
@@ -472,8 +491,7 @@ struct Chunked {
                 const float val = (blk != 0 && row + e == lo) ? diag : m[e];
                 m[e] = keep ? val : 0.f;
             }
-            short *dst = (blk == 0) ? o.mkk : (blk == 2 ? o.mkr : o.mbr);
-            st_a(dst, lane, to_bf16(m));
+            st_pair(blk == 0 ? o.mkz : o.mrb, blk == 3 ? 1 : 0, lane, to_bf16(m));
         }
     }
 };
@@ -591,6 +609,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
             lnb[0] = q.x; lnb[1] = q.y; lnb[2] = q.z; lnb[3] = q.w;
         }
         Pending pd;
+        bf16x8s VU = {0, 0, 0, 0, 0, 0, 0, 0};  // (V | -U) of the chunk, as B operand
         // element offset of (token lo of the chunk, value channel 16blk + 4g)
         long ylane = K.tok0 + (long)lo * K.TS + 16 * blk + 4 * g;
         // added readouts of a chunk, loaded at the start of its iteration and used
@@ -635,27 +654,31 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                         gsrc + K.tok0 + (long)min(c * kC + lo, K.Tl - 1) * K.TS + 16 * blk + 4 * g);
                 }
                 const ChunkOps &o = sm.ops[c % 3];
-                const bf16x4 Vb = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
-                bf16x4 Zb[4];
-#pragma unroll
-                for (int jb = 0; jb < 4; ++jb) Zb[jb] = to_bf16(Z[jb]);
-                // rhs = M_kk V + Kp S0^T: five 16-k products in three K = 32 MFMAs (the
-                // last one half empty), so the accumulation chain stays within one
-                // MFMA opcode
-                f32x4 rhs = mfma2(ld_a(o.mkk, lane), ld_a(o.kp[0], lane), Vb, Zb[0], zero4());
-                rhs = mfma2(ld_a(o.kp[1], lane), ld_a(o.kp[2], lane), Zb[1], Zb[2], rhs);
-                rhs = mfma2(ld_a(o.kp[3], lane), bf16x4{0, 0, 0, 0}, Zb[3], bf16x4{0, 0, 0, 0}, rhs);
+                // B operands as 8-wide pairs: (V | -U) and the state pairs; one K =
+                // 32 MFMA per two 16-k products, accumulation chains within that
+                // one opcode
+                VU.lo = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
+                bf16x8s Z01, Z23;
+                Z01.lo = to_bf16(Z[0]);
+                Z01.hi = to_bf16(Z[1]);
+                Z23.lo = to_bf16(Z[2]);
+                Z23.hi = to_bf16(Z[3]);
+                // rhs = M_kk V + Kp S0^T; (M_kk | 0) meets (V | the previous chunk's
+                // -U), whose product with the zero half vanishes
+                f32x4 rhs = mfma2(ld_pair(o.mkz, lane), VU, zero4());
+                rhs = mfma2(ld_pair(o.kp[0], lane), Z01, rhs);
+                rhs = mfma2(ld_pair(o.kp[1], lane), Z23, rhs);
                 // readouts as Y^T = S0 Rp^T + V^T M_kr^T - U^T M_br^T (the operands of
                 // Y with their roles swapped): lane holds Y^T[i = 4g+e][t = lo]; the
                 // terms without U first, so only one product waits for U
-                f32x4 Y = mfma2(Zb[0], Zb[1], ld_a(o.rp[0], lane), ld_a(o.rp[1], lane), zero4());
-                Y = mfma2(Zb[2], Zb[3], ld_a(o.rp[2], lane), ld_a(o.rp[3], lane), Y);
+                f32x4 Y = mfma2(Z01, ld_pair(o.rp[0], lane), zero4());
+                Y = mfma2(Z23, ld_pair(o.rp[1], lane), Y);
                 const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
-                const bf16x4 Ub = to_bf16(U);
-                Y = mfma2(Vb, Ub, ld_a(o.mkr, lane), ld_a(o.mbr, lane), Y);
+                VU.hi = to_bf16(U);
+                Y = mfma2(VU, ld_pair(o.mrb, lane), Y);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
-                    Z[jb] = mfma2(ld_a(o.kmt[jb], lane), ld_a(o.bmt[jb], lane), Vb, Ub, Z[jb]);
+                    Z[jb] = mfma2(ld_pair(o.kbt[jb], lane), VU, Z[jb]);
                     const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
                     Z[jb][0] *= gc.x;
                     Z[jb][1] *= gc.y;
@@ -696,6 +719,11 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
+        // the zero half of (M_kk | 0) in every buffer, once (read after the
+        // barriers that precede the first chain step)
+        for (int i = (int)threadIdx.x - 256; i < 3 * 16 * 4; i += 256)
+            *reinterpret_cast<uint2 *>(sm.ops[i >> 6].mkz + ((i >> 2) & 15) * kPRow +
+                                       8 * (i & 3) + 4) = make_uint2(0u, 0u);
         // The prep waves bound each interval (the chain waves wait at the barrier),
         // so they win the issue arbitration on their SIMD.
         __builtin_amdgcn_s_setprio(2);
