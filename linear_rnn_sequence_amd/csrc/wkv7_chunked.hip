@@ -357,15 +357,20 @@ struct Chunked {
         const bool odd = g & 1, upper = g >= 2;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
+            // the two results hold the lane's own value and its partner's in an
+            // order that depends on the row, so the pair product uses both and
+            // the own value needs no separate copy
             const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[e]),
                                                               __float_as_uint(w[e]), false, false);
-            const float partner = __uint_as_float(odd ? h16[0] : h16[1]);
-            const float pair = w[e] * partner;
+            const float h0 = __uint_as_float(h16[0]), h1 = __uint_as_float(h16[1]);
+            const float pair = h0 * h1;
+            const float in1 = odd ? pair : h0;   // even rows: h0 is the own value
+            const float ex1 = odd ? h0 : 1.f;    // odd rows: h0 is the row below
             const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
                                                               __float_as_uint(pair), false, false);
             const float below = upper ? __uint_as_float(h32[0]) : 1.f;
-            lp[e] = (odd ? pair : w[e]) * below;
-            lx[e] = (odd ? partner : 1.f) * below;
+            lp[e] = in1 * below;
+            lx[e] = ex1 * below;
         }
         if (g == 3) {
             const float4 t = make_float4(lp[0], lp[1], lp[2], lp[3]);
