@@ -43,7 +43,9 @@
 //     leaves registers; they run chunk c's MFMA chain and finish chunk c-1's
 //     readouts (GroupNorm statistics need all four value blocks).
 // A SIMD thus holds one chain wave and one prep wave; LDS holds the operands
-// of three chunks (72 KB, so two workgroups fit on a CU).  Alone on a CU an
+// of three chunks (81,760 bytes, so two workgroups fit on a CU), each MFMA
+// operand pair stored side by side per row so that a lane reads both halves
+// of a 16x16x32 operand with one 16-byte LDS read.  Alone on a CU an
 // interval is bound by the inverse wave; with two workgroups, by instruction
 // issue on the SIMDs (the prep waves run at a raised wave priority).
 //
