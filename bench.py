@@ -121,6 +121,50 @@ def read_profile_value(profile_name, key, src_hash):
         return None
 
 
+def copy_ceiling(torch, wkv, stream, launch_bytes):
+    """Measured HBM ceiling for traffic that reads and writes each byte once: the
+    library's streaming copy (rwkv7_stream_copy) over one 4 GiB buffer, and in
+    launches that each copy `launch_bytes` (cycling through 4 GiB so that no
+    launch finds its data in the caches).  HIP events on `stream`; GB/s count the
+    bytes read plus the bytes written."""
+    total = 4 << 30
+    n_pieces = max(1, total // launch_bytes)
+    src = torch.empty(total // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def timed(fn, reps):
+        ts = []
+        for _ in range(reps):
+            a, b = ev(), ev()
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def whole():
+        wkv.stream_copy(src, dst, stream=stream)
+
+    n_el = launch_bytes // 4
+
+    def pieces():
+        for i in range(n_pieces):
+            wkv.stream_copy(src[i * n_el:(i + 1) * n_el], dst[i * n_el:(i + 1) * n_el],
+                            stream=stream)
+
+    timed(whole, 3)
+    whole_ms = timed(whole, 10)
+    timed(pieces, 1)
+    piece_ms = timed(pieces, 5) / n_pieces
+    del src, dst
+    return {"kernel": "rwkv7_stream_copy (non-temporal, 1 KiB per wave access)",
+            "GBps_4GiB_one_launch": 2 * total / (whole_ms / 1e3) / 1e9,
+            "GBps_at_launch_size": 2 * launch_bytes / (piece_ms / 1e3) / 1e9,
+            "launch_bytes_copied": launch_bytes}
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -507,6 +551,7 @@ def main():
         },
     }
 
+    copy_cc = None
     if do_decode:
         run_ms = np.array([a.elapsed_time(b) for a, b in launch_ms])
         avg_ms = float(run_ms.sum() / (len(run_ms) * n_launch))  # per launch, gaps included
@@ -525,6 +570,11 @@ def main():
             "timing": "HIP events around each replay of the 2048-launch decode graph / 2048",
         }
         out["decode_ms_per_step"] = float(run_ms.mean())
+        # the same achieved rate against a copy that moves each launch's state bytes
+        cc = copy_ceiling(torch, wkv, stream, DB * DH * DN * DN * 4)
+        copy_cc = cc
+        out["roofline"]["copy_ceiling"] = cc
+        out["roofline"]["frac_of_copy"] = achieved / cc["GBps_at_launch_size"]
     if do_prefill:
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         # six inputs + y, the final state, and the epilogue parameters when fused
@@ -545,6 +595,11 @@ def main():
                          "frac": ach / HBM_PEAK_GBS, "traffic": traffic,
                          "bytes_per_launch": p_bytes},
         }
+        if copy_cc is None:
+            copy_cc = copy_ceiling(torch, wkv, stream, 256 << 20)
+        out["prefill"]["roofline"]["frac_of_copy"] = ach / copy_cc["GBps_4GiB_one_launch"]
+        if not do_decode:
+            out["prefill"]["roofline"]["copy_ceiling"] = copy_cc
         if chunked and not long_shape:
             # executed MFMA work per launch is fixed by the kernel (counted once with
             # SQ_INSTS_VALU_MFMA_MOPS_BF16); divided by the live duration it gives the

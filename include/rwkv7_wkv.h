@@ -267,6 +267,20 @@ rwkv7_status rwkv7_wkv_decode_fused(const void *r, const void *w, const void *k,
                                     void *y, int B, int H, int N, rwkv7_dtype dt,
                                     const rwkv7_epilogue *epi, void *stream);
 
+/*
+ * Measurement helper, not a step of the method: copies `bytes` bytes from src
+ * to dst (device pointers, caller-owned) with whole 1 KiB wave accesses and
+ * non-temporal loads and stores, every byte read and written once.  Its rate
+ * is the HBM ceiling for a stream that reads and writes each byte once, which
+ * is the traffic of the decode step.
+ * bytes == 0 launches nothing.  Errors: RWKV7_ERR_NULL (a NULL pointer),
+ * RWKV7_ERR_ALIGN (a pointer not 16-byte aligned), RWKV7_ERR_SHAPE (bytes not
+ * a multiple of 16, or more than 2^31 workgroups of 8 KiB), RWKV7_ERR_ALIAS
+ * (the ranges overlap), RWKV7_ERR_HIP (the launch failed).  Enqueued on
+ * `stream` (NULL = default stream); returns before the copy completes.
+ */
+rwkv7_status rwkv7_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
+
 /* Static description of a status code (never NULL). */
 const char *rwkv7_status_str(rwkv7_status s);
 

@@ -9,19 +9,20 @@
 // summary, §8 Speed and Memory.  The state read and write (32 KiB per head)
 // is all but the whole traffic, so the kernel is laid out for HBM streaming.
 //
-// Head size 64: two waves per head (each owns 32 value rows, 8 per lane), one
-// wave per workgroup; with the fused epilogue the head's two waves share a
-// 128-thread workgroup so the GroupNorm statistics can meet in LDS.  (Measured
-// against 1, 2, 4, 8 and 16 waves per workgroup, whole heads per wave, four
-// waves per head and persistent waves: this layout streamed fastest, ~76% of
-// 8 TB/s.)  Head size 128 uses the same lane layout with 32 lanes per row:
-// eight waves per head (see DecodeShape).
+// Head size 64: one 256-thread workgroup per head, four waves of 16 value rows
+// each, 4 rows per lane; the GroupNorm statistics of the fused epilogue meet in
+// LDS.  (Measured against 1, 2, 4, 8 and 16 value rows per lane, one wave per
+// workgroup, one, two and four heads per workgroup, and persistent waves: this
+// layout streamed fastest, ~81% of 8 TB/s, ahead of the best plain copy kernel
+// found at the same launch size.  Workgroups of a single wave were held back
+// by the rate at which workgroups are dispatched.)  Head size 128 uses 32 lanes
+// per row and 8 rows per lane: eight waves per head (see DecodeShape).
 // Lane (c, g) = (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value
-// rows r0 + 8g .. r0 + 8g + 7: every state load instruction reads four complete
-// 256-byte rows (16 lanes x 16 bytes each), so each wave moves its 8 KiB in
-// eight fully coalesced dwordx4 loads issued back to back.  Row sums (S kappa
-// and S (w*r)) are 16-lane DPP reductions.  Lanes c < 8 finally hold y of rows
-// r0 + 8g + c, so each wave's 32 readouts leave as one 64-byte (bf16) store.
+// rows r0 + 4g .. r0 + 4g + 3: every state load instruction reads four complete
+// 256-byte rows (16 lanes x 16 bytes each), so each wave moves its 4 KiB in
+// four fully coalesced dwordx4 loads issued back to back.  Row sums (S kappa
+// and S (w*r)) are 16-lane DPP reductions.  Lanes c < 4 finally hold y of rows
+// r0 + 4g + c, so each wave's 16 readouts leave as one 32-byte (bf16) store.
 // State loads and stores are non-temporal: each state is touched once per call
 // and the next layer's states should not be evicted for it.
 #include "wkv7_device.h"
@@ -29,8 +30,6 @@
 
 namespace wkv7 {
 namespace {
-
-constexpr int kRows = 8;  // value rows per lane
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -47,19 +46,20 @@ __device__ __forceinline__ void st_state(float *p, f32x4 x) {
         *reinterpret_cast<f32x4 *>(p) = x;
 }
 
-// 8 consecutive elements (value rows r .. r+7), widened to float.
-__device__ __forceinline__ void load8(const uint16_t *p, float *out) {
-    const uint4 a = *reinterpret_cast<const uint4 *>(p);
-    const uint32_t u[4] = {a.x, a.y, a.z, a.w};
+// R consecutive elements (value rows r .. r+R-1, R = 4 or 8), widened to float.
+template <int R>
+__device__ __forceinline__ void load_rows(const uint16_t *p, float *out) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        out[2 * e] = bf16_lo(u[e]);
-        out[2 * e + 1] = bf16_hi(u[e]);
+    for (int q = 0; q < R / 4; ++q) {
+        const uint2 a = *reinterpret_cast<const uint2 *>(p + 4 * q);
+        out[4 * q] = bf16_lo(a.x); out[4 * q + 1] = bf16_hi(a.x);
+        out[4 * q + 2] = bf16_lo(a.y); out[4 * q + 3] = bf16_hi(a.y);
     }
 }
-__device__ __forceinline__ void load8(const float *p, float *out) {
+template <int R>
+__device__ __forceinline__ void load_rows(const float *p, float *out) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < R / 4; ++q) {
         const float4 x = *reinterpret_cast<const float4 *>(p + 4 * q);
         out[4 * q] = x.x; out[4 * q + 1] = x.y; out[4 * q + 2] = x.z; out[4 * q + 3] = x.w;
     }
@@ -69,10 +69,14 @@ __device__ __forceinline__ void load8(const float *p, float *out) {
 // each, 16 bytes), so a wave holds 64/(N/4) row groups of kRows rows.
 template <int N>
 struct DecodeShape {
+    static constexpr int kRows = N == 64 ? 4 : 8;               // value rows per lane
     static constexpr int kLanesPerRow = N / 4;                  // 16 (N=64) or 32 (N=128)
     static constexpr int kGroups = 64 / kLanesPerRow;           // 4 or 2
-    static constexpr int kRowsPerWave = kGroups * kRows;        // 32 or 16
-    static constexpr int kWavesPerHead = N / kRowsPerWave;      // 2 or 8
+    static constexpr int kRowsPerWave = kGroups * kRows;        // 16 at either size
+    static constexpr int kWavesPerHead = N / kRowsPerWave;      // 4 or 8
+    // one workgroup per head even without the epilogue (N = 64); at N = 128 a
+    // call without the epilogue launches one single-wave workgroup per wave
+    static constexpr bool kHeadPerGroup = N == 64;
 };
 
 // Sum over the lanes of one state row (16 or 32 lanes).
@@ -84,19 +88,22 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 template <class IO, bool EPI, bool NT, bool W32, int N, bool FUSED = false>
-__global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void decode_kernel(
-    DecodeArgs p) {
+__global__ __launch_bounds__((EPI || DecodeShape<N>::kHeadPerGroup)
+                                 ? 64 * DecodeShape<N>::kWavesPerHead
+                                 : 64) void decode_kernel(DecodeArgs p) {
     using E = typename IO::elem;
     using Sh = DecodeShape<N>;
     constexpr int kW = Sh::kWavesPerHead;
+    constexpr int kRows = Sh::kRows;
+    constexpr bool kWhole = EPI || Sh::kHeadPerGroup;  // the workgroup holds the whole head
     __shared__ float2 xch[kW];  // epilogue: (mean, M2) of each wave's rows
     const int lane = threadIdx.x & 63;
-    const long head = EPI ? (long)blockIdx.x : (long)(blockIdx.x / kW);
-    const int part = EPI ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x % kW);
+    const long head = kWhole ? (long)blockIdx.x : (long)(blockIdx.x / kW);
+    const int part = kWhole ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x % kW);
     if (head >= (long)p.B * p.H) return;  // whole workgroup leaves together
     const int h = (int)(head % p.H);
     const int c = lane % Sh::kLanesPerRow, g = lane / Sh::kLanesPerRow;
-    const int r0 = Sh::kRowsPerWave * part + kRows * g;  // this lane's value rows r0 .. r0+7
+    const int r0 = Sh::kRowsPerWave * part + kRows * g;  // this lane's value rows r0 .. +kRows-1
 
     float *st = p.state + head * (N * N) + r0 * N + 4 * c;
     f32x4 S[kRows];
@@ -126,7 +133,7 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
     }
     const float4 r = IO::load4(pr + 4 * c);
     float v[kRows];
-    load8(static_cast<const E *>(p.v) + vo + r0, v);
+    load_rows<kRows>(static_cast<const E *>(p.v) + vo + r0, v);
 
     const float4 bb = make_float4(a.x * kap.x, a.y * kap.y, a.z * kap.z, a.w * kap.w);
     const float4 wr = make_float4(w.x * r.x, w.y * r.y, w.z * r.z, w.w * r.w);
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
         st_state<NT>(st + m * N, s);
     }
 
-    // lane c < 8 keeps row r0 + c
+    // lane c < kRows keeps row r0 + c
     const int sel = c & (kRows - 1);
     float yo = y[0], vo1 = v[0];
 #pragma unroll
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
         float s1 = 0.f;
 #pragma unroll
         for (int m = 0; m < kRows; ++m) s1 += y[m];
-        // sum over the wave's row groups (every lane of a group holds its 8 rows' sums)
+        // sum over the wave's row groups (every lane of a group holds its rows' sums)
         s1 = (N == 64) ? sum_rows4(s1) : swap32_add(s1, s1);
         const float mu_w = s1 * (1.f / Sh::kRowsPerWave);
         float s2 = 0.f;
@@ -206,7 +213,7 @@ __global__ __launch_bounds__(EPI ? 64 * DecodeShape<N>::kWavesPerHead : 64) void
     }
     if (FUSED && p.g) {  // output gate
         float gv[kRows];
-        load8(static_cast<const E *>(p.g) + vo + r0, gv);
+        load_rows<kRows>(static_cast<const E *>(p.g) + vo + r0, gv);
         float gsel = gv[0];
 #pragma unroll
         for (int m = 1; m < kRows; ++m) gsel = (sel == m) ? gv[m] : gsel;
@@ -219,10 +226,13 @@ template <int N, class IO, bool W32, bool FUSED>
 hipError_t launch_decode_n(const DecodeArgs &p, hipStream_t stream) {
     constexpr int kW = DecodeShape<N>::kWavesPerHead;
     const long heads = (long)p.B * p.H;
-    // without the epilogue: one 64-thread workgroup per wave of a head; with it:
-    // one workgroup per head holding all its waves
+    // one workgroup per head holding all its waves (with the epilogue, and at
+    // N = 64 always); else one 64-thread workgroup per wave of a head
     if (p.epilogue)
         hipLaunchKernelGGL((decode_kernel<IO, true, true, W32, N, FUSED>), dim3((unsigned)heads),
+                           dim3(64 * kW), 0, stream, p);
+    else if (DecodeShape<N>::kHeadPerGroup)
+        hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N, FUSED>), dim3((unsigned)heads),
                            dim3(64 * kW), 0, stream, p);
     else
         hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N, FUSED>),

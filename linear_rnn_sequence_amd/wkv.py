@@ -75,6 +75,8 @@ def lib():
         L.rwkv7_wkv_forward_train.restype = ci
         L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [ci] * 5 + [vp]
         L.rwkv7_wkv_backward.restype = ci
+        L.rwkv7_stream_copy.argtypes = [vp, vp, sz, vp]
+        L.rwkv7_stream_copy.restype = ci
         L.rwkv7_status_str.argtypes = [ci]
         L.rwkv7_status_str.restype = ctypes.c_char_p
         L.rwkv7_abi_version.argtypes = []
@@ -370,6 +372,23 @@ def prepare_decode(r, w, k, v, kappa, a, state, *, y, epilogue=None, stream=None
 
     launch.keep = (keep, r, w, k, v, kappa, a, state, y)
     return launch
+
+
+def stream_copy(src, dst, *, stream=None):
+    """rwkv7_stream_copy: copy the bytes of ``src`` into ``dst`` (contiguous device
+    tensors of equal byte size) with the library's streaming copy kernel, the
+    measured HBM ceiling for one read and one write of every byte."""
+    import torch
+
+    if not (src.is_contiguous() and dst.is_contiguous()):
+        raise ValueError("stream_copy needs contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("stream_copy needs tensors of equal byte size")
+    code = lib().rwkv7_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(torch, stream))
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_stream_copy")
+    return dst
 
 
 def abi_version() -> int:

@@ -253,3 +253,16 @@ def test_decode_fused_validation_codes():
     assert dfu(ok, N=96) == 4
     assert dfu(ok, y=fake(13, 64)) == 6            # y over the gate
     assert dfu(ok, state=fake(11)) == 6            # state over k_k
+
+
+def test_stream_copy_validation_codes():
+    L = wkv.lib()
+    src, dst = A, A + STRIDE
+    assert L.rwkv7_stream_copy(src, dst, 0, None) == 0          # nothing to do, no launch
+    assert L.rwkv7_stream_copy(None, dst, 64, None) == 1
+    assert L.rwkv7_stream_copy(src, None, 64, None) == 1
+    assert L.rwkv7_stream_copy(src + 8, dst, 64, None) == 5
+    assert L.rwkv7_stream_copy(src, dst + 4, 64, None) == 5
+    assert L.rwkv7_stream_copy(src, dst, 72, None) == 2          # not a multiple of 16
+    assert L.rwkv7_stream_copy(src, src + 32, 64, None) == 6     # overlapping ranges
+    assert L.rwkv7_stream_copy(src + 32, src, 64, None) == 6
