@@ -9,20 +9,22 @@
 // summary, §8 Speed and Memory.  The state read and write (32 KiB per head)
 // is all but the whole traffic, so the kernel is laid out for HBM streaming.
 //
-// Head size 64: one 256-thread workgroup per head, four waves of 16 value rows
-// each, 4 rows per lane; the GroupNorm statistics of the fused epilogue meet in
-// LDS.  (Measured against 1, 2, 4, 8 and 16 value rows per lane, one wave per
-// workgroup, one, two and four heads per workgroup, and persistent waves: this
-// layout streamed fastest, ~81% of 8 TB/s, ahead of the best plain copy kernel
-// found at the same launch size.  Workgroups of a single wave were held back
-// by the rate at which workgroups are dispatched.)  Head size 128 uses 32 lanes
-// per row and 8 rows per lane: eight waves per head (see DecodeShape).
+// One workgroup per head, 4 value rows per lane: at head size 64 four waves of
+// 16 rows (256 threads), at 128 sixteen waves of 8 rows (1024 threads, 32
+// lanes per row; see DecodeShape).  The GroupNorm statistics of the fused
+// epilogue meet in LDS.  (Measured against 1, 2, 4, 8 and 16 value rows per
+// lane, one wave per workgroup, one, two and four heads per workgroup, and
+// persistent waves: this layout streamed fastest, ~80% of 8 TB/s at head size
+// 64, level with the best plain copy kernel found at the same launch size.
+// Workgroups of a single wave were held back by the rate at which workgroups
+// are dispatched.)
 // Lane (c, g) = (lane & 15, lane >> 4) owns key columns 4c .. 4c+3 of value
 // rows r0 + 4g .. r0 + 4g + 3: every state load instruction reads four complete
-// 256-byte rows (16 lanes x 16 bytes each), so each wave moves its 4 KiB in
-// four fully coalesced dwordx4 loads issued back to back.  Row sums (S kappa
-// and S (w*r)) are 16-lane DPP reductions.  Lanes c < 4 finally hold y of rows
-// r0 + 4g + c, so each wave's 16 readouts leave as one 32-byte (bf16) store.
+// 256-byte rows (16 lanes x 16 bytes each; at head size 128, two 512-byte
+// rows), so each wave moves its 4 KiB in four fully coalesced dwordx4 loads
+// issued back to back.  Row sums (S kappa and S (w*r)) are DPP reductions over
+// a row's lanes.  Lanes c < 4 finally hold y of rows r0 + 4g + c, so each
+// wave's readouts leave as one contiguous store.
 // State loads and stores are non-temporal: each state is touched once per call
 // and the next layer's states should not be evicted for it.
 #include "wkv7_device.h"
@@ -69,14 +71,11 @@ __device__ __forceinline__ void load_rows(const float *p, float *out) {
 // each, 16 bytes), so a wave holds 64/(N/4) row groups of kRows rows.
 template <int N>
 struct DecodeShape {
-    static constexpr int kRows = N == 64 ? 4 : 8;               // value rows per lane
+    static constexpr int kRows = 4;                             // value rows per lane
     static constexpr int kLanesPerRow = N / 4;                  // 16 (N=64) or 32 (N=128)
     static constexpr int kGroups = 64 / kLanesPerRow;           // 4 or 2
-    static constexpr int kRowsPerWave = kGroups * kRows;        // 16 at either size
-    static constexpr int kWavesPerHead = N / kRowsPerWave;      // 4 or 8
-    // one workgroup per head even without the epilogue (N = 64); at N = 128 a
-    // call without the epilogue launches one single-wave workgroup per wave
-    static constexpr bool kHeadPerGroup = N == 64;
+    static constexpr int kRowsPerWave = kGroups * kRows;        // 16 or 8
+    static constexpr int kWavesPerHead = N / kRowsPerWave;      // 4 or 16: one workgroup
 };
 
 // Sum over the lanes of one state row (16 or 32 lanes).
@@ -88,18 +87,16 @@ __device__ __forceinline__ float row_sum(float x) {
 }
 
 template <class IO, bool EPI, bool NT, bool W32, int N, bool FUSED = false>
-__global__ __launch_bounds__((EPI || DecodeShape<N>::kHeadPerGroup)
-                                 ? 64 * DecodeShape<N>::kWavesPerHead
-                                 : 64) void decode_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(64 * DecodeShape<N>::kWavesPerHead) void decode_kernel(
+    DecodeArgs p) {
     using E = typename IO::elem;
     using Sh = DecodeShape<N>;
     constexpr int kW = Sh::kWavesPerHead;
     constexpr int kRows = Sh::kRows;
-    constexpr bool kWhole = EPI || Sh::kHeadPerGroup;  // the workgroup holds the whole head
     __shared__ float2 xch[kW];  // epilogue: (mean, M2) of each wave's rows
     const int lane = threadIdx.x & 63;
-    const long head = kWhole ? (long)blockIdx.x : (long)(blockIdx.x / kW);
-    const int part = kWhole ? (int)(threadIdx.x >> 6) : (int)(blockIdx.x % kW);
+    const long head = (long)blockIdx.x;
+    const int part = (int)(threadIdx.x >> 6);
     if (head >= (long)p.B * p.H) return;  // whole workgroup leaves together
     const int h = (int)(head % p.H);
     const int c = lane % Sh::kLanesPerRow, g = lane / Sh::kLanesPerRow;
@@ -226,17 +223,13 @@ template <int N, class IO, bool W32, bool FUSED>
 hipError_t launch_decode_n(const DecodeArgs &p, hipStream_t stream) {
     constexpr int kW = DecodeShape<N>::kWavesPerHead;
     const long heads = (long)p.B * p.H;
-    // one workgroup per head holding all its waves (with the epilogue, and at
-    // N = 64 always); else one 64-thread workgroup per wave of a head
+    // one workgroup per head holding all its waves
     if (p.epilogue)
         hipLaunchKernelGGL((decode_kernel<IO, true, true, W32, N, FUSED>), dim3((unsigned)heads),
                            dim3(64 * kW), 0, stream, p);
-    else if (DecodeShape<N>::kHeadPerGroup)
+    else
         hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N, FUSED>), dim3((unsigned)heads),
                            dim3(64 * kW), 0, stream, p);
-    else
-        hipLaunchKernelGGL((decode_kernel<IO, false, true, W32, N, FUSED>),
-                           dim3((unsigned)(kW * heads)), dim3(64), 0, stream, p);
     return hipGetLastError();
 }
 
