@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define RWKV7_ABI_VERSION 1
+#define RWKV7_ABI_VERSION 2
 
 typedef enum {
     RWKV7_OK = 0,
@@ -246,15 +246,35 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
  *   dr, dw, dk, dv, dkappa, da : [B,T,H,N] in dt (outputs)
  *   ds0    : [B,H,N,N] float32 gradient for s0 (output), or NULL to skip it;
  *            may equal ds_T (in place)
- * Computed in fp32 (states recomputed from s_ckpt, token by token), rounded
- * once to dt.  The six gradient outputs must not overlap each other or any
- * input.  T == 0: ds0 receives ds_T (or zeros).
+ *   algo   : RWKV7_ALGO_SCAN: token by token in fp32 VALU (states recomputed
+ *              from s_ckpt), any dtype, no workspace;
+ *            RWKV7_ALGO_CHUNKED: bf16 only; the chunked form on bf16 MFMA with
+ *              fp32 accumulation: a reverse pass over the 16-token chunks
+ *              carries the state cotangent and stores it at every chunk's end
+ *              in the workspace, then every chunk's gradients are formed in
+ *              parallel from its stored state and cotangent;
+ *            RWKV7_ALGO_AUTO: CHUNKED for bf16, SCAN for f32.
+ *   workspace / workspace_bytes : device scratch of at least
+ *            rwkv7_wkv_backward_workspace(...) bytes (16 KiB per head and
+ *            chunk for CHUNKED; may be NULL when that is 0); it must not
+ *            overlap any other argument.
+ * Gradients are rounded once to dt.  The six gradient outputs must not
+ * overlap each other or any input.  T == 0: ds0 receives ds_T (or zeros).
+ * The chunked form is the derivative of the chunked forward of the RWKV-7
+ * "Goose" summary, §4 Method (parallel chunked form of the
+ * diagonal-plus-rank-one transition); its algebra is stated with the kernels.
  */
 rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v,
                                 const void *kappa, const void *a, const void *dy,
                                 const float *s_ckpt, const float *ds_T, void *dr, void *dw,
                                 void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
-                                int T, int H, int N, rwkv7_dtype dt, void *stream);
+                                int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace rwkv7_wkv_backward needs (0 if none; 0 also for
+ * invalid arguments). */
+size_t rwkv7_wkv_backward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
+                                    rwkv7_algo algo);
 
 /*
  * rwkv7_wkv_decode fed from raw keys through the fused time-mix prologue

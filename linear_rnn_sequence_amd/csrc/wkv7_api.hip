@@ -326,15 +326,40 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
                         algo, nullptr, workspace, workspace_bytes, stream);
 }
 
+// AUTO: the chunked backward for bf16, else the token-by-token one.
+static rwkv7_algo resolve_bwd_algo(rwkv7_algo algo, rwkv7_dtype dt) {
+    if (algo == RWKV7_ALGO_AUTO)
+        return dt == RWKV7_DT_BF16 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+    return algo;
+}
+
+size_t rwkv7_wkv_backward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
+                                    rwkv7_algo algo) {
+    if (B < 1 || H < 1 || T <= 0 || N != kN) return 0;
+    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return 0;
+    if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED) return 0;
+    if (resolve_bwd_algo(algo, dt) != RWKV7_ALGO_CHUNKED) return 0;
+    size_t n = 1;
+    if (!mul_ok(n, (size_t)B) || !mul_ok(n, (size_t)H) ||
+        !mul_ok(n, (size_t)((T + kCkpt - 1) / kCkpt)) || !mul_ok(n, (size_t)kN * kN * 4))
+        return 0;
+    return backward_chunked_workspace_bytes(B, T, H);
+}
+
 rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, const void *v,
                                 const void *kappa, const void *a, const void *dy,
                                 const float *s_ckpt, const float *ds_T, void *dr, void *dw,
                                 void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
-                                int T, int H, int N, rwkv7_dtype dt, void *stream) {
+                                int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                void *workspace, size_t workspace_bytes, void *stream) {
     if (dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
+        return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
+    const rwkv7_algo use = resolve_bwd_algo(algo, dt);
+    if (use == RWKV7_ALGO_CHUNKED && dt != RWKV7_DT_BF16) return RWKV7_ERR_UNSUPPORTED;
     const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
     size_t tok = 1, st = 1;
     if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
@@ -361,6 +386,13 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
         if (p && !aligned16(p)) return RWKV7_ERR_ALIGN;
     if ((s_ckpt && !aligned16(s_ckpt)) || (ds_T && !aligned16(ds_T)) || (ds0 && !aligned16(ds0)))
         return RWKV7_ERR_ALIGN;
+    const bool chunked = use == RWKV7_ALGO_CHUNKED && T > 0;
+    const size_t ws_need = chunked ? rwkv7_wkv_backward_workspace(B, T, H, N, dt, use) : 0;
+    if (chunked) {
+        if (ws_need == 0) return RWKV7_ERR_SHAPE;
+        if (!workspace || workspace_bytes < ws_need) return RWKV7_ERR_WORKSPACE;
+        if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
+    }
 
     // outputs overlap neither each other nor an input (ds0 == ds_T is the in-place case)
     auto rng = [](const void *p, size_t n) {
@@ -387,6 +419,16 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
         }
         if (ds_T && ds_T != ds0 && overlap(rd, rng(ds_T, st))) return RWKV7_ERR_ALIAS;
     }
+    if (chunked) {  // the workspace is written: it overlaps no argument
+        const Range rw = rng(workspace, ws_need);
+        for (const void *q : ins)
+            if (overlap(rw, rng(q, tok))) return RWKV7_ERR_ALIAS;
+        for (const void *q : outs)
+            if (overlap(rw, rng(q, tok))) return RWKV7_ERR_ALIAS;
+        if (overlap(rw, rng(s_ckpt, ck)) || (ds_T && overlap(rw, rng(ds_T, st))) ||
+            (ds0 && overlap(rw, rng(ds0, st))))
+            return RWKV7_ERR_ALIAS;
+    }
 
     hipStream_t hs = static_cast<hipStream_t>(stream);
     if (T == 0) {
@@ -400,6 +442,10 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     p.ds0 = ds0;
     p.B = B; p.T = T; p.H = H;
     p.bf16 = dt == RWKV7_DT_BF16;
+    if (chunked) {
+        p.ds_ws = static_cast<float *>(workspace);
+        return launch_backward_chunked(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
+    }
     return launch_backward(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
 }
 

@@ -1,0 +1,515 @@
+// WKV7 backward in the chunked form on bf16 MFMA (fp32 accumulation).
+//
+// The recurrence (RWKV-7 "Goose" author response, numpy time_mixing listing;
+// ARWKV verdict, key_machinery field) is, per head, with S[i = value][j = key]
+//   S_t = S_{t-1} A_t + v_t k_t^T,   A_t = diag(w_t) - kappa_t (a_t * kappa_t)^T,
+//   y_t = S_t r_t,
+// and the gradients are those of L = sum_t <y_t, dy_t> + <S_T, dS_T>.  Over a
+// chunk of 16 tokens with entry state S0 (the stored checkpoint) the forward is
+// (derivation not on the pages, checked in fp64 against the per-token loop):
+//   g_t = prod_{s<=t} w_s, gp_t = g_{t-1}; Kp = kappa*gp, Rp = r*g, Km = k/g,
+//   Bm = (a*kappa)/g; Mkk = stril(Kp Km^T), N = stril(Kp Bm^T),
+//   Mkr = tril(Rp Km^T), Mbr = tril(Rp Bm^T); X = (I + N)^-1;
+//   U = X (Kp S0^T + Mkk V) (the chunk's S_{t-1} kappa_t), Y = Rp S0^T + Mkr V - Mbr U,
+//   S_C = (S0 + V^T Km - U^T Bm) diag(g_C).
+// Its reverse-mode derivative, with dSh = dS_C diag(g_C) and dS_C the cotangent
+// of the chunk's exit state:
+//   dU = -Bm dSh^T - Mbr^T dY,  dZ = X^T dU,
+//   dS0 = dSh + dY^T Rp + dZ^T Kp                      (the reverse chain)
+//   dV = Km dSh^T + Mkr^T dY + Mkk^T dZ
+//   dMkr = tril(dY V^T), dMbr = -tril(dY U^T), dMkk = stril(dZ V^T), dMbk = -stril(dZ U^T)
+//   dKm = V dSh + dMkr^T Rp + dMkk^T Kp,  dBm = -U dSh + dMbr^T Rp + dMbk^T Kp
+//   dRp = dY S0 + dMkr Km + dMbr Bm,      dKp = dZ S0 + dMkk Km + dMbk Bm
+// and back to the inputs: dr = dRp g, dk = dKm / g, db = dBm / g, da = db kappa,
+// dkappa = dKp gp + db a.  The decays enter only through g: with
+//   dlg_t = dRp_t Rp_t - dKm_t Km_t - dBm_t Bm_t + dKp_{t+1} Kp_{t+1}
+// (elementwise) plus, at the chunk's last slot, the exit-state term
+//   sum_i dS_C S_C = sum_i dSh S0 + sum_s Km_s (V dSh)_s + sum_s Bm_s (-U dSh)_s,
+// dw_s = (sum_{t >= s} dlg_t) / w_s.
+//
+// Two kernels:
+//  - bwd_chain_kernel: one workgroup per (b, h) walks the chunks backwards and
+//    carries dS^T as fp32 MFMA accumulator tiles (wave q owns values 16q..16q+15,
+//    like the forward chunked kernel's state); it stores each chunk's exit
+//    cotangent to the workspace and writes ds0;
+//  - bwd_grad_kernel: one workgroup per (b, h, chunk), all independent: from the
+//    stored entry state and exit cotangent it recomputes the chunk's operands
+//    and forms every gradient.
+// A ragged last chunk is padded with neutral tokens (w = 1, all else 0), which
+// leave every product and the decay totals unchanged.
+//
+// MFMA layouts (v_mfma_f32_16x16x16_bf16, lane l: lo = l & 15, g = l >> 4):
+//   A operand of P (16 x 16):   lane holds P[lo][4g + e]
+//   B operand of Q (16 x 16):   lane holds Q[4g + e][lo]
+//   result D (16 x 16):         lane holds D[4g + e][lo]
+// so D(M) is the B operand of M and the A operand of M^T.  Every operand read
+// from LDS below is `frag(M, row0, col0)`, four consecutive bf16 of row
+// row0 + lo at columns col0 + 4g: the A operand of a matrix stored with the
+// contraction index along its rows, or the B operand of one whose transpose is
+// stored that way.
+#include "wkv7_device.h"
+#include "wkv7_internal.h"
+
+namespace wkv7 {
+namespace {
+
+typedef short bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kC = 16;        // tokens per chunk (the checkpoint interval)
+constexpr int kThreads = 256;  // four waves
+constexpr int kSK = 68;       // row stride (bf16) of 16 x 64 and 64 x 64 tiles
+constexpr int kST = 20;       // row stride (bf16) of 64 x 16 (transposed) tiles
+
+static_assert(kC == kCkpt, "chunks are the checkpoint intervals");
+
+__device__ __forceinline__ f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// two floats -> packed bf16 pair, round to nearest even (a vector conversion, so
+// the compiler inserts the wait states an MFMA result needs before a VALU read)
+__device__ __forceinline__ unsigned cvt2(float lo, float hi) {
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) {
+    const u32x2 v = {cvt2(x[0], x[1]), cvt2(x[2], x[3])};
+    return __builtin_bit_cast(bf16x4, v);
+}
+__device__ __forceinline__ short bf1(float x) { return (short)f32_to_bf16_rne(x); }
+__device__ __forceinline__ float fbf(short s) { return __uint_as_float(((uint32_t)(uint16_t)s) << 16); }
+__device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f32x4 neg(f32x4 x) { return f32x4{-x[0], -x[1], -x[2], -x[3]}; }
+
+template <int S>
+__device__ __forceinline__ bf16x4 frag(const short (*m)[S], int row0, int col0, int lane) {
+    return *reinterpret_cast<const bf16x4 *>(&m[row0 + (lane & 15)][col0 + 4 * (lane >> 4)]);
+}
+
+// Keep the entries of a result tile D[4g+e][lo] that satisfy a triangle:
+// kLower: col <= row (kStrict: col < row); else row <= col (kStrict: row < col).
+template <bool kLower, bool kStrict>
+__device__ __forceinline__ f32x4 mask(f32x4 d, int lane) {
+    const int lo = lane & 15, row = 4 * (lane >> 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = row + e;
+        const bool keep = kLower ? (kStrict ? lo < r : lo <= r) : (kStrict ? r < lo : r <= lo);
+        d[e] = keep ? d[e] : 0.f;
+    }
+    return d;
+}
+
+// D(((I + M)^-1)^T) for a nilpotent 16 x 16 M given dm = D(M), dmt = D(M^T):
+// (I + M)^-1 = (I - M)(I + M^2)(I + M^4)(I + M^8), evaluated transposed as
+//   F^T = (I - M^T) + (M^2)^T (I - M^T),  G^T = F^T + (M^4)^T F^T,
+//   X^T = G^T + (M^8)^T G^T.
+// Called with (D(N), D(N^T)) it gives D(X^T) = A operand of X; with the
+// arguments swapped it gives D(X) = A operand of X^T.
+__device__ __forceinline__ f32x4 inverse_t(f32x4 dm, f32x4 dmt, int lane) {
+    const int lo = lane & 15, row = 4 * (lane >> 4);
+    f32x4 imt;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) imt[e] = (row + e == lo ? 1.f : 0.f) - dmt[e];
+    const bf16x4 Mb = bf4(dm), Ma = bf4(dmt);
+    const f32x4 m2 = mma(Ma, Mb, z4());   // D(M^2)
+    const f32x4 m2t = mma(Mb, Ma, z4());  // D((M^2)^T)
+    const bf16x4 M2b = bf4(m2), M2a = bf4(m2t);
+    const f32x4 m4 = mma(M2a, M2b, z4());   // D(M^4)
+    const f32x4 m4t = mma(M2b, M2a, z4());  // D((M^4)^T)
+    const f32x4 ft = mma(M2b, bf4(imt), imt);  // D(F^T)
+    const bf16x4 M4b = bf4(m4);
+    const f32x4 gt = mma(M4b, bf4(ft), ft);    // D(G^T)
+    const f32x4 m8 = mma(bf4(m4t), M4b, z4()); // D(M^8)
+    return mma(bf4(m8), bf4(gt), gt);          // D(X^T)
+}
+
+// Element offset of token t of (b, h) in a [B,T,H,64] tensor.
+__device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, long t) {
+    return ((b * p.T + t) * p.H + h) * kN;
+}
+
+// ---------------------------------------------------------------- reverse chain
+struct ChainLds {
+    short kp[kC][kSK], rp[kC][kSK], bm[kC][kSK];  // tokens x keys
+    short kpt[kN][kST], rpt[kN][kST];             // keys x tokens
+    short dyt[kN][kST];                           // values x tokens
+    float carry[4][kN];                           // decay product of each wave's 4 tokens
+    float gc[kN];                                 // decay total of the chunk
+};
+
+__global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
+    __shared__ ChainLds L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lo = lane & 15, g4 = 4 * (lane >> 4);
+    const long bh = blockIdx.x;
+    const long b = bh / p.H;
+    const int h = (int)(bh % p.H);
+    const int nch = (p.T + kC - 1) / kC;
+    const uint16_t *pr = static_cast<const uint16_t *>(p.r), *pw = static_cast<const uint16_t *>(p.w);
+    const uint16_t *pkap = static_cast<const uint16_t *>(p.kappa), *pa = static_cast<const uint16_t *>(p.a);
+    const uint16_t *pdy = static_cast<const uint16_t *>(p.dy);
+
+    // dS^T tiles: St[jb] holds dS^T[16jb + g4 + e][16 wave + lo] = dS[16 wave + lo][16jb + g4 + e]
+    f32x4 St[4];
+    const long srow = (long)(16 * wave + lo) * kN;
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        if (p.ds_T) {
+            const float4 x = *reinterpret_cast<const float4 *>(p.ds_T + bh * kN * kN + srow + 16 * jb + g4);
+            St[jb] = f32x4{x.x, x.y, x.z, x.w};
+        } else {
+            St[jb] = z4();
+        }
+    }
+
+    for (int c = nch - 1; c >= 0; --c) {
+        // ---- operands of chunk c: thread (wave, lane) takes key/value `lane` of
+        // tokens 4 wave .. 4 wave + 3
+        float wv[4], kv[4], av[4], rv[4], dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long t = (long)c * kC + 4 * wave + e;
+            const bool ok = t < p.T;
+            const long o = tok_off(p, b, h, ok ? t : 0) + lane;
+            wv[e] = ok ? bf16_lo(pw[o]) : 1.f;
+            kv[e] = ok ? bf16_lo(pkap[o]) : 0.f;
+            av[e] = ok ? bf16_lo(pa[o]) : 0.f;
+            rv[e] = ok ? bf16_lo(pr[o]) : 0.f;
+            dv[e] = ok ? bf16_lo(pdy[o]) : 0.f;
+        }
+        float cp[4];
+        cp[0] = wv[0];
+#pragma unroll
+        for (int e = 1; e < 4; ++e) cp[e] = cp[e - 1] * wv[e];
+        L.carry[wave][lane] = cp[3];
+        __syncthreads();
+        float pre = 1.f, tot = 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float x = L.carry[q][lane];
+            pre = q < wave ? pre * x : pre;
+            tot *= x;
+        }
+        if (wave == 0) L.gc[lane] = tot;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * wave + e;
+            const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
+            const float Kp = kv[e] * gprev, Rp = rv[e] * gam, Bm = av[e] * kv[e] / gam;
+            L.kp[t][lane] = bf1(Kp);
+            L.rp[t][lane] = bf1(Rp);
+            L.bm[t][lane] = bf1(Bm);
+            L.kpt[lane][t] = bf1(Kp);
+            L.rpt[lane][t] = bf1(Rp);
+            L.dyt[lane][t] = bf1(dv[e]);
+        }
+        __syncthreads();
+
+        // ---- chunk matrices (every wave forms its own copy)
+        f32x4 dn = z4(), dnt = z4(), dmbr = z4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), bma = frag(L.bm, 0, 16 * kb, lane);
+            const bf16x4 rpa = frag(L.rp, 0, 16 * kb, lane);
+            dn = mma(kpa, bma, dn);     // D(N), N = Kp Bm^T
+            dnt = mma(bma, kpa, dnt);   // D(N^T)
+            dmbr = mma(rpa, bma, dmbr); // D(Mbr), Mbr = Rp Bm^T
+        }
+        dn = mask<true, true>(dn, lane);
+        dnt = mask<false, true>(dnt, lane);
+        dmbr = mask<true, false>(dmbr, lane);
+        const f32x4 dx = inverse_t(dnt, dn, lane);  // D(X) = A operand of X^T
+
+        // ---- chain step: store the exit cotangent, then dS0 of the chunk
+        float *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            *reinterpret_cast<float4 *>(ck + 16 * jb + g4) =
+                make_float4(St[jb][0], St[jb][1], St[jb][2], St[jb][3]);
+        bf16x4 Sb[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) St[jb][e] *= L.gc[16 * jb + g4 + e];
+            Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
+        }
+        const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY (tokens x values)
+        f32x4 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) rhs = mma(frag(L.bm, 0, 16 * jb, lane), Sb[jb], rhs);  // + Bm dSh^T
+        const f32x4 up = mma(bf4(dx), bf4(rhs), z4());  // X^T rhs = -dZ
+        const bf16x4 dzb = bf4(neg(up));
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            St[jb] = mma(frag(L.rpt, 16 * jb, 0, lane), dyb, St[jb]);  // + Rp^T dY
+            St[jb] = mma(frag(L.kpt, 16 * jb, 0, lane), dzb, St[jb]);  // + Kp^T dZ
+        }
+        __syncthreads();  // the next chunk's operands overwrite LDS
+    }
+    if (p.ds0) {
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+            *reinterpret_cast<float4 *>(p.ds0 + bh * kN * kN + srow + 16 * jb + g4) =
+                make_float4(St[jb][0], St[jb][1], St[jb][2], St[jb][3]);
+    }
+}
+
+// ------------------------------------------------------- per-chunk gradients
+struct GradLds {
+    short kp[kC][kSK], rp[kC][kSK], km[kC][kSK], bm[kC][kSK];   // tokens x keys
+    short kpt[kN][kST], rpt[kN][kST], kmt[kN][kST], bmt[kN][kST];  // keys x tokens
+    short vv[kC][kSK], dyy[kC][kSK], uu[kC][kSK], dzz[kC][kSK];  // tokens x values
+    short vt[kN][kST], dyt[kN][kST];                             // values x tokens
+    short s0t[kN][kSK], dsht[kN][kSK];                           // keys x values
+    short rr[kC][kSK], kk[kC][kSK], ka[kC][kSK], aa[kC][kSK], ww[kC][kSK];  // raw inputs
+    float gam[kC][kN];       // cumulative decay within the chunk
+    float dlg[kC][kN];       // decay-gradient terms of each token
+    float dkk[kC][kN];       // dKp * Kp (belongs to the previous token's decay)
+    float dlgc[8][kN];       // exit-state term: partial sums (4 value blocks, 4 token groups)
+    float carry[4][kN];
+};
+
+__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
+    __shared__ GradLds L;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lo = lane & 15, g4 = 4 * (lane >> 4);
+    const int nch = (p.T + kC - 1) / kC;
+    const long bh = blockIdx.x / nch;
+    const int c = (int)(blockIdx.x % nch);
+    const long b = bh / p.H;
+    const int h = (int)(bh % p.H);
+    const long t0 = (long)c * kC;
+
+    // entry state and exit cotangent of this chunk, rows 16 wave + lo, keys 16jb + g4 + e
+    const long srow = (long)(16 * wave + lo) * kN;
+    const float *s0p = p.s_ckpt + (bh * nch + c) * (long)(kN * kN) + srow;
+    const float *dsp = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
+    f32x4 S0[4], Dh[4];
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const float4 x = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4);
+        const float4 y = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4);
+        S0[jb] = f32x4{x.x, x.y, x.z, x.w};
+        Dh[jb] = f32x4{y.x, y.y, y.z, y.w};
+    }
+
+    // ---- phase 1: operands.  Thread (wave, lane): tokens 4 wave .. +3, key/value `lane`
+    {
+        const uint16_t *in[7] = {static_cast<const uint16_t *>(p.r), static_cast<const uint16_t *>(p.w),
+                                 static_cast<const uint16_t *>(p.k), static_cast<const uint16_t *>(p.v),
+                                 static_cast<const uint16_t *>(p.kappa), static_cast<const uint16_t *>(p.a),
+                                 static_cast<const uint16_t *>(p.dy)};
+        float x[7][4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long t = t0 + 4 * wave + e;
+            const bool ok = t < p.T;
+            const long o = tok_off(p, b, h, ok ? t : 0) + lane;
+#pragma unroll
+            for (int s = 0; s < 7; ++s) x[s][e] = ok ? bf16_lo(in[s][o]) : (s == 1 ? 1.f : 0.f);
+        }
+        float cp[4];
+        cp[0] = x[1][0];
+#pragma unroll
+        for (int e = 1; e < 4; ++e) cp[e] = cp[e - 1] * x[1][e];
+        L.carry[wave][lane] = cp[3];
+        __syncthreads();
+        float pre = 1.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pre = q < wave ? pre * L.carry[q][lane] : pre;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = 4 * wave + e;
+            const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
+            const float r = x[0][e], k = x[2][e], v = x[3][e], kap = x[4][e], a = x[5][e], dy = x[6][e];
+            const float Kp = kap * gprev, Rp = r * gam, Km = k / gam, Bm = a * kap / gam;
+            L.gam[t][lane] = gam;
+            L.kp[t][lane] = bf1(Kp); L.kpt[lane][t] = bf1(Kp);
+            L.rp[t][lane] = bf1(Rp); L.rpt[lane][t] = bf1(Rp);
+            L.km[t][lane] = bf1(Km); L.kmt[lane][t] = bf1(Km);
+            L.bm[t][lane] = bf1(Bm); L.bmt[lane][t] = bf1(Bm);
+            L.vv[t][lane] = bf1(v); L.vt[lane][t] = bf1(v);
+            L.dyy[t][lane] = bf1(dy); L.dyt[lane][t] = bf1(dy);
+            L.rr[t][lane] = bf1(r); L.kk[t][lane] = bf1(k); L.ka[t][lane] = bf1(kap);
+            L.aa[t][lane] = bf1(a); L.ww[t][lane] = bf1(x[1][e]);
+        }
+        __syncthreads();
+    }
+
+    // ---- chunk matrices (every wave forms its own copy)
+    f32x4 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
+        const bf16x4 bma = frag(L.bm, 0, 16 * kb, lane), rpa = frag(L.rp, 0, 16 * kb, lane);
+        dmkk = mma(kpa, kma, dmkk);
+        dmkkt = mma(kma, kpa, dmkkt);
+        dn = mma(kpa, bma, dn);
+        dnt = mma(bma, kpa, dnt);
+        dmkr = mma(rpa, kma, dmkr);
+        dmbr = mma(rpa, bma, dmbr);
+    }
+    dmkk = mask<true, true>(dmkk, lane);
+    dmkkt = mask<false, true>(dmkkt, lane);
+    dn = mask<true, true>(dn, lane);
+    dnt = mask<false, true>(dnt, lane);
+    dmkr = mask<true, false>(dmkr, lane);
+    dmbr = mask<true, false>(dmbr, lane);
+    const f32x4 dxt = inverse_t(dn, dnt, lane);  // D(X^T) = A operand of X
+    const f32x4 dx = inverse_t(dnt, dn, lane);   // D(X)   = A operand of X^T
+
+    // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
+    {
+        // dSh = dS_C diag(g_C); exit-state term sum_i dSh S0 over this block's values
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * jb + g4 + e;
+                Dh[jb][e] *= L.gam[kC - 1][j];
+                const float s = sum_lanes16(Dh[jb][e] * S0[jb][e]);
+                if (lo == 0) L.dlgc[wave][j] = s;
+                L.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
+                L.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
+            }
+        }
+        const bf16x4 vb = frag(L.vt, 16 * wave, 0, lane);    // B operand of V
+        const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY
+        f32x4 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
+        f32x4 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
+        f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            const bf16x4 s0b = bf4(S0[jb]), dhb = bf4(Dh[jb]);  // B operands of S0^T, dSh^T
+            z = mma(frag(L.kp, 0, 16 * jb, lane), s0b, z);      // + Kp S0^T
+            du = mma(frag(L.bm, 0, 16 * jb, lane), dhb, du);    // + Bm dSh^T
+            dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
+        }
+        du = neg(du);
+        const f32x4 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
+        const f32x4 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
+        dv = mma(bf4(dmkk), bf4(dz), dv);              // + Mkk^T dZ
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = g4 + e;
+            L.uu[t][16 * wave + lo] = bf1(u[e]);
+            L.dzz[t][16 * wave + lo] = bf1(dz[e]);
+            if (t0 + t < p.T)
+                static_cast<uint16_t *>(p.dv)[tok_off(p, b, h, t0 + t) + 16 * wave + lo] =
+                    (uint16_t)f32_to_bf16_rne(dv[e]);
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: key block `wave` (tokens x keys 16 wave ..)
+    {
+        f32x4 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
+        f32x4 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
+        f32x4 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+            const bf16x4 ya = frag(L.dyy, 0, 16 * vb, lane), va = frag(L.vv, 0, 16 * vb, lane);
+            const bf16x4 ua = frag(L.uu, 0, 16 * vb, lane), za = frag(L.dzz, 0, 16 * vb, lane);
+            dmr = mma(ya, va, dmr);
+            dmrt = mma(va, ya, dmrt);
+            dmb = mma(ya, ua, dmb);
+            dmbt = mma(ua, ya, dmbt);
+            dmk = mma(za, va, dmk);
+            dmkt = mma(va, za, dmkt);
+            dmn = mma(za, ua, dmn);
+            dmnt = mma(ua, za, dmnt);
+            const bf16x4 dsb = frag(L.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
+            const bf16x4 s0b = frag(L.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
+            dkms = mma(va, dsb, dkms);
+            dbms = mma(ua, dsb, dbms);
+            drp = mma(ya, s0b, drp);
+            dkp = mma(za, s0b, dkp);
+        }
+        dmr = mask<true, false>(dmr, lane);
+        dmrt = mask<false, false>(dmrt, lane);
+        dmb = mask<true, false>(dmb, lane);
+        dmbt = mask<false, false>(dmbt, lane);
+        dmk = mask<true, true>(dmk, lane);
+        dmkt = mask<false, true>(dmkt, lane);
+        dmn = mask<true, true>(dmn, lane);
+        dmnt = mask<false, true>(dmnt, lane);
+        const bf16x4 rpb = frag(L.rpt, 16 * wave, 0, lane), kpb = frag(L.kpt, 16 * wave, 0, lane);
+        const bf16x4 kmb = frag(L.kmt, 16 * wave, 0, lane), bmb = frag(L.bmt, 16 * wave, 0, lane);
+        // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
+        f32x4 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
+        // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
+        f32x4 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
+        dbm = neg(dbm);
+        // dRp = dY S0 + dMkr Km + dMbr Bm
+        drp = mma(bf4(dmrt), kmb, drp);
+        drp = mma(bf4(neg(dmbt)), bmb, drp);
+        // dKp = dZ S0 + dMkk Km + dMbk Bm
+        dkp = mma(bf4(dmkt), kmb, dkp);
+        dkp = mma(bf4(neg(dmnt)), bmb, dkp);
+
+        // elementwise: lane (token g4 + e, key 16 wave + lo)
+        const int j = 16 * wave + lo;
+        float csum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int t = g4 + e;
+            const float gam = L.gam[t][j], gprev = t ? L.gam[t - 1][j] : 1.f;
+            const float r = fbf(L.rr[t][j]), k = fbf(L.kk[t][j]), kap = fbf(L.ka[t][j]);
+            const float a = fbf(L.aa[t][j]);
+            const float Kp = kap * gprev, Rp = r * gam, Km = k / gam, Bm = a * kap / gam;
+            const float dr = drp[e] * gam, dk = dkm[e] / gam, db = dbm[e] / gam;
+            const float da = db * kap, dkap = dkp[e] * gprev + db * a;
+            L.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
+            L.dkk[t][j] = dkp[e] * Kp;
+            csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
+            if (t0 + t < p.T) {
+                const long o = tok_off(p, b, h, t0 + t) + j;
+                static_cast<uint16_t *>(p.dr)[o] = (uint16_t)f32_to_bf16_rne(dr);
+                static_cast<uint16_t *>(p.dk)[o] = (uint16_t)f32_to_bf16_rne(dk);
+                static_cast<uint16_t *>(p.da)[o] = (uint16_t)f32_to_bf16_rne(da);
+                static_cast<uint16_t *>(p.dkappa)[o] = (uint16_t)f32_to_bf16_rne(dkap);
+            }
+        }
+        L.dlgc[4 + (lane >> 4)][j] = csum;
+    }
+    __syncthreads();
+
+    // ---- phase 4: decay gradients, a reverse sum over the chunk's tokens per key
+    if (wave == 0) {
+        const int j = lane;
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc += L.dlgc[q][j];
+#pragma unroll
+        for (int t = kC - 1; t >= 0; --t) {
+            acc += L.dlg[t][j] + (t + 1 < kC ? L.dkk[t + 1][j] : 0.f);
+            if (t0 + t < p.T)
+                static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
+                    (uint16_t)f32_to_bf16_rne(acc / fbf(L.ww[t][j]));
+        }
+    }
+}
+
+}  // namespace
+
+size_t backward_chunked_workspace_bytes(int B, int T, int H) {
+    const size_t nch = (size_t)(T + kC - 1) / kC;
+    return (size_t)B * H * nch * kN * kN * sizeof(float);
+}
+
+hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream) {
+    const long heads = (long)p.B * p.H;
+    const long nch = (p.T + kC - 1) / kC;
+    hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)heads), dim3(kThreads), 0, stream, p);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(heads * nch)), dim3(kThreads), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
+}  // namespace wkv7

@@ -59,6 +59,7 @@ struct BackwardArgs {
     float *ds0;                             // [B,H,N,N] or nullptr
     int B, T, H;
     bool bf16;
+    float *ds_ws;  // chunked: [B,H,ceil(T/kCkpt),N,N] exit cotangent of every chunk
 };
 
 struct DecodeArgs {
@@ -84,6 +85,10 @@ hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream);
 size_t chunked_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
+// chunked backward (bf16, head size 64): reverse chain over the chunks, then
+// every chunk's gradients in parallel; needs ds_ws of the size below
+hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream);
+size_t backward_chunked_workspace_bytes(int B, int T, int H);
 // S_T for T == 0: copy s0 (or zeros) into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream);
 

@@ -73,8 +73,10 @@ def lib():
         L.rwkv7_wkv_forward_bidir_workspace.restype = sz
         L.rwkv7_wkv_forward_train.argtypes = [vp] * 10 + [ci] * 6 + [vp, sz, vp]
         L.rwkv7_wkv_forward_train.restype = ci
-        L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [ci] * 5 + [vp]
+        L.rwkv7_wkv_backward.argtypes = [vp] * 16 + [ci] * 6 + [vp, sz, vp]
         L.rwkv7_wkv_backward.restype = ci
+        L.rwkv7_wkv_backward_workspace.argtypes = [ci] * 6
+        L.rwkv7_wkv_backward_workspace.restype = sz
         L.rwkv7_stream_copy.argtypes = [vp, vp, sz, vp]
         L.rwkv7_stream_copy.restype = ci
         L.rwkv7_status_str.argtypes = [ci]
@@ -280,11 +282,19 @@ def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=N
     return y, s_out, s_ckpt
 
 
+def backward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
+    """rwkv7_wkv_backward_workspace."""
+    dt = DT_BF16 if dtype == "bf16" else DT_F32
+    return int(lib().rwkv7_wkv_backward_workspace(B, T, H, N, dt, ALGOS[algo]))
+
+
 def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=None,
-             want_ds0=True, stream=None):
+             want_ds0=True, algo="auto", workspace=None, stream=None):
     """rwkv7_wkv_backward.  Returns (dr, dw, dk, dv, dkappa, da, ds0): the gradients of
     sum_t <y_t, dy_t> + <S_T, ds_T> for the inputs of :func:`forward_train`.  ``grads``
-    may pass the six output tensors; ``ds0`` may be ``ds_T`` (in place)."""
+    may pass the six output tensors; ``ds0`` may be ``ds_T`` (in place).  ``algo`` is
+    "auto", "scan" or "chunked"; the chunked form's workspace is allocated here unless
+    ``workspace`` (a uint8 device tensor of at least backward_workspace_bytes) is given."""
     import torch
 
     B, T, H, N = r.shape
@@ -294,10 +304,14 @@ def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=Non
         grads = tuple(torch.empty_like(r) for _ in range(6))
     if ds0 is None and want_ds0:
         ds0 = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
+    need = int(lib().rwkv7_wkv_backward_workspace(B, T, H, N, dt, ALGOS[algo]))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=r.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     code = lib().rwkv7_wkv_backward(
         _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(dy), _ptr(s_ckpt),
-        _ptr(ds_T), *(_ptr(g) for g in grads), _ptr(ds0), B, T, H, N, dt,
-        _stream(torch, stream))
+        _ptr(ds_T), *(_ptr(g) for g in grads), _ptr(ds0), B, T, H, N, dt, ALGOS[algo],
+        _ptr(workspace), nbytes, _stream(torch, stream))
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_backward")
     return (*grads, ds0)

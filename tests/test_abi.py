@@ -32,7 +32,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert wkv.abi_version() == 1
+    assert wkv.abi_version() == 2
     L = wkv.lib()
     for code in range(9):
         assert L.rwkv7_status_str(code)
@@ -137,10 +137,11 @@ def test_forward_train_validation_codes():
 
 
 def bwd(B=2, T=8, H=3, N=64, dt=1, ins=None, dy=fake(6), ck=fake(7), dsT=fake(8), outs=None,
-        ds0=fake(15)):
+        ds0=fake(15), algo=1, ws=None, ws_bytes=0):
     ins = ins or [fake(i) for i in range(6)]
     outs = outs or [fake(9 + i) for i in range(6)]
-    return wkv.lib().rwkv7_wkv_backward(*ins, dy, ck, dsT, *outs, ds0, B, T, H, N, dt, None)
+    return wkv.lib().rwkv7_wkv_backward(*ins, dy, ck, dsT, *outs, ds0, B, T, H, N, dt, algo,
+                                        ws, ws_bytes, None)
 
 
 def test_backward_validation_codes():
@@ -266,3 +267,24 @@ def test_stream_copy_validation_codes():
     assert L.rwkv7_stream_copy(src, dst, 72, None) == 2          # not a multiple of 16
     assert L.rwkv7_stream_copy(src, src + 32, 64, None) == 6     # overlapping ranges
     assert L.rwkv7_stream_copy(src + 32, src, 64, None) == 6
+
+
+def test_backward_chunked_workspace_codes():
+    L = wkv.lib()
+    B, T, H = 2, 40, 3
+    need = L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 2)
+    assert need == B * H * 3 * 64 * 64 * 4                   # 16 KiB per head and chunk
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 0) == need    # auto -> chunked
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 0, 0) == 0       # f32 -> scan
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 1) == 0
+    assert L.rwkv7_wkv_backward_workspace(B, 0, H, 64, 1, 2) == 0
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 128, 1, 2) == 0
+    ws = fake(20)
+    assert bwd(T=T, algo=2) == 7                              # no workspace
+    assert bwd(T=T, algo=2, ws=ws, ws_bytes=need - 16) == 7   # too small
+    assert bwd(T=T, algo=2, ws=fake(20, 8), ws_bytes=need) == 5
+    assert bwd(T=T, algo=2, ws=fake(7), ws_bytes=need) == 6   # over the stored states
+    assert bwd(T=T, algo=2, ws=fake(12), ws_bytes=need) == 6  # over dk
+    assert bwd(T=T, algo=2, dt=0) == 4                        # chunked is bf16 only
+    assert bwd(T=T, algo=9) == 3
+    assert bwd(T=0, algo=2, ds0=None, ck=None) == 0           # nothing to do

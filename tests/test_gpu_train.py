@@ -64,13 +64,14 @@ def cot_device(dy, ds_T, dtype):
     return dyt, dy64, dst
 
 
-def run_and_check(wkv, x, dy, ds_T, *, algo="auto", b_idx=None, h_idx=None, what=""):
+def run_and_check(wkv, x, dy, ds_T, *, algo="auto", bwd="auto", b_idx=None, h_idx=None,
+                  what=""):
     dtype = x["meta"]["dtype"]
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
     dyt, dy64, dst = cot_device(dy, ds_T, dtype)
     y, s, ck = wkv.forward_train(*ins, s0=d["s0"], algo=algo)
-    *g, ds0 = wkv.backward(*ins, dyt, ck, dst)
+    *g, ds0 = wkv.backward(*ins, dyt, ck, dst, algo=bwd)
     torch.cuda.synchronize()
     ref = og.backward(*(x.as_f64(n) for n in NAMES), dy64, s0=x["s0"],
                       ds_T=None if ds_T is None else ds_T.astype(np.float64),
@@ -98,22 +99,27 @@ def test_train_forward_stores_states(wkv, dtype, algo):
     assert_close(to_f64(ck), oracle_ckpts(x), TOL[dtype], "stored states")
 
 
+# backward algorithms: the token-by-token one for both dtypes, the chunked one for bf16
+BWD = [("f32", "scan"), ("bf16", "scan"), ("bf16", "chunked")]
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 33, 64, 100])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_sweep_T(wkv, T, dtype):
+@pytest.mark.parametrize("dtype,bwd", BWD)
+def test_backward_sweep_T(wkv, T, dtype, bwd):
     x = synth.draw(1, T, 2, seed=300 + T, dtype=dtype, s0="normal")
     dy, ds_T = synth.cotangents(1, T, 2, seed=400 + T, dtype=dtype)
-    run_and_check(wkv, x, dy, ds_T, what=f"{dtype} T={T}")
+    run_and_check(wkv, x, dy, ds_T, bwd=bwd, what=f"{dtype} {bwd} T={T}")
 
 
 @pytest.mark.parametrize("B,H,T", [(2, 3, 37), (3, 1, 129), (1, 5, 256)])
 @pytest.mark.parametrize("with_dsT", [False, True])
 @pytest.mark.parametrize("s0", ["zero", "normal"])
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_backward_sweep(wkv, B, H, T, with_dsT, s0, dtype):
+@pytest.mark.parametrize("dtype,bwd", BWD)
+def test_backward_sweep(wkv, B, H, T, with_dsT, s0, dtype, bwd):
     x = synth.draw(B, T, H, seed=B * 1000 + H * 100 + T, dtype=dtype, s0=s0, w_recipe="wide")
     dy, ds_T = synth.cotangents(B, T, H, seed=7 + T, dtype=dtype, with_state=with_dsT)
-    run_and_check(wkv, x, dy, ds_T, what=f"{dtype} B{B} H{H} T{T} dsT={with_dsT} s0={s0}")
+    run_and_check(wkv, x, dy, ds_T, bwd=bwd,
+                  what=f"{dtype} {bwd} B{B} H{H} T{T} dsT={with_dsT} s0={s0}")
 
 
 def test_backward_fp32_inputs_on_bf16_path_agree(wkv):
@@ -133,17 +139,18 @@ def test_backward_fp32_inputs_on_bf16_path_agree(wkv):
         assert rel_err(to_f64(a), to_f64(b)) <= TOL_GRAD["bf16"]
 
 
-def test_backward_ds0_in_place_and_optional(wkv):
-    x = synth.draw(1, 50, 2, seed=31, dtype="f32", s0="normal")
-    dy, ds_T = synth.cotangents(1, 50, 2, seed=32, dtype="f32")
+@pytest.mark.parametrize("dtype,bwd", BWD)
+def test_backward_ds0_in_place_and_optional(wkv, dtype, bwd):
+    x = synth.draw(1, 50, 2, seed=31, dtype=dtype, s0="normal")
+    dy, ds_T = synth.cotangents(1, 50, 2, seed=32, dtype=dtype)
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
-    dyt, _, dst = cot_device(dy, ds_T, "f32")
+    dyt, _, dst = cot_device(dy, ds_T, dtype)
     _, _, ck = wkv.forward_train(*ins, s0=d["s0"])
-    ref = wkv.backward(*ins, dyt, ck, dst)
+    ref = wkv.backward(*ins, dyt, ck, dst, algo=bwd)
     buf = dst.clone()
-    got = wkv.backward(*ins, dyt, ck, buf, ds0=buf)
-    nods0 = wkv.backward(*ins, dyt, ck, dst, want_ds0=False)
+    got = wkv.backward(*ins, dyt, ck, buf, ds0=buf, algo=bwd)
+    nods0 = wkv.backward(*ins, dyt, ck, dst, want_ds0=False, algo=bwd)
     torch.cuda.synchronize()
     assert torch.equal(got[6], ref[6]) and got[6].data_ptr() == buf.data_ptr()
     for a, b, c in zip(ref[:6], got[:6], nods0[:6]):
@@ -151,8 +158,9 @@ def test_backward_ds0_in_place_and_optional(wkv):
     assert nods0[6] is None
 
 
-def test_backward_T0_copies_state_cotangent(wkv):
-    z = torch.empty((2, 0, 3, 64), dtype=torch.float32, device="cuda")
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_backward_T0_copies_state_cotangent(wkv, dt):
+    z = torch.empty((2, 0, 3, 64), dtype=dt, device="cuda")
     dst = torch.randn(2, 3, 64, 64, device="cuda")
     ck = torch.empty((2, 3, 0, 64, 64), device="cuda")
     *g, ds0 = wkv.backward(z, z, z, z, z, z, z, ck, dst)
