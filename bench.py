@@ -56,6 +56,8 @@ def parse():
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 4 GiB device copy (counter calibration)")
     ap.add_argument("--prefill-algo", default="auto", choices=["auto", "scan", "chunked"])
+    ap.add_argument("--bwd-algo", default="auto", choices=["auto", "scan", "chunked"],
+                    help="backward algorithm of --only train (auto: chunked for bf16)")
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' needs --only prefill")
     ap.add_argument("--decode-head", type=int, default=64, choices=[64, 128],
@@ -234,6 +236,9 @@ def bench_train(args, torch, wkv, synth, dev):
     ck = torch.empty((B, H, (T + 15) // 16, N, N), dtype=torch.float32, device=dev)
     grads = tuple(torch.empty_like(ins[0]) for _ in range(6))
     ds0 = torch.empty_like(s_out)
+    bws = wkv.backward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.bwd_algo)
+    bwork = torch.empty(max(bws, 16), dtype=torch.uint8, device=dev)
+    chunked_bwd = bws > 0
     stream = torch.cuda.current_stream()
 
     def fwd():
@@ -241,7 +246,8 @@ def bench_train(args, torch, wkv, synth, dev):
                           workspace=ws)
 
     def bwd():
-        wkv.backward(*ins, dy, ck, dst, grads=grads, ds0=ds0)
+        wkv.backward(*ins, dy, ck, dst, grads=grads, ds0=ds0, algo=args.bwd_algo,
+                     workspace=bwork)
 
     for wi in range(args.warmup):
         fwd()
@@ -277,7 +283,8 @@ def bench_train(args, torch, wkv, synth, dev):
     nck = (T + 15) // 16
     fwd_bytes = work * 7 * N * 2 + B * H * N * N * 4 * (1 + nck)
     bwd_bytes = work * 13 * N * 2 + B * H * N * N * 4 * (2 + nck)
-    src = source_hash("wkv7_backward.hip", "wkv7_device.h")
+    src = source_hash("wkv7_backward_chunked.hip" if chunked_bwd else "wkv7_backward.hip",
+                      "wkv7_device.h")
     out = {
         "metric": "WKV7 training tokens x heads per second (forward with stored states + backward)",
         "value": work / (ms_per_step / 1e3),
@@ -289,13 +296,23 @@ def bench_train(args, torch, wkv, synth, dev):
                                 "every 16 tokens, then backward to r, w, k, v, kappa, a, S0; "
                                 "B8 T4096 H40 N64, no epilogue"),
                    "B": B, "T": T, "H": H, "N": N, "forward_algo": args.prefill_algo,
+                   "backward_algo": "chunked" if chunked_bwd else "scan",
                    "state_dtype": "f32"},
-        "roofline": {"kernel": "wkv7 backward_kernel<bf16>", "bound": "alu",
-                     "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": tf / FP32_VALU_PEAK_TFLOPS,
-                     "traffic": read_traffic("backward_kernel_traffic_b8_t4096_h40.txt", src),
-                     "flops_per_launch": bwd_flops, "avg_launch_us": bwd_ms * 1e3,
-                     "hbm_GBps_algorithmic": bwd_bytes / (bwd_ms / 1e3) / 1e9},
+        "roofline": ({"kernel": "wkv7 chunked backward (reverse chain + per-chunk gradients)",
+                      "bound": "hbm", "achieved": bwd_bytes / (bwd_ms / 1e3) / 1e9,
+                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
+                      "traffic": read_traffic("backward_chunked_traffic_b8_t4096_h40.txt", src),
+                      "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_ms * 1e3,
+                      "workspace_bytes": bws,
+                      "valu_tflops_equivalent": tf}
+                     if chunked_bwd else
+                     {"kernel": "wkv7 backward_kernel<bf16>", "bound": "alu",
+                      "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                      "frac": tf / FP32_VALU_PEAK_TFLOPS,
+                      "traffic": read_traffic("backward_kernel_traffic_b8_t4096_h40.txt", src),
+                      "flops_per_launch": bwd_flops, "avg_launch_us": bwd_ms * 1e3,
+                      "hbm_GBps_algorithmic": bwd_bytes / (bwd_ms / 1e3) / 1e9}),
         "forward_train": {"ms": fwd_ms, "bytes_per_launch": fwd_bytes,
                           "hbm_GBps": fwd_bytes / (fwd_ms / 1e3) / 1e9},
         "backward_ms": bwd_ms,

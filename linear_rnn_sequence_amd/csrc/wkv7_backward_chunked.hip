@@ -32,9 +32,10 @@
 //    carries dS^T as fp32 MFMA accumulator tiles (wave q owns values 16q..16q+15,
 //    like the forward chunked kernel's state); it stores each chunk's exit
 //    cotangent to the workspace and writes ds0;
-//  - bwd_grad_kernel: one workgroup per (b, h, chunk), all independent: from the
-//    stored entry state and exit cotangent it recomputes the chunk's operands
-//    and forms every gradient.
+//  - bwd_grad_kernel: the chunks are independent here: from a chunk's stored
+//    entry state and exit cotangent a workgroup recomputes its operands and
+//    forms every gradient; each workgroup takes 8 consecutive chunks of one
+//    head and loads the next chunk's inputs while it works on the current one.
 // A ragged last chunk is padded with neutral tokens (w = 1, all else 0), which
 // leave every product and the decay totals unchanged.
 //
@@ -63,6 +64,7 @@ constexpr int kC = 16;        // tokens per chunk (the checkpoint interval)
 constexpr int kThreads = 256;  // four waves
 constexpr int kSK = 68;       // row stride (bf16) of 16 x 64 and 64 x 64 tiles
 constexpr int kST = 20;       // row stride (bf16) of 64 x 16 (transposed) tiles
+constexpr int kGradChunks = 8;  // consecutive chunks of one head per gradient workgroup
 
 static_assert(kC == kCkpt, "chunks are the checkpoint intervals");
 
@@ -166,21 +168,31 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         }
     }
 
+    // raw bf16 inputs of a chunk: thread (wave, lane) takes key/value `lane` of
+    // tokens 4 wave .. 4 wave + 3; the next chunk's are loaded while this one runs
+    uint16_t nw[4], nk[4], na[4], nr[4], nd[4];
+    auto load_chunk = [&](int cc) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const long t = (long)cc * kC + 4 * wave + e;
+            const long o = tok_off(p, b, h, t < p.T ? t : 0) + lane;
+            nw[e] = pw[o]; nk[e] = pkap[o]; na[e] = pa[o]; nr[e] = pr[o]; nd[e] = pdy[o];
+        }
+    };
+    load_chunk(nch - 1);
+
     for (int c = nch - 1; c >= 0; --c) {
-        // ---- operands of chunk c: thread (wave, lane) takes key/value `lane` of
-        // tokens 4 wave .. 4 wave + 3
         float wv[4], kv[4], av[4], rv[4], dv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const long t = (long)c * kC + 4 * wave + e;
-            const bool ok = t < p.T;
-            const long o = tok_off(p, b, h, ok ? t : 0) + lane;
-            wv[e] = ok ? bf16_lo(pw[o]) : 1.f;
-            kv[e] = ok ? bf16_lo(pkap[o]) : 0.f;
-            av[e] = ok ? bf16_lo(pa[o]) : 0.f;
-            rv[e] = ok ? bf16_lo(pr[o]) : 0.f;
-            dv[e] = ok ? bf16_lo(pdy[o]) : 0.f;
+            const bool ok = (long)c * kC + 4 * wave + e < p.T;
+            wv[e] = ok ? bf16_lo(nw[e]) : 1.f;
+            kv[e] = ok ? bf16_lo(nk[e]) : 0.f;
+            av[e] = ok ? bf16_lo(na[e]) : 0.f;
+            rv[e] = ok ? bf16_lo(nr[e]) : 0.f;
+            dv[e] = ok ? bf16_lo(nd[e]) : 0.f;
         }
+        if (c > 0) load_chunk(c - 1);
         float cp[4];
         cp[0] = wv[0];
 #pragma unroll
@@ -199,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         for (int e = 0; e < 4; ++e) {
             const int t = 4 * wave + e;
             const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
-            const float Kp = kv[e] * gprev, Rp = rv[e] * gam, Bm = av[e] * kv[e] / gam;
+            const float Kp = kv[e] * gprev, Rp = rv[e] * gam;
+            const float Bm = av[e] * kv[e] * __builtin_amdgcn_rcpf(gam);
             L.kp[t][lane] = bf1(Kp);
             L.rp[t][lane] = bf1(Rp);
             L.bm[t][lane] = bf1(Bm);
@@ -278,219 +291,276 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lo = lane & 15, g4 = 4 * (lane >> 4);
     const int nch = (p.T + kC - 1) / kC;
-    const long bh = blockIdx.x / nch;
-    const int c = (int)(blockIdx.x % nch);
+    const int ngrp = (nch + kGradChunks - 1) / kGradChunks;
+    const long bh = blockIdx.x / ngrp;
+    const int c_begin = (int)(blockIdx.x % ngrp) * kGradChunks;
+    const int c_end = min(nch, c_begin + kGradChunks);
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
-    const long t0 = (long)c * kC;
+    const uint16_t *in[7] = {static_cast<const uint16_t *>(p.r), static_cast<const uint16_t *>(p.w),
+                             static_cast<const uint16_t *>(p.k), static_cast<const uint16_t *>(p.v),
+                             static_cast<const uint16_t *>(p.kappa), static_cast<const uint16_t *>(p.a),
+                             static_cast<const uint16_t *>(p.dy)};
 
-    // entry state and exit cotangent of this chunk, rows 16 wave + lo, keys 16jb + g4 + e
+    // A chunk's global inputs, loaded one chunk ahead: its entry state and exit
+    // cotangent (rows 16 wave + lo, keys 16jb + g4 + e) and the raw inputs as
+    // 16-byte row pieces: piece q = threadIdx.x + 256 i (i < 4, q < 7 * 128) is
+    // keys/values 8 (q & 7) .. +7 of token (q >> 3) & 15 of input q >> 7
+    // (r, w, k, v, kappa, a, dy).
     const long srow = (long)(16 * wave + lo) * kN;
-    const float *s0p = p.s_ckpt + (bh * nch + c) * (long)(kN * kN) + srow;
-    const float *dsp = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
-    f32x4 S0[4], Dh[4];
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        const float4 x = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4);
-        const float4 y = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4);
-        S0[jb] = f32x4{x.x, x.y, x.z, x.w};
-        Dh[jb] = f32x4{y.x, y.y, y.z, y.w};
-    }
-
-    // ---- phase 1: operands.  Thread (wave, lane): tokens 4 wave .. +3, key/value `lane`
-    {
-        const uint16_t *in[7] = {static_cast<const uint16_t *>(p.r), static_cast<const uint16_t *>(p.w),
-                                 static_cast<const uint16_t *>(p.k), static_cast<const uint16_t *>(p.v),
-                                 static_cast<const uint16_t *>(p.kappa), static_cast<const uint16_t *>(p.a),
-                                 static_cast<const uint16_t *>(p.dy)};
-        float x[7][4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const long t = t0 + 4 * wave + e;
-            const bool ok = t < p.T;
-            const long o = tok_off(p, b, h, ok ? t : 0) + lane;
-#pragma unroll
-            for (int s = 0; s < 7; ++s) x[s][e] = ok ? bf16_lo(in[s][o]) : (s == 1 ? 1.f : 0.f);
-        }
-        float cp[4];
-        cp[0] = x[1][0];
-#pragma unroll
-        for (int e = 1; e < 4; ++e) cp[e] = cp[e - 1] * x[1][e];
-        L.carry[wave][lane] = cp[3];
-        __syncthreads();
-        float pre = 1.f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pre = q < wave ? pre * L.carry[q][lane] : pre;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 4 * wave + e;
-            const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
-            const float r = x[0][e], k = x[2][e], v = x[3][e], kap = x[4][e], a = x[5][e], dy = x[6][e];
-            const float Kp = kap * gprev, Rp = r * gam, Km = k / gam, Bm = a * kap / gam;
-            L.gam[t][lane] = gam;
-            L.kp[t][lane] = bf1(Kp); L.kpt[lane][t] = bf1(Kp);
-            L.rp[t][lane] = bf1(Rp); L.rpt[lane][t] = bf1(Rp);
-            L.km[t][lane] = bf1(Km); L.kmt[lane][t] = bf1(Km);
-            L.bm[t][lane] = bf1(Bm); L.bmt[lane][t] = bf1(Bm);
-            L.vv[t][lane] = bf1(v); L.vt[lane][t] = bf1(v);
-            L.dyy[t][lane] = bf1(dy); L.dyt[lane][t] = bf1(dy);
-            L.rr[t][lane] = bf1(r); L.kk[t][lane] = bf1(k); L.ka[t][lane] = bf1(kap);
-            L.aa[t][lane] = bf1(a); L.ww[t][lane] = bf1(x[1][e]);
-        }
-        __syncthreads();
-    }
-
-    // ---- chunk matrices (every wave forms its own copy)
-    f32x4 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
-        const bf16x4 bma = frag(L.bm, 0, 16 * kb, lane), rpa = frag(L.rp, 0, 16 * kb, lane);
-        dmkk = mma(kpa, kma, dmkk);
-        dmkkt = mma(kma, kpa, dmkkt);
-        dn = mma(kpa, bma, dn);
-        dnt = mma(bma, kpa, dnt);
-        dmkr = mma(rpa, kma, dmkr);
-        dmbr = mma(rpa, bma, dmbr);
-    }
-    dmkk = mask<true, true>(dmkk, lane);
-    dmkkt = mask<false, true>(dmkkt, lane);
-    dn = mask<true, true>(dn, lane);
-    dnt = mask<false, true>(dnt, lane);
-    dmkr = mask<true, false>(dmkr, lane);
-    dmbr = mask<true, false>(dmbr, lane);
-    const f32x4 dxt = inverse_t(dn, dnt, lane);  // D(X^T) = A operand of X
-    const f32x4 dx = inverse_t(dnt, dn, lane);   // D(X)   = A operand of X^T
-
-    // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
-    {
-        // dSh = dS_C diag(g_C); exit-state term sum_i dSh S0 over this block's values
+    float4 S0n[4], Dhn[4];
+    uint4 rawn[4];
+    auto load_chunk = [&](int cc) {
+        const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srow;
+        const float *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srow;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
+            S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4);
+            Dhn[jb] = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = threadIdx.x + kThreads * i;
+            if (q < 7 * 128) {
+                const long t = (long)cc * kC + ((q >> 3) & 15);
+                const long o = tok_off(p, b, h, t < p.T ? t : 0) + 8 * (q & 7);
+                rawn[i] = *reinterpret_cast<const uint4 *>(in[q >> 7] + o);
+            }
+        }
+    };
+    // raw pieces into the LDS input tiles (tokens x keys/values); tokens past T
+    // become neutral: w = 1, all else 0
+    auto stage_chunk = [&](long t0s) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int q = threadIdx.x + kThreads * i;
+            if (q < 7 * 128) {
+                const int s = q >> 7, t = (q >> 3) & 15, k0 = 8 * (q & 7);
+                uint4 x = rawn[i];
+                if (t0s + t >= p.T) {
+                    const unsigned fill = s == 1 ? 0x3F803F80u : 0u;  // bf16 1.0 pairs
+                    x = make_uint4(fill, fill, fill, fill);
+                }
+                short *dst = s == 0 ? &L.rr[t][k0] : s == 1 ? &L.ww[t][k0] : s == 2 ? &L.kk[t][k0]
+                           : s == 3 ? &L.vv[t][k0] : s == 4 ? &L.ka[t][k0] : s == 5 ? &L.aa[t][k0]
+                                                                              : &L.dyy[t][k0];
+                reinterpret_cast<uint2 *>(dst)[0] = make_uint2(x.x, x.y);
+                reinterpret_cast<uint2 *>(dst)[1] = make_uint2(x.z, x.w);
+            }
+        }
+    };
+    load_chunk(c_begin);
+
+    for (int c = c_begin; c < c_end; ++c) {
+        // the lane index, opaque to the compiler in each iteration: otherwise every
+        // LDS fragment address derived from it is hoisted out of the loop and held
+        // in registers for the whole loop
+        int lane_op = threadIdx.x & 63;
+        asm volatile("" : "+v"(lane_op));
+        const int lane = lane_op, lo = lane & 15, g4 = 4 * (lane >> 4);
+        const long t0 = (long)c * kC;
+        f32x4 S0[4], Dh[4];
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            S0[jb] = f32x4{S0n[jb].x, S0n[jb].y, S0n[jb].z, S0n[jb].w};
+            Dh[jb] = f32x4{Dhn[jb].x, Dhn[jb].y, Dhn[jb].z, Dhn[jb].w};
+        }
+
+        // ---- phase 1: operands.  Thread (wave, lane): tokens 4 wave .. +3, key/value `lane`
+        stage_chunk(t0);
+        __syncthreads();
+        {
+            float x[7][4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int j = 16 * jb + g4 + e;
-                Dh[jb][e] *= L.gam[kC - 1][j];
-                const float s = sum_lanes16(Dh[jb][e] * S0[jb][e]);
-                if (lo == 0) L.dlgc[wave][j] = s;
-                L.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
-                L.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
+                const int t = 4 * wave + e;
+                x[0][e] = fbf(L.rr[t][lane]); x[1][e] = fbf(L.ww[t][lane]);
+                x[2][e] = fbf(L.kk[t][lane]); x[3][e] = fbf(L.vv[t][lane]);
+                x[4][e] = fbf(L.ka[t][lane]); x[5][e] = fbf(L.aa[t][lane]);
+                x[6][e] = fbf(L.dyy[t][lane]);
+            }
+            float cp[4];
+            cp[0] = x[1][0];
+#pragma unroll
+            for (int e = 1; e < 4; ++e) cp[e] = cp[e - 1] * x[1][e];
+            L.carry[wave][lane] = cp[3];
+            __syncthreads();
+            float pre = 1.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pre = q < wave ? pre * L.carry[q][lane] : pre;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = 4 * wave + e;
+                const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
+                const float r = x[0][e], k = x[2][e], v = x[3][e], kap = x[4][e], a = x[5][e], dy = x[6][e];
+                const float ig = __builtin_amdgcn_rcpf(gam);
+                const float Kp = kap * gprev, Rp = r * gam, Km = k * ig, Bm = a * kap * ig;
+                L.gam[t][lane] = gam;
+                L.kp[t][lane] = bf1(Kp); L.kpt[lane][t] = bf1(Kp);
+                L.rp[t][lane] = bf1(Rp); L.rpt[lane][t] = bf1(Rp);
+                L.km[t][lane] = bf1(Km); L.kmt[lane][t] = bf1(Km);
+                L.bm[t][lane] = bf1(Bm); L.bmt[lane][t] = bf1(Bm);
+                L.vt[lane][t] = bf1(v);
+                L.dyt[lane][t] = bf1(dy);
+            }
+            __syncthreads();
+        }
+        if (c + 1 < c_end) load_chunk(c + 1);  // in flight during the rest of this chunk
+
+        // ---- chunk matrices (every wave forms its own copy)
+        f32x4 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
+            const bf16x4 bma = frag(L.bm, 0, 16 * kb, lane), rpa = frag(L.rp, 0, 16 * kb, lane);
+            dmkk = mma(kpa, kma, dmkk);
+            dmkkt = mma(kma, kpa, dmkkt);
+            dn = mma(kpa, bma, dn);
+            dnt = mma(bma, kpa, dnt);
+            dmkr = mma(rpa, kma, dmkr);
+            dmbr = mma(rpa, bma, dmbr);
+        }
+        dmkk = mask<true, true>(dmkk, lane);
+        dmkkt = mask<false, true>(dmkkt, lane);
+        dn = mask<true, true>(dn, lane);
+        dnt = mask<false, true>(dnt, lane);
+        dmkr = mask<true, false>(dmkr, lane);
+        dmbr = mask<true, false>(dmbr, lane);
+        const f32x4 dxt = inverse_t(dn, dnt, lane);  // D(X^T) = A operand of X
+        const f32x4 dx = inverse_t(dnt, dn, lane);   // D(X)   = A operand of X^T
+
+        // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
+        {
+            // dSh = dS_C diag(g_C); exit-state term sum_i dSh S0 over this block's values
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * jb + g4 + e;
+                    Dh[jb][e] *= L.gam[kC - 1][j];
+                    const float s = sum_lanes16(Dh[jb][e] * S0[jb][e]);
+                    if (lo == 0) L.dlgc[wave][j] = s;
+                    L.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
+                    L.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
+                }
+            }
+            const bf16x4 vb = frag(L.vt, 16 * wave, 0, lane);    // B operand of V
+            const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY
+            f32x4 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
+            f32x4 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
+            f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const bf16x4 s0b = bf4(S0[jb]), dhb = bf4(Dh[jb]);  // B operands of S0^T, dSh^T
+                z = mma(frag(L.kp, 0, 16 * jb, lane), s0b, z);      // + Kp S0^T
+                du = mma(frag(L.bm, 0, 16 * jb, lane), dhb, du);    // + Bm dSh^T
+                dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
+            }
+            du = neg(du);
+            const f32x4 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
+            const f32x4 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
+            dv = mma(bf4(dmkk), bf4(dz), dv);              // + Mkk^T dZ
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = g4 + e;
+                L.uu[t][16 * wave + lo] = bf1(u[e]);
+                L.dzz[t][16 * wave + lo] = bf1(dz[e]);
+                if (t0 + t < p.T)
+                    static_cast<uint16_t *>(p.dv)[tok_off(p, b, h, t0 + t) + 16 * wave + lo] =
+                        (uint16_t)f32_to_bf16_rne(dv[e]);
             }
         }
-        const bf16x4 vb = frag(L.vt, 16 * wave, 0, lane);    // B operand of V
-        const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY
-        f32x4 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
-        f32x4 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
-        f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            const bf16x4 s0b = bf4(S0[jb]), dhb = bf4(Dh[jb]);  // B operands of S0^T, dSh^T
-            z = mma(frag(L.kp, 0, 16 * jb, lane), s0b, z);      // + Kp S0^T
-            du = mma(frag(L.bm, 0, 16 * jb, lane), dhb, du);    // + Bm dSh^T
-            dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
-        }
-        du = neg(du);
-        const f32x4 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
-        const f32x4 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
-        dv = mma(bf4(dmkk), bf4(dz), dv);              // + Mkk^T dZ
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = g4 + e;
-            L.uu[t][16 * wave + lo] = bf1(u[e]);
-            L.dzz[t][16 * wave + lo] = bf1(dz[e]);
-            if (t0 + t < p.T)
-                static_cast<uint16_t *>(p.dv)[tok_off(p, b, h, t0 + t) + 16 * wave + lo] =
-                    (uint16_t)f32_to_bf16_rne(dv[e]);
-        }
-    }
-    __syncthreads();
+        __syncthreads();
 
-    // ---- phase 3: key block `wave` (tokens x keys 16 wave ..)
-    {
-        f32x4 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
-        f32x4 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
-        f32x4 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
+        // ---- phase 3: key block `wave` (tokens x keys 16 wave ..)
+        {
+            f32x4 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
+            f32x4 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
+            f32x4 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb) {
-            const bf16x4 ya = frag(L.dyy, 0, 16 * vb, lane), va = frag(L.vv, 0, 16 * vb, lane);
-            const bf16x4 ua = frag(L.uu, 0, 16 * vb, lane), za = frag(L.dzz, 0, 16 * vb, lane);
-            dmr = mma(ya, va, dmr);
-            dmrt = mma(va, ya, dmrt);
-            dmb = mma(ya, ua, dmb);
-            dmbt = mma(ua, ya, dmbt);
-            dmk = mma(za, va, dmk);
-            dmkt = mma(va, za, dmkt);
-            dmn = mma(za, ua, dmn);
-            dmnt = mma(ua, za, dmnt);
-            const bf16x4 dsb = frag(L.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
-            const bf16x4 s0b = frag(L.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
-            dkms = mma(va, dsb, dkms);
-            dbms = mma(ua, dsb, dbms);
-            drp = mma(ya, s0b, drp);
-            dkp = mma(za, s0b, dkp);
-        }
-        dmr = mask<true, false>(dmr, lane);
-        dmrt = mask<false, false>(dmrt, lane);
-        dmb = mask<true, false>(dmb, lane);
-        dmbt = mask<false, false>(dmbt, lane);
-        dmk = mask<true, true>(dmk, lane);
-        dmkt = mask<false, true>(dmkt, lane);
-        dmn = mask<true, true>(dmn, lane);
-        dmnt = mask<false, true>(dmnt, lane);
-        const bf16x4 rpb = frag(L.rpt, 16 * wave, 0, lane), kpb = frag(L.kpt, 16 * wave, 0, lane);
-        const bf16x4 kmb = frag(L.kmt, 16 * wave, 0, lane), bmb = frag(L.bmt, 16 * wave, 0, lane);
-        // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
-        f32x4 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
-        // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
-        f32x4 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
-        dbm = neg(dbm);
-        // dRp = dY S0 + dMkr Km + dMbr Bm
-        drp = mma(bf4(dmrt), kmb, drp);
-        drp = mma(bf4(neg(dmbt)), bmb, drp);
-        // dKp = dZ S0 + dMkk Km + dMbk Bm
-        dkp = mma(bf4(dmkt), kmb, dkp);
-        dkp = mma(bf4(neg(dmnt)), bmb, dkp);
+            for (int vb = 0; vb < 4; ++vb) {
+                const bf16x4 ya = frag(L.dyy, 0, 16 * vb, lane), va = frag(L.vv, 0, 16 * vb, lane);
+                const bf16x4 ua = frag(L.uu, 0, 16 * vb, lane), za = frag(L.dzz, 0, 16 * vb, lane);
+                dmr = mma(ya, va, dmr);
+                dmrt = mma(va, ya, dmrt);
+                dmb = mma(ya, ua, dmb);
+                dmbt = mma(ua, ya, dmbt);
+                dmk = mma(za, va, dmk);
+                dmkt = mma(va, za, dmkt);
+                dmn = mma(za, ua, dmn);
+                dmnt = mma(ua, za, dmnt);
+                const bf16x4 dsb = frag(L.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
+                const bf16x4 s0b = frag(L.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
+                dkms = mma(va, dsb, dkms);
+                dbms = mma(ua, dsb, dbms);
+                drp = mma(ya, s0b, drp);
+                dkp = mma(za, s0b, dkp);
+            }
+            dmr = mask<true, false>(dmr, lane);
+            dmrt = mask<false, false>(dmrt, lane);
+            dmb = mask<true, false>(dmb, lane);
+            dmbt = mask<false, false>(dmbt, lane);
+            dmk = mask<true, true>(dmk, lane);
+            dmkt = mask<false, true>(dmkt, lane);
+            dmn = mask<true, true>(dmn, lane);
+            dmnt = mask<false, true>(dmnt, lane);
+            const bf16x4 rpb = frag(L.rpt, 16 * wave, 0, lane), kpb = frag(L.kpt, 16 * wave, 0, lane);
+            const bf16x4 kmb = frag(L.kmt, 16 * wave, 0, lane), bmb = frag(L.bmt, 16 * wave, 0, lane);
+            // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
+            f32x4 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
+            // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
+            f32x4 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
+            dbm = neg(dbm);
+            // dRp = dY S0 + dMkr Km + dMbr Bm
+            drp = mma(bf4(dmrt), kmb, drp);
+            drp = mma(bf4(neg(dmbt)), bmb, drp);
+            // dKp = dZ S0 + dMkk Km + dMbk Bm
+            dkp = mma(bf4(dmkt), kmb, dkp);
+            dkp = mma(bf4(neg(dmnt)), bmb, dkp);
 
-        // elementwise: lane (token g4 + e, key 16 wave + lo)
-        const int j = 16 * wave + lo;
-        float csum = 0.f;
+            // elementwise: lane (token g4 + e, key 16 wave + lo)
+            const int j = 16 * wave + lo;
+            float csum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = g4 + e;
-            const float gam = L.gam[t][j], gprev = t ? L.gam[t - 1][j] : 1.f;
-            const float r = fbf(L.rr[t][j]), k = fbf(L.kk[t][j]), kap = fbf(L.ka[t][j]);
-            const float a = fbf(L.aa[t][j]);
-            const float Kp = kap * gprev, Rp = r * gam, Km = k / gam, Bm = a * kap / gam;
-            const float dr = drp[e] * gam, dk = dkm[e] / gam, db = dbm[e] / gam;
-            const float da = db * kap, dkap = dkp[e] * gprev + db * a;
-            L.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
-            L.dkk[t][j] = dkp[e] * Kp;
-            csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
-            if (t0 + t < p.T) {
-                const long o = tok_off(p, b, h, t0 + t) + j;
-                static_cast<uint16_t *>(p.dr)[o] = (uint16_t)f32_to_bf16_rne(dr);
-                static_cast<uint16_t *>(p.dk)[o] = (uint16_t)f32_to_bf16_rne(dk);
-                static_cast<uint16_t *>(p.da)[o] = (uint16_t)f32_to_bf16_rne(da);
-                static_cast<uint16_t *>(p.dkappa)[o] = (uint16_t)f32_to_bf16_rne(dkap);
+            for (int e = 0; e < 4; ++e) {
+                const int t = g4 + e;
+                const float gam = L.gam[t][j], gprev = t ? L.gam[t - 1][j] : 1.f;
+                const float r = fbf(L.rr[t][j]), k = fbf(L.kk[t][j]), kap = fbf(L.ka[t][j]);
+                const float a = fbf(L.aa[t][j]);
+                const float ig = __builtin_amdgcn_rcpf(gam);
+                const float Kp = kap * gprev, Rp = r * gam, Km = k * ig, Bm = a * kap * ig;
+                const float dr = drp[e] * gam, dk = dkm[e] * ig, db = dbm[e] * ig;
+                const float da = db * kap, dkap = dkp[e] * gprev + db * a;
+                L.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
+                L.dkk[t][j] = dkp[e] * Kp;
+                csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
+                if (t0 + t < p.T) {
+                    const long o = tok_off(p, b, h, t0 + t) + j;
+                    static_cast<uint16_t *>(p.dr)[o] = (uint16_t)f32_to_bf16_rne(dr);
+                    static_cast<uint16_t *>(p.dk)[o] = (uint16_t)f32_to_bf16_rne(dk);
+                    static_cast<uint16_t *>(p.da)[o] = (uint16_t)f32_to_bf16_rne(da);
+                    static_cast<uint16_t *>(p.dkappa)[o] = (uint16_t)f32_to_bf16_rne(dkap);
+                }
+            }
+            L.dlgc[4 + (lane >> 4)][j] = csum;
+        }
+        __syncthreads();
+
+        // ---- phase 4: decay gradients, a reverse sum over the chunk's tokens per key
+        if (wave == 0) {
+            const int j = lane;
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc += L.dlgc[q][j];
+#pragma unroll
+            for (int t = kC - 1; t >= 0; --t) {
+                acc += L.dlg[t][j] + (t + 1 < kC ? L.dkk[t + 1][j] : 0.f);
+                if (t0 + t < p.T)
+                    static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
+                        (uint16_t)f32_to_bf16_rne(acc * __builtin_amdgcn_rcpf(fbf(L.ww[t][j])));
             }
         }
-        L.dlgc[4 + (lane >> 4)][j] = csum;
-    }
-    __syncthreads();
-
-    // ---- phase 4: decay gradients, a reverse sum over the chunk's tokens per key
-    if (wave == 0) {
-        const int j = lane;
-        float acc = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) acc += L.dlgc[q][j];
-#pragma unroll
-        for (int t = kC - 1; t >= 0; --t) {
-            acc += L.dlg[t][j] + (t + 1 < kC ? L.dkk[t + 1][j] : 0.f);
-            if (t0 + t < p.T)
-                static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
-                    (uint16_t)f32_to_bf16_rne(acc / fbf(L.ww[t][j]));
-        }
+        __syncthreads();  // the next chunk's operands overwrite LDS
     }
 }
 
@@ -507,8 +577,9 @@ hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream) {
     hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)heads), dim3(kThreads), 0, stream, p);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(heads * nch)), dim3(kThreads), 0, stream,
-                       p);
+    const long ngrp = (nch + kGradChunks - 1) / kGradChunks;
+    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(heads * ngrp)), dim3(kThreads), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
