@@ -81,7 +81,9 @@ __device__ __forceinline__ bf16x4 bf4(f32x4 x) {
     const u32x2 v = {cvt2(x[0], x[1]), cvt2(x[2], x[3])};
     return __builtin_bit_cast(bf16x4, v);
 }
-__device__ __forceinline__ short bf1(float x) { return (short)f32_to_bf16_rne(x); }
+// one float -> bf16 bits, round to nearest even (the same hardware conversion)
+__device__ __forceinline__ short bf1(float x) { return (short)(cvt2(x, 0.f) & 0xffffu); }
+__device__ __forceinline__ uint16_t bf1u(float x) { return (uint16_t)(cvt2(x, 0.f) & 0xffffu); }
 __device__ __forceinline__ float fbf(short s) { return __uint_as_float(((uint32_t)(uint16_t)s) << 16); }
 __device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f32x4 neg(f32x4 x) { return f32x4{-x[0], -x[1], -x[2], -x[3]}; }
@@ -467,7 +469,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                 L.dzz[t][16 * wave + lo] = bf1(dz[e]);
                 if (t0 + t < p.T)
                     static_cast<uint16_t *>(p.dv)[tok_off(p, b, h, t0 + t) + 16 * wave + lo] =
-                        (uint16_t)f32_to_bf16_rne(dv[e]);
+                        bf1u(dv[e]);
             }
         }
         __syncthreads();
@@ -536,10 +538,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                 csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
                 if (t0 + t < p.T) {
                     const long o = tok_off(p, b, h, t0 + t) + j;
-                    static_cast<uint16_t *>(p.dr)[o] = (uint16_t)f32_to_bf16_rne(dr);
-                    static_cast<uint16_t *>(p.dk)[o] = (uint16_t)f32_to_bf16_rne(dk);
-                    static_cast<uint16_t *>(p.da)[o] = (uint16_t)f32_to_bf16_rne(da);
-                    static_cast<uint16_t *>(p.dkappa)[o] = (uint16_t)f32_to_bf16_rne(dkap);
+                    static_cast<uint16_t *>(p.dr)[o] = bf1u(dr);
+                    static_cast<uint16_t *>(p.dk)[o] = bf1u(dk);
+                    static_cast<uint16_t *>(p.da)[o] = bf1u(da);
+                    static_cast<uint16_t *>(p.dkappa)[o] = bf1u(dkap);
                 }
             }
             L.dlgc[4 + (lane >> 4)][j] = csum;
@@ -557,7 +559,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                 acc += L.dlg[t][j] + (t + 1 < kC ? L.dkk[t + 1][j] : 0.f);
                 if (t0 + t < p.T)
                     static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
-                        (uint16_t)f32_to_bf16_rne(acc * __builtin_amdgcn_rcpf(fbf(L.ww[t][j])));
+                        bf1u(acc * __builtin_amdgcn_rcpf(fbf(L.ww[t][j])));
             }
         }
         __syncthreads();  // the next chunk's operands overwrite LDS
