@@ -93,6 +93,14 @@ __device__ __forceinline__ bf16x4 frag(const short (*m)[S], int row0, int col0, 
     return *reinterpret_cast<const bf16x4 *>(&m[row0 + (lane & 15)][col0 + 4 * (lane >> 4)]);
 }
 
+// B operand of a 16-row tile stored row-major (rows = the contraction index):
+// rows g4 .. g4+3 of column col0 + lo, four 2-byte reads
+template <int S>
+__device__ __forceinline__ bf16x4 colfrag(const short (*m)[S], int col0, int lane) {
+    const int c = col0 + (lane & 15), r = 4 * (lane >> 4);
+    return bf16x4{m[r][c], m[r + 1][c], m[r + 2][c], m[r + 3][c]};
+}
+
 // Keep the entries of a result tile D[4g+e][lo] that satisfy a triangle:
 // kLower: col <= row (kStrict: col < row); else row <= col (kStrict: row < col).
 template <bool kLower, bool kStrict>
@@ -139,8 +147,7 @@ __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, lo
 // ---------------------------------------------------------------- reverse chain
 struct ChainLds {
     short kp[kC][kSK], rp[kC][kSK], bm[kC][kSK];  // tokens x keys
-    short kpt[kN][kST], rpt[kN][kST];             // keys x tokens
-    short dyt[kN][kST];                           // values x tokens
+    short dyy[kC][kSK];                           // tokens x values
     float carry[4][kN];                           // decay product of each wave's 4 tokens
     float gc[kN];                                 // decay total of the chunk
 };
@@ -218,9 +225,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
             L.kp[t][lane] = bf1(Kp);
             L.rp[t][lane] = bf1(Rp);
             L.bm[t][lane] = bf1(Bm);
-            L.kpt[lane][t] = bf1(Kp);
-            L.rpt[lane][t] = bf1(Rp);
-            L.dyt[lane][t] = bf1(dv[e]);
+            L.dyy[t][lane] = bf1(dv[e]);
         }
         __syncthreads();
 
@@ -252,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
             for (int e = 0; e < 4; ++e) St[jb][e] *= L.gc[16 * jb + g4 + e];
             Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
         }
-        const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY (tokens x values)
+        const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY (tokens x values)
         f32x4 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) rhs = mma(frag(L.bm, 0, 16 * jb, lane), Sb[jb], rhs);  // + Bm dSh^T
@@ -260,8 +265,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         const bf16x4 dzb = bf4(neg(up));
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-            St[jb] = mma(frag(L.rpt, 16 * jb, 0, lane), dyb, St[jb]);  // + Rp^T dY
-            St[jb] = mma(frag(L.kpt, 16 * jb, 0, lane), dzb, St[jb]);  // + Kp^T dZ
+            St[jb] = mma(colfrag(L.rp, 16 * jb, lane), dyb, St[jb]);  // + Rp^T dY (A of Rp^T)
+            St[jb] = mma(colfrag(L.kp, 16 * jb, lane), dzb, St[jb]);  // + Kp^T dZ
         }
         __syncthreads();  // the next chunk's operands overwrite LDS
     }
@@ -276,19 +281,24 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
 // ------------------------------------------------------- per-chunk gradients
 struct GradLds {
     short kp[kC][kSK], rp[kC][kSK], km[kC][kSK], bm[kC][kSK];   // tokens x keys
-    short kpt[kN][kST], rpt[kN][kST], kmt[kN][kST], bmt[kN][kST];  // keys x tokens
     short vv[kC][kSK], dyy[kC][kSK], uu[kC][kSK], dzz[kC][kSK];  // tokens x values
-    short vt[kN][kST], dyt[kN][kST];                             // values x tokens
-    short s0t[kN][kSK], dsht[kN][kSK];                           // keys x values
+    union {
+        struct {
+            short s0t[kN][kSK], dsht[kN][kSK];  // keys x values (phases 2-3)
+        } m;
+        struct {                  // phase 3's elementwise part onwards
+            float dlg[kC][kN];    // decay-gradient terms of each token
+            float dkk[kC][kN];    // dKp * Kp (belongs to the previous token's decay)
+        } e;
+    } u;
     short rr[kC][kSK], kk[kC][kSK], ka[kC][kSK], aa[kC][kSK], ww[kC][kSK];  // raw inputs
     float gam[kC][kN];       // cumulative decay within the chunk
-    float dlg[kC][kN];       // decay-gradient terms of each token
-    float dkk[kC][kN];       // dKp * Kp (belongs to the previous token's decay)
     float dlgc[8][kN];       // exit-state term: partial sums (4 value blocks, 4 token groups)
     float carry[4][kN];
 };
 
-__global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_grad_kernel(
+    BackwardArgs p) {
     __shared__ GradLds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lo = lane & 15, g4 = 4 * (lane >> 4);
@@ -377,9 +387,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * wave + e;
                 x[0][e] = fbf(L.rr[t][lane]); x[1][e] = fbf(L.ww[t][lane]);
-                x[2][e] = fbf(L.kk[t][lane]); x[3][e] = fbf(L.vv[t][lane]);
+                x[2][e] = fbf(L.kk[t][lane]);
                 x[4][e] = fbf(L.ka[t][lane]); x[5][e] = fbf(L.aa[t][lane]);
-                x[6][e] = fbf(L.dyy[t][lane]);
             }
             float cp[4];
             cp[0] = x[1][0];
@@ -394,16 +403,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * wave + e;
                 const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
-                const float r = x[0][e], k = x[2][e], v = x[3][e], kap = x[4][e], a = x[5][e], dy = x[6][e];
+                const float r = x[0][e], k = x[2][e], kap = x[4][e], a = x[5][e];
                 const float ig = __builtin_amdgcn_rcpf(gam);
                 const float Kp = kap * gprev, Rp = r * gam, Km = k * ig, Bm = a * kap * ig;
                 L.gam[t][lane] = gam;
-                L.kp[t][lane] = bf1(Kp); L.kpt[lane][t] = bf1(Kp);
-                L.rp[t][lane] = bf1(Rp); L.rpt[lane][t] = bf1(Rp);
-                L.km[t][lane] = bf1(Km); L.kmt[lane][t] = bf1(Km);
-                L.bm[t][lane] = bf1(Bm); L.bmt[lane][t] = bf1(Bm);
-                L.vt[lane][t] = bf1(v);
-                L.dyt[lane][t] = bf1(dy);
+                L.kp[t][lane] = bf1(Kp);
+                L.rp[t][lane] = bf1(Rp);
+                L.km[t][lane] = bf1(Km);
+                L.bm[t][lane] = bf1(Bm);
             }
             __syncthreads();
         }
@@ -442,12 +449,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                     Dh[jb][e] *= L.gam[kC - 1][j];
                     const float s = sum_lanes16(Dh[jb][e] * S0[jb][e]);
                     if (lo == 0) L.dlgc[wave][j] = s;
-                    L.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
-                    L.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
+                    L.u.m.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
+                    L.u.m.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
                 }
             }
-            const bf16x4 vb = frag(L.vt, 16 * wave, 0, lane);    // B operand of V
-            const bf16x4 dyb = frag(L.dyt, 16 * wave, 0, lane);  // B operand of dY
+            const bf16x4 vb = colfrag(L.vv, 16 * wave, lane);    // B operand of V
+            const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY
             f32x4 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
             f32x4 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
             f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
@@ -491,8 +498,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                 dmkt = mma(va, za, dmkt);
                 dmn = mma(za, ua, dmn);
                 dmnt = mma(ua, za, dmnt);
-                const bf16x4 dsb = frag(L.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
-                const bf16x4 s0b = frag(L.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
+                const bf16x4 dsb = frag(L.u.m.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
+                const bf16x4 s0b = frag(L.u.m.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
                 dkms = mma(va, dsb, dkms);
                 dbms = mma(ua, dsb, dbms);
                 drp = mma(ya, s0b, drp);
@@ -506,8 +513,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
             dmkt = mask<false, true>(dmkt, lane);
             dmn = mask<true, true>(dmn, lane);
             dmnt = mask<false, true>(dmnt, lane);
-            const bf16x4 rpb = frag(L.rpt, 16 * wave, 0, lane), kpb = frag(L.kpt, 16 * wave, 0, lane);
-            const bf16x4 kmb = frag(L.kmt, 16 * wave, 0, lane), bmb = frag(L.bmt, 16 * wave, 0, lane);
+            const bf16x4 rpb = colfrag(L.rp, 16 * wave, lane), kpb = colfrag(L.kp, 16 * wave, lane);
+            const bf16x4 kmb = colfrag(L.km, 16 * wave, lane), bmb = colfrag(L.bm, 16 * wave, lane);
             // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
             f32x4 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
             // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
@@ -519,6 +526,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
             // dKp = dZ S0 + dMkk Km + dMbk Bm
             dkp = mma(bf4(dmkt), kmb, dkp);
             dkp = mma(bf4(neg(dmnt)), bmb, dkp);
+            __syncthreads();  // the state tiles are read: their LDS is reused below
 
             // elementwise: lane (token g4 + e, key 16 wave + lo)
             const int j = 16 * wave + lo;
@@ -533,8 +541,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
                 const float Kp = kap * gprev, Rp = r * gam, Km = k * ig, Bm = a * kap * ig;
                 const float dr = drp[e] * gam, dk = dkm[e] * ig, db = dbm[e] * ig;
                 const float da = db * kap, dkap = dkp[e] * gprev + db * a;
-                L.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
-                L.dkk[t][j] = dkp[e] * Kp;
+                L.u.e.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
+                L.u.e.dkk[t][j] = dkp[e] * Kp;
                 csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
                 if (t0 + t < p.T) {
                     const long o = tok_off(p, b, h, t0 + t) + j;
@@ -556,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_kernel(BackwardArgs p) {
             for (int q = 0; q < 8; ++q) acc += L.dlgc[q][j];
 #pragma unroll
             for (int t = kC - 1; t >= 0; --t) {
-                acc += L.dlg[t][j] + (t + 1 < kC ? L.dkk[t + 1][j] : 0.f);
+                acc += L.u.e.dlg[t][j] + (t + 1 < kC ? L.u.e.dkk[t + 1][j] : 0.f);
                 if (t0 + t < p.T)
                     static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
                         bf1u(acc * __builtin_amdgcn_rcpf(fbf(L.ww[t][j])));
