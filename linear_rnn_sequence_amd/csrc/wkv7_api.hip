@@ -390,6 +390,7 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     const size_t ws_need = chunked ? rwkv7_wkv_backward_workspace(B, T, H, N, dt, use) : 0;
     if (chunked) {
         if (ws_need == 0) return RWKV7_ERR_SHAPE;
+        if (!backward_chunked_grid_ok(B, T, H)) return RWKV7_ERR_SHAPE;
         if (!workspace || workspace_bytes < ws_need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
     }

@@ -581,6 +581,12 @@ size_t backward_chunked_workspace_bytes(int B, int T, int H) {
     return (size_t)B * H * nch * kN * kN * sizeof(float);
 }
 
+bool backward_chunked_grid_ok(int B, int T, int H) {
+    const long heads = (long)B * H;
+    const long ngrp = ((long)(T + kC - 1) / kC + kGradChunks - 1) / kGradChunks;
+    return heads <= 0x7fffffffL && heads * ngrp <= 0x7fffffffL;
+}
+
 hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream) {
     const long heads = (long)p.B * p.H;
     const long nch = (p.T + kC - 1) / kC;

@@ -89,6 +89,9 @@ hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
 // every chunk's gradients in parallel; needs ds_ws of the size below
 hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream);
 size_t backward_chunked_workspace_bytes(int B, int T, int H);
+// whether the chunked backward's launch grids fit (B*H workgroups, and B*H
+// times the number of 8-chunk groups)
+bool backward_chunked_grid_ok(int B, int T, int H);
 // S_T for T == 0: copy s0 (or zeros) into s_out.
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream);
 

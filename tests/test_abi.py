@@ -288,3 +288,7 @@ def test_backward_chunked_workspace_codes():
     assert bwd(T=T, algo=2, dt=0) == 4                        # chunked is bf16 only
     assert bwd(T=T, algo=9) == 3
     assert bwd(T=0, algo=2, ds0=None, ck=None) == 0           # nothing to do
+    # gradient grid of B*H x ceil(chunks / 8) workgroups past 2^31: refused up front
+    Bb, Hb, Tb = 1 << 15, 1 << 10, 1 << 13
+    needb = L.rwkv7_wkv_backward_workspace(Bb, Tb, Hb, 64, 1, 2)
+    assert bwd(B=Bb, H=Hb, T=Tb, algo=2, ws=ws, ws_bytes=needb) == 2
