@@ -141,20 +141,20 @@ __global__ __launch_bounds__(ScanShape<N>::kThreads) void scan_kernel(ForwardArg
 
     typename L::T xr, xk, xv, xkap, xa;
     typename LW::T xw;
+    // the loads of a round, without a branch around them (one that assigns the
+    // registers on two paths keeps them in scratch memory): a token past T
+    // reads token T-1 and is zeroed at use
+    bool x_ok = false;
     auto issue = [&](int chunk) {
         const int t = chunk * kTC + s_t;
-        if (t < T) {
-            const long off = tok0 + (long)t * HN + 4 * s_q;
-            xr = L::load(p.r, off);
-            xw = LW::load(p.w, off);
-            xk = L::load(p.k, off);
-            xv = L::load(p.v, off);
-            xkap = p.fused ? L::zero() : L::load(p.kappa, off);
-            xa = L::load(p.a, off);
-        } else {
-            xr = xk = xv = xkap = xa = L::zero();
-            xw = LW::zero();
-        }
+        x_ok = t < T;
+        const long off = tok0 + (long)min(t, T - 1) * HN + 4 * s_q;
+        xr = L::load(p.r, off);
+        xw = LW::load(p.w, off);
+        xk = L::load(p.k, off);
+        xv = L::load(p.v, off);
+        xkap = L::load(p.fused ? p.k : p.kappa, off);  // (unused when fused)
+        xa = L::load(p.a, off);
     };
 
     const int nchunks = (T + kTC - 1) / kTC;
@@ -165,9 +165,10 @@ __global__ __launch_bounds__(ScanShape<N>::kThreads) void scan_kernel(ForwardArg
         if (p.s_ckpt)  // the state before token ch * kTC
             st_rows(p.s_ckpt + ((long)bh * nchunks + ch) * N * N, S);
         // ---- stage this chunk's vectors ----
-        const float4 r4 = L::widen(xr), w4 = LW::widen(xw);
-        float4 k4 = L::widen(xk), kap4 = L::widen(xkap);
-        const float4 v4 = L::widen(xv), a4 = L::widen(xa);
+        const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+        const float4 r4 = x_ok ? L::widen(xr) : z4, w4 = x_ok ? LW::widen(xw) : z4;
+        float4 k4 = x_ok ? L::widen(xk) : z4, kap4 = x_ok ? L::widen(xkap) : z4;
+        const float4 v4 = x_ok ? L::widen(xv) : z4, a4 = x_ok ? L::widen(xa) : z4;
         if (p.fused) {
             // kappa = normalise(k * k_k) over the token's N channels (its staging
             // lanes); k <- k + k (a-1) k_a
@@ -195,8 +196,14 @@ __global__ __launch_bounds__(ScanShape<N>::kThreads) void scan_kernel(ForwardArg
         if (ch + 1 < nchunks) issue(ch + 1);
 
         // ---- the recurrence over this chunk's tokens ----
-        for (int tt = 0; tt < tl; ++tt) {
+        // a token's columns are read from LDS one token ahead, alternating
+        // between two register sets, so the reads overlap the previous token
+        struct Cols {
             float kap[kCols], w[kCols], bb[kCols], kk[kCols], wr[kCols];
+            float2 vv;
+            float4 sc;
+        };
+        auto ld_tok = [&](Cols &d, int tt) {
             auto ld_cols = [&](const float (&arr)[kTC][N], float (&dst)[kCols]) {
 #pragma unroll
                 for (int q = 0; q < kCols / 4; ++q) {
@@ -204,33 +211,53 @@ __global__ __launch_bounds__(ScanShape<N>::kThreads) void scan_kernel(ForwardArg
                     dst[4 * q] = x.x; dst[4 * q + 1] = x.y; dst[4 * q + 2] = x.z; dst[4 * q + 3] = x.w;
                 }
             };
-            ld_cols(st.kap, kap);
-            ld_cols(st.w, w);
-            ld_cols(st.b, bb);
-            ld_cols(st.k, kk);
-            ld_cols(st.wr, wr);
-            const float2 vv = *reinterpret_cast<const float2 *>(&st.v[tt][i0]);
-            const float4 sc = st.sc[tt];
+            ld_cols(st.kap, d.kap);
+            ld_cols(st.w, d.w);
+            ld_cols(st.b, d.bb);
+            ld_cols(st.k, d.kk);
+            ld_cols(st.wr, d.wr);
+            d.vv = *reinterpret_cast<const float2 *>(&st.v[tt][i0]);
+            d.sc = st.sc[tt];
+        };
+        auto step = [&](const Cols &x, int tt) {
             float pu0 = 0.f, pu1 = 0.f, py0 = 0.f, py1 = 0.f;
 #pragma unroll
             for (int e = 0; e < kCols; ++e) {
-                pu0 += S[0][e] * kap[e];
-                pu1 += S[1][e] * kap[e];
-                py0 += S[0][e] * wr[e];
-                py1 += S[1][e] * wr[e];
+                pu0 += S[0][e] * x.kap[e];
+                pu1 += S[1][e] * x.kap[e];
+                py0 += S[0][e] * x.wr[e];
+                py1 += S[1][e] * x.wr[e];
             }
             pu0 = sum_lanes8(pu0);
             pu1 = sum_lanes8(pu1);
             py0 = sum_lanes8(py0);
             py1 = sum_lanes8(py1);
-            const float y0 = py0 + vv.x * sc.x - pu0 * sc.y;
-            const float y1 = py1 + vv.y * sc.x - pu1 * sc.y;
+            const float y0 = py0 + x.vv.x * x.sc.x - pu0 * x.sc.y;
+            const float y1 = py1 + x.vv.y * x.sc.x - pu1 * x.sc.y;
 #pragma unroll
             for (int e = 0; e < kCols; ++e) {
-                S[0][e] = S[0][e] * w[e] - pu0 * bb[e] + vv.x * kk[e];
-                S[1][e] = S[1][e] * w[e] - pu1 * bb[e] + vv.y * kk[e];
+                S[0][e] = S[0][e] * x.w[e] - pu0 * x.bb[e] + x.vv.x * x.kk[e];
+                S[1][e] = S[1][e] * x.w[e] - pu1 * x.bb[e] + x.vv.y * x.kk[e];
             }
             if (c == 0) *reinterpret_cast<float2 *>(&st.ybuf[tt][i0]) = make_float2(y0, y1);
+        };
+        if constexpr (N == 64) {
+            Cols ca, cb;
+            ld_tok(ca, 0);
+            for (int tt = 0; tt < tl; tt += 2) {
+                ld_tok(cb, min(tt + 1, kTC - 1));
+                step(ca, tt);
+                if (tt + 1 < tl) {
+                    ld_tok(ca, min(tt + 2, kTC - 1));
+                    step(cb, tt + 1);
+                }
+            }
+        } else {  // N = 128: two sets of 16 columns would not fit in registers
+            for (int tt = 0; tt < tl; ++tt) {
+                Cols cx;
+                ld_tok(cx, tt);
+                step(cx, tt);
+            }
         }
         __syncthreads();
 
