@@ -371,6 +371,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         asm volatile("" : "+v"(lane_op));
         const int lane = lane_op, lo = lane & 15, g4 = 4 * (lane >> 4);
         const long t0 = (long)c * kC;
+        // outputs: element offset of the chunk's first token and the token stride;
+        // every chunk but a ragged last one stores all 16 tokens without a test
+        const long tb = tok_off(p, b, h, t0), TS = (long)p.H * kN;
+        const bool full = t0 + kC <= p.T;
+        auto put4 = [&](void *base, long off, const float (&x)[4]) {  // tokens g4 .. g4+3
+            uint16_t *q = static_cast<uint16_t *>(base) + tb + off;
+            if (full) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) q[(g4 + e) * TS] = bf1u(x[e]);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t0 + g4 + e < p.T) q[(g4 + e) * TS] = bf1u(x[e]);
+            }
+        };
         f32x4 S0[4], Dh[4];
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
@@ -474,10 +489,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 const int t = g4 + e;
                 L.uu[t][16 * wave + lo] = bf1(u[e]);
                 L.dzz[t][16 * wave + lo] = bf1(dz[e]);
-                if (t0 + t < p.T)
-                    static_cast<uint16_t *>(p.dv)[tok_off(p, b, h, t0 + t) + 16 * wave + lo] =
-                        bf1u(dv[e]);
             }
+            const float dvv[4] = {dv[0], dv[1], dv[2], dv[3]};
+            put4(p.dv, 16 * wave + lo, dvv);
         }
         __syncthreads();
 
@@ -531,6 +545,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             // elementwise: lane (token g4 + e, key 16 wave + lo)
             const int j = 16 * wave + lo;
             float csum = 0.f;
+            float o_dr[4], o_dk[4], o_da[4], o_dkap[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = g4 + e;
@@ -544,30 +559,45 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 L.u.e.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
                 L.u.e.dkk[t][j] = dkp[e] * Kp;
                 csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
-                if (t0 + t < p.T) {
-                    const long o = tok_off(p, b, h, t0 + t) + j;
-                    static_cast<uint16_t *>(p.dr)[o] = bf1u(dr);
-                    static_cast<uint16_t *>(p.dk)[o] = bf1u(dk);
-                    static_cast<uint16_t *>(p.da)[o] = bf1u(da);
-                    static_cast<uint16_t *>(p.dkappa)[o] = bf1u(dkap);
-                }
+                o_dr[e] = dr; o_dk[e] = dk; o_da[e] = da; o_dkap[e] = dkap;
             }
             L.dlgc[4 + (lane >> 4)][j] = csum;
+            put4(p.dr, j, o_dr);
+            put4(p.dk, j, o_dk);
+            put4(p.da, j, o_da);
+            put4(p.dkappa, j, o_dkap);
         }
         __syncthreads();
 
         // ---- phase 4: decay gradients, a reverse sum over the chunk's tokens per key
         if (wave == 0) {
             const int j = lane;
-            float acc = 0.f;
+            // every LDS value first, then the sums
+            float dl[kC], dkn[kC], wv[kC], part[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) acc += L.dlgc[q][j];
+            for (int t = 0; t < kC; ++t) {
+                dl[t] = L.u.e.dlg[t][j];
+                dkn[t] = L.u.e.dkk[t][j];
+                wv[t] = fbf(L.ww[t][j]);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) part[q] = L.dlgc[q][j];
+            float acc = ((part[0] + part[1]) + (part[2] + part[3])) +
+                        ((part[4] + part[5]) + (part[6] + part[7]));
+            float dwv[kC];
 #pragma unroll
             for (int t = kC - 1; t >= 0; --t) {
-                acc += L.u.e.dlg[t][j] + (t + 1 < kC ? L.u.e.dkk[t + 1][j] : 0.f);
-                if (t0 + t < p.T)
-                    static_cast<uint16_t *>(p.dw)[tok_off(p, b, h, t0 + t) + j] =
-                        bf1u(acc * __builtin_amdgcn_rcpf(fbf(L.ww[t][j])));
+                acc += dl[t] + (t + 1 < kC ? dkn[t + 1] : 0.f);
+                dwv[t] = acc * __builtin_amdgcn_rcpf(wv[t]);
+            }
+            uint16_t *q = static_cast<uint16_t *>(p.dw) + tb + j;
+            if (full) {
+#pragma unroll
+                for (int t = 0; t < kC; ++t) q[t * TS] = bf1u(dwv[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < kC; ++t)
+                    if (t0 + t < p.T) q[t * TS] = bf1u(dwv[t]);
             }
         }
         __syncthreads();  // the next chunk's operands overwrite LDS
