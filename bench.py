@@ -658,6 +658,27 @@ def main():
         par["prefill_state_rel_err"] = float(np.abs(p_s_first - s_ref).max()
                                              / np.abs(s_ref).max())
         par["prefill_checked"] = "all outputs"
+        if long_shape and not args.fused and not args.bidir:
+            # the same sequence as 32 chained calls of 2048 tokens (each too short to be
+            # split into segments), the state passed between them: against the oracle
+            # and against the single call
+            seg_T = 2048
+            st = torch.zeros((PREFILL["B"], PREFILL["H"], N, N), dtype=torch.float32, device=dev)
+            ys = []
+            for s_i in range(PREFILL["T"] // seg_T):
+                sl = slice(s_i * seg_T, (s_i + 1) * seg_T)
+                ys.append(wkv.forward(*(pd[n][:, sl].contiguous() for n in NAMES), s0=st,
+                                      s_out=st, algo=args.prefill_algo)[0])
+            torch.cuda.synchronize()
+            y_chain = torch.cat(ys, 1).float().cpu().numpy()
+            par["prefill_chained_y_rel_err"] = float(np.abs(y_chain - y_ref).max()
+                                                     / np.abs(y_ref).max())
+            par["prefill_chained_state_rel_err"] = float(
+                np.abs(st.cpu().numpy() - s_ref).max() / np.abs(s_ref).max())
+            par["prefill_drift_single_vs_chained"] = float(np.abs(p_y_first - y_chain).max()
+                                                           / np.abs(y_chain).max())
+            par["prefill_chained"] = f"{PREFILL['T'] // seg_T} calls of {seg_T} tokens"
+            del y_chain, ys
         del y_ref, s_ref
     if do_decode and not args.no_cpu_baseline:
         errs = []
