@@ -69,8 +69,8 @@ def parse():
     ap.add_argument("--bidir", action="store_true",
                     help="time the bidirectional forward (needs --only prefill)")
     ap.add_argument("--decay-f32", action="store_true",
-                    help="prefill with the decay w in float32 (other vectors bf16); "
-                         "needs --only prefill")
+                    help="the decay w in float32, other vectors bf16 (--only prefill: "
+                         "long context; --only train: the training step, dw float32)")
     return ap.parse_args()
 
 
@@ -227,6 +227,8 @@ def bench_train(args, torch, wkv, synth, dev):
     px = synth.config_inputs(2)
     bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     ins = [bf(px[n]) for n in NAMES]
+    if args.decay_f32:  # the same decays held in float32 (dtype RWKV7_DT_BF16_W32)
+        ins[1] = ins[1].float()
     dy_bits, ds_T = synth.cotangents(B, T, H, seed=102, dtype="bf16")
     dy, dst = bf(dy_bits), torch.from_numpy(ds_T).to(dev)
     ws_bytes = wkv.forward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
@@ -234,7 +236,7 @@ def bench_train(args, torch, wkv, synth, dev):
     y = torch.empty_like(ins[0])
     s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=dev)
     ck = torch.empty((B, H, (T + 15) // 16, N, N), dtype=torch.float32, device=dev)
-    grads = tuple(torch.empty_like(ins[0]) for _ in range(6))
+    grads = tuple(torch.empty_like(ins[1] if i == 1 else ins[0]) for i in range(6))
     ds0 = torch.empty_like(s_out)
     bws = wkv.backward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.bwd_algo)
     bwork = torch.empty(max(bws, 16), dtype=torch.uint8, device=dev)
@@ -281,8 +283,9 @@ def bench_train(args, torch, wkv, synth, dev):
     bwd_flops = work * BWD_FLOPS_PER_TOKEN_HEAD
     tf = bwd_flops / (bwd_ms / 1e3) / 1e12
     nck = (T + 15) // 16
-    fwd_bytes = work * 7 * N * 2 + B * H * N * N * 4 * (1 + nck)
-    bwd_bytes = work * 13 * N * 2 + B * H * N * N * 4 * (2 + nck)
+    wx = 2 if args.decay_f32 else 0  # extra bytes per decay element (w in, dw out)
+    fwd_bytes = work * (7 * 2 + wx) * N + B * H * N * N * 4 * (1 + nck)
+    bwd_bytes = work * (13 * 2 + 2 * wx) * N + B * H * N * N * 4 * (2 + nck)
     src = source_hash("wkv7_backward_chunked.hip" if chunked_bwd else "wkv7_backward.hip",
                       "wkv7_device.h")
     out = {
@@ -297,12 +300,14 @@ def bench_train(args, torch, wkv, synth, dev):
                                 "B8 T4096 H40 N64, no epilogue"),
                    "B": B, "T": T, "H": H, "N": N, "forward_algo": args.prefill_algo,
                    "backward_algo": "chunked" if chunked_bwd else "scan",
+                   "decay_dtype": "f32" if args.decay_f32 else "bf16",
                    "state_dtype": "f32"},
         "roofline": ({"kernel": "wkv7 chunked backward (reverse chain + per-chunk gradients)",
                       "bound": "hbm", "achieved": bwd_bytes / (bwd_ms / 1e3) / 1e9,
                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
                       "frac": bwd_bytes / (bwd_ms / 1e3) / 1e9 / HBM_PEAK_GBS,
-                      "traffic": read_traffic("backward_chunked_traffic_b8_t4096_h40.txt", src),
+                      "traffic": (None if args.decay_f32 else
+                                  read_traffic("backward_chunked_traffic_b8_t4096_h40.txt", src)),
                       "bytes_per_launch": bwd_bytes, "avg_launch_us": bwd_ms * 1e3,
                       "workspace_bytes": bws,
                       "valu_tflops_equivalent": tf}
@@ -360,10 +365,13 @@ def main():
     if args.fused and args.only not in ("prefill", "decode"):
         print("bench.py: --fused needs --only prefill or --only decode", file=sys.stderr)
         sys.exit(2)
-    if (args.prefill_shape != "2.9b" or args.decay_f32 or args.bidir) and \
-            args.only != "prefill":
-        print("bench.py: --prefill-shape long and --decay-f32 are prefill-only measurements "
+    if (args.prefill_shape != "2.9b" or args.bidir) and args.only != "prefill":
+        print("bench.py: --prefill-shape long and --bidir are prefill-only measurements "
               "(--only prefill)", file=sys.stderr)
+        sys.exit(2)
+    if args.decay_f32 and args.only not in ("prefill", "train"):
+        print("bench.py: --decay-f32 needs --only prefill (long context) or --only train",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -239,21 +239,26 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
 /*
  * Gradients of L = sum_t <y_t, dy_t> + <S_T, ds_T> with respect to the inputs
  * of rwkv7_wkv_forward_train (without epilogue):
- *   r, w, k, v, kappa, a : [B,T,H,N] in dt, the forward's inputs
- *   dy     : [B,T,H,N] in dt, the cotangent of y
+ *   r, w, k, v, kappa, a : [B,T,H,N] in dt, the forward's inputs (with
+ *            RWKV7_DT_BF16_W32: w float32, the rest bfloat16)
+ *   dy     : [B,T,H,N] in dt (bfloat16 for RWKV7_DT_BF16_W32), the cotangent of y
  *   s_ckpt : [B,H,C,N,N] float32 from rwkv7_wkv_forward_train on these inputs
  *   ds_T   : [B,H,N,N] float32 cotangent of the final state, or NULL (zero)
- *   dr, dw, dk, dv, dkappa, da : [B,T,H,N] in dt (outputs)
+ *   dr, dw, dk, dv, dkappa, da : [B,T,H,N] in dt (outputs; for
+ *            RWKV7_DT_BF16_W32 dw is float32 and the rest bfloat16)
  *   ds0    : [B,H,N,N] float32 gradient for s0 (output), or NULL to skip it;
  *            may equal ds_T (in place)
  *   algo   : RWKV7_ALGO_SCAN: token by token in fp32 VALU (states recomputed
- *              from s_ckpt), any dtype, no workspace;
- *            RWKV7_ALGO_CHUNKED: bf16 only; the chunked form on bf16 MFMA with
+ *              from s_ckpt), f32 or bf16, no workspace (RWKV7_DT_BF16_W32 is
+ *              refused with RWKV7_ERR_UNSUPPORTED);
+ *            RWKV7_ALGO_CHUNKED: bf16 or bf16 with float32 w (f32 refused with
+ *              RWKV7_ERR_UNSUPPORTED); the chunked form on bf16 MFMA with
  *              fp32 accumulation: a reverse pass over the 16-token chunks
  *              carries the state cotangent and stores it at every chunk's end
  *              in the workspace, then every chunk's gradients are formed in
  *              parallel from its stored state and cotangent;
- *            RWKV7_ALGO_AUTO: CHUNKED for bf16, SCAN for f32.
+ *            RWKV7_ALGO_AUTO: CHUNKED for bf16 and bf16 with float32 w, SCAN
+ *              for f32.
  *   workspace / workspace_bytes : device scratch of at least
  *            rwkv7_wkv_backward_workspace(...) bytes (16 KiB per head and
  *            chunk for CHUNKED; may be NULL when that is 0); it must not

@@ -326,17 +326,18 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
                         algo, nullptr, workspace, workspace_bytes, stream);
 }
 
-// AUTO: the chunked backward for bf16, else the token-by-token one.
+// AUTO: the chunked backward for bf16 (also with an fp32 decay), else the
+// token-by-token one.
 static rwkv7_algo resolve_bwd_algo(rwkv7_algo algo, rwkv7_dtype dt) {
     if (algo == RWKV7_ALGO_AUTO)
-        return dt == RWKV7_DT_BF16 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+        return dt != RWKV7_DT_F32 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
     return algo;
 }
 
 size_t rwkv7_wkv_backward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                     rwkv7_algo algo) {
     if (B < 1 || H < 1 || T <= 0 || N != kN) return 0;
-    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return 0;
+    if (!valid_dtype(dt)) return 0;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED) return 0;
     if (resolve_bwd_algo(algo, dt) != RWKV7_ALGO_CHUNKED) return 0;
     size_t n = 1;
@@ -352,19 +353,22 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
                                 void *dk, void *dv, void *dkappa, void *da, float *ds0, int B,
                                 int T, int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
                                 void *workspace, size_t workspace_bytes, void *stream) {
-    if (dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
-    if (dt != RWKV7_DT_F32 && dt != RWKV7_DT_BF16) return RWKV7_ERR_DTYPE;
+    if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
     if (N != kN) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
     const rwkv7_algo use = resolve_bwd_algo(algo, dt);
-    if (use == RWKV7_ALGO_CHUNKED && dt != RWKV7_DT_BF16) return RWKV7_ERR_UNSUPPORTED;
-    const size_t esz = dt == RWKV7_DT_BF16 ? 2 : 4;
+    // chunked: bf16, or bf16 with an fp32 decay; the token-by-token kernel: f32 or bf16
+    if (use == RWKV7_ALGO_CHUNKED && dt == RWKV7_DT_F32) return RWKV7_ERR_UNSUPPORTED;
+    if (use == RWKV7_ALGO_SCAN && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
+    const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
     if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
         !mul_ok(tok, (size_t)N) || !mul_ok(tok, esz))
         return RWKV7_ERR_SHAPE;
+    // w and dw: float32 with an fp32 decay
+    const size_t tokw = dt == RWKV7_DT_BF16_W32 ? 2 * tok : tok;
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     size_t ck = st;
@@ -399,13 +403,14 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     auto rng = [](const void *p, size_t n) {
         return Range{reinterpret_cast<uintptr_t>(p), reinterpret_cast<uintptr_t>(p) + n};
     };
+    auto vbytes = [&](int i) { return i == 1 ? tokw : tok; };  // index 1: w / dw
     if (T > 0) {
         for (int o = 0; o < 6; ++o) {
-            const Range ro = rng(outs[o], tok);
-            for (const void *p : ins)
-                if (overlap(ro, rng(p, tok))) return RWKV7_ERR_ALIAS;
+            const Range ro = rng(outs[o], vbytes(o));
+            for (int i = 0; i < 7; ++i)
+                if (overlap(ro, rng(ins[i], vbytes(i)))) return RWKV7_ERR_ALIAS;
             for (int o2 = o + 1; o2 < 6; ++o2)
-                if (overlap(ro, rng(outs[o2], tok))) return RWKV7_ERR_ALIAS;
+                if (overlap(ro, rng(outs[o2], vbytes(o2)))) return RWKV7_ERR_ALIAS;
             if (overlap(ro, rng(s_ckpt, ck)) || (ds_T && overlap(ro, rng(ds_T, st))) ||
                 (ds0 && overlap(ro, rng(ds0, st))))
                 return RWKV7_ERR_ALIAS;
@@ -414,18 +419,18 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     if (ds0) {
         const Range rd = rng(ds0, st);
         if (T > 0) {
-            for (const void *p : ins)
-                if (overlap(rd, rng(p, tok))) return RWKV7_ERR_ALIAS;
+            for (int i = 0; i < 7; ++i)
+                if (overlap(rd, rng(ins[i], vbytes(i)))) return RWKV7_ERR_ALIAS;
             if (overlap(rd, rng(s_ckpt, ck))) return RWKV7_ERR_ALIAS;
         }
         if (ds_T && ds_T != ds0 && overlap(rd, rng(ds_T, st))) return RWKV7_ERR_ALIAS;
     }
     if (chunked) {  // the workspace is written: it overlaps no argument
         const Range rw = rng(workspace, ws_need);
-        for (const void *q : ins)
-            if (overlap(rw, rng(q, tok))) return RWKV7_ERR_ALIAS;
-        for (const void *q : outs)
-            if (overlap(rw, rng(q, tok))) return RWKV7_ERR_ALIAS;
+        for (int i = 0; i < 7; ++i)
+            if (overlap(rw, rng(ins[i], vbytes(i)))) return RWKV7_ERR_ALIAS;
+        for (int o = 0; o < 6; ++o)
+            if (overlap(rw, rng(outs[o], vbytes(o)))) return RWKV7_ERR_ALIAS;
         if (overlap(rw, rng(s_ckpt, ck)) || (ds_T && overlap(rw, rng(ds_T, st))) ||
             (ds0 && overlap(rw, rng(ds0, st))))
             return RWKV7_ERR_ALIAS;
@@ -442,7 +447,8 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     p.dr = dr; p.dw = dw; p.dk = dk; p.dv = dv; p.dkappa = dkappa; p.da = da;
     p.ds0 = ds0;
     p.B = B; p.T = T; p.H = H;
-    p.bf16 = dt == RWKV7_DT_BF16;
+    p.bf16 = dt != RWKV7_DT_F32;
+    p.w32 = dt == RWKV7_DT_BF16_W32;
     if (chunked) {
         p.ds_ws = static_cast<float *>(workspace);
         return launch_backward_chunked(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

@@ -139,6 +139,12 @@ __device__ __forceinline__ f32x4 inverse_t(f32x4 dm, f32x4 dmt, int lane) {
     return mma(bf4(m8), bf4(gt), gt);          // D(X^T)
 }
 
+// the decay's element type: bf16 bits, or float32 (RWKV7_DT_BF16_W32)
+template <bool W32> struct DecayT { using type = uint16_t; };
+template <> struct DecayT<true> { using type = float; };
+__device__ __forceinline__ float widen(uint16_t u) { return bf16_lo(u); }
+__device__ __forceinline__ float widen(float x) { return x; }
+
 // Element offset of token t of (b, h) in a [B,T,H,64] tensor.
 __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, long t) {
     return ((b * p.T + t) * p.H + h) * kN;
@@ -152,7 +158,9 @@ struct ChainLds {
     float gc[kN];                                 // decay total of the chunk
 };
 
+template <bool W32>
 __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
+    using WT = typename DecayT<W32>::type;
     __shared__ ChainLds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lo = lane & 15, g4 = 4 * (lane >> 4);
@@ -160,7 +168,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
     const int nch = (p.T + kC - 1) / kC;
-    const uint16_t *pr = static_cast<const uint16_t *>(p.r), *pw = static_cast<const uint16_t *>(p.w);
+    const uint16_t *pr = static_cast<const uint16_t *>(p.r);
+    const WT *pw = static_cast<const WT *>(p.w);
     const uint16_t *pkap = static_cast<const uint16_t *>(p.kappa), *pa = static_cast<const uint16_t *>(p.a);
     const uint16_t *pdy = static_cast<const uint16_t *>(p.dy);
 
@@ -179,7 +188,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
 
     // raw bf16 inputs of a chunk: thread (wave, lane) takes key/value `lane` of
     // tokens 4 wave .. 4 wave + 3; the next chunk's are loaded while this one runs
-    uint16_t nw[4], nk[4], na[4], nr[4], nd[4];
+    WT nw[4];
+    uint16_t nk[4], na[4], nr[4], nd[4];
     auto load_chunk = [&](int cc) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -195,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const bool ok = (long)c * kC + 4 * wave + e < p.T;
-            wv[e] = ok ? bf16_lo(nw[e]) : 1.f;
+            wv[e] = ok ? widen(nw[e]) : 1.f;
             kv[e] = ok ? bf16_lo(nk[e]) : 0.f;
             av[e] = ok ? bf16_lo(na[e]) : 0.f;
             rv[e] = ok ? bf16_lo(nr[e]) : 0.f;
@@ -297,6 +307,13 @@ struct GradLds {
     float carry[4][kN];
 };
 
+// input (r, w, k, v, kappa, a, dy = 0..6) of the 128-piece row `slot` of a
+// chunk's loads; a float32 decay is loaded apart, so its rows skip w
+template <bool W32> __device__ constexpr int slot_input(int slot) {
+    return (W32 && slot >= 1) ? (slot + 1 < 7 ? slot + 1 : 6) : (slot < 7 ? slot : 6);
+}
+
+template <bool W32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_grad_kernel(
     BackwardArgs p) {
     __shared__ GradLds L;
@@ -316,27 +333,51 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
     // A chunk's global inputs, loaded one chunk ahead: its entry state and exit
     // cotangent (rows 16 wave + lo, keys 16jb + g4 + e) and the raw inputs as
-    // 16-byte row pieces: piece q = threadIdx.x + 256 i (i < 4, q < 7 * 128) is
-    // keys/values 8 (q & 7) .. +7 of token (q >> 3) & 15 of input q >> 7
-    // (r, w, k, v, kappa, a, dy).
+    // 16-byte row pieces, piece q = threadIdx.x + 256 i (i < 4):
+    //  - bf16 decay: q < 7 * 128 is keys/values 8 (q & 7) .. +7 of token
+    //    (q >> 3) & 15 of input q >> 7 (r, w, k, v, kappa, a, dy);
+    //  - float32 decay: q < 6 * 128 likewise over r, k, v, kappa, a, dy, and
+    //    q' = q - 768 is keys 4 (q' & 15) .. +3 of token q' >> 4 of w.
+    constexpr int kPieces = W32 ? 8 * 128 : 7 * 128;
+    static_assert(kThreads == 256 && kPieces > 3 * kThreads && kPieces <= 4 * kThreads,
+                  "three whole row pieces per thread and a partial fourth");
     const long srow = (long)(16 * wave + lo) * kN;
     float4 S0n[4], Dhn[4];
     uint4 rawn[4];
     auto load_chunk = [&](int cc) {
-        const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srow;
-        const float *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srow;
+        // thread index opaque per call, as for the LDS addresses below: the
+        // per-thread address parts are recomputed instead of held across the loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int g4l = 4 * ((tid & 63) >> 4);
+        const long srowl = (long)(16 * (tid >> 6) + (tid & 15)) * kN;
+        const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srowl;
+        const float *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srowl;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
-            S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4);
-            Dhn[jb] = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4);
+            S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4l);
+            Dhn[jb] = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4l);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q = threadIdx.x + kThreads * i;
-            if (q < 7 * 128) {
-                const long t = (long)cc * kC + ((q >> 3) & 15);
-                const long o = tok_off(p, b, h, t < p.T ? t : 0) + 8 * (q & 7);
-                rawn[i] = *reinterpret_cast<const uint4 *>(in[q >> 7] + o);
+            const int q = tid + kThreads * i;
+            // known per i (256 threads): pieces 0..2 are bf16 row pieces; piece 3
+            // is the float32 decay's, or dy's for the first 128 threads
+            if (W32 || i < 3 || q < kPieces) {
+                if (!(W32 && i == 3)) {
+                    // input q >> 7, one of two known per i (the float32 decay's
+                    // row skips w): a select of two pointers, not an indexed array
+                    const uint16_t *src = ((q >> 7) & 1) ? in[slot_input<W32>(2 * i + 1)]
+                                                          : in[slot_input<W32>(2 * i)];
+                    const long t = (long)cc * kC + ((q >> 3) & 15);
+                    const long o = tok_off(p, b, h, t < p.T ? t : 0) + 8 * (q & 7);
+                    rawn[i] = *reinterpret_cast<const uint4 *>(src + o);
+                } else {
+                    const int qq = q - 6 * 128;
+                    const long t = (long)cc * kC + (qq >> 4);
+                    const long o = tok_off(p, b, h, t < p.T ? t : 0) + 4 * (qq & 15);
+                    rawn[i] = *reinterpret_cast<const uint4 *>(static_cast<const float *>(p.w) + o);
+                }
             }
         }
     };
@@ -346,18 +387,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = threadIdx.x + kThreads * i;
-            if (q < 7 * 128) {
-                const int s = q >> 7, t = (q >> 3) & 15, k0 = 8 * (q & 7);
-                uint4 x = rawn[i];
-                if (t0s + t >= p.T) {
-                    const unsigned fill = s == 1 ? 0x3F803F80u : 0u;  // bf16 1.0 pairs
-                    x = make_uint4(fill, fill, fill, fill);
+            if (W32 || i < 3 || q < kPieces) {
+                if (!(W32 && i == 3)) {
+                    const int s = ((q >> 7) & 1) ? slot_input<W32>(2 * i + 1)
+                                                  : slot_input<W32>(2 * i);
+                    const int t = (q >> 3) & 15, k0 = 8 * (q & 7);
+                    uint4 x = rawn[i];
+                    if (t0s + t >= p.T) {
+                        const unsigned fill = s == 1 ? 0x3F803F80u : 0u;  // bf16 1.0 pairs
+                        x = make_uint4(fill, fill, fill, fill);
+                    }
+                    short *dst = s == 0 ? &L.rr[t][k0] : s == 1 ? &L.ww[t][k0]
+                               : s == 2 ? &L.kk[t][k0] : s == 3 ? &L.vv[t][k0]
+                               : s == 4 ? &L.ka[t][k0] : s == 5 ? &L.aa[t][k0] : &L.dyy[t][k0];
+                    reinterpret_cast<uint2 *>(dst)[0] = make_uint2(x.x, x.y);
+                    reinterpret_cast<uint2 *>(dst)[1] = make_uint2(x.z, x.w);
+                } else {
+                    // float32 decay: staged in the decay-product tile, which phase 1
+                    // then overwrites element by element with the products
+                    const int qq = q - 6 * 128, t = qq >> 4, k0 = 4 * (qq & 15);
+                    uint4 x = rawn[i];
+                    if (t0s + t >= p.T) x = make_uint4(0x3F800000u, 0x3F800000u, 0x3F800000u,
+                                                       0x3F800000u);  // 1.0f
+                    *reinterpret_cast<uint4 *>(&L.gam[t][k0]) = x;
                 }
-                short *dst = s == 0 ? &L.rr[t][k0] : s == 1 ? &L.ww[t][k0] : s == 2 ? &L.kk[t][k0]
-                           : s == 3 ? &L.vv[t][k0] : s == 4 ? &L.ka[t][k0] : s == 5 ? &L.aa[t][k0]
-                                                                              : &L.dyy[t][k0];
-                reinterpret_cast<uint2 *>(dst)[0] = make_uint2(x.x, x.y);
-                reinterpret_cast<uint2 *>(dst)[1] = make_uint2(x.z, x.w);
             }
         }
     };
@@ -401,7 +454,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = 4 * wave + e;
-                x[0][e] = fbf(L.rr[t][lane]); x[1][e] = fbf(L.ww[t][lane]);
+                x[0][e] = fbf(L.rr[t][lane]);
+                x[1][e] = W32 ? L.gam[t][lane] : fbf(L.ww[t][lane]);  // w
                 x[2][e] = fbf(L.kk[t][lane]);
                 x[4][e] = fbf(L.ka[t][lane]); x[5][e] = fbf(L.aa[t][lane]);
             }
@@ -573,12 +627,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (wave == 0) {
             const int j = lane;
             // every LDS value first, then the sums
+            // (float32 decay: w_t = g_t / g_{t-1} from the decay products, whose
+            // tile held the raw w until phase 1)
             float dl[kC], dkn[kC], wv[kC], part[8];
 #pragma unroll
             for (int t = 0; t < kC; ++t) {
                 dl[t] = L.u.e.dlg[t][j];
                 dkn[t] = L.u.e.dkk[t][j];
-                wv[t] = fbf(L.ww[t][j]);
+                wv[t] = W32 ? L.gam[t][j] : fbf(L.ww[t][j]);
             }
 #pragma unroll
             for (int q = 0; q < 8; ++q) part[q] = L.dlgc[q][j];
@@ -588,16 +644,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
             for (int t = kC - 1; t >= 0; --t) {
                 acc += dl[t] + (t + 1 < kC ? dkn[t + 1] : 0.f);
-                dwv[t] = acc * __builtin_amdgcn_rcpf(wv[t]);
+                dwv[t] = W32 ? acc * (t ? wv[t - 1] : 1.f) * __builtin_amdgcn_rcpf(wv[t])
+                             : acc * __builtin_amdgcn_rcpf(wv[t]);
             }
-            uint16_t *q = static_cast<uint16_t *>(p.dw) + tb + j;
-            if (full) {
-#pragma unroll
-                for (int t = 0; t < kC; ++t) q[t * TS] = bf1u(dwv[t]);
-            } else {
+            if constexpr (W32) {
+                float *q = static_cast<float *>(p.dw) + tb + j;
 #pragma unroll
                 for (int t = 0; t < kC; ++t)
-                    if (t0 + t < p.T) q[t * TS] = bf1u(dwv[t]);
+                    if (full || t0 + t < p.T) q[t * TS] = dwv[t];
+            } else {
+                uint16_t *q = static_cast<uint16_t *>(p.dw) + tb + j;
+                if (full) {
+#pragma unroll
+                    for (int t = 0; t < kC; ++t) q[t * TS] = bf1u(dwv[t]);
+                } else {
+#pragma unroll
+                    for (int t = 0; t < kC; ++t)
+                        if (t0 + t < p.T) q[t * TS] = bf1u(dwv[t]);
+                }
             }
         }
         __syncthreads();  // the next chunk's operands overwrite LDS
@@ -620,12 +684,22 @@ bool backward_chunked_grid_ok(int B, int T, int H) {
 hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream) {
     const long heads = (long)p.B * p.H;
     const long nch = (p.T + kC - 1) / kC;
-    hipLaunchKernelGGL(bwd_chain_kernel, dim3((unsigned)heads), dim3(kThreads), 0, stream, p);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const long ngrp = (nch + kGradChunks - 1) / kGradChunks;
-    hipLaunchKernelGGL(bwd_grad_kernel, dim3((unsigned)(heads * ngrp)), dim3(kThreads), 0,
-                       stream, p);
+    if (p.w32) {
+        hipLaunchKernelGGL(bwd_chain_kernel<true>, dim3((unsigned)heads), dim3(kThreads), 0,
+                           stream, p);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(bwd_grad_kernel<true>, dim3((unsigned)(heads * ngrp)), dim3(kThreads),
+                           0, stream, p);
+    } else {
+        hipLaunchKernelGGL(bwd_chain_kernel<false>, dim3((unsigned)heads), dim3(kThreads), 0,
+                           stream, p);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL(bwd_grad_kernel<false>, dim3((unsigned)(heads * ngrp)), dim3(kThreads),
+                           0, stream, p);
+    }
     return hipGetLastError();
 }
 

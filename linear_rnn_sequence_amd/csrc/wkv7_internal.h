@@ -60,6 +60,7 @@ struct BackwardArgs {
     int B, T, H;
     bool bf16;
     float *ds_ws;  // chunked: [B,H,ceil(T/kCkpt),N,N] exit cotangent of every chunk
+    bool w32;      // chunked: w and dw float32 (the other vectors bf16)
 };
 
 struct DecodeArgs {

@@ -294,14 +294,15 @@ def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=Non
     sum_t <y_t, dy_t> + <S_T, ds_T> for the inputs of :func:`forward_train`.  ``grads``
     may pass the six output tensors; ``ds0`` may be ``ds_T`` (in place).  ``algo`` is
     "auto", "scan" or "chunked"; the chunked form's workspace is allocated here unless
-    ``workspace`` (a uint8 device tensor of at least backward_workspace_bytes) is given."""
+    ``workspace`` (a uint8 device tensor of at least backward_workspace_bytes) is given.
+    With a float32 decay w (other inputs bf16; chunked only), dw is float32 too."""
     import torch
 
     B, T, H, N = r.shape
-    _check_same(torch, (r, w, k, v, kappa, a, dy), r.shape, r.dtype)
-    dt = _dtype_code(torch, r.dtype)
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    _check_same(torch, (dy,), r.shape, r.dtype)
     if grads is None:
-        grads = tuple(torch.empty_like(r) for _ in range(6))
+        grads = tuple(torch.empty_like(w if i == 1 else r) for i in range(6))
     if ds0 is None and want_ds0:
         ds0 = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
     need = int(lib().rwkv7_wkv_backward_workspace(B, T, H, N, dt, ALGOS[algo]))

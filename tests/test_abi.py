@@ -164,15 +164,24 @@ def test_backward_validation_codes():
 
 def test_fp32_decay_dtype_codes():
     # RWKV7_DT_BF16_W32 = 2: accepted by forward (scan and chunked) and decode
-    # validation; the backward refuses it; w spans 4 bytes per element
+    # validation, and by the chunked backward (dw float32 too); the token-by-token
+    # backward refuses it; w spans 4 bytes per element
     assert fwd(dt=2, algo=1, T=0, s_out=None) == 0
     assert fwd(dt=2, algo=2, T=0, s_out=None) == 0
     assert fwd(dt=3) == 3
     B, T, H = 2, 8, 3
     half_w = B * T * H * 64 * 2
     assert fwd(dt=2, y=fake(1, half_w)) == 6     # y over the float32 w's second half
-    assert bwd(dt=2) == 4
+    assert bwd(dt=2, algo=1) == 4                 # scan backward: bf16 or f32 only
     L = wkv.lib()
+    need = L.rwkv7_wkv_backward_workspace(B, T, H, 64, 2, 0)
+    assert need == L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 2) > 0
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 2, 1) == 0
+    assert bwd(dt=2, algo=0) == 7                 # auto -> chunked, which needs a workspace
+    assert bwd(dt=2, algo=2, T=0, ds0=None, ck=None) == 0
+    outs = [fake(9 + i) for i in range(6)]
+    outs[2] = fake(10, half_w)                    # dk over the float32 dw's second half
+    assert bwd(dt=2, algo=2, outs=outs, ws=fake(20), ws_bytes=need) == 6
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 2, 0) == \
         L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 0)
 

@@ -85,7 +85,7 @@ def test_decode_fp32_decay(wkv, epi):
     assert_close(to_f64(st), s_ref, TOL, "decode S")
 
 
-def test_train_forward_fp32_decay_and_backward_refused(wkv):
+def test_train_forward_fp32_decay_stores_states(wkv):
     x = slow(1, 100, 2, seed=17, s0="normal")
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
@@ -95,6 +95,30 @@ def test_train_forward_fp32_decay_and_backward_refused(wkv):
     assert torch.equal(y, y0) and torch.equal(s, s0)
     _, s16 = oracle.forward(*(x.as_f64(n)[:, :16] for n in NAMES), s0=x["s0"])
     assert_close(to_f64(ck[:, :, 1]), s16, TOL, "stored state at token 16")
-    dy = torch.zeros_like(ins[0])
-    with pytest.raises(TypeError):  # the binding refuses mixed dtypes for the backward
-        wkv.backward(*ins, dy, ck)
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 2, 100), (2, 3, 300), (1, 1, 17)])
+def test_backward_fp32_decay_chunked(wkv, B, H, T):
+    """The chunked backward with a float32 decay (dw float32 as well) against the
+    float64 autograd oracle on the same values; the token-by-token backward
+    refuses this dtype."""
+    from oracle import grad as og
+
+    x = slow(B, T, H, seed=40 + T, s0="normal")
+    d = to_device(x, torch)
+    ins = [d[n] for n in NAMES]
+    _, _, ck = wkv.forward_train(*ins, s0=d["s0"], algo="chunked")
+    dy_bits, ds_T = synth.cotangents(B, T, H, seed=41 + T, dtype="bf16")
+    dy = torch.from_numpy(dy_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    dst = torch.from_numpy(ds_T).cuda()
+    *g, ds0 = wkv.backward(*ins, dy, ck, dst)
+    torch.cuda.synchronize()
+    assert g[1].dtype == torch.float32 and g[0].dtype == torch.bfloat16
+    ref = og.backward(*(x.as_f64(n) for n in NAMES),
+                      synth.bf16_bits_to_f32(dy_bits).astype(np.float64), s0=x["s0"],
+                      ds_T=ds_T.astype(np.float64))
+    for n, gt in zip(NAMES, g):
+        assert_close(to_f64(gt), ref[n], TOL, f"d{n}")
+    assert_close(to_f64(ds0), ref["s0"], TOL, "ds0")
+    with pytest.raises(wkv.Rwkv7Error):
+        wkv.backward(*ins, dy, ck, dst, algo="scan")
