@@ -260,9 +260,10 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
  *            RWKV7_ALGO_AUTO: CHUNKED for bf16 and bf16 with float32 w, SCAN
  *              for f32.
  *   workspace / workspace_bytes : device scratch of at least
- *            rwkv7_wkv_backward_workspace(...) bytes (16 KiB per head and
- *            chunk for CHUNKED; may be NULL when that is 0); it must not
- *            overlap any other argument.
+ *            rwkv7_wkv_backward_workspace(...) bytes (8 KiB per head and
+ *            chunk for CHUNKED: each chunk's decayed exit cotangent in bf16;
+ *            may be NULL when that is 0); it must not overlap any other
+ *            argument.
  * Gradients are rounded once to dt.  The six gradient outputs must not
  * overlap each other or any input.  T == 0: ds0 receives ds_T (or zeros).
  * The chunked form is the derivative of the chunked forward of the RWKV-7

@@ -450,7 +450,7 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     p.bf16 = dt != RWKV7_DT_F32;
     p.w32 = dt == RWKV7_DT_BF16_W32;
     if (chunked) {
-        p.ds_ws = static_cast<float *>(workspace);
+        p.ds_ws = static_cast<uint16_t *>(workspace);
         return launch_backward_chunked(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;
     }
     return launch_backward(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

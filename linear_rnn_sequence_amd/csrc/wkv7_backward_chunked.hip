@@ -254,18 +254,16 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         dmbr = mask<true, false>(dmbr, lane);
         const f32x4 dx = inverse_t(dnt, dn, lane);  // D(X) = A operand of X^T
 
-        // ---- chain step: store the exit cotangent, then dS0 of the chunk
-        float *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            *reinterpret_cast<float4 *>(ck + 16 * jb + g4) =
-                make_float4(St[jb][0], St[jb][1], St[jb][2], St[jb][3]);
+        // ---- chain step: dSh = dS_C diag(g_C), stored as the bf16 MFMA operand
+        // that both kernels use, then dS0 of the chunk
+        uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
         bf16x4 Sb[4];
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) St[jb][e] *= L.gc[16 * jb + g4 + e];
             Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
+            *reinterpret_cast<bf16x4 *>(ck + 16 * jb + g4) = Sb[jb];
         }
         const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY (tokens x values)
         f32x4 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
@@ -342,7 +340,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     static_assert(kThreads == 256 && kPieces > 3 * kThreads && kPieces <= 4 * kThreads,
                   "three whole row pieces per thread and a partial fourth");
     const long srow = (long)(16 * wave + lo) * kN;
-    float4 S0n[4], Dhn[4];
+    float4 S0n[4];
+    uint2 Dhn[4];  // bf16 dSh
     uint4 rawn[4];
     auto load_chunk = [&](int cc) {
         // thread index opaque per call, as for the LDS addresses below: the
@@ -352,11 +351,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int g4l = 4 * ((tid & 63) >> 4);
         const long srowl = (long)(16 * (tid >> 6) + (tid & 15)) * kN;
         const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srowl;
-        const float *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srowl;
+        const uint16_t *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srowl;
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4l);
-            Dhn[jb] = *reinterpret_cast<const float4 *>(dsp + 16 * jb + g4l);
+            Dhn[jb] = *reinterpret_cast<const uint2 *>(dsp + 16 * jb + g4l);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -439,11 +438,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                     if (t0 + g4 + e < p.T) q[(g4 + e) * TS] = bf1u(x[e]);
             }
         };
-        f32x4 S0[4], Dh[4];
+        f32x4 S0[4];
+        bf16x4 Dh[4];  // dSh, bf16 as stored
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             S0[jb] = f32x4{S0n[jb].x, S0n[jb].y, S0n[jb].z, S0n[jb].w};
-            Dh[jb] = f32x4{Dhn[jb].x, Dhn[jb].y, Dhn[jb].z, Dhn[jb].w};
+            Dh[jb] = __builtin_bit_cast(bf16x4, Dhn[jb]);
         }
 
         // ---- phase 1: operands.  Thread (wave, lane): tokens 4 wave .. +3, key/value `lane`
@@ -509,17 +509,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
         // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
         {
-            // dSh = dS_C diag(g_C); exit-state term sum_i dSh S0 over this block's values
+            // exit-state term sum_i dSh S0 over this block's values
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * jb + g4 + e;
-                    Dh[jb][e] *= L.gam[kC - 1][j];
-                    const float s = sum_lanes16(Dh[jb][e] * S0[jb][e]);
+                    const float s = sum_lanes16(fbf(Dh[jb][e]) * S0[jb][e]);
                     if (lo == 0) L.dlgc[wave][j] = s;
                     L.u.m.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
-                    L.u.m.dsht[j][16 * wave + lo] = bf1(Dh[jb][e]);
+                    L.u.m.dsht[j][16 * wave + lo] = Dh[jb][e];
                 }
             }
             const bf16x4 vb = colfrag(L.vv, 16 * wave, lane);    // B operand of V
@@ -529,7 +528,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
-                const bf16x4 s0b = bf4(S0[jb]), dhb = bf4(Dh[jb]);  // B operands of S0^T, dSh^T
+                const bf16x4 s0b = bf4(S0[jb]), dhb = Dh[jb];  // B operands of S0^T, dSh^T
                 z = mma(frag(L.kp, 0, 16 * jb, lane), s0b, z);      // + Kp S0^T
                 du = mma(frag(L.bm, 0, 16 * jb, lane), dhb, du);    // + Bm dSh^T
                 dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
@@ -672,7 +671,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 size_t backward_chunked_workspace_bytes(int B, int T, int H) {
     const size_t nch = (size_t)(T + kC - 1) / kC;
-    return (size_t)B * H * nch * kN * kN * sizeof(float);
+    return (size_t)B * H * nch * kN * kN * sizeof(uint16_t);
 }
 
 bool backward_chunked_grid_ok(int B, int T, int H) {

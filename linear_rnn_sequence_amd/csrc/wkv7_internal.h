@@ -59,7 +59,7 @@ struct BackwardArgs {
     float *ds0;                             // [B,H,N,N] or nullptr
     int B, T, H;
     bool bf16;
-    float *ds_ws;  // chunked: [B,H,ceil(T/kCkpt),N,N] exit cotangent of every chunk
+    uint16_t *ds_ws;  // chunked: [B,H,ceil(T/kCkpt),N,N] bf16 dS_C diag(g_C) of every chunk
     bool w32;      // chunked: w and dw float32 (the other vectors bf16)
 };
 

@@ -282,7 +282,7 @@ def test_backward_chunked_workspace_codes():
     L = wkv.lib()
     B, T, H = 2, 40, 3
     need = L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 2)
-    assert need == B * H * 3 * 64 * 64 * 4                   # 16 KiB per head and chunk
+    assert need == B * H * 3 * 64 * 64 * 2                   # 8 KiB per head and chunk
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 0) == need    # auto -> chunked
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 0, 0) == 0       # f32 -> scan
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 1) == 0
