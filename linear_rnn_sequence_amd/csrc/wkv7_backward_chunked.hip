@@ -30,10 +30,10 @@
 // Two kernels:
 //  - bwd_chain_kernel: one workgroup per (b, h) walks the chunks backwards and
 //    carries dS^T as fp32 MFMA accumulator tiles (wave q owns values 16q..16q+15,
-//    like the forward chunked kernel's state); it stores each chunk's exit
-//    cotangent to the workspace and writes ds0;
+//    like the forward chunked kernel's state); it stores each chunk's dSh in
+//    bf16 (the MFMA operand both kernels use) to the workspace and writes ds0;
 //  - bwd_grad_kernel: the chunks are independent here: from a chunk's stored
-//    entry state and exit cotangent a workgroup recomputes its operands and
+//    entry state and dSh a workgroup recomputes its operands and
 //    forms every gradient; each workgroup takes 8 consecutive chunks of one
 //    head and loads the next chunk's inputs while it works on the current one.
 // A ragged last chunk is padded with neutral tokens (w = 1, all else 0), which
@@ -329,8 +329,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                              static_cast<const uint16_t *>(p.kappa), static_cast<const uint16_t *>(p.a),
                              static_cast<const uint16_t *>(p.dy)};
 
-    // A chunk's global inputs, loaded one chunk ahead: its entry state and exit
-    // cotangent (rows 16 wave + lo, keys 16jb + g4 + e) and the raw inputs as
+    // A chunk's global inputs, loaded one chunk ahead: its entry state and dSh
+    // (rows 16 wave + lo, keys 16jb + g4 + e) and the raw inputs as
     // 16-byte row pieces, piece q = threadIdx.x + 256 i (i < 4):
     //  - bf16 decay: q < 7 * 128 is keys/values 8 (q & 7) .. +7 of token
     //    (q >> 3) & 15 of input q >> 7 (r, w, k, v, kappa, a, dy);
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     //    q' = q - 768 is keys 4 (q' & 15) .. +3 of token q' >> 4 of w.
     constexpr int kPieces = W32 ? 8 * 128 : 7 * 128;
     static_assert(kThreads == 256 && kPieces > 3 * kThreads && kPieces <= 4 * kThreads,
-                  "three whole row pieces per thread and a partial fourth");
+                  "three whole row pieces per thread and a fourth, whole or partial");
     const long srow = (long)(16 * wave + lo) * kN;
     float4 S0n[4];
     uint2 Dhn[4];  // bf16 dSh
@@ -580,6 +580,40 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             dmkt = mask<false, true>(dmkt, lane);
             dmn = mask<true, true>(dmn, lane);
             dmnt = mask<false, true>(dmnt, lane);
+            // Same-token parts of the decay terms below: the diagonals of dMkr and
+            // dMbr and the first sub-diagonals of dMkk and dMbk enter one token's
+            // dlg twice with opposite signs (through dRp and dKm, dBm, or dKm, dBm
+            // and the next token's dKp), which cancel exactly, but only up to bf16
+            // rounding once formed from differently rounded operands; dlg is taken
+            // without them.  Wave 0 keeps them (as the products rounded them) in
+            // the carry tile, free after phase 1: row k of 16 tokens.
+            float *dg = &L.carry[0][0];
+            if (wave == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int row = g4 + e;  // lane holds rows g4 .. g4+3 of column lo
+                    if (row == lo) {
+                        dg[0 * kC + lo] = fbf(bf1(dmrt[e]));  // dMkr[t][t], as dRp took it
+                        dg[1 * kC + lo] = fbf(bf1(dmbt[e]));  // -dMbr[t][t], as dRp took it
+                        dg[2 * kC + lo] = fbf(bf1(dmr[e]));   // dMkr[t][t], as dKm took it
+                        dg[3 * kC + lo] = fbf(bf1(dmb[e]));   // -dMbr[t][t], as dBm took it
+                    }
+                    if (row == lo + 1) {
+                        dg[4 * kC + lo] = fbf(bf1(dmk[e]));   // dMkk[t+1][t] (dKm)
+                        dg[5 * kC + lo] = fbf(bf1(dmn[e]));   // -dMbk[t+1][t] (dBm)
+                    }
+                    if (row + 1 == lo) {
+                        dg[6 * kC + lo] = fbf(bf1(dmkt[e]));  // dMkk[t][t-1] (dKp)
+                        dg[7 * kC + lo] = fbf(bf1(dmnt[e]));  // -dMbk[t][t-1] (dKp)
+                    }
+                }
+                if (lane == 0) {  // no token 16 or -1
+                    dg[4 * kC + kC - 1] = 0.f;
+                    dg[5 * kC + kC - 1] = 0.f;
+                    dg[6 * kC] = 0.f;
+                    dg[7 * kC] = 0.f;
+                }
+            }
             const bf16x4 rpb = colfrag(L.rp, 16 * wave, lane), kpb = colfrag(L.kp, 16 * wave, lane);
             const bf16x4 kmb = colfrag(L.km, 16 * wave, lane), bmb = colfrag(L.bm, 16 * wave, lane);
             // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
@@ -599,9 +633,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const int j = 16 * wave + lo;
             float csum = 0.f;
             float o_dr[4], o_dk[4], o_da[4], o_dkap[4];
+            float4 sd[8];  // the same-token parts of tokens g4 .. g4+3
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sd[q] = *reinterpret_cast<const float4 *>(&dg[q * kC + g4]);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = g4 + e;
+                const float sA = (&sd[0].x)[e], sB = (&sd[1].x)[e], sC = (&sd[2].x)[e];
+                const float sD = (&sd[3].x)[e], sE = (&sd[4].x)[e], sF = (&sd[5].x)[e];
+                const float sG = (&sd[6].x)[e], sH = (&sd[7].x)[e];
+                // the bf16 operands the products took
+                const float bKm = fbf(L.km[t][j]), bRp = fbf(L.rp[t][j]), bBm = fbf(L.bm[t][j]);
+                const int tn = t < kC - 1 ? t + 1 : t, tp = t ? t - 1 : t;
+                const float bKpn = t < kC - 1 ? fbf(L.kp[tn][j]) : 0.f;
+                const float bKmp = fbf(L.km[tp][j]), bBmp = fbf(L.bm[tp][j]);  // (0 weights at t = 0)
                 const float gam = L.gam[t][j], gprev = t ? L.gam[t - 1][j] : 1.f;
                 const float r = fbf(L.rr[t][j]), k = fbf(L.kk[t][j]), kap = fbf(L.ka[t][j]);
                 const float a = fbf(L.aa[t][j]);
@@ -609,8 +654,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 const float Kp = kap * gprev, Rp = r * gam, Km = k * ig, Bm = a * kap * ig;
                 const float dr = drp[e] * gam, dk = dkm[e] * ig, db = dbm[e] * ig;
                 const float da = db * kap, dkap = dkp[e] * gprev + db * a;
-                L.u.e.dlg[t][j] = drp[e] * Rp - dkm[e] * Km - dbm[e] * Bm;
-                L.u.e.dkk[t][j] = dkp[e] * Kp;
+                const float drp_d = drp[e] - sA * bKm + sB * bBm;
+                const float dkm_d = dkm[e] - sC * bRp - sE * bKpn;
+                const float dbm_d = dbm[e] + sD * bRp + sF * bKpn;
+                const float dkp_d = dkp[e] - sG * bKmp + sH * bBmp;
+                L.u.e.dlg[t][j] = drp_d * Rp - dkm_d * Km - dbm_d * Bm;
+                L.u.e.dkk[t][j] = dkp_d * Kp;
                 csum += Km * dkms[e] - Bm * dbms[e];  // exit-state term (dBm_S = -U dSh)
                 o_dr[e] = dr; o_dk[e] = dk; o_da[e] = da; o_dkap[e] = dkap;
             }

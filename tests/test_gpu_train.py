@@ -111,6 +111,21 @@ def test_backward_sweep_T(wkv, T, dtype, bwd):
     run_and_check(wkv, x, dy, ds_T, bwd=bwd, what=f"{dtype} {bwd} T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 2, 3])
+def test_backward_chunked_short_small_dw(wkv, T):
+    """Short sequences, slow decay, near-full replacement, no state cotangent: dw is
+    small next to the intra-chunk terms of the decay gradient.  The chunked
+    backward takes dlg without its same-token parts (they cancel exactly, but
+    only up to bf16 rounding once formed).  A CPU emulation of the same steps
+    with bf16 operands puts dw at 6.2e-3 with them and 2.2e-3 without them at
+    T = 1 for this draw; the float32-decay case of the same kind reached 2.3e-2
+    with them (tests/test_gpu_w32.py, T = 1)."""
+    x = synth.draw(2, T, 2, seed=500 + T, dtype="bf16", s0="normal", w_recipe="slow",
+                   a_mean=2.0)
+    dy, ds_T = synth.cotangents(2, T, 2, seed=600 + T, dtype="bf16", with_state=False)
+    run_and_check(wkv, x, dy, ds_T, bwd="chunked", what=f"short T={T}")
+
+
 @pytest.mark.parametrize("B,H,T", [(2, 3, 37), (3, 1, 129), (1, 5, 256)])
 @pytest.mark.parametrize("with_dsT", [False, True])
 @pytest.mark.parametrize("s0", ["zero", "normal"])

@@ -97,8 +97,10 @@ def test_train_forward_fp32_decay_stores_states(wkv):
     assert_close(to_f64(ck[:, :, 1]), s16, TOL, "stored state at token 16")
 
 
-@pytest.mark.parametrize("B,H,T", [(1, 2, 100), (2, 3, 300), (1, 1, 17)])
-def test_backward_fp32_decay_chunked(wkv, B, H, T):
+@pytest.mark.parametrize("B,H,T,with_dsT", [(1, 2, 100, True), (2, 3, 300, True),
+                                            (1, 1, 17, True), (1, 2, 16, False),
+                                            (2, 1, 1, False)])
+def test_backward_fp32_decay_chunked(wkv, B, H, T, with_dsT):
     """The chunked backward with a float32 decay (dw float32 as well) against the
     float64 autograd oracle on the same values; the token-by-token backward
     refuses this dtype."""
@@ -108,15 +110,15 @@ def test_backward_fp32_decay_chunked(wkv, B, H, T):
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
     _, _, ck = wkv.forward_train(*ins, s0=d["s0"], algo="chunked")
-    dy_bits, ds_T = synth.cotangents(B, T, H, seed=41 + T, dtype="bf16")
+    dy_bits, ds_T = synth.cotangents(B, T, H, seed=41 + T, dtype="bf16", with_state=with_dsT)
     dy = torch.from_numpy(dy_bits.view(np.int16)).cuda().view(torch.bfloat16)
-    dst = torch.from_numpy(ds_T).cuda()
+    dst = None if ds_T is None else torch.from_numpy(ds_T).cuda()
     *g, ds0 = wkv.backward(*ins, dy, ck, dst)
     torch.cuda.synchronize()
     assert g[1].dtype == torch.float32 and g[0].dtype == torch.bfloat16
     ref = og.backward(*(x.as_f64(n) for n in NAMES),
                       synth.bf16_bits_to_f32(dy_bits).astype(np.float64), s0=x["s0"],
-                      ds_T=ds_T.astype(np.float64))
+                      ds_T=None if ds_T is None else ds_T.astype(np.float64))
     for n, gt in zip(NAMES, g):
         assert_close(to_f64(gt), ref[n], TOL, f"d{n}")
     assert_close(to_f64(ds0), ref["s0"], TOL, "ds0")
