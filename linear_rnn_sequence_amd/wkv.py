@@ -148,8 +148,20 @@ def _check_same(torch, xs, shape, dtype):
             raise ValueError("inputs must live on the GPU")
 
 
+# dtype names of the workspace queries
+DTYPE_NAMES = {"f32": DT_F32, "float32": DT_F32, "bf16": DT_BF16, "bfloat16": DT_BF16,
+               "bf16_w32": DT_BF16_W32}
+
+
+def _dtype_code(dtype):
+    try:
+        return DTYPE_NAMES[dtype]
+    except KeyError:
+        raise ValueError(f"dtype must be one of {sorted(DTYPE_NAMES)}, not {dtype!r}") from None
+
+
 def forward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
-    dt = DT_BF16 if dtype in ("bf16", "bfloat16") else DT_F32
+    dt = _dtype_code(dtype)
     return int(lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
@@ -247,7 +259,7 @@ def forward_bidir(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, 
 
 
 def forward_bidir_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
-    dt = {"bf16": DT_BF16, "bfloat16": DT_BF16, "f32": DT_F32, "bf16_w32": DT_BF16_W32}[dtype]
+    dt = _dtype_code(dtype)
     return int(lib().rwkv7_wkv_forward_bidir_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
@@ -284,7 +296,7 @@ def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=N
 
 def backward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
     """rwkv7_wkv_backward_workspace."""
-    dt = DT_BF16 if dtype == "bf16" else DT_F32
+    dt = _dtype_code(dtype)
     return int(lib().rwkv7_wkv_backward_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 

@@ -301,3 +301,16 @@ def test_backward_chunked_workspace_codes():
     Bb, Hb, Tb = 1 << 15, 1 << 10, 1 << 13
     needb = L.rwkv7_wkv_backward_workspace(Bb, Tb, Hb, 64, 1, 2)
     assert bwd(B=Bb, H=Hb, T=Tb, algo=2, ws=ws, ws_bytes=needb) == 2
+
+
+def test_binding_workspace_dtype_names():
+    # the binding's workspace queries name dtypes as strings; each maps to its own code
+    assert wkv.backward_workspace_bytes(2, 40, 3, dtype="bf16_w32") == \
+        wkv.backward_workspace_bytes(2, 40, 3, dtype="bf16") == 2 * 3 * 3 * 64 * 64 * 2
+    assert wkv.backward_workspace_bytes(2, 40, 3, dtype="f32") == 0          # auto -> scan
+    assert wkv.forward_workspace_bytes(1, 65536, 1, dtype="bf16_w32") == \
+        wkv.forward_workspace_bytes(1, 65536, 1, dtype="bfloat16") > 0
+    assert wkv.forward_bidir_workspace_bytes(1, 65536, 1, dtype="float32") == \
+        wkv.lib().rwkv7_wkv_forward_bidir_workspace(1, 65536, 1, 64, 0, 0)
+    with pytest.raises(ValueError):
+        wkv.backward_workspace_bytes(2, 40, 3, dtype="fp16")
