@@ -153,7 +153,7 @@ DTYPE_NAMES = {"f32": DT_F32, "float32": DT_F32, "bf16": DT_BF16, "bfloat16": DT
                "bf16_w32": DT_BF16_W32}
 
 
-def _dtype_code(dtype):
+def _dtype_name_code(dtype):
     try:
         return DTYPE_NAMES[dtype]
     except KeyError:
@@ -161,7 +161,7 @@ def _dtype_code(dtype):
 
 
 def forward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
-    dt = _dtype_code(dtype)
+    dt = _dtype_name_code(dtype)
     return int(lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
@@ -259,7 +259,7 @@ def forward_bidir(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, 
 
 
 def forward_bidir_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
-    dt = _dtype_code(dtype)
+    dt = _dtype_name_code(dtype)
     return int(lib().rwkv7_wkv_forward_bidir_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
@@ -296,7 +296,7 @@ def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=N
 
 def backward_workspace_bytes(B, T, H, N=N_HEAD, *, dtype="bf16", algo="auto") -> int:
     """rwkv7_wkv_backward_workspace."""
-    dt = _dtype_code(dtype)
+    dt = _dtype_name_code(dtype)
     return int(lib().rwkv7_wkv_backward_workspace(B, T, H, N, dt, ALGOS[algo]))
 
 
