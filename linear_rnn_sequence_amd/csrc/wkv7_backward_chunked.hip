@@ -6,7 +6,8 @@
 //   y_t = S_t r_t,
 // and the gradients are those of L = sum_t <y_t, dy_t> + <S_T, dS_T>.  Over a
 // chunk of 16 tokens with entry state S0 (the stored checkpoint) the forward is
-// (derivation not on the pages, checked in fp64 against the per-token loop):
+// (derivation not on the pages; tests/test_chunked_backward_algebra.py checks
+// these formulas in fp64 against autograd of the per-token loop):
 //   g_t = prod_{s<=t} w_s, gp_t = g_{t-1}; Kp = kappa*gp, Rp = r*g, Km = k/g,
 //   Bm = (a*kappa)/g; Mkk = stril(Kp Km^T), N = stril(Kp Bm^T),
 //   Mkr = tril(Rp Km^T), Mbr = tril(Rp Bm^T); X = (I + N)^-1;
@@ -25,7 +26,9 @@
 //   dlg_t = dRp_t Rp_t - dKm_t Km_t - dBm_t Bm_t + dKp_{t+1} Kp_{t+1}
 // (elementwise) plus, at the chunk's last slot, the exit-state term
 //   sum_i dS_C S_C = sum_i dSh S0 + sum_s Km_s (V dSh)_s + sum_s Bm_s (-U dSh)_s,
-// dw_s = (sum_{t >= s} dlg_t) / w_s.
+// dw_s = (sum_{t >= s} dlg_t) / w_s.  The same-token parts of dlg_t (from the
+// diagonals of dMkr, dMbr and the first sub-diagonals of dMkk, dMbk) cancel
+// exactly and are left out (phase 3 of the gradient kernel).
 //
 // Two kernels:
 //  - bwd_chain_kernel: one workgroup per (b, h) walks the chunks backwards and
