@@ -124,3 +124,23 @@ def test_backward_fp32_decay_chunked(wkv, B, H, T, with_dsT):
     assert_close(to_f64(ds0), ref["s0"], TOL, "ds0")
     with pytest.raises(wkv.Rwkv7Error):
         wkv.backward(*ins, dy, ck, dst, algo="scan")
+
+
+def test_backward_fp32_decay_ds0_in_place_and_optional(wkv):
+    """ds0 written over ds_T, or not at all: the six gradients are the same bits."""
+    x = slow(1, 50, 2, seed=61, s0="normal")
+    d = to_device(x, torch)
+    ins = [d[n] for n in NAMES]
+    _, _, ck = wkv.forward_train(*ins, s0=d["s0"])
+    dy_bits, ds_T = synth.cotangents(1, 50, 2, seed=62, dtype="bf16")
+    dy = torch.from_numpy(dy_bits.view(np.int16)).cuda().view(torch.bfloat16)
+    dst = torch.from_numpy(ds_T).cuda()
+    ref = wkv.backward(*ins, dy, ck, dst)
+    buf = dst.clone()
+    got = wkv.backward(*ins, dy, ck, buf, ds0=buf)
+    nods0 = wkv.backward(*ins, dy, ck, dst, want_ds0=False)
+    torch.cuda.synchronize()
+    assert torch.equal(got[6], ref[6]) and got[6].data_ptr() == buf.data_ptr()
+    for a, b, c in zip(ref[:6], got[:6], nods0[:6]):
+        assert torch.equal(a, b) and torch.equal(a, c)
+    assert ref[1].dtype == torch.float32 and nods0[6] is None
