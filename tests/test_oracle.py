@@ -486,3 +486,21 @@ def test_forward_fused_composes():
     yg, _ = oracle.forward_fused(d["r"], d["w"], d["k"], d["v"], d["a"], k_k, k_a, g=g, s0=S0)
     assert np.array_equal(y1, y_ref) and np.array_equal(s1, s_ref)
     assert np.array_equal(yg, y_ref * g)
+
+
+def test_forward_fused_worked_example():
+    """Prologue, recurrence, GroupNorm, bonus and gate on one N = 4 token, worked by
+    hand (tests/golden/fused_gate_n4_t1.json, exact dyadic values): fails if the
+    gate moves before the norm or the bonus, if the bonus uses the raw key, or if
+    kappa is formed after the booster ([listing]: group_norm, the bonus line,
+    Wo @ (y * g))."""
+    gd = json.load(open(os.path.join(HERE, "golden", "fused_gate_n4_t1.json")))
+    sh = lambda x: np.array(x, dtype=np.float64)[None, None, None, :]  # [1,1,1,N]
+    epi = dict(ln_w=np.array(gd["ln_w"], float), ln_b=np.array(gd["ln_b"], float),
+               r_k=np.array(gd["r_k"], float), eps=gd["eps"])
+    y, sT = oracle.forward_fused(sh(gd["r"]), sh(gd["w"]), sh(gd["k"]), sh(gd["v"]),
+                                 sh(gd["a"]), np.array(gd["k_k"], float),
+                                 np.array(gd["k_a"], float), g=sh(gd["g"]),
+                                 s0=np.array(gd["s0"], float)[None, None], epilogue=epi)
+    assert np.array_equal(y[0, 0, 0], np.array(gd["y"], float))
+    assert np.array_equal(sT[0, 0], np.array(gd["s_T"], float))

@@ -97,3 +97,70 @@ def test_unmodified_source_passes_every_pin(tmp_path, monkeypatch):
     monkeypatch.setattr(oracle, "_lib", _as_oracle_lib(path))
     for pin, call in PIN_CALLS:
         call()
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes in the Python oracle's fused prologue / gate composition
+# (oracle.prologue and oracle.forward_fused).  Each mutant is a copy of the
+# function's source with one mistake, executed in the oracle's namespace; the
+# hand-worked fused example must fail for every one of them.
+# ---------------------------------------------------------------------------
+import inspect  # noqa: E402
+
+_FUSED_SRC = inspect.getsource(oracle.forward_fused)
+_PRO_SRC = inspect.getsource(oracle.prologue)
+_GATE_LATE = ("    y, sT = forward(r, w, k_t, v, kappa, a, s0=s0, epilogue=epilogue, threads=threads)\n"
+              "    if g is not None:\n"
+              "        y = y * np.asarray(g, np.float64)\n")
+
+FUSED_MUTANTS = {
+    # the gate multiplies the readouts before the GroupNorm
+    "gate before norm": ("forward_fused", _FUSED_SRC, _GATE_LATE,
+                         "    y, sT = forward(r, w, k_t, v, kappa, a, s0=s0, threads=threads)\n"
+                         "    if g is not None:\n"
+                         "        y = y * np.asarray(g, np.float64)\n"
+                         "    if epilogue is not None:\n"
+                         "        H, N = y.shape[-2:]\n"
+                         "        y = group_norm_heads(y, epilogue.get('ln_w'), epilogue.get('ln_b'),\n"
+                         "                             epilogue.get('eps', 64e-5))\n"
+                         "        y = y + bonus(r, k_t, np.asarray(epilogue['r_k']).reshape(H, N), v)\n"),
+    # the gate multiplies after the norm but before the bonus is added
+    "gate before bonus": ("forward_fused", _FUSED_SRC, _GATE_LATE,
+                          "    y, sT = forward(r, w, k_t, v, kappa, a, s0=s0, threads=threads)\n"
+                          "    if epilogue is not None:\n"
+                          "        H, N = y.shape[-2:]\n"
+                          "        y = group_norm_heads(y, epilogue.get('ln_w'), epilogue.get('ln_b'),\n"
+                          "                             epilogue.get('eps', 64e-5))\n"
+                          "    if g is not None:\n"
+                          "        y = y * np.asarray(g, np.float64)\n"
+                          "    if epilogue is not None:\n"
+                          "        y = y + bonus(r, k_t, np.asarray(epilogue['r_k']).reshape(H, N), v)\n"),
+    # the raw key is written (and used by the bonus) instead of the boosted one
+    "raw key written": ("forward_fused", _FUSED_SRC, "forward(r, w, k_t, v,", "forward(r, w, k, v,"),
+    # the removal key is formed from the boosted key
+    "kappa after booster": ("prologue", _PRO_SRC, "kk = k * np.asarray(k_k",
+                            "kk = (k + k * (a - 1.0) * np.asarray(k_a, np.float64).reshape(H, N))"
+                            " * np.asarray(k_k"),
+    # the removal key is not normalised
+    "kappa not normalised": ("prologue", _PRO_SRC, "kappa = kk / np.maximum(nrm, 1e-12)",
+                             "kappa = kk"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED_MUTANTS))
+def test_planted_fused_mistake_is_caught(name, monkeypatch):
+    fname, src, old, new = FUSED_MUTANTS[name]
+    assert old in src, f"mutation site for {name!r} not found"
+    ns = dict(vars(oracle))
+    exec(compile(src.replace(old, new), f"<mutant {name}>", "exec"), ns)
+    monkeypatch.setattr(oracle, fname, ns[fname])
+    if fname == "prologue":  # forward_fused looks the prologue up in the module
+        ns2 = dict(vars(oracle))
+        exec(compile(_FUSED_SRC, "<forward_fused>", "exec"), ns2)
+        monkeypatch.setattr(oracle, "forward_fused", ns2["forward_fused"])
+    with pytest.raises(AssertionError):
+        pins.test_forward_fused_worked_example()
+
+
+def test_unmodified_fused_passes_the_pin():
+    pins.test_forward_fused_worked_example()
