@@ -81,6 +81,21 @@ def decay_from_logit(z: np.ndarray) -> np.ndarray:
     return np.exp(-_sigmoid(z.astype(np.float32)) * np.float32(_INV_SQRT_E)).astype(np.float32)
 
 
+def _correlated_keys(rng, B, T, H, N, cos, flip):
+    """Removal keys [B,T,H,N] float32 sharing a direction per (b, h) (see draw)."""
+    f32 = np.float32
+    if flip is not None:
+        base = np.where(rng.random((B, 1, H, N)) < 0.5, f32(-1.0), f32(1.0))
+        flips = np.where(rng.random((B, T, H, N)) < flip, f32(-1.0), f32(1.0))
+        return (base * flips * f32(1.0 / math.sqrt(N))).astype(f32)
+    d = _normalise_last(rng.standard_normal((B, 1, H, N), dtype=f32)).astype(np.float64)
+    n = rng.standard_normal((B, T, H, N), dtype=f32).astype(np.float64) / math.sqrt(N)
+    if cos >= 1.0:
+        return np.broadcast_to(d, (B, T, H, N)).astype(f32)
+    alpha = math.sqrt(cos / (1.0 - cos))
+    return _normalise_last(alpha * d + n)
+
+
 class Inputs(dict):
     """Dict of arrays plus metadata (shape, dtype name, epilogue flag)."""
 
@@ -114,6 +129,11 @@ def draw(
     w_recipe: str = "default",
     a_mean: float = 0.0,
     epilogue: bool = False,
+    kappa_cos: float | None = None,
+    kappa_signs: float | None = None,
+    k_align: bool = False,
+    a_const: float | None = None,
+    w_const: float | None = None,
 ) -> Inputs:
     """Draw one forward-pass input set.
 
@@ -127,6 +147,24 @@ def draw(
       "slow"    : w = clamp(exp(-sigmoid(z - 8)/sqrt(e)), 0.99, 1)
     s0: "zero" or "normal" (N(0, s0_std), float32).
     dtype: "bf16", "f32", or "bf16_w32" (bf16 except w, which stays float32).
+
+    Removal keys correlated within a sequence (the delta-rule regime of the
+    RWKV-7 "Goose" summary, §2 Background and App. D.3: repeated or similar
+    keys overwrite what the state holds for them).  These draws come after all
+    of the above, so the other draws are the same with or without them:
+      kappa_cos   : kappa = normalise(alpha d + n / sqrt(N)) with one unit
+                    direction d ~ normalised N(0, I) per (b, h) and n ~ N(0, I)
+                    per token, alpha = sqrt(c / (1 - c)): the mean pairwise
+                    cosine of two tokens' keys is close to c (c = 1: one
+                    repeated key);
+      kappa_signs : kappa = s / sqrt(N) with s in {-1, +1}^N: one sign pattern
+                    per (b, h), each sign flipped independently per token with
+                    this probability p (mean cosine (1 - 2p)^2).  For N = 64 every
+                    entry is +-1/8, so the bf16 key has norm exactly 1;
+      k_align     : the written key is k = sqrt(N) kappa (the listing forms kappa
+                    from k, so the two point the same way); for N = 64 a power
+                    of two times kappa, so bf16(k) = 8 bf16(kappa);
+      a_const, w_const : every a (every w) equal to this value.
     """
     rng = np.random.default_rng(seed)
     shp = (B, T, H, N)
@@ -151,6 +189,14 @@ def draw(
     del kz
     a = _sigmoid(az + f32(a_mean)).astype(f32)
     del az
+    if kappa_cos is not None or kappa_signs is not None:
+        kappa = _correlated_keys(rng, B, T, H, N, kappa_cos, kappa_signs)
+    if k_align:
+        k = (kappa * f32(math.sqrt(N))).astype(f32)
+    if a_const is not None:
+        a = np.full(shp, a_const, dtype=f32)
+    if w_const is not None:
+        w = np.full(shp, w_const, dtype=f32)
     if s0 == "zero":
         S0 = None
     elif s0 == "normal":
