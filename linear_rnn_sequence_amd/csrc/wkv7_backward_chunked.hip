@@ -10,7 +10,8 @@
 // these formulas in fp64 against autograd of the per-token loop):
 //   g_t = prod_{s<=t} w_s, gp_t = g_{t-1}; Kp = kappa*gp, Rp = r*g, Km = k/g,
 //   Bm = (a*kappa)/g; Mkk = stril(Kp Km^T), N = stril(Kp Bm^T),
-//   Mkr = tril(Rp Km^T), Mbr = tril(Rp Bm^T); X = (I + N)^-1;
+//   Mkr = tril(Rp Km^T), Mbr = tril(Rp Bm^T); X = (I + N)^-1 (by block
+//   substitution, tri_inverse in wkv7_mfma.h);
 //   U = X (Kp S0^T + Mkk V) (the chunk's S_{t-1} kappa_t), Y = Rp S0^T + Mkr V - Mbr U,
 //   S_C = (S0 + V^T Km - U^T Bm) diag(g_C).
 // Its reverse-mode derivative, with dSh = dS_C diag(g_C) and dS_C the cotangent
@@ -53,15 +54,10 @@
 // stored that way.
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 namespace {
-
-typedef short bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kC = 16;        // tokens per chunk (the checkpoint interval)
 constexpr int kThreads = 256;  // four waves
@@ -71,25 +67,18 @@ constexpr int kGradChunks = 8;  // consecutive chunks of one head per gradient w
 
 static_assert(kC == kCkpt, "chunks are the checkpoint intervals");
 
-__device__ __forceinline__ f32x4 mma(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-// two floats -> packed bf16 pair, round to nearest even (a vector conversion, so
-// the compiler inserts the wait states an MFMA result needs before a VALU read)
-__device__ __forceinline__ unsigned cvt2(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ bf16x4 bf4(f32x4 x) {
-    const u32x2 v = {cvt2(x[0], x[1]), cvt2(x[2], x[3])};
-    return __builtin_bit_cast(bf16x4, v);
-}
+// every product of this file is a 16x16x16 MFMA: accumulators are Acc16
+__device__ __forceinline__ Acc16 mma(bf16x4 a, bf16x4 b, Acc16 c) { return mfma16(a, b, c); }
+// two floats -> packed bf16 pair, round to nearest even (the hardware conversion)
+__device__ __forceinline__ unsigned cvt2(float lo, float hi) { return cvt_pk(lo, hi); }
+__device__ __forceinline__ bf16x4 bf4(f32x4 x) { return to_bf16(x); }
+__device__ __forceinline__ bf16x4 bf4(Acc16 x) { return to_bf16(x.v); }
 // one float -> bf16 bits, round to nearest even (the same hardware conversion)
 __device__ __forceinline__ short bf1(float x) { return (short)(cvt2(x, 0.f) & 0xffffu); }
 __device__ __forceinline__ uint16_t bf1u(float x) { return (uint16_t)(cvt2(x, 0.f) & 0xffffu); }
 __device__ __forceinline__ float fbf(short s) { return __uint_as_float(((uint32_t)(uint16_t)s) << 16); }
-__device__ __forceinline__ f32x4 z4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-__device__ __forceinline__ f32x4 neg(f32x4 x) { return f32x4{-x[0], -x[1], -x[2], -x[3]}; }
+__device__ __forceinline__ Acc16 z4() { return Acc16::zero(); }
+__device__ __forceinline__ Acc16 neg(Acc16 x) { return Acc16{-x.v}; }
 
 template <int S>
 __device__ __forceinline__ bf16x4 frag(const short (*m)[S], int row0, int col0, int lane) {
@@ -107,39 +96,15 @@ __device__ __forceinline__ bf16x4 colfrag(const short (*m)[S], int col0, int lan
 // Keep the entries of a result tile D[4g+e][lo] that satisfy a triangle:
 // kLower: col <= row (kStrict: col < row); else row <= col (kStrict: row < col).
 template <bool kLower, bool kStrict>
-__device__ __forceinline__ f32x4 mask(f32x4 d, int lane) {
+__device__ __forceinline__ Acc16 mask(Acc16 d, int lane) {
     const int lo = lane & 15, row = 4 * (lane >> 4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int r = row + e;
         const bool keep = kLower ? (kStrict ? lo < r : lo <= r) : (kStrict ? r < lo : r <= lo);
-        d[e] = keep ? d[e] : 0.f;
+        d.v[e] = keep ? d[e] : 0.f;
     }
     return d;
-}
-
-// D(((I + M)^-1)^T) for a nilpotent 16 x 16 M given dm = D(M), dmt = D(M^T):
-// (I + M)^-1 = (I - M)(I + M^2)(I + M^4)(I + M^8), evaluated transposed as
-//   F^T = (I - M^T) + (M^2)^T (I - M^T),  G^T = F^T + (M^4)^T F^T,
-//   X^T = G^T + (M^8)^T G^T.
-// Called with (D(N), D(N^T)) it gives D(X^T) = A operand of X; with the
-// arguments swapped it gives D(X) = A operand of X^T.
-__device__ __forceinline__ f32x4 inverse_t(f32x4 dm, f32x4 dmt, int lane) {
-    const int lo = lane & 15, row = 4 * (lane >> 4);
-    f32x4 imt;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) imt[e] = (row + e == lo ? 1.f : 0.f) - dmt[e];
-    const bf16x4 Mb = bf4(dm), Ma = bf4(dmt);
-    const f32x4 m2 = mma(Ma, Mb, z4());   // D(M^2)
-    const f32x4 m2t = mma(Mb, Ma, z4());  // D((M^2)^T)
-    const bf16x4 M2b = bf4(m2), M2a = bf4(m2t);
-    const f32x4 m4 = mma(M2a, M2b, z4());   // D(M^4)
-    const f32x4 m4t = mma(M2b, M2a, z4());  // D((M^4)^T)
-    const f32x4 ft = mma(M2b, bf4(imt), imt);  // D(F^T)
-    const bf16x4 M4b = bf4(m4);
-    const f32x4 gt = mma(M4b, bf4(ft), ft);    // D(G^T)
-    const f32x4 m8 = mma(bf4(m4t), M4b, z4()); // D(M^8)
-    return mma(bf4(m8), bf4(gt), gt);          // D(X^T)
 }
 
 // the decay's element type: bf16 bits, or float32 (RWKV7_DT_BF16_W32)
@@ -177,13 +142,13 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
     const uint16_t *pdy = static_cast<const uint16_t *>(p.dy);
 
     // dS^T tiles: St[jb] holds dS^T[16jb + g4 + e][16 wave + lo] = dS[16 wave + lo][16jb + g4 + e]
-    f32x4 St[4];
+    Acc16 St[4];
     const long srow = (long)(16 * wave + lo) * kN;
 #pragma unroll
     for (int jb = 0; jb < 4; ++jb) {
         if (p.ds_T) {
             const float4 x = *reinterpret_cast<const float4 *>(p.ds_T + bh * kN * kN + srow + 16 * jb + g4);
-            St[jb] = f32x4{x.x, x.y, x.z, x.w};
+            St[jb] = Acc16{f32x4{x.x, x.y, x.z, x.w}};
         } else {
             St[jb] = z4();
         }
@@ -243,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         __syncthreads();
 
         // ---- chunk matrices (every wave forms its own copy)
-        f32x4 dn = z4(), dnt = z4(), dmbr = z4();
+        Acc16 dn = z4(), dnt = z4(), dmbr = z4();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), bma = frag(L.bm, 0, 16 * kb, lane);
@@ -255,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
         dn = mask<true, true>(dn, lane);
         dnt = mask<false, true>(dnt, lane);
         dmbr = mask<true, false>(dmbr, lane);
-        const f32x4 dx = inverse_t(dnt, dn, lane);  // D(X) = A operand of X^T
+        f32x4 dx, dxt;  // D(X) = A operand of X^T (D(X^T) unused here)
+        tri_inverse(dn.v, dnt.v, lane, dx, dxt);
 
         // ---- chain step: dSh = dS_C diag(g_C), stored as the bf16 MFMA operand
         // that both kernels use, then dS0 of the chunk
@@ -264,15 +230,15 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) St[jb][e] *= L.gc[16 * jb + g4 + e];
+            for (int e = 0; e < 4; ++e) St[jb].v[e] *= L.gc[16 * jb + g4 + e];
             Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
             *reinterpret_cast<bf16x4 *>(ck + 16 * jb + g4) = Sb[jb];
         }
         const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY (tokens x values)
-        f32x4 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
+        Acc16 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) rhs = mma(frag(L.bm, 0, 16 * jb, lane), Sb[jb], rhs);  // + Bm dSh^T
-        const f32x4 up = mma(bf4(dx), bf4(rhs), z4());  // X^T rhs = -dZ
+        const Acc16 up = mma(bf4(dx), bf4(rhs), z4());  // X^T rhs = -dZ
         const bf16x4 dzb = bf4(neg(up));
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
@@ -486,10 +452,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
             __syncthreads();
         }
-        if (c + 1 < c_end) load_chunk(c + 1);  // in flight during the rest of this chunk
 
         // ---- chunk matrices (every wave forms its own copy)
-        f32x4 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
+        Acc16 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
@@ -507,8 +472,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         dnt = mask<false, true>(dnt, lane);
         dmkr = mask<true, false>(dmkr, lane);
         dmbr = mask<true, false>(dmbr, lane);
-        const f32x4 dxt = inverse_t(dn, dnt, lane);  // D(X^T) = A operand of X
-        const f32x4 dx = inverse_t(dnt, dn, lane);   // D(X)   = A operand of X^T
+        f32x4 dx, dxt;  // D(X) = A operand of X^T, D(X^T) = A operand of X
+        tri_inverse(dn.v, dnt.v, lane, dx, dxt);
+        // the next chunk's inputs, in flight during the rest of this chunk (issued
+        // after the inverse, whose temporaries would otherwise sit beside them)
+        if (c + 1 < c_end) load_chunk(c + 1);
 
         // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
         {
@@ -526,9 +494,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
             const bf16x4 vb = colfrag(L.vv, 16 * wave, lane);    // B operand of V
             const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY
-            f32x4 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
-            f32x4 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
-            f32x4 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
+            Acc16 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
+            Acc16 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
+            Acc16 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 const bf16x4 s0b = bf4(S0[jb]), dhb = Dh[jb];  // B operands of S0^T, dSh^T
@@ -537,8 +505,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
             }
             du = neg(du);
-            const f32x4 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
-            const f32x4 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
+            const Acc16 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
+            const Acc16 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
             dv = mma(bf4(dmkk), bf4(dz), dv);              // + Mkk^T dZ
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -553,9 +521,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
         // ---- phase 3: key block `wave` (tokens x keys 16 wave ..)
         {
-            f32x4 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
-            f32x4 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
-            f32x4 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
+            Acc16 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
+            Acc16 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
+            Acc16 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
                 const bf16x4 ya = frag(L.dyy, 0, 16 * vb, lane), va = frag(L.vv, 0, 16 * vb, lane);
@@ -620,9 +588,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const bf16x4 rpb = colfrag(L.rp, 16 * wave, lane), kpb = colfrag(L.kp, 16 * wave, lane);
             const bf16x4 kmb = colfrag(L.km, 16 * wave, lane), bmb = colfrag(L.bm, 16 * wave, lane);
             // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
-            f32x4 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
+            Acc16 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
             // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
-            f32x4 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
+            Acc16 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
             dbm = neg(dbm);
             // dRp = dY S0 + dMkr Km + dMbr Bm
             drp = mma(bf4(dmrt), kmb, drp);

@@ -23,10 +23,11 @@
 // needs a sign flip.
 // Every product is a 16 x 16 bf16 MFMA with fp32 accumulation (pairs of K = 16
 // products as one v_mfma_f32_16x16x32_bf16); the state stays fp32 in the
-// accumulators.  The unit lower-triangular inverse uses
-// (I+N)^-1 = (I-N)(I+N^2)(I+N^4)(I+N^8) for the nilpotent N = M_bk (N^16 = 0),
-// also on MFMA.  The decay ratios stay within w_min^-16 (1.6e4 for the pages'
-// w > 0.545).  Requires 0 < w <= 1.
+// accumulators.  The unit lower-triangular inverse (I + M_bk)^-1 is formed by
+// block substitution (tri_inverse in wkv7_mfma.h: float32 4 x 4 diagonal
+// blocks, then products on split bf16 operands), so it stays accurate when
+// removal keys repeat or correlate within a chunk.  The decay ratios stay
+// within w_min^-16 (1.6e4 for the pages' w > 0.545).  Requires 0 < w <= 1.
 //
 // Work split: one workgroup of 8 waves per (batch, head), walking the chunks
 // in order as a three-stage pipeline with one barrier per chunk:
@@ -75,6 +76,7 @@
 // So a D tile is directly a B operand, and the A form of X is the B form of X^T.
 #include "wkv7_device.h"
 #include "wkv7_internal.h"
+#include "wkv7_mfma.h"
 
 namespace wkv7 {
 
@@ -124,50 +126,6 @@ constexpr int kPTileRows = 672;  // Kp, Rp, Km, Bm pair tiles
 constexpr int kPTileCols = 648;  // (Km^T | Bm^T) pair tiles
 constexpr int kTileVt = 324;     // V^T tiles
 constexpr int kTileVr = 336;     // V row tiles
-
-typedef short bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ f32x4 mfma(bf16x4 a, bf16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
-}
-
-typedef short bf16x8s __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
-// Two K = 16 products summed in one v_mfma_f32_16x16x32_bf16:
-//   c + A0 B0 + A1 B1   (A0, A1 in K = 16 A form; B0, B1 in K = 16 B form),
-// with a = (A0 | A1) and b = (B0 | B1) side by side in the lanes.  Each lane
-// holds 8 consecutive k of the K = 32 operands in both A and B, so every k of
-// A0 pairs with the same k of B0 and likewise for A1, B1: the contraction over
-// the 32 k is the sum of the two 16-k contractions.
-__device__ __forceinline__ f32x4 mfma2(bf16x8s a, bf16x8s b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-}
-
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32;
-// written as a vector conversion so the compiler sees it and inserts the wait
-// states an MFMA result needs before a VALU reads it)
-__device__ __forceinline__ unsigned cvt_pk(float lo, float hi) {
-    const f32x2 v = {lo, hi};
-    return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ bf16x4 to_bf16(f32x4 x) {
-    u32x2 v = {cvt_pk(x[0], x[1]), cvt_pk(x[2], x[3])};
-    return __builtin_bit_cast(bf16x4, v);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// value of lane E of this lane's quad (DPP quad_perm [E, E, E, E])
-template <int E>
-__device__ __forceinline__ float quad_bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), E * 0x55, 0xF, 0xF, true));
-}
 
 struct __align__(16) ChunkOps {
     // pair tiles over key blocks (2p | 2p+1), rows t (or s), columns j
@@ -458,38 +416,23 @@ struct Chunked {
             // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
             const bf16x8s kp01 = ld_pair(o.kp[0], lane), kp23 = ld_pair(o.kp[1], lane);
             const bf16x8s bm01 = ld_pair(o.bm[0], lane), bm23 = ld_pair(o.bm[1], lane);
-            f32x4 nb = mfma2(kp23, bm23, mfma2(kp01, bm01, zero4()));
-            f32x4 na = mfma2(bm23, kp23, mfma2(bm01, kp01, zero4()));
-            f32x4 imnt;  // D(I - N^T)
+            f32x4 nb = mfma32(kp23, bm23, mfma32(kp01, bm01, Acc32::zero())).v;
+            f32x4 na = mfma32(bm23, kp23, mfma32(bm01, kp01, Acc32::zero())).v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 nb[e] = (lo < row + e) ? nb[e] : 0.f;   // [t = row+e][s = lo], s < t
                 na[e] = (row + e < lo) ? na[e] : 0.f;   // [s = row+e][t = lo], s < t
-                imnt[e] = (row + e == lo ? 1.f : 0.f) - na[e];
             }
-            // X = (I + N)^-1 = F1 (I + N^4)(I + N^8) with F1 = (I - N)(I + N^2), all
-            // polynomials in N (they commute); evaluated as
-            //   F1^T = (I - N^T) + N2^T (I - N^T),  G^T = F1^T + N4^T F1^T,
-            //   X^T = G^T + N8^T G^T
-            // so the chain is N, N^2, N^4 | F1^T, N^8 | G^T, X^T: four products deep
-            const bf16x4 Nb = to_bf16(nb), Na = to_bf16(na);
-            const f32x4 n2 = mfma(Na, Nb, zero4());                // D(N^2)
-            const f32x4 n2t = mfma(Nb, Na, zero4());               // D(N^2^T)
-            const bf16x4 N2b = to_bf16(n2), N2a = to_bf16(n2t);
-            const f32x4 n4 = mfma(N2a, N2b, zero4());              // D(N^4)
-            const f32x4 n4t = mfma(N2b, N2a, zero4());             // D(N^4^T)
-            const f32x4 f1t = mfma(N2b, to_bf16(imnt), imnt);      // D(F1^T)
-            const bf16x4 N4b = to_bf16(n4);
-            const f32x4 gt = mfma(N4b, to_bf16(f1t), f1t);         // D(G^T)
-            const f32x4 n8 = mfma(to_bf16(n4t), N4b, zero4());     // D(N^8)
-            const f32x4 z = mfma(to_bf16(n8), to_bf16(gt), gt);    // D(X^T) = A form of X
-            st_a(o.xinv, lane, to_bf16(-z));                       // stored negated
+            f32x4 dx, dxt;
+            tri_inverse(nb, na, lane, dx, dxt);
+            st_a(o.xinv, lane, to_bf16(-dxt));  // A form of X = D(X^T), stored negated
         } else {
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kPTileRows] = (blk == 3) ? o.bm : o.km;
             const short(*rhs)[kPTileRows] = (blk == 0) ? o.kp : o.rp;
-            f32x4 m = mfma2(ld_pair(lhs[0], lane), ld_pair(rhs[0], lane), zero4());
-            m = mfma2(ld_pair(lhs[1], lane), ld_pair(rhs[1], lane), m);
+            f32x4 m = mfma32(ld_pair(lhs[1], lane), ld_pair(rhs[1], lane),
+                             mfma32(ld_pair(lhs[0], lane), ld_pair(rhs[0], lane), Acc32::zero()))
+                          .v;
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
             const float diag = (blk != 0) ? o.rsum[blk == 2 ? 0 : 1][lo] : 0.f;
 #pragma unroll
@@ -561,7 +504,8 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
 // YADD: add the float32 readouts p.y_add (the reverse pass of a bidirectional
 // call) before the epilogue.
 template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD>
-__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_kernel(
+__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads)
+__attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
     ChunkedParams cp) {
     __shared__ ChunkSmem sm;
     const ForwardArgs &p = cp.p;
@@ -592,16 +536,16 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
     if (chain_wave) {
         // ---------------- chain waves: state, MFMA chain, readouts ----------------
         // S^T tile jb holds rows j = 16jb + 4g + e, column i = 16blk + lo
-        f32x4 Z[4];
+        Acc32 Z[4];
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             if (s_in) {
                 const float4 x = *reinterpret_cast<const float4 *>(s_in + srow + 16 * jb + 4 * g);
-                Z[jb] = f32x4{x.x, x.y, x.z, x.w};
+                Z[jb].v = f32x4{x.x, x.y, x.z, x.w};
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)  // identity for the transition rows
-                    Z[jb][e] = (p_rows && 16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
+                    Z[jb].v[e] = (p_rows && 16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
             }
         }
         // GroupNorm weight and bias of this lane's four value channels
@@ -635,7 +579,7 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
         auto store_state = [&](float *dst) {  // non-temporal: read back only by the backward
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb)
-                __builtin_nontemporal_store(Z[jb],
+                __builtin_nontemporal_store(Z[jb].v,
                                             reinterpret_cast<f32x4 *>(dst + srow + 16 * jb + 4 * g));
         };
         if (ckpt && nch > 0) store_state(ckpt);  // the state before chunk 0
@@ -666,39 +610,39 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
                 // one opcode
                 VU.lo = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
                 bf16x8s Z01, Z23;
-                Z01.lo = to_bf16(Z[0]);
-                Z01.hi = to_bf16(Z[1]);
-                Z23.lo = to_bf16(Z[2]);
-                Z23.hi = to_bf16(Z[3]);
+                Z01.lo = to_bf16(Z[0].v);
+                Z01.hi = to_bf16(Z[1].v);
+                Z23.lo = to_bf16(Z[2].v);
+                Z23.hi = to_bf16(Z[3].v);
                 // rhs = M_kk V + Kp S0^T; (M_kk | 0) meets (V | the previous chunk's
                 // -U), whose product with the zero half vanishes
-                f32x4 rhs = mfma2(ld_pair(o.mkz, lane), VU, zero4());
-                rhs = mfma2(ld_pair(o.kp[0], lane), Z01, rhs);
-                rhs = mfma2(ld_pair(o.kp[1], lane), Z23, rhs);
+                Acc32 rhs = mfma32(ld_pair(o.mkz, lane), VU, Acc32::zero());
+                rhs = mfma32(ld_pair(o.kp[0], lane), Z01, rhs);
+                rhs = mfma32(ld_pair(o.kp[1], lane), Z23, rhs);
                 // readouts as Y^T = S0 Rp^T + V^T M_kr^T - U^T M_br^T (the operands of
                 // Y with their roles swapped): lane holds Y^T[i = 4g+e][t = lo]; the
                 // terms without U first, so only one product waits for U
-                f32x4 Y = mfma2(Z01, ld_pair(o.rp[0], lane), zero4());
-                Y = mfma2(Z23, ld_pair(o.rp[1], lane), Y);
-                const f32x4 U = mfma(ld_a(o.xinv, lane), to_bf16(rhs), zero4());  // -U
-                VU.hi = to_bf16(U);
-                Y = mfma2(VU, ld_pair(o.mrb, lane), Y);
+                Acc32 Y = mfma32(Z01, ld_pair(o.rp[0], lane), Acc32::zero());
+                Y = mfma32(Z23, ld_pair(o.rp[1], lane), Y);
+                const Acc16 U = mfma16(ld_a(o.xinv, lane), to_bf16(rhs.v), Acc16::zero());  // -U
+                VU.hi = to_bf16(U.v);
+                Y = mfma32(VU, ld_pair(o.mrb, lane), Y);
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
-                    Z[jb] = mfma2(ld_pair(o.kbt[jb], lane), VU, Z[jb]);
+                    Z[jb] = mfma32(ld_pair(o.kbt[jb], lane), VU, Z[jb]);
                     const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
-                    Z[jb][0] *= gc.x;
-                    Z[jb][1] *= gc.y;
-                    Z[jb][2] *= gc.z;
-                    Z[jb][3] *= gc.w;
+                    Z[jb].v[0] *= gc.x;
+                    Z[jb].v[1] *= gc.y;
+                    Z[jb].v[2] *= gc.z;
+                    Z[jb].v[3] *= gc.w;
                 }
                 if (kYadd) {  // (a padding token's sum is never stored)
-                    Y[0] += ya.x;
-                    Y[1] += ya.y;
-                    Y[2] += ya.z;
-                    Y[3] += ya.w;
+                    Y.v[0] += ya.x;
+                    Y.v[1] += ya.y;
+                    Y.v[2] += ya.z;
+                    Y.v[3] += ya.w;
                 }
-                pd.y = Y;
+                pd.y = Y.v;
                 // stored states: the one leaving this chunk enters the next; stored
                 // here, in the slack before the barrier, rather than just before
                 // the MFMAs that overwrite the accumulators
@@ -797,14 +741,16 @@ __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads) void chunked_
             for (int d = 0; d < kUnroll; ++d) {
                 const int q = q0 + d;
                 Raw<W32> &x = xs[d % kPrefetch];
-                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
-                // widen the slot, form chunk q's operands and refill the slot with
-                // chunk q + kPrefetch (clamped: always the same loads per
-                // interval; refilling before the operands are formed keeps both
-                // live and, with the fused prologue, costs the register budget
-                // that lets two workgroups share a CU)
+                // widen the slot and form chunk q's operands, then chunk q-1's
+                // matrices (q >= 1) while the slot is free, then refill the slot
+                // with chunk q + kPrefetch (clamped: always the same loads per
+                // interval).  Refilling before the operands are formed keeps both
+                // live, and forming the matrices with all four slots full keeps
+                // the triangular inverse's temporaries beside them: either costs
+                // the register budget that lets two workgroups share a CU.
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
                 K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1][blk]);
+                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];
