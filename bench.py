@@ -12,7 +12,9 @@ layer's heads).  Inputs are resident in HBM before the timed region.
 Prints ONE JSON line.  Extra options (--only, --copy-probe, --steps,
 --prefill-shape) exist for profiling runs; "--only prefill --prefill-shape long"
 times the long-context prefill instead (B=1, T=65536, H=40, slow decay, no
-epilogue), which the chunked path splits into parallel time segments.
+epilogue), which the chunked path splits into parallel time segments, and
+"--only prefill --prefill-shape 0.19b" the 0.19B-model shape (B=4, T=1024,
+H=12, initial states ~ N(0, 0.1), no epilogue).
 """
 from __future__ import annotations
 
@@ -36,7 +38,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0
 N = 64
 PREFILL = dict(B=8, T=4096, H=40)
 # prefill shapes: (synthetic config index, shape, fused epilogue)
-PREFILL_SHAPES = {"2.9b": (2, PREFILL, True), "long": (4, dict(B=1, T=65536, H=40), False)}
+PREFILL_SHAPES = {"2.9b": (2, PREFILL, True), "long": (4, dict(B=1, T=65536, H=40), False),
+                  "0.19b": (1, dict(B=4, T=1024, H=12), False)}
 DECODE = dict(layers=32, B=256, H=40, steps=64)
 
 
@@ -59,7 +62,7 @@ def parse():
     ap.add_argument("--bwd-algo", default="auto", choices=["auto", "scan", "chunked"],
                     help="backward algorithm of --only train (auto: chunked for bf16)")
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
-                    help="'long' needs --only prefill")
+                    help="'long' and '0.19b' need --only prefill")
     ap.add_argument("--decode-head", type=int, default=64, choices=[64, 128],
                     help="decode head size; 128 keeps the state bytes (H = 20) and needs "
                          "--only decode")
@@ -188,6 +191,9 @@ BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
 
 
 def workload_name(args, long_shape, do_prefill, do_decode):
+    if args.prefill_shape == "0.19b":
+        return ("0.19B-shape WKV7 prefill B4 T1024 H12 N64 from initial states ~ N(0, 0.1) "
+                "(no epilogue)")
     if long_shape:
         return ("long-context WKV7 prefill B1 T65536 H40 N64 (slow decay, no epilogue"
                 + (", decay w in float32)" if args.decay_f32 else ")"))
@@ -366,8 +372,8 @@ def main():
         print("bench.py: --fused needs --only prefill or --only decode", file=sys.stderr)
         sys.exit(2)
     if (args.prefill_shape != "2.9b" or args.bidir) and args.only != "prefill":
-        print("bench.py: --prefill-shape long and --bidir are prefill-only measurements "
-              "(--only prefill)", file=sys.stderr)
+        print("bench.py: --prefill-shape long / 0.19b and --bidir are prefill-only "
+              "measurements (--only prefill)", file=sys.stderr)
         sys.exit(2)
     if args.decay_f32 and args.only not in ("prefill", "train"):
         print("bench.py: --decay-f32 needs --only prefill (long context) or --only train",
@@ -414,6 +420,7 @@ def main():
             if cfg_idx != 4:
                 raise SystemExit("--decay-f32 is defined for the long-context shape")
             pd["w"] = torch.from_numpy(_slow_decay_f32(px)).to(dev)
+        p_s0 = None if px["s0"] is None else torch.from_numpy(px["s0"]).to(dev)
         e = px["epi"]
         p_epi = None
         if p_with_epi:
@@ -441,8 +448,8 @@ def main():
                                   s_out=p_s, workspace=p_ws)
                 return
             (wkv.forward_bidir if args.bidir else wkv.forward)(
-                *(pd[n] for n in NAMES), s0=None, algo=args.prefill_algo, epilogue=p_epi, y=p_y,
-                s_out=p_s, workspace=p_ws)
+                *(pd[n] for n in NAMES), s0=p_s0, algo=args.prefill_algo, epilogue=p_epi,
+                y=p_y, s_out=p_s, workspace=p_ws)
 
     # ------------------------------------------------------------------- decode
     if do_decode:
@@ -506,6 +513,8 @@ def main():
             torch.cuda.synchronize()
             if do_decode and not args.no_cpu_baseline:
                 d_y_first = d_y[:, samp_l].cpu()
+                # final states of the first and last layer after one 64-token run
+                d_s_first = {l: pool[l].cpu().numpy() for l in (0, L - 1) if l in samp_l}
             if do_prefill:
                 p_y_first = p_y.float().cpu().numpy()
                 p_s_first = p_s.cpu().numpy()
@@ -550,6 +559,8 @@ def main():
     long_shape = args.prefill_shape == "long"
     out = {
         "metric": ("WKV7 tokens x heads per second (long-context prefill)" if long_shape else
+                   "WKV7 tokens x heads per second (0.19B-shape prefill)"
+                   if args.prefill_shape == "0.19b" else
                    "WKV7 tokens x heads per second (bidirectional 2.9B-shape prefill)"
                    if args.bidir else
                    "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)"),
@@ -602,15 +613,19 @@ def main():
         out["roofline"]["frac_of_copy"] = achieved / cc["GBps_at_launch_size"]
     if do_prefill:
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
-        # six inputs + y, the final state, and the epilogue parameters when fused
-        p_bytes = B * T * H * (7 + (1 if args.decay_f32 else 0)) * N * 2 + B * H * N * N * 4
+        # six inputs + y, the final state (and the initial one when given), and the
+        # epilogue parameters when fused
+        p_bytes = (B * T * H * (7 + (1 if args.decay_f32 else 0)) * N * 2
+                   + B * H * N * N * 4 * (1 if p_s0 is None else 2))
         if p_with_epi:
             p_bytes += 2 * H * N * 4 + H * N * 4
         ach = p_bytes / (prefill_ms / 1e3) / 1e9
         chunked = args.prefill_algo in ("auto", "chunked")
         src = source_hash("wkv7_chunked.hip", "wkv7_device.h")
+        plain_29b = (chunked and args.prefill_shape == "2.9b" and not args.fused
+                     and not args.bidir)
         traffic = (read_traffic("chunked_kernel_traffic_b8_t4096_h40_epilogue.txt", src)
-                   if chunked and not long_shape else None)
+                   if plain_29b else None)
         out["prefill"] = {
             "ms": prefill_ms, "token_heads_per_s": B * T * H / (prefill_ms / 1e3),
             "algo": args.prefill_algo,
@@ -625,7 +640,7 @@ def main():
         out["prefill"]["roofline"]["frac_of_copy"] = ach / copy_cc["GBps_4GiB_one_launch"]
         if not do_decode:
             out["prefill"]["roofline"]["copy_ceiling"] = copy_cc
-        if chunked and not long_shape:
+        if plain_29b:
             # executed MFMA work per launch is fixed by the kernel (counted once with
             # SQ_INSTS_VALU_MFMA_MOPS_BF16); divided by the live duration it gives the
             # MFMA utilisation against the 2.5 PFLOP/s dense bf16 peak
@@ -658,7 +673,7 @@ def main():
                 epilogue=px["epi"] if p_with_epi else None, threads=threads)
         else:
             y_ref, s_ref = (oracle.forward_bidir if args.bidir else oracle.forward)(
-                *sub, s0=None, epilogue=px["epi"] if p_with_epi else None, threads=threads)
+                *sub, s0=px["s0"], epilogue=px["epi"] if p_with_epi else None, threads=threads)
         cpu_s += time.perf_counter() - t0
         cpu_work += PREFILL["B"] * PREFILL["T"] * PREFILL["H"]
         del sub
@@ -689,7 +704,7 @@ def main():
             del y_chain, ys
         del y_ref, s_ref
     if do_decode and not args.no_cpu_baseline:
-        errs = []
+        errs, s_errs = [], []
         for li, l in enumerate(samp_l):
             # inputs of layer l for every token: [DS, B, H, N] -> [B, DS, H, N]
             seq = [np.ascontiguousarray(np.moveaxis(d_in[n][:, l].cpu().double().numpy(), 0, 1))
@@ -703,7 +718,10 @@ def main():
                                                 dk_a.cpu().double().numpy(), g=gseq,
                                                 s0=s_init[li], threads=threads)
             else:
-                y_ref, _ = oracle.forward(*seq, s0=s_init[li], threads=threads)
+                y_ref, s_ref = oracle.forward(*seq, s0=s_init[li], threads=threads)
+                if l in d_s_first:
+                    s_errs.append(np.abs(d_s_first[l] - s_ref).max() / np.abs(s_ref).max())
+                del s_ref
             cpu_s += time.perf_counter() - t0
             cpu_work += seq[0].shape[0] * seq[0].shape[1] * seq[0].shape[2]
             del seq
@@ -711,6 +729,11 @@ def main():
             errs.append(np.abs(y_got - y_ref).max() / np.abs(y_ref).max())
             del y_ref, y_got
         par["decode_y_rel_err"] = float(max(errs))
+        if s_errs:
+            par["decode_state_rel_err"] = float(max(s_errs))
+            par["decode_state_checked"] = (f"final states of layers {sorted(d_s_first)} after "
+                                           f"one {DS}-token run (all {DB} sequences x {DH} "
+                                           "heads)")
         par["decode_checked"] = (f"every output of layers 0..{len(samp_l) - 1} (all {DB} "
                                  f"sequences x {DH} heads x {DS} tokens)")
     if par:
@@ -728,6 +751,34 @@ def main():
                        + (" and " if do_prefill and do_decode else "")
                        + (f"the full decode runs of {len(samp_l)} layers" if do_decode else "")),
         }
+
+        # the same oracle on one host core, over a bounded sample of the same work
+        t0 = time.perf_counter()
+        if do_prefill and not args.fused and not args.bidir:
+            one = [px.as_f64(n)[:1] for n in NAMES]
+            if args.decay_f32:
+                one[1] = pd["w"][:1].cpu().numpy().astype(np.float64)
+            s0_one = None if px["s0"] is None else px["s0"][:1]
+            t0 = time.perf_counter()
+            oracle.forward(*one, s0=s0_one, epilogue=px["epi"] if p_with_epi else None,
+                           threads=1)
+            one_work, one_what = one[0].shape[1] * one[0].shape[2], "batch 0 of the prefill"
+        elif do_decode and not args.fused:
+            seq = [np.ascontiguousarray(np.moveaxis(d_in[n][:, 0].cpu().double().numpy(), 0, 1))
+                   for n in NAMES]
+            t0 = time.perf_counter()
+            oracle.forward(*seq, s0=s_init[0], threads=1)
+            one_work = seq[0].shape[0] * seq[0].shape[1] * seq[0].shape[2]
+            one_what = "the decode run of layer 0"
+        else:
+            one_work = 0
+        one_s = time.perf_counter() - t0
+        if one_work:
+            out["cpu_baseline_1core"] = {
+                "value": one_work / one_s, "unit": "token*heads/s", "cores": 1,
+                "kind": "oracle",
+                "sample": f"fp64 C oracle on 1 thread over {one_work} token*heads "
+                          f"({one_what}) in {one_s:.2f} s"}
 
     print(json.dumps(out))
 

@@ -44,8 +44,16 @@
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *    the call returns without waiting.
  *  - Numerics: float32 state and accumulation; y is rounded to nearest even
- *    when dt is bf16; NaN/Inf propagate; kappa is used exactly as given (not
- *    renormalised); a is not clamped.
+ *    when dt is bf16; kappa is used exactly as given (not renormalised); a is
+ *    not clamped.
+ *  - Non-finite inputs propagate, never across (batch, head) pairs: a NaN or
+ *    Inf in token t's inputs of one pair reaches that pair's readouts from
+ *    token t on (where the recurrence carries it) and its final state.  The
+ *    scan and decode leave every earlier readout as it would be without it.
+ *    RWKV7_ALGO_CHUNKED works on chunks of 16 tokens whose tokens meet in one
+ *    matrix product (where 0 * NaN is NaN): the readouts of the tokens of t's
+ *    chunk before t (tokens 16 floor(t/16) .. t-1) may become non-finite too;
+ *    earlier chunks are unaffected.
  */
 #ifndef RWKV7_WKV_H
 #define RWKV7_WKV_H
@@ -77,16 +85,24 @@ typedef enum {
                               forgetting (w near 1) survives the input rounding.  The
                               RWKV-7 "Goose" author response (paperhub) names precision
                               sensitivity of the kernel; with w in (0.99, 1), bf16 rounds
-                              most decays to exactly 1.  Forward, training forward and
-                              decode; the backward returns RWKV7_ERR_UNSUPPORTED.       */
+                              most decays to exactly 1.  Forward, training forward,
+                              bidirectional forward, decode, and the chunked backward
+                              (whose dw is then float32 too); the scan backward returns
+                              RWKV7_ERR_UNSUPPORTED, and so does the fused prologue.    */
 } rwkv7_dtype;
 
 typedef enum {
     RWKV7_ALGO_AUTO = 0,    /* CHUNKED for bf16, SCAN for f32                          */
     RWKV7_ALGO_SCAN = 1,    /* token-by-token recurrence, state kept on chip           */
-    RWKV7_ALGO_CHUNKED = 2  /* chunked-parallel form on bf16 MFMA, float32 state;      */
-                            /* bf16 only; requires 0 < w <= 1 (the pages' decay        */
-                            /* parameterisation keeps w above 0.545)                   */
+    RWKV7_ALGO_CHUNKED = 2  /* chunked-parallel form on bf16 MFMA, float32 state;
+                               bf16 only.  Domain of the decay: 2^-6 <= w <= 1.  Inside
+                               a 16-token chunk the form divides by products of up to
+                               16 decays (down to w^16 >= 2^-96, far inside the float32
+                               and bf16 exponent range); below about w = 0.0043 they
+                               underflow and the results are not finite.  The library
+                               does not read the data, so it cannot reject such w; the
+                               pages' parameterisation keeps w above 0.545.  The scan
+                               and decode accept any w.                                  */
 } rwkv7_algo;
 
 /*

@@ -741,16 +741,14 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
             for (int d = 0; d < kUnroll; ++d) {
                 const int q = q0 + d;
                 Raw<W32> &x = xs[d % kPrefetch];
-                // widen the slot and form chunk q's operands, then chunk q-1's
-                // matrices (q >= 1) while the slot is free, then refill the slot
-                // with chunk q + kPrefetch (clamped: always the same loads per
-                // interval).  Refilling before the operands are formed keeps both
-                // live, and forming the matrices with all four slots full keeps
-                // the triangular inverse's temporaries beside them: either costs
-                // the register budget that lets two workgroups share a CU.
+                // chunk q-1's matrices (q >= 1), then widen the slot, form chunk
+                // q's operands and refill the slot with chunk q + kPrefetch
+                // (clamped: always the same loads per interval; refilling before
+                // the operands are formed keeps both live and costs the register
+                // budget that lets two workgroups share a CU)
+                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
                 K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1][blk]);
-                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];

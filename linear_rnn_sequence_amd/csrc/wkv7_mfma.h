@@ -1,6 +1,6 @@
-// bf16 MFMA helpers shared by the chunked kernels (gfx950, wave64): operand
-// types, the two matrix-core opcodes with distinct accumulator types, bf16
-// conversion and splitting, and the unit lower-triangular inverse of a chunk.
+// MFMA helpers shared by the chunked kernels (gfx950, wave64): operand types,
+// the matrix-core opcodes with distinct accumulator types, bf16 conversion, and
+// the unit lower-triangular inverse of a chunk.
 //
 // Lane layouts of v_mfma_f32_16x16x16_bf16 (lane l, g = l >> 4, lo = l & 15,
 // e = 0..3):
@@ -37,6 +37,7 @@ struct Acc {
 };
 using Acc16 = Acc<16>;
 using Acc32 = Acc<32>;
+using Acc4 = Acc<4>;  // v_mfma_f32_16x16x4_f32 (float32 operands)
 
 __device__ __forceinline__ Acc16 mfma16(bf16x4 a, bf16x4 b, Acc16 c) {
     return Acc16{__builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c.v, 0, 0, 0)};
@@ -46,6 +47,40 @@ __device__ __forceinline__ Acc32 mfma32(bf16x8s a, bf16x8s b, Acc32 c) {
     return Acc32{__builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
                                                          __builtin_bit_cast(bf16x8, b), c.v, 0,
                                                          0, 0)};
+}
+
+// float32 operands, K = 4: lane (g, lo) gives A[lo][k_g] and B[k_g][lo] for the
+// instruction's g-th k.
+__device__ __forceinline__ Acc4 mfma_f32(float a, float b, Acc4 c) {
+    return Acc4{__builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c.v, 0, 0, 0)};
+}
+
+// k-block layout of a 16 x 16 M from its D layout: lane (g, lo) then holds
+// M[4e + g][lo] at element e (a transpose of the 4 x 4 (row group, element)
+// block of every column): v_permlane32_swap exchanges the upper half of its
+// first operand with the lower half of its second, v_permlane16_swap the odd
+// rows of its first with the even rows of its second.
+__device__ __forceinline__ f32x4 kblock(f32x4 x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[0]), __float_as_uint(x[2]),
+                                                    false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[1]), __float_as_uint(x[3]),
+                                                    false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    return f32x4{__uint_as_float(c[0]), __uint_as_float(c[1]), __uint_as_float(d[0]),
+                 __uint_as_float(d[1])};
+}
+// D(A B) in float32, summed over the k in the blocks of MASK (bit i: k = 4i ..
+// 4i + 3; the others hold zeros of A or B), from ka = kblock(D(A^T)) and
+// kb = kblock(D(B)): at element i lane (g, lo) holds A[lo][4i + g] and
+// B[4i + g][lo], the operands of one v_mfma_f32_16x16x4_f32 for block i.
+template <int MASK>
+__device__ __forceinline__ f32x4 mul_kblocks(f32x4 ka, f32x4 kb) {
+    Acc4 c = Acc4::zero();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        if (MASK & (1 << i)) c = mfma_f32(ka[i], kb[i], c);
+    return c.v;
 }
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
@@ -67,28 +102,6 @@ __device__ __forceinline__ f32x4 from_bf16(bf16x4 b) {
                  __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
 }
 
-// x = hi + lo to about 2^-16 of |x|: hi the nearest bf16, lo the nearest bf16 of
-// the (exact) remainder.
-struct Split {
-    bf16x4 hi, lo;
-};
-__device__ __forceinline__ Split split(f32x4 x) {
-    const bf16x4 hi = to_bf16(x);
-    return Split{hi, to_bf16(x - from_bf16(hi))};
-}
-__device__ __forceinline__ bf16x8s pair(bf16x4 x, bf16x4 y) {
-    bf16x8s p;
-    p.lo = x;
-    p.hi = y;
-    return p;
-}
-// D(A B) from the A operand of A and the B operand of B, both split: all four
-// cross products of the parts, accumulated in float32 (one opcode throughout)
-__device__ __forceinline__ f32x4 mul_split(const Split &a, const Split &b) {
-    const bf16x8s ahl = pair(a.hi, a.lo);
-    return mfma32(ahl, pair(b.hi, b.hi), mfma32(ahl, pair(b.lo, b.lo), Acc32::zero())).v;
-}
-
 // value of lane E of this lane's quad (DPP quad_perm [E, E, E, E])
 template <int E>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -102,17 +115,18 @@ __device__ __forceinline__ float quad_bcast(float x) {
 // Block substitution, whose intermediates never exceed the true inverse's
 // blocks times N's (a product form such as (I - N)(I + N^2)(I + N^4)(I + N^8)
 // builds up binomial-sized entries that must cancel, and fails for repeated or
-// correlated removal keys):
-//  1. the four 4 x 4 diagonal blocks by forward substitution in float32 on the
-//     quad of lanes that holds each block (column-wise for X, row-wise for X^T),
-//     the entries of N broadcast within the quad;
+// correlated removal keys), all in float32:
+//  1. the four 4 x 4 diagonal blocks by forward substitution on the quad of
+//     lanes that holds each block (column-wise for X, row-wise for X^T), the
+//     entries of N broadcast within the quad;
 //  2. for blocks of size 4, then 8: with N_l the entries of N below the
 //     diagonal blocks of that size (t in the lower, s in the upper half of a
 //     diagonal block of twice the size), T = N_l X and X <- X - X T (each new
 //     block is -D^-1 C A^-1 from the diagonal blocks' inverses), and likewise
-//     X^T <- X^T - T^T X^T.  The products run on the matrix cores with both
-//     operands split into high and low bf16 parts, so X keeps about 2^-16 of its
-//     size.
+//     X^T <- X^T - T^T X^T, as float32 matrix-core products
+//     (v_mfma_f32_16x16x4_f32, one per block of four k that is not all zero).
+// A caller that uses only one of dx, dxt leaves the last level's other product
+// to dead-code elimination.
 __device__ __forceinline__ void tri_inverse(f32x4 dn, f32x4 dnt, int lane, f32x4 &dx,
                                             f32x4 &dxt) {
     const int g = lane >> 4, lo = lane & 15, e0 = lo & 3;
@@ -132,20 +146,25 @@ __device__ __forceinline__ void tri_inverse(f32x4 dn, f32x4 dnt, int lane, f32x4
                y3 * quad_bcast<3>(dnt[0]);
     dx = diag ? f32x4{x0, x1, x2, x3} : zero4();
     dxt = diag ? f32x4{y0, y1, y2, y3} : zero4();
+    // N in k-block layout: element i of lane (g, lo) is N[t = lo][s = 4i + g]
+    const f32x4 kn = kblock(dnt);
+    f32x4 n4, n8;  // N below the diagonal blocks of size 4, and of size 8
 #pragma unroll
-    for (int sz = 4; sz <= 8; sz *= 2) {
-        // D(N_l^T): lane holds N[t = lo][s = 4g + e]
-        f32x4 nlt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = lo, s = 4 * g + e;
-            const bool keep = (t / (2 * sz) == s / (2 * sz)) && ((t / sz) & 1) && !((s / sz) & 1);
-            nlt[e] = keep ? dnt[e] : 0.f;
-        }
-        const Split st = split(mul_split(split(nlt), split(dx)));  // D(T), T = N_l X
-        const Split sxt = split(dxt);
-        dx = dx - mul_split(sxt, st);    // D(X - X T)
-        dxt = dxt - mul_split(st, sxt);  // D(X^T - T^T X^T)
+    for (int i = 0; i < 4; ++i) {
+        n4[i] = ((lo >> 3) == (i >> 1) && ((lo >> 2) & 1) && !(i & 1)) ? kn[i] : 0.f;
+        n8[i] = (lo >= 8 && i < 2) ? kn[i] : 0.f;
+    }
+    {  // blocks of size 4: N_4 has columns in k-blocks 0, 2 and T its rows in 1, 3
+        const f32x4 kx = kblock(dx), kxt = kblock(dxt);
+        const f32x4 kt = kblock(mul_kblocks<0x5>(n4, kx));  // T = N_4 X
+        dx = dx - mul_kblocks<0xA>(kxt, kt);                // X - X T
+        dxt = dxt - mul_kblocks<0xA>(kt, kxt);              // X^T - T^T X^T
+    }
+    {  // blocks of size 8: N_8 has columns in k-blocks 0, 1 and T its rows in 2, 3
+        const f32x4 kx = kblock(dx), kxt = kblock(dxt);
+        const f32x4 kt = kblock(mul_kblocks<0x3>(n8, kx));
+        dx = dx - mul_kblocks<0xC>(kxt, kt);
+        dxt = dxt - mul_kblocks<0xC>(kt, kxt);
     }
 }
 
