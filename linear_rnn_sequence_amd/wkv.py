@@ -148,6 +148,42 @@ def _check_same(torch, xs, shape, dtype):
             raise ValueError("inputs must live on the GPU")
 
 
+def _check_tensor(torch, t, name, shape, dtype, device):
+    """A state, output, epilogue or workspace tensor: the kernels trust the sizes the
+    C interface cannot see, so shape, dtype, layout and device are checked here."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}, not {t.device}")
+
+
+def _check_epilogue(torch, epilogue, H, N, device):
+    if epilogue is None:
+        return
+    for key in ("ln_w", "ln_b", "r_k"):
+        t = epilogue.get(key)
+        if t is None:
+            if key == "r_k":
+                raise ValueError("the epilogue needs r_k")
+            continue
+        if t.dtype != torch.float32 or t.numel() != H * N or not t.is_contiguous():
+            raise ValueError(f"epilogue {key} must be a contiguous float32 tensor of H*N "
+                             f"= {H * N} elements")
+        if t.device != device:
+            raise ValueError(f"epilogue {key} must live on {device}")
+
+
+def _check_workspace(torch, ws, device):
+    if ws is not None and (not ws.is_contiguous() or ws.device != device):
+        raise ValueError(f"the workspace must be a contiguous tensor on {device}")
+
+
 # dtype names of the workspace queries
 DTYPE_NAMES = {"f32": DT_F32, "float32": DT_F32, "bf16": DT_BF16, "bfloat16": DT_BF16,
                "bf16_w32": DT_BF16_W32}
@@ -177,6 +213,12 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
 
     B, T, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    f32, dev = torch.float32, r.device
+    _check_tensor(torch, s0, "s0", (B, H, N, N), f32, dev)
+    _check_tensor(torch, y, "y", r.shape, r.dtype, dev)
+    _check_tensor(torch, s_out, "s_out", (B, H, N, N), f32, dev)
+    _check_epilogue(torch, epilogue, H, N, dev)
+    _check_workspace(torch, workspace, dev)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
@@ -209,6 +251,14 @@ def forward_fused(r, w, k, v, a, k_k, k_a, g=None, s0=None, *, algo="auto", epil
     for prm in (k_k, k_a):
         if prm.dtype != torch.float32 or prm.numel() != H * N or not prm.is_contiguous():
             raise ValueError("k_k and k_a must be contiguous float32 tensors of H*N elements")
+        if prm.device != r.device:
+            raise ValueError(f"k_k and k_a must live on {r.device}")
+    f32, dev = torch.float32, r.device
+    _check_tensor(torch, s0, "s0", (B, H, N, N), f32, dev)
+    _check_tensor(torch, y, "y", r.shape, r.dtype, dev)
+    _check_tensor(torch, s_out, "s_out", (B, H, N, N), f32, dev)
+    _check_epilogue(torch, epilogue, H, N, dev)
+    _check_workspace(torch, workspace, dev)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
@@ -239,6 +289,12 @@ def forward_bidir(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, 
 
     B, T, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    f32, dev = torch.float32, r.device
+    _check_tensor(torch, s0, "s0", (2, B, H, N, N), f32, dev)
+    _check_tensor(torch, y, "y", r.shape, r.dtype, dev)
+    _check_tensor(torch, s_out, "s_out", (2, B, H, N, N), f32, dev)
+    _check_epilogue(torch, epilogue, H, N, dev)
+    _check_workspace(torch, workspace, dev)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
@@ -274,12 +330,18 @@ def forward_train(r, w, k, v, kappa, a, s0=None, *, algo="auto", y=None, s_out=N
 
     B, T, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    f32, dev = torch.float32, r.device
+    nck = (T + CKPT_INTERVAL - 1) // CKPT_INTERVAL
+    _check_tensor(torch, s0, "s0", (B, H, N, N), f32, dev)
+    _check_tensor(torch, y, "y", r.shape, r.dtype, dev)
+    _check_tensor(torch, s_out, "s_out", (B, H, N, N), f32, dev)
+    _check_tensor(torch, s_ckpt, "s_ckpt", (B, H, nck, N, N), f32, dev)
+    _check_workspace(torch, workspace, dev)
     if y is None:
         y = torch.empty_like(r)
     if s_out is None and want_state:
         s_out = torch.empty((B, H, N, N), dtype=torch.float32, device=r.device)
     if s_ckpt is None:
-        nck = (T + CKPT_INTERVAL - 1) // CKPT_INTERVAL
         s_ckpt = torch.empty((B, H, nck, N, N), dtype=torch.float32, device=r.device)
     need = lib().rwkv7_wkv_forward_workspace(B, T, H, N, dt, ALGOS[algo])
     if need and workspace is None:
@@ -313,6 +375,20 @@ def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=Non
     B, T, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
     _check_same(torch, (dy,), r.shape, r.dtype)
+    f32, dev = torch.float32, r.device
+    nck = (T + CKPT_INTERVAL - 1) // CKPT_INTERVAL
+    _check_tensor(torch, s_ckpt, "s_ckpt", (B, H, nck, N, N), f32, dev)
+    _check_tensor(torch, ds_T, "ds_T", (B, H, N, N), f32, dev)
+    _check_tensor(torch, ds0, "ds0", (B, H, N, N), f32, dev)
+    _check_workspace(torch, workspace, dev)
+    if grads is not None:
+        if len(grads) != 6:
+            raise ValueError("grads must hold the six gradient tensors (dr, dw, dk, dv, "
+                             "dkappa, da)")
+        for i, (name, gt) in enumerate(zip(("dr", "dw", "dk", "dv", "dkappa", "da"), grads)):
+            _check_tensor(torch, gt, name, r.shape, w.dtype if i == 1 else r.dtype, dev)
+            if gt is None:
+                raise ValueError(f"{name} is required")
     if grads is None:
         grads = tuple(torch.empty_like(w if i == 1 else r) for i in range(6))
     if ds0 is None and want_ds0:
@@ -337,6 +413,11 @@ def decode(r, w, k, v, kappa, a, state, *, epilogue=None, y=None, stream=None):
 
     B, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    _check_tensor(torch, state, "state", (B, H, N, N), torch.float32, r.device)
+    if state is None:
+        raise ValueError("decode needs the state")
+    _check_tensor(torch, y, "y", r.shape, r.dtype, r.device)
+    _check_epilogue(torch, epilogue, H, N, r.device)
     if y is None:
         y = torch.empty_like(r)
     epi_ptr, keep = _epilogue(epilogue)
@@ -362,6 +443,13 @@ def decode_fused(r, w, k, v, a, k_k, k_a, state, *, g=None, epilogue=None, y=Non
     for prm in (k_k, k_a):
         if prm.dtype != torch.float32 or prm.numel() != H * N or not prm.is_contiguous():
             raise ValueError("k_k and k_a must be contiguous float32 tensors of H*N elements")
+        if prm.device != r.device:
+            raise ValueError(f"k_k and k_a must live on {r.device}")
+    _check_tensor(torch, state, "state", (B, H, N, N), torch.float32, r.device)
+    if state is None:
+        raise ValueError("decode needs the state")
+    _check_tensor(torch, y, "y", r.shape, r.dtype, r.device)
+    _check_epilogue(torch, epilogue, H, N, r.device)
     if y is None:
         y = torch.empty_like(r)
     pro = Prologue(k_k=k_k.data_ptr(), k_a=k_a.data_ptr(),
@@ -385,8 +473,11 @@ def prepare_decode(r, w, k, v, kappa, a, state, *, y, epilogue=None, stream=None
 
     B, H, N = r.shape
     dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
-    if tuple(y.shape) != (B, H, N) or y.dtype != r.dtype:
-        raise ValueError("y must match the inputs")
+    if y is None or state is None:
+        raise ValueError("prepare_decode needs y and the state")
+    _check_tensor(torch, y, "y", r.shape, r.dtype, r.device)
+    _check_tensor(torch, state, "state", (B, H, N, N), torch.float32, r.device)
+    _check_epilogue(torch, epilogue, H, N, r.device)
     epi_ptr, keep = _epilogue(epilogue)
     fn = lib().rwkv7_wkv_decode
     args = (_ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(state), _ptr(y),
@@ -409,6 +500,8 @@ def stream_copy(src, dst, *, stream=None):
 
     if not (src.is_contiguous() and dst.is_contiguous()):
         raise ValueError("stream_copy needs contiguous tensors")
+    if src.device.type != "cuda" or dst.device != src.device:
+        raise ValueError("stream_copy needs two tensors on the same GPU")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() != nbytes:
         raise ValueError("stream_copy needs tensors of equal byte size")
