@@ -152,6 +152,27 @@ size_t rwkv7_wkv_forward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                    rwkv7_algo algo);
 
 /*
+ * rwkv7_wkv_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace.  The workspace the chunked path
+ * needs for long sequences of few heads comes from a fixed 24 MiB device array
+ * of the library (one per device, held until the process ends); its address is
+ * looked up once per device on the first call with that device current.  The
+ * call itself allocates nothing.
+ * Errors: those of rwkv7_wkv_forward, and RWKV7_ERR_WORKSPACE when
+ * rwkv7_wkv_forward_workspace(...) for these arguments exceeds 24 MiB (it does
+ * not on a device of up to 256 compute units).
+ * Every call on one device shares that device's array: calls that overlap in
+ * time on one device (several streams or host threads) race on it and must be
+ * serialised by the caller; calls whose workspace size is 0 do not touch it.
+ */
+rwkv7_status rwkv7_wkv_forward_noalloc(const void *r, const void *w, const void *k,
+                                       const void *v, const void *kappa, const void *a,
+                                       const float *s0, void *y, float *s_out, int B, int T,
+                                       int H, int N, rwkv7_dtype dt, rwkv7_algo algo,
+                                       const rwkv7_epilogue *epi, void *stream);
+
+/*
  * Fused time-mix prologue and output gate (RWKV-7 "Goose" author response,
  * paperhub, numpy time_mixing listing): from raw keys k the kernels form
  *   kappa = (k * k_k) / max(||k * k_k||, 1e-12)   (per head, over its N channels)

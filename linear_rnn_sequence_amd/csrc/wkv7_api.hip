@@ -4,6 +4,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "wkv7_internal.h"
 
 namespace wkv7 {
@@ -549,3 +551,58 @@ rwkv7_status rwkv7_wkv_decode_fused(const void *r, const void *w, const void *k,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// rwkv7_wkv_forward_noalloc: rwkv7_wkv_forward for callers that cannot
+// allocate.  The workspace of the chunked path (three float32 64 x 64 states
+// per (batch, head, time segment), present only when a long sequence of few
+// heads is split into parallel segments) lives in `scratch`, a fixed device
+// array of this library; every call on a device shares that device's copy.
+// The split keeps at most two segments per compute unit, so on a 256-CU device
+// the workspace never exceeds 3 x 512 x 16 KiB = 24 MiB.  Nothing in it needs
+// to start at zero: each call writes every slot it reads.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)24 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch`, per device
+
+// The device address of the current device's `scratch`, looked up once per
+// device (with that device current).  In host code the array's name is only a
+// host-side stand-in; kernels receive this address.
+rwkv7_status scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return RWKV7_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+            return RWKV7_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return RWKV7_OK;
+}
+
+}  // namespace
+
+extern "C" rwkv7_status rwkv7_wkv_forward_noalloc(const void *r, const void *w, const void *k,
+                                                  const void *v, const void *kappa,
+                                                  const void *a, const float *s0, void *y,
+                                                  float *s_out, int B, int T, int H, int N,
+                                                  rwkv7_dtype dt, rwkv7_algo algo,
+                                                  const rwkv7_epilogue *epi, void *stream) {
+    const size_t need = rwkv7_wkv_forward_workspace(B, T, H, N, dt, algo);
+    if (need > kScratchBytes) return RWKV7_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const rwkv7_status st = scratch_address(&ws);
+        if (st != RWKV7_OK) return st;
+    }
+    return rwkv7_wkv_forward(r, w, k, v, kappa, a, s0, y, s_out, B, T, H, N, dt, algo, epi, ws,
+                             need, stream);
+}

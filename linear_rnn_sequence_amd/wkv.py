@@ -55,6 +55,9 @@ def lib():
         L.rwkv7_wkv_forward.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue), vp,
                                                              sz, vp]
         L.rwkv7_wkv_forward.restype = ci
+        L.rwkv7_wkv_forward_noalloc.argtypes = [vp] * 9 + [ci] * 6 + [ctypes.POINTER(Epilogue),
+                                                                     vp]
+        L.rwkv7_wkv_forward_noalloc.restype = ci
         L.rwkv7_wkv_forward_workspace.argtypes = [ci] * 6
         L.rwkv7_wkv_forward_workspace.restype = sz
         L.rwkv7_wkv_decode.argtypes = [vp] * 8 + [ci] * 4 + [ctypes.POINTER(Epilogue), vp]
@@ -235,6 +238,33 @@ def forward(r, w, k, v, kappa, a, s0=None, *, algo="auto", epilogue=None, y=None
     del keep
     if code != 0:
         raise Rwkv7Error(code, "rwkv7_wkv_forward")
+    return y, s_out
+
+
+def forward_noalloc(r, w, k, v, kappa, a, s0=None, *, y, s_out=None, algo="auto",
+                    epilogue=None, stream=None):
+    """rwkv7_wkv_forward_noalloc: the forward without a workspace argument, for callers
+    that cannot allocate (the library's fixed device array serves as the chunked
+    path's workspace; calls that overlap in time on one device race on it).  ``y``
+    (and ``s_out``, if the final state is wanted) must be given.  Returns (y, s_out)."""
+    import torch
+
+    B, T, H, N = r.shape
+    dt = _inputs_dtype(torch, r, w, k, v, kappa, a)
+    f32, dev = torch.float32, r.device
+    if y is None:
+        raise ValueError("forward_noalloc needs y")
+    _check_tensor(torch, s0, "s0", (B, H, N, N), f32, dev)
+    _check_tensor(torch, y, "y", r.shape, r.dtype, dev)
+    _check_tensor(torch, s_out, "s_out", (B, H, N, N), f32, dev)
+    _check_epilogue(torch, epilogue, H, N, dev)
+    epi_ptr, keep = _epilogue(epilogue)
+    code = lib().rwkv7_wkv_forward_noalloc(
+        _ptr(r), _ptr(w), _ptr(k), _ptr(v), _ptr(kappa), _ptr(a), _ptr(s0), _ptr(y),
+        _ptr(s_out), B, T, H, N, dt, ALGOS[algo], epi_ptr, _stream(torch, stream))
+    del keep
+    if code != 0:
+        raise Rwkv7Error(code, "rwkv7_wkv_forward_noalloc")
     return y, s_out
 
 
