@@ -682,9 +682,9 @@ def main():
                                              / np.abs(s_ref).max())
         par["prefill_checked"] = "all outputs"
         if long_shape and not args.fused and not args.bidir:
-            # the same sequence as 32 chained calls of 2048 tokens (each too short to be
-            # split into segments), the state passed between them: against the oracle
-            # and against the single call
+            # the same sequence as 32 chained calls of 2048 tokens (each split into
+            # shorter segments of its own), the state passed between them: against the
+            # oracle and against the single call
             seg_T = 2048
             st = torch.zeros((PREFILL["B"], PREFILL["H"], N, N), dtype=torch.float32, device=dev)
             ys = []

@@ -120,18 +120,21 @@ def test_workspace_query_is_pure():
 
 
 def test_workspace_query_segments():
-    """Long sequences of few heads are split into segments (one workgroup per
-    compute unit); each segment keeps three float32 N x N states in the
-    workspace.  Many heads, short sequences or the scan need none."""
+    """Long sequences of few heads are split into segments (up to two
+    workgroups per compute unit, at least 256 tokens each); each segment keeps
+    three float32 N x N states in the workspace.  Many heads, short sequences
+    or the scan need none."""
     L = wkv.lib()
     per_seg = 3 * 64 * 64 * 4
     big = L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 2)
     assert big > 0 and big % per_seg == 0 and 2 <= big // per_seg <= 64
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 0) == big  # auto = chunked
-    assert L.rwkv7_wkv_forward_workspace(1, 4095, 1, 64, 1, 2) == 0
+    assert L.rwkv7_wkv_forward_workspace(1, 511, 1, 64, 1, 2) == 0
     assert L.rwkv7_wkv_forward_workspace(64, 65536, 64, 64, 1, 2) == 0
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 1) == 0
-    assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 4 * per_seg  # 1024 tokens each
+    assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 16 * per_seg  # 256 tokens each
+    assert L.rwkv7_wkv_forward_workspace(1, 512, 1, 64, 1, 2) == 2 * per_seg
+    assert L.rwkv7_wkv_forward_workspace(200, 4096, 1, 64, 1, 2) == 0   # B*H > CUs / 2
 
 
 def fwd_train(B=2, T=8, H=3, N=64, dt=1, algo=1, s0=fake(6), y=fake(7), s_out=fake(8),

@@ -84,14 +84,15 @@ def test_chunked_29b_shape_with_epilogue(wkv):
 
 def test_chunked_long_context_single_pass_and_segments(wkv):
     """T = 65536, slow decay, near-full replacement: one call (which splits the
-    sequence into parallel segments) and 32 calls of 2048 tokens (too short to
-    split) with the state passed between them, both against the oracle, and the
-    drift between the two."""
+    sequence into parallel segments) and 32 calls of 2048 tokens (each split
+    into shorter segments of its own) with the state passed between them, both
+    against the oracle, and the drift between the two."""
     x = synth.config_inputs(4)
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
     assert wkv.forward_workspace_bytes(1, 65536, 40) > 0  # split into segments
-    assert wkv.forward_workspace_bytes(1, 2048, 40) == 0
+    assert 0 < wkv.forward_workspace_bytes(1, 2048, 40) < wkv.forward_workspace_bytes(1, 65536,
+                                                                                      40)
     y1, s1 = wkv.forward(*ins, algo="chunked")
     st = torch.zeros_like(s1)
     ys = []
@@ -127,7 +128,7 @@ def test_segmented_sweep(wkv, B, H, T, epi, s0):
 
 def test_segmented_in_place_and_pieces(wkv):
     """s_out == s0 with a split sequence, against the same tokens run as pieces
-    of 2000 (each too short to split) with the state passed between them."""
+    of 2000 (each split differently) with the state passed between them."""
     x = synth.draw(1, 10000, 2, seed=71, dtype="bf16", s0="normal", w_recipe="slow",
                    a_mean=2.0, epilogue=True)
     d = to_device(x, torch)
@@ -207,3 +208,19 @@ def test_chunked_rejects_fp32(wkv):
     d = to_device(x, torch)
     with pytest.raises(wkv.Rwkv7Error):
         wkv.forward(*(d[n] for n in NAMES), algo="chunked")
+
+
+@pytest.mark.parametrize("kind", ["lower end", "uniform"])
+def test_chunked_decay_domain(wkv, kind):
+    """The chunked form's stated decay domain 2^-6 <= w <= 1 (include/rwkv7_wkv.h):
+    at its lower end every w = 2^-6, so the decay ratios inside a 16-token chunk
+    reach 2^90; and w drawn uniformly over the domain."""
+    if kind == "lower end":
+        x = synth.draw(2, 200, 3, seed=81, dtype="bf16", s0="normal", w_const=2.0 ** -6)
+    else:
+        x = synth.draw(2, 200, 3, seed=82, dtype="bf16", s0="normal")
+        rng = np.random.default_rng(83)
+        w = rng.uniform(2.0 ** -6, 1.0, x["w"].shape).astype(np.float32)
+        x["w"] = synth.f32_to_bf16_bits(w)
+    assert synth.bf16_bits_to_f32(x["w"]).min() >= 2.0 ** -6
+    check(wkv, x, f"decay domain, {kind}")
