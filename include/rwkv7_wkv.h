@@ -31,11 +31,12 @@
  *  - States are float32 [B, H, N, N], row-major: state[b][h][i][j], i = value
  *    index, j = key index.
  *  - N = 64 (the head size the pages' kernels are tuned for) everywhere; N = 128
- *    also for rwkv7_wkv_decode and for the scan algorithm of the forward,
- *    bidirectional and fused entry points (RWKV7_ALGO_AUTO picks the scan
- *    there; chunked, the training forward and the backward return
- *    RWKV7_ERR_UNSUPPORTED).  B, H >= 1; T >= 0.  All internal offsets are
- *    64-bit.
+ *    also for rwkv7_wkv_decode, for both algorithms of rwkv7_wkv_forward (and
+ *    rwkv7_wkv_forward_noalloc; RWKV7_ALGO_AUTO picks the chunked one for
+ *    bf16), and for the scan algorithm of the bidirectional and fused entry
+ *    points (RWKV7_ALGO_AUTO picks the scan there; their chunked algorithm,
+ *    the training forward and the backward return RWKV7_ERR_UNSUPPORTED at
+ *    128).  B, H >= 1; T >= 0.  All internal offsets are 64-bit.
  *  - Every pointer must be 16-byte aligned.
  *  - All validation runs on the host, synchronously, before anything is
  *    enqueued: on any error nothing is launched and nothing is written.

@@ -91,11 +91,14 @@ static bool valid_dtype(rwkv7_dtype dt) {
     return dt == RWKV7_DT_F32 || dt == RWKV7_DT_BF16 || dt == RWKV7_DT_BF16_W32;
 }
 
-// AUTO: the chunked kernel for bf16 inputs at head size 64, else the scan.
-static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt, int N = kN) {
+// AUTO: the chunked kernel for bf16 inputs at head size 64 (and at 128 where the
+// entry point has a chunked kernel of that size: chunked128), else the scan.
+static rwkv7_algo resolve_algo(rwkv7_algo algo, rwkv7_dtype dt, int N = kN,
+                               bool chunked128 = false) {
     if (algo == RWKV7_ALGO_AUTO)
-        return (dt != RWKV7_DT_F32 && N == kN && kChunkedAvailable) ? RWKV7_ALGO_CHUNKED
-                                                                    : RWKV7_ALGO_SCAN;
+        return (dt != RWKV7_DT_F32 && (N == kN || (N == 128 && chunked128)) && kChunkedAvailable)
+                   ? RWKV7_ALGO_CHUNKED
+                   : RWKV7_ALGO_SCAN;
     return algo;
 }
 
@@ -137,8 +140,11 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
         return RWKV7_ERR_DTYPE;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
-    const rwkv7_algo al = resolve_algo(algo, dt, N);
-    if (al == RWKV7_ALGO_CHUNKED && (dt == RWKV7_DT_F32 || N != kN || !kChunkedAvailable))
+    // the chunked kernel at head size 128 runs the plain forward only
+    const bool chunked128 = N == 128 && !pro && !bidir && !want_ckpt;
+    const rwkv7_algo al = resolve_algo(algo, dt, N, chunked128);
+    if (al == RWKV7_ALGO_CHUNKED &&
+        (dt == RWKV7_DT_F32 || (N != kN && !chunked128) || !kChunkedAvailable))
         return RWKV7_ERR_UNSUPPORTED;
     // the stored states feed the backward, which is built for head size 64
     if (want_ckpt && N != kN) return RWKV7_ERR_UNSUPPORTED;

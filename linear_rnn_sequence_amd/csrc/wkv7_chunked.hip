@@ -107,8 +107,19 @@ constexpr int wait_older_chunks(int loads_per_chunk) {
     return ((loads_per_chunk * (kPrefetch - 1)) & 0xF) | (0x7 << 4) | (0xF << 8) |
            ((((loads_per_chunk * (kPrefetch - 1)) >> 4) & 0x3) << 14);
 }
-constexpr int kThreads = 512;           // 4 chain waves + 4 prep waves
-constexpr int kThreadsSummary = 768;    // + 4 chain waves for the transition rows
+// Head-size geometry (NH = 64 or 128 keys and values per head): one chain wave
+// per 16-value block; prep waves in groups of four, each group preparing 64 of
+// every token's keys.
+template <int NH>
+struct Geo {
+    static constexpr int KB = NH / 16;      // key blocks (= value blocks = chain waves)
+    static constexpr int KH = NH / 64;      // prep groups
+    static constexpr int CW = KB;           // chain waves
+    static constexpr int PW = 4 * KH;       // prep waves
+    static constexpr int threads = 64 * (CW + PW);
+};
+constexpr int kThreads = Geo<64>::threads;  // 4 chain waves + 4 prep waves
+constexpr int kThreadsSummary = 768;        // + 4 chain waves for the transition rows
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
 // A pair tile holds two 16x16 tiles (X | Y) so that a lane's K = 32 operand
@@ -127,22 +138,30 @@ constexpr int kPTileCols = 648;  // (Km^T | Bm^T) pair tiles
 constexpr int kTileVt = 324;     // V^T tiles
 constexpr int kTileVr = 336;     // V row tiles
 
+template <int NH>
 struct __align__(16) ChunkOps {
     // pair tiles over key blocks (2p | 2p+1), rows t (or s), columns j
-    short kp[2][kPTileRows];  // Kp  (A form rows t; also B form of Kp^T)
-    short rp[2][kPTileRows];  // Rp
-    short km[2][kPTileRows];  // Km
-    short bm[2][kPTileRows];  // Bm
-    short kbt[4][kPTileCols]; // (Km^T | Bm^T) of key block jb: rows j, columns s
+    short kp[NH / 32][kPTileRows];  // Kp  (A form rows t; also B form of Kp^T)
+    short rp[NH / 32][kPTileRows];  // Rp
+    short km[NH / 32][kPTileRows];  // Km
+    short bm[NH / 32][kPTileRows];  // Bm
+    short kbt[NH / 16][kPTileCols]; // (Km^T | Bm^T) of key block jb: rows j, columns s
     short mkz[kPTile];     // (M_kk | 0)  [t][s]; the zero half is set once
     short mrb[kPTile];     // (M_kr | M_br)  [t][s]
     short xinv[kTile];     // -(I + M_bk)^-1 [t][s]
-    short vt[4][kTileVt];  // V^T [value block][i][t]  (B form of V)
-    short vr[4][kTileVr];  // V   [value block][t][i]  (epilogue only)
-    float gc[64];          // G_C per key j
-    // per token sums over the 64 keys, fp32: [0] r_t.k_t, [1] r_t.(a_t*kappa_t),
-    // [2] the bonus sum_j r k r_k
-    float rsum[3][16];
+    short vt[NH / 16][kTileVt];  // V^T [value block][i][t]  (B form of V)
+    short vr[NH / 16][kTileVr];  // V   [value block][t][i]  (epilogue only)
+    float gc[NH];          // G_C per key j
+    // per token sums over each prep group's 64 keys, fp32: [0] r_t.k_t,
+    // [1] r_t.(a_t*kappa_t), [2] the bonus sum_j r k r_k
+    float rsum[NH / 64][3][16];
+    // the sum over all keys of token t, quantity q
+    __device__ __forceinline__ float rsum_all(int q, int t) const {
+        float x = rsum[0][q][t];
+#pragma unroll
+        for (int h = 1; h < NH / 64; ++h) x += rsum[h][q][t];
+        return x;
+    }
 };
 
 // Launch description: the sequence may be split into nseg segments of seg_len
@@ -156,13 +175,14 @@ struct ChunkedParams {
     float *ws_p, *ws_ds, *ws_sin;
 };
 
+template <int NH>
 struct __align__(16) ChunkSmem {
-    ChunkOps ops[3];
-    float2 stats[2][16][4];  // per token, per value block: (mean, M2) of 16 readouts
-    // per chunk parity, reading prep wave r and slot b < 3: the product of w over
-    // prep wave b's four tokens if b < r, else 1 (set once), so a reader
-    // multiplies its three slots without selects
-    float4 carry[2][4][3][16];
+    ChunkOps<NH> ops[3];
+    float2 stats[2][16][NH / 16];  // per token, per value block: (mean, M2) of 16 readouts
+    // per prep group and chunk parity, reading prep wave r and slot b < 3: the
+    // product of w over prep wave b's four tokens if b < r, else 1 (set once), so
+    // a reader multiplies its three slots without selects
+    float4 carry[NH / 64][2][4][3][16];
 };
 
 // lane's K = 32 operand of a pair tile (A form of X | Y side by side)
@@ -203,30 +223,35 @@ struct ProParams {
     float ka[4];
 };
 
-template <bool EPI, bool W32, bool FUSED>
+template <bool EPI, bool W32, bool FUSED, int NH>
 struct Chunked {
+    static_assert(!FUSED || NH == 64, "the fused prologue is built for head size 64");
+    using Ops = ChunkOps<NH>;
     const ForwardArgs &p;
-    const int lane, blk, g, lo;  // blk = key block (prep waves) / value block (chain waves)
+    // blk: value block (chain waves) or prep wave within its group; kh: prep group
+    // (keys 64kh .. 64kh+63 of every token)
+    const int lane, blk, kh, g, lo;
     const int Tl;                // tokens of this workgroup's range
     // Elements from one token to the next in processing order (negative when the
     // sequence is walked from its end), and the offset of (b, token t0 of the
     // processing order, h, 0).
     const long TS, tok0;
-    const long lane_off;         // prep lane: its token (ptok) of chunk 0, channels 4lo..4lo+3
+    const long lane_off;  // prep lane: its token (ptok) of chunk 0, keys 64kh + 4lo .. +3
 
-    __device__ Chunked(const ForwardArgs &p_, int b_, int h_, int t0, int tl)
-        : p(p_), lane(threadIdx.x & 63), blk((threadIdx.x >> 6) & 3),
+    __device__ Chunked(const ForwardArgs &p_, int b_, int h_, int t0, int tl, int blk_, int kh_)
+        : p(p_), lane(threadIdx.x & 63), blk(blk_), kh(kh_),
           g((threadIdx.x & 63) >> 4), lo(threadIdx.x & 15), Tl(tl),
-          TS(p_.reverse ? -(long)p_.H * kN : (long)p_.H * kN),
-          tok0(((long)b_ * p_.T + (p_.reverse ? p_.T - 1 - t0 : t0)) * ((long)p_.H * kN) +
-               (long)h_ * kN),
-          lane_off(tok0 + (long)(4 * ((threadIdx.x >> 6) & 3) + ((threadIdx.x & 63) >> 4)) * TS +
+          TS(p_.reverse ? -(long)p_.H * NH : (long)p_.H * NH),
+          tok0(((long)b_ * p_.T + (p_.reverse ? p_.T - 1 - t0 : t0)) * ((long)p_.H * NH) +
+               (long)h_ * NH),
+          lane_off(tok0 + (long)(4 * blk_ + ((threadIdx.x & 63) >> 4)) * TS + 64 * kh_ +
                    4 * (threadIdx.x & 15)) {}
 
-    // Prep lanes are token-major: prep wave b holds tokens 4b .. 4b+3 of a chunk,
-    // one per DPP row g, and lane lo of the row holds keys 4lo .. 4lo+3, so the
-    // row holds the token's whole 64-key vector and each load instruction reads
-    // four whole rows (a key-block split would touch sixteen partial lines).
+    // Prep lanes are token-major: prep wave b of group kh holds tokens 4b .. 4b+3
+    // of a chunk, one per DPP row g, and lane lo of the row holds keys 64kh + 4lo
+    // .. +3, so the row holds 64 consecutive keys of the token and each load
+    // instruction reads four whole 128-byte rows (a key-block split would touch
+    // sixteen partial lines).
     __device__ __forceinline__ int ptok() const { return 4 * blk + g; }
 
     // Issues the same loads on every path (no branch around them), so the
@@ -342,7 +367,7 @@ struct Chunked {
 
     // Chunk operands of the lane's token and keys, written to LDS buffer `o`.
     // lp, lx: the scan of this chunk; carry: this wave's slots of the chunk.
-    __device__ void prep(const Unpacked &u, ChunkOps &o, const float (&rk)[4],
+    __device__ void prep(const Unpacked &u, Ops &o, const float (&rk)[4],
                          const float (&lp)[4], const float (&lx)[4],
                          const float4 (&carry)[3][16]) const {
         const float *r = u.r, *k = u.k, *a = u.a, *kp = u.kp;
@@ -369,7 +394,7 @@ struct Chunked {
         }
         // the lane's 4 keys sit in key block jb at columns c0 .. c0+3: row t of
         // half jb % 2 of pair tile jb / 2
-        const int t = ptok(), jb = lo >> 2, c0 = 4 * (lo & 3);
+        const int t = ptok(), jb = 4 * kh + (lo >> 2), c0 = 4 * (lo & 3);
         const int rowoff = t * kRow + c0;
         const int poff = t * kPRow + 8 * (lo & 3) + 4 * (jb & 1);
         *reinterpret_cast<bf16x4 *>(o.kp[jb >> 1] + poff) = to_bf16(Kp);
@@ -390,34 +415,40 @@ struct Chunked {
         o.vt[jb][(c0 + 2) * kRow + t] = (short)(u.v.y & 0xffffu);
         o.vt[jb][(c0 + 3) * kRow + t] = (short)(u.v.y >> 16);
         // the last token's lanes hold the whole-chunk decay G_C
-        if (t == kC - 1) *reinterpret_cast<float4 *>(&o.gc[4 * lo]) =
+        if (t == kC - 1) *reinterpret_cast<float4 *>(&o.gc[64 * kh + 4 * lo]) =
             make_float4(G[0], G[1], G[2], G[3]);
         // fp32 diagonals of M_kr and M_br: at s = t the decay ratio is exactly 1, so
         // r_t.k_t and r_t.(a_t*kappa_t) need no bf16 factors; the two-factor bf16
         // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
-        // early readouts whose dot product nearly cancels.  Sums over the token's
-        // 64 keys: the 16 lanes of the DPP row.
+        // early readouts whose dot product nearly cancels.  Sums over the group's
+        // 64 keys of the token: the 16 lanes of the DPP row.
         dkr = sum_lanes16(dkr);
         dbr = sum_lanes16(dbr);
         if (EPI) bon = sum_lanes16(bon);
         if (lo == 0) {
-            o.rsum[0][t] = dkr;
-            o.rsum[1][t] = dbr;
-            if (EPI) o.rsum[2][t] = bon;
+            o.rsum[kh][0][t] = dkr;
+            o.rsum[kh][1][t] = dbr;
+            if (EPI) o.rsum[kh][2][t] = bon;
         }
     }
 
-    // One C x C matrix of a chunk per prep wave; wave 5 forms the triangular inverse.
-    __device__ void matrices(ChunkOps &o) const {
+    // One C x C matrix of a chunk per prep wave of group 0 (contractions over all
+    // NH keys); wave 1 of the group forms the triangular inverse.
+    __device__ void matrices(Ops &o) const {
         const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
+        if (kh != 0) return;
         if (blk == 1) {
             // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
             // is the B form of M and the A form of M^T.
             // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
-            const bf16x8s kp01 = ld_pair(o.kp[0], lane), kp23 = ld_pair(o.kp[1], lane);
-            const bf16x8s bm01 = ld_pair(o.bm[0], lane), bm23 = ld_pair(o.bm[1], lane);
-            f32x4 nb = mfma32(kp23, bm23, mfma32(kp01, bm01, Acc32::zero())).v;
-            f32x4 na = mfma32(bm23, kp23, mfma32(bm01, kp01, Acc32::zero())).v;
+            Acc32 anb = Acc32::zero(), ana = Acc32::zero();
+#pragma unroll
+            for (int q = 0; q < NH / 32; ++q) {
+                const bf16x8s kpq = ld_pair(o.kp[q], lane), bmq = ld_pair(o.bm[q], lane);
+                anb = mfma32(kpq, bmq, anb);
+                ana = mfma32(bmq, kpq, ana);
+            }
+            f32x4 nb = anb.v, na = ana.v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 nb[e] = (lo < row + e) ? nb[e] : 0.f;   // [t = row+e][s = lo], s < t
@@ -430,11 +461,13 @@ struct Chunked {
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kPTileRows] = (blk == 3) ? o.bm : o.km;
             const short(*rhs)[kPTileRows] = (blk == 0) ? o.kp : o.rp;
-            f32x4 m = mfma32(ld_pair(lhs[1], lane), ld_pair(rhs[1], lane),
-                             mfma32(ld_pair(lhs[0], lane), ld_pair(rhs[0], lane), Acc32::zero()))
-                          .v;
+            Acc32 am = Acc32::zero();
+#pragma unroll
+            for (int q = 0; q < NH / 32; ++q)
+                am = mfma32(ld_pair(lhs[q], lane), ld_pair(rhs[q], lane), am);
+            f32x4 m = am.v;
             // D[s = row+e][t = lo] = A form of M at [t = lo][s = row+e]
-            const float diag = (blk != 0) ? o.rsum[blk == 2 ? 0 : 1][lo] : 0.f;
+            const float diag = (blk != 0) ? o.rsum_all(blk == 2 ? 0 : 1, lo) : 0.f;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const bool keep = (blk == 0) ? (row + e < lo) : (row + e <= lo);
@@ -458,24 +491,35 @@ struct Pending {
     uint2 v;     // four bf16 values
 };
 
-template <bool EPI, bool W32, bool FUSED>
+template <bool EPI, bool W32, bool FUSED, int NH>
 __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
-                                                const Chunked<EPI, W32, FUSED> &K,
-                                                const ChunkSmem &sm, const Pending &pd, int c,
-                                                const float (&lnw)[4], const float (&lnb)[4],
-                                                long yoff) {
+                                                const Chunked<EPI, W32, FUSED, NH> &K,
+                                                const ChunkSmem<NH> &sm, const Pending &pd,
+                                                int c, const float (&lnw)[4],
+                                                const float (&lnb)[4], long yoff) {
     float yv[4] = {pd.y[0], pd.y[1], pd.y[2], pd.y[3]};
     if (EPI) {
-        // GroupNorm statistics of this lane's token from the four value blocks'
-        // (mean, M2) (Chan et al. pairwise combination of equal-sized groups)
-        const float2 *st = sm.stats[c & 1][K.lo];
-        const float4 m01 = *reinterpret_cast<const float4 *>(st);
-        const float4 m23 = *reinterpret_cast<const float4 *>(st + 2);
-        const float mu = 0.25f * (m01.x + m01.z + m23.x + m23.z);
-        const float d0 = m01.x - mu, d1 = m01.z - mu, d2 = m23.x - mu, d3 = m23.z - mu;
-        const float m2 = (m01.y + m01.w + m23.y + m23.w) +
-                         16.f * (d0 * d0 + d1 * d1 + d2 * d2 + d3 * d3);
-        const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / 64.f) + p.epi.eps);
+        // GroupNorm statistics of this lane's token from the value blocks' (mean,
+        // M2) (Chan et al. pairwise combination of equal-sized groups)
+        constexpr int VB = NH / 16;
+        const float4 *st = reinterpret_cast<const float4 *>(sm.stats[c & 1][K.lo]);
+        float4 m[VB / 2];
+        float ssum = 0.f, m2 = 0.f;
+#pragma unroll
+        for (int i = 0; i < VB / 2; ++i) {
+            m[i] = st[i];
+            ssum += m[i].x + m[i].z;
+            m2 += m[i].y + m[i].w;
+        }
+        const float mu = ssum * (1.f / VB);
+        float dev = 0.f;
+#pragma unroll
+        for (int i = 0; i < VB / 2; ++i) {
+            const float d0 = m[i].x - mu, d1 = m[i].z - mu;
+            dev += d0 * d0 + d1 * d1;
+        }
+        m2 += 16.f * dev;
+        const float rs = __builtin_amdgcn_rsqf(m2 * (1.f / NH) + p.epi.eps);
         const float v[4] = {bf16_lo(pd.v.x), bf16_hi(pd.v.x), bf16_lo(pd.v.y), bf16_hi(pd.v.y)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) yv[e] = (yv[e] - mu) * (rs * lnw[e]) + lnb[e] + pd.bon * v[e];
@@ -503,42 +547,55 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
 //   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
 // YADD: add the float32 readouts p.y_add (the reverse pass of a bidirectional
 // call) before the epilogue.
-template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD>
-__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : kThreads)
+//
+// NH = 128 (head size 128): eight chain waves (one per value block) and two prep
+// groups of four waves, each group preparing 64 of every token's keys; 1024
+// threads.  No segments (the summary pass would need eight more chain waves),
+// no fused prologue, no bidirectional pass and no stored states.
+template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD, int NH>
+__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : Geo<NH>::threads)
 __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
     ChunkedParams cp) {
-    __shared__ ChunkSmem sm;
+    static_assert(NH == 64 || (!SUMMARY && !YADD), "head size 128: plain forward only");
+    using G = Geo<NH>;
+    constexpr int KB = G::KB;
+    __shared__ ChunkSmem<NH> sm;
     const ForwardArgs &p = cp.p;
     const int bh = blockIdx.x / cp.nseg_launch;
     const int seg = blockIdx.x - bh * cp.nseg_launch;
     const int b = bh / p.H, h = bh - b * p.H;
     const int t0 = seg * cp.seg_len;
-    const Chunked<EPI, W32, FUSED> K(p, b, h, t0, min(cp.seg_len, p.T - t0));
-    const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
     const int wave = threadIdx.x >> 6;
-    const bool chain_wave = wave < 4 || wave >= 8;  // waves 0..3 (and 8..11 in SUMMARY)
+    // chain waves 0 .. CW-1 (and 8..11, the transition rows, in SUMMARY); prep
+    // waves CW .. CW+PW-1 in groups of four
+    const bool chain_wave = wave < G::CW || (SUMMARY && wave >= 8);
+    const int wblk = chain_wave ? (wave & (G::CW - 1)) : ((wave - G::CW) & 3);
+    const int wkh = chain_wave ? 0 : (wave - G::CW) >> 2;
+    const Chunked<EPI, W32, FUSED, NH> K(p, b, h, t0, min(cp.seg_len, p.T - t0), wblk, wkh);
+    const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
     const bool p_rows = SUMMARY && wave >= 8;       // transition rows
     const int nch = (K.Tl + kC - 1) / kC;
-    const long srow = (long)(16 * blk + lo) * kN;   // this lane's value row i in a state
+    constexpr long NN = (long)NH * NH;
+    const long srow = (long)(16 * blk + lo) * NH;   // this lane's value row i in a state
     const long sidx = (long)bh * cp.nseg + seg;     // (b, h, segment) slot in the workspace
     // entry state and where the final state goes
     const float *s_in = SUMMARY ? nullptr
-                      : (cp.nseg == 1 ? (p.s0 ? p.s0 + (long)bh * kN * kN : nullptr)
-                                      : cp.ws_sin + sidx * kN * kN);
-    float *s_fin = SUMMARY ? (p_rows ? cp.ws_p : cp.ws_ds) + sidx * kN * kN
-                 : (seg == cp.nseg - 1 && p.s_out ? p.s_out + (long)bh * kN * kN : nullptr);
+                      : (cp.nseg == 1 ? (p.s0 ? p.s0 + (long)bh * NN : nullptr)
+                                      : cp.ws_sin + sidx * NN);
+    float *s_fin = SUMMARY ? (p_rows ? cp.ws_p : cp.ws_ds) + sidx * NN
+                 : (seg == cp.nseg - 1 && p.s_out ? p.s_out + (long)bh * NN : nullptr);
     // stored states (training forward): chunk c of this range is global chunk t0/kC + c
     static_assert(kC == kCkpt, "a chunk is one checkpoint interval");
     float *ckpt = (!SUMMARY && p.s_ckpt)
-                      ? p.s_ckpt + ((long)bh * ((p.T + kC - 1) / kC) + t0 / kC) * kN * kN
+                      ? p.s_ckpt + ((long)bh * ((p.T + kC - 1) / kC) + t0 / kC) * NN
                       : nullptr;
 
     if (chain_wave) {
         // ---------------- chain waves: state, MFMA chain, readouts ----------------
         // S^T tile jb holds rows j = 16jb + 4g + e, column i = 16blk + lo
-        Acc32 Z[4];
+        Acc32 Z[KB];
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
+        for (int jb = 0; jb < KB; ++jb) {
             if (s_in) {
                 const float4 x = *reinterpret_cast<const float4 *>(s_in + srow + 16 * jb + 4 * g);
                 Z[jb].v = f32x4{x.x, x.y, x.z, x.w};
@@ -550,7 +607,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         }
         // GroupNorm weight and bias of this lane's four value channels
         float lnw[4] = {1.f, 1.f, 1.f, 1.f}, lnb[4] = {0.f, 0.f, 0.f, 0.f};
-        const int ich = h * kN + 16 * blk + 4 * g;
+        const int ich = h * NH + 16 * blk + 4 * g;
         if (EPI && p.epi.ln_w) {
             const float4 q = *reinterpret_cast<const float4 *>(p.epi.ln_w + ich);
             lnw[0] = q.x; lnw[1] = q.y; lnw[2] = q.z; lnw[3] = q.w;
@@ -578,7 +635,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         const long ystep = (long)kC * K.TS;
         auto store_state = [&](float *dst) {  // non-temporal: read back only by the backward
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
+            for (int jb = 0; jb < KB; ++jb)
                 __builtin_nontemporal_store(Z[jb].v,
                                             reinterpret_cast<f32x4 *>(dst + srow + 16 * jb + 4 * g));
         };
@@ -588,7 +645,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         __syncthreads();  // interval 1: chunk 0 matrices, chunk 1 prepared
         for (int c = 0; c <= nch; ++c) {
             if (!SUMMARY && c > 0) {
-                finish_readouts<EPI, W32, FUSED>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
+                finish_readouts<EPI, W32, FUSED, NH>(p, K, sm, pd, c - 1, lnw, lnb, ylane);
                 ylane += ystep;
             }
             if (c < nch) {
@@ -604,31 +661,33 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
                     pd.graw = *reinterpret_cast<const uint2 *>(
                         gsrc + K.tok0 + (long)min(c * kC + lo, K.Tl - 1) * K.TS + 16 * blk + 4 * g);
                 }
-                const ChunkOps &o = sm.ops[c % 3];
+                const ChunkOps<NH> &o = sm.ops[c % 3];
                 // B operands as 8-wide pairs: (V | -U) and the state pairs; one K =
                 // 32 MFMA per two 16-k products, accumulation chains within that
                 // one opcode
                 VU.lo = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
-                bf16x8s Z01, Z23;
-                Z01.lo = to_bf16(Z[0].v);
-                Z01.hi = to_bf16(Z[1].v);
-                Z23.lo = to_bf16(Z[2].v);
-                Z23.hi = to_bf16(Z[3].v);
+                bf16x8s ZP[KB / 2];  // state pairs (key blocks 2q | 2q+1)
+#pragma unroll
+                for (int q = 0; q < KB / 2; ++q) {
+                    ZP[q].lo = to_bf16(Z[2 * q].v);
+                    ZP[q].hi = to_bf16(Z[2 * q + 1].v);
+                }
                 // rhs = M_kk V + Kp S0^T; (M_kk | 0) meets (V | the previous chunk's
                 // -U), whose product with the zero half vanishes
                 Acc32 rhs = mfma32(ld_pair(o.mkz, lane), VU, Acc32::zero());
-                rhs = mfma32(ld_pair(o.kp[0], lane), Z01, rhs);
-                rhs = mfma32(ld_pair(o.kp[1], lane), Z23, rhs);
+#pragma unroll
+                for (int q = 0; q < KB / 2; ++q) rhs = mfma32(ld_pair(o.kp[q], lane), ZP[q], rhs);
                 // readouts as Y^T = S0 Rp^T + V^T M_kr^T - U^T M_br^T (the operands of
                 // Y with their roles swapped): lane holds Y^T[i = 4g+e][t = lo]; the
                 // terms without U first, so only one product waits for U
-                Acc32 Y = mfma32(Z01, ld_pair(o.rp[0], lane), Acc32::zero());
-                Y = mfma32(Z23, ld_pair(o.rp[1], lane), Y);
+                Acc32 Y = Acc32::zero();
+#pragma unroll
+                for (int q = 0; q < KB / 2; ++q) Y = mfma32(ZP[q], ld_pair(o.rp[q], lane), Y);
                 const Acc16 U = mfma16(ld_a(o.xinv, lane), to_bf16(rhs.v), Acc16::zero());  // -U
                 VU.hi = to_bf16(U.v);
                 Y = mfma32(VU, ld_pair(o.mrb, lane), Y);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
+                for (int jb = 0; jb < KB; ++jb) {
                     Z[jb] = mfma32(ld_pair(o.kbt[jb], lane), VU, Z[jb]);
                     const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
                     Z[jb].v[0] *= gc.x;
@@ -646,9 +705,9 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
                 // stored states: the one leaving this chunk enters the next; stored
                 // here, in the slack before the barrier, rather than just before
                 // the MFMAs that overwrite the accumulators
-                if (ckpt && c + 1 < nch) store_state(ckpt + (long)(c + 1) * kN * kN);
+                if (ckpt && c + 1 < nch) store_state(ckpt + (long)(c + 1) * NN);
                 if (EPI && !SUMMARY) {
-                    pd.bon = o.rsum[2][lo];
+                    pd.bon = o.rsum_all(2, lo);
                     pd.v = *reinterpret_cast<const uint2 *>(o.vr[blk] + lo * kRow + 4 * g);
                     // mean and M2 of token lo's readouts over this value block: four
                     // in the lane, summed over the four DPP rows g
@@ -664,7 +723,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         for (int q = nch + 3; q < steady_intervals(nch); ++q) __syncthreads();
         if (s_fin) {
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb)
+            for (int jb = 0; jb < KB; ++jb)
                 *reinterpret_cast<float4 *>(s_fin + srow + 16 * jb + 4 * g) =
                     make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
         }
@@ -672,14 +731,14 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
         // the zero half of (M_kk | 0) in every buffer, once (read after the
         // barriers that precede the first chain step)
-        for (int i = (int)threadIdx.x - 256; i < 3 * 16 * 4; i += 256)
+        for (int i = (int)threadIdx.x - 64 * G::CW; i < 3 * 16 * 4; i += 64 * G::PW)
             *reinterpret_cast<uint2 *>(sm.ops[i >> 6].mkz + ((i >> 2) & 15) * kPRow +
                                        8 * (i & 3) + 4) = make_uint2(0u, 0u);
         // The prep waves bound each interval (the chain waves wait at the barrier),
         // so they win the issue arbitration on their SIMD.
         __builtin_amdgcn_s_setprio(2);
         ProParams pro{};
-        const int kch = h * kN + 4 * lo;  // the lane's four keys
+        const int kch = h * NH + 64 * K.kh + 4 * lo;  // the lane's four keys
         if (FUSED) {
             const float4 q = *reinterpret_cast<const float4 *>(p.k_k + kch);
             pro.kk[0] = q.x; pro.kk[1] = q.y; pro.kk[2] = q.z; pro.kk[3] = q.w;
@@ -728,10 +787,10 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
             if (g == 0) {
 #pragma unroll
                 for (int b = 0; b < 3; ++b)
-                    if (b >= blk) sm.carry[0][blk][b][lo] = sm.carry[1][blk][b][lo] =
-                        make_float4(1.f, 1.f, 1.f, 1.f);
+                    if (b >= blk) sm.carry[K.kh][0][blk][b][lo] =
+                        sm.carry[K.kh][1][blk][b][lo] = make_float4(1.f, 1.f, 1.f, 1.f);
             }
-            K.scan(w, lp, lx, sm.carry[0]);
+            K.scan(w, lp, lx, sm.carry[K.kh][0]);
         }
         __syncthreads();  // interval -1: decay totals of chunk 0
         static_assert(kUnroll % kPrefetch == 0, "the loop advances whole ring turns");
@@ -748,12 +807,12 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
                 // budget that lets two workgroups share a CU)
                 K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
-                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[q & 1][blk]);
+                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[K.kh][q & 1][blk]);
                 K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];
                 K.unpack_w(xs[(d + 1) % kPrefetch], (q + 1) * kC + K.ptok() < K.Tl, w);
-                K.scan(w, lp, lx, sm.carry[(q + 1) & 1]);
+                K.scan(w, lp, lx, sm.carry[K.kh][(q + 1) & 1]);
                 __syncthreads();
             }
         }
@@ -889,7 +948,7 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
         cp.ws_sin = cp.ws_ds + slab;
         // 1. transitions and offsets of every segment but the last
         cp.nseg_launch = cp.nseg - 1;
-        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED, false>),
+        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED, false, 64>),
                            dim3((unsigned)(bh * cp.nseg_launch)), dim3(kThreadsSummary), 0,
                            stream, cp);
         hipError_t e = hipGetLastError();
@@ -904,10 +963,26 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     cp.nseg_launch = cp.nseg;
     const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED, YADD>), grid, block, 0, stream,
-                           cp);
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED, YADD, 64>), grid, block, 0,
+                           stream, cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED, YADD>), grid, block, 0,
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED, YADD, 64>), grid, block, 0,
+                           stream, cp);
+    return hipGetLastError();
+}
+
+// Head size 128: one workgroup per (b, h), no segments.
+template <bool W32>
+hipError_t launch_chunked128(ChunkedParams cp, hipStream_t stream) {
+    const ForwardArgs &p = cp.p;
+    cp.nseg = cp.nseg_launch = 1;
+    cp.seg_len = p.T;
+    const dim3 grid((unsigned)((long)p.B * p.H)), block(Geo<128>::threads);
+    if (p.epilogue)
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32, false, false, 128>), grid, block, 0,
+                           stream, cp);
+    else
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32, false, false, 128>), grid, block, 0,
                            stream, cp);
     return hipGetLastError();
 }
@@ -915,6 +990,10 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
 hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream) {
     ChunkedParams cp{};
     cp.p = p;
+    // head size 128: plain forward only (the API routes the other entry points to
+    // the scan), no stored states
+    if (p.N == 128)
+        return p.w32 ? launch_chunked128<true>(cp, stream) : launch_chunked128<false>(cp, stream);
     segment_plan(p.B, p.T, p.H, cp.nseg, cp.seg_len);
     // the fused prologue comes with bf16 decays only (the API refuses it with float32 w)
     if (p.fused) return launch_chunked_w<false, true, false>(cp, stream);

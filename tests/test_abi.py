@@ -271,7 +271,15 @@ def test_decode_head_size_128_validation():
 @fake_addresses
 def test_forward_head_size_128_validation():
     assert fwd(N=96) == 4
-    assert fwd(N=128, algo=2) == 4                 # chunked is built for 64
+    assert fwd(N=128, algo=2, dt=0) == 4           # chunked is bf16 only, at 128 too
+    L = wkv.lib()
+    # the chunked kernel at 128 runs the plain forward only
+    assert L.rwkv7_wkv_forward_bidir(*[fake(i) for i in range(6)], None, fake(7), None, 2, 8,
+                                     3, 128, 1, 2, None, fake(8), 1 << 24, None) == 4
+    pro = _Pro(k_k=A + 11 * STRIDE, k_a=A + 12 * STRIDE, g=None)
+    assert L.rwkv7_wkv_forward_fused(*[fake(i) for i in range(5)], ctypes.byref(pro), None,
+                                     fake(7), None, 2, 8, 3, 128, 1, 2, None, None, 0,
+                                     None) == 4
     assert fwd_train(N=128) == 4                   # the backward is built for 64
     assert fwd(N=128, T=0, s_out=None) == 0        # scan at 128 passes validation
 

@@ -34,7 +34,7 @@ def test_scan_n128(wkv, dtype, B, H, T, epi):
                    epilogue=epi)
     d = to_device(x, torch)
     assert wkv.forward_workspace_bytes(B, T, H, 128) == 0
-    y, s = wkv.forward(*(d[n] for n in NAMES), s0=d["s0"], epilogue=d["epi"])  # auto: scan
+    y, s = wkv.forward(*(d[n] for n in NAMES), s0=d["s0"], epilogue=d["epi"], algo="scan")
     torch.cuda.synchronize()
     y_ref, s_ref = oracle.forward(*(x.as_f64(n) for n in NAMES), s0=x["s0"], epilogue=x["epi"])
     assert_close(to_f64(y), y_ref, tol(dtype), "y")
@@ -69,7 +69,7 @@ def test_n128_refusals(wkv):
     x = synth.draw(1, 20, 1, 128, seed=11, dtype="bf16")
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
-    with pytest.raises(wkv.Rwkv7Error):
-        wkv.forward(*ins, algo="chunked")
+    with pytest.raises(wkv.Rwkv7Error):  # the chunked kernel is bf16 only
+        wkv.forward(*(t.float() for t in ins), algo="chunked")
     with pytest.raises(wkv.Rwkv7Error):
         wkv.forward_train(*ins)
