@@ -63,6 +63,9 @@ def parse():
                     help="backward algorithm of --only train (auto: chunked for bf16)")
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' and '0.19b' need --only prefill")
+    ap.add_argument("--prefill-head", type=int, default=64, choices=[64, 128],
+                    help="prefill head size; 128 keeps the model width of the 2.9B shape "
+                         "(H = 20) and needs --only prefill")
     ap.add_argument("--decode-head", type=int, default=64, choices=[64, 128],
                     help="decode head size; 128 keeps the state bytes (H = 20) and needs "
                          "--only decode")
@@ -191,6 +194,9 @@ BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
 
 
 def workload_name(args, long_shape, do_prefill, do_decode):
+    if args.prefill_head == 128:
+        return ("2.9B-width WKV7 prefill at head size 128: B8 T4096 H20 N128 with fused "
+                "GroupNorm+bonus epilogue")
     if args.prefill_shape == "0.19b":
         return ("0.19B-shape WKV7 prefill B4 T1024 H12 N64 from initial states ~ N(0, 0.1) "
                 "(no epilogue)")
@@ -292,8 +298,8 @@ def bench_train(args, torch, wkv, synth, dev):
     wx = 2 if args.decay_f32 else 0  # extra bytes per decay element (w in, dw out)
     fwd_bytes = work * (7 * 2 + wx) * N + B * H * N * N * 4 * (1 + nck)
     bwd_bytes = work * (13 * 2 + 2 * wx) * N + B * H * N * N * 4 * (2 + nck)
-    src = source_hash("wkv7_backward_chunked.hip" if chunked_bwd else "wkv7_backward.hip",
-                      "wkv7_device.h")
+    src = (source_hash("wkv7_backward_chunked.hip", "wkv7_device.h", "wkv7_mfma.h")
+           if chunked_bwd else source_hash("wkv7_backward.hip", "wkv7_device.h"))
     out = {
         "metric": "WKV7 training tokens x heads per second (forward with stored states + backward)",
         "value": work / (ms_per_step / 1e3),
@@ -375,6 +381,11 @@ def main():
         print("bench.py: --prefill-shape long / 0.19b and --bidir are prefill-only "
               "measurements (--only prefill)", file=sys.stderr)
         sys.exit(2)
+    if args.prefill_head != 64 and (args.only != "prefill" or args.prefill_shape != "2.9b"
+                                    or args.fused or args.bidir or args.decay_f32):
+        print("bench.py: --prefill-head 128 times the 2.9B-width prefill alone (--only prefill)",
+              file=sys.stderr)
+        sys.exit(2)
     if args.decay_f32 and args.only not in ("prefill", "train"):
         print("bench.py: --decay-f32 needs --only prefill (long context) or --only train",
               file=sys.stderr)
@@ -412,7 +423,15 @@ def main():
     # ------------------------------------------------------------------ prefill
     if do_prefill:
         t0 = time.time()
-        px = synth.config_inputs(cfg_idx)
+        PN = args.prefill_head
+        if PN == 128:  # the 2.9B-shape recipe at head size 128, model width kept (H = 20)
+            c = synth.CONFIGS[2]
+            PREFILL = dict(PREFILL, H=PREFILL["H"] * 64 // PN)
+            px = synth.draw(PREFILL["B"], PREFILL["T"], PREFILL["H"], PN, seed=2,
+                            dtype=c["dtype"], s0=c["s0"], w_recipe=c["w_recipe"],
+                            a_mean=c["a_mean"], epilogue=c["epilogue"])
+        else:
+            px = synth.config_inputs(cfg_idx)
         pd = {}
         for n in NAMES:
             pd[n] = torch.from_numpy(px[n].view(np.int16)).to(dev).view(torch.bfloat16)
@@ -428,11 +447,12 @@ def main():
                      "ln_b": torch.from_numpy(e["ln_b"]).to(dev),
                      "r_k": torch.from_numpy(e["r_k"]).to(dev), "eps": e["eps"]}
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
-        p_y = torch.empty((B, T, H, N), dtype=torch.bfloat16, device=dev)
-        p_s = torch.empty(((2,) if args.bidir else ()) + (B, H, N, N), dtype=torch.float32,
+        p_y = torch.empty((B, T, H, PN), dtype=torch.bfloat16, device=dev)
+        p_s = torch.empty(((2,) if args.bidir else ()) + (B, H, PN, PN), dtype=torch.float32,
                           device=dev)
         ws_bytes = (wkv.forward_bidir_workspace_bytes if args.bidir else
-                    wkv.forward_workspace_bytes)(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
+                    wkv.forward_workspace_bytes)(B, T, H, PN, dtype="bf16",
+                                                 algo=args.prefill_algo)
         p_ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
         p_gen_s = time.time() - t0
 
@@ -563,7 +583,15 @@ def main():
                    if args.prefill_shape == "0.19b" else
                    "WKV7 tokens x heads per second (bidirectional 2.9B-shape prefill)"
                    if args.bidir else
-                   "WKV7 tokens x heads per second (2.9B-shape prefill + B=256 decode)"),
+                   "WKV7 tokens x heads per second (2.9B-width prefill, head size 128)"
+                   if do_prefill and args.prefill_head == 128 else
+                   "WKV7 tokens x heads per second (2.9B-shape prefill)"
+                   if do_prefill and not do_decode else
+                   "WKV7 tokens x heads per second (B=256 decode)"
+                   if do_decode and not do_prefill else
+                   # the default run: the headline metric of the workload
+                   "WKV7 tokens\u00d7heads/s and % HBM roofline (2.9B-shape prefill + B=256 "
+                   "decode)"),
         "value": value,
         "unit": "token*heads/s",
         "n_gpus": 1,
@@ -577,7 +605,7 @@ def main():
         "data": "synthetic (seeded; recipes of the pages' parameterisations)",
         "config": {
             "workload": workload_name(args, long_shape, do_prefill, do_decode),
-            "prefill": dict(PREFILL, N=N, algo=args.prefill_algo, epilogue=p_with_epi,
+            "prefill": dict(PREFILL, N=PN, algo=args.prefill_algo, epilogue=p_with_epi,
                             workspace_bytes=ws_bytes, bidirectional=args.bidir,
                             fused_prologue=args.fused,
                             decay_dtype="f32" if args.decay_f32 else "bf16")
@@ -615,15 +643,15 @@ def main():
         B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
         # six inputs + y, the final state (and the initial one when given), and the
         # epilogue parameters when fused
-        p_bytes = (B * T * H * (7 + (1 if args.decay_f32 else 0)) * N * 2
-                   + B * H * N * N * 4 * (1 if p_s0 is None else 2))
+        p_bytes = (B * T * H * (7 + (1 if args.decay_f32 else 0)) * PN * 2
+                   + B * H * PN * PN * 4 * (1 if p_s0 is None else 2))
         if p_with_epi:
-            p_bytes += 2 * H * N * 4 + H * N * 4
+            p_bytes += 2 * H * PN * 4 + H * PN * 4
         ach = p_bytes / (prefill_ms / 1e3) / 1e9
         chunked = args.prefill_algo in ("auto", "chunked")
-        src = source_hash("wkv7_chunked.hip", "wkv7_device.h")
+        src = source_hash("wkv7_chunked.hip", "wkv7_device.h", "wkv7_mfma.h")
         plain_29b = (chunked and args.prefill_shape == "2.9b" and not args.fused
-                     and not args.bidir)
+                     and not args.bidir and PN == 64)
         traffic = (read_traffic("chunked_kernel_traffic_b8_t4096_h40_epilogue.txt", src)
                    if plain_29b else None)
         out["prefill"] = {
