@@ -119,15 +119,51 @@ __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, lo
 }
 
 // ---------------------------------------------------------------- reverse chain
-struct ChainLds {
+// One workgroup of eight waves per (b, h) walks the chunks from the last to the
+// first as a three-stage pipeline with one barrier per interval (as the
+// forward chunked kernel does).  At interval q, with i = q - 2 the chain index
+// of the chunk whose cotangent step runs (chunk nch - 1 - i):
+//   waves 4..7 ("prep"): wave 4+b forms the operands of tokens 4b .. 4b+3 of
+//     chain index q (thread = key / value `lane`), writes them to buffer q % 3,
+//     and issues the loads of index q + 2 into its two-deep register ring; at
+//     the end it multiplies the decays of index q + 1 over its four tokens and
+//     leaves the total in LDS for the later waves (read after the barrier).
+//     Wave 4 also forms X = (I + N)^-1 of index q - 1 and wave 5 its Mbr, into
+//     the matrix tiles of parity (q - 1) & 1;
+//   waves 0..3 ("chain"): wave c owns values 16c .. 16c+15 of dS^T as fp32 MFMA
+//     accumulator tiles and runs the cotangent step of index q - 2 from buffer
+//     (q - 2) % 3 and the matrix tiles of parity q & 1: it stores the chunk's
+//     dSh (bf16, the operand the gradient kernel reads) and forms dS0.
+// Every load is issued on every path (chunk indices clamped), so the ring's
+// wait counts stay exact.
+constexpr int kChainThreads = 512;  // 4 chain waves + 4 prep waves
+
+struct __align__(16) ChainOps {
     short kp[kC][kSK], rp[kC][kSK], bm[kC][kSK];  // tokens x keys
-    short dyy[kC][kSK];                           // tokens x values
-    float carry[4][kN];                           // decay product of each wave's 4 tokens
+    short kpt[kN][kST], rpt[kN][kST];             // keys x tokens
+    short dyt[kN][kST];                           // values x tokens
     float gc[kN];                                 // decay total of the chunk
+};
+struct __align__(16) ChainMatTiles {
+    short xa[kC][kST];    // A operand of X^T: [lo][4g + e] = X[4g + e][lo]
+    short mbra[kC][kST];  // A operand of Mbr^T: [lo][4g + e] = Mbr[4g + e][lo]
+};
+struct __align__(16) ChainLds {
+    ChainOps o[3];
+    ChainMatTiles m[2];
+    float carry[2][4][kN];  // per index parity: decay product of each prep wave's 4 tokens
+};
+
+// raw inputs of one chain index held by a prep lane: key / value `lane` of the
+// wave's four tokens
+template <bool W32>
+struct ChainRaw {
+    typename DecayT<W32>::type w[4];
+    uint16_t k[4], a[4], r[4], d[4];  // kappa, a, r, dy
 };
 
 template <bool W32>
-__global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
+__global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p) {
     using WT = typename DecayT<W32>::type;
     __shared__ ChainLds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -136,122 +172,189 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_kernel(BackwardArgs p) {
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
     const int nch = (p.T + kC - 1) / kC;
+    const int S = (nch + 3) & ~1;  // intervals: nch + 2, rounded up to whole loop trips
+
+    if (wave < 4) {
+        // ---------------- chain waves ----------------
+        // dS^T tiles: St[jb] holds dS^T[16jb + g4 + e][16 wave + lo] = dS[16 wave + lo][16jb + g4 + e]
+        Acc16 St[4];
+        const long srow = (long)(16 * wave + lo) * kN;
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) {
+            if (p.ds_T) {
+                const float4 x =
+                    *reinterpret_cast<const float4 *>(p.ds_T + bh * kN * kN + srow + 16 * jb + g4);
+                St[jb] = Acc16{f32x4{x.x, x.y, x.z, x.w}};
+            } else {
+                St[jb] = z4();
+            }
+        }
+        __syncthreads();  // the decay totals of index 0
+        for (int q = 0; q < S; ++q) {
+            const int i = q - 2;
+            if (i >= 0 && i < nch) {
+                const int c = nch - 1 - i;
+                const ChainOps &o = L.o[i % 3];
+                const ChainMatTiles &mt = L.m[i & 1];
+                // dSh = dS_C diag(g_C), stored as the bf16 MFMA operand that both
+                // kernels use, then dS0 of the chunk
+                uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
+                bf16x4 Sb[4];
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + g4]);
+                    St[jb].v[0] *= gc.x;
+                    St[jb].v[1] *= gc.y;
+                    St[jb].v[2] *= gc.z;
+                    St[jb].v[3] *= gc.w;
+                    Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
+                    *reinterpret_cast<bf16x4 *>(ck + 16 * jb + g4) = Sb[jb];
+                }
+                const bf16x4 dyb = frag(o.dyt, 16 * wave, 0, lane);  // B operand of dY (tokens x values)
+                Acc16 rhs = mma(frag(mt.mbra, 0, 0, lane), dyb, z4());  // Mbr^T dY
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb)
+                    rhs = mma(frag(o.bm, 0, 16 * jb, lane), Sb[jb], rhs);  // + Bm dSh^T
+                const Acc16 up = mma(frag(mt.xa, 0, 0, lane), bf4(rhs), z4());  // X^T rhs = -dZ
+                const bf16x4 dzb = bf4(neg(up));
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    St[jb] = mma(frag(o.rpt, 16 * jb, 0, lane), dyb, St[jb]);  // + Rp^T dY
+                    St[jb] = mma(frag(o.kpt, 16 * jb, 0, lane), dzb, St[jb]);  // + Kp^T dZ
+                }
+            }
+            __syncthreads();
+        }
+        if (p.ds0) {
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+                *reinterpret_cast<float4 *>(p.ds0 + bh * kN * kN + srow + 16 * jb + g4) =
+                    make_float4(St[jb][0], St[jb][1], St[jb][2], St[jb][3]);
+        }
+        return;
+    }
+
+    // ---------------- prep waves ----------------
+    const int pb = wave - 4;  // tokens 4pb .. 4pb+3 of each chunk
     const uint16_t *pr = static_cast<const uint16_t *>(p.r);
     const WT *pw = static_cast<const WT *>(p.w);
     const uint16_t *pkap = static_cast<const uint16_t *>(p.kappa), *pa = static_cast<const uint16_t *>(p.a);
     const uint16_t *pdy = static_cast<const uint16_t *>(p.dy);
-
-    // dS^T tiles: St[jb] holds dS^T[16jb + g4 + e][16 wave + lo] = dS[16 wave + lo][16jb + g4 + e]
-    Acc16 St[4];
-    const long srow = (long)(16 * wave + lo) * kN;
-#pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        if (p.ds_T) {
-            const float4 x = *reinterpret_cast<const float4 *>(p.ds_T + bh * kN * kN + srow + 16 * jb + g4);
-            St[jb] = Acc16{f32x4{x.x, x.y, x.z, x.w}};
-        } else {
-            St[jb] = z4();
-        }
-    }
-
-    // raw bf16 inputs of a chunk: thread (wave, lane) takes key/value `lane` of
-    // tokens 4 wave .. 4 wave + 3; the next chunk's are loaded while this one runs
-    WT nw[4];
-    uint16_t nk[4], na[4], nr[4], nd[4];
-    auto load_chunk = [&](int cc) {
+    const long TSH = (long)p.H * kN;  // elements from one token to the next
+    // Issues the same loads on every path: the index is clamped to the last one
+    // and each token to T - 1, which keeps every address inside the tensors;
+    // prep() replaces the values of tokens past T.
+    auto load = [&](int i, ChainRaw<W32> &x) {
+        const int c = nch - 1 - min(i, nch - 1);
+        const long base = ((b * p.T + (long)c * kC) * p.H + h) * kN;  // token c*16, key 0
+        const int tmax = p.T - 1 - c * kC;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const long t = (long)cc * kC + 4 * wave + e;
-            const long o = tok_off(p, b, h, t < p.T ? t : 0) + lane;
-            nw[e] = pw[o]; nk[e] = pkap[o]; na[e] = pa[o]; nr[e] = pr[o]; nd[e] = pdy[o];
+            const long o = base + (long)min(4 * pb + e, tmax) * TSH + lane;
+            x.w[e] = pw[o];
+            x.k[e] = pkap[o];
+            x.a[e] = pa[o];
+            x.r[e] = pr[o];
+            x.d[e] = pdy[o];
         }
     };
-    load_chunk(nch - 1);
-
-    for (int c = nch - 1; c >= 0; --c) {
+    // decay product over the wave's four tokens of index i (1 past T)
+    auto total = [&](int i, const ChainRaw<W32> &x) {
+        const int t0 = (nch - 1 - min(i, nch - 1)) * kC + 4 * pb;
+        float cp = 1.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cp *= (t0 + e < p.T) ? widen(x.w[e]) : 1.f;
+        return cp;
+    };
+    // operands of index i into buffer i % 3
+    auto prep = [&](int i, const ChainRaw<W32> &x) {
+        const int c = nch - 1 - min(i, nch - 1);
+        ChainOps &o = L.o[i % 3];
         float wv[4], kv[4], av[4], rv[4], dv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool ok = (long)c * kC + 4 * wave + e < p.T;
-            wv[e] = ok ? widen(nw[e]) : 1.f;
-            kv[e] = ok ? bf16_lo(nk[e]) : 0.f;
-            av[e] = ok ? bf16_lo(na[e]) : 0.f;
-            rv[e] = ok ? bf16_lo(nr[e]) : 0.f;
-            dv[e] = ok ? bf16_lo(nd[e]) : 0.f;
+            const bool ok = c * kC + 4 * pb + e < p.T;
+            wv[e] = ok ? widen(x.w[e]) : 1.f;
+            kv[e] = ok ? bf16_lo(x.k[e]) : 0.f;
+            av[e] = ok ? bf16_lo(x.a[e]) : 0.f;
+            rv[e] = ok ? bf16_lo(x.r[e]) : 0.f;
+            dv[e] = ok ? bf16_lo(x.d[e]) : 0.f;
         }
-        if (c > 0) load_chunk(c - 1);
-        float cp[4];
-        cp[0] = wv[0];
-#pragma unroll
-        for (int e = 1; e < 4; ++e) cp[e] = cp[e - 1] * wv[e];
-        L.carry[wave][lane] = cp[3];
-        __syncthreads();
         float pre = 1.f, tot = 1.f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const float x = L.carry[q][lane];
-            pre = q < wave ? pre * x : pre;
-            tot *= x;
+            const float y = L.carry[i & 1][q][lane];
+            pre = q < pb ? pre * y : pre;
+            tot *= y;
         }
-        if (wave == 0) L.gc[lane] = tot;
+        if (pb == 0) o.gc[lane] = tot;
+        f32x4 Kp, Rp;
+        float gam = pre;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int t = 4 * wave + e;
-            const float gam = pre * cp[e], gprev = e ? pre * cp[e - 1] : pre;
-            const float Kp = kv[e] * gprev, Rp = rv[e] * gam;
+            const int t = 4 * pb + e;
+            const float gprev = gam;
+            gam *= wv[e];
+            Kp[e] = kv[e] * gprev;
+            Rp[e] = rv[e] * gam;
             const float Bm = av[e] * kv[e] * __builtin_amdgcn_rcpf(gam);
-            L.kp[t][lane] = bf1(Kp);
-            L.rp[t][lane] = bf1(Rp);
-            L.bm[t][lane] = bf1(Bm);
-            L.dyy[t][lane] = bf1(dv[e]);
+            o.kp[t][lane] = bf1(Kp[e]);
+            o.rp[t][lane] = bf1(Rp[e]);
+            o.bm[t][lane] = bf1(Bm);
         }
+        // the transposed tiles: this lane's key (value) over the wave's four tokens
+        *reinterpret_cast<bf16x4 *>(&o.kpt[lane][4 * pb]) = bf4(Kp);
+        *reinterpret_cast<bf16x4 *>(&o.rpt[lane][4 * pb]) = bf4(Rp);
+        *reinterpret_cast<bf16x4 *>(&o.dyt[lane][4 * pb]) = bf4(f32x4{dv[0], dv[1], dv[2], dv[3]});
+    };
+    // matrices of index i from buffer i % 3 into tiles of parity i & 1: wave 4
+    // the inverse, wave 5 Mbr
+    auto matrices = [&](int i) {
+        const ChainOps &o = L.o[i % 3];
+        ChainMatTiles &mt = L.m[i & 1];
+        if (pb == 0) {
+            Acc16 dn = z4(), dnt = z4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x4 kpa = frag(o.kp, 0, 16 * kb, lane), bma = frag(o.bm, 0, 16 * kb, lane);
+                dn = mma(kpa, bma, dn);    // D(N), N = Kp Bm^T
+                dnt = mma(bma, kpa, dnt);  // D(N^T)
+            }
+            f32x4 dx, dxt;  // D(X) = A operand of X^T (D(X^T) unused here)
+            tri_inverse(mask<true, true>(dn, lane).v, mask<false, true>(dnt, lane).v, lane, dx, dxt);
+            *reinterpret_cast<bf16x4 *>(&mt.xa[lo][g4]) = bf4(dx);
+        } else if (pb == 1) {
+            Acc16 dmbr = z4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                dmbr = mma(frag(o.rp, 0, 16 * kb, lane), frag(o.bm, 0, 16 * kb, lane), dmbr);
+            *reinterpret_cast<bf16x4 *>(&mt.mbra[lo][g4]) = bf4(mask<true, false>(dmbr, lane));
+        }
+    };
+    // s_waitcnt immediate letting the loads of one index (20 per lane) stay in
+    // flight: vmcnt = 20 (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14),
+    // expcnt and lgkmcnt unlimited
+    constexpr int kLoads = 20;
+    constexpr int kWaitOneIndex = (kLoads & 0xF) | (0x7 << 4) | (0xF << 8) | (((kLoads >> 4) & 0x3) << 14);
+
+    ChainRaw<W32> xa, xb;  // the ring: indices of even and odd parity
+    load(0, xa);
+    load(1, xb);
+    __builtin_amdgcn_s_waitcnt(kWaitOneIndex);  // index 0 in registers
+    L.carry[0][pb][lane] = total(0, xa);
+    __syncthreads();  // the decay totals of index 0
+    // interval q: matrices of q - 1, operands of q, loads of q + 2, totals of q + 1
+    auto interval = [&](int q, ChainRaw<W32> &cur, ChainRaw<W32> &nxt) {
+        matrices(q - 1 < 0 ? 2 : q - 1);  // (q = 0: buffer 2 holds nothing yet; unused)
+        prep(q, cur);
+        load(q + 2, cur);
+        __builtin_amdgcn_s_waitcnt(kWaitOneIndex);  // index q + 1 in registers
+        L.carry[(q + 1) & 1][pb][lane] = total(q + 1, nxt);
         __syncthreads();
-
-        // ---- chunk matrices (every wave forms its own copy)
-        Acc16 dn = z4(), dnt = z4(), dmbr = z4();
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), bma = frag(L.bm, 0, 16 * kb, lane);
-            const bf16x4 rpa = frag(L.rp, 0, 16 * kb, lane);
-            dn = mma(kpa, bma, dn);     // D(N), N = Kp Bm^T
-            dnt = mma(bma, kpa, dnt);   // D(N^T)
-            dmbr = mma(rpa, bma, dmbr); // D(Mbr), Mbr = Rp Bm^T
-        }
-        dn = mask<true, true>(dn, lane);
-        dnt = mask<false, true>(dnt, lane);
-        dmbr = mask<true, false>(dmbr, lane);
-        f32x4 dx, dxt;  // D(X) = A operand of X^T (D(X^T) unused here)
-        tri_inverse(dn.v, dnt.v, lane, dx, dxt);
-
-        // ---- chain step: dSh = dS_C diag(g_C), stored as the bf16 MFMA operand
-        // that both kernels use, then dS0 of the chunk
-        uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
-        bf16x4 Sb[4];
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) St[jb].v[e] *= L.gc[16 * jb + g4 + e];
-            Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
-            *reinterpret_cast<bf16x4 *>(ck + 16 * jb + g4) = Sb[jb];
-        }
-        const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY (tokens x values)
-        Acc16 rhs = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) rhs = mma(frag(L.bm, 0, 16 * jb, lane), Sb[jb], rhs);  // + Bm dSh^T
-        const Acc16 up = mma(bf4(dx), bf4(rhs), z4());  // X^T rhs = -dZ
-        const bf16x4 dzb = bf4(neg(up));
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            St[jb] = mma(colfrag(L.rp, 16 * jb, lane), dyb, St[jb]);  // + Rp^T dY (A of Rp^T)
-            St[jb] = mma(colfrag(L.kp, 16 * jb, lane), dzb, St[jb]);  // + Kp^T dZ
-        }
-        __syncthreads();  // the next chunk's operands overwrite LDS
-    }
-    if (p.ds0) {
-#pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
-            *reinterpret_cast<float4 *>(p.ds0 + bh * kN * kN + srow + 16 * jb + g4) =
-                make_float4(St[jb][0], St[jb][1], St[jb][2], St[jb][3]);
+    };
+    for (int q = 0; q < S; q += 2) {
+        interval(q, xa, xb);
+        interval(q + 1, xb, xa);
     }
 }
 
@@ -705,14 +808,14 @@ hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream) {
     const long nch = (p.T + kC - 1) / kC;
     const long ngrp = (nch + kGradChunks - 1) / kGradChunks;
     if (p.w32) {
-        hipLaunchKernelGGL(bwd_chain_kernel<true>, dim3((unsigned)heads), dim3(kThreads), 0,
+        hipLaunchKernelGGL(bwd_chain_kernel<true>, dim3((unsigned)heads), dim3(kChainThreads), 0,
                            stream, p);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL(bwd_grad_kernel<true>, dim3((unsigned)(heads * ngrp)), dim3(kThreads),
                            0, stream, p);
     } else {
-        hipLaunchKernelGGL(bwd_chain_kernel<false>, dim3((unsigned)heads), dim3(kThreads), 0,
+        hipLaunchKernelGGL(bwd_chain_kernel<false>, dim3((unsigned)heads), dim3(kChainThreads), 0,
                            stream, p);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;

@@ -25,7 +25,7 @@
 // products as one v_mfma_f32_16x16x32_bf16); the state stays fp32 in the
 // accumulators.  The unit lower-triangular inverse (I + M_bk)^-1 is formed by
 // block substitution (tri_inverse in wkv7_mfma.h: float32 4 x 4 diagonal
-// blocks, then products on split bf16 operands), so it stays accurate when
+// blocks, then float32 matrix-core products), so it stays accurate when
 // removal keys repeat or correlate within a chunk.  The decay ratios stay
 // within w_min^-16 (1.6e4 for the pages' w > 0.545).  Requires 0 < w <= 1.
 //
