@@ -107,11 +107,6 @@ __device__ __forceinline__ Acc16 mask(Acc16 d, int lane) {
     return d;
 }
 
-// the decay's element type: bf16 bits, or float32 (RWKV7_DT_BF16_W32)
-template <bool W32> struct DecayT { using type = uint16_t; };
-template <> struct DecayT<true> { using type = float; };
-__device__ __forceinline__ float widen(uint16_t u) { return bf16_lo(u); }
-__device__ __forceinline__ float widen(float x) { return x; }
 
 // Element offset of token t of (b, h) in a [B,T,H,64] tensor.
 __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, long t) {
@@ -119,24 +114,27 @@ __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, lo
 }
 
 // ---------------------------------------------------------------- reverse chain
-// One workgroup of eight waves per (b, h) walks the chunks from the last to the
+// One workgroup of nine waves per (b, h) walks the chunks from the last to the
 // first as a three-stage pipeline with one barrier per interval (as the
 // forward chunked kernel does).  At interval q, with i = q - 2 the chain index
 // of the chunk whose cotangent step runs (chunk nch - 1 - i):
 //   waves 4..7 ("prep"): wave 4+b forms the operands of tokens 4b .. 4b+3 of
-//     chain index q (thread = key / value `lane`), writes them to buffer q % 3,
-//     and issues the loads of index q + 2 into its two-deep register ring; at
-//     the end it multiplies the decays of index q + 1 over its four tokens and
-//     leaves the total in LDS for the later waves (read after the barrier).
-//     Wave 4 also forms X = (I + N)^-1 of index q - 1 and wave 5 its Mbr, into
-//     the matrix tiles of parity (q - 1) & 1;
+//     chain index q (one token per DPP row, four keys per lane, so each load
+//     reads whole token rows), writes them to buffer q % 3, and issues the
+//     loads of index q + 3 into its three-deep register ring; at the end it
+//     multiplies the decays of index q + 1 over its four tokens and leaves the
+//     total in LDS for the later waves (read after the barrier);
+//   wave 8 ("matrix"): forms X = (I + N)^-1 and Mbr of index q - 1 from buffer
+//     (q - 1) % 3 into the matrix tiles of parity (q - 1) & 1;
 //   waves 0..3 ("chain"): wave c owns values 16c .. 16c+15 of dS^T as fp32 MFMA
 //     accumulator tiles and runs the cotangent step of index q - 2 from buffer
 //     (q - 2) % 3 and the matrix tiles of parity q & 1: it stores the chunk's
 //     dSh (bf16, the operand the gradient kernel reads) and forms dS0.
 // Every load is issued on every path (chunk indices clamped), so the ring's
 // wait counts stay exact.
-constexpr int kChainThreads = 512;  // 4 chain waves + 4 prep waves
+constexpr int kChainThreads = 576;  // 4 chain waves + 4 prep waves + 1 matrix wave
+// s_waitcnt immediate: vmcnt(0) only (expcnt and lgkmcnt unlimited)
+constexpr int kWaitAllLoads = (0x7 << 4) | (0xF << 8);
 
 struct __align__(16) ChainOps {
     short kp[kC][kSK], rp[kC][kSK], bm[kC][kSK];  // tokens x keys
@@ -154,17 +152,18 @@ struct __align__(16) ChainLds {
     float carry[2][4][kN];  // per index parity: decay product of each prep wave's 4 tokens
 };
 
-// raw inputs of one chain index held by a prep lane: key / value `lane` of the
-// wave's four tokens
+// raw inputs of one chain index held by a prep lane: keys (values) 4lo .. 4lo+3
+// of its token, as four bf16 (the decay as four float32 with W32)
+template <bool W32> struct ChainRawW { using type = uint2; };
+template <> struct ChainRawW<true> { using type = float4; };
 template <bool W32>
 struct ChainRaw {
-    typename DecayT<W32>::type w[4];
-    uint16_t k[4], a[4], r[4], d[4];  // kappa, a, r, dy
+    typename ChainRawW<W32>::type w;
+    uint2 k, a, r, d;  // kappa, a, r, dy
 };
 
 template <bool W32>
 __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p) {
-    using WT = typename DecayT<W32>::type;
     __shared__ ChainLds L;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int lo = lane & 15, g4 = 4 * (lane >> 4);
@@ -172,7 +171,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
     const int nch = (p.T + kC - 1) / kC;
-    const int S = (nch + 3) & ~1;  // intervals: nch + 2, rounded up to whole loop trips
+    const int S = (nch + 4) / 3 * 3;  // intervals: nch + 2, rounded up to whole loop trips
 
     if (wave < 4) {
         // ---------------- chain waves ----------------
@@ -189,6 +188,11 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
                 St[jb] = z4();
             }
         }
+        // the state cotangent is in registers before the loop: a load still in
+        // flight at its head would make the compiler wait for every vector memory
+        // operation there, the previous chunk's dSh stores included (on this
+        // target stores count in the same counter as loads)
+        __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         __syncthreads();  // the decay totals of index 0
         for (int q = 0; q < S; ++q) {
             const int i = q - 2;
@@ -234,127 +238,180 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
         return;
     }
 
+    if (wave == 8) {
+        // ---------------- matrix wave: X = (I + N)^-1 and Mbr of index q - 1 ----------------
+        // (the interval's critical path: the prep waves' operand formation runs
+        // beside it on the other SIMDs)
+        __builtin_amdgcn_s_setprio(2);
+        __syncthreads();  // the decay totals of index 0
+        for (int q = 0; q < S; ++q) {
+            const int i = q - 1;
+            if (i >= 0 && i < nch) {
+                const ChainOps &o = L.o[i % 3];
+                ChainMatTiles &mt = L.m[i & 1];
+                Acc16 dn = z4(), dnt = z4(), dmbr = z4();
+#pragma unroll
+                for (int kb = 0; kb < 4; ++kb) {
+                    const bf16x4 kpa = frag(o.kp, 0, 16 * kb, lane), bma = frag(o.bm, 0, 16 * kb, lane);
+                    dn = mma(kpa, bma, dn);    // D(N), N = Kp Bm^T
+                    dnt = mma(bma, kpa, dnt);  // D(N^T)
+                    dmbr = mma(frag(o.rp, 0, 16 * kb, lane), bma, dmbr);  // D(Mbr), Mbr = Rp Bm^T
+                }
+                *reinterpret_cast<bf16x4 *>(&mt.mbra[lo][g4]) = bf4(mask<true, false>(dmbr, lane));
+                f32x4 dx, dxt;  // D(X) = A operand of X^T (D(X^T) unused here)
+                tri_inverse(mask<true, true>(dn, lane).v, mask<false, true>(dnt, lane).v, lane, dx,
+                            dxt);
+                *reinterpret_cast<bf16x4 *>(&mt.xa[lo][g4]) = bf4(dx);
+            }
+            __syncthreads();
+        }
+        return;
+    }
+
     // ---------------- prep waves ----------------
-    const int pb = wave - 4;  // tokens 4pb .. 4pb+3 of each chunk
-    const uint16_t *pr = static_cast<const uint16_t *>(p.r);
-    const WT *pw = static_cast<const WT *>(p.w);
-    const uint16_t *pkap = static_cast<const uint16_t *>(p.kappa), *pa = static_cast<const uint16_t *>(p.a);
-    const uint16_t *pdy = static_cast<const uint16_t *>(p.dy);
+    // Token-major lanes: prep wave pb holds tokens 4pb .. 4pb+3 of a chunk, one
+    // per DPP row g, and lane lo of the row keys (values) 4lo .. 4lo+3, so each
+    // load instruction reads four whole 128-byte token rows.
+    const int pb = wave - 4, t_in = 4 * pb + (lane >> 4), k0 = 4 * lo;
     const long TSH = (long)p.H * kN;  // elements from one token to the next
     // Issues the same loads on every path: the index is clamped to the last one
-    // and each token to T - 1, which keeps every address inside the tensors;
+    // and the token to T - 1, which keeps every address inside the tensors;
     // prep() replaces the values of tokens past T.
     auto load = [&](int i, ChainRaw<W32> &x) {
         const int c = nch - 1 - min(i, nch - 1);
-        const long base = ((b * p.T + (long)c * kC) * p.H + h) * kN;  // token c*16, key 0
-        const int tmax = p.T - 1 - c * kC;
+        const long o = ((b * p.T + (long)c * kC) * p.H + h) * kN +
+                       (long)min(t_in, p.T - 1 - c * kC) * TSH + k0;
+        x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + o);
+        if constexpr (W32)
+            x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + o);
+        else
+            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + o);
+        x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + o);
+        x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + o);
+        x.d = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.dy) + o);
+    };
+    // the lane's four decays of index i (1 past T)
+    auto decays = [&](int i, const ChainRaw<W32> &x, float (&w)[4]) {
+        const bool ok = (nch - 1 - min(i, nch - 1)) * kC + t_in < p.T;
+        if constexpr (W32) {
+            w[0] = x.w.x; w[1] = x.w.y; w[2] = x.w.z; w[3] = x.w.w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const long o = base + (long)min(4 * pb + e, tmax) * TSH + lane;
-            x.w[e] = pw[o];
-            x.k[e] = pkap[o];
-            x.a[e] = pa[o];
-            x.r[e] = pr[o];
-            x.d[e] = pdy[o];
+            for (int e = 0; e < 4; ++e) w[e] = ok ? w[e] : 1.f;
+        } else {
+            const unsigned w01 = ok ? x.w.x : 0x3F803F80u, w23 = ok ? x.w.y : 0x3F803F80u;
+            w[0] = bf16_lo(w01); w[1] = bf16_hi(w01); w[2] = bf16_lo(w23); w[3] = bf16_hi(w23);
         }
     };
-    // decay product over the wave's four tokens of index i (1 past T)
-    auto total = [&](int i, const ChainRaw<W32> &x) {
-        const int t0 = (nch - 1 - min(i, nch - 1)) * kC + 4 * pb;
-        float cp = 1.f;
+    // Products of w over the wave's four tokens (the DPP rows) for the lane's
+    // keys: lp inclusive, lx exclusive.  Row pairs by v_permlane16_swap (its two
+    // results hold rows 2k and 2k+1 of the pair k), then the pair (0, 1) total
+    // into rows 2, 3 by v_permlane32_swap (its first result holds, in the upper
+    // rows, the lower rows of the second operand).
+    const bool odd = (lane >> 4) & 1, upper = lane >= 32;
+    auto scan = [&](const float (&w)[4], float (&lp)[4], float (&lx)[4]) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) cp *= (t0 + e < p.T) ? widen(x.w[e]) : 1.f;
-        return cp;
+        for (int e = 0; e < 4; ++e) {
+            const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(w[e]),
+                                                              __float_as_uint(w[e]), false, false);
+            const float h0 = __uint_as_float(h16[0]), h1 = __uint_as_float(h16[1]);
+            const float pair = h0 * h1;
+            const float in1 = odd ? pair : h0;
+            const float ex1 = odd ? h0 : 1.f;
+            const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(pair),
+                                                              __float_as_uint(pair), false, false);
+            const float below = upper ? __uint_as_float(h32[0]) : 1.f;
+            lp[e] = in1 * below;
+            lx[e] = ex1 * below;
+        }
+    };
+    // the wave's decay total of index i (row 3's inclusive product) into LDS
+    auto total = [&](int i, const ChainRaw<W32> &x) {
+        float w[4], lp[4], lx[4];
+        decays(i, x, w);
+        scan(w, lp, lx);
+        if (lane >= 48)
+            *reinterpret_cast<float4 *>(&L.carry[i & 1][pb][k0]) = make_float4(lp[0], lp[1], lp[2], lp[3]);
     };
     // operands of index i into buffer i % 3
     auto prep = [&](int i, const ChainRaw<W32> &x) {
         const int c = nch - 1 - min(i, nch - 1);
+        const bool ok = c * kC + t_in < p.T;
         ChainOps &o = L.o[i % 3];
-        float wv[4], kv[4], av[4], rv[4], dv[4];
+        float w[4], lp[4], lx[4];
+        decays(i, x, w);
+        scan(w, lp, lx);
+        const unsigned k01 = ok ? x.k.x : 0u, k23 = ok ? x.k.y : 0u;
+        const unsigned a01 = ok ? x.a.x : 0u, a23 = ok ? x.a.y : 0u;
+        const unsigned r01 = ok ? x.r.x : 0u, r23 = ok ? x.r.y : 0u;
+        const float kv[4] = {bf16_lo(k01), bf16_hi(k01), bf16_lo(k23), bf16_hi(k23)};
+        const float av[4] = {bf16_lo(a01), bf16_hi(a01), bf16_lo(a23), bf16_hi(a23)};
+        const float rv[4] = {bf16_lo(r01), bf16_hi(r01), bf16_lo(r23), bf16_hi(r23)};
+        const uint2 dyb = ok ? x.d : make_uint2(0u, 0u);
+        // decay of the chunk's tokens before this wave's four (the earlier waves'
+        // totals) and the chunk's total
+        float4 cw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) cw[q] = *reinterpret_cast<const float4 *>(&L.carry[i & 1][q][k0]);
+        f32x4 Kp, Rp, Bm, tot;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const bool ok = c * kC + 4 * pb + e < p.T;
-            wv[e] = ok ? widen(x.w[e]) : 1.f;
-            kv[e] = ok ? bf16_lo(x.k[e]) : 0.f;
-            av[e] = ok ? bf16_lo(x.a[e]) : 0.f;
-            rv[e] = ok ? bf16_lo(x.r[e]) : 0.f;
-            dv[e] = ok ? bf16_lo(x.d[e]) : 0.f;
-        }
-        float pre = 1.f, tot = 1.f;
+            float pr = 1.f, tt = 1.f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float y = L.carry[i & 1][q][lane];
-            pre = q < pb ? pre * y : pre;
-            tot *= y;
-        }
-        if (pb == 0) o.gc[lane] = tot;
-        f32x4 Kp, Rp;
-        float gam = pre;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int t = 4 * pb + e;
-            const float gprev = gam;
-            gam *= wv[e];
+            for (int q = 0; q < 4; ++q) {
+                const float y = (&cw[q].x)[e];
+                pr = q < pb ? pr * y : pr;
+                tt *= y;
+            }
+            tot[e] = tt;
+            const float gam = pr * lp[e], gprev = pr * lx[e];
             Kp[e] = kv[e] * gprev;
             Rp[e] = rv[e] * gam;
-            const float Bm = av[e] * kv[e] * __builtin_amdgcn_rcpf(gam);
-            o.kp[t][lane] = bf1(Kp[e]);
-            o.rp[t][lane] = bf1(Rp[e]);
-            o.bm[t][lane] = bf1(Bm);
+            Bm[e] = av[e] * kv[e] * __builtin_amdgcn_rcpf(gam);
         }
-        // the transposed tiles: this lane's key (value) over the wave's four tokens
-        *reinterpret_cast<bf16x4 *>(&o.kpt[lane][4 * pb]) = bf4(Kp);
-        *reinterpret_cast<bf16x4 *>(&o.rpt[lane][4 * pb]) = bf4(Rp);
-        *reinterpret_cast<bf16x4 *>(&o.dyt[lane][4 * pb]) = bf4(f32x4{dv[0], dv[1], dv[2], dv[3]});
-    };
-    // matrices of index i from buffer i % 3 into tiles of parity i & 1: wave 4
-    // the inverse, wave 5 Mbr
-    auto matrices = [&](int i) {
-        const ChainOps &o = L.o[i % 3];
-        ChainMatTiles &mt = L.m[i & 1];
-        if (pb == 0) {
-            Acc16 dn = z4(), dnt = z4();
+        if (pb == 0 && lane < 16)
+            *reinterpret_cast<float4 *>(&o.gc[k0]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
+        const bf16x4 kpb = bf4(Kp), rpb = bf4(Rp);
+        *reinterpret_cast<bf16x4 *>(&o.kp[t_in][k0]) = kpb;
+        *reinterpret_cast<bf16x4 *>(&o.rp[t_in][k0]) = rpb;
+        *reinterpret_cast<bf16x4 *>(&o.bm[t_in][k0]) = bf4(Bm);
+        // the transposed tiles: keys (values) k0 .. k0+3 at this token's column
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const bf16x4 kpa = frag(o.kp, 0, 16 * kb, lane), bma = frag(o.bm, 0, 16 * kb, lane);
-                dn = mma(kpa, bma, dn);    // D(N), N = Kp Bm^T
-                dnt = mma(bma, kpa, dnt);  // D(N^T)
-            }
-            f32x4 dx, dxt;  // D(X) = A operand of X^T (D(X^T) unused here)
-            tri_inverse(mask<true, true>(dn, lane).v, mask<false, true>(dnt, lane).v, lane, dx, dxt);
-            *reinterpret_cast<bf16x4 *>(&mt.xa[lo][g4]) = bf4(dx);
-        } else if (pb == 1) {
-            Acc16 dmbr = z4();
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
-                dmbr = mma(frag(o.rp, 0, 16 * kb, lane), frag(o.bm, 0, 16 * kb, lane), dmbr);
-            *reinterpret_cast<bf16x4 *>(&mt.mbra[lo][g4]) = bf4(mask<true, false>(dmbr, lane));
+        for (int e = 0; e < 4; ++e) {
+            o.kpt[k0 + e][t_in] = kpb[e];
+            o.rpt[k0 + e][t_in] = rpb[e];
         }
+        o.dyt[k0 + 0][t_in] = (short)(dyb.x & 0xffffu);
+        o.dyt[k0 + 1][t_in] = (short)(dyb.x >> 16);
+        o.dyt[k0 + 2][t_in] = (short)(dyb.y & 0xffffu);
+        o.dyt[k0 + 3][t_in] = (short)(dyb.y >> 16);
     };
-    // s_waitcnt immediate letting the loads of one index (20 per lane) stay in
-    // flight: vmcnt = 20 (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits 15:14),
-    // expcnt and lgkmcnt unlimited
-    constexpr int kLoads = 20;
-    constexpr int kWaitOneIndex = (kLoads & 0xF) | (0x7 << 4) | (0xF << 8) | (((kLoads >> 4) & 0x3) << 14);
+    // s_waitcnt immediate letting the loads of two indices (five per lane each)
+    // stay in flight: vmcnt = 10 (gfx9 encoding: vmcnt[3:0] + vmcnt[5:4] at bits
+    // 15:14), expcnt and lgkmcnt unlimited
+    constexpr int kLoads = 10;
+    constexpr int kWaitTwoIndices = (kLoads & 0xF) | (0x7 << 4) | (0xF << 8) | (((kLoads >> 4) & 0x3) << 14);
 
-    ChainRaw<W32> xa, xb;  // the ring: indices of even and odd parity
-    load(0, xa);
-    load(1, xb);
-    __builtin_amdgcn_s_waitcnt(kWaitOneIndex);  // index 0 in registers
-    L.carry[0][pb][lane] = total(0, xa);
+    // the ring: index q in xs[q % 3], loaded three intervals ahead (one interval
+    // of loads did not cover the memory latency)
+    ChainRaw<W32> xs[3];
+    load(0, xs[0]);
+    load(1, xs[1]);
+    load(2, xs[2]);
+    __builtin_amdgcn_s_waitcnt(kWaitTwoIndices);  // index 0 in registers
+    total(0, xs[0]);
     __syncthreads();  // the decay totals of index 0
-    // interval q: matrices of q - 1, operands of q, loads of q + 2, totals of q + 1
+    // interval q: operands of q, loads of q + 3, totals of q + 1
     auto interval = [&](int q, ChainRaw<W32> &cur, ChainRaw<W32> &nxt) {
-        matrices(q - 1 < 0 ? 2 : q - 1);  // (q = 0: buffer 2 holds nothing yet; unused)
         prep(q, cur);
-        load(q + 2, cur);
-        __builtin_amdgcn_s_waitcnt(kWaitOneIndex);  // index q + 1 in registers
-        L.carry[(q + 1) & 1][pb][lane] = total(q + 1, nxt);
+        load(q + 3, cur);
+        __builtin_amdgcn_s_waitcnt(kWaitTwoIndices);  // index q + 1 in registers
+        total(q + 1, nxt);
         __syncthreads();
     };
-    for (int q = 0; q < S; q += 2) {
-        interval(q, xa, xb);
-        interval(q + 1, xb, xa);
+    for (int q = 0; q < S; q += 3) {
+        interval(q, xs[0], xs[1]);
+        interval(q + 1, xs[1], xs[2]);
+        interval(q + 2, xs[2], xs[0]);
     }
 }
 
@@ -387,8 +444,7 @@ template <bool W32>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void bwd_grad_kernel(
     BackwardArgs p) {
     __shared__ GradLds L;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int lo = lane & 15, g4 = 4 * (lane >> 4);
+    const int wave = threadIdx.x >> 6;
     const int nch = (p.T + kC - 1) / kC;
     const int ngrp = (nch + kGradChunks - 1) / kGradChunks;
     const long bh = blockIdx.x / ngrp;
@@ -411,7 +467,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     constexpr int kPieces = W32 ? 8 * 128 : 7 * 128;
     static_assert(kThreads == 256 && kPieces > 3 * kThreads && kPieces <= 4 * kThreads,
                   "three whole row pieces per thread and a fourth, whole or partial");
-    const long srow = (long)(16 * wave + lo) * kN;
     float4 S0n[4];
     uint2 Dhn[4];  // bf16 dSh
     uint4 rawn[4];
