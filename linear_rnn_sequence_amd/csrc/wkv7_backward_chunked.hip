@@ -113,6 +113,15 @@ __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, lo
     return ((b * p.T + t) * p.H + h) * kN;
 }
 
+// The workspace holds each chunk's dSh (64 x 64 bf16, 8 KiB) in the order the
+// lanes hold it, not row by row: the four bf16 that lane l of wave q holds of
+// key block jb (dSh[16q + (l & 15)][16jb + 4(l >> 4) + e], e < 4) are at
+// element 4 (64 (4q + jb) + l), so each store and load instruction moves 512
+// contiguous bytes (row by row, it touched sixteen 32-byte pieces).
+__device__ __forceinline__ int dsh_tile_offset(int q, int jb, int l) {
+    return 4 * (64 * (4 * q + jb) + l);
+}
+
 // ---------------------------------------------------------------- reverse chain
 // One workgroup of nine waves per (b, h) walks the chunks from the last to the
 // first as a three-stage pipeline with one barrier per interval (as the
@@ -171,7 +180,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
     const int nch = (p.T + kC - 1) / kC;
-    const int S = (nch + 4) / 3 * 3;  // intervals: nch + 2, rounded up to whole loop trips
+    const int S = (nch + 7) / 6 * 6;  // intervals: nch + 2, rounded up to whole loop trips
 
     if (wave < 4) {
         // ---------------- chain waves ----------------
@@ -202,7 +211,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
                 const ChainMatTiles &mt = L.m[i & 1];
                 // dSh = dS_C diag(g_C), stored as the bf16 MFMA operand that both
                 // kernels use, then dS0 of the chunk
-                uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN) + srow;
+                uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN);
                 bf16x4 Sb[4];
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
                     St[jb].v[2] *= gc.z;
                     St[jb].v[3] *= gc.w;
                     Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
-                    *reinterpret_cast<bf16x4 *>(ck + 16 * jb + g4) = Sb[jb];
+                    *reinterpret_cast<bf16x4 *>(ck + dsh_tile_offset(wave, jb, lane)) = Sb[jb];
                 }
                 const bf16x4 dyb = frag(o.dyt, 16 * wave, 0, lane);  // B operand of dY (tokens x values)
                 Acc16 rhs = mma(frag(mt.mbra, 0, 0, lane), dyb, z4());  // Mbr^T dY
@@ -273,22 +282,23 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     // per DPP row g, and lane lo of the row keys (values) 4lo .. 4lo+3, so each
     // load instruction reads four whole 128-byte token rows.
     const int pb = wave - 4, t_in = 4 * pb + (lane >> 4), k0 = 4 * lo;
-    const long TSH = (long)p.H * kN;  // elements from one token to the next
+    const int TSH = p.H * kN;  // elements from one token to the next
     // Issues the same loads on every path: the index is clamped to the last one
     // and the token to T - 1, which keeps every address inside the tensors;
     // prep() replaces the values of tokens past T.
     auto load = [&](int i, ChainRaw<W32> &x) {
         const int c = nch - 1 - min(i, nch - 1);
-        const long o = ((b * p.T + (long)c * kC) * p.H + h) * kN +
-                       (long)min(t_in, p.T - 1 - c * kC) * TSH + k0;
-        x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + o);
+        // the chunk's first token, key 0 (uniform), and the lane's offset from it
+        const long base = ((b * p.T + (long)c * kC) * p.H + h) * kN;
+        const unsigned o = (unsigned)(min(t_in, p.T - 1 - c * kC) * TSH) + k0;
+        x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + base + o);
         if constexpr (W32)
-            x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + o);
+            x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + base + o);
         else
-            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + o);
-        x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + o);
-        x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + o);
-        x.d = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.dy) + o);
+            x.w = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.w) + base + o);
+        x.k = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.kappa) + base + o);
+        x.a = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.a) + base + o);
+        x.d = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.dy) + base + o);
     };
     // the lane's four decays of index i (1 past T)
     auto decays = [&](int i, const ChainRaw<W32> &x, float (&w)[4]) {
@@ -324,22 +334,26 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
             lx[e] = ex1 * below;
         }
     };
-    // the wave's decay total of index i (row 3's inclusive product) into LDS
-    auto total = [&](int i, const ChainRaw<W32> &x) {
-        float w[4], lp[4], lx[4];
+    // the decay products of index i over the wave's four tokens (kept for its
+    // operands one interval later) and the wave's total (row 3's inclusive
+    // product) into LDS
+    struct Scan {
+        float lp[4], lx[4];
+    };
+    auto total = [&](int i, const ChainRaw<W32> &x, Scan &sc) {
+        float w[4];
         decays(i, x, w);
-        scan(w, lp, lx);
+        scan(w, sc.lp, sc.lx);
         if (lane >= 48)
-            *reinterpret_cast<float4 *>(&L.carry[i & 1][pb][k0]) = make_float4(lp[0], lp[1], lp[2], lp[3]);
+            *reinterpret_cast<float4 *>(&L.carry[i & 1][pb][k0]) =
+                make_float4(sc.lp[0], sc.lp[1], sc.lp[2], sc.lp[3]);
     };
     // operands of index i into buffer i % 3
-    auto prep = [&](int i, const ChainRaw<W32> &x) {
+    auto prep = [&](int i, const ChainRaw<W32> &x, const Scan &sc) {
         const int c = nch - 1 - min(i, nch - 1);
         const bool ok = c * kC + t_in < p.T;
         ChainOps &o = L.o[i % 3];
-        float w[4], lp[4], lx[4];
-        decays(i, x, w);
-        scan(w, lp, lx);
+        const float *lp = sc.lp, *lx = sc.lx;
         const unsigned k01 = ok ? x.k.x : 0u, k23 = ok ? x.k.y : 0u;
         const unsigned a01 = ok ? x.a.x : 0u, a23 = ok ? x.a.y : 0u;
         const unsigned r01 = ok ? x.r.x : 0u, r23 = ok ? x.r.y : 0u;
@@ -347,29 +361,35 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
         const float av[4] = {bf16_lo(a01), bf16_hi(a01), bf16_lo(a23), bf16_hi(a23)};
         const float rv[4] = {bf16_lo(r01), bf16_hi(r01), bf16_lo(r23), bf16_hi(r23)};
         const uint2 dyb = ok ? x.d : make_uint2(0u, 0u);
-        // decay of the chunk's tokens before this wave's four (the earlier waves'
-        // totals) and the chunk's total
-        float4 cw[4];
+        // decay of the chunk's tokens before this wave's four: the earlier waves'
+        // totals (pb is the same over the wave, so the tests are scalar branches)
+        const float4(*cw)[kN / 4] = reinterpret_cast<const float4(*)[kN / 4]>(L.carry[i & 1]);
+        float4 pre = make_float4(1.f, 1.f, 1.f, 1.f);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) cw[q] = *reinterpret_cast<const float4 *>(&L.carry[i & 1][q][k0]);
-        f32x4 Kp, Rp, Bm, tot;
+        for (int q = 0; q < 3; ++q) {
+            if (q < pb) {
+                const float4 y = cw[q][lo];
+                pre.x *= y.x; pre.y *= y.y; pre.z *= y.z; pre.w *= y.w;
+            }
+        }
+        if (pb == 0 && lane < 16) {  // the chunk's total, from all four waves
+            float4 tot = cw[0][lo];
+#pragma unroll
+            for (int q = 1; q < 4; ++q) {
+                const float4 y = cw[q][lo];
+                tot.x *= y.x; tot.y *= y.y; tot.z *= y.z; tot.w *= y.w;
+            }
+            *reinterpret_cast<float4 *>(&o.gc[k0]) = tot;
+        }
+        f32x4 Kp, Rp, Bm;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            float pr = 1.f, tt = 1.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float y = (&cw[q].x)[e];
-                pr = q < pb ? pr * y : pr;
-                tt *= y;
-            }
-            tot[e] = tt;
+            const float pr = (&pre.x)[e];
             const float gam = pr * lp[e], gprev = pr * lx[e];
             Kp[e] = kv[e] * gprev;
             Rp[e] = rv[e] * gam;
             Bm[e] = av[e] * kv[e] * __builtin_amdgcn_rcpf(gam);
         }
-        if (pb == 0 && lane < 16)
-            *reinterpret_cast<float4 *>(&o.gc[k0]) = make_float4(tot[0], tot[1], tot[2], tot[3]);
         const bf16x4 kpb = bf4(Kp), rpb = bf4(Rp);
         *reinterpret_cast<bf16x4 *>(&o.kp[t_in][k0]) = kpb;
         *reinterpret_cast<bf16x4 *>(&o.rp[t_in][k0]) = rpb;
@@ -394,24 +414,29 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     // the ring: index q in xs[q % 3], loaded three intervals ahead (one interval
     // of loads did not cover the memory latency)
     ChainRaw<W32> xs[3];
+    Scan sc[2];  // the decay products of the index being prepared and of the next
     load(0, xs[0]);
     load(1, xs[1]);
     load(2, xs[2]);
     __builtin_amdgcn_s_waitcnt(kWaitTwoIndices);  // index 0 in registers
-    total(0, xs[0]);
+    total(0, xs[0], sc[0]);
     __syncthreads();  // the decay totals of index 0
     // interval q: operands of q, loads of q + 3, totals of q + 1
-    auto interval = [&](int q, ChainRaw<W32> &cur, ChainRaw<W32> &nxt) {
-        prep(q, cur);
+    auto interval = [&](int q, ChainRaw<W32> &cur, ChainRaw<W32> &nxt, const Scan &scur,
+                        Scan &snxt) {
+        prep(q, cur, scur);
         load(q + 3, cur);
         __builtin_amdgcn_s_waitcnt(kWaitTwoIndices);  // index q + 1 in registers
-        total(q + 1, nxt);
+        total(q + 1, nxt, snxt);
         __syncthreads();
     };
-    for (int q = 0; q < S; q += 3) {
-        interval(q, xs[0], xs[1]);
-        interval(q + 1, xs[1], xs[2]);
-        interval(q + 2, xs[2], xs[0]);
+    for (int q = 0; q < S; q += 6) {  // (S is a multiple of 6)
+        interval(q, xs[0], xs[1], sc[0], sc[1]);
+        interval(q + 1, xs[1], xs[2], sc[1], sc[0]);
+        interval(q + 2, xs[2], xs[0], sc[0], sc[1]);
+        interval(q + 3, xs[0], xs[1], sc[1], sc[0]);
+        interval(q + 4, xs[1], xs[2], sc[0], sc[1]);
+        interval(q + 5, xs[2], xs[0], sc[1], sc[0]);
     }
 }
 
@@ -478,11 +503,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int g4l = 4 * ((tid & 63) >> 4);
         const long srowl = (long)(16 * (tid >> 6) + (tid & 15)) * kN;
         const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srowl;
-        const uint16_t *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN) + srowl;
+        const uint16_t *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4l);
-            Dhn[jb] = *reinterpret_cast<const uint2 *>(dsp + 16 * jb + g4l);
+            Dhn[jb] = *reinterpret_cast<const uint2 *>(dsp + dsh_tile_offset(tid >> 6, jb, tid & 63));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
