@@ -451,6 +451,7 @@ struct GradLds {
         struct {                  // phase 3's elementwise part onwards
             float dlg[kC][kN];    // decay-gradient terms of each token
             float dkk[kC][kN];    // dKp * Kp (belongs to the previous token's decay)
+            short outg[4][kC][kSK];  // dr, dk, da, dkappa (bf16), tokens x keys
         } e;
     } u;
     short rr[kC][kSK], kk[kC][kSK], ka[kC][kSK], aa[kC][kSK], ww[kC][kSK];  // raw inputs
@@ -579,17 +580,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         // every chunk but a ragged last one stores all 16 tokens without a test
         const long tb = tok_off(p, b, h, t0), TS = (long)p.H * kN;
         const bool full = t0 + kC <= p.T;
-        auto put4 = [&](void *base, long off, const float (&x)[4]) {  // tokens g4 .. g4+3
-            uint16_t *q = static_cast<uint16_t *>(base) + tb + off;
-            if (full) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) q[(g4 + e) * TS] = bf1u(x[e]);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (t0 + g4 + e < p.T) q[(g4 + e) * TS] = bf1u(x[e]);
-            }
-        };
         f32x4 S0[4];
         bf16x4 Dh[4];  // dSh, bf16 as stored
 #pragma unroll
@@ -662,6 +652,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         if (c + 1 < c_end) load_chunk(c + 1);
 
         // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
+        bf16x4 dvb;  // this lane's dv (tokens g4 .. g4+3, value 16 wave + lo)
         {
             // exit-state term sum_i dSh S0 over this block's values
 #pragma unroll
@@ -697,8 +688,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 L.uu[t][16 * wave + lo] = bf1(u[e]);
                 L.dzz[t][16 * wave + lo] = bf1(dz[e]);
             }
-            const float dvv[4] = {dv[0], dv[1], dv[2], dv[3]};
-            put4(p.dv, 16 * wave + lo, dvv);
+            dvb = bf4(dv);  // stored with the other gradients after phase 3
         }
         __syncthreads();
 
@@ -782,6 +772,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             dkp = mma(bf4(dmkt), kmb, dkp);
             dkp = mma(bf4(neg(dmnt)), bmb, dkp);
             __syncthreads();  // the state tiles are read: their LDS is reused below
+            // (and the value tiles: dv waits in U's)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) L.uu[g4 + e][16 * wave + lo] = dvb[e];
 
             // elementwise: lane (token g4 + e, key 16 wave + lo)
             const int j = 16 * wave + lo;
@@ -818,12 +811,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 o_dr[e] = dr; o_dk[e] = dk; o_da[e] = da; o_dkap[e] = dkap;
             }
             L.dlgc[4 + (lane >> 4)][j] = csum;
-            put4(p.dr, j, o_dr);
-            put4(p.dk, j, o_dk);
-            put4(p.da, j, o_da);
-            put4(p.dkappa, j, o_dkap);
+            // the gradients go out through LDS: stored from here, each store
+            // instruction would write sixteen 32-byte pieces of token rows
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int t = g4 + e;
+                L.u.e.outg[0][t][j] = bf1(o_dr[e]);
+                L.u.e.outg[1][t][j] = bf1(o_dk[e]);
+                L.u.e.outg[2][t][j] = bf1(o_da[e]);
+                L.u.e.outg[3][t][j] = bf1(o_dkap[e]);
+            }
         }
         __syncthreads();
+
+        // ---- the chunk's dr, dk, da, dkappa and dv as whole token rows: wave q
+        // stores tokens 4q .. 4q+3, four keys (values) per lane
+        {
+            const int tok = 4 * wave + (lane >> 4), k0 = 4 * lo;
+            if (full || t0 + tok < p.T) {
+                void *const dst[4] = {p.dr, p.dk, p.da, p.dkappa};
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(dst[q]) + tb + tok * TS + k0) =
+                        *reinterpret_cast<const uint2 *>(&L.u.e.outg[q][tok][k0]);
+                *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.dv) + tb + tok * TS + k0) =
+                    *reinterpret_cast<const uint2 *>(&L.uu[tok][k0]);
+            }
+        }
 
         // ---- phase 4: decay gradients, a reverse sum over the chunk's tokens per key
         if (wave == 0) {
