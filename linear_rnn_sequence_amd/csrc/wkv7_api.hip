@@ -484,8 +484,9 @@ static rwkv7_status decode_impl(const void *r, const void *w, const void *k, con
     tok = tok / 4 * esz;                                       // bytes of the other vectors
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
-    // N/32 * 2 waves (workgroups) per head: keep the grid within its x limit
-    if ((size_t)B * H * (N == 128 ? 8 : 2) > 0xffffffffu) return RWKV7_ERR_SHAPE;
+    // one workgroup per head, 256 threads (1024 at N = 128): the grid's extent in
+    // threads must fit in 32 bits
+    if ((size_t)B * H * (N == 128 ? 1024 : 256) > 0xffffffffu) return RWKV7_ERR_SHAPE;
     // the six vectors (kappa unused with the prologue) and the prologue's gate
     const void *ins[7] = {r, w, k, v, pro ? nullptr : kappa, a, pro ? pro->g : nullptr};
     auto in_rng = [&](int i) {

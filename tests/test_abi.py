@@ -111,6 +111,12 @@ def test_decode_validation_codes():
     assert dec(state=fake(6, 8)) == 5
     assert dec(y=fake(6, 64)) == 6             # y inside the state
     assert dec(state=fake(1)) == 6             # state overlaps w
+    # one 256-thread workgroup per head (1024 at N = 128): a grid of more than
+    # 2^32 - 1 threads is a shape error, the largest one that fits is not
+    assert dec(B=(1 << 24) + 1, H=1) == 2
+    assert dec(B=(1 << 24) - 1, H=1) != 2
+    assert dec(B=1 << 22, H=1, N=128) == 2
+    assert dec(B=(1 << 22) - 1, H=1, N=128) != 2
 
 
 def test_workspace_query_is_pure():
