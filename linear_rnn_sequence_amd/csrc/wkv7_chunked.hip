@@ -58,8 +58,10 @@
 //
 // Variants (template parameters and ForwardArgs fields):
 //   - segments: long sequences of few heads are cut into parallel time
-//     segments; a 12-wave summary pass computes each segment's transition
-//     (state started at I, v = 0) and offset (started at 0), a combine kernel
+//     segments; a summary pass computes each segment's transition (state
+//     started at I, v = 0) and offset (started at 0), each chain wave carrying
+//     both for its value rows (the same eight waves, so two workgroups still
+//     share a CU), a combine kernel
 //     forms the entry states S_in[g+1] = S_in[g] P_g + dS_g in fp32, and the
 //     main pass reruns every segment from its entry state;
 //   - W32: the decay arrives as float32;
@@ -119,7 +121,7 @@ struct Geo {
     static constexpr int threads = 64 * (CW + PW);
 };
 constexpr int kThreads = Geo<64>::threads;  // 4 chain waves + 4 prep waves
-constexpr int kThreadsSummary = 768;        // + 4 chain waves for the transition rows
+constexpr int kThreadsSummary = kThreads;  // the same waves; each chain wave carries two states
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
 // A pair tile holds two 16x16 tiles (X | Y) so that a lane's K = 32 operand
@@ -543,18 +545,19 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
 // SUMMARY = false: y and the final state of each (b, h, segment) from its entry
 //   state (the whole sequence when there is one segment).
 // SUMMARY = true: for each (b, h, segment) but the last, the segment's offset
-//   dS (waves 0..3: entry state 0) and transition P (waves 8..11: entry state I,
-//   v = 0), both as final states; no readouts.  Final state = S_in P + dS.
+//   dS (entry state 0) and transition P (entry state I, v = 0), both as final
+//   states, both carried by chain wave b for value rows 16b .. 16b+15; no
+//   readouts.  Final state = S_in P + dS.
 // YADD: add the float32 readouts p.y_add (the reverse pass of a bidirectional
 // call) before the epilogue.
 //
 // NH = 128 (head size 128): eight chain waves (one per value block) and two prep
 // groups of four waves, each group preparing 64 of every token's keys; 1024
-// threads.  No segments (the summary pass would need eight more chain waves),
-// no fused prologue, no bidirectional pass and no stored states.
+// threads.  No segments (one workgroup per CU already), no fused prologue, no
+// bidirectional pass and no stored states.
 template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD, int NH>
 __global__ __launch_bounds__(SUMMARY ? kThreadsSummary : Geo<NH>::threads)
-__attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
+__attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
     ChunkedParams cp) {
     static_assert(NH == 64 || (!SUMMARY && !YADD), "head size 128: plain forward only");
     using G = Geo<NH>;
@@ -566,14 +569,12 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
     const int b = bh / p.H, h = bh - b * p.H;
     const int t0 = seg * cp.seg_len;
     const int wave = threadIdx.x >> 6;
-    // chain waves 0 .. CW-1 (and 8..11, the transition rows, in SUMMARY); prep
-    // waves CW .. CW+PW-1 in groups of four
-    const bool chain_wave = wave < G::CW || (SUMMARY && wave >= 8);
+    // chain waves 0 .. CW-1; prep waves CW .. CW+PW-1 in groups of four
+    const bool chain_wave = wave < G::CW;
     const int wblk = chain_wave ? (wave & (G::CW - 1)) : ((wave - G::CW) & 3);
     const int wkh = chain_wave ? 0 : (wave - G::CW) >> 2;
     const Chunked<EPI, W32, FUSED, NH> K(p, b, h, t0, min(cp.seg_len, p.T - t0), wblk, wkh);
     const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
-    const bool p_rows = SUMMARY && wave >= 8;       // transition rows
     const int nch = (K.Tl + kC - 1) / kC;
     constexpr long NN = (long)NH * NH;
     const long srow = (long)(16 * blk + lo) * NH;   // this lane's value row i in a state
@@ -582,7 +583,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
     const float *s_in = SUMMARY ? nullptr
                       : (cp.nseg == 1 ? (p.s0 ? p.s0 + (long)bh * NN : nullptr)
                                       : cp.ws_sin + sidx * NN);
-    float *s_fin = SUMMARY ? (p_rows ? cp.ws_p : cp.ws_ds) + sidx * NN
+    float *s_fin = SUMMARY ? cp.ws_ds + sidx * NN
                  : (seg == cp.nseg - 1 && p.s_out ? p.s_out + (long)bh * NN : nullptr);
     // stored states (training forward): chunk c of this range is global chunk t0/kC + c
     static_assert(kC == kCkpt, "a chunk is one checkpoint interval");
@@ -592,18 +593,21 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
 
     if (chain_wave) {
         // ---------------- chain waves: state, MFMA chain, readouts ----------------
-        // S^T tile jb holds rows j = 16jb + 4g + e, column i = 16blk + lo
-        Acc32 Z[KB];
+        // S^T tile jb holds rows j = 16jb + 4g + e, column i = 16blk + lo.  SUMMARY:
+        // Z is the offset (entry state 0) and Zp the transition (entry state I,
+        // v = 0) of the same value rows, advanced side by side over the chunks.
+        Acc32 Z[KB], Zp[KB];
 #pragma unroll
         for (int jb = 0; jb < KB; ++jb) {
             if (s_in) {
                 const float4 x = *reinterpret_cast<const float4 *>(s_in + srow + 16 * jb + 4 * g);
                 Z[jb].v = f32x4{x.x, x.y, x.z, x.w};
             } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)  // identity for the transition rows
-                    Z[jb].v[e] = (p_rows && 16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
+                Z[jb] = Acc32::zero();
             }
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                Zp[jb].v[e] = (16 * jb + 4 * g + e == 16 * blk + lo) ? 1.f : 0.f;
         }
         // GroupNorm weight and bias of this lane's four value channels
         float lnw[4] = {1.f, 1.f, 1.f, 1.f}, lnb[4] = {0.f, 0.f, 0.f, 0.f};
@@ -618,6 +622,7 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
         }
         Pending pd;
         bf16x8s VU = {0, 0, 0, 0, 0, 0, 0, 0};  // (V | -U) of the chunk, as B operand
+        bf16x8s VUp = {0, 0, 0, 0, 0, 0, 0, 0};  // SUMMARY: (0 | -U) of the transition
         // element offset of (token lo of the chunk, value channel 16blk + 4g)
         long ylane = K.tok0 + (long)lo * K.TS + 16 * blk + 4 * g;
         // added readouts of a chunk, loaded at the start of its iteration and used
@@ -662,10 +667,42 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
                         gsrc + K.tok0 + (long)min(c * kC + lo, K.Tl - 1) * K.TS + 16 * blk + 4 * g);
                 }
                 const ChunkOps<NH> &o = sm.ops[c % 3];
+                if constexpr (SUMMARY) {
+                    // the offset's and the transition's chunk steps (independent,
+                    // so the two dependent MFMA chains interleave); no readouts
+                    auto advance = [&](Acc32(&Zs)[KB], bf16x8s & VUs) {
+                        bf16x8s ZP[KB / 2];
+#pragma unroll
+                        for (int q = 0; q < KB / 2; ++q) {
+                            ZP[q].lo = to_bf16(Zs[2 * q].v);
+                            ZP[q].hi = to_bf16(Zs[2 * q + 1].v);
+                        }
+                        Acc32 rhs = mfma32(ld_pair(o.mkz, lane), VUs, Acc32::zero());
+#pragma unroll
+                        for (int q = 0; q < KB / 2; ++q)
+                            rhs = mfma32(ld_pair(o.kp[q], lane), ZP[q], rhs);
+                        const Acc16 U = mfma16(ld_a(o.xinv, lane), to_bf16(rhs.v), Acc16::zero());
+                        VUs.hi = to_bf16(U.v);
+#pragma unroll
+                        for (int jb = 0; jb < KB; ++jb) {
+                            Zs[jb] = mfma32(ld_pair(o.kbt[jb], lane), VUs, Zs[jb]);
+                            const float4 gc = *reinterpret_cast<const float4 *>(&o.gc[16 * jb + 4 * g]);
+                            Zs[jb].v[0] *= gc.x;
+                            Zs[jb].v[1] *= gc.y;
+                            Zs[jb].v[2] *= gc.z;
+                            Zs[jb].v[3] *= gc.w;
+                        }
+                    };
+                    VU.lo = ld_a(o.vt[blk], lane);
+                    advance(Z, VU);
+                    advance(Zp, VUp);  // (V | -U) with V = 0
+                    __syncthreads();
+                    continue;
+                }
                 // B operands as 8-wide pairs: (V | -U) and the state pairs; one K =
                 // 32 MFMA per two 16-k products, accumulation chains within that
                 // one opcode
-                VU.lo = p_rows ? bf16x4{0, 0, 0, 0} : ld_a(o.vt[blk], lane);
+                VU.lo = ld_a(o.vt[blk], lane);
                 bf16x8s ZP[KB / 2];  // state pairs (key blocks 2q | 2q+1)
 #pragma unroll
                 for (int q = 0; q < KB / 2; ++q) {
@@ -726,6 +763,13 @@ __attribute__((amdgpu_waves_per_eu(SUMMARY ? 3 : 4))) void chunked_kernel(
             for (int jb = 0; jb < KB; ++jb)
                 *reinterpret_cast<float4 *>(s_fin + srow + 16 * jb + 4 * g) =
                     make_float4(Z[jb][0], Z[jb][1], Z[jb][2], Z[jb][3]);
+        }
+        if (SUMMARY) {
+            float *p_fin = cp.ws_p + sidx * NN;
+#pragma unroll
+            for (int jb = 0; jb < KB; ++jb)
+                *reinterpret_cast<float4 *>(p_fin + srow + 16 * jb + 4 * g) =
+                    make_float4(Zp[jb][0], Zp[jb][1], Zp[jb][2], Zp[jb][3]);
         }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
