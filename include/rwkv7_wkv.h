@@ -32,11 +32,13 @@
  *    index, j = key index.
  *  - N = 64 (the head size the pages' kernels are tuned for) everywhere; N = 128
  *    also for rwkv7_wkv_decode, for both algorithms of rwkv7_wkv_forward (and
- *    rwkv7_wkv_forward_noalloc; RWKV7_ALGO_AUTO picks the chunked one for
- *    bf16), and for the scan algorithm of the bidirectional and fused entry
- *    points (RWKV7_ALGO_AUTO picks the scan there; their chunked algorithm,
- *    the training forward and the backward return RWKV7_ERR_UNSUPPORTED at
- *    128).  B, H >= 1; T >= 0.  All internal offsets are 64-bit.
+ *    rwkv7_wkv_forward_noalloc) and of rwkv7_wkv_forward_train (RWKV7_ALGO_AUTO
+ *    picks the chunked one for bf16), for the token-by-token algorithm of
+ *    rwkv7_wkv_backward (which RWKV7_ALGO_AUTO picks at 128), and for the scan
+ *    algorithm of the bidirectional and fused entry points (RWKV7_ALGO_AUTO
+ *    picks the scan there).  The chunked algorithm of the bidirectional and
+ *    fused entry points and of the backward returns RWKV7_ERR_UNSUPPORTED at
+ *    128.  B, H >= 1; T >= 0.  All internal offsets are 64-bit.
  *  - Every pointer must be 16-byte aligned.
  *  - All validation runs on the host, synchronously, before anything is
  *    enqueued: on any error nothing is launched and nothing is written.
@@ -87,9 +89,9 @@ typedef enum {
                               RWKV-7 "Goose" author response (paperhub) names precision
                               sensitivity of the kernel; with w in (0.99, 1), bf16 rounds
                               most decays to exactly 1.  Forward, training forward,
-                              bidirectional forward, decode, and the chunked backward
-                              (whose dw is then float32 too); the scan backward returns
-                              RWKV7_ERR_UNSUPPORTED, and so does the fused prologue.    */
+                              bidirectional forward, decode, and both backward
+                              algorithms (whose dw is then float32 too); the fused
+                              prologue returns RWKV7_ERR_UNSUPPORTED.                   */
 } rwkv7_dtype;
 
 typedef enum {
@@ -287,21 +289,28 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
  *   ds0    : [B,H,N,N] float32 gradient for s0 (output), or NULL to skip it;
  *            may equal ds_T (in place)
  *   algo   : RWKV7_ALGO_SCAN: token by token in fp32 VALU (states recomputed
- *              from s_ckpt), f32 or bf16, no workspace (RWKV7_DT_BF16_W32 is
- *              refused with RWKV7_ERR_UNSUPPORTED);
- *            RWKV7_ALGO_CHUNKED: bf16 or bf16 with float32 w (f32 refused with
- *              RWKV7_ERR_UNSUPPORTED); the chunked form on bf16 MFMA with
- *              fp32 accumulation: a reverse pass over the 16-token chunks
- *              carries the state cotangent and stores it at every chunk's end
- *              in the workspace, then every chunk's gradients are formed in
- *              parallel from its stored state and cotangent;
- *            RWKV7_ALGO_AUTO: CHUNKED for bf16 and bf16 with float32 w, SCAN
- *              for f32.
+ *              from s_ckpt), every dtype, head size 64 or 128.  At 128 each
+ *              head's value rows are split over four workgroups whose partial
+ *              sums over rows (of dr, dk, dw, dkappa, da) meet in the workspace
+ *              and are added in a fixed order by a second kernel; the sequence
+ *              is cut into slices of whole 16-token intervals whose partial
+ *              sums stay within 256 MiB, walked last to first with the state
+ *              cotangent carried between them;
+ *            RWKV7_ALGO_CHUNKED: bf16 or bf16 with float32 w at head size 64
+ *              (f32, or N = 128, refused with RWKV7_ERR_UNSUPPORTED); the
+ *              chunked form on bf16 MFMA with fp32 accumulation: a reverse
+ *              pass over the 16-token chunks carries the state cotangent and
+ *              stores it at every chunk's end in the workspace, then every
+ *              chunk's gradients are formed in parallel from its stored state
+ *              and cotangent;
+ *            RWKV7_ALGO_AUTO: CHUNKED for bf16 and bf16 with float32 w at head
+ *              size 64, SCAN otherwise.
  *   workspace / workspace_bytes : device scratch of at least
- *            rwkv7_wkv_backward_workspace(...) bytes (8 KiB per head and
- *            chunk for CHUNKED: each chunk's decayed exit cotangent in bf16;
- *            may be NULL when that is 0); it must not overlap any other
- *            argument.
+ *            rwkv7_wkv_backward_workspace(...) bytes (CHUNKED: 8 KiB per head
+ *            and chunk, each chunk's decayed exit cotangent in bf16; SCAN: none
+ *            at head size 64; at 128, 5 x 4 float32 per element of a slice,
+ *            B*H*128*128*4 bytes more when there are several slices; may be
+ *            NULL when that is 0); it must not overlap any other argument.
  * Gradients are rounded once to dt.  The six gradient outputs must not
  * overlap each other or any input.  T == 0: ds0 receives ds_T (or zeros).
  * The chunked form is the derivative of the chunked forward of the RWKV-7

@@ -140,14 +140,12 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
         return RWKV7_ERR_DTYPE;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
-    // the chunked kernel at head size 128 runs the plain forward only
-    const bool chunked128 = N == 128 && !pro && !bidir && !want_ckpt;
+    // the chunked kernel at head size 128 runs the plain and the training forward
+    const bool chunked128 = N == 128 && !pro && !bidir;
     const rwkv7_algo al = resolve_algo(algo, dt, N, chunked128);
     if (al == RWKV7_ALGO_CHUNKED &&
         (dt == RWKV7_DT_F32 || (N != kN && !chunked128) || !kChunkedAvailable))
         return RWKV7_ERR_UNSUPPORTED;
-    // the stored states feed the backward, which is built for head size 64
-    if (want_ckpt && N != kN) return RWKV7_ERR_UNSUPPORTED;
 
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
@@ -159,6 +157,11 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (!mul_ok(st, (size_t)B) || !mul_ok(st, (size_t)H) || !mul_ok(st, (size_t)N * N * 4))
         return RWKV7_ERR_SHAPE;
     if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
+    // one workgroup per head (scan: 4N threads; chunked: 512, 1024 at N = 128):
+    // the grid's extent in threads must fit in 32 bits
+    const size_t head_threads =
+        al == RWKV7_ALGO_CHUNKED ? (N == 128 ? 1024 : 512) : (size_t)4 * N;
+    if ((size_t)B * H * head_threads > 0xffffffffu) return RWKV7_ERR_SHAPE;
     const size_t st1 = st;  // bytes of one state per head
     if (bidir && !mul_ok(st, 2)) return RWKV7_ERR_SHAPE;
     size_t ck = st1;  // bytes of the stored states
@@ -334,24 +337,27 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
                         algo, nullptr, workspace, workspace_bytes, stream);
 }
 
-// AUTO: the chunked backward for bf16 (also with an fp32 decay), else the
-// token-by-token one.
-static rwkv7_algo resolve_bwd_algo(rwkv7_algo algo, rwkv7_dtype dt) {
+// AUTO: the chunked backward for bf16 (also with an fp32 decay) at head size 64,
+// else the token-by-token one.
+static rwkv7_algo resolve_bwd_algo(rwkv7_algo algo, rwkv7_dtype dt, int N) {
     if (algo == RWKV7_ALGO_AUTO)
-        return dt != RWKV7_DT_F32 ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
+        return dt != RWKV7_DT_F32 && N == kN ? RWKV7_ALGO_CHUNKED : RWKV7_ALGO_SCAN;
     return algo;
 }
 
 size_t rwkv7_wkv_backward_workspace(int B, int T, int H, int N, rwkv7_dtype dt,
                                     rwkv7_algo algo) {
-    if (B < 1 || H < 1 || T <= 0 || N != kN) return 0;
+    if (B < 1 || H < 1 || T <= 0 || (N != 64 && N != 128)) return 0;
     if (!valid_dtype(dt)) return 0;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED) return 0;
-    if (resolve_bwd_algo(algo, dt) != RWKV7_ALGO_CHUNKED) return 0;
     size_t n = 1;
     if (!mul_ok(n, (size_t)B) || !mul_ok(n, (size_t)H) ||
-        !mul_ok(n, (size_t)((T + kCkpt - 1) / kCkpt)) || !mul_ok(n, (size_t)kN * kN * 4))
+        !mul_ok(n, (size_t)((T + kCkpt - 1) / kCkpt)) || !mul_ok(n, (size_t)N * N * 4))
         return 0;
+    if ((size_t)B * H > 0x7fffffffu) return 0;
+    if (resolve_bwd_algo(algo, dt, N) != RWKV7_ALGO_CHUNKED)
+        return backward_scan_workspace_bytes(B, T, H, N);
+    if (N != kN) return 0;
     return backward_chunked_workspace_bytes(B, T, H);
 }
 
@@ -364,12 +370,13 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
-    if (N != kN) return RWKV7_ERR_UNSUPPORTED;
+    if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
     if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
-    const rwkv7_algo use = resolve_bwd_algo(algo, dt);
-    // chunked: bf16, or bf16 with an fp32 decay; the token-by-token kernel: f32 or bf16
-    if (use == RWKV7_ALGO_CHUNKED && dt == RWKV7_DT_F32) return RWKV7_ERR_UNSUPPORTED;
-    if (use == RWKV7_ALGO_SCAN && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
+    const rwkv7_algo use = resolve_bwd_algo(algo, dt, N);
+    // chunked: bf16, or bf16 with an fp32 decay, at head size 64; the
+    // token-by-token kernel: every dtype, head size 64 or 128
+    if (use == RWKV7_ALGO_CHUNKED && (dt == RWKV7_DT_F32 || N != kN))
+        return RWKV7_ERR_UNSUPPORTED;
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
     if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)T) || !mul_ok(tok, (size_t)H) ||
@@ -399,10 +406,16 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     if ((s_ckpt && !aligned16(s_ckpt)) || (ds_T && !aligned16(ds_T)) || (ds0 && !aligned16(ds0)))
         return RWKV7_ERR_ALIGN;
     const bool chunked = use == RWKV7_ALGO_CHUNKED && T > 0;
-    const size_t ws_need = chunked ? rwkv7_wkv_backward_workspace(B, T, H, N, dt, use) : 0;
-    if (chunked) {
-        if (ws_need == 0) return RWKV7_ERR_SHAPE;
-        if (!backward_chunked_grid_ok(B, T, H)) return RWKV7_ERR_SHAPE;
+    // the token-by-token kernel at N = 128 keeps partial sums in the workspace
+    const bool scan_ws = !chunked && N == 128 && T > 0;
+    const size_t ws_need =
+        chunked || scan_ws ? rwkv7_wkv_backward_workspace(B, T, H, N, dt, use) : 0;
+    if ((chunked || scan_ws) && ws_need == 0) return RWKV7_ERR_SHAPE;
+    if (chunked && !backward_chunked_grid_ok(B, T, H)) return RWKV7_ERR_SHAPE;
+    // token by token: 256-thread workgroups, one per head at N = 64 and four at
+    // 128; the grid's extent in threads must fit in 32 bits
+    if (!chunked && (size_t)B * H * (N == 128 ? 1024 : 256) > 0xffffffffu) return RWKV7_ERR_SHAPE;
+    if (chunked || scan_ws) {
         if (!workspace || workspace_bytes < ws_need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
     }
@@ -433,7 +446,7 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
         }
         if (ds_T && ds_T != ds0 && overlap(rd, rng(ds_T, st))) return RWKV7_ERR_ALIAS;
     }
-    if (chunked) {  // the workspace is written: it overlaps no argument
+    if (ws_need > 0) {  // the workspace is written: it overlaps no argument
         const Range rw = rng(workspace, ws_need);
         for (int i = 0; i < 7; ++i)
             if (overlap(rw, rng(ins[i], vbytes(i)))) return RWKV7_ERR_ALIAS;
@@ -454,9 +467,10 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     p.s_ckpt = s_ckpt; p.ds_T = ds_T;
     p.dr = dr; p.dw = dw; p.dk = dk; p.dv = dv; p.dkappa = dkappa; p.da = da;
     p.ds0 = ds0;
-    p.B = B; p.T = T; p.H = H;
+    p.B = B; p.T = T; p.H = H; p.N = N;
     p.bf16 = dt != RWKV7_DT_F32;
     p.w32 = dt == RWKV7_DT_BF16_W32;
+    if (scan_ws) p.scan_ws = static_cast<float *>(workspace);
     if (chunked) {
         p.ds_ws = static_cast<uint16_t *>(workspace);
         return launch_backward_chunked(p, hs) == hipSuccess ? RWKV7_OK : RWKV7_ERR_HIP;

@@ -10,7 +10,7 @@
 
 namespace wkv7 {
 
-constexpr int kN = 64;  // head size (the only one supported)
+constexpr int kN = 64;  // head size of the chunked kernels (the scan and decode also take 128)
 extern const bool kChunkedAvailable;
 
 struct EpilogueArgs {
@@ -26,7 +26,7 @@ struct ForwardArgs {
     void *y;                                // [B,T,H,N] in dt
     float *s_out;                           // [B,H,N,N] or nullptr
     int B, T, H;
-    int N;  // head size: 64, or 128 (scan only)
+    int N;  // head size: 64 or 128
     bool bf16;
     bool w32;  // bf16 inputs except w, which is float32
     bool epilogue;
@@ -58,9 +58,11 @@ struct BackwardArgs {
     void *dr, *dw, *dk, *dv, *dkappa, *da;  // [B,T,H,N] in dt
     float *ds0;                             // [B,H,N,N] or nullptr
     int B, T, H;
+    int N;  // head size: 64, or 128 (token-by-token kernel only)
     bool bf16;
     uint16_t *ds_ws;  // chunked: per (b, h, chunk) the bf16 dS_C diag(g_C), 8 KiB in lane order
-    bool w32;      // chunked: w and dw float32 (the other vectors bf16)
+    float *scan_ws;   // token-by-token at N = 128: partial column sums and the carried cotangent
+    bool w32;      // w and dw float32 (the other vectors bf16)
 };
 
 struct DecodeArgs {
@@ -85,7 +87,10 @@ hipError_t launch_scan(const ForwardArgs &p, hipStream_t stream);
 hipError_t launch_chunked(const ForwardArgs &p, hipStream_t stream);
 size_t chunked_workspace_bytes(int B, int T, int H);
 hipError_t launch_decode(const DecodeArgs &p, hipStream_t stream);
+// token-by-token backward (f32, bf16, bf16 with float32 w; head size 64 or 128);
+// at 128 it needs scan_ws of the size below (0 at 64)
 hipError_t launch_backward(const BackwardArgs &p, hipStream_t stream);
+size_t backward_scan_workspace_bytes(int B, int T, int H, int N);
 // chunked backward (bf16, head size 64): reverse chain over the chunks, then
 // every chunk's gradients in parallel; needs ds_ws of the size below
 hipError_t launch_backward_chunked(const BackwardArgs &p, hipStream_t stream);

@@ -397,9 +397,10 @@ def backward(r, w, k, v, kappa, a, dy, s_ckpt, ds_T=None, *, grads=None, ds0=Non
     """rwkv7_wkv_backward.  Returns (dr, dw, dk, dv, dkappa, da, ds0): the gradients of
     sum_t <y_t, dy_t> + <S_T, ds_T> for the inputs of :func:`forward_train`.  ``grads``
     may pass the six output tensors; ``ds0`` may be ``ds_T`` (in place).  ``algo`` is
-    "auto", "scan" or "chunked"; the chunked form's workspace is allocated here unless
-    ``workspace`` (a uint8 device tensor of at least backward_workspace_bytes) is given.
-    With a float32 decay w (other inputs bf16; chunked only), dw is float32 too."""
+    "auto", "scan" or "chunked" (head size 64 only); a workspace, where the algorithm
+    needs one (chunked; scan at head size 128), is allocated here unless ``workspace``
+    (a uint8 device tensor of at least backward_workspace_bytes) is given.  With a
+    float32 decay w (other inputs bf16), dw is float32 too."""
     import torch
 
     B, T, H, N = r.shape

@@ -174,7 +174,9 @@ def bwd(B=2, T=8, H=3, N=64, dt=1, ins=None, dy=fake(6), ck=fake(7), dsT=fake(8)
 
 @fake_addresses
 def test_backward_validation_codes():
-    assert bwd(N=128) == 4
+    assert bwd(N=96) == 4
+    assert bwd(N=128, algo=2) == 4                 # the chunked backward is built for 64
+    assert bwd(N=128) == 7                         # token by token at 128: a workspace
     assert bwd(B=0) == 2 and bwd(H=0) == 2 and bwd(T=-1) == 2
     assert bwd(dt=7) == 3
     assert bwd(dy=None) == 1 and bwd(ck=None) == 1
@@ -194,15 +196,17 @@ def test_backward_validation_codes():
 @fake_addresses
 def test_fp32_decay_dtype_codes():
     # RWKV7_DT_BF16_W32 = 2: accepted by forward (scan and chunked) and decode
-    # validation, and by the chunked backward (dw float32 too); the token-by-token
-    # backward refuses it; w spans 4 bytes per element
+    # validation, and by both backward algorithms (dw float32 too); w spans 4 bytes
+    # per element
     assert fwd(dt=2, algo=1, T=0, s_out=None) == 0
     assert fwd(dt=2, algo=2, T=0, s_out=None) == 0
     assert fwd(dt=3) == 3
     B, T, H = 2, 8, 3
     half_w = B * T * H * 64 * 2
     assert fwd(dt=2, y=fake(1, half_w)) == 6     # y over the float32 w's second half
-    assert bwd(dt=2, algo=1) == 4                 # scan backward: bf16 or f32 only
+    outs = [fake(9 + i) for i in range(6)]
+    outs[2] = fake(10, half_w)                    # dk over the float32 dw's second half
+    assert bwd(dt=2, algo=1, outs=outs) == 6      # token by token: w and dw float32 too
     L = wkv.lib()
     need = L.rwkv7_wkv_backward_workspace(B, T, H, 64, 2, 0)
     assert need == L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 2) > 0
@@ -286,7 +290,12 @@ def test_forward_head_size_128_validation():
     assert L.rwkv7_wkv_forward_fused(*[fake(i) for i in range(5)], ctypes.byref(pro), None,
                                      fake(7), None, 2, 8, 3, 128, 1, 2, None, None, 0,
                                      None) == 4
-    assert fwd_train(N=128) == 4                   # the backward is built for 64
+    # the training forward at 128 (scan and chunked): the stored states span
+    # 2*3*128*128*4 bytes (one interval at T = 8), so y just inside their end overlaps
+    ck_bytes = 2 * 3 * 128 * 128 * 4
+    assert fwd_train(N=128, y=fake(9, ck_bytes - 16)) == 6
+    assert fwd_train(N=128, algo=2, y=fake(9, ck_bytes - 16)) == 6
+    assert fwd_train(N=128, algo=2, ck=fake(9, 8)) == 5
     assert fwd(N=128, T=0, s_out=None) == 0        # scan at 128 passes validation
 
 
@@ -332,7 +341,7 @@ def test_backward_chunked_workspace_codes():
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 0, 0) == 0       # f32 -> scan
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 1) == 0
     assert L.rwkv7_wkv_backward_workspace(B, 0, H, 64, 1, 2) == 0
-    assert L.rwkv7_wkv_backward_workspace(B, T, H, 128, 1, 2) == 0
+    assert L.rwkv7_wkv_backward_workspace(B, T, H, 128, 1, 2) == 0   # chunked: 64 only
     ws = fake(20)
     assert bwd(T=T, algo=2) == 7                              # no workspace
     assert bwd(T=T, algo=2, ws=ws, ws_bytes=need - 16) == 7   # too small
@@ -359,3 +368,55 @@ def test_binding_workspace_dtype_names():
         wkv.lib().rwkv7_wkv_forward_bidir_workspace(1, 65536, 1, 64, 0, 0)
     with pytest.raises(ValueError):
         wkv.backward_workspace_bytes(2, 40, 3, dtype="fp16")
+
+
+@fake_addresses
+def test_backward_head_size_128_workspace_codes():
+    """Token by token at head size 128: four workgroups of 32 value rows per head
+    leave float32 partial column sums (5 sums x 4 parts per element) in the
+    workspace; sequences are cut into slices of whole 16-token intervals so that
+    one slice's sums stay within 256 MiB, and the cotangent of the state is
+    carried between slices (B*H*128*128*4 bytes, only when there are several)."""
+    L = wkv.lib()
+    per_tok = lambda B, H: 5 * 4 * B * H * 128 * 4
+    # one slice: T rounded up to whole intervals
+    assert L.rwkv7_wkv_backward_workspace(2, 40, 3, 128, 1, 1) == per_tok(2, 3) * 48
+    assert L.rwkv7_wkv_backward_workspace(2, 40, 3, 128, 1, 0) == per_tok(2, 3) * 48  # auto
+    assert L.rwkv7_wkv_backward_workspace(2, 40, 3, 128, 0, 0) == per_tok(2, 3) * 48  # f32
+    assert L.rwkv7_wkv_backward_workspace(2, 40, 3, 128, 2, 0) == per_tok(2, 3) * 48  # w32
+    assert L.rwkv7_wkv_backward_workspace(2, 0, 3, 128, 1, 1) == 0
+    # several slices: 96 tokens each at B4 H64, plus the carried cotangent
+    slice_len = (256 << 20) // per_tok(4, 64) // 16 * 16
+    assert slice_len == 96
+    assert L.rwkv7_wkv_backward_workspace(4, 1000, 64, 128, 1, 1) == \
+        per_tok(4, 64) * 96 + 4 * 64 * 128 * 128 * 4
+    # at least one interval per slice, however many heads
+    assert L.rwkv7_wkv_backward_workspace(4096, 100, 64, 128, 1, 1) == \
+        per_tok(4096, 64) * 16 + 4096 * 64 * 128 * 128 * 4
+    need = L.rwkv7_wkv_backward_workspace(2, 40, 3, 128, 1, 1)
+    assert bwd(T=40, N=128, ws=fake(20), ws_bytes=need - 16) == 7
+    assert bwd(T=40, N=128, ws=fake(20, 8), ws_bytes=need) == 5
+    assert bwd(T=40, N=128, ws=fake(12), ws_bytes=need) == 6   # over dk
+    assert bwd(T=40, N=128, ws=fake(7), ws_bytes=need) == 6    # over the stored states
+    assert bwd(T=0, N=128, ds0=None, ck=None) == 0             # nothing to do
+
+
+@fake_addresses
+def test_launch_grid_limits():
+    """Every grid's extent in threads fits in 32 bits: one workgroup per head of
+    4N threads (scan), 512 (chunked at 64) or 1024 (chunked at 128); the
+    token-by-token backward: 256 per head at 64, four of 256 at 128.  Calls just
+    under a limit fail later in validation instead (overlapping fake buffers, a
+    missing workspace)."""
+    assert fwd(B=1 << 24, H=1, algo=1) == 2
+    assert fwd(B=(1 << 24) - 1, H=1, algo=1) != 2
+    assert fwd(B=1 << 23, H=1, algo=2) == 2
+    assert fwd(B=(1 << 23) - 1, H=1, algo=2) != 2
+    assert fwd(B=1 << 23, H=1, N=128, algo=1) == 2
+    assert fwd(B=(1 << 23) - 1, H=1, N=128, algo=1) != 2
+    assert fwd(B=1 << 22, H=1, N=128, algo=2) == 2
+    assert fwd(B=(1 << 22) - 1, H=1, N=128, algo=2) != 2
+    assert bwd(B=1 << 24, H=1, algo=1) == 2
+    assert bwd(B=(1 << 24) - 1, H=1, algo=1) != 2
+    assert bwd(B=1 << 22, H=1, N=128) == 2
+    assert bwd(B=(1 << 22) - 1, H=1, N=128) != 2

@@ -101,9 +101,8 @@ def test_train_forward_fp32_decay_stores_states(wkv):
                                             (1, 1, 17, True), (1, 2, 16, False),
                                             (2, 1, 1, False)])
 def test_backward_fp32_decay_chunked(wkv, B, H, T, with_dsT):
-    """The chunked backward with a float32 decay (dw float32 as well) against the
-    float64 autograd oracle on the same values; the token-by-token backward
-    refuses this dtype."""
+    """Both backward algorithms with a float32 decay (dw float32 as well) against
+    the float64 autograd oracle on the same values."""
     from oracle import grad as og
 
     x = slow(B, T, H, seed=40 + T, s0="normal")
@@ -122,8 +121,12 @@ def test_backward_fp32_decay_chunked(wkv, B, H, T, with_dsT):
     for n, gt in zip(NAMES, g):
         assert_close(to_f64(gt), ref[n], TOL, f"d{n}")
     assert_close(to_f64(ds0), ref["s0"], TOL, "ds0")
-    with pytest.raises(wkv.Rwkv7Error):
-        wkv.backward(*ins, dy, ck, dst, algo="scan")
+    *g, ds0 = wkv.backward(*ins, dy, ck, dst, algo="scan")
+    torch.cuda.synchronize()
+    assert g[1].dtype == torch.float32 and g[0].dtype == torch.bfloat16
+    for n, gt in zip(NAMES, g):
+        assert_close(to_f64(gt), ref[n], TOL, f"scan d{n}")
+    assert_close(to_f64(ds0), ref["s0"], TOL, "scan ds0")
 
 
 def test_backward_fp32_decay_ds0_in_place_and_optional(wkv):
