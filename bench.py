@@ -64,8 +64,8 @@ def parse():
     ap.add_argument("--prefill-shape", default="2.9b", choices=sorted(PREFILL_SHAPES),
                     help="'long' and '0.19b' need --only prefill")
     ap.add_argument("--prefill-head", type=int, default=64, choices=[64, 128],
-                    help="prefill head size; 128 keeps the model width of the 2.9B shape "
-                         "(H = 20) and needs --only prefill")
+                    help="prefill (or training) head size; 128 keeps the model width of the "
+                         "2.9B shape (H = 20) and needs --only prefill or --only train")
     ap.add_argument("--decode-head", type=int, default=64, choices=[64, 128],
                     help="decode head size; 128 keeps the state bytes (H = 20) and needs "
                          "--only decode")
@@ -190,7 +190,8 @@ FP32_VALU_PEAK_TFLOPS = 256 * 4 * 16 * 2 * 2.4e9 / 1e12
 # column sums dr, dk, db, dw, S^T du, the row sums dv, du: 2N^2 each; the
 # cotangent update G diag(w) + du kappa^T: 3N^2) plus one forward recompute of
 # the states (probe 2N^2, update 5N^2)
-BWD_FLOPS_PER_TOKEN_HEAD = (19 + 7) * N * N
+def bwd_flops_per_token_head(n):
+    return (19 + 7) * n * n
 
 
 def workload_name(args, long_shape, do_prefill, do_decode):
@@ -234,14 +235,21 @@ def _slow_decay_f32(px):
 
 def bench_train(args, torch, wkv, synth, dev):
     """Training step on the 2.9B prefill shape (no epilogue): forward with stored
-    states + backward, inputs and cotangents resident before timing."""
-    B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"]
-    px = synth.config_inputs(2)
+    states + backward, inputs and cotangents resident before timing.  At head size
+    128 the model width is kept (H = 20)."""
+    N = args.prefill_head
+    B, T, H = PREFILL["B"], PREFILL["T"], PREFILL["H"] * 64 // N
+    if N == 64:
+        px = synth.config_inputs(2)
+    else:  # the 2.9B-shape recipe at head size 128, without the epilogue
+        c = synth.CONFIGS[2]
+        px = synth.draw(B, T, H, N, seed=2, dtype=c["dtype"], s0=c["s0"],
+                        w_recipe=c["w_recipe"], a_mean=c["a_mean"])
     bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
     ins = [bf(px[n]) for n in NAMES]
     if args.decay_f32:  # the same decays held in float32 (dtype RWKV7_DT_BF16_W32)
         ins[1] = ins[1].float()
-    dy_bits, ds_T = synth.cotangents(B, T, H, seed=102, dtype="bf16")
+    dy_bits, ds_T = synth.cotangents(B, T, H, N, seed=102, dtype="bf16")
     dy, dst = bf(dy_bits), torch.from_numpy(ds_T).to(dev)
     ws_bytes = wkv.forward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.prefill_algo)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
@@ -252,7 +260,7 @@ def bench_train(args, torch, wkv, synth, dev):
     ds0 = torch.empty_like(s_out)
     bws = wkv.backward_workspace_bytes(B, T, H, N, dtype="bf16", algo=args.bwd_algo)
     bwork = torch.empty(max(bws, 16), dtype=torch.uint8, device=dev)
-    chunked_bwd = bws > 0
+    chunked_bwd = N == 64 and bws > 0
     stream = torch.cuda.current_stream()
 
     def fwd():
@@ -292,7 +300,7 @@ def bench_train(args, torch, wkv, synth, dev):
     bwd_ms = float(np.median([e[2].elapsed_time(e[3]) for e in ev]))
 
     work = B * T * H
-    bwd_flops = work * BWD_FLOPS_PER_TOKEN_HEAD
+    bwd_flops = work * bwd_flops_per_token_head(N)
     tf = bwd_flops / (bwd_ms / 1e3) / 1e12
     nck = (T + 15) // 16
     wx = 2 if args.decay_f32 else 0  # extra bytes per decay element (w in, dw out)
@@ -309,7 +317,9 @@ def bench_train(args, torch, wkv, synth, dev):
         "data": "synthetic (seeded; recipes of the pages' parameterisations)",
         "config": {"workload": ("2.9B-shape WKV7 training step: forward with fp32 states stored "
                                 "every 16 tokens, then backward to r, w, k, v, kappa, a, S0; "
-                                "B8 T4096 H40 N64, no epilogue"),
+                                + ("B8 T4096 H40 N64, no epilogue" if N == 64 else
+                                   "2.9B width at head size 128: B8 T4096 H20 N128, "
+                                   "no epilogue")),
                    "B": B, "T": T, "H": H, "N": N, "forward_algo": args.prefill_algo,
                    "backward_algo": "chunked" if chunked_bwd else "scan",
                    "decay_dtype": "f32" if args.decay_f32 else "bf16",
@@ -324,10 +334,14 @@ def bench_train(args, torch, wkv, synth, dev):
                       "workspace_bytes": bws,
                       "valu_tflops_equivalent": tf}
                      if chunked_bwd else
-                     {"kernel": "wkv7 backward_kernel<bf16>", "bound": "alu",
+                     {"kernel": ("wkv7 backward_kernel<bf16>" if N == 64 else
+                                 "wkv7 backward_kernel<bf16, 128> + partial-sum combine"),
+                      "bound": "alu",
                       "achieved": tf, "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                       "frac": tf / FP32_VALU_PEAK_TFLOPS,
-                      "traffic": read_traffic("backward_kernel_traffic_b8_t4096_h40.txt", src),
+                      "traffic": (read_traffic("backward_kernel_traffic_b8_t4096_h40.txt", src)
+                                  if N == 64 else None),
+                      "workspace_bytes": bws,
                       "flops_per_launch": bwd_flops, "avg_launch_us": bwd_ms * 1e3,
                       "hbm_GBps_algorithmic": bwd_bytes / (bwd_ms / 1e3) / 1e9}),
         "forward_train": {"ms": fwd_ms, "bytes_per_launch": fwd_bytes,
@@ -337,7 +351,7 @@ def bench_train(args, torch, wkv, synth, dev):
     if not args.no_cpu_baseline:
         from oracle import grad as og
 
-        b_idx, h_idx = [0, 7], [3, 39]
+        b_idx, h_idx = [0, 7], [3, H - 1]
         dy64 = synth.bf16_bits_to_f32(dy_bits).astype(np.float64)
         t0 = time.perf_counter()
         ref = og.backward(*(px.as_f64(n) for n in NAMES), dy64, s0=None,
@@ -349,7 +363,7 @@ def bench_train(args, torch, wkv, synth, dev):
             got = got[:, :, h_idx] if n != "s0" else got[:, h_idx]
             errs["d" + n] = float(np.abs(got - ref[n]).max() / np.abs(ref[n]).max())
         out["parity_sampled"] = dict(errs, bound=2e-2, checked=(
-            "every gradient element of (b, h) in {0, 7} x {3, 39}, all 4096 tokens"))
+            f"every gradient element of (b, h) in {{0, 7}} x {{3, {H - 1}}}, all 4096 tokens"))
         cpu_work = len(b_idx) * len(h_idx) * T
         out["cpu_baseline"] = {
             "value": cpu_work / cpu_s, "unit": "token*heads/s",
@@ -381,10 +395,11 @@ def main():
         print("bench.py: --prefill-shape long / 0.19b and --bidir are prefill-only "
               "measurements (--only prefill)", file=sys.stderr)
         sys.exit(2)
-    if args.prefill_head != 64 and (args.only != "prefill" or args.prefill_shape != "2.9b"
-                                    or args.fused or args.bidir or args.decay_f32):
-        print("bench.py: --prefill-head 128 times the 2.9B-width prefill alone (--only prefill)",
-              file=sys.stderr)
+    if args.prefill_head != 64 and (args.only not in ("prefill", "train")
+                                    or args.prefill_shape != "2.9b" or args.fused or args.bidir
+                                    or (args.decay_f32 and args.only == "prefill")):
+        print("bench.py: --prefill-head 128 times the 2.9B-width prefill alone (--only prefill) "
+              "or the training step at that width (--only train)", file=sys.stderr)
         sys.exit(2)
     if args.decay_f32 and args.only not in ("prefill", "train"):
         print("bench.py: --decay-f32 needs --only prefill (long context) or --only train",

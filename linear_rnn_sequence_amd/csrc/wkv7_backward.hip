@@ -65,12 +65,18 @@ struct BwdGeo {
     static_assert(P * RB == N && SLOTS * kBwdThreads == kCkpt * LR, "geometry");
 };
 
+// LDS.  At N = 128 (partial sums) the column sums leave after every token
+// instead of every block of kBlk tokens, a is not staged (the second kernel
+// forms dkappa and da) and v, dy only for the band's rows: 65 KB, so two
+// workgroups share a CU.
 template <int N>
 struct __align__(16) BwdSmem {
-    float r[kCkpt][N], w[kCkpt][N], k[kCkpt][N], v[kCkpt][N];
-    float kap[kCkpt][N], a[kCkpt][N], b[kCkpt][N], dy[kCkpt][N];
-    float col[2][4][kBlk][kNCol][N];     // [buffer][wave][token][sum][column]
-    float dv[2][kBlk][BwdGeo<N>::RB];    // [buffer][token][row of the workgroup]
+    using Geo = BwdGeo<N>;
+    static constexpr int CT = Geo::P > 1 ? 1 : kBlk;  // tokens per write-out
+    float r[kCkpt][N], w[kCkpt][N], k[kCkpt][N], v[kCkpt][Geo::RB];
+    float kap[kCkpt][N], a[kCkpt][Geo::P > 1 ? 4 : N], b[kCkpt][N], dy[kCkpt][Geo::RB];
+    float col[2][4][CT][kNCol][N];  // [buffer][wave][token][sum][column]
+    float dv[2][CT][Geo::RB];       // [buffer][token][row of the band]
 };
 
 // One slice of the sequence: intervals [c_begin, c_end) of kCkpt tokens.
@@ -94,8 +100,16 @@ __device__ __forceinline__ float row_sum(float x) {
     return x;
 }
 
+// At N = 128 with bf16 vectors two workgroups share a CU (LDS 65 KB each, at
+// most 256 registers per lane; the compiler spills a few): measured on the
+// 2.9B width (B8 T4096 H20), 15.4 ms against 21.1 ms with one.  The float32
+// variant would spill about 90 registers and keeps one.
+template <class IO, int N>
+constexpr int kBwdWavesPerEU = (N == 128 && std::is_same<IO, Bf16In>::value) ? 2 : 1;
+
 template <class IO, bool W32, int N>
-__global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, BwdSlice sl) {
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(
+    kBwdWavesPerEU<IO, N>))) void backward_kernel(BackwardArgs p, BwdSlice sl) {
     using Geo = BwdGeo<N>;
     using L = RawLoad<IO>;
     using LW = std::conditional_t<W32, RawLoad<F32In>, L>;  // the decay's loads
@@ -168,7 +182,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, B
     auto step = [&](float (&S)[4][4], int t, float (&u)[4]) {
         const float4 kp = lds4(&sm.kap[t][j0]), w4 = lds4(&sm.w[t][j0]);
         const float4 b4 = lds4(&sm.b[t][j0]), k4 = lds4(&sm.k[t][j0]);
-        const float4 v4 = lds4(&sm.v[t][i0]);
+        const float4 v4 = lds4(&sm.v[t][il0]);
         const float wq[4] = {w4.x, w4.y, w4.z, w4.w}, bq[4] = {b4.x, b4.y, b4.z, b4.w};
         const float kq[4] = {k4.x, k4.y, k4.z, k4.w}, ve[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
@@ -201,14 +215,17 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, B
             const float4 b4 =
                 make_float4(a4.x * kp4.x, a4.y * kp4.y, a4.z * kp4.z, a4.w * kp4.w);
             const int st = s_t[q], sc = 4 * s_q[q];
+            const int sv = sc - Geo::RB * part;  // value channel within the band
             *reinterpret_cast<float4 *>(&sm.r[st][sc]) = r4;
             *reinterpret_cast<float4 *>(&sm.w[st][sc]) = w4;
             *reinterpret_cast<float4 *>(&sm.k[st][sc]) = k4;
-            *reinterpret_cast<float4 *>(&sm.v[st][sc]) = v4;
             *reinterpret_cast<float4 *>(&sm.kap[st][sc]) = kp4;
-            *reinterpret_cast<float4 *>(&sm.a[st][sc]) = a4;
+            if constexpr (!kPart) *reinterpret_cast<float4 *>(&sm.a[st][sc]) = a4;
             *reinterpret_cast<float4 *>(&sm.b[st][sc]) = b4;
-            *reinterpret_cast<float4 *>(&sm.dy[st][sc]) = dy4;
+            if (!kPart || (unsigned)sv < (unsigned)Geo::RB) {
+                *reinterpret_cast<float4 *>(&sm.v[st][sv]) = v4;
+                *reinterpret_cast<float4 *>(&sm.dy[st][sv]) = dy4;
+            }
         }
         __syncthreads();
         if (c > sl.c_begin) {
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, B
                 const float4 r4t = lds4(&sm.r[t][j0]), w4t = lds4(&sm.w[t][j0]);
                 const float4 k4t = lds4(&sm.k[t][j0]), kp4t = lds4(&sm.kap[t][j0]);
                 const float4 b4t = lds4(&sm.b[t][j0]);
-                const float4 v4t = lds4(&sm.v[t][i0]), dy4t = lds4(&sm.dy[t][i0]);
+                const float4 v4t = lds4(&sm.v[t][il0]), dy4t = lds4(&sm.dy[t][il0]);
                 const float rq[4] = {r4t.x, r4t.y, r4t.z, r4t.w};
                 const float wq[4] = {w4t.x, w4t.y, w4t.z, w4t.w};
                 const float kq[4] = {k4t.x, k4t.y, k4t.z, k4t.w};
@@ -319,28 +336,51 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, B
 #pragma unroll
                     for (int q = 0; q < 4; ++q) G[e][q] = G[e][q] * wq[q] + du[e] * kpq[q];
                 // column sums over the wave's rows
+                const int ct = kPart ? 0 : tt;  // token slot of the write-out buffer
 #pragma unroll
                 for (int x = 0; x < kNCol; ++x) {
                     if constexpr (N == 64) {
                         // four row groups, four columns per register: lanes of row
                         // group rg end with column j0 + packed_col(rg)
                         const float s4 = sum_rows4_packed(cs[x][0], cs[x][1], cs[x][2], cs[x][3]);
-                        sm.col[buf][wave][tt][x][j0 + packed_col(rg)] = s4;
+                        sm.col[buf][wave][ct][x][j0 + packed_col(rg)] = s4;
                     } else {
                         // two row groups (lane bit 5): rg 0 ends with columns j0 and
                         // j0 + 2, rg 1 with j0 + 1 and j0 + 3
-                        sm.col[buf][wave][tt][x][j0 + rg] = swap32_add(cs[x][0], cs[x][1]);
-                        sm.col[buf][wave][tt][x][j0 + 2 + rg] = swap32_add(cs[x][2], cs[x][3]);
+                        sm.col[buf][wave][ct][x][j0 + rg] = swap32_add(cs[x][0], cs[x][1]);
+                        sm.col[buf][wave][ct][x][j0 + 2 + rg] = swap32_add(cs[x][2], cs[x][3]);
                     }
                 }
                 if (cg == 0)
-                    *reinterpret_cast<float4 *>(&sm.dv[buf][tt][il0]) =
+                    *reinterpret_cast<float4 *>(&sm.dv[buf][ct][il0]) =
                         make_float4(dv[0], dv[1], dv[2], dv[3]);
+                if constexpr (kPart) {
+                    // ---- this token's partial column sums (float32) and dv ----
+                    __syncthreads();
+                    const int tg = tb + t;
+                    if (tg < T) {
+                        const long plane = (long)p.B * sl.L * HN;  // elements per (sum, part)
+                        const long pbase =
+                            ((long)b * sl.L + (tg - sl.c_begin * kCkpt)) * HN + (long)h * N;
+                        for (int e = tid; e < kNCol * N; e += kBwdThreads) {
+                            const int x = e / N, j = e % N;
+                            sl.part[(long)(x * Geo::P + part) * plane + pbase + j] =
+                                (sm.col[buf][0][0][x][j] + sm.col[buf][1][0][x][j]) +
+                                (sm.col[buf][2][0][x][j] + sm.col[buf][3][0][x][j]);
+                        }
+                        // dv is a row sum: complete for the band's rows
+                        if (tid < Geo::RB)
+                            IO::store1(static_cast<E *>(p.dv) + tok0 + (long)tg * HN +
+                                           Geo::RB * part + tid,
+                                       sm.dv[buf][0][tid]);
+                    }
+                    buf ^= 1;
+                }
             }
-            __syncthreads();
 
             // ---- write out the block's gradients: thread = (token, channel) ----
             if constexpr (!kPart) {
+                __syncthreads();
                 const int tt = tid >> 6, j = tid & 63;
                 const int t = tb + t0 + tt;
                 if (t < T) {
@@ -358,35 +398,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BackwardArgs p, B
                     IO::store1(static_cast<E *>(p.da) + o, kj * s[2]);
                     IO::store1(static_cast<E *>(p.dv) + o, sm.dv[buf][tt][j]);
                 }
-            } else {
-                // partial column sums of this band of rows, float32
-                const long plane = (long)p.B * sl.L * HN;  // elements per (sum, part)
-#pragma unroll
-                for (int q = 0; q < kBlk * N / kBwdThreads; ++q) {
-                    const int e = tid + kBwdThreads * q;
-                    const int tt = e / N, j = e % N;
-                    const int t = tb + t0 + tt;
-                    if (t < T) {
-                        const long po = ((long)b * sl.L + (t - sl.c_begin * kCkpt)) * HN +
-                                        (long)h * N + j;
-#pragma unroll
-                        for (int x = 0; x < kNCol; ++x)
-                            sl.part[(long)(x * Geo::P + part) * plane + po] =
-                                (sm.col[buf][0][tt][x][j] + sm.col[buf][1][tt][x][j]) +
-                                (sm.col[buf][2][tt][x][j] + sm.col[buf][3][tt][x][j]);
-                    }
-                }
-                // dv is a row sum: complete for the band's rows
-                if (tid < kBlk * Geo::RB) {
-                    const int tt = tid / Geo::RB, il = tid % Geo::RB;
-                    const int t = tb + t0 + tt;
-                    if (t < T)
-                        IO::store1(static_cast<E *>(p.dv) + tok0 + (long)t * HN +
-                                       Geo::RB * part + il,
-                                   sm.dv[buf][tt][il]);
-                }
+                buf ^= 1;
             }
-            buf ^= 1;
         }
     }
 
