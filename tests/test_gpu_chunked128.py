@@ -138,10 +138,16 @@ def test_chunked128_exact_transitions(wkv):
 
 
 def test_chunked128_rejected_where_not_built(wkv):
+    """At head size 128 the chunked algorithm serves the plain and the training
+    forward; the bidirectional forward and the backward refuse it."""
     x = synth.draw(1, 20, 1, N, seed=1360, dtype="bf16")
     d = to_device(x, torch)
     ins = [d[n] for n in NAMES]
-    with pytest.raises(wkv.Rwkv7Error):
-        wkv.forward_train(*ins, algo="chunked")
+    y, s, ck = wkv.forward_train(*ins, algo="chunked")
+    y0, s0 = wkv.forward(*ins, algo="chunked")
+    torch.cuda.synchronize()
+    assert torch.equal(y, y0) and torch.equal(s, s0)
     with pytest.raises(wkv.Rwkv7Error):
         wkv.forward_bidir(*ins, algo="chunked")
+    with pytest.raises(wkv.Rwkv7Error):
+        wkv.backward(*ins, ins[0], ck, None, algo="chunked")

@@ -71,5 +71,5 @@ def test_n128_refusals(wkv):
     ins = [d[n] for n in NAMES]
     with pytest.raises(wkv.Rwkv7Error):  # the chunked kernel is bf16 only
         wkv.forward(*(t.float() for t in ins), algo="chunked")
-    with pytest.raises(wkv.Rwkv7Error):
-        wkv.forward_train(*ins)
+    with pytest.raises(wkv.Rwkv7Error):  # the training forward too
+        wkv.forward_train(*(t.float() for t in ins), algo="chunked")
