@@ -38,7 +38,8 @@
  *    algorithm of the bidirectional and fused entry points (RWKV7_ALGO_AUTO
  *    picks the scan there).  The chunked algorithm of the bidirectional and
  *    fused entry points and of the backward returns RWKV7_ERR_UNSUPPORTED at
- *    128.  B, H >= 1; T >= 0.  All internal offsets are 64-bit.
+ *    128.  B, H >= 1; T >= 0; H * N < 2^31 (RWKV7_ERR_SHAPE otherwise).  All
+ *    offsets into tensors are 64-bit.
  *  - Every pointer must be 16-byte aligned.
  *  - All validation runs on the host, synchronously, before anything is
  *    enqueued: on any error nothing is launched and nothing is written.

@@ -11,9 +11,11 @@
 namespace wkv7 {
 namespace {
 
+// grid-stride, so that any state size fits a grid of at most 2^16 workgroups
 __global__ void state_copy_kernel(const float4 *src, float4 *dst, size_t n4) {
-    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n4) dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride)
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 struct Range {
@@ -55,7 +57,8 @@ EpilogueArgs to_epi(const rwkv7_epilogue *epi) {
 
 hipError_t launch_state_copy(const float *s0, float *s_out, size_t count, hipStream_t stream) {
     const size_t n4 = count / 4;
-    const unsigned blocks = (unsigned)((n4 + 255) / 256);
+    const size_t need = (n4 + 255) / 256;
+    const unsigned blocks = (unsigned)(need < 65536 ? need : 65536);
     if (blocks == 0) return hipSuccess;
     hipLaunchKernelGGL(state_copy_kernel, dim3(blocks), dim3(256), 0, stream,
                        reinterpret_cast<const float4 *>(s0), reinterpret_cast<float4 *>(s_out),
@@ -86,6 +89,10 @@ const char *rwkv7_status_str(rwkv7_status s) {
     }
     return "unknown status";
 }
+
+// The kernels index a head's channels (h * N + i, the per-channel epilogue and
+// prologue parameters) in 32 bits: H * N must stay below 2^31.
+static bool heads_fit(int H, int N) { return (long long)H * N <= 0x7fffffffLL; }
 
 static bool valid_dtype(rwkv7_dtype dt) {
     return dt == RWKV7_DT_F32 || dt == RWKV7_DT_BF16 || dt == RWKV7_DT_BF16_W32;
@@ -139,7 +146,7 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
+    if (B < 1 || H < 1 || T < 0 || !heads_fit(H, N)) return RWKV7_ERR_SHAPE;
     // the chunked kernel at head size 128 runs the plain and the training forward
     const bool chunked128 = N == 128 && !pro && !bidir;
     const rwkv7_algo al = resolve_algo(algo, dt, N, chunked128);
@@ -158,10 +165,10 @@ static rwkv7_status forward_impl(const void *r, const void *w, const void *k, co
         return RWKV7_ERR_SHAPE;
     if ((size_t)B * H > 0x7fffffffu) return RWKV7_ERR_SHAPE;
     // one workgroup per head (scan: 4N threads; chunked: 512, 1024 at N = 128):
-    // the grid's extent in threads must fit in 32 bits
+    // the grid's extent in threads must fit in 32 bits (T == 0 runs only the state copy)
     const size_t head_threads =
         al == RWKV7_ALGO_CHUNKED ? (N == 128 ? 1024 : 512) : (size_t)4 * N;
-    if ((size_t)B * H * head_threads > 0xffffffffu) return RWKV7_ERR_SHAPE;
+    if (T > 0 && (size_t)B * H * head_threads > 0xffffffffu) return RWKV7_ERR_SHAPE;
     const size_t st1 = st;  // bytes of one state per head
     if (bidir && !mul_ok(st, 2)) return RWKV7_ERR_SHAPE;
     size_t ck = st1;  // bytes of the stored states
@@ -371,7 +378,7 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     if (algo != RWKV7_ALGO_AUTO && algo != RWKV7_ALGO_SCAN && algo != RWKV7_ALGO_CHUNKED)
         return RWKV7_ERR_DTYPE;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1 || T < 0) return RWKV7_ERR_SHAPE;
+    if (B < 1 || H < 1 || T < 0 || !heads_fit(H, N)) return RWKV7_ERR_SHAPE;
     const rwkv7_algo use = resolve_bwd_algo(algo, dt, N);
     // chunked: bf16, or bf16 with an fp32 decay, at head size 64; the
     // token-by-token kernel: every dtype, head size 64 or 128
@@ -413,8 +420,9 @@ rwkv7_status rwkv7_wkv_backward(const void *r, const void *w, const void *k, con
     if ((chunked || scan_ws) && ws_need == 0) return RWKV7_ERR_SHAPE;
     if (chunked && !backward_chunked_grid_ok(B, T, H)) return RWKV7_ERR_SHAPE;
     // token by token: 256-thread workgroups, one per head at N = 64 and four at
-    // 128; the grid's extent in threads must fit in 32 bits
-    if (!chunked && (size_t)B * H * (N == 128 ? 1024 : 256) > 0xffffffffu) return RWKV7_ERR_SHAPE;
+    // 128; the grid's extent in threads must fit in 32 bits (T == 0: the state copy only)
+    if (!chunked && T > 0 && (size_t)B * H * (N == 128 ? 1024 : 256) > 0xffffffffu)
+        return RWKV7_ERR_SHAPE;
     if (chunked || scan_ws) {
         if (!workspace || workspace_bytes < ws_need) return RWKV7_ERR_WORKSPACE;
         if (!aligned16(workspace)) return RWKV7_ERR_ALIGN;
@@ -489,7 +497,7 @@ static rwkv7_status decode_impl(const void *r, const void *w, const void *k, con
     if (!valid_dtype(dt)) return RWKV7_ERR_DTYPE;
     if (pro && dt == RWKV7_DT_BF16_W32) return RWKV7_ERR_UNSUPPORTED;
     if (N != 64 && N != 128) return RWKV7_ERR_UNSUPPORTED;
-    if (B < 1 || H < 1) return RWKV7_ERR_SHAPE;
+    if (B < 1 || H < 1 || !heads_fit(H, N)) return RWKV7_ERR_SHAPE;
     const size_t esz = dt == RWKV7_DT_F32 ? 4 : 2;
     size_t tok = 1, st = 1;
     if (!mul_ok(tok, (size_t)B) || !mul_ok(tok, (size_t)H) || !mul_ok(tok, (size_t)N * 4))

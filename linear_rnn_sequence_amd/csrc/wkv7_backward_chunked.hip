@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     // per DPP row g, and lane lo of the row keys (values) 4lo .. 4lo+3, so each
     // load instruction reads four whole 128-byte token rows.
     const int pb = wave - 4, t_in = 4 * pb + (lane >> 4), k0 = 4 * lo;
-    const int TSH = p.H * kN;  // elements from one token to the next
+    const long TSH = (long)p.H * kN;  // elements from one token to the next
     // Issues the same loads on every path: the index is clamped to the last one
     // and the token to T - 1, which keeps every address inside the tensors;
     // prep() replaces the values of tokens past T.
@@ -290,7 +290,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
         const int c = nch - 1 - min(i, nch - 1);
         // the chunk's first token, key 0 (uniform), and the lane's offset from it
         const long base = ((b * p.T + (long)c * kC) * p.H + h) * kN;
-        const unsigned o = (unsigned)(min(t_in, p.T - 1 - c * kC) * TSH) + k0;
+        const long o = (long)min(t_in, p.T - 1 - c * kC) * TSH + k0;
         x.r = *reinterpret_cast<const uint2 *>(static_cast<const uint16_t *>(p.r) + base + o);
         if constexpr (W32)
             x.w = *reinterpret_cast<const float4 *>(static_cast<const float *>(p.w) + base + o);

@@ -330,3 +330,37 @@ def decode_step_inputs_device(torch, device, *, B, H, N, seed, count=1):
     bf = torch.bfloat16
     return {n: x.to(bf).contiguous() for n, x in
             dict(r=r, w=w, k=k, v=v, kappa=kappa, a=a).items()}
+
+
+def sequence_inputs_device(torch, device, *, B, T, H, N, seed, s0_std=None, rows=4096):
+    """Per-token inputs [B, T, H, N] bf16 drawn on ``device`` (for sizes whose host
+    copies would be impractical), with the recipe of the tiny forward workload:
+    r, k, v ~ N(0,1); a = sigmoid(N(0,1)); w = exp(-sigmoid(N(0,1)+0.5)/sqrt(e));
+    kappa = L2-normalised N(0,1) per (b, t, h).  Drawn ``rows`` sequences at a
+    time (bounded float32 temporaries), names in the order r, w, k, v, kappa, a
+    per block.  With ``s0_std``, also "s0" [B, H, N, N] float32 ~ N(0, s0_std)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    bf = torch.bfloat16
+    out = {n: torch.empty((B, T, H, N), dtype=bf, device=device)
+           for n in ("r", "w", "k", "v", "kappa", "a")}
+    for b0 in range(0, B, rows):
+        b1 = min(B, b0 + rows)
+        shp = (b1 - b0, T, H, N)
+
+        def nrm():
+            return torch.randn(shp, generator=g, device=device, dtype=torch.float32)
+
+        out["r"][b0:b1] = nrm().to(bf)
+        out["w"][b0:b1] = torch.exp(-torch.sigmoid(nrm() + 0.5) * _INV_SQRT_E).to(bf)
+        out["k"][b0:b1] = nrm().to(bf)
+        out["v"][b0:b1] = nrm().to(bf)
+        kz = nrm()
+        out["kappa"][b0:b1] = (kz / torch.clamp(torch.linalg.vector_norm(kz, dim=-1, keepdim=True),
+                                                min=1e-12)).to(bf)
+        out["a"][b0:b1] = torch.sigmoid(nrm()).to(bf)
+    if s0_std is not None:
+        s0 = torch.empty((B, H, N, N), dtype=torch.float32, device=device)
+        s0.normal_(0.0, s0_std, generator=g)
+        out["s0"] = s0
+    return out

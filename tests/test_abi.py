@@ -407,7 +407,7 @@ def test_launch_grid_limits():
     4N threads (scan), 512 (chunked at 64) or 1024 (chunked at 128); the
     token-by-token backward: 256 per head at 64, four of 256 at 128.  Calls just
     under a limit fail later in validation instead (overlapping fake buffers, a
-    missing workspace)."""
+    missing workspace).  Head channels are indexed in 32 bits: H * N < 2^31."""
     assert fwd(B=1 << 24, H=1, algo=1) == 2
     assert fwd(B=(1 << 24) - 1, H=1, algo=1) != 2
     assert fwd(B=1 << 23, H=1, algo=2) == 2
@@ -420,3 +420,10 @@ def test_launch_grid_limits():
     assert bwd(B=(1 << 24) - 1, H=1, algo=1) != 2
     assert bwd(B=1 << 22, H=1, N=128) == 2
     assert bwd(B=(1 << 22) - 1, H=1, N=128) != 2
+    # T == 0 launches no recurrence kernel: only H * N < 2^31 applies then
+    assert fwd(B=1 << 24, H=1, T=0, s_out=None) == 0
+    assert fwd(B=1, H=1 << 25, T=0, s_out=None) == 2
+    assert fwd(B=1, H=(1 << 25) - 1, T=0, s_out=None) == 0
+    assert fwd(B=1, H=1 << 24, N=128, T=0, s_out=None) == 2
+    assert bwd(B=1 << 24, H=1, T=0, ds0=None, ck=None) == 0
+    assert bwd(B=1, H=1 << 25, T=0, ds0=None, ck=None) == 2
