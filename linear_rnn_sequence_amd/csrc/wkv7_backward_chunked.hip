@@ -40,6 +40,9 @@
 //    entry state and dSh a workgroup recomputes its operands and
 //    forms every gradient; each workgroup takes 8 consecutive chunks of one
 //    head and loads the next chunk's inputs while it works on the current one.
+//    Its four waves each form a share of the chunk's C x C matrices (X, M_kk,
+//    M_kr, M_br, then the cotangent matrices dM) and pass them to the others
+//    through LDS as bf16 MFMA operands.
 // A ragged last chunk is padded with neutral tokens (w = 1, all else 0), which
 // leave every product and the decay totals unchanged.
 //
@@ -107,6 +110,22 @@ __device__ __forceinline__ Acc16 mask(Acc16 d, int lane) {
     return d;
 }
 
+
+// mask<kLower, strict>, the strictness a run-time (wave-uniform) value
+template <bool kLower>
+__device__ __forceinline__ Acc16 mask_rt(Acc16 d, int lane, bool strict) {
+    const int lo = lane & 15, row = 4 * (lane >> 4), ofs = strict ? 0 : 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int r = row + e;
+        const bool keep = kLower ? (lo < r + ofs) : (r < lo + ofs);
+        d.v[e] = keep ? d[e] : 0.f;
+    }
+    return d;
+}
+
+// bf16 operand with every element negated (exact: a sign flip)
+__device__ __forceinline__ bf16x4 negb(bf16x4 x) { return x ^ (short)0x8000; }
 
 // Element offset of token t of (b, h) in a [B,T,H,64] tensor.
 __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, long t) {
@@ -626,30 +645,52 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             __syncthreads();
         }
 
-        // ---- chunk matrices (every wave forms its own copy)
-        Acc16 dmkk = z4(), dmkkt = z4(), dn = z4(), dnt = z4(), dmkr = z4(), dmbr = z4();
+        // ---- chunk matrices, one share per wave, left in LDS as the bf16 A
+        // operands every wave reads (wave 0: X = (I + N)^-1 and X^T from N = M_bk;
+        // wave 1: M_kk, M_kk^T; wave 2: M_kr; wave 3: M_br).  They sit in the
+        // state tiles' LDS, written only later in phase 2, hence the second
+        // barrier.  (Every wave forming all of them, as it once did, was 45% of
+        // the kernel's matrix-core products; a separate 4 KiB region would leave
+        // two workgroups per CU instead of three and was slower.)
+        bf16x4 (*fr)[64] = reinterpret_cast<bf16x4 (*)[64]>(&L.u);
+        if (wave == 0) {
+            Acc16 dn = z4(), dnt = z4();
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
-            const bf16x4 bma = frag(L.bm, 0, 16 * kb, lane), rpa = frag(L.rp, 0, 16 * kb, lane);
-            dmkk = mma(kpa, kma, dmkk);
-            dmkkt = mma(kma, kpa, dmkkt);
-            dn = mma(kpa, bma, dn);
-            dnt = mma(bma, kpa, dnt);
-            dmkr = mma(rpa, kma, dmkr);
-            dmbr = mma(rpa, bma, dmbr);
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), bma = frag(L.bm, 0, 16 * kb, lane);
+                dn = mma(kpa, bma, dn);
+                dnt = mma(bma, kpa, dnt);
+            }
+            dn = mask<true, true>(dn, lane);
+            dnt = mask<false, true>(dnt, lane);
+            f32x4 dx, dxt;  // D(X) = A operand of X^T, D(X^T) = A operand of X
+            tri_inverse(dn.v, dnt.v, lane, dx, dxt);
+            fr[0][lane] = bf4(dx);
+            fr[1][lane] = bf4(dxt);
+        } else if (wave == 1) {
+            Acc16 m = z4(), mt = z4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x4 kpa = frag(L.kp, 0, 16 * kb, lane), kma = frag(L.km, 0, 16 * kb, lane);
+                m = mma(kpa, kma, m);
+                mt = mma(kma, kpa, mt);
+            }
+            fr[2][lane] = bf4(mask<true, true>(m, lane));
+            fr[3][lane] = bf4(mask<false, true>(mt, lane));
+        } else {
+            const short(*rhs)[kSK] = wave == 2 ? L.km : L.bm;
+            Acc16 m = z4();
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb)
+                m = mma(frag(L.rp, 0, 16 * kb, lane), frag(rhs, 0, 16 * kb, lane), m);
+            fr[2 + wave][lane] = bf4(mask<true, false>(m, lane));
         }
-        dmkk = mask<true, true>(dmkk, lane);
-        dmkkt = mask<false, true>(dmkkt, lane);
-        dn = mask<true, true>(dn, lane);
-        dnt = mask<false, true>(dnt, lane);
-        dmkr = mask<true, false>(dmkr, lane);
-        dmbr = mask<true, false>(dmbr, lane);
-        f32x4 dx, dxt;  // D(X) = A operand of X^T, D(X^T) = A operand of X
-        tri_inverse(dn.v, dnt.v, lane, dx, dxt);
-        // the next chunk's inputs, in flight during the rest of this chunk (issued
-        // after the inverse, whose temporaries would otherwise sit beside them)
+        // the next chunk's inputs, in flight during the rest of this chunk
         if (c + 1 < c_end) load_chunk(c + 1);
+        __syncthreads();
+        const bf16x4 fx = fr[0][lane], fxt = fr[1][lane], fmkk = fr[2][lane];
+        const bf16x4 fmkkt = fr[3][lane], fmkr = fr[4][lane], fmbr = fr[5][lane];
+        __syncthreads();  // phase 2 writes over the fragments
 
         // ---- phase 2: value block `wave` (tokens x values 16 wave ..)
         bf16x4 dvb;  // this lane's dv (tokens g4 .. g4+3, value 16 wave + lo)
@@ -668,9 +709,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
             const bf16x4 vb = colfrag(L.vv, 16 * wave, lane);    // B operand of V
             const bf16x4 dyb = colfrag(L.dyy, 16 * wave, lane);  // B operand of dY
-            Acc16 z = mma(bf4(dmkkt), vb, z4());                 // Mkk V
-            Acc16 du = mma(bf4(dmbr), dyb, z4());                // Mbr^T dY
-            Acc16 dv = mma(bf4(dmkr), dyb, z4());                // Mkr^T dY
+            Acc16 z = mma(fmkkt, vb, z4());                      // Mkk V
+            Acc16 du = mma(fmbr, dyb, z4());                     // Mbr^T dY
+            Acc16 dv = mma(fmkr, dyb, z4());                     // Mkr^T dY
 #pragma unroll
             for (int jb = 0; jb < 4; ++jb) {
                 const bf16x4 s0b = bf4(S0[jb]), dhb = Dh[jb];  // B operands of S0^T, dSh^T
@@ -679,9 +720,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 dv = mma(frag(L.km, 0, 16 * jb, lane), dhb, dv);    // + Km dSh^T
             }
             du = neg(du);
-            const Acc16 u = mma(bf4(dxt), bf4(z), z4());   // U = X Z
-            const Acc16 dz = mma(bf4(dx), bf4(du), z4());  // dZ = X^T dU
-            dv = mma(bf4(dmkk), bf4(dz), dv);              // + Mkk^T dZ
+            const Acc16 u = mma(fxt, bf4(z), z4());   // U = X Z
+            const Acc16 dz = mma(fx, bf4(du), z4());  // dZ = X^T dU
+            dv = mma(fmkk, bf4(dz), dv);              // + Mkk^T dZ
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = g4 + e;
@@ -694,21 +735,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
         // ---- phase 3: key block `wave` (tokens x keys 16 wave ..)
         {
-            Acc16 dmr = z4(), dmrt = z4(), dmb = z4(), dmbt = z4();   // dMkr, dMkr^T, -dMbr, -dMbr^T
-            Acc16 dmk = z4(), dmkt = z4(), dmn = z4(), dmnt = z4();   // dMkk, dMkk^T, -dMbk, -dMbk^T
+            // this wave's share of the chunk's cotangent matrices (wave 0: dMkr =
+            // dY V^T and its transpose; wave 1: -dMbr = dY U^T; wave 2: dMkk = dZ V^T;
+            // wave 3: -dMbk = dZ U^T), and the products with the state tiles
+            Acc16 m0 = z4(), m1 = z4();
             Acc16 dkms = z4(), dbms = z4(), drp = z4(), dkp = z4();   // V dSh, U dSh, dY S0, dZ S0
 #pragma unroll
             for (int vb = 0; vb < 4; ++vb) {
                 const bf16x4 ya = frag(L.dyy, 0, 16 * vb, lane), va = frag(L.vv, 0, 16 * vb, lane);
                 const bf16x4 ua = frag(L.uu, 0, 16 * vb, lane), za = frag(L.dzz, 0, 16 * vb, lane);
-                dmr = mma(ya, va, dmr);
-                dmrt = mma(va, ya, dmrt);
-                dmb = mma(ya, ua, dmb);
-                dmbt = mma(ua, ya, dmbt);
-                dmk = mma(za, va, dmk);
-                dmkt = mma(va, za, dmkt);
-                dmn = mma(za, ua, dmn);
-                dmnt = mma(ua, za, dmnt);
+                const bf16x4 lhs = wave < 2 ? ya : za, rhs = (wave & 1) ? ua : va;
+                m0 = mma(lhs, rhs, m0);
+                m1 = mma(rhs, lhs, m1);
                 const bf16x4 dsb = frag(L.u.m.dsht, 16 * wave, 16 * vb, lane);  // B operand of dSh
                 const bf16x4 s0b = frag(L.u.m.s0t, 16 * wave, 16 * vb, lane);   // B operand of S0
                 dkms = mma(va, dsb, dkms);
@@ -716,14 +754,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 drp = mma(ya, s0b, drp);
                 dkp = mma(za, s0b, dkp);
             }
-            dmr = mask<true, false>(dmr, lane);
-            dmrt = mask<false, false>(dmrt, lane);
-            dmb = mask<true, false>(dmb, lane);
-            dmbt = mask<false, false>(dmbt, lane);
-            dmk = mask<true, true>(dmk, lane);
-            dmkt = mask<false, true>(dmkt, lane);
-            dmn = mask<true, true>(dmn, lane);
-            dmnt = mask<false, true>(dmnt, lane);
+            // dMkr, -dMbr keep s <= t; dMkk, -dMbk s < t
+            const bool strict = wave >= 2;
+            __syncthreads();  // the state tiles are read: the fragments go over them
+            fr[2 * wave][lane] = bf4(mask_rt<true>(m0, lane, strict));
+            fr[2 * wave + 1][lane] = bf4(mask_rt<false>(m1, lane, strict));
+            __syncthreads();
+            const bf16x4 fdmr = fr[0][lane], fdmrt = fr[1][lane], fdmb = fr[2][lane];
+            const bf16x4 fdmbt = fr[3][lane], fdmk = fr[4][lane], fdmkt = fr[5][lane];
+            const bf16x4 fdmn = fr[6][lane], fdmnt = fr[7][lane];
             // Same-token parts of the decay terms below: the diagonals of dMkr and
             // dMbr and the first sub-diagonals of dMkk and dMbk enter one token's
             // dlg twice with opposite signs (through dRp and dKm, dBm, or dKm, dBm
@@ -737,18 +776,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                 for (int e = 0; e < 4; ++e) {
                     const int row = g4 + e;  // lane holds rows g4 .. g4+3 of column lo
                     if (row == lo) {
-                        dg[0 * kC + lo] = fbf(bf1(dmrt[e]));  // dMkr[t][t], as dRp took it
-                        dg[1 * kC + lo] = fbf(bf1(dmbt[e]));  // -dMbr[t][t], as dRp took it
-                        dg[2 * kC + lo] = fbf(bf1(dmr[e]));   // dMkr[t][t], as dKm took it
-                        dg[3 * kC + lo] = fbf(bf1(dmb[e]));   // -dMbr[t][t], as dBm took it
+                        dg[0 * kC + lo] = fbf(fdmrt[e]);  // dMkr[t][t], as dRp took it
+                        dg[1 * kC + lo] = fbf(fdmbt[e]);  // -dMbr[t][t], as dRp took it
+                        dg[2 * kC + lo] = fbf(fdmr[e]);   // dMkr[t][t], as dKm took it
+                        dg[3 * kC + lo] = fbf(fdmb[e]);   // -dMbr[t][t], as dBm took it
                     }
                     if (row == lo + 1) {
-                        dg[4 * kC + lo] = fbf(bf1(dmk[e]));   // dMkk[t+1][t] (dKm)
-                        dg[5 * kC + lo] = fbf(bf1(dmn[e]));   // -dMbk[t+1][t] (dBm)
+                        dg[4 * kC + lo] = fbf(fdmk[e]);   // dMkk[t+1][t] (dKm)
+                        dg[5 * kC + lo] = fbf(fdmn[e]);   // -dMbk[t+1][t] (dBm)
                     }
                     if (row + 1 == lo) {
-                        dg[6 * kC + lo] = fbf(bf1(dmkt[e]));  // dMkk[t][t-1] (dKp)
-                        dg[7 * kC + lo] = fbf(bf1(dmnt[e]));  // -dMbk[t][t-1] (dKp)
+                        dg[6 * kC + lo] = fbf(fdmkt[e]);  // dMkk[t][t-1] (dKp)
+                        dg[7 * kC + lo] = fbf(fdmnt[e]);  // -dMbk[t][t-1] (dKp)
                     }
                 }
                 if (lane == 0) {  // no token 16 or -1
@@ -761,16 +800,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const bf16x4 rpb = colfrag(L.rp, 16 * wave, lane), kpb = colfrag(L.kp, 16 * wave, lane);
             const bf16x4 kmb = colfrag(L.km, 16 * wave, lane), bmb = colfrag(L.bm, 16 * wave, lane);
             // dKm = V dSh + dMkr^T Rp + dMkk^T Kp
-            Acc16 dkm = mma(bf4(dmk), kpb, mma(bf4(dmr), rpb, dkms));
+            Acc16 dkm = mma(fdmk, kpb, mma(fdmr, rpb, dkms));
             // dBm = -U dSh - (-dMbr)^T Rp - (-dMbk)^T Kp
-            Acc16 dbm = mma(bf4(dmn), kpb, mma(bf4(dmb), rpb, dbms));
+            Acc16 dbm = mma(fdmn, kpb, mma(fdmb, rpb, dbms));
             dbm = neg(dbm);
             // dRp = dY S0 + dMkr Km + dMbr Bm
-            drp = mma(bf4(dmrt), kmb, drp);
-            drp = mma(bf4(neg(dmbt)), bmb, drp);
+            drp = mma(fdmrt, kmb, drp);
+            drp = mma(negb(fdmbt), bmb, drp);
             // dKp = dZ S0 + dMkk Km + dMbk Bm
-            dkp = mma(bf4(dmkt), kmb, dkp);
-            dkp = mma(bf4(neg(dmnt)), bmb, dkp);
+            dkp = mma(fdmkt, kmb, dkp);
+            dkp = mma(negb(fdmnt), bmb, dkp);
             __syncthreads();  // the state tiles are read: their LDS is reused below
             // (and the value tiles: dv waits in U's)
 #pragma unroll
