@@ -639,10 +639,25 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
         __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
         const long ystep = (long)kC * K.TS;
         auto store_state = [&](float *dst) {  // non-temporal: read back only by the backward
+            // key tiles 2h and 2h+1 trade the halves of their rows between lanes lo
+            // and lo ^ 8 (DPP row rotation by 8), so that each store writes 8 rows x
+            // 128 bytes (whole lines) instead of 16 rows x 64 bytes
+            const bool upper = lo >= 8;
+            const int rA = 16 * blk + (upper ? lo - 8 : lo), rB = rA + 8;
 #pragma unroll
-            for (int jb = 0; jb < KB; ++jb)
-                __builtin_nontemporal_store(Z[jb].v,
-                                            reinterpret_cast<f32x4 *>(dst + srow + 16 * jb + 4 * g));
+            for (int h = 0; h < KB / 2; ++h) {
+                f32x4 A, B;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float ra = dpp_mov<kDppRowRor8>(Z[2 * h].v[e]);
+                    const float rb = dpp_mov<kDppRowRor8>(Z[2 * h + 1].v[e]);
+                    A[e] = upper ? rb : Z[2 * h].v[e];
+                    B[e] = upper ? Z[2 * h + 1].v[e] : ra;
+                }
+                const int col = 32 * h + (upper ? 16 : 0) + 4 * g;
+                __builtin_nontemporal_store(A, reinterpret_cast<f32x4 *>(dst + (long)rA * NH + col));
+                __builtin_nontemporal_store(B, reinterpret_cast<f32x4 *>(dst + (long)rB * NH + col));
+            }
         };
         if (ckpt && nch > 0) store_state(ckpt);  // the state before chunk 0
         __syncthreads();  // interval -1: decay totals of chunk 0

@@ -87,6 +87,7 @@ constexpr int kDppQuadXor1 = 0xB1;       // quad_perm [1,0,3,2]
 constexpr int kDppQuadXor2 = 0x4E;       // quad_perm [2,3,0,1]
 constexpr int kDppRowHalfMirror = 0x141;
 constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowRor8 = 0x128;  // row_ror:8, lanes lo and lo ^ 8 of each row trade values
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
