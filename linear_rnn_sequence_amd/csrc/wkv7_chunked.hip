@@ -369,6 +369,9 @@ struct Chunked {
 
     // Chunk operands of the lane's token and keys, written to LDS buffer `o`.
     // lp, lx: the scan of this chunk; carry: this wave's slots of the chunk.
+    // RD = false (the segment summary pass, no readouts): without Rp and the
+    // diagonals of M_kr and M_br, which only the readouts use.
+    template <bool RD>
     __device__ void prep(const Unpacked &u, Ops &o, const float (&rk)[4],
                          const float (&lp)[4], const float (&lx)[4],
                          const float4 (&carry)[3][16]) const {
@@ -387,12 +390,14 @@ struct Chunked {
             const float iG = __builtin_amdgcn_rcpf(q);  // 1 ulp; operands are rounded to bf16
             const float be = a[e] * kp[e];
             Kp[e] = kp[e] * (c[e] * lx[e]);             // kappa_t G_{t-1} (G_{-1} = 1)
-            Rp[e] = r[e] * q;
             Km[e] = k[e] * iG;
             Bm[e] = be * iG;
-            if (EPI) bon += r[e] * k[e] * rk[e];
-            dkr += r[e] * k[e];
-            dbr += r[e] * be;
+            if constexpr (RD) {
+                Rp[e] = r[e] * q;
+                if (EPI) bon += r[e] * k[e] * rk[e];
+                dkr += r[e] * k[e];
+                dbr += r[e] * be;
+            }
         }
         // the lane's 4 keys sit in key block jb at columns c0 .. c0+3: row t of
         // half jb % 2 of pair tile jb / 2
@@ -400,7 +405,7 @@ struct Chunked {
         const int rowoff = t * kRow + c0;
         const int poff = t * kPRow + 8 * (lo & 3) + 4 * (jb & 1);
         *reinterpret_cast<bf16x4 *>(o.kp[jb >> 1] + poff) = to_bf16(Kp);
-        *reinterpret_cast<bf16x4 *>(o.rp[jb >> 1] + poff) = to_bf16(Rp);
+        if constexpr (RD) *reinterpret_cast<bf16x4 *>(o.rp[jb >> 1] + poff) = to_bf16(Rp);
         const bf16x4 kmb = to_bf16(Km), bmb = to_bf16(Bm);
         *reinterpret_cast<bf16x4 *>(o.km[jb >> 1] + poff) = kmb;
         *reinterpret_cast<bf16x4 *>(o.bm[jb >> 1] + poff) = bmb;
@@ -424,21 +429,25 @@ struct Chunked {
         // form would leave an absolute error of ~2^-9 sum_j |r_j k_j| that dominates
         // early readouts whose dot product nearly cancels.  Sums over the group's
         // 64 keys of the token: the 16 lanes of the DPP row.
-        dkr = sum_lanes16(dkr);
-        dbr = sum_lanes16(dbr);
-        if (EPI) bon = sum_lanes16(bon);
-        if (lo == 0) {
-            o.rsum[kh][0][t] = dkr;
-            o.rsum[kh][1][t] = dbr;
-            if (EPI) o.rsum[kh][2][t] = bon;
+        if constexpr (RD) {
+            dkr = sum_lanes16(dkr);
+            dbr = sum_lanes16(dbr);
+            if (EPI) bon = sum_lanes16(bon);
+            if (lo == 0) {
+                o.rsum[kh][0][t] = dkr;
+                o.rsum[kh][1][t] = dbr;
+                if (EPI) o.rsum[kh][2][t] = bon;
+            }
         }
     }
 
     // One C x C matrix of a chunk per prep wave of group 0 (contractions over all
-    // NH keys); wave 1 of the group forms the triangular inverse.
+    // NH keys); wave 1 of the group forms the triangular inverse.  RD = false:
+    // M_kr and M_br (waves 2 and 3), which only the readouts use, are skipped.
+    template <bool RD>
     __device__ void matrices(Ops &o) const {
         const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
-        if (kh != 0) return;
+        if (kh != 0 || (!RD && blk >= 2)) return;
         if (blk == 1) {
             // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
             // is the B form of M and the A form of M^T.
@@ -864,9 +873,10 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
                 // (clamped: always the same loads per interval; refilling before
                 // the operands are formed keeps both live and costs the register
                 // budget that lets two workgroups share a CU)
-                K.matrices(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
+                K.template matrices<!SUMMARY>(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
-                K.prep(u, sm.ops[q % 3], rk, lp, lx, sm.carry[K.kh][q & 1][blk]);
+                K.template prep<!SUMMARY>(u, sm.ops[q % 3], rk, lp, lx,
+                                          sm.carry[K.kh][q & 1][blk]);
                 K.load(q + kPrefetch, x);
                 __builtin_amdgcn_s_waitcnt(wait_older_chunks(kLoads));
                 float w[4];
@@ -878,7 +888,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
         // the intervals left up to nch + 2: the last chunk's matrices if the loop
         // stopped at interval nch, then barriers only
         for (int q = S; q < nch + 3; ++q) {
-            if (q == nch) K.matrices(sm.ops[(nch - 1) % 3]);
+            if (q == nch) K.template matrices<!SUMMARY>(sm.ops[(nch - 1) % 3]);
             __syncthreads();
         }
     }
