@@ -803,8 +803,14 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
             *reinterpret_cast<uint2 *>(sm.ops[i >> 6].mkz + ((i >> 2) & 15) * kPRow +
                                        8 * (i & 3) + 4) = make_uint2(0u, 0u);
         // The prep waves bound each interval (the chain waves wait at the barrier),
-        // so they win the issue arbitration on their SIMD.
-        __builtin_amdgcn_s_setprio(2);
+        // so they win the issue arbitration on their SIMD.  Two workgroups on one
+        // CU: at equal priority the older one wins every tie, finishes ~15% ahead
+        // and leaves the other to run its tail alone; the workgroup in an odd slot
+        // of its CU (HW_ID bits 19:16, the second one placed) takes one level more,
+        // which evens out their finishing times.  Alone on a CU it changes nothing
+        // (the order within the workgroup stays the same).
+        if (workgroup_slot_odd()) __builtin_amdgcn_s_setprio(3);
+        else __builtin_amdgcn_s_setprio(2);
         ProParams pro{};
         const int kch = h * NH + 64 * K.kh + 4 * lo;  // the lane's four keys
         if (FUSED) {
