@@ -88,15 +88,21 @@ namespace {
 
 constexpr int kC = 16;                  // tokens per chunk
 constexpr int kPrefetch = 4;            // chunks of raw inputs in flight per lane
-// s_waitcnt immediate (gfx9 encoding: vmcnt[3:0] + vmcnt[15:14], expcnt[6:4],
-// lgkmcnt[11:8]) that waits until at most 6*(kPrefetch-1) vector loads are
-// outstanding and does not wait on expcnt or lgkmcnt.
-// s_waitcnt immediate that lets the (kPrefetch-1) youngest chunks' loads stay in
-// flight: vmcnt = loads per chunk x (kPrefetch-1), lgkmcnt and expcnt unlimited.
-// Six loads per chunk (r, w, k, kappa, a, v); eight with the fused prologue
-// (r, w, k, a, v and the raw keys of the three other key blocks).
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] + vmcnt[15:14], expcnt[6:4],
+// lgkmcnt[11:8]); expcnt and lgkmcnt are left unlimited.  wait_older_chunks
+// lets the (kPrefetch-1) youngest chunks' loads stay in flight: vmcnt = loads
+// per chunk x (kPrefetch-1), six loads per chunk (r, w, k, kappa, a, v), five
+// with the fused prologue (no kappa).
 constexpr int kWaitAllLoads = (0x7 << 4) | (0xF << 8);  // vmcnt(0) only
 constexpr int kUnroll = 2 * kPrefetch;                   // prep loop unroll
+
+// Whether this workgroup holds an odd slot on its CU: the thread-group ID field
+// of the HW_ID hardware register (bits 19:16; s_getreg operand = register 4,
+// offset 16, width 4).  Of two workgroups placed on one CU the first gets
+// slot 0 and the second slot 1.
+__device__ __forceinline__ bool workgroup_slot_odd() {
+    return (__builtin_amdgcn_s_getreg(4 | (16 << 6) | (3 << 11)) & 1u) != 0;
+}
 
 // Intervals 0 .. S-1 of the prep waves' loop: the nch chunks rounded up to
 // whole loop trips.  In all, the prep waves run max(nch + 3, S) intervals and

@@ -77,14 +77,6 @@ struct RawLoad<F32In> {
     static __device__ __forceinline__ T zero() { return make_float4(0.f, 0.f, 0.f, 0.f); }
 };
 
-// Whether this workgroup holds an odd slot on its CU: the thread-group ID field
-// of the HW_ID hardware register (bits 19:16; s_getreg operand = register 4,
-// offset 16, width 4).  Of two workgroups placed on one CU the first gets
-// slot 0 and the second slot 1.
-__device__ __forceinline__ bool workgroup_slot_odd() {
-    return (__builtin_amdgcn_s_getreg(4 | (16 << 6) | (3 << 11)) & 1u) != 0;
-}
-
 // ---------------------------------------------------------------------------
 // Cross-lane sums with DPP (no LDS traffic).  Lanes are grouped in DPP "rows"
 // of 16; quad_perm swaps within groups of 4, row_half_mirror reverses each
