@@ -301,14 +301,16 @@ rwkv7_status rwkv7_wkv_forward_train(const void *r, const void *w, const void *k
  *              (f32, or N = 128, refused with RWKV7_ERR_UNSUPPORTED); the
  *              chunked form on bf16 MFMA with fp32 accumulation: a reverse
  *              pass over the 16-token chunks carries the state cotangent and
- *              stores it at every chunk's end in the workspace, then every
- *              chunk's gradients are formed in parallel from its stored state
- *              and cotangent;
+ *              stores it at the end of every eighth chunk (the last of each
+ *              group of 8) in the workspace, then the groups' gradients are
+ *              formed in parallel, each group walked last to first from its
+ *              stored cotangent and the stored states;
  *            RWKV7_ALGO_AUTO: CHUNKED for bf16 and bf16 with float32 w at head
  *              size 64, SCAN otherwise.
  *   workspace / workspace_bytes : device scratch of at least
  *            rwkv7_wkv_backward_workspace(...) bytes (CHUNKED: 8 KiB per head
- *            and chunk, each chunk's decayed exit cotangent in bf16; SCAN: none
+ *            and group of 8 chunks, the decayed exit cotangent of the group's
+ *            last chunk in bf16; SCAN: none
  *            at head size 64; at 128, 5 x 4 float32 per element of a slice,
  *            B*H*128*128*4 bytes more when there are several slices; may be
  *            NULL when that is 0); it must not overlap any other argument.

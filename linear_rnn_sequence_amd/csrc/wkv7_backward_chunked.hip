@@ -34,12 +34,16 @@
 // Two kernels:
 //  - bwd_chain_kernel: one workgroup per (b, h) walks the chunks backwards and
 //    carries dS^T as fp32 MFMA accumulator tiles (wave q owns values 16q..16q+15,
-//    like the forward chunked kernel's state); it stores each chunk's dSh in
-//    bf16 (the MFMA operand both kernels use) to the workspace and writes ds0;
-//  - bwd_grad_kernel: the chunks are independent here: from a chunk's stored
-//    entry state and dSh a workgroup recomputes its operands and
-//    forms every gradient; each workgroup takes 8 consecutive chunks of one
-//    head and loads the next chunk's inputs while it works on the current one.
+//    like the forward chunked kernel's state); it stores the dSh of the last
+//    chunk of every group of 8 in bf16 (the MFMA operand both kernels use) to
+//    the workspace and writes ds0;
+//  - bwd_grad_kernel: each workgroup takes one such group (8 consecutive chunks
+//    of one head) and walks it last to first: from a chunk's stored entry
+//    state and dSh it recomputes the chunk's operands and forms every gradient,
+//    and the chunk's dS0 (the products the chain kernel forms) gives the
+//    earlier chunk's dSh, so the state cotangent crosses the group in fp32
+//    registers; it loads the next chunk's inputs while it works on the current
+//    one.
 //    Its four waves each form a share of the chunk's C x C matrices (X, M_kk,
 //    M_kr, M_br, then the cotangent matrices dM) and pass them to the others
 //    through LDS as bf16 MFMA operands.
@@ -132,7 +136,8 @@ __device__ __forceinline__ long tok_off(const BackwardArgs &p, long b, int h, lo
     return ((b * p.T + t) * p.H + h) * kN;
 }
 
-// The workspace holds each chunk's dSh (64 x 64 bf16, 8 KiB) in the order the
+// The workspace holds, per (b, h) and group of 8 chunks, the dSh of the group's
+// last chunk (64 x 64 bf16, 8 KiB) in the order the
 // lanes hold it, not row by row: the four bf16 that lane l of wave q holds of
 // key block jb (dSh[16q + (l & 15)][16jb + 4(l >> 4) + e], e < 4) are at
 // element 4 (64 (4q + jb) + l), so each store and load instruction moves 512
@@ -156,8 +161,9 @@ __device__ __forceinline__ int dsh_tile_offset(int q, int jb, int l) {
 //     (q - 1) % 3 into the matrix tiles of parity (q - 1) & 1;
 //   waves 0..3 ("chain"): wave c owns values 16c .. 16c+15 of dS^T as fp32 MFMA
 //     accumulator tiles and runs the cotangent step of index q - 2 from buffer
-//     (q - 2) % 3 and the matrix tiles of parity q & 1: it stores the chunk's
-//     dSh (bf16, the operand the gradient kernel reads) and forms dS0.
+//     (q - 2) % 3 and the matrix tiles of parity q & 1: it forms the chunk's
+//     dSh (bf16 at a group's last chunk, the operand the gradient kernel reads,
+//     stored) and dS0.
 // Every load is issued on every path (chunk indices clamped), so the ring's
 // wait counts stay exact.
 constexpr int kChainThreads = 576;  // 4 chain waves + 4 prep waves + 1 matrix wave
@@ -199,6 +205,7 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
     const int nch = (p.T + kC - 1) / kC;
+    const int ngrp = (nch + kGradChunks - 1) / kGradChunks;  // gradient groups (workspace slots)
     const int S = (nch + 7) / 6 * 6;  // intervals: nch + 2, rounded up to whole loop trips
 
     if (wave < 4) {
@@ -228,9 +235,10 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
                 const int c = nch - 1 - i;
                 const ChainOps &o = L.o[i % 3];
                 const ChainMatTiles &mt = L.m[i & 1];
-                // dSh = dS_C diag(g_C), stored as the bf16 MFMA operand that both
-                // kernels use, then dS0 of the chunk
-                uint16_t *ck = p.ds_ws + (bh * nch + c) * (long)(kN * kN);
+                // dSh = dS_C diag(g_C), then dS0 of the chunk.  The last chunk of
+                // each gradient group stores its dSh (bf16, the MFMA operand) in
+                // the group's workspace slot; the gradient kernel carries the
+                // cotangent through the group's other chunks itself.
                 bf16x4 Sb[4];
 #pragma unroll
                 for (int jb = 0; jb < 4; ++jb) {
@@ -240,7 +248,12 @@ __global__ __launch_bounds__(kChainThreads) void bwd_chain_kernel(BackwardArgs p
                     St[jb].v[2] *= gc.z;
                     St[jb].v[3] *= gc.w;
                     Sb[jb] = bf4(St[jb]);  // B operand of dSh^T (keys x values)
-                    *reinterpret_cast<bf16x4 *>(ck + dsh_tile_offset(wave, jb, lane)) = Sb[jb];
+                }
+                if (c % kGradChunks == kGradChunks - 1 || c == nch - 1) {
+                    uint16_t *ck = p.ds_ws + (bh * ngrp + c / kGradChunks) * (long)(kN * kN);
+#pragma unroll
+                    for (int jb = 0; jb < 4; ++jb)
+                        *reinterpret_cast<bf16x4 *>(ck + dsh_tile_offset(wave, jb, lane)) = Sb[jb];
                 }
                 const bf16x4 dyb = frag(o.dyt, 16 * wave, 0, lane);  // B operand of dY (tokens x values)
                 Acc16 rhs = mma(frag(mt.mbra, 0, 0, lane), dyb, z4());  // Mbr^T dY
@@ -493,7 +506,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int nch = (p.T + kC - 1) / kC;
     const int ngrp = (nch + kGradChunks - 1) / kGradChunks;
     const long bh = blockIdx.x / ngrp;
-    const int c_begin = (int)(blockIdx.x % ngrp) * kGradChunks;
+    const int grp = (int)(blockIdx.x % ngrp);
+    const int c_begin = grp * kGradChunks;
     const int c_end = min(nch, c_begin + kGradChunks);
     const long b = bh / p.H;
     const int h = (int)(bh % p.H);
@@ -502,8 +516,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                              static_cast<const uint16_t *>(p.kappa), static_cast<const uint16_t *>(p.a),
                              static_cast<const uint16_t *>(p.dy)};
 
-    // A chunk's global inputs, loaded one chunk ahead: its entry state and dSh
-    // (rows 16 wave + lo, keys 16jb + g4 + e) and the raw inputs as
+    // A chunk's global inputs, loaded one chunk ahead (the chunks of the group
+    // are walked last to first): its entry state (rows 16 wave + lo, keys
+    // 16jb + g4 + e), for the group's last chunk its dSh from the workspace
+    // (same layout), and the raw inputs as
     // 16-byte row pieces, piece q = threadIdx.x + 256 i (i < 4):
     //  - bf16 decay: q < 7 * 128 is keys/values 8 (q & 7) .. +7 of token
     //    (q >> 3) & 15 of input q >> 7 (r, w, k, v, kappa, a, dy);
@@ -515,7 +531,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     float4 S0n[4];
     uint2 Dhn[4];  // bf16 dSh
     uint4 rawn[4];
-    auto load_chunk = [&](int cc) {
+    auto load_chunk = [&](int cc, bool with_dsh) {
         // thread index opaque per call, as for the LDS addresses below: the
         // per-thread address parts are recomputed instead of held across the loop
         int tid = threadIdx.x;
@@ -523,11 +539,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const int g4l = 4 * ((tid & 63) >> 4);
         const long srowl = (long)(16 * (tid >> 6) + (tid & 15)) * kN;
         const float *s0p = p.s_ckpt + (bh * nch + cc) * (long)(kN * kN) + srowl;
-        const uint16_t *dsp = p.ds_ws + (bh * nch + cc) * (long)(kN * kN);
+        const uint16_t *dsp = p.ds_ws + (bh * ngrp + grp) * (long)(kN * kN);
 #pragma unroll
         for (int jb = 0; jb < 4; ++jb) {
             S0n[jb] = *reinterpret_cast<const float4 *>(s0p + 16 * jb + g4l);
-            Dhn[jb] = *reinterpret_cast<const uint2 *>(dsp + dsh_tile_offset(tid >> 6, jb, tid & 63));
+            if (with_dsh)
+                Dhn[jb] = *reinterpret_cast<const uint2 *>(dsp + dsh_tile_offset(tid >> 6, jb, tid & 63));
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -585,9 +602,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
         }
     };
-    load_chunk(c_begin);
+    load_chunk(c_end - 1, true);
+    // The state cotangent in fp32, in the layout of the dSh^T tiles: the group's
+    // last chunk starts from its stored dSh; after each chunk's phase 2 it holds
+    // that chunk's dS0, the earlier chunk's dS_C, whose dSh is it times the
+    // earlier chunk's decay total per key (applied after that chunk's phase 1)
+    f32x4 Dhf[4];
+    __builtin_amdgcn_s_waitcnt(kWaitAllLoads);
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const bf16x4 d = __builtin_bit_cast(bf16x4, Dhn[jb]);
+        Dhf[jb] = f32x4{fbf(d[0]), fbf(d[1]), fbf(d[2]), fbf(d[3])};
+    }
 
-    for (int c = c_begin; c < c_end; ++c) {
+    for (int c = c_end - 1; c >= c_begin; --c) {
         // the lane index, opaque to the compiler in each iteration: otherwise every
         // LDS fragment address derived from it is hoisted out of the loop and held
         // in registers for the whole loop
@@ -600,12 +628,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         const long tb = tok_off(p, b, h, t0), TS = (long)p.H * kN;
         const bool full = t0 + kC <= p.T;
         f32x4 S0[4];
-        bf16x4 Dh[4];  // dSh, bf16 as stored
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) {
-            S0[jb] = f32x4{S0n[jb].x, S0n[jb].y, S0n[jb].z, S0n[jb].w};
-            Dh[jb] = __builtin_bit_cast(bf16x4, Dhn[jb]);
-        }
+        for (int jb = 0; jb < 4; ++jb) S0[jb] = f32x4{S0n[jb].x, S0n[jb].y, S0n[jb].z, S0n[jb].w};
 
         // ---- phase 1: operands.  Thread (wave, lane): tokens 4 wave .. +3, key/value `lane`
         stage_chunk(t0);
@@ -644,6 +668,18 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             }
             __syncthreads();
         }
+        if (c != c_end - 1) {
+            // dSh = dS_C diag(g_C) with dS_C the later chunk's dS0
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) {
+                const float4 gc = *reinterpret_cast<const float4 *>(&L.gam[kC - 1][16 * jb + g4]);
+                Dhf[jb] = f32x4{Dhf[jb][0] * gc.x, Dhf[jb][1] * gc.y, Dhf[jb][2] * gc.z,
+                                Dhf[jb][3] * gc.w};
+            }
+        }
+        bf16x4 Dh[4];  // dSh as the bf16 MFMA operand
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) Dh[jb] = bf4(Dhf[jb]);
 
         // ---- chunk matrices, one share per wave, left in LDS as the bf16 A
         // operands every wave reads (wave 0: X = (I + N)^-1 and X^T from N = M_bk;
@@ -686,7 +722,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             fr[2 + wave][lane] = bf4(mask<true, false>(m, lane));
         }
         // the next chunk's inputs, in flight during the rest of this chunk
-        if (c + 1 < c_end) load_chunk(c + 1);
+        if (c > c_begin) load_chunk(c - 1, false);
         __syncthreads();
         const bf16x4 fx = fr[0][lane], fxt = fr[1][lane], fmkk = fr[2][lane];
         const bf16x4 fmkkt = fr[3][lane], fmkr = fr[4][lane], fmbr = fr[5][lane];
@@ -701,7 +737,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int j = 16 * jb + g4 + e;
-                    const float s = sum_lanes16(fbf(Dh[jb][e]) * S0[jb][e]);
+                    const float s = sum_lanes16(Dhf[jb][e] * S0[jb][e]);
                     if (lo == 0) L.dlgc[wave][j] = s;
                     L.u.m.s0t[j][16 * wave + lo] = bf1(S0[jb][e]);
                     L.u.m.dsht[j][16 * wave + lo] = Dh[jb][e];
@@ -723,6 +759,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
             const Acc16 u = mma(fxt, bf4(z), z4());   // U = X Z
             const Acc16 dz = mma(fx, bf4(du), z4());  // dZ = X^T dU
             dv = mma(fmkk, bf4(dz), dv);              // + Mkk^T dZ
+            // the chunk's entry cotangent dS0 = dSh + dY^T Rp + dZ^T Kp (as dS0^T
+            // tiles: keys 16jb .., values 16 wave ..), the next chunk's dS_C
+            if (c > c_begin) {
+                const bf16x4 dzb = bf4(dz);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    Acc16 t = mma(colfrag(L.rp, 16 * jb, lane), dyb, Acc16{Dhf[jb]});
+                    t = mma(colfrag(L.kp, 16 * jb, lane), dzb, t);
+                    Dhf[jb] = t.v;
+                }
+            }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int t = g4 + e;
@@ -927,7 +974,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
 size_t backward_chunked_workspace_bytes(int B, int T, int H) {
     const size_t nch = (size_t)(T + kC - 1) / kC;
-    return (size_t)B * H * nch * kN * kN * sizeof(uint16_t);
+    const size_t ngrp = (nch + kGradChunks - 1) / kGradChunks;
+    return (size_t)B * H * ngrp * kN * kN * sizeof(uint16_t);
 }
 
 bool backward_chunked_grid_ok(int B, int T, int H) {

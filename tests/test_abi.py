@@ -336,7 +336,7 @@ def test_backward_chunked_workspace_codes():
     L = wkv.lib()
     B, T, H = 2, 40, 3
     need = L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 2)
-    assert need == B * H * 3 * 64 * 64 * 2                   # 8 KiB per head and chunk
+    assert need == B * H * 1 * 64 * 64 * 2   # 8 KiB per head and group of 8 chunks (3 chunks)
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 0) == need    # auto -> chunked
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 0, 0) == 0       # f32 -> scan
     assert L.rwkv7_wkv_backward_workspace(B, T, H, 64, 1, 1) == 0
@@ -360,7 +360,9 @@ def test_backward_chunked_workspace_codes():
 def test_binding_workspace_dtype_names():
     # the binding's workspace queries name dtypes as strings; each maps to its own code
     assert wkv.backward_workspace_bytes(2, 40, 3, dtype="bf16_w32") == \
-        wkv.backward_workspace_bytes(2, 40, 3, dtype="bf16") == 2 * 3 * 3 * 64 * 64 * 2
+        wkv.backward_workspace_bytes(2, 40, 3, dtype="bf16") == 2 * 3 * 1 * 64 * 64 * 2
+    # one 8 KiB slot per (b, h) and group of 8 chunks: 129 chunks make 17 groups
+    assert wkv.backward_workspace_bytes(1, 129 * 16, 1, dtype="bf16") == 17 * 64 * 64 * 2
     assert wkv.backward_workspace_bytes(2, 40, 3, dtype="f32") == 0          # auto -> scan
     assert wkv.forward_workspace_bytes(1, 65536, 1, dtype="bf16_w32") == \
         wkv.forward_workspace_bytes(1, 65536, 1, dtype="bfloat16") > 0
