@@ -908,59 +908,103 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
 
 // Entry states of the segments of one (b, h): S_in[0] = s0 (or 0) and
 // S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  The value rows i are independent,
-// so each workgroup owns kCombineRows rows of one (b, h); thread (rr, c) keeps
-// columns 2c, 2c+1 of row rr.  P_g (shared by the rows) goes through a double
-// buffer in LDS, one barrier per segment; the next segment's P and dS are
-// loaded while the current product runs.
+// so each workgroup owns kCombineRows rows of one (b, h); wave q keeps rows 2q
+// and 2q+1 and lane j column j of both, so one LDS read of P serves two rows
+// and the waves' P reads are conflict-free 256-byte rows.  The chain of
+// products is short (about 0.2 us per segment) and latency-bound: P_g and the
+// rows of dS_g are loaded three segments ahead into a four-slot register ring
+// (the loop unrolled by four, so every slot keeps its registers and the
+// compiler's wait counts leave the younger slots in flight; the slots are
+// native vectors and both helpers are forced inline, else they live in scratch
+// memory; indices past the
+// last transition are clamped, so every load is issued on every path), and
+// P_g reaches the workgroup through a double buffer in LDS, one barrier per
+// segment.
 constexpr int kCombineRows = 8;
 constexpr int kCombineParts = kN / kCombineRows;
 
+struct CombineSlot {
+    f32x4 p0, p1, p2, p3;  // thread t's part of P_g: elements 4 (t + 256 m) .. +3, m = 0..3
+    float d0, d1;           // dS_g at (row 2q, column j) and (row 2q + 1, column j)
+};
+
 __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) {
-    __shared__ float2 Pl[2][kN][kN / 2];
-    __shared__ float Sl[2][kCombineRows][kN];
+    __shared__ float Pl[2][kN * kN];
+    __shared__ float4 Sl[2][kCombineRows][kN / 4];
     const long bh = blockIdx.x / kCombineParts;
     const int part = blockIdx.x - (int)bh * kCombineParts;
-    const int t = threadIdx.x, rr = t >> 5, c = t & 31;
-    const long cell = (long)(kCombineRows * part + rr) * kN + 2 * c;  // (i, 2c) in a state
-    const long slot0 = bh * cp.nseg * kN * kN;                          // segment 0 of (b, h)
-    float2 acc = make_float2(0.f, 0.f);
-    if (cp.p.s0) acc = *reinterpret_cast<const float2 *>(cp.p.s0 + bh * kN * kN + cell);
-    // thread t carries P elements 4 (t + 256 m) .. +3, m = 0..3, between global and LDS
-    float4 pn[4];
-    float2 dn = make_float2(0.f, 0.f);
-    if (cp.nseg > 1) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-            pn[m] = *reinterpret_cast<const float4 *>(cp.ws_p + slot0 + 4 * (t + 256 * m));
-        dn = *reinterpret_cast<const float2 *>(cp.ws_ds + slot0 + cell);
+    const int t = threadIdx.x, q = t >> 6, j = t & 63;
+    const int r0 = 2 * q, r1 = 2 * q + 1;                                   // rows of the workgroup
+    const long c0 = (long)(kCombineRows * part + r0) * kN + j, c1 = c0 + kN;  // cells in a state
+    const long slot0 = bh * cp.nseg * kN * kN;                            // segment 0 of (b, h)
+    const int last = cp.nseg - 1;  // transitions and offsets exist for segments 0 .. last - 1
+    float a0 = 0.f, a1 = 0.f;      // S_in of the current segment at (r0, j), (r1, j)
+    if (cp.p.s0) {
+        a0 = cp.p.s0[bh * kN * kN + c0];
+        a1 = cp.p.s0[bh * kN * kN + c1];
     }
-    for (int sg = 0; sg < cp.nseg; ++sg) {
-        const long slot = slot0 + (long)sg * kN * kN;
-        *reinterpret_cast<float2 *>(cp.ws_sin + slot + cell) = acc;
-        if (sg == cp.nseg - 1) break;
+    auto issue = [&](CombineSlot &s, int sg) __attribute__((always_inline)) {
+        const long o = slot0 + (long)min(sg, last - 1) * kN * kN;
+        const f32x4 *pp = reinterpret_cast<const f32x4 *>(cp.ws_p + o) + t;
+        s.p0 = pp[0];
+        s.p1 = pp[256];
+        s.p2 = pp[512];
+        s.p3 = pp[768];
+        s.d0 = cp.ws_ds[o + c0];
+        s.d1 = cp.ws_ds[o + c1];
+        // keep the slots in issue order (the scheduler would otherwise move the
+        // prologue's first slot behind the others and every wait would cover it)
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    // segment sg: store its entry state, issue the loads of segment sg + 3 into
+    // nxt and, unless sg is the last, form the next entry state from cur.  Past
+    // the last segment a step repeats the last store with the same values, so
+    // every step issues the same memory operations and the loop needs no exit
+    // in its body (exits there made the compiler wait for the whole ring).
+    auto step = [&](CombineSlot &cur, CombineSlot &nxt, int sg) __attribute__((always_inline)) {
+        const long o = slot0 + (long)min(sg, last) * kN * kN;
+        cp.ws_sin[o + c0] = a0;
+        cp.ws_sin[o + c1] = a1;
+        issue(nxt, sg + 3);
         const int buf = sg & 1;
-        float *pl = &Pl[buf][0][0].x;
-#pragma unroll
-        for (int m = 0; m < 4; ++m) *reinterpret_cast<float4 *>(pl + 4 * (t + 256 * m)) = pn[m];
-        Sl[buf][rr][2 * c] = acc.x;
-        Sl[buf][rr][2 * c + 1] = acc.y;
-        const float2 d = dn;
-        if (sg + 1 < cp.nseg - 1) {  // operands of the next segment
-            const long nx = slot + kN * kN;
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-                pn[m] = *reinterpret_cast<const float4 *>(cp.ws_p + nx + 4 * (t + 256 * m));
-            dn = *reinterpret_cast<const float2 *>(cp.ws_ds + nx + cell);
+        if (sg < last) {
+            f32x4 *pl = reinterpret_cast<f32x4 *>(Pl[buf]) + t;
+            pl[0] = cur.p0;
+            pl[256] = cur.p1;
+            pl[512] = cur.p2;
+            pl[768] = cur.p3;
+            reinterpret_cast<float *>(Sl[buf][r0])[j] = a0;
+            reinterpret_cast<float *>(Sl[buf][r1])[j] = a1;
         }
         __syncthreads();
-        acc = d;
+        if (sg < last) {
+            // four partial sums per row break the chain of dependent additions
+            float x0[4] = {cur.d0, 0.f, 0.f, 0.f}, x1[4] = {cur.d1, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < kN; ++k) {
-            const float sk = Sl[buf][rr][k];
-            const float2 pk = Pl[buf][k][c];
-            acc.x += sk * pk.x;
-            acc.y += sk * pk.y;
+            for (int k4 = 0; k4 < kN / 4; ++k4) {
+                const float4 s0v = Sl[buf][r0][k4], s1v = Sl[buf][r1][k4];
+                const float sa[4] = {s0v.x, s0v.y, s0v.z, s0v.w};
+                const float sb[4] = {s1v.x, s1v.y, s1v.z, s1v.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float pk = Pl[buf][(4 * k4 + e) * kN + j];
+                    x0[e] += sa[e] * pk;
+                    x1[e] += sb[e] * pk;
+                }
+            }
+            a0 = (x0[0] + x0[1]) + (x0[2] + x0[3]);
+            a1 = (x1[0] + x1[1]) + (x1[2] + x1[3]);
         }
+    };
+    CombineSlot s0, s1, s2, s3;
+    issue(s0, 0);
+    issue(s1, 1);
+    issue(s2, 2);
+    for (int sg = 0; sg <= last; sg += 4) {
+        step(s0, s3, sg);
+        step(s1, s0, sg + 1);
+        step(s2, s1, sg + 2);
+        step(s3, s2, sg + 3);
     }
 }
 
