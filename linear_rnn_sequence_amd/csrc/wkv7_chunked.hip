@@ -127,7 +127,7 @@ struct Geo {
     static constexpr int threads = 64 * (CW + PW);
 };
 constexpr int kThreads = Geo<64>::threads;  // 4 chain waves + 4 prep waves
-constexpr int kThreadsSummary = kThreads;  // the same waves; each chain wave carries two states
+constexpr int kThreadsMW = kThreads + 64;   // ... and a matrix wave
 constexpr int kRow = 20;                // bf16 per LDS tile row (16 + 4 pad, 40 bytes)
 constexpr int kTile = 16 * kRow;        // bf16 per 16x16 tile
 // A pair tile holds two 16x16 tiles (X | Y) so that a lane's K = 32 operand
@@ -230,6 +230,11 @@ struct ProParams {
     float kk[4];
     float ka[4];
 };
+
+// Who forms a chunk's triangular inverse (Chunked::matrices)
+constexpr int kMatInPrep = 0;  // prep wave 1 of group 0, after its other work
+constexpr int kMatSplit = 1;   // a matrix wave of its own; the prep waves skip it
+constexpr int kMatWave = 2;    // the matrix wave itself
 
 template <bool EPI, bool W32, bool FUSED, int NH>
 struct Chunked {
@@ -450,30 +455,19 @@ struct Chunked {
     // One C x C matrix of a chunk per prep wave of group 0 (contractions over all
     // NH keys); wave 1 of the group forms the triangular inverse.  RD = false:
     // M_kr and M_br (waves 2 and 3), which only the readouts use, are skipped.
-    template <bool RD>
+    // MODE kMatInPrep: as above; kMatSplit: a prep wave whose workgroup has a
+    // matrix wave (wave 1 forms nothing); kMatWave: the matrix wave, which forms
+    // the inverse only.
+    template <bool RD, int MODE>
     __device__ void matrices(Ops &o) const {
         const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
+        if (MODE == kMatWave) {
+            inverse(o);
+            return;
+        }
         if (kh != 0 || (!RD && blk >= 2)) return;
         if (blk == 1) {
-            // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
-            // is the B form of M and the A form of M^T.
-            // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
-            Acc32 anb = Acc32::zero(), ana = Acc32::zero();
-#pragma unroll
-            for (int q = 0; q < NH / 32; ++q) {
-                const bf16x8s kpq = ld_pair(o.kp[q], lane), bmq = ld_pair(o.bm[q], lane);
-                anb = mfma32(kpq, bmq, anb);
-                ana = mfma32(bmq, kpq, ana);
-            }
-            f32x4 nb = anb.v, na = ana.v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                nb[e] = (lo < row + e) ? nb[e] : 0.f;   // [t = row+e][s = lo], s < t
-                na[e] = (row + e < lo) ? na[e] : 0.f;   // [s = row+e][t = lo], s < t
-            }
-            f32x4 dx, dxt;
-            tri_inverse(nb, na, lane, dx, dxt);
-            st_a(o.xinv, lane, to_bf16(-dxt));  // A form of X = D(X^T), stored negated
+            if (MODE == kMatInPrep) inverse(o);
         } else {
             // blk 0: M_kk^T = Km.Kp^T, strict; blk 2: M_kr^T = Km.Rp^T; blk 3: M_br^T
             const short(*lhs)[kPTileRows] = (blk == 3) ? o.bm : o.km;
@@ -493,6 +487,30 @@ struct Chunked {
             }
             st_pair(blk == 0 ? o.mkz : o.mrb, blk == 3 ? 1 : 0, lane, to_bf16(m));
         }
+    }
+
+    // -(I + M_bk)^-1 of a chunk into o.xinv (its A form, negated)
+    __device__ void inverse(Ops &o) const {
+        const int row = 4 * g;  // D rows of this lane: row .. row+3; D column: lo
+        // D(M) below: the MFMA result layout of M (lane holds M[4g+e][lo]), which
+        // is the B form of M and the A form of M^T.
+        // N = M_bk (strictly lower): nb = D(N) from Kp.Bm^T, na = D(N^T) from Bm.Kp^T
+        Acc32 anb = Acc32::zero(), ana = Acc32::zero();
+#pragma unroll
+        for (int q = 0; q < NH / 32; ++q) {
+            const bf16x8s kpq = ld_pair(o.kp[q], lane), bmq = ld_pair(o.bm[q], lane);
+            anb = mfma32(kpq, bmq, anb);
+            ana = mfma32(bmq, kpq, ana);
+        }
+        f32x4 nb = anb.v, na = ana.v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            nb[e] = (lo < row + e) ? nb[e] : 0.f;   // [t = row+e][s = lo], s < t
+            na[e] = (row + e < lo) ? na[e] : 0.f;   // [s = row+e][t = lo], s < t
+        }
+        f32x4 dx, dxt;
+        tri_inverse(nb, na, lane, dx, dxt);
+        st_a(o.xinv, lane, to_bf16(-dxt));  // A form of X = D(X^T), stored negated
     }
 };
 
@@ -570,11 +588,11 @@ __device__ __forceinline__ void finish_readouts(const ForwardArgs &p,
 // groups of four waves, each group preparing 64 of every token's keys; 1024
 // threads.  No segments (one workgroup per CU already), no fused prologue, no
 // bidirectional pass and no stored states.
-template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD, int NH>
-__global__ __launch_bounds__(SUMMARY ? kThreadsSummary : Geo<NH>::threads)
-__attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
+template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD, int NH, bool MW>
+__global__ __launch_bounds__(Geo<NH>::threads + (MW ? 64 : 0))
+__attribute__((amdgpu_waves_per_eu(MW ? 3 : 4))) void chunked_kernel(
     ChunkedParams cp) {
-    static_assert(NH == 64 || (!SUMMARY && !YADD), "head size 128: plain forward only");
+    static_assert(NH == 64 || (!SUMMARY && !YADD && !MW), "head size 128: plain forward only");
     using G = Geo<NH>;
     constexpr int KB = G::KB;
     __shared__ ChunkSmem<NH> sm;
@@ -586,8 +604,11 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
     const int wave = threadIdx.x >> 6;
     // chain waves 0 .. CW-1; prep waves CW .. CW+PW-1 in groups of four
     const bool chain_wave = wave < G::CW;
-    const int wblk = chain_wave ? (wave & (G::CW - 1)) : ((wave - G::CW) & 3);
-    const int wkh = chain_wave ? 0 : (wave - G::CW) >> 2;
+    // MW: wave CW + PW forms each chunk's triangular inverse and nothing else (it
+    // takes the place of prep wave 1 of group 0 in the inverse's index math)
+    const bool matrix_wave = MW && wave == G::CW + G::PW;
+    const int wblk = chain_wave ? (wave & (G::CW - 1)) : matrix_wave ? 1 : ((wave - G::CW) & 3);
+    const int wkh = (chain_wave || matrix_wave) ? 0 : (wave - G::CW) >> 2;
     const Chunked<EPI, W32, FUSED, NH> K(p, b, h, t0, min(cp.seg_len, p.T - t0), wblk, wkh);
     const int lane = K.lane, blk = K.blk, g = K.g, lo = K.lo;
     const int nch = (K.Tl + kC - 1) / kC;
@@ -801,6 +822,22 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
                 *reinterpret_cast<float4 *>(p_fin + srow + 16 * jb + 4 * g) =
                     make_float4(Zp[jb][0], Zp[jb][1], Zp[jb][2], Zp[jb][3]);
         }
+    } else if (matrix_wave) {
+        // ---------------- matrix wave: the triangular inverse of chunk q-1 ----------------
+        // The same intervals and barriers as the prep waves (below): interval -1,
+        // the S intervals of their loop and the ones left up to nch + 2.  It is
+        // each interval's longest dependent path, so it takes the highest priority.
+        __builtin_amdgcn_s_setprio(3);
+        __syncthreads();  // interval -1: decay totals of chunk 0
+        const int S = steady_intervals(nch);
+        for (int q = 0; q < S; ++q) {
+            K.template matrices<!SUMMARY, kMatWave>(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
+            __syncthreads();
+        }
+        for (int q = S; q < nch + 3; ++q) {
+            if (q == nch) K.template matrices<!SUMMARY, kMatWave>(sm.ops[(nch - 1) % 3]);
+            __syncthreads();
+        }
     } else {
         // ---------------- prep waves: loads, operands, chunk matrices ----------------
         // the zero half of (M_kk | 0) in every buffer, once (read after the
@@ -815,7 +852,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
         // of its CU (HW_ID bits 19:16, the second one placed) takes one level more,
         // which evens out their finishing times.  Alone on a CU it changes nothing
         // (the order within the workgroup stays the same).
-        if (workgroup_slot_odd()) __builtin_amdgcn_s_setprio(3);
+        if (!MW && workgroup_slot_odd()) __builtin_amdgcn_s_setprio(3);
         else __builtin_amdgcn_s_setprio(2);
         ProParams pro{};
         const int kch = h * NH + 64 * K.kh + 4 * lo;  // the lane's four keys
@@ -851,6 +888,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
         //     (clamped loads).
         // Both are harmless because interval q writes only the buffers of
         // chunks q and q-1 while the chain waves read chunk q-2's.
+        constexpr int kMat = MW ? kMatSplit : kMatInPrep;
         Raw<W32> xs[kPrefetch];
 #pragma unroll
         for (int d = 0; d < kPrefetch; ++d) K.load(d, xs[d]);
@@ -885,7 +923,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
                 // (clamped: always the same loads per interval; refilling before
                 // the operands are formed keeps both live and costs the register
                 // budget that lets two workgroups share a CU)
-                K.template matrices<!SUMMARY>(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
+                K.template matrices<!SUMMARY, kMat>(sm.ops[(q + 2) % 3]);  // chunk q-1 (q >= 1)
                 const auto u = K.unpack(x, q * kC + K.ptok() < K.Tl, pro);
                 K.template prep<!SUMMARY>(u, sm.ops[q % 3], rk, lp, lx,
                                           sm.carry[K.kh][q & 1][blk]);
@@ -900,7 +938,7 @@ __attribute__((amdgpu_waves_per_eu(4))) void chunked_kernel(
         // the intervals left up to nch + 2: the last chunk's matrices if the loop
         // stopped at interval nch, then barriers only
         for (int q = S; q < nch + 3; ++q) {
-            if (q == nch) K.template matrices<!SUMMARY>(sm.ops[(nch - 1) % 3]);
+            if (q == nch) K.template matrices<!SUMMARY, kMat>(sm.ops[(nch - 1) % 3]);
             __syncthreads();
         }
     }
@@ -1062,6 +1100,23 @@ size_t chunked_workspace_bytes(int B, int T, int H) {
     return (size_t)3 * B * H * nseg * kN * kN * sizeof(float);
 }
 
+// One launch of the head-size-64 kernel over `wgs` workgroups.  When every
+// workgroup has a compute unit to itself, the variant with a matrix wave runs:
+// alone on a CU an interval waits for the wave that forms the triangular
+// inverse, and without its share of the operands that wave finishes sooner.
+// With two workgroups per CU the eight-wave form keeps its register budget
+// (a ninth wave would not leave room for the second workgroup).
+template <bool EPI, bool SUMMARY, bool W32, bool FUSED, bool YADD>
+hipError_t launch_chunked64(const ChunkedParams &cp, long wgs, hipStream_t stream) {
+    if (wgs <= device_cu_count())
+        hipLaunchKernelGGL((chunked_kernel<EPI, SUMMARY, W32, FUSED, YADD, 64, true>),
+                           dim3((unsigned)wgs), dim3(kThreadsMW), 0, stream, cp);
+    else
+        hipLaunchKernelGGL((chunked_kernel<EPI, SUMMARY, W32, FUSED, YADD, 64, false>),
+                           dim3((unsigned)wgs), dim3(kThreads), 0, stream, cp);
+    return hipGetLastError();
+}
+
 template <bool W32, bool FUSED, bool YADD>
 hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     const ForwardArgs &p = cp.p;
@@ -1073,10 +1128,8 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
         cp.ws_sin = cp.ws_ds + slab;
         // 1. transitions and offsets of every segment but the last
         cp.nseg_launch = cp.nseg - 1;
-        hipLaunchKernelGGL((chunked_kernel<false, true, W32, FUSED, false, 64>),
-                           dim3((unsigned)(bh * cp.nseg_launch)), dim3(kThreadsSummary), 0,
-                           stream, cp);
-        hipError_t e = hipGetLastError();
+        hipError_t e =
+            launch_chunked64<false, true, W32, FUSED, false>(cp, bh * cp.nseg_launch, stream);
         if (e != hipSuccess) return e;
         // 2. entry state of every segment
         hipLaunchKernelGGL(segment_combine_kernel, dim3((unsigned)(bh * kCombineParts)), dim3(256),
@@ -1086,14 +1139,8 @@ hipError_t launch_chunked_w(ChunkedParams cp, hipStream_t stream) {
     }
     // 3. readouts and final states, all segments in parallel
     cp.nseg_launch = cp.nseg;
-    const dim3 grid((unsigned)(bh * cp.nseg)), block(kThreads);
-    if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false, W32, FUSED, YADD, 64>), grid, block, 0,
-                           stream, cp);
-    else
-        hipLaunchKernelGGL((chunked_kernel<false, false, W32, FUSED, YADD, 64>), grid, block, 0,
-                           stream, cp);
-    return hipGetLastError();
+    if (p.epilogue) return launch_chunked64<true, false, W32, FUSED, YADD>(cp, bh * cp.nseg, stream);
+    return launch_chunked64<false, false, W32, FUSED, YADD>(cp, bh * cp.nseg, stream);
 }
 
 // Head size 128: one workgroup per (b, h), no segments.
@@ -1104,10 +1151,10 @@ hipError_t launch_chunked128(ChunkedParams cp, hipStream_t stream) {
     cp.seg_len = p.T;
     const dim3 grid((unsigned)((long)p.B * p.H)), block(Geo<128>::threads);
     if (p.epilogue)
-        hipLaunchKernelGGL((chunked_kernel<true, false, W32, false, false, 128>), grid, block, 0,
+        hipLaunchKernelGGL((chunked_kernel<true, false, W32, false, false, 128, false>), grid, block, 0,
                            stream, cp);
     else
-        hipLaunchKernelGGL((chunked_kernel<false, false, W32, false, false, 128>), grid, block, 0,
+        hipLaunchKernelGGL((chunked_kernel<false, false, W32, false, false, 128, false>), grid, block, 0,
                            stream, cp);
     return hipGetLastError();
 }
