@@ -224,3 +224,34 @@ def test_chunked_decay_domain(wkv, kind):
         x["w"] = synth.f32_to_bf16_bits(w)
     assert synth.bf16_bits_to_f32(x["w"]).min() >= 2.0 ** -6
     check(wkv, x, f"decay domain, {kind}")
+
+
+@pytest.mark.parametrize("epi", [False, True])
+def test_variants_agree_bitwise(wkv, epi):
+    """A launch with no more workgroups than compute units runs the variant whose
+    ninth wave forms the triangular inverse; a larger one runs the eight-wave
+    form.  Both do the same arithmetic, so the first batch of a large call equals
+    a call made of that batch alone, bit for bit (readouts, final state and, in
+    the training forward, every stored state).  T < 512 keeps both calls in one
+    time segment."""
+    H, T = 40, 500
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    B = cus // H + 1  # B * H workgroups > compute units
+    x = synth.draw(B, T, H, seed=4242, dtype="bf16", s0="normal", epilogue=epi)
+    d = to_device(x, torch)
+    y, s = run(wkv, x, d=d)
+    one = {n: d[n][:1].contiguous() for n in NAMES}
+    y1, s1 = wkv.forward(*(one[n] for n in NAMES), s0=d["s0"][:1].contiguous(), algo="chunked",
+                         epilogue=d["epi"])
+    torch.cuda.synchronize()
+    assert torch.equal(y[:1], y1) and torch.equal(s[:1], s1)
+    if not epi:
+        _, st, ck = wkv.forward_train(*(d[n] for n in NAMES), s0=d["s0"], algo="chunked")
+        _, st1, ck1 = wkv.forward_train(*(one[n] for n in NAMES), s0=d["s0"][:1].contiguous(),
+                                        algo="chunked")
+        torch.cuda.synchronize()
+        assert torch.equal(st[:1], st1) and torch.equal(ck[:1], ck1)
+    # and both agree with the oracle on that batch
+    y_ref, s_ref = oracle_forward(x, b_idx=[0])
+    assert_close(to_f64(y1), y_ref, TOL, "one batch y")
+    assert_close(to_f64(s1), s_ref, TOL, "one batch S_T")
