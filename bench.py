@@ -80,6 +80,21 @@ def parse():
     return ap.parse_args()
 
 
+SPIN_UP_S = 0.5
+
+
+def spin_up(torch, step):
+    """Untimed repetitions of a short step until about SPIN_UP_S seconds of GPU
+    work have run.  A timed run of a few sub-millisecond steps right after start
+    would otherwise be measured partly before the GPU's clocks have settled
+    under sustained load (the default run's 110 ms decode steps do not need it)."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < SPIN_UP_S:
+        for _ in range(8):
+            step()
+        torch.cuda.synchronize()
+
+
 def source_hash(*names):
     """Hash of the kernel sources' code: comments and whitespace are removed
     first, so a profile summary stays attached to the code it measured."""
@@ -278,6 +293,7 @@ def bench_train(args, torch, wkv, synth, dev):
             torch.cuda.synchronize()
             g_first = [g.float().cpu().numpy() for g in grads] + [ds0.cpu().numpy()]
     torch.cuda.synchronize()
+    spin_up(torch, lambda: (fwd(), bwd()))
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(args.steps):
@@ -554,6 +570,8 @@ def main():
                 p_y_first = p_y.float().cpu().numpy()
                 p_s_first = p_s.cpu().numpy()
     torch.cuda.synchronize()
+    if not do_decode:
+        spin_up(torch, prefill)
 
     # ------------------------------------------------------------- timed region
     launch_ms = []
