@@ -948,16 +948,18 @@ __attribute__((amdgpu_waves_per_eu(MW ? 3 : 4))) void chunked_kernel(
 // S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  The value rows i are independent,
 // so each workgroup owns kCombineRows rows of one (b, h); wave q keeps rows 2q
 // and 2q+1 and lane j column j of both, so one LDS read of P serves two rows
-// and the waves' P reads are conflict-free 256-byte rows.  The chain of
-// products is short (about 0.2 us per segment) and latency-bound: P_g and the
-// rows of dS_g are loaded three segments ahead into a four-slot register ring
-// (the loop unrolled by four, so every slot keeps its registers and the
-// compiler's wait counts leave the younger slots in flight; the slots are
-// native vectors and both helpers are forced inline, else they live in scratch
-// memory; indices past the
-// last transition are clamped, so every load is issued on every path), and
-// P_g reaches the workgroup through a double buffer in LDS, one barrier per
-// segment.
+// and the waves' P reads are conflict-free 256-byte rows.  Each product is
+// small, so the chain of G - 1 of them is latency-bound:
+//  - P_g and the rows of dS_g are loaded three segments ahead into a
+//    four-slot register ring; the loop is unrolled by four so that every slot
+//    keeps its registers and the compiler's wait counts leave the younger
+//    slots in flight;
+//  - the slots are native vectors and both helpers are forced inline (else
+//    the slots live in scratch memory);
+//  - indices past the last transition are clamped, so every load is issued on
+//    every path;
+//  - P_g reaches the workgroup through a double buffer in LDS, one barrier per
+//    segment.
 constexpr int kCombineRows = 8;
 constexpr int kCombineParts = kN / kCombineRows;
 
