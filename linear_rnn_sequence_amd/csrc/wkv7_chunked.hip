@@ -946,11 +946,13 @@ __attribute__((amdgpu_waves_per_eu(MW ? 3 : 4))) void chunked_kernel(
 
 // Entry states of the segments of one (b, h): S_in[0] = s0 (or 0) and
 // S_in[g+1] = S_in[g] P_g + dS_g, in fp32.  The value rows i are independent,
-// so each workgroup owns kCombineRows rows of one (b, h); wave q keeps rows 2q
-// and 2q+1 and lane j column j of both, so one LDS read of P serves two rows
-// and the waves' P reads are conflict-free 256-byte rows.  Each product is
-// small, so the chain of G - 1 of them is latency-bound:
-//  - P_g and the rows of dS_g are loaded three segments ahead into a
+// so each workgroup owns kCombineRows = 16 rows of one (b, h), and wave w forms
+// columns 16w .. 16w+15 of them as one 16 x 16 tile of fp32 matrix-core
+// products (v_mfma_f32_16x16x4_f32: the state rows as A, P_g's columns as B,
+// the tile in the accumulator, dS_g its initial value), four partial chains
+// of four products each.  Each product is small, so the chain of G - 1 of
+// them is latency-bound:
+//  - P_g and the tile's rows of dS_g are loaded three segments ahead into a
 //    four-slot register ring; the loop is unrolled by four so that every slot
 //    keeps its registers and the compiler's wait counts leave the younger
 //    slots in flight;
@@ -958,31 +960,48 @@ __attribute__((amdgpu_waves_per_eu(MW ? 3 : 4))) void chunked_kernel(
 //    the slots live in scratch memory);
 //  - indices past the last transition are clamped, so every load is issued on
 //    every path;
-//  - P_g reaches the workgroup through a double buffer in LDS, one barrier per
-//    segment.
-constexpr int kCombineRows = 8;
+//  - P_g and the current state rows reach every wave through double buffers in
+//    LDS, one barrier per segment.
+// The products take k in the order k = 4kb + g (lane group g supplies the g-th
+// k of product kb), so that a lane's B operands, P[4kb + g][16w + lo], sit in
+// LDS rows 80 floats apart (conflict-free across the wave), and the state rows
+// are kept with column 4kb + g at position 16g + kb, so a lane's sixteen A
+// operands are four 16-byte reads.
+constexpr int kCombineRows = 16;
 constexpr int kCombineParts = kN / kCombineRows;
+constexpr int kCombPStride = 80;  // floats per P row in LDS
+constexpr int kCombSStride = 68;  // floats per state row in LDS
 
 struct CombineSlot {
     f32x4 p0, p1, p2, p3;  // thread t's part of P_g: elements 4 (t + 256 m) .. +3, m = 0..3
-    float d0, d1;           // dS_g at (row 2q, column j) and (row 2q + 1, column j)
+    f32x4 d;               // dS_g at rows 4g + e of the block, column 16w + lo
 };
 
 __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) {
-    __shared__ float Pl[2][kN * kN];
-    __shared__ float4 Sl[2][kCombineRows][kN / 4];
+    __shared__ __align__(16) float Pl[2][kN * kCombPStride];
+    __shared__ __align__(16) float Sl[2][kCombineRows * kCombSStride];
     const long bh = blockIdx.x / kCombineParts;
     const int part = blockIdx.x - (int)bh * kCombineParts;
-    const int t = threadIdx.x, q = t >> 6, j = t & 63;
-    const int r0 = 2 * q, r1 = 2 * q + 1;                                   // rows of the workgroup
-    const long c0 = (long)(kCombineRows * part + r0) * kN + j, c1 = c0 + kN;  // cells in a state
-    const long slot0 = bh * cp.nseg * kN * kN;                            // segment 0 of (b, h)
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, lo = lane & 15;
+    const int col = 16 * w + lo;                                      // this lane's column
+    const long cell = (long)(kCombineRows * part + 4 * g) * kN + col;  // element 0's cell; e: + e kN
+    const long slot0 = bh * cp.nseg * kN * kN;                        // segment 0 of (b, h)
     const int last = cp.nseg - 1;  // transitions and offsets exist for segments 0 .. last - 1
-    float a0 = 0.f, a1 = 0.f;      // S_in of the current segment at (r0, j), (r1, j)
+    // S_in of the current segment: element e = row 4g + e of the block, column col
+    f32x4 st = {0.f, 0.f, 0.f, 0.f};
     if (cp.p.s0) {
-        a0 = cp.p.s0[bh * kN * kN + c0];
-        a1 = cp.p.s0[bh * kN * kN + c1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) st[e] = cp.p.s0[bh * kN * kN + cell + e * kN];
     }
+    // where thread t puts its 4 float4 of P in LDS, and where a lane writes its
+    // tile element e in the state rows (column col at position 16 (col & 3) + col / 4)
+    int poff[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const int i = 4 * (t + 256 * m);
+        poff[m] = (i / kN) * kCombPStride + i % kN;
+    }
+    const int spos = 16 * (col & 3) + (col >> 2);
     auto issue = [&](CombineSlot &s, int sg) __attribute__((always_inline)) {
         const long o = slot0 + (long)min(sg, last - 1) * kN * kN;
         const f32x4 *pp = reinterpret_cast<const f32x4 *>(cp.ws_p + o) + t;
@@ -990,8 +1009,8 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) 
         s.p1 = pp[256];
         s.p2 = pp[512];
         s.p3 = pp[768];
-        s.d0 = cp.ws_ds[o + c0];
-        s.d1 = cp.ws_ds[o + c1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s.d[e] = cp.ws_ds[o + cell + e * kN];
         // keep the slots in issue order (the scheduler would otherwise move the
         // prologue's first slot behind the others and every wait would cover it)
         __builtin_amdgcn_sched_barrier(0);
@@ -1003,37 +1022,30 @@ __global__ __launch_bounds__(256) void segment_combine_kernel(ChunkedParams cp) 
     // in its body (exits there made the compiler wait for the whole ring).
     auto step = [&](CombineSlot &cur, CombineSlot &nxt, int sg) __attribute__((always_inline)) {
         const long o = slot0 + (long)min(sg, last) * kN * kN;
-        cp.ws_sin[o + c0] = a0;
-        cp.ws_sin[o + c1] = a1;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) cp.ws_sin[o + cell + e * kN] = st[e];
         issue(nxt, sg + 3);
         const int buf = sg & 1;
         if (sg < last) {
-            f32x4 *pl = reinterpret_cast<f32x4 *>(Pl[buf]) + t;
-            pl[0] = cur.p0;
-            pl[256] = cur.p1;
-            pl[512] = cur.p2;
-            pl[768] = cur.p3;
-            reinterpret_cast<float *>(Sl[buf][r0])[j] = a0;
-            reinterpret_cast<float *>(Sl[buf][r1])[j] = a1;
+            float *pl = Pl[buf];
+            *reinterpret_cast<f32x4 *>(pl + poff[0]) = cur.p0;
+            *reinterpret_cast<f32x4 *>(pl + poff[1]) = cur.p1;
+            *reinterpret_cast<f32x4 *>(pl + poff[2]) = cur.p2;
+            *reinterpret_cast<f32x4 *>(pl + poff[3]) = cur.p3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) Sl[buf][(4 * g + e) * kCombSStride + spos] = st[e];
         }
         __syncthreads();
         if (sg < last) {
-            // four partial sums per row break the chain of dependent additions
-            float x0[4] = {cur.d0, 0.f, 0.f, 0.f}, x1[4] = {cur.d1, 0.f, 0.f, 0.f};
+            // A operands: row lo of the block at columns 4kb + g, kb = 0..15
+            const f32x4 *srow = reinterpret_cast<const f32x4 *>(&Sl[buf][lo * kCombSStride + 16 * g]);
+            const f32x4 a4[4] = {srow[0], srow[1], srow[2], srow[3]};
+            const float *pcol = &Pl[buf][g * kCombPStride + col];  // P[4kb + g][col]: + 4kb rows
+            Acc4 acc[4] = {Acc4{cur.d}, Acc4::zero(), Acc4::zero(), Acc4::zero()};
 #pragma unroll
-            for (int k4 = 0; k4 < kN / 4; ++k4) {
-                const float4 s0v = Sl[buf][r0][k4], s1v = Sl[buf][r1][k4];
-                const float sa[4] = {s0v.x, s0v.y, s0v.z, s0v.w};
-                const float sb[4] = {s1v.x, s1v.y, s1v.z, s1v.w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float pk = Pl[buf][(4 * k4 + e) * kN + j];
-                    x0[e] += sa[e] * pk;
-                    x1[e] += sb[e] * pk;
-                }
-            }
-            a0 = (x0[0] + x0[1]) + (x0[2] + x0[3]);
-            a1 = (x1[0] + x1[1]) + (x1[2] + x1[3]);
+            for (int kb = 0; kb < 16; ++kb)
+                acc[kb & 3] = mfma_f32(a4[kb >> 2][kb & 3], pcol[4 * kb * kCombPStride], acc[kb & 3]);
+            st = (acc[0].v + acc[1].v) + (acc[2].v + acc[3].v);
         }
     };
     CombineSlot s0, s1, s2, s3;
