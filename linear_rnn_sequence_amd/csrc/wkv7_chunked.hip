@@ -1080,11 +1080,13 @@ int device_cu_count() {
 
 // Segments per sequence: split the time axis only when the (b, h) pairs alone
 // leave at least half the compute units idle and each segment keeps at least
-// 16 chunks (the split costs a summary pass over all but the last segment).
-// G segments per (b, h) with B*H*G <= 2 CUs: two workgroups per compute unit,
-// as LDS and registers allow (a pair shortens every segment's serial walk more
-// than it slows each interval: B1 T65536 H40 1.73 -> 1.53 ms against one per
-// CU, B4 T1024 H12 85 -> 67 us against no split).
+// 8 chunks (the split costs a summary pass over all but the last segment, and
+// each pass fills and drains its pipeline).  G segments per (b, h) with
+// B*H*G <= 2 CUs: two workgroups per compute unit, as LDS and registers allow
+// (a pair shortens every segment's serial walk more than it slows each
+// interval: B1 T65536 H40 1.73 -> 1.53 ms against one per CU, B4 T1024 H12
+// 85 -> 67 us against no split; with the matrix-core combine, 8-chunk
+// segments took B4 T1024 H12 from 51.2 to 49.3 us against 16-chunk ones).
 void segment_plan(int B, int T, int H, int &nseg, int &seg_len) {
     nseg = 1;
     seg_len = T;
@@ -1092,7 +1094,7 @@ void segment_plan(int B, int T, int H, int &nseg, int &seg_len) {
     const int cu = device_cu_count();
     if (T < 512 || 2 * bh > cu) return;
     int G = (int)(2 * cu / bh);
-    G = min(G, T / 256);
+    G = min(G, T / 128);
     G = min(G, 64);
     if (G < 2) return;
     int L = (T + G - 1) / G;

@@ -127,7 +127,7 @@ def test_workspace_query_is_pure():
 
 def test_workspace_query_segments():
     """Long sequences of few heads are split into segments (up to two
-    workgroups per compute unit, at least 256 tokens each); each segment keeps
+    workgroups per compute unit, at least 128 tokens each); each segment keeps
     three float32 N x N states in the workspace.  Many heads, short sequences
     or the scan need none."""
     L = wkv.lib()
@@ -138,8 +138,8 @@ def test_workspace_query_segments():
     assert L.rwkv7_wkv_forward_workspace(1, 511, 1, 64, 1, 2) == 0
     assert L.rwkv7_wkv_forward_workspace(64, 65536, 64, 64, 1, 2) == 0
     assert L.rwkv7_wkv_forward_workspace(1, 65536, 1, 64, 1, 1) == 0
-    assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 16 * per_seg  # 256 tokens each
-    assert L.rwkv7_wkv_forward_workspace(1, 512, 1, 64, 1, 2) == 2 * per_seg
+    assert L.rwkv7_wkv_forward_workspace(1, 4096, 1, 64, 1, 2) == 32 * per_seg  # 128 tokens each
+    assert L.rwkv7_wkv_forward_workspace(1, 512, 1, 64, 1, 2) == 4 * per_seg
     assert L.rwkv7_wkv_forward_workspace(200, 4096, 1, 64, 1, 2) == 0   # B*H > CUs / 2
 
 
